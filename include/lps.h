@@ -1,0 +1,287 @@
+/*
+ * lps.h — C ABI of liblps, the MI355X (gfx950) staged single-token decode path.
+ *
+ * A transformer's layers are cut into contiguous ranges ("stages").  Each
+ * stage walks its own layers on its own HIP stream; the only tensor that
+ * crosses a stage boundary is the [n_embd] f32 hidden state, passed through
+ * two persistent, event-ordered slots per boundary; the last stage's logits
+ * are read back later on a dedicated stream.  (memra-engine `pp` module docs:
+ * header, the stage map / boundary runtimes / ownership across a boundary /
+ * deferred readback; functions pp_cuts, stage_of, pp2_overlap.)
+ *
+ * Conventions for every entry point:
+ *  - Return value: LPS_OK (0) or a negative LPS_E* status.  On error nothing
+ *    has been enqueued, and lps_last_error() names the call and the argument
+ *    at fault (thread-local text, valid until the next failing call on the
+ *    same thread).  No entry point aborts, exits or silently falls back.
+ *  - Pointers marked (dev) are device memory of the current HIP device,
+ *    (host) are host memory.  The caller owns every buffer passed in; the
+ *    library never allocates or frees caller memory.  The library owns only
+ *    the opaque handles it creates (and the hipEvents inside them).
+ *  - `stream` arguments are hipStream_t values passed as void*; NULL is the
+ *    null stream.  Work is enqueued, never waited for, unless stated.
+ *  - Row-major layouts: a weight "[N, K]" has row n at offset n*K elements.
+ *    bf16 values are raw 16-bit patterns; MXFP4 is OCP MX v1.0: codes
+ *    u8 [N, K/2] (element 2b in the low nibble of byte b, 2b+1 in the high
+ *    nibble) plus e8m0 scales u8 [N, K/32] (value 2^(s-127)).
+ */
+#ifndef LPS_H
+#define LPS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status ------------------------------------------------------------- */
+enum {
+  LPS_OK = 0,
+  LPS_EINVAL = -1,  /* a bad argument (null pointer, shape, dtype, plan) */
+  LPS_ERANGE = -2,  /* an index or size outside what the objects allow */
+  LPS_ESTATE = -3,  /* a call out of protocol order (e.g. recv of an unsent step) */
+  LPS_EHIP = -4,    /* a HIP runtime call failed; the text names it */
+  LPS_ENOMEM = -5,  /* a host-side allocation for a handle failed */
+  LPS_EUNSUP = -6   /* a combination this build does not implement */
+};
+
+/* Text of the last failure on this thread ("" when none). */
+const char* lps_last_error(void);
+
+/* Library version string; never fails. */
+const char* lps_version(void);
+
+/* ---- dtypes and epilogue modes ----------------------------------------- */
+enum { LPS_F32 = 0, LPS_BF16 = 1, LPS_MXFP4 = 2 };
+enum { LPS_EPI_STORE = 0, LPS_EPI_ADD = 1, LPS_EPI_SWIGLU = 2 };
+
+/* ---- A1: stage plan (host only; needs no GPU) ------------------------------
+ * memra `pp` module docs, header (stage map) and fn pp_cuts; ninfer "Multi-GPU:
+ * layer pipeline stages", How it works (StagePlan, per-stage layer counts).
+ *
+ * lps_stage_plan: writes the fence [0, c1, .., cN-1, n_layers] (n_stages + 1
+ * int32 into fence_out, host).  cuts == NULL with n_cuts == 0 selects the even
+ * split cut_s = floor(s * n_layers / n_stages).  Explicit cuts must number
+ * n_stages - 1, be strictly increasing and lie in (0, n_layers).  n_stages must
+ * lie in [1, n_layers].  Any violation -> LPS_EINVAL (never a silent N = 1).
+ */
+int lps_stage_plan(int32_t n_layers, int32_t n_stages, const int32_t* cuts, int32_t n_cuts,
+                   int32_t* fence_out);
+/* Per-stage layer counts (each >= 1, summing to n_layers) -> fence. */
+int lps_stage_plan_counts(int32_t n_layers, int32_t n_stages, const int32_t* counts,
+                          int32_t* fence_out);
+/* The stage s with fence[s] <= layer < fence[s+1] (>= 0), or a negative status
+ * for an invalid fence or a layer outside [0, fence[n_stages]). (fn stage_of) */
+int lps_stage_of(const int32_t* fence, int32_t n_stages, int32_t layer);
+
+/* ---- A2-A9, A17: one decoder layer ----------------------------------------
+ * The pre-norm block: h = RMSNorm(x)*g_attn; [q|k|v] = W_qkv h; RoPE on the
+ * pairs (i, i+hd/2) of every q and k head at position pos; k, v stored at row
+ * pos of this layer's caches; q head j attends kv head j / (nq/nkv) over rows
+ * 0..pos; x += W_o o; h' = RMSNorm(x)*g_ffn; x += W_d (silu(W_g h') * W_u h')
+ * with W_gu holding the ff gate rows and then the ff up rows.  (TP3 zero-padded
+ * dummy heads plan, Geometry and Weight-padding design for the GQA map and the
+ * padded-head layout; ninfer pipeline stages, Tensor parallelism: status, for
+ * the gate-then-up row order.)
+ */
+typedef struct lps_layer_desc {
+  int32_t d;          /* n_embd */
+  int32_t nq, nkv;    /* q heads, kv heads (nq % nkv == 0) */
+  int32_t hd;         /* head dim (even; 64, 128, 256 supported) */
+  int32_t ff;         /* FFN width */
+  int32_t wdtype;     /* LPS_F32 | LPS_BF16 | LPS_MXFP4 for every matrix */
+  int32_t kvdtype;    /* LPS_F32 | LPS_BF16 */
+  int32_t ctx_max;    /* rows allocated per kv head in each cache */
+  float eps;          /* RMSNorm epsilon */
+  float rope_base;    /* RoPE base (theta_i = base^(-2i/hd)) */
+  const float* g_attn;             /* (dev) [d] f32 */
+  const void* w_qkv; const uint8_t* s_qkv;   /* (dev) [(nq+2nkv)hd, d] (+ scales) */
+  const void* w_o;   const uint8_t* s_o;     /* (dev) [d, nq*hd] */
+  const float* g_ffn;              /* (dev) [d] f32 */
+  const void* w_gu;  const uint8_t* s_gu;    /* (dev) [2ff, d] gate rows, then up rows */
+  const void* w_d;   const uint8_t* s_d;     /* (dev) [d, ff] */
+  void* k_cache;     /* (dev) [nkv, ctx_max, hd] kvdtype, owned by this layer's stage */
+  void* v_cache;     /* (dev) [nkv, ctx_max, hd] kvdtype */
+} lps_layer_desc;
+
+/* Scratch bytes lps_layer_forward needs for this layer (0 on invalid desc). */
+size_t lps_layer_scratch_bytes(const lps_layer_desc* L);
+
+/* One layer on `stream`: x (dev, [d] f32) is updated in place; pos in
+ * [0, ctx_max) is a by-value position (no device scalar is read).  scratch
+ * (dev) of at least lps_layer_scratch_bytes(L) bytes; its contents on entry do
+ * not matter; it must not be used by another stream while this call's work
+ * runs.  Scales (s_*) are required for LPS_MXFP4 and ignored otherwise.
+ * MXFP4 needs d, nq*hd and ff to be multiples of 32; bf16 multiples of 8;
+ * f32 multiples of 4. */
+int lps_layer_forward(const lps_layer_desc* L, float* x, int32_t pos, void* scratch,
+                      size_t scratch_bytes, void* stream);
+
+/* ---- a model handle and the stage walk ----------------------------------- */
+typedef struct lps_model lps_model;
+/* Copies the n_layers descriptors (the device buffers they point at stay the
+ * caller's).  *out receives the handle. */
+int lps_model_create(const lps_layer_desc* layers, int32_t n_layers, lps_model** out);
+int lps_model_destroy(lps_model* m);
+/* Max scratch over the model's layers. */
+size_t lps_model_scratch_bytes(const lps_model* m);
+/* Walks layers [fence[stage], fence[stage+1]) of the model on `stream` over x
+ * (dev [d] f32, in place) at position pos.  The fence is validated (as
+ * lps_stage_plan would produce) before anything is enqueued.  Bumps the
+ * stage_walks counter.  (ninfer pipeline stages, How it works: run_staged.) */
+int lps_stage_forward(const lps_model* m, const int32_t* fence, int32_t n_stages, int32_t stage,
+                      float* x, int32_t pos, void* scratch, size_t scratch_bytes, void* stream);
+
+/* ---- A2: embedding gather ------------------------------------------------
+ * x[0..d) = E[*tok] widened to f32; tok (dev int32) is read on the device so a
+ * previous step's argmax can feed it.  table (dev) [vocab, d] of wdtype
+ * (LPS_F32 | LPS_BF16).  A token outside [0, vocab) writes NaN into x (the
+ * host cannot see the device token; the NaN poisons the step loudly). */
+int lps_embed(const void* table, int32_t wdtype, int32_t vocab, int32_t d, const int32_t* tok,
+              float* x, void* stream);
+
+/* ---- A15, A16: final RMSNorm + LM head + argmax --------------------------
+ * logits (dev [vocab] f32) = W_lm (RMSNorm(x) * g_out); *tok_out (dev int32) =
+ * the lowest index of the maximum logit.  memra pp docs: output_norm and the
+ * LM head live with the last stage. */
+typedef struct lps_head_desc {
+  int32_t d, vocab, wdtype;  /* wdtype LPS_F32 | LPS_BF16 */
+  float eps;
+  const float* g_out;        /* (dev) [d] */
+  const void* w_lm;          /* (dev) [vocab, d] */
+} lps_head_desc;
+size_t lps_head_scratch_bytes(const lps_head_desc* h);
+int lps_head_forward(const lps_head_desc* h, const float* x, float* logits, int32_t* tok_out,
+                     void* scratch, size_t scratch_bytes, void* stream);
+
+/* ---- step-level entry points (the pieces lps_layer_forward launches) ------ */
+/* A3: y = x / sqrt(mean(x^2) + eps) * g, all (dev) [d] f32. */
+int lps_rmsnorm(const float* x, const float* g, float eps, int32_t d, float* y, void* stream);
+/* A4/A7/A8/A9/A17: y = W x' with x' = RMSNorm(x)*norm_g when norm_g != NULL, else x.
+ *  mode LPS_EPI_STORE:  y[n] = (W x')[n], n < N
+ *  mode LPS_EPI_ADD:    y[n] += (W x')[n]          (the residual add)
+ *  mode LPS_EPI_SWIGLU: y[i] = silu(r_i) * r_{N/2+i}, i < N/2, r = W x' (N even)
+ * W (dev) [N, K] of wdtype, s (dev) its e8m0 scales for LPS_MXFP4.  x (dev)
+ * [K] f32.  The K tail is handled per 32-value group for MXFP4 (no read past a
+ * row's end whatever K % 128 is: TP3 plan, Implementation status, item 1). */
+int lps_gemv(int32_t wdtype, const void* w, const uint8_t* s, int32_t N, int32_t K,
+             const float* x, const float* norm_g, float eps, float* y, int32_t mode, void* stream);
+/* A3+A4+A5: q (dev [nq*hd] f32) = RoPE(W_q h); RoPE(W_k h) and W_v h are written
+ * to row pos of the layer's caches; h = RMSNorm(x)*g_attn.  Uses the layer desc's
+ * shapes, weights and caches. */
+int lps_qkv_rope_append(const lps_layer_desc* L, const float* x, int32_t pos, float* q,
+                        void* stream);
+/* A6: o (dev [nq*hd] f32) = softmax(q K^T / sqrt(hd)) V per q head over cache
+ * rows 0..n_rows-1 of kv head j/(nq/nkv).  Caches (dev) [nkv, ctx_max, hd].
+ * scratch (dev) of lps_attention_scratch_bytes(nq, nkv, hd, ctx_max) bytes. */
+size_t lps_attention_scratch_bytes(int32_t nq, int32_t nkv, int32_t hd, int32_t ctx_max);
+int lps_attention_decode(int32_t nq, int32_t nkv, int32_t hd, int32_t kvdtype,
+                         const void* k_cache, const void* v_cache, int32_t ctx_max,
+                         int32_t n_rows, const float* q, float* o, void* scratch,
+                         size_t scratch_bytes, void* stream);
+
+/* ---- A14: boundary slots -------------------------------------------------
+ * memra pp docs, header: each boundary runtime has TWO persistent
+ * double-buffered slots with ev_tx / ev_rx per slot; fn pp2_overlap: the slots
+ * alternate per step.  Slot k = step & 1.
+ *  send(step t): the producer stream waits ev_rx[k] (slot k drained by the
+ *    recv of step t-2), copies x -> slot[k], records ev_tx[k].
+ *  recv(step t): the consumer stream waits ev_tx[k], copies slot[k] -> x,
+ *    records ev_rx[k].
+ * Steps must be sent in order 0, 1, 2, ... and received in the same order;
+ * a recv of a step that was not sent, or out of order, is LPS_ESTATE.
+ * The two slots (dev [n_elems] f32 each) are the caller's. */
+typedef struct lps_boundary lps_boundary;
+int lps_boundary_create(int32_t n_elems, float* slot0, float* slot1, lps_boundary** out);
+int lps_boundary_send(lps_boundary* b, const float* x, int64_t step, void* producer);
+int lps_boundary_recv(lps_boundary* b, float* x, int64_t step, void* consumer);
+/* Synchronizes the boundary's events, then frees the handle. */
+int lps_boundary_destroy(lps_boundary* b);
+
+/* A copy of n f32 values on `stream` (the slot transport, also usable alone). */
+int lps_copy_f32(const float* src, float* dst, int64_t n, void* stream);
+
+/* ---- A16: deferred logits readback ----------------------------------------
+ * memra pp docs, struct PendingLogits: a step's logits stay on the device with
+ * a completion event; wait() orders a dedicated readback stream behind it,
+ * copies and synchronizes; dropping without waiting is safe.
+ * lps_logits_defer records a completion event on `last_stage`, makes
+ * `readback` wait it, enqueues the D2H copies of logits (dev [vocab] f32,
+ * may be NULL) and *tok (dev int32, may be NULL) into host_logits / host_tok
+ * (host; pinned for a truly asynchronous copy), and records a drained event.
+ * The caller must not overwrite the device buffers until the pending is
+ * drained: lps_pending_order(p, stream) makes `stream` wait the drained event.
+ */
+typedef struct lps_pending lps_pending;
+int lps_logits_defer(const float* logits, const int32_t* tok, int32_t vocab, void* last_stage,
+                     void* readback, float* host_logits, int32_t* host_tok, lps_pending** out);
+/* Makes `stream` wait until the pending's copies are done (no host block). */
+int lps_pending_order(lps_pending* p, void* stream);
+/* Blocks the host until host_logits / host_tok hold the step; then frees p.
+ * A second wait on a freed handle is undefined (the handle is gone). */
+int lps_pending_wait(lps_pending* p);
+/* Frees p without waiting: its copies still complete on the readback stream;
+ * the events are released once they have fired. */
+int lps_pending_drop(lps_pending* p);
+
+/* ---- A10-A12: MoE FFN layer ------------------------------------------------
+ * strata PR #3648 (Problem and result; Approach): per-token sums of the
+ * "remote" half of the experts travel as FP16, converted back exactly in
+ * pieces; the combine adds in a fixed order and may write over an input.
+ * Layer: h = RMSNorm(x)*g_ffn; router r = W_r h; pi = softmax(r); top_k by pi
+ * (ties to the lower id), listed by descending pi; w = pi_sel / sum pi_sel;
+ * e_j = W_d,j (silu(W_g,j h) * W_u,j h); local = sum of w_j e_j over selected
+ * j < remote_from in ascending j; remote likewise over j >= remote_from;
+ * shared = the shared expert's output; x += (shared + local) + f32(f16(remote)).
+ */
+typedef struct lps_moe_desc {
+  int32_t d, n_experts, top_k, ff, remote_from;
+  float eps;
+  const float* g_ffn;    /* (dev) [d] f32 */
+  const void* w_r;       /* (dev) [E, d] bf16 */
+  const void* w_gu_e;    /* (dev) [E, 2ff, d] bf16: per expert gate rows then up rows */
+  const void* w_d_e;     /* (dev) [E, d, ff] bf16 */
+  const void* w_gu_s;    /* (dev) [2ff, d] bf16, the shared expert */
+  const void* w_d_s;     /* (dev) [d, ff] bf16 */
+} lps_moe_desc;
+
+/* A10: for T rows of x (dev [T, d] f32): idx (dev [T, top_k] int32), w (dev
+ * [T, top_k] f32).  top_k <= 16, n_experts <= 256. */
+size_t lps_moe_route_scratch_bytes(const lps_moe_desc* m, int32_t T);
+int lps_moe_route(const lps_moe_desc* m, const float* x, int32_t T, int32_t* idx, float* w,
+                  void* scratch, size_t scratch_bytes, void* stream);
+/* A12: x (dev [T, d]) = f32(x + ((shared + local) + bo)) where bo (dev [T, d] f32)
+ * receives f32(remote16), converted piece by piece on `s_remote`: piece p covers
+ * rows [floor(pT/P), floor((p+1)T/P)); each piece's conversion is followed by an
+ * event, and `s_main` waits the last one before the combine.  remote16 (dev
+ * [T, d]) holds f16 bit patterns.  bo may be the same buffer as local. */
+int lps_moe_combine(float* x, const float* shared, const float* local, const uint16_t* remote16,
+                    float* bo, int32_t T, int32_t d, int32_t n_pieces, void* s_remote,
+                    void* s_main);
+/* f32 -> f16 bits (round to nearest even) of n values: the remote half's
+ * "sums_to_f16" step (strata PR #3648, Approach: sums). */
+int lps_f32_to_f16(const float* src, uint16_t* dst, int64_t n, void* stream);
+/* One whole MoE layer for one token (decode): x (dev [d]) updated in place. */
+size_t lps_moe_layer_scratch_bytes(const lps_moe_desc* m);
+int lps_moe_layer_decode(const lps_moe_desc* m, float* x, void* scratch, size_t scratch_bytes,
+                         void* stream);
+
+/* ---- liveness counters ------------------------------------------------------
+ * memra pp docs, Statics (PRIME_SPLIT_CHUNKS and friends): counters that prove
+ * the staged walker ran, so that bit-identity gates cannot pass vacuously.
+ * Process-wide, bumped at enqueue time. */
+typedef struct lps_counters_t {
+  int64_t stage_walks;     /* lps_stage_forward calls that enqueued work */
+  int64_t boundary_sends;
+  int64_t boundary_recvs;
+  int64_t pieces;          /* FP16 pieces converted by lps_moe_combine */
+  int64_t drains;          /* pendings waited or dropped */
+} lps_counters_t;
+int lps_counters(lps_counters_t* out);
+int lps_counters_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LPS_H */

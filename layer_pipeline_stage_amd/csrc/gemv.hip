@@ -1,0 +1,360 @@
+// Batch-1 weight-streaming GEMV for gfx950, with the decode path's fused
+// prologues and epilogues.
+//
+// Decode at batch 1 reads every weight byte once per token and does ~1 flop per
+// byte, so these kernels are HBM-bound (ninfer "Multi-GPU: layer pipeline
+// stages", What it is and is not: decode is weight-bandwidth-bound).  Design:
+//  - one wave (64 lanes) computes one "unit" of two rows; lane l takes the
+//    16-byte chunks l, l+64, l+128, ... of both rows, so a wave issues fully
+//    coalesced 1 KiB loads per instruction and keeps U of them in flight per
+//    row; every chunk of a row always lands on the same lane in the same order
+//    whatever the row length, so zero chunks appended at the end of K (the
+//    padded dummy columns) leave each lane's partial sum, and the result,
+//    bit for bit unchanged;
+//  - the activation vector (f32, optionally RMS-normalised on the way in) sits
+//    in LDS, read once per block from L2 and shared by the block's waves;
+//  - the two rows of a unit are chosen so that the epilogue has what it needs:
+//    rows (i, i + hd/2) of one head for RoPE, rows (i, ff + i) for SwiGLU;
+//  - MXFP4 chunks are 16 bytes of codes = one 32-value e8m0 group, decoded by
+//    the gfx950 scaled FP4 -> f32 conversion; the K loop is bounded per group,
+//    so no K % 128 assumption exists (TP3 zero-padded dummy heads plan,
+//    Implementation status, item 1).
+#include "dev.h"
+#include "gemv_core.h"
+#include "internal.h"
+
+#include <cmath>
+
+namespace lps {
+
+enum { EPI_STORE = LPS_EPI_STORE, EPI_ADD = LPS_EPI_ADD, EPI_SWIGLU = LPS_EPI_SWIGLU,
+       EPI_QKV = 3, EPI_LOGITS = 4 };
+
+struct GemvP {
+  const uint8_t* w;
+  const uint8_t* s;
+  long long wrow;   // bytes per weight row
+  long long srow;   // bytes per scale row (MXFP4)
+  int N, K, units;
+  const float* x;
+  const float* g;
+  float eps;
+  float* y;
+  // QKV epilogue
+  int nq, nkv, hd, pos, ctx_max, kvdtype;
+  float base;
+  void* kc;
+  void* vc;
+  int* zero_ptr;
+  int n_zero;
+  // LM-head epilogue
+  float* pval;
+  int* pidx;
+  int* done;
+  int* tok;
+};
+
+template <int EPI>
+__device__ __forceinline__ void unit_rows(const GemvP& p, int u, int& r0, int& r1) {
+  if constexpr (EPI == EPI_SWIGLU) {
+    r0 = u;
+    r1 = u + (p.N >> 1);
+  } else if constexpr (EPI == EPI_QKV) {
+    const int half = p.hd >> 1;
+    const int hh = u / half, i = u - hh * half;
+    r0 = hh * p.hd + i;
+    r1 = r0 + half;
+  } else {
+    r0 = 2 * u;
+    r1 = (2 * u + 1 < p.N) ? 2 * u + 1 : -1;
+  }
+}
+
+__device__ __forceinline__ void store_kv(void* base, int kvdtype, long long off, float v) {
+  if (kvdtype == LPS_F32)
+    reinterpret_cast<float*>(base)[off] = v;
+  else
+    reinterpret_cast<uint16_t*>(base)[off] = f32_to_bf16(v);
+}
+
+template <int EPI>
+__device__ __forceinline__ void epilogue(const GemvP& p, int u, int r0, int r1, float a0, float a1,
+                                         float& best, int& bidx) {
+  if constexpr (EPI == EPI_STORE) {
+    p.y[r0] = a0;
+    if (r1 >= 0) p.y[r1] = a1;
+  } else if constexpr (EPI == EPI_ADD) {
+    p.y[r0] += a0;
+    if (r1 >= 0) p.y[r1] += a1;
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    p.y[u] = silu(a0) * a1;
+  } else if constexpr (EPI == EPI_LOGITS) {
+    p.y[r0] = a0;
+    if (a0 > best) { best = a0; bidx = r0; }
+    if (r1 >= 0) {
+      p.y[r1] = a1;
+      if (a1 > best) { best = a1; bidx = r1; }
+    }
+  } else {  // QKV: rotate q and k heads at pos, store q, append k and v to the caches
+    const int half = p.hd >> 1;
+    const int hh = u / half, i = u - hh * half;
+    float o0 = a0, o1 = a1;
+    if (hh < p.nq + p.nkv) {
+      const double theta = pow(double(p.base), -2.0 * double(i) / double(p.hd));
+      const double ang = double(p.pos) * theta;
+      double sn, cs;
+      sincos(ang, &sn, &cs);
+      o0 = float(double(a0) * cs - double(a1) * sn);
+      o1 = float(double(a0) * sn + double(a1) * cs);
+    }
+    if (hh < p.nq) {
+      p.y[r0] = o0;
+      p.y[r1] = o1;
+    } else {
+      const bool is_k = hh < p.nq + p.nkv;
+      const int gkv = is_k ? hh - p.nq : hh - p.nq - p.nkv;
+      const long long off = ((long long)gkv * p.ctx_max + p.pos) * p.hd + i;
+      void* base = is_k ? p.kc : p.vc;
+      store_kv(base, p.kvdtype, off, o0);
+      store_kv(base, p.kvdtype, off + half, o1);
+    }
+  }
+}
+
+template <int WT, int EPI, int U, bool NORM>
+__global__ __launch_bounds__(GEMV_THREADS) void k_gemv(GemvP p) {
+  extern __shared__ float xs[];
+  if constexpr (EPI == EPI_QKV) {
+    if (blockIdx.x == 0 && int(threadIdx.x) < p.n_zero) p.zero_ptr[threadIdx.x] = 0;
+  }
+  stage_x<NORM>(p.x, p.g, p.eps, p.K, xs);
+  constexpr int CH = Fmt<WT>::CH;
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int wv = threadIdx.x / WAVE;
+  constexpr int NW = GEMV_THREADS / WAVE;
+  const int nck = p.K / CH;
+  float best = -INFINITY;
+  int bidx = 0x7fffffff;
+  for (int u = blockIdx.x * NW + wv; u < p.units; u += gridDim.x * NW) {
+    int r0, r1;
+    unit_rows<EPI>(p, u, r0, r1);
+    const int rr1 = r1 >= 0 ? r1 : r0;
+    const uint8_t* w0 = p.w + (long long)r0 * p.wrow;
+    const uint8_t* w1 = p.w + (long long)rr1 * p.wrow;
+    const uint8_t* s0 = nullptr;
+    const uint8_t* s1 = nullptr;
+    if constexpr (WT == LPS_MXFP4) {
+      s0 = p.s + (long long)r0 * p.srow;
+      s1 = p.s + (long long)rr1 * p.srow;
+    }
+    float a0 = 0.f, a1 = 0.f;
+    for (int j0 = lane; j0 < nck; j0 += WAVE * U) {
+      u32x4 v0[U], v1[U];
+      uint32_t sc0[U], sc1[U];
+#pragma unroll
+      for (int i = 0; i < U; ++i) {
+        const int c = j0 + WAVE * i;
+        if (c < nck) {
+          v0[i] = ld_stream16(w0 + (long long)c * 16);
+          v1[i] = ld_stream16(w1 + (long long)c * 16);
+          if constexpr (WT == LPS_MXFP4) {
+            sc0[i] = s0[c];
+            sc1[i] = s1[c];
+          } else {
+            sc0[i] = sc1[i] = 0;
+          }
+        } else {
+          v0[i] = v1[i] = u32x4{0, 0, 0, 0};
+          sc0[i] = sc1[i] = 127;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < U; ++i) {
+        const int c = j0 + WAVE * i;
+        if (c < nck) {
+          acc_chunk<WT>(v0[i], sc0[i], xs + c * CH, a0);
+          acc_chunk<WT>(v1[i], sc1[i], xs + c * CH, a1);
+        }
+      }
+    }
+    a0 = wave_sum(a0);
+    a1 = wave_sum(a1);
+    if (lane == 0) epilogue<EPI>(p, u, r0, r1, a0, a1, best, bidx);
+  }
+  if constexpr (EPI == EPI_LOGITS) {
+    __shared__ float bv[NW];
+    __shared__ int bi[NW];
+    __shared__ int is_last;
+    if (lane == 0) {
+      bv[wv] = best;
+      bi[wv] = bidx;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float b = bv[0];
+      int ix = bi[0];
+      for (int i = 1; i < NW; ++i)
+        if (bv[i] > b || (bv[i] == b && bi[i] < ix)) { b = bv[i]; ix = bi[i]; }
+      p.pval[blockIdx.x] = b;
+      p.pidx[blockIdx.x] = ix;
+      __threadfence();
+      const int prev = atomicAdd(p.done, 1);
+      is_last = (prev == int(gridDim.x) - 1);
+    }
+    __syncthreads();
+    if (is_last) {
+      __threadfence();
+      // max with lowest-index ties is an exact selection: any order gives the same answer
+      float b = -INFINITY;
+      int ix = 0x7fffffff;
+      for (int i = threadIdx.x; i < int(gridDim.x); i += GEMV_THREADS) {
+        const float v = __hip_atomic_load(p.pval + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int j = __hip_atomic_load(p.pidx + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (v > b || (v == b && j < ix)) { b = v; ix = j; }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const float ob = __shfl_xor(b, o, WAVE);
+        const int oi = __shfl_xor(ix, o, WAVE);
+        if (ob > b || (ob == b && oi < ix)) { b = ob; ix = oi; }
+      }
+      if (lane == 0) {
+        bv[wv] = b;
+        bi[wv] = ix;
+      }
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        for (int i = 1; i < NW; ++i)
+          if (bv[i] > bv[0] || (bv[i] == bv[0] && bi[i] < bi[0])) { bv[0] = bv[i]; bi[0] = bi[i]; }
+        *p.tok = bi[0];
+        *p.done = 0;   // ready for the next launch
+      }
+    }
+  }
+}
+
+// ---- launch configuration ---------------------------------------------------
+static int max_blocks() { return 256 * 8; }
+
+// The activation vector can exceed 64 KiB (K up to 40960 f32 in 160 KiB of LDS).
+static bool allow_big_lds(const void* fn) {
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess;
+}
+
+template <int WT, int EPI, bool NORM>
+static int launch_t(const GemvP& p, hipStream_t st) {
+  const int NW = GEMV_THREADS / WAVE;
+  int grid = (p.units + NW - 1) / NW;
+  if (grid > max_blocks()) grid = max_blocks();
+  if (EPI == EPI_LOGITS && grid > 4096) grid = 4096;
+  if (grid < 1) grid = 1;
+  const size_t lds = size_t(p.K) * sizeof(float);
+  constexpr int CH = Fmt<WT>::CH;
+  const int per_lane = (p.K / CH + WAVE - 1) / WAVE;
+  // keep up to 8 chunk loads per row in flight per lane
+  if (per_lane <= 4) {
+    static bool attr = allow_big_lds((const void*)k_gemv<WT, EPI, 4, NORM>);
+    (void)attr;
+    hipLaunchKernelGGL((k_gemv<WT, EPI, 4, NORM>), dim3(grid), dim3(GEMV_THREADS), lds, st, p);
+  } else {
+    static bool attr = allow_big_lds((const void*)k_gemv<WT, EPI, 8, NORM>);
+    (void)attr;
+    hipLaunchKernelGGL((k_gemv<WT, EPI, 8, NORM>), dim3(grid), dim3(GEMV_THREADS), lds, st, p);
+  }
+  LPS_HIP(hipGetLastError());
+  return LPS_OK;
+}
+
+template <int EPI, bool NORM>
+static int launch_wt(int wdtype, const GemvP& p, hipStream_t st) {
+  switch (wdtype) {
+    case LPS_F32: return launch_t<LPS_F32, EPI, NORM>(p, st);
+    case LPS_BF16: return launch_t<LPS_BF16, EPI, NORM>(p, st);
+    case LPS_MXFP4: return launch_t<LPS_MXFP4, EPI, NORM>(p, st);
+  }
+  return fail(LPS_EINVAL, "gemv: unknown wdtype %d", wdtype);
+}
+
+static void set_rows(GemvP& p, int wdtype, int K) {
+  if (wdtype == LPS_F32) p.wrow = (long long)K * 4;
+  else if (wdtype == LPS_BF16) p.wrow = (long long)K * 2;
+  else { p.wrow = K / 2; p.srow = K / 32; }
+}
+
+int launch_gemv(int wdtype, const void* w, const uint8_t* s, int N, int K, const float* x,
+                const float* g, float eps, float* y, int mode, hipStream_t st) {
+  GemvP p{};
+  p.w = static_cast<const uint8_t*>(w);
+  p.s = s;
+  p.N = N;
+  p.K = K;
+  p.x = x;
+  p.g = g;
+  p.eps = eps;
+  p.y = y;
+  set_rows(p, wdtype, K);
+  const bool norm = g != nullptr;
+  if (mode == EPI_SWIGLU) {
+    p.units = N / 2;
+    return norm ? launch_wt<EPI_SWIGLU, true>(wdtype, p, st) : launch_wt<EPI_SWIGLU, false>(wdtype, p, st);
+  }
+  p.units = (N + 1) / 2;
+  if (mode == EPI_ADD)
+    return norm ? launch_wt<EPI_ADD, true>(wdtype, p, st) : launch_wt<EPI_ADD, false>(wdtype, p, st);
+  return norm ? launch_wt<EPI_STORE, true>(wdtype, p, st) : launch_wt<EPI_STORE, false>(wdtype, p, st);
+}
+
+int launch_qkv(const QkvArgs& a, hipStream_t st) {
+  const lps_layer_desc* L = a.L;
+  GemvP p{};
+  p.w = static_cast<const uint8_t*>(L->w_qkv);
+  p.s = L->s_qkv;
+  p.N = (L->nq + 2 * L->nkv) * L->hd;
+  p.K = L->d;
+  p.x = a.x;
+  p.g = L->g_attn;
+  p.eps = L->eps;
+  p.y = a.q;
+  p.units = p.N / 2;
+  p.nq = L->nq;
+  p.nkv = L->nkv;
+  p.hd = L->hd;
+  p.pos = a.pos;
+  p.ctx_max = L->ctx_max;
+  p.kvdtype = L->kvdtype;
+  p.base = L->rope_base;
+  p.kc = L->k_cache;
+  p.vc = L->v_cache;
+  p.zero_ptr = a.zero_ptr;
+  p.n_zero = a.zero_ptr ? a.n_zero : 0;
+  set_rows(p, L->wdtype, L->d);
+  return launch_wt<EPI_QKV, true>(L->wdtype, p, st);
+}
+
+size_t head_scratch(const lps_head_desc* h) {
+  (void)h;
+  return align256(256) + align256(4096 * 4) * 2;
+}
+
+int launch_head(const lps_head_desc* h, const float* x, float* logits, int32_t* tok, void* scratch,
+                size_t bytes, hipStream_t st) {
+  (void)bytes;
+  GemvP p{};
+  p.w = static_cast<const uint8_t*>(h->w_lm);
+  p.N = h->vocab;
+  p.K = h->d;
+  p.x = x;
+  p.g = h->g_out;
+  p.eps = h->eps;
+  p.y = logits;
+  p.units = (h->vocab + 1) / 2;
+  char* sc = static_cast<char*>(scratch);
+  p.done = reinterpret_cast<int*>(sc);
+  p.pval = reinterpret_cast<float*>(sc + align256(256));
+  p.pidx = reinterpret_cast<int*>(sc + align256(256) + align256(4096 * 4));
+  p.tok = tok;
+  set_rows(p, h->wdtype, h->d);
+  return launch_wt<EPI_LOGITS, true>(h->wdtype, p, st);
+}
+
+}  // namespace lps

@@ -1,0 +1,517 @@
+// Host side of liblps: status text, the stage plan, liveness counters, boundary
+// slots, deferred logits readback, the model handle and the layer / stage walks.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "internal.h"
+
+namespace lps {
+
+static thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+void clear_error() { g_err[0] = 0; }
+
+static std::atomic<long long> c_walks{0}, c_sends{0}, c_recvs{0}, c_pieces{0}, c_drains{0};
+void count_stage_walk() { c_walks.fetch_add(1, std::memory_order_relaxed); }
+void count_send() { c_sends.fetch_add(1, std::memory_order_relaxed); }
+void count_recv() { c_recvs.fetch_add(1, std::memory_order_relaxed); }
+void count_pieces(int64_t n) { c_pieces.fetch_add(n, std::memory_order_relaxed); }
+void count_drain() { c_drains.fetch_add(1, std::memory_order_relaxed); }
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+static int chunk_of(int wdtype) { return wdtype == LPS_F32 ? 4 : wdtype == LPS_BF16 ? 8 : 32; }
+
+int check_layer(const lps_layer_desc* L, const char* who) {
+  LPS_REQUIRE(L, LPS_EINVAL, "%s: null layer descriptor", who);
+  LPS_REQUIRE(L->d > 0 && L->nq > 0 && L->nkv > 0 && L->hd > 0 && L->ff > 0, LPS_EINVAL,
+              "%s: d/nq/nkv/hd/ff must be > 0 (got %d/%d/%d/%d/%d)", who, L->d, L->nq, L->nkv,
+              L->hd, L->ff);
+  LPS_REQUIRE(L->nq % L->nkv == 0 && L->nq / L->nkv <= 8, LPS_EUNSUP,
+              "%s: nq %d must be a multiple of nkv %d with at most 8 q heads per kv head", who,
+              L->nq, L->nkv);
+  LPS_REQUIRE(L->hd == 64 || L->hd == 128 || L->hd == 256, LPS_EUNSUP,
+              "%s: head dim %d not built (64, 128, 256)", who, L->hd);
+  LPS_REQUIRE(L->wdtype == LPS_F32 || L->wdtype == LPS_BF16 || L->wdtype == LPS_MXFP4, LPS_EINVAL,
+              "%s: wdtype %d", who, L->wdtype);
+  LPS_REQUIRE(L->kvdtype == LPS_F32 || L->kvdtype == LPS_BF16, LPS_EINVAL, "%s: kvdtype %d", who,
+              L->kvdtype);
+  const int ch = chunk_of(L->wdtype);
+  LPS_REQUIRE(L->d % ch == 0 && (L->nq * L->hd) % ch == 0 && L->ff % ch == 0, LPS_EINVAL,
+              "%s: d %d, nq*hd %d and ff %d must be multiples of %d for this weight dtype", who,
+              L->d, L->nq * L->hd, L->ff, ch);
+  LPS_REQUIRE(L->ctx_max > 0, LPS_EINVAL, "%s: ctx_max %d", who, L->ctx_max);
+  LPS_REQUIRE(L->d * 4 <= 160 * 1024 && L->ff * 4 <= 160 * 1024 && L->nq * L->hd * 4 <= 160 * 1024,
+              LPS_EUNSUP, "%s: an activation vector exceeds 160 KiB of LDS", who);
+  LPS_REQUIRE(L->g_attn && L->w_qkv && L->w_o && L->g_ffn && L->w_gu && L->w_d && L->k_cache &&
+                  L->v_cache,
+              LPS_EINVAL, "%s: null weight / gain / cache pointer", who);
+  LPS_REQUIRE(aligned16(L->w_qkv) && aligned16(L->w_o) && aligned16(L->w_gu) && aligned16(L->w_d) &&
+                  aligned16(L->g_attn) && aligned16(L->g_ffn) && aligned16(L->k_cache) &&
+                  aligned16(L->v_cache),
+              LPS_EINVAL, "%s: weights, gains and caches must be 16-byte aligned", who);
+  if (L->wdtype == LPS_MXFP4)
+    LPS_REQUIRE(L->s_qkv && L->s_o && L->s_gu && L->s_d, LPS_EINVAL,
+                "%s: MXFP4 weights need their e8m0 scale arrays", who);
+  return LPS_OK;
+}
+
+// scratch layout of one layer: q | o | m | attention partials
+struct LayerScratch {
+  size_t q, o, m, attn, total;
+};
+static LayerScratch layer_scratch(const lps_layer_desc* L) {
+  LayerScratch s{};
+  s.q = 0;
+  s.o = align256(size_t(L->nq) * L->hd * 4);
+  s.m = s.o + align256(size_t(L->nq) * L->hd * 4);
+  s.attn = s.m + align256(size_t(L->ff) * 4);
+  s.total = s.attn + attn_scratch(L->nq, L->nkv, L->hd, L->ctx_max);
+  return s;
+}
+
+static int layer_forward(const lps_layer_desc* L, float* x, int pos, void* scratch, hipStream_t st) {
+  const LayerScratch s = layer_scratch(L);
+  char* sc = static_cast<char*>(scratch);
+  float* q = reinterpret_cast<float*>(sc + s.q);
+  float* o = reinterpret_cast<float*>(sc + s.o);
+  float* m = reinterpret_cast<float*>(sc + s.m);
+  void* at = sc + s.attn;
+  QkvArgs qa{L, x, pos, q, reinterpret_cast<int*>(at), attn_counters(L->nkv)};
+  int rc = launch_qkv(qa, st);
+  if (rc) return rc;
+  rc = launch_attention(L->nq, L->nkv, L->hd, L->kvdtype, L->k_cache, L->v_cache, L->ctx_max,
+                        pos + 1, q, o, at, true, st);
+  if (rc) return rc;
+  rc = launch_gemv(L->wdtype, L->w_o, L->s_o, L->d, L->nq * L->hd, o, nullptr, 0.f, x,
+                   LPS_EPI_ADD, st);
+  if (rc) return rc;
+  rc = launch_gemv(L->wdtype, L->w_gu, L->s_gu, 2 * L->ff, L->d, x, L->g_ffn, L->eps, m,
+                   LPS_EPI_SWIGLU, st);
+  if (rc) return rc;
+  return launch_gemv(L->wdtype, L->w_d, L->s_d, L->d, L->ff, m, nullptr, 0.f, x, LPS_EPI_ADD, st);
+}
+
+static int check_fence(const int32_t* fence, int32_t n_stages, int32_t n_layers, const char* who) {
+  LPS_REQUIRE(fence, LPS_EINVAL, "%s: null fence", who);
+  LPS_REQUIRE(n_stages >= 1, LPS_EINVAL, "%s: n_stages %d < 1", who, n_stages);
+  LPS_REQUIRE(fence[0] == 0, LPS_EINVAL, "%s: fence[0] = %d, must be 0", who, fence[0]);
+  if (n_layers >= 0)
+    LPS_REQUIRE(fence[n_stages] == n_layers, LPS_EINVAL, "%s: fence[%d] = %d, must be n_layers %d",
+                who, n_stages, fence[n_stages], n_layers);
+  for (int s = 0; s < n_stages; ++s)
+    LPS_REQUIRE(fence[s + 1] > fence[s], LPS_EINVAL,
+                "%s: fence not strictly increasing at stage %d (%d -> %d)", who, s, fence[s],
+                fence[s + 1]);
+  return LPS_OK;
+}
+
+}  // namespace lps
+
+struct lps_model {
+  std::vector<lps_layer_desc> layers;
+  size_t scratch = 0;
+};
+
+struct lps_boundary {
+  int32_t n;
+  float* slot[2];
+  hipEvent_t ev_tx[2];
+  hipEvent_t ev_rx[2];
+  bool tx_recorded[2];
+  bool rx_recorded[2];
+  int64_t next_send;
+  int64_t next_recv;
+};
+
+struct lps_pending {
+  hipEvent_t drained;
+  hipStream_t readback;
+};
+
+using namespace lps;
+
+extern "C" {
+
+const char* lps_last_error(void) { return g_err; }
+const char* lps_version(void) { return "liblps 0.1 (gfx950)"; }
+
+// ---- A1 ------------------------------------------------------------------------
+int lps_stage_plan(int32_t n_layers, int32_t n_stages, const int32_t* cuts, int32_t n_cuts,
+                   int32_t* fence_out) {
+  LPS_REQUIRE(fence_out, LPS_EINVAL, "lps_stage_plan: null fence_out");
+  LPS_REQUIRE(n_layers >= 1, LPS_EINVAL, "lps_stage_plan: n_layers %d < 1", n_layers);
+  LPS_REQUIRE(n_stages >= 1 && n_stages <= n_layers, LPS_EINVAL,
+              "lps_stage_plan: n_stages %d outside [1, n_layers=%d]", n_stages, n_layers);
+  std::vector<int32_t> c;
+  if (cuts == nullptr && n_cuts == 0) {
+    for (int s = 1; s < n_stages; ++s) c.push_back(int32_t((int64_t)s * n_layers / n_stages));
+  } else {
+    LPS_REQUIRE(cuts, LPS_EINVAL, "lps_stage_plan: n_cuts %d with a null cuts array", n_cuts);
+    LPS_REQUIRE(n_cuts == n_stages - 1, LPS_EINVAL,
+                "lps_stage_plan: %d cuts given, n_stages %d needs %d", n_cuts, n_stages,
+                n_stages - 1);
+    c.assign(cuts, cuts + n_cuts);
+  }
+  int32_t prev = 0;
+  for (size_t i = 0; i < c.size(); ++i) {
+    LPS_REQUIRE(c[i] > 0 && c[i] < n_layers && c[i] > prev, LPS_EINVAL,
+                "lps_stage_plan: cut %zu = %d must be strictly increasing inside (0, %d)", i, c[i],
+                n_layers);
+    prev = c[i];
+  }
+  fence_out[0] = 0;
+  for (size_t i = 0; i < c.size(); ++i) fence_out[i + 1] = c[i];
+  fence_out[n_stages] = n_layers;
+  clear_error();
+  return LPS_OK;
+}
+
+int lps_stage_plan_counts(int32_t n_layers, int32_t n_stages, const int32_t* counts,
+                          int32_t* fence_out) {
+  LPS_REQUIRE(counts && fence_out, LPS_EINVAL, "lps_stage_plan_counts: null pointer");
+  LPS_REQUIRE(n_stages >= 1, LPS_EINVAL, "lps_stage_plan_counts: n_stages %d < 1", n_stages);
+  std::vector<int32_t> cuts;
+  int64_t acc = 0;
+  for (int s = 0; s < n_stages; ++s) {
+    LPS_REQUIRE(counts[s] >= 1, LPS_EINVAL, "lps_stage_plan_counts: counts[%d] = %d < 1", s,
+                counts[s]);
+    acc += counts[s];
+    if (s < n_stages - 1) cuts.push_back(int32_t(acc));
+  }
+  LPS_REQUIRE(acc == n_layers, LPS_EINVAL, "lps_stage_plan_counts: counts sum to %lld, not %d",
+              (long long)acc, n_layers);
+  return lps_stage_plan(n_layers, n_stages, cuts.empty() ? nullptr : cuts.data(),
+                        int32_t(cuts.size()), fence_out);
+}
+
+int lps_stage_of(const int32_t* fence, int32_t n_stages, int32_t layer) {
+  int rc = check_fence(fence, n_stages, -1, "lps_stage_of");
+  if (rc) return rc;
+  LPS_REQUIRE(layer >= 0 && layer < fence[n_stages], LPS_ERANGE,
+              "lps_stage_of: layer %d outside [0, %d)", layer, fence[n_stages]);
+  for (int s = 0; s < n_stages; ++s)
+    if (layer < fence[s + 1]) return s;
+  return fail(LPS_ERANGE, "lps_stage_of: unreachable");
+}
+
+// ---- counters ---------------------------------------------------------------------
+int lps_counters(lps_counters_t* out) {
+  LPS_REQUIRE(out, LPS_EINVAL, "lps_counters: null out");
+  out->stage_walks = c_walks.load();
+  out->boundary_sends = c_sends.load();
+  out->boundary_recvs = c_recvs.load();
+  out->pieces = c_pieces.load();
+  out->drains = c_drains.load();
+  return LPS_OK;
+}
+int lps_counters_reset(void) {
+  c_walks = 0;
+  c_sends = 0;
+  c_recvs = 0;
+  c_pieces = 0;
+  c_drains = 0;
+  return LPS_OK;
+}
+
+// ---- layer / model / stage walk ------------------------------------------------------
+size_t lps_layer_scratch_bytes(const lps_layer_desc* L) {
+  if (check_layer(L, "lps_layer_scratch_bytes")) return 0;
+  return layer_scratch(L).total;
+}
+
+int lps_layer_forward(const lps_layer_desc* L, float* x, int32_t pos, void* scratch,
+                      size_t scratch_bytes, void* stream) {
+  int rc = check_layer(L, "lps_layer_forward");
+  if (rc) return rc;
+  LPS_REQUIRE(x && scratch, LPS_EINVAL, "lps_layer_forward: null x or scratch");
+  LPS_REQUIRE(aligned16(x) && aligned16(scratch), LPS_EINVAL,
+              "lps_layer_forward: x and scratch must be 16-byte aligned");
+  LPS_REQUIRE(pos >= 0 && pos < L->ctx_max, LPS_ERANGE, "lps_layer_forward: pos %d outside [0, %d)",
+              pos, L->ctx_max);
+  LPS_REQUIRE(scratch_bytes >= layer_scratch(L).total, LPS_EINVAL,
+              "lps_layer_forward: scratch %zu bytes < %zu needed", scratch_bytes,
+              layer_scratch(L).total);
+  return layer_forward(L, x, pos, scratch, as_stream(stream));
+}
+
+int lps_model_create(const lps_layer_desc* layers, int32_t n_layers, lps_model** out) {
+  LPS_REQUIRE(out, LPS_EINVAL, "lps_model_create: null out");
+  LPS_REQUIRE(layers && n_layers >= 1, LPS_EINVAL, "lps_model_create: need >= 1 layer");
+  size_t mx = 0;
+  for (int i = 0; i < n_layers; ++i) {
+    char who[64];
+    snprintf(who, sizeof who, "lps_model_create(layer %d)", i);
+    int rc = check_layer(&layers[i], who);
+    if (rc) return rc;
+    mx = std::max(mx, layer_scratch(&layers[i]).total);
+  }
+  lps_model* m = new (std::nothrow) lps_model;
+  LPS_REQUIRE(m, LPS_ENOMEM, "lps_model_create: out of host memory");
+  m->layers.assign(layers, layers + n_layers);
+  m->scratch = mx;
+  *out = m;
+  return LPS_OK;
+}
+
+int lps_model_destroy(lps_model* m) {
+  delete m;
+  return LPS_OK;
+}
+
+size_t lps_model_scratch_bytes(const lps_model* m) { return m ? m->scratch : 0; }
+
+int lps_stage_forward(const lps_model* m, const int32_t* fence, int32_t n_stages, int32_t stage,
+                      float* x, int32_t pos, void* scratch, size_t scratch_bytes, void* stream) {
+  LPS_REQUIRE(m, LPS_EINVAL, "lps_stage_forward: null model");
+  int rc = check_fence(fence, n_stages, int32_t(m->layers.size()), "lps_stage_forward");
+  if (rc) return rc;
+  LPS_REQUIRE(stage >= 0 && stage < n_stages, LPS_ERANGE, "lps_stage_forward: stage %d outside [0, %d)",
+              stage, n_stages);
+  LPS_REQUIRE(x && scratch, LPS_EINVAL, "lps_stage_forward: null x or scratch");
+  LPS_REQUIRE(aligned16(x) && aligned16(scratch), LPS_EINVAL,
+              "lps_stage_forward: x and scratch must be 16-byte aligned");
+  LPS_REQUIRE(scratch_bytes >= m->scratch, LPS_EINVAL, "lps_stage_forward: scratch %zu < %zu needed",
+              scratch_bytes, m->scratch);
+  for (int l = fence[stage]; l < fence[stage + 1]; ++l)
+    LPS_REQUIRE(pos >= 0 && pos < m->layers[l].ctx_max, LPS_ERANGE,
+                "lps_stage_forward: pos %d outside layer %d's cache [0, %d)", pos, l,
+                m->layers[l].ctx_max);
+  hipStream_t st = as_stream(stream);
+  for (int l = fence[stage]; l < fence[stage + 1]; ++l) {
+    rc = layer_forward(&m->layers[l], x, pos, scratch, st);
+    if (rc) return rc;
+  }
+  count_stage_walk();
+  return LPS_OK;
+}
+
+// ---- step-level entry points -----------------------------------------------------------
+int lps_gemv(int32_t wdtype, const void* w, const uint8_t* s, int32_t N, int32_t K, const float* x,
+             const float* norm_g, float eps, float* y, int32_t mode, void* stream) {
+  LPS_REQUIRE(wdtype == LPS_F32 || wdtype == LPS_BF16 || wdtype == LPS_MXFP4, LPS_EINVAL,
+              "lps_gemv: wdtype %d", wdtype);
+  LPS_REQUIRE(mode == LPS_EPI_STORE || mode == LPS_EPI_ADD || mode == LPS_EPI_SWIGLU, LPS_EINVAL,
+              "lps_gemv: mode %d", mode);
+  LPS_REQUIRE(N > 0 && K > 0, LPS_EINVAL, "lps_gemv: N %d / K %d must be > 0", N, K);
+  LPS_REQUIRE(K % chunk_of(wdtype) == 0, LPS_EINVAL, "lps_gemv: K %d must be a multiple of %d", K,
+              chunk_of(wdtype));
+  LPS_REQUIRE(mode != LPS_EPI_SWIGLU || N % 2 == 0, LPS_EINVAL, "lps_gemv: SwiGLU needs an even N (%d)", N);
+  LPS_REQUIRE(size_t(K) * 4 <= 160 * 1024, LPS_EUNSUP, "lps_gemv: K %d exceeds the LDS vector", K);
+  LPS_REQUIRE(w && x && y, LPS_EINVAL, "lps_gemv: null w, x or y");
+  LPS_REQUIRE(wdtype != LPS_MXFP4 || s, LPS_EINVAL, "lps_gemv: MXFP4 needs scales");
+  LPS_REQUIRE(aligned16(w) && aligned16(x) && (!norm_g || aligned16(norm_g)), LPS_EINVAL,
+              "lps_gemv: w, x and norm_g must be 16-byte aligned");
+  return launch_gemv(wdtype, w, s, N, K, x, norm_g, eps, y, mode, as_stream(stream));
+}
+
+int lps_qkv_rope_append(const lps_layer_desc* L, const float* x, int32_t pos, float* q,
+                        void* stream) {
+  int rc = check_layer(L, "lps_qkv_rope_append");
+  if (rc) return rc;
+  LPS_REQUIRE(x && q && aligned16(x), LPS_EINVAL, "lps_qkv_rope_append: null or unaligned x / q");
+  LPS_REQUIRE(pos >= 0 && pos < L->ctx_max, LPS_ERANGE,
+              "lps_qkv_rope_append: pos %d outside [0, %d)", pos, L->ctx_max);
+  QkvArgs qa{L, x, pos, q, nullptr, 0};
+  return launch_qkv(qa, as_stream(stream));
+}
+
+size_t lps_attention_scratch_bytes(int32_t nq, int32_t nkv, int32_t hd, int32_t ctx_max) {
+  if (nq <= 0 || nkv <= 0 || nq % nkv || hd <= 0 || ctx_max <= 0) return 0;
+  return attn_scratch(nq, nkv, hd, ctx_max);
+}
+
+int lps_attention_decode(int32_t nq, int32_t nkv, int32_t hd, int32_t kvdtype, const void* k_cache,
+                         const void* v_cache, int32_t ctx_max, int32_t n_rows, const float* q,
+                         float* o, void* scratch, size_t scratch_bytes, void* stream) {
+  LPS_REQUIRE(nq > 0 && nkv > 0 && nq % nkv == 0 && nq / nkv <= 8, LPS_EUNSUP,
+              "lps_attention_decode: nq %d / nkv %d (nq %% nkv == 0, at most 8 per group)", nq, nkv);
+  LPS_REQUIRE(hd == 64 || hd == 128 || hd == 256, LPS_EUNSUP, "lps_attention_decode: head dim %d", hd);
+  LPS_REQUIRE(kvdtype == LPS_F32 || kvdtype == LPS_BF16, LPS_EINVAL, "lps_attention_decode: kvdtype %d",
+              kvdtype);
+  LPS_REQUIRE(n_rows >= 1 && n_rows <= ctx_max, LPS_ERANGE,
+              "lps_attention_decode: n_rows %d outside [1, ctx_max=%d]", n_rows, ctx_max);
+  LPS_REQUIRE(k_cache && v_cache && q && o && scratch, LPS_EINVAL, "lps_attention_decode: null pointer");
+  LPS_REQUIRE(aligned16(k_cache) && aligned16(v_cache), LPS_EINVAL,
+              "lps_attention_decode: caches must be 16-byte aligned");
+  LPS_REQUIRE(scratch_bytes >= attn_scratch(nq, nkv, hd, ctx_max), LPS_EINVAL,
+              "lps_attention_decode: scratch %zu < %zu", scratch_bytes,
+              attn_scratch(nq, nkv, hd, ctx_max));
+  return launch_attention(nq, nkv, hd, kvdtype, k_cache, v_cache, ctx_max, n_rows, q, o, scratch,
+                          false, as_stream(stream));
+}
+
+size_t lps_head_scratch_bytes(const lps_head_desc* h) { return h ? head_scratch(h) : 0; }
+
+int lps_head_forward(const lps_head_desc* h, const float* x, float* logits, int32_t* tok_out,
+                     void* scratch, size_t scratch_bytes, void* stream) {
+  LPS_REQUIRE(h, LPS_EINVAL, "lps_head_forward: null head");
+  LPS_REQUIRE(h->d > 0 && h->vocab > 0, LPS_EINVAL, "lps_head_forward: d %d / vocab %d", h->d, h->vocab);
+  LPS_REQUIRE(h->wdtype == LPS_F32 || h->wdtype == LPS_BF16, LPS_EINVAL,
+              "lps_head_forward: wdtype %d (f32 or bf16)", h->wdtype);
+  LPS_REQUIRE(h->d % chunk_of(h->wdtype) == 0 && size_t(h->d) * 4 <= 160 * 1024, LPS_EINVAL,
+              "lps_head_forward: d %d", h->d);
+  LPS_REQUIRE(h->g_out && h->w_lm && x && logits && tok_out && scratch, LPS_EINVAL,
+              "lps_head_forward: null pointer");
+  LPS_REQUIRE(aligned16(h->w_lm) && aligned16(h->g_out) && aligned16(x), LPS_EINVAL,
+              "lps_head_forward: weights, gain and x must be 16-byte aligned");
+  LPS_REQUIRE(scratch_bytes >= head_scratch(h), LPS_EINVAL, "lps_head_forward: scratch %zu < %zu",
+              scratch_bytes, head_scratch(h));
+  return launch_head(h, x, logits, tok_out, scratch, scratch_bytes, as_stream(stream));
+}
+
+// ---- A14 boundaries ----------------------------------------------------------------------
+int lps_boundary_create(int32_t n_elems, float* slot0, float* slot1, lps_boundary** out) {
+  LPS_REQUIRE(out, LPS_EINVAL, "lps_boundary_create: null out");
+  LPS_REQUIRE(n_elems > 0, LPS_EINVAL, "lps_boundary_create: n_elems %d", n_elems);
+  LPS_REQUIRE(slot0 && slot1 && slot0 != slot1, LPS_EINVAL,
+              "lps_boundary_create: need two distinct slots");
+  LPS_REQUIRE(aligned16(slot0) && aligned16(slot1), LPS_EINVAL,
+              "lps_boundary_create: slots must be 16-byte aligned");
+  lps_boundary* b = new (std::nothrow) lps_boundary;
+  LPS_REQUIRE(b, LPS_ENOMEM, "lps_boundary_create: out of host memory");
+  b->n = n_elems;
+  b->slot[0] = slot0;
+  b->slot[1] = slot1;
+  b->next_send = 0;
+  b->next_recv = 0;
+  for (int k = 0; k < 2; ++k) {
+    b->tx_recorded[k] = b->rx_recorded[k] = false;
+    hipError_t e1 = hipEventCreateWithFlags(&b->ev_tx[k], hipEventDisableTiming);
+    hipError_t e2 = hipEventCreateWithFlags(&b->ev_rx[k], hipEventDisableTiming);
+    if (e1 != hipSuccess || e2 != hipSuccess) {
+      delete b;
+      return fail(LPS_EHIP, "lps_boundary_create: hipEventCreate failed");
+    }
+  }
+  *out = b;
+  return LPS_OK;
+}
+
+int lps_boundary_send(lps_boundary* b, const float* x, int64_t step, void* producer) {
+  LPS_REQUIRE(b && x, LPS_EINVAL, "lps_boundary_send: null boundary or x");
+  LPS_REQUIRE(aligned16(x), LPS_EINVAL, "lps_boundary_send: x must be 16-byte aligned");
+  LPS_REQUIRE(step == b->next_send, LPS_ESTATE,
+              "lps_boundary_send: step %lld sent out of order (expected %lld)", (long long)step,
+              (long long)b->next_send);
+  LPS_REQUIRE(step - b->next_recv < 2, LPS_ESTATE,
+              "lps_boundary_send: step %lld would overwrite slot %d before step %lld was received",
+              (long long)step, int(step & 1), (long long)(step - 2));
+  const int k = int(step & 1);
+  hipStream_t st = as_stream(producer);
+  if (b->rx_recorded[k]) LPS_HIP(hipStreamWaitEvent(st, b->ev_rx[k], 0));
+  int rc = launch_copy_f32(x, b->slot[k], b->n, st);
+  if (rc) return rc;
+  LPS_HIP(hipEventRecord(b->ev_tx[k], st));
+  b->tx_recorded[k] = true;
+  b->next_send = step + 1;
+  count_send();
+  return LPS_OK;
+}
+
+int lps_boundary_recv(lps_boundary* b, float* x, int64_t step, void* consumer) {
+  LPS_REQUIRE(b && x, LPS_EINVAL, "lps_boundary_recv: null boundary or x");
+  LPS_REQUIRE(aligned16(x), LPS_EINVAL, "lps_boundary_recv: x must be 16-byte aligned");
+  LPS_REQUIRE(step == b->next_recv, LPS_ESTATE,
+              "lps_boundary_recv: step %lld received out of order (expected %lld)", (long long)step,
+              (long long)b->next_recv);
+  LPS_REQUIRE(step < b->next_send, LPS_ESTATE, "lps_boundary_recv: step %lld was never sent",
+              (long long)step);
+  const int k = int(step & 1);
+  hipStream_t st = as_stream(consumer);
+  LPS_HIP(hipStreamWaitEvent(st, b->ev_tx[k], 0));
+  int rc = launch_copy_f32(b->slot[k], x, b->n, st);
+  if (rc) return rc;
+  LPS_HIP(hipEventRecord(b->ev_rx[k], st));
+  b->rx_recorded[k] = true;
+  b->next_recv = step + 1;
+  count_recv();
+  return LPS_OK;
+}
+
+int lps_boundary_destroy(lps_boundary* b) {
+  if (!b) return LPS_OK;
+  int rc = LPS_OK;
+  for (int k = 0; k < 2; ++k) {
+    if (hipEventSynchronize(b->ev_tx[k]) != hipSuccess) rc = LPS_EHIP;
+    if (hipEventSynchronize(b->ev_rx[k]) != hipSuccess) rc = LPS_EHIP;
+    (void)hipEventDestroy(b->ev_tx[k]);
+    (void)hipEventDestroy(b->ev_rx[k]);
+  }
+  delete b;
+  if (rc) return fail(rc, "lps_boundary_destroy: hipEventSynchronize failed");
+  return LPS_OK;
+}
+
+// ---- A16 deferred readback ------------------------------------------------------------------
+int lps_logits_defer(const float* logits, const int32_t* tok, int32_t vocab, void* last_stage,
+                     void* readback, float* host_logits, int32_t* host_tok, lps_pending** out) {
+  LPS_REQUIRE(out, LPS_EINVAL, "lps_logits_defer: null out");
+  LPS_REQUIRE(logits || tok, LPS_EINVAL, "lps_logits_defer: nothing to read back");
+  LPS_REQUIRE(!logits || (host_logits && vocab > 0), LPS_EINVAL,
+              "lps_logits_defer: logits need host_logits and vocab > 0");
+  LPS_REQUIRE(!tok || host_tok, LPS_EINVAL, "lps_logits_defer: tok needs host_tok");
+  hipStream_t ls = as_stream(last_stage), rb = as_stream(readback);
+  hipEvent_t done;
+  LPS_HIP(hipEventCreateWithFlags(&done, hipEventDisableTiming));
+  lps_pending* p = new (std::nothrow) lps_pending;
+  if (!p) {
+    (void)hipEventDestroy(done);
+    return fail(LPS_ENOMEM, "lps_logits_defer: out of host memory");
+  }
+  p->readback = rb;
+  hipError_t e = hipEventCreateWithFlags(&p->drained, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventRecord(done, ls);
+  if (e == hipSuccess) e = hipStreamWaitEvent(rb, done, 0);
+  if (e == hipSuccess && logits)
+    e = hipMemcpyAsync(host_logits, logits, size_t(vocab) * 4, hipMemcpyDeviceToHost, rb);
+  if (e == hipSuccess && tok) e = hipMemcpyAsync(host_tok, tok, 4, hipMemcpyDeviceToHost, rb);
+  if (e == hipSuccess) e = hipEventRecord(p->drained, rb);
+  (void)hipEventDestroy(done);
+  if (e != hipSuccess) {
+    delete p;
+    return fail(LPS_EHIP, "lps_logits_defer: %s", hipGetErrorString(e));
+  }
+  *out = p;
+  return LPS_OK;
+}
+
+int lps_pending_order(lps_pending* p, void* stream) {
+  LPS_REQUIRE(p, LPS_EINVAL, "lps_pending_order: null pending");
+  LPS_HIP(hipStreamWaitEvent(as_stream(stream), p->drained, 0));
+  return LPS_OK;
+}
+
+int lps_pending_wait(lps_pending* p) {
+  LPS_REQUIRE(p, LPS_EINVAL, "lps_pending_wait: null pending");
+  hipError_t e = hipEventSynchronize(p->drained);
+  (void)hipEventDestroy(p->drained);
+  delete p;
+  count_drain();
+  if (e != hipSuccess) return fail(LPS_EHIP, "lps_pending_wait: %s", hipGetErrorString(e));
+  return LPS_OK;
+}
+
+int lps_pending_drop(lps_pending* p) {
+  LPS_REQUIRE(p, LPS_EINVAL, "lps_pending_drop: null pending");
+  // the copies stay enqueued; destroying the event defers its release until it fires
+  (void)hipEventDestroy(p->drained);
+  delete p;
+  count_drain();
+  return LPS_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,70 @@
+// Internal declarations shared by the liblps translation units (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/lps.h"
+
+namespace lps {
+
+// ---- errors -----------------------------------------------------------------
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
+#define LPS_HIP(call)                                                                  \
+  do {                                                                                 \
+    hipError_t e_ = (call);                                                            \
+    if (e_ != hipSuccess)                                                              \
+      return ::lps::fail(LPS_EHIP, "%s: %s failed: %s", __func__, #call,               \
+                         hipGetErrorString(e_));                                       \
+  } while (0)
+
+#define LPS_REQUIRE(cond, code, ...)                                                   \
+  do {                                                                                 \
+    if (!(cond)) return ::lps::fail((code), __VA_ARGS__);                              \
+  } while (0)
+
+// ---- counters -----------------------------------------------------------------
+void count_stage_walk();
+void count_send();
+void count_recv();
+void count_pieces(int64_t n);
+void count_drain();
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// ---- scratch carving ------------------------------------------------------------
+inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+// ---- launchers (each validates nothing; callers validate first) -------------------
+struct QkvArgs {
+  const lps_layer_desc* L;
+  const float* x;
+  int pos;
+  float* q;
+  int* zero_ptr;   // ints to clear before the attention kernel runs (may be null)
+  int n_zero;
+};
+int launch_gemv(int wdtype, const void* w, const uint8_t* s, int N, int K, const float* x,
+                const float* g, float eps, float* y, int mode, hipStream_t st);
+int launch_qkv(const QkvArgs& a, hipStream_t st);
+int launch_head(const lps_head_desc* h, const float* x, float* logits, int32_t* tok,
+                void* scratch, size_t bytes, hipStream_t st);
+size_t head_scratch(const lps_head_desc* h);
+
+size_t attn_scratch(int nq, int nkv, int hd, int ctx_max);
+int attn_counters(int nkv);  // number of leading int counters in the attention scratch
+int launch_attention(int nq, int nkv, int hd, int kvdtype, const void* kc, const void* vc,
+                     int ctx_max, int n_rows, const float* q, float* o, void* scratch,
+                     bool counters_zeroed, hipStream_t st);
+
+int launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t st);
+
+// validation helpers shared by entry points
+int check_layer(const lps_layer_desc* L, const char* who);
+
+}  // namespace lps

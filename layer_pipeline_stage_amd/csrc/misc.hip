@@ -1,0 +1,170 @@
+// Small kernels of the decode path: embedding gather, standalone RMSNorm, the
+// boundary-slot copy, f32 <-> f16 piece conversions and the MoE combine.
+#include "dev.h"
+#include "internal.h"
+
+#include <cmath>
+
+namespace lps {
+
+// ---- A2: x = E[tok] (the token is read on the device) ------------------------
+template <int WT>
+__global__ void k_embed(const void* table, int vocab, int d, const int32_t* tok, float* x) {
+  const int t = *tok;
+  const bool ok = t >= 0 && t < vocab;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < d; i += gridDim.x * blockDim.x) {
+    float v;
+    if (!ok) v = __uint_as_float(0x7FC00000u);
+    else if (WT == LPS_F32) v = static_cast<const float*>(table)[(long long)t * d + i];
+    else v = bf16_to_f32(static_cast<const uint16_t*>(table)[(long long)t * d + i]);
+    x[i] = v;
+  }
+}
+
+// ---- A3 standalone: y = x / sqrt(mean(x^2) + eps) * g (one workgroup) ----------
+__global__ __launch_bounds__(256) void k_rmsnorm(const float* x, const float* g, float eps, int d,
+                                                  float* y) {
+  __shared__ float red[4];
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < d; i += 256) ss += x[i] * x[i];
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x / 64] = ss;
+  __syncthreads();
+  const float r = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / float(d) + eps);
+  for (int i = threadIdx.x; i < d; i += 256) y[i] = x[i] * r * g[i];
+}
+
+// ---- A14 transport: plain copy ----------------------------------------------------
+__global__ void k_copy(const float* __restrict__ src, float* __restrict__ dst, long long n) {
+  const long long n4 = n / 4;
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n4;
+       i += (long long)gridDim.x * blockDim.x)
+    reinterpret_cast<f32x4*>(dst)[i] = reinterpret_cast<const f32x4*>(src)[i];
+  for (long long i = n4 * 4 + blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n;
+       i += (long long)gridDim.x * blockDim.x)
+    dst[i] = src[i];
+}
+
+// ---- A12: f32 -> f16 (RNE), f16 -> f32 (exact) ----------------------------------------
+__global__ void k_f32_to_f16(const float* src, uint16_t* dst, long long n) {
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n;
+       i += (long long)gridDim.x * blockDim.x) {
+    const _Float16 h = static_cast<_Float16>(src[i]);
+    dst[i] = __builtin_bit_cast(uint16_t, h);
+  }
+}
+__global__ void k_f16_to_f32(const uint16_t* src, float* dst, long long lo, long long hi) {
+  for (long long i = lo + blockIdx.x * (long long)blockDim.x + threadIdx.x; i < hi;
+       i += (long long)gridDim.x * blockDim.x)
+    dst[i] = static_cast<float>(__builtin_bit_cast(_Float16, src[i]));
+}
+// x = f32(x + ((shared + local) + bo)); bo may be the same buffer as local: every
+// element is read before it is written, by the same thread.
+__global__ void k_combine(float* x, const float* shared, const float* local, const float* bo,
+                          long long n) {
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n;
+       i += (long long)gridDim.x * blockDim.x) {
+    const float y = (shared[i] + local[i]) + bo[i];
+    x[i] = x[i] + y;
+  }
+}
+
+static dim3 grid_for(long long n, int threads = 256) {
+  long long b = (n + threads - 1) / threads;
+  if (b < 1) b = 1;
+  if (b > 4096) b = 4096;
+  return dim3(unsigned(b));
+}
+
+int launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t st) {
+  if (n == 0) return LPS_OK;
+  hipLaunchKernelGGL(k_copy, grid_for(n / 4 + 1), dim3(256), 0, st, src, dst, (long long)n);
+  LPS_HIP(hipGetLastError());
+  return LPS_OK;
+}
+
+}  // namespace lps
+
+using namespace lps;
+
+extern "C" int lps_embed(const void* table, int32_t wdtype, int32_t vocab, int32_t d,
+                         const int32_t* tok, float* x, void* stream) {
+  LPS_REQUIRE(table && tok && x, LPS_EINVAL, "lps_embed: null pointer");
+  LPS_REQUIRE(vocab > 0 && d > 0, LPS_EINVAL, "lps_embed: vocab %d / d %d must be > 0", vocab, d);
+  LPS_REQUIRE(wdtype == LPS_F32 || wdtype == LPS_BF16, LPS_EINVAL,
+              "lps_embed: table dtype %d (f32 or bf16 only)", wdtype);
+  const dim3 grid = grid_for(d);
+  if (wdtype == LPS_F32)
+    hipLaunchKernelGGL(k_embed<LPS_F32>, grid, dim3(256), 0, as_stream(stream), table, vocab, d, tok, x);
+  else
+    hipLaunchKernelGGL(k_embed<LPS_BF16>, grid, dim3(256), 0, as_stream(stream), table, vocab, d, tok, x);
+  LPS_HIP(hipGetLastError());
+  return LPS_OK;
+}
+
+extern "C" int lps_rmsnorm(const float* x, const float* g, float eps, int32_t d, float* y,
+                           void* stream) {
+  LPS_REQUIRE(x && g && y, LPS_EINVAL, "lps_rmsnorm: null pointer");
+  LPS_REQUIRE(d > 0, LPS_EINVAL, "lps_rmsnorm: d %d must be > 0", d);
+  hipLaunchKernelGGL(k_rmsnorm, dim3(1), dim3(256), 0, as_stream(stream), x, g, eps, d, y);
+  LPS_HIP(hipGetLastError());
+  return LPS_OK;
+}
+
+extern "C" int lps_copy_f32(const float* src, float* dst, int64_t n, void* stream) {
+  LPS_REQUIRE(n >= 0, LPS_EINVAL, "lps_copy_f32: n %lld < 0", (long long)n);
+  LPS_REQUIRE(n == 0 || (src && dst), LPS_EINVAL, "lps_copy_f32: null pointer");
+  LPS_REQUIRE(n == 0 || ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) == 0,
+              LPS_EINVAL, "lps_copy_f32: src and dst must be 16-byte aligned");
+  return launch_copy_f32(src, dst, n, as_stream(stream));
+}
+
+extern "C" int lps_f32_to_f16(const float* src, uint16_t* dst, int64_t n, void* stream) {
+  LPS_REQUIRE(n >= 0, LPS_EINVAL, "lps_f32_to_f16: n %lld < 0", (long long)n);
+  if (n == 0) return LPS_OK;
+  LPS_REQUIRE(src && dst, LPS_EINVAL, "lps_f32_to_f16: null pointer");
+  hipLaunchKernelGGL(k_f32_to_f16, grid_for(n), dim3(256), 0, as_stream(stream), src, dst, (long long)n);
+  LPS_HIP(hipGetLastError());
+  return LPS_OK;
+}
+
+// strata PR #3648, Approach (sums; the combine kernel; piece bounds): the FP16
+// sums are widened into bo one piece at a time on the remote stream, an event
+// after each piece; the main stream waits the last event and then combines.
+extern "C" int lps_moe_combine(float* x, const float* shared, const float* local,
+                               const uint16_t* remote16, float* bo, int32_t T, int32_t d,
+                               int32_t n_pieces, void* s_remote, void* s_main) {
+  LPS_REQUIRE(T >= 0 && d > 0, LPS_EINVAL, "lps_moe_combine: T %d / d %d", T, d);
+  LPS_REQUIRE(n_pieces >= 1 && n_pieces <= 64, LPS_EINVAL,
+              "lps_moe_combine: n_pieces %d outside [1, 64]", n_pieces);
+  if (T == 0) return LPS_OK;
+  LPS_REQUIRE(x && shared && local && remote16 && bo, LPS_EINVAL, "lps_moe_combine: null pointer");
+  hipStream_t sr = as_stream(s_remote), sm = as_stream(s_main);
+  hipEvent_t start, done;
+  LPS_HIP(hipEventCreateWithFlags(&start, hipEventDisableTiming));
+  LPS_HIP(hipEventCreateWithFlags(&done, hipEventDisableTiming));
+  // the remote stream may only overwrite bo once the main stream's earlier work
+  // (which may still read bo or local) is done
+  LPS_HIP(hipEventRecord(start, sm));
+  LPS_HIP(hipStreamWaitEvent(sr, start, 0));
+  int pieces = 0;
+  for (int pc = 0; pc < n_pieces; ++pc) {
+    const long long lo = (long long)pc * T / n_pieces, hi = (long long)(pc + 1) * T / n_pieces;
+    if (hi > lo) {
+      const long long a = lo * d, b = hi * d;
+      hipLaunchKernelGGL(k_f16_to_f32, grid_for(b - a), dim3(256), 0, sr, remote16, bo, a, b);
+      LPS_HIP(hipGetLastError());
+      ++pieces;
+    }
+  }
+  LPS_HIP(hipEventRecord(done, sr));
+  LPS_HIP(hipStreamWaitEvent(sm, done, 0));
+  const long long n = (long long)T * d;
+  hipLaunchKernelGGL(k_combine, grid_for(n), dim3(256), 0, sm, x, shared, local, bo, n);
+  LPS_HIP(hipGetLastError());
+  // events are released once they have fired (the runtime keeps them alive)
+  LPS_HIP(hipEventDestroy(start));
+  LPS_HIP(hipEventDestroy(done));
+  count_pieces(pieces);
+  return LPS_OK;
+}

@@ -1,0 +1,314 @@
+"""Decode driver over liblps: device buffers and streams from PyTorch, every
+step of the path in the library's kernels.
+
+memra-engine `pp` module docs (header): the trunk is cut into N stages with a
+stream each; N-1 boundary runtimes with two persistent slots and
+ev_tx / ev_rx events carry the [n_embd] f32 hidden; the embedding lives with
+stage 0, the final norm and LM head with the last stage; a step's logits stay
+on the device and drain through a dedicated readback stream while later
+steps keep being enqueued (struct PendingLogits).  ninfer "Multi-GPU: layer
+pipeline stages" (What it is and is not): repeating one device id runs the
+whole staged path on a single card, which is what this driver does: every
+stage is a stream on the same GPU.
+
+Nothing here computes: this module allocates, uploads, picks pointers and
+calls the C entry points in order.  There is no CPU fallback; without the
+built library or a GPU, construction fails.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import _lib as lps
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        raise RuntimeError("liblps needs a ROCm GPU (gfx950); none is visible")
+    lps.load()
+
+
+def to_dev(a: np.ndarray, device) -> torch.Tensor:
+    """Upload a numpy array unchanged (uint16 bf16 bits travel as int16)."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(device, non_blocking=False)
+
+
+def ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def sp(stream) -> int:
+    """hipStream_t of a torch stream, as an int for ctypes."""
+    return stream.cuda_stream
+
+
+def _weight(w, device):
+    if isinstance(w, tuple):  # MXFP4 (codes, scales)
+        return to_dev(w[0], device), to_dev(w[1], device)
+    return to_dev(w, device), None
+
+
+@dataclass
+class StepResult:
+    fed: list
+    argmax: list
+    logits: list
+
+
+class DeviceDecoder:
+    """A synth decoder model (dense f32/bf16 or MXFP4) resident on one GPU,
+    walked as N stages on N streams of that GPU."""
+
+    def __init__(self, model: dict, fence=None, device="cuda:0", ring: int = 4,
+                 streams: str = "per-stage"):
+        _need_gpu()
+        self.cfg = cfg = model["cfg"]
+        self.device = torch.device(device)
+        self.ring = ring
+        dev = self.device
+        wdt = lps.DTYPES[cfg.wdtype]
+        kvdt = lps.DTYPES[cfg.kvdtype]
+        self.layers = []
+        descs = (lps.LayerDesc * cfg.n_layers)()
+        kv_torch = torch.float32 if cfg.kvdtype == "f32" else torch.int16
+        for l, L in enumerate(model["layers"]):
+            t = {}
+            t["g_attn"] = to_dev(L["g_attn"], dev)
+            t["g_ffn"] = to_dev(L["g_ffn"], dev)
+            for n in ("w_qkv", "w_o", "w_gu", "w_d"):
+                t[n], t["s" + n[1:]] = _weight(L[n], dev)
+            t["k"] = torch.zeros((cfg.nkv, cfg.ctx_max, cfg.hd), dtype=kv_torch, device=dev)
+            t["v"] = torch.zeros_like(t["k"])
+            if cfg.prefix:
+                t["k_prefix"] = to_dev(L["k_prefix"], dev)
+                t["v_prefix"] = to_dev(L["v_prefix"], dev)
+            self.layers.append(t)
+            d = descs[l]
+            d.d, d.nq, d.nkv, d.hd, d.ff = cfg.d, cfg.nq, cfg.nkv, cfg.hd, cfg.ff
+            d.wdtype, d.kvdtype, d.ctx_max = wdt, kvdt, cfg.ctx_max
+            d.eps, d.rope_base = cfg.eps, cfg.rope_base
+            d.g_attn, d.g_ffn = ptr(t["g_attn"]), ptr(t["g_ffn"])
+            d.w_qkv, d.s_qkv = ptr(t["w_qkv"]), ptr(t["s_qkv"])
+            d.w_o, d.s_o = ptr(t["w_o"]), ptr(t["s_o"])
+            d.w_gu, d.s_gu = ptr(t["w_gu"]), ptr(t["s_gu"])
+            d.w_d, d.s_d = ptr(t["w_d"]), ptr(t["s_d"])
+            d.k_cache, d.v_cache = ptr(t["k"]), ptr(t["v"])
+        self.descs = descs
+        h = C.c_void_p()
+        lps.lps_model_create(descs, cfg.n_layers, C.byref(h))
+        self.model = h
+        self.scratch_bytes = lps.lps_model_scratch_bytes(h)
+        self.head = None
+        if cfg.vocab:
+            self.embed = to_dev(model["embed"], dev)
+            self.g_out = to_dev(model["g_out"], dev)
+            self.w_lm = to_dev(model["w_lm"], dev)
+            hd = lps.HeadDesc()
+            hd.d, hd.vocab, hd.wdtype, hd.eps = cfg.d, cfg.vocab, wdt, cfg.eps
+            hd.g_out, hd.w_lm = ptr(self.g_out), ptr(self.w_lm)
+            self.head = hd
+            self.head_scratch = torch.zeros(lps.lps_head_scratch_bytes(C.byref(hd)),
+                                            dtype=torch.uint8, device=dev)
+            self.logits_ring = torch.zeros((ring, cfg.vocab), dtype=torch.float32, device=dev)
+            self.tok_ring = torch.zeros(ring, dtype=torch.int32, device=dev)
+            self.host_logits = torch.zeros((ring, cfg.vocab), dtype=torch.float32).pin_memory()
+            self.host_tok = torch.zeros(ring, dtype=torch.int32).pin_memory()
+        self.readback = torch.cuda.Stream(device=dev)
+        self._streams_mode = streams
+        self.reset()
+        self.set_fence(fence)
+
+    # ---- stage plan / stage runtime ----------------------------------------------
+    def set_fence(self, fence=None):
+        cfg = self.cfg
+        if fence is None:
+            fence = lps.stage_plan(cfg.n_layers, 1)
+        fence = list(fence)
+        # validated by the library (raises on an invalid plan)
+        lps.stage_plan(cfg.n_layers, len(fence) - 1, fence[1:-1])
+        self.fence = fence
+        self.n_stages = n = len(fence) - 1
+        self._fence_c = lps.i32_array(fence)
+        dev = self.device
+        if self._streams_mode == "single":
+            s = torch.cuda.Stream(device=dev)
+            self.streams = [s] * n
+        else:
+            self.streams = [torch.cuda.Stream(device=dev) for _ in range(n)]
+        self.x = [torch.zeros(cfg.d, dtype=torch.float32, device=dev) for _ in range(n)]
+        self.scratch = [torch.zeros(self.scratch_bytes, dtype=torch.uint8, device=dev)
+                        for _ in range(n)]
+        self._close_boundaries()
+        self.slots, self.bounds = [], []
+        for _ in range(n - 1):
+            s0 = torch.full((cfg.d,), float("nan"), dtype=torch.float32, device=dev)
+            s1 = torch.full((cfg.d,), float("nan"), dtype=torch.float32, device=dev)
+            b = C.c_void_p()
+            lps.lps_boundary_create(cfg.d, ptr(s0), ptr(s1), C.byref(b))
+            self.slots.append((s0, s1))
+            self.bounds.append(b)
+        self.step_no = 0   # boundary step counter (monotone across runs)
+        torch.cuda.synchronize(dev)
+
+    def _close_boundaries(self):
+        for b in getattr(self, "bounds", []):
+            lps.lps_boundary_destroy(b)
+        self.bounds = []
+
+    def reset(self):
+        """Restore every cache to its seeded prefix (rows past it are rewritten
+        before they are read)."""
+        for t in self.layers:
+            if "k_prefix" in t:
+                P = t["k_prefix"].shape[1]
+                t["k"][:, :P].copy_(t["k_prefix"])
+                t["v"][:, :P].copy_(t["v_prefix"])
+        torch.cuda.synchronize(self.device)
+
+    def close(self):
+        torch.cuda.synchronize(self.device)
+        self._close_boundaries()
+        if getattr(self, "model", None):
+            lps.lps_model_destroy(self.model)
+            self.model = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # ---- one step ------------------------------------------------------------------
+    def _walk(self, pos):
+        """Enqueue all stages of one step; stage 0's input is already in x[0]."""
+        n, st = self.n_stages, self.streams
+        t = self.step_no
+        for s in range(n):
+            if s > 0:
+                lps.lps_boundary_send(self.bounds[s - 1], ptr(self.x[s - 1]), t, sp(st[s - 1]))
+                lps.lps_boundary_recv(self.bounds[s - 1], ptr(self.x[s]), t, sp(st[s]))
+            lps.lps_stage_forward(self.model, self._fence_c, n, s, ptr(self.x[s]), pos,
+                                  ptr(self.scratch[s]), self.scratch_bytes, sp(st[s]))
+        self.step_no += 1
+
+    def run_tokens(self, prompt, n_steps=0, feed=None, p0=None) -> StepResult:
+        """Feed the prompt ids one per step from position p0 (default: right after
+        the cache prefix), then n_steps greedy steps whose token is the device
+        argmax of the step before (it never visits the host).  feed: a full id
+        list to feed instead (teacher forcing).  Logits drain through the
+        readback ring; the host runs up to `ring` steps ahead of the GPU."""
+        cfg = self.cfg
+        assert self.head is not None, "model has no vocabulary"
+        p = cfg.prefix if p0 is None else p0
+        ids = list(prompt) if feed is None else list(feed)
+        P = len(ids)
+        total = P + (0 if feed is not None else n_steps)
+        assert p + total <= cfg.ctx_max, "cache too short for this run"
+        dev = self.device
+        feed_dev = torch.tensor(ids + [0], dtype=torch.int32, device=dev)
+        torch.cuda.synchronize(dev)
+        st0, stl = self.streams[0], self.streams[-1]
+        done = [torch.cuda.Event() for _ in range(self.ring)]
+        pend = [None] * self.ring
+        out_logits, out_tok = [None] * total, [None] * total
+        R = self.ring
+
+        def drain(i):
+            lps.lps_pending_wait(pend[i % R])
+            pend[i % R] = None
+            out_logits[i] = self.host_logits[i % R].numpy().copy()
+            out_tok[i] = int(self.host_tok[i % R])
+
+        for i in range(total):
+            if i >= R:
+                drain(i - R)
+            if i < P:
+                tok_ptr = ptr(feed_dev) + 4 * i
+            else:
+                tok_ptr = ptr(self.tok_ring) + 4 * ((i - 1) % R)
+                if stl is not st0:
+                    st0.wait_event(done[(i - 1) % R])
+            lps.lps_embed(ptr(self.embed), lps.DTYPES[cfg.wdtype], cfg.vocab, cfg.d, tok_ptr,
+                          ptr(self.x[0]), sp(st0))
+            self._walk(p + i)
+            k = i % R
+            lps.lps_head_forward(C.byref(self.head), ptr(self.x[-1]), ptr(self.logits_ring[k]),
+                                 ptr(self.tok_ring) + 4 * k, ptr(self.head_scratch),
+                                 self.head_scratch.numel(), sp(stl))
+            done[k].record(stl)
+            h = C.c_void_p()
+            lps.lps_logits_defer(ptr(self.logits_ring[k]), ptr(self.tok_ring) + 4 * k, cfg.vocab,
+                                 sp(stl), sp(self.readback), ptr(self.host_logits[k]),
+                                 ptr(self.host_tok) + 4 * k, C.byref(h))
+            pend[k] = h
+        for i in range(max(0, total - R), total):
+            drain(i)
+        fed = ids[:P] + [out_tok[i - 1] for i in range(P, total)]
+        return StepResult(fed=fed, argmax=out_tok, logits=out_logits)
+
+    def run_hidden(self, xs: np.ndarray, p0=None) -> np.ndarray:
+        """Models without a vocabulary: step t feeds the f32 row xs[t] at position
+        p0 + t and returns the last stage's hidden rows [steps, d]."""
+        cfg = self.cfg
+        p = cfg.prefix if p0 is None else p0
+        T = xs.shape[0]
+        assert p + T <= cfg.ctx_max
+        dev = self.device
+        xin = to_dev(np.ascontiguousarray(xs, dtype=np.float32), dev)
+        out = torch.zeros((T, cfg.d), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize(dev)
+        st0, stl = self.streams[0], self.streams[-1]
+        for t in range(T):
+            lps.lps_copy_f32(ptr(xin) + 4 * cfg.d * t, ptr(self.x[0]), cfg.d, sp(st0))
+            self._walk(p + t)
+            lps.lps_copy_f32(ptr(self.x[-1]), ptr(out) + 4 * cfg.d * t, cfg.d, sp(stl))
+        torch.cuda.synchronize(dev)
+        return out.cpu().numpy()
+
+
+class DeviceMoEStack:
+    """A synth MoE FFN stack resident on one GPU (decode: one token per step)."""
+
+    def __init__(self, model: dict, device="cuda:0"):
+        _need_gpu()
+        self.cfg = cfg = model["cfg"]
+        self.device = dev = torch.device(device)
+        self.layers, self.descs = [], []
+        for L in model["layers"]:
+            t = {k: to_dev(L[k], dev) for k in ("g_ffn", "w_r", "w_gu_e", "w_d_e", "w_gu_s", "w_d_s")}
+            d = lps.MoEDesc()
+            d.d, d.n_experts, d.top_k, d.ff = cfg.d, cfg.n_experts, cfg.top_k, cfg.ff
+            d.remote_from, d.eps = cfg.remote_from, cfg.eps
+            d.g_ffn, d.w_r = ptr(t["g_ffn"]), ptr(t["w_r"])
+            d.w_gu_e, d.w_d_e = ptr(t["w_gu_e"]), ptr(t["w_d_e"])
+            d.w_gu_s, d.w_d_s = ptr(t["w_gu_s"]), ptr(t["w_d_s"])
+            self.layers.append(t)
+            self.descs.append(d)
+        self.scratch_bytes = lps.lps_moe_layer_scratch_bytes(C.byref(self.descs[0]))
+        self.scratch = torch.zeros(self.scratch_bytes, dtype=torch.uint8, device=dev)
+        self.x = torch.zeros(cfg.d, dtype=torch.float32, device=dev)
+        self.stream = torch.cuda.Stream(device=dev)
+
+    def decode_step(self, x_ptr_in: int, out_ptr: int):
+        cfg, st = self.cfg, sp(self.stream)
+        lps.lps_copy_f32(x_ptr_in, ptr(self.x), cfg.d, st)
+        for d in self.descs:
+            lps.lps_moe_layer_decode(C.byref(d), ptr(self.x), ptr(self.scratch), self.scratch_bytes, st)
+        lps.lps_copy_f32(ptr(self.x), out_ptr, cfg.d, st)
+
+    def decode(self, xs: np.ndarray) -> np.ndarray:
+        cfg, dev = self.cfg, self.device
+        xin = to_dev(np.ascontiguousarray(xs, dtype=np.float32), dev)
+        out = torch.zeros_like(xin)
+        torch.cuda.synchronize(dev)
+        for t in range(xs.shape[0]):
+            self.decode_step(ptr(xin) + 4 * cfg.d * t, ptr(out) + 4 * cfg.d * t)
+        torch.cuda.synchronize(dev)
+        return out.cpu().numpy()

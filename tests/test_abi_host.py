@@ -1,0 +1,110 @@
+"""The C-ABI library loads on a machine without a GPU, exports every symbol
+include/lps.h declares, and its host-only logic (stage plan, validation that
+runs before anything is enqueued) behaves as specified."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from oracle.plan import stage_plan as oracle_plan
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from layer_pipeline_stage_amd import lps
+    lps.load()
+    return lps
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "lps.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"\b(lps_[a-z0-9_]+)\s*\(", src)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) >= 35
+    lib = C.CDLL(L.LIB_PATH)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    # and the binding wraps exactly the declared set
+    assert set(L.SIGS) == set(names)
+
+
+def test_stage_plan_matches_oracle_everywhere(L):
+    import itertools
+    for nl in range(1, 9):
+        for n in range(1, nl + 1):
+            assert L.stage_plan(nl, n) == oracle_plan(nl, n)
+        for r in range(nl):
+            for cuts in itertools.combinations(range(1, nl), r):
+                f = L.stage_plan(nl, r + 1, list(cuts))
+                assert f == oracle_plan(nl, r + 1, list(cuts))
+                assert [L.stage_of(f, l) for l in range(nl)] == \
+                    [sum(c <= l for c in cuts) for l in range(nl)]
+
+
+@pytest.mark.parametrize("nl,n,cuts", [
+    (4, 0, None), (4, 5, None), (0, 1, None), (4, 2, [0]), (4, 2, [4]), (4, 3, [2, 2]),
+    (4, 3, [3, 1]), (4, 3, [1]), (4, 2, [1, 2]), (4, 2, [-1]),
+])
+def test_invalid_plans_refused_with_text(L, nl, n, cuts):
+    with pytest.raises(L.LpsError) as e:
+        L.stage_plan(nl, n, cuts)
+    assert e.value.code == L.LPS_EINVAL
+    assert "lps_stage_plan" in str(e.value)
+
+
+def test_counts_and_stage_of_errors(L):
+    assert L.stage_plan_counts(64, [30, 34]) == [0, 30, 64]
+    for counts in ([0, 4], [2, 3], [5, -1]):
+        with pytest.raises(L.LpsError):
+            L.stage_plan_counts(4, counts)
+    with pytest.raises(L.LpsError) as e:
+        L.stage_of([0, 2, 4], 4)
+    assert e.value.code == L.LPS_ERANGE
+    with pytest.raises(L.LpsError):
+        L.stage_of([0, 2, 2], 1)
+
+
+def test_validation_before_enqueue(L):
+    """Bad descriptors and arguments are refused before any HIP call, so the
+    refusals are observable without a GPU."""
+    d = L.LayerDesc()
+    d.d, d.nq, d.nkv, d.hd, d.ff = 256, 4, 3, 64, 704          # nq % nkv != 0
+    d.wdtype, d.kvdtype, d.ctx_max = 0, 0, 16
+    with pytest.raises(L.LpsError) as e:
+        L.lps_layer_forward(C.byref(d), 16, 0, 16, 1 << 20, None)
+    assert e.value.code == L.LPS_EUNSUP and "lps_layer_forward" in str(e.value)
+    d.nkv, d.hd = 2, 96                                         # head dim not built
+    with pytest.raises(L.LpsError) as e:
+        L.lps_layer_forward(C.byref(d), 16, 0, 16, 1 << 20, None)
+    assert e.value.code == L.LPS_EUNSUP
+    d.hd = 64
+    with pytest.raises(L.LpsError) as e:                        # null weights
+        L.lps_layer_forward(C.byref(d), 16, 0, 16, 1 << 20, None)
+    assert e.value.code == L.LPS_EINVAL
+    assert L.lps_layer_scratch_bytes(C.byref(d)) == 0           # invalid desc -> 0
+    with pytest.raises(L.LpsError):
+        L.lps_gemv(2, 16, 16, 8, 100, 16, None, 0.0, 16, 0, None)   # K % 32 for MXFP4
+    with pytest.raises(L.LpsError):
+        L.lps_gemv(1, 16, None, 7, 64, 16, None, 0.0, 16, 2, None)  # SwiGLU needs even N
+    with pytest.raises(L.LpsError):
+        L.lps_attention_decode(4, 2, 64, 0, 16, 16, 8, 9, 16, 16, 16, 1 << 20, None)  # n_rows > ctx
+    with pytest.raises(L.LpsError):
+        L.lps_moe_combine(16, 16, 16, 16, 16, 4, 64, 0, None, None)    # 0 pieces
+    assert L.lps_attention_scratch_bytes(32, 8, 128, 4224) > 0
+    assert L.lps_attention_scratch_bytes(3, 2, 128, 10) == 0
+
+
+def test_error_text_is_thread_local_and_cleared(L):
+    with pytest.raises(L.LpsError):
+        L.stage_plan(4, 9)
+    assert "n_stages" in L.last_error()
+    L.stage_plan(4, 2)
+    assert L.last_error() == ""

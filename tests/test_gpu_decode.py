@@ -1,0 +1,144 @@
+"""Staged decode on the GPU: bit identity of staged vs unstaged runs (every N and
+cut set of the tiny model), the deferred readback ring, liveness counters,
+and teacher-forced logits against the float64 oracle."""
+import itertools
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle.decoder import Decoder
+from oracle.plan import stage_plan
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def rt():
+    from layer_pipeline_stage_amd import runtime, lps
+    lps.load()
+    assert torch.cuda.is_available(), "GPU tests need a visible ROCm GPU"
+    return runtime
+
+
+def _cut_sets(L):
+    for r in range(L):
+        for cuts in itertools.combinations(range(1, L), r):
+            yield list(cuts)
+
+
+def _check_against_oracle(model, res, tol_rel):
+    """Teacher forcing: the oracle is fed the GPU's token sequence; logits per
+    step within tol_rel * max|oracle logits|; the GPU's argmax must be the
+    oracle's, unless the oracle's top two logits are closer than the tolerance
+    (a certified near tie, counted)."""
+    dec = Decoder(model)
+    _, am, lg = dec.greedy([], 0, feed=res.fed)
+    near = 0
+    for i, (a, b) in enumerate(zip(res.logits, lg)):
+        tol = tol_rel * np.abs(b).max()
+        assert np.max(np.abs(a - b)) <= tol, (i, np.max(np.abs(a - b)), tol)
+        if res.argmax[i] != am[i]:
+            top2 = np.sort(b)[-2:]
+            assert top2[1] - top2[0] <= 2 * tol and b[res.argmax[i]] >= top2[1] - 2 * tol
+            near += 1
+    return near
+
+
+def test_tiny_unstaged_matches_oracle(rt):
+    cfg = synth.TINY
+    m = synth.make_tiny(cfg)
+    dd = rt.DeviceDecoder(m)
+    res = dd.run_tokens(m["prompt"], cfg.steps)
+    assert len(res.logits) == cfg.prompt + cfg.steps
+    assert _check_against_oracle(m, res, 1e-5) == 0
+    dd.close()
+
+
+def test_tiny_staged_equals_unstaged_every_cut_set(rt):
+    """memra pp docs (header; PendingLogits) and ninfer Verification: staged
+    output bit-identical to one stage, for all 8 cut sets of the 4-layer model,
+    with the liveness counters proving the staged walk and the slots ran."""
+    from layer_pipeline_stage_amd import lps
+    cfg = synth.TINY
+    m = synth.make_tiny(cfg)
+    dd = rt.DeviceDecoder(m)
+    ref = dd.run_tokens(m["prompt"], cfg.steps)
+    steps = cfg.prompt + cfg.steps
+    for cuts in _cut_sets(cfg.n_layers):
+        n = len(cuts) + 1
+        dd.set_fence(stage_plan(cfg.n_layers, n, cuts))
+        dd.reset()
+        lps.lps_counters_reset()
+        got = dd.run_tokens(m["prompt"], cfg.steps)
+        c = lps.counters()
+        assert c["stage_walks"] == n * steps
+        assert c["boundary_sends"] == c["boundary_recvs"] == (n - 1) * steps
+        assert c["drains"] == steps
+        assert got.fed == ref.fed and got.argmax == ref.argmax
+        assert all(np.array_equal(a, b) for a, b in zip(got.logits, ref.logits)), cuts
+    dd.close()
+
+
+def test_tiny_n4_deferred_per_step_identity_and_soak(rt):
+    """Same model at context 32 -> 96: N = 4 (cuts 1, 2, 3) on one device, the
+    deferred readback ring letting the host run ahead, 64 greedy steps;
+    per-step bit identity against N = 1, repeated 20 times (memra's one-device
+    pipelined arm failed 7 of 20 such soaks from a race; here the stages share
+    no mutable state beyond the event-ordered slots)."""
+    cfg = synth.TINY_N4
+    m = synth.make_tiny(cfg)
+    dd = rt.DeviceDecoder(m)
+    ref = dd.run_tokens(m["prompt"], cfg.steps)
+    assert len(ref.logits) == 96
+    assert _check_against_oracle(m, ref, 1e-5) == 0
+    dd.set_fence(stage_plan(4, 4, [1, 2, 3]))
+    for run in range(20):
+        dd.reset()
+        got = dd.run_tokens(m["prompt"], cfg.steps)
+        assert got.argmax == ref.argmax, run
+        for i, (a, b) in enumerate(zip(got.logits, ref.logits)):
+            assert np.array_equal(a, b), (run, i)
+    dd.close()
+
+
+def test_single_stream_seam_equals_per_stage_streams(rt):
+    """The same-stream seam (every stage on one stream, the boundary as plain
+    copies) gives the same bits as one stream per stage."""
+    cfg = replace(synth.TINY, prompt=5, steps=6)
+    m = synth.make_tiny(cfg)
+    a = rt.DeviceDecoder(m, fence=[0, 1, 3, 4])
+    b = rt.DeviceDecoder(m, fence=[0, 1, 3, 4], streams="single")
+    ra = a.run_tokens(m["prompt"], cfg.steps)
+    rb = b.run_tokens(m["prompt"], cfg.steps)
+    assert ra.argmax == rb.argmax
+    assert all(np.array_equal(x, y) for x, y in zip(ra.logits, rb.logits))
+    a.close()
+    b.close()
+
+
+def test_invalid_fence_refused(rt):
+    from layer_pipeline_stage_amd import lps
+    m = synth.make_tiny(replace(synth.TINY, prompt=2, steps=1))
+    dd = rt.DeviceDecoder(m)
+    for bad in ([0, 2, 2, 4], [0, 5], [1, 2, 4], [0, 3, 2, 4]):
+        with pytest.raises(lps.LpsError):
+            dd.set_fence(bad)
+    dd.close()
+
+
+def test_moe_decode_small_matches_oracle(rt):
+    from oracle.moe import MoEStack
+    cfg = synth.MoEConfig("moe-gpu-small", n_layers=2, d=512, n_experts=16, top_k=4, ff=128,
+                          remote_from=8, prefill_T=0, steps=6)
+    m = synth.make_moe(cfg)
+    st = rt.DeviceMoEStack(m)
+    got = st.decode(m["x_in"])
+    ref_st = MoEStack(m)
+    for t in range(cfg.steps):
+        traces = []
+        ref = ref_st.forward(m["x_in"][t], traces=traces)
+        tol = 2e-3 * np.abs(ref).max()
+        assert np.max(np.abs(got[t] - ref)) <= tol
