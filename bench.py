@@ -1,0 +1,208 @@
+"""Decode throughput of the staged path on one MI355X.
+
+Workload: the dense 8B-class slice (bf16 weights ~N(0, 0.02), f32 hidden;
+8 layers, n_embd 4096, 32 q / 8 kv heads of 128, SwiGLU 14336, vocab 32000),
+batch-1 greedy decode with a seeded 4096-row random bf16 KV prefix per layer,
+split into N = 4 stages (even split) on one GPU, deferred logits readback.
+A step is one token through all four stages and the LM head (+ argmax on the
+device, which feeds the next step's embedding).
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu]
+
+Prints one JSON line: decode tokens/s, the algorithmic HBM bytes per token
+turned into GB/s and a fraction of MI355X's 8 TB/s, the dominant kernel's
+roofline (timed with HIP events on its own stream during a measured pass),
+and the float64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+from dataclasses import replace
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, vendor figure
+METRIC = "decode tokens/s + achieved HBM GB/s (% of MI355X peak), 1 GPU"
+
+
+def algorithmic_bytes(cfg, n_rows: int) -> dict:
+    """Bytes one decode step must move at context n_rows (rows visible after
+    the append): every weight once, every visible K/V row once, the appended
+    rows, the embedding row and the logits."""
+    d, hd, ff = cfg.d, cfg.hd, cfg.ff
+    wb = 2  # bf16
+    per_layer_w = ((cfg.nq + 2 * cfg.nkv) * hd * d + d * cfg.nq * hd + 2 * ff * d + d * ff) * wb
+    norms = 2 * d * 4
+    kv_read = 2 * cfg.nkv * n_rows * hd * 2
+    kv_write = 2 * cfg.nkv * hd * 2
+    head = cfg.vocab * d * wb + d * 4
+    return {
+        "weights": cfg.n_layers * (per_layer_w + norms) + head,
+        "kv": cfg.n_layers * (kv_read + kv_write),
+        "io": d * wb + cfg.vocab * 4,
+    }
+
+
+def gateup_bytes(cfg) -> int:
+    """The fused RMSNorm + gate/up GEMV + SwiGLU kernel: its weights once, x and
+    the norm gain in, the SwiGLU output out."""
+    return 2 * cfg.ff * cfg.d * 2 + 2 * cfg.d * 4 + cfg.ff * 4
+
+
+KERNEL_BYTES = {
+    "qkv": lambda c, n: (c.nq + 2 * c.nkv) * c.hd * c.d * 2 + 2 * c.d * 4 + c.nq * c.hd * 4
+    + 2 * c.nkv * c.hd * 2,
+    "attn": lambda c, n: 2 * c.nkv * n * c.hd * 2 + 2 * c.nq * c.hd * 4,
+    "oproj": lambda c, n: c.d * c.nq * c.hd * 2 + c.nq * c.hd * 4 + 2 * c.d * 4,
+    "gateup": lambda c, n: gateup_bytes(c),
+    "down": lambda c, n: c.d * c.ff * 2 + c.ff * 4 + 2 * c.d * 4,
+    "head": lambda c, n: c.vocab * c.d * 2 + 2 * c.d * 4 + c.vocab * 4,
+}
+
+
+def cpu_baseline(model, first_token, n_steps=2):
+    """The float64 oracle as it is, on this host, on the first n_steps of the
+    same greedy run (teacher-forced to the GPU's tokens is not needed: the
+    oracle's own greedy steps are the same work)."""
+    import threadpoolctl  # noqa: F401  (present in the image; reports BLAS threads)
+    from threadpoolctl import threadpool_info
+
+    from oracle.decoder import Decoder
+    cores = len(os.sched_getaffinity(0))
+    dec = Decoder(model, weight_cache=False)
+    t0 = time.perf_counter()
+    dec.greedy([first_token], n_steps - 1)
+    dt = time.perf_counter() - t0
+    blas = [i.get("num_threads") for i in threadpool_info() if i.get("user_api") == "blas"]
+    return {
+        "value": round(n_steps / dt, 4), "unit": "tok/s", "cores": int(blas[0]) if blas else cores,
+        "kind": "oracle",
+        "sample": f"{n_steps} greedy decode steps of the same workload at context 4096 "
+                  f"(numpy float64, BLAS threads {blas[0] if blas else '?'} of {cores} host cores, "
+                  f"{dt:.1f} s)",
+        "cpu": platform.processor() or _cpu_model(),
+    }
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--stages", type=int, default=4)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-steps", type=int, default=2)
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py: this path runs on one GPU (stages are streams of that GPU); "
+              f"--gpus {a.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import synth
+    from layer_pipeline_stage_amd import lps, runtime
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    K, W = a.steps, a.warmup
+    cfg = replace(synth.DENSE8B, steps=max(K, W, 128) - 1)
+    t0 = time.perf_counter()
+    model = synth.make_dense(cfg)
+    t_gen = time.perf_counter() - t0
+    fence = lps.stage_plan(cfg.n_layers, a.stages)
+    dd = runtime.DeviceDecoder(model, fence=fence)
+    start_tok = [int(model["prompt"][0])]
+
+    # warmup
+    dd.reset()
+    dd.run_tokens(start_tok, W - 1)
+    # timed region: K steps (the start token + K-1 greedy steps), all on the device
+    dd.reset()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    res = dd.run_tokens(start_tok, K - 1)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    tok_s = K / dt
+    rows = [cfg.prefix + 1 + i for i in range(K)]
+    b = [algorithmic_bytes(cfg, n) for n in rows]
+    bytes_tok = sum(x["weights"] + x["kv"] + x["io"] for x in b) / K
+    gbs = bytes_tok * tok_s / 1e9
+
+    # per-kernel durations, HIP events on each kernel's own stream, one pass each
+    kernels = {}
+    for name, kind in lps.KINDS.items():
+        dd.reset()
+        lps.lps_timer_start(kind, 8 * K + 8)
+        dd.run_tokens(start_tok, K - 1)
+        ms = lps.timer_stop()
+        per = KERNEL_BYTES[name]
+        launches_per_step = 1 if name == "head" else cfg.n_layers
+        n_rows = np.repeat(rows, launches_per_step)[:len(ms)]
+        byts = np.array([per(cfg, n) for n in n_rows], dtype=np.float64)
+        avg_us = 1e3 * float(np.mean(ms))
+        kernels[name] = {"launches": len(ms), "avg_us": round(avg_us, 2),
+                         "gbs": round(float(np.sum(byts) / (np.sum(ms) * 1e-3) / 1e9), 1)}
+    gk = kernels["gateup"]
+    achieved = gateup_bytes(cfg) / (gk["avg_us"] * 1e-6) / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": round(tok_s, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(1e3 * dt / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) bf16 weights, N(0,1) bf16 KV prefix, device greedy tokens)",
+        "config": {
+            "workload": "dense 8B-class slice decode: 8 layers, n_embd 4096, 32q/8kv x 128, "
+                        "SwiGLU 14336, vocab 32000, bf16 weights, f32 hidden, KV context 4096 + "
+                        f"{K} steps, batch 1, {a.stages} stages (even split) on one GPU, "
+                        "deferred logits readback",
+            "global_batch": 1, "seq_len": cfg.prefix + K, "stages": fence,
+        },
+        "hbm_bytes_per_token": int(bytes_tok),
+        "hbm_gbs": round(gbs, 1),
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "roofline": {
+            "bound": "hbm", "kernel": "rmsnorm+gate_up GEMV+SwiGLU (bf16 [28672, 4096])",
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "avg_us": gk["avg_us"], "bytes_per_launch": gateup_bytes(cfg),
+        },
+        "kernels": kernels,
+        "first_tokens": res.fed[:8],
+        "gen_s": round(t_gen, 1),
+    }
+    dd.close()
+    if not a.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(model, start_tok[0], a.cpu_steps)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -251,14 +251,17 @@ typedef struct lps_moe_desc {
 size_t lps_moe_route_scratch_bytes(const lps_moe_desc* m, int32_t T);
 int lps_moe_route(const lps_moe_desc* m, const float* x, int32_t T, int32_t* idx, float* w,
                   void* scratch, size_t scratch_bytes, void* stream);
-/* A12: x (dev [T, d]) = f32(x + ((shared + local) + bo)) where bo (dev [T, d] f32)
- * receives f32(remote16), converted piece by piece on `s_remote`: piece p covers
- * rows [floor(pT/P), floor((p+1)T/P)); each piece's conversion is followed by an
- * event, and `s_main` waits the last one before the combine.  remote16 (dev
- * [T, d]) holds f16 bit patterns.  bo may be the same buffer as local. */
-int lps_moe_combine(float* x, const float* shared, const float* local, const uint16_t* remote16,
-                    float* bo, int32_t T, int32_t d, int32_t n_pieces, void* s_remote,
-                    void* s_main);
+/* A12: out (dev [T, d]) = f32(x + ((shared + local) + bo)) where bo (dev [T, d]
+ * f32) first receives f32(remote16), converted piece by piece on `s_remote`:
+ * piece p covers rows [floor(pT/P), floor((p+1)T/P)); `s_remote` first waits
+ * for the work already enqueued on `s_main`, and `s_main` waits an event
+ * recorded after the last piece before it combines.  remote16 (dev [T, d])
+ * holds f16 bit patterns.  out may be the same buffer as bo or as x (each
+ * element is read before it is written, by the same thread); bo must not
+ * overlap shared, local or remote16.  Bumps the pieces counter. */
+int lps_moe_combine(float* out, const float* x, const float* shared, const float* local,
+                    const uint16_t* remote16, float* bo, int32_t T, int32_t d, int32_t n_pieces,
+                    void* s_remote, void* s_main);
 /* f32 -> f16 bits (round to nearest even) of n values: the remote half's
  * "sums_to_f16" step (strata PR #3648, Approach: sums). */
 int lps_f32_to_f16(const float* src, uint16_t* dst, int64_t n, void* stream);
@@ -280,6 +283,25 @@ typedef struct lps_counters_t {
 } lps_counters_t;
 int lps_counters(lps_counters_t* out);
 int lps_counters_reset(void);
+
+/* ---- kernel timing (benchmarks) -------------------------------------------
+ * While a timer runs, every launch of the chosen kind made by lps_layer_forward,
+ * lps_stage_forward or lps_head_forward is bracketed by a pair of hipEvents
+ * recorded on the launching stream (so the durations are those of that kernel
+ * on that stream).  capacity bounds the pairs recorded (later launches are not
+ * timed).  One timer at a time per process. */
+enum {
+  LPS_KIND_QKV = 1,     /* RMSNorm + QKV GEMV + RoPE + KV append */
+  LPS_KIND_ATTN = 2,    /* decode attention incl. the chunk merge */
+  LPS_KIND_OPROJ = 3,   /* O projection + residual */
+  LPS_KIND_GATEUP = 4,  /* RMSNorm + gate/up GEMV + SwiGLU */
+  LPS_KIND_DOWN = 5,    /* down projection + residual */
+  LPS_KIND_HEAD = 6     /* final RMSNorm + LM head + argmax */
+};
+int lps_timer_start(int32_t kind, int32_t capacity);
+/* Synchronizes the recorded events, writes up to cap durations (milliseconds)
+ * to ms_out (host) and their count to *n_out, and stops the timer. */
+int lps_timer_stop(float* ms_out, int32_t cap, int32_t* n_out);
 
 #ifdef __cplusplus
 }

@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(_HERE, "liblps.so")
 LPS_OK, LPS_EINVAL, LPS_ERANGE, LPS_ESTATE, LPS_EHIP, LPS_ENOMEM, LPS_EUNSUP = 0, -1, -2, -3, -4, -5, -6
 LPS_F32, LPS_BF16, LPS_MXFP4 = 0, 1, 2
 LPS_EPI_STORE, LPS_EPI_ADD, LPS_EPI_SWIGLU = 0, 1, 2
+KINDS = {"qkv": 1, "attn": 2, "oproj": 3, "gateup": 4, "down": 5, "head": 6}
 DTYPES = {"f32": LPS_F32, "bf16": LPS_BF16, "mxfp4": LPS_MXFP4}
 
 
@@ -93,11 +94,13 @@ SIGS = {
     "lps_pending_drop": (C.c_int, [P], True),
     "lps_moe_route_scratch_bytes": (SZ, [C.POINTER(MoEDesc), I32], False),
     "lps_moe_route": (C.c_int, [C.POINTER(MoEDesc), P, I32, P, P, P, SZ, P], True),
-    "lps_moe_combine": (C.c_int, [P, P, P, P, P, I32, I32, I32, P, P], True),
+    "lps_moe_combine": (C.c_int, [P, P, P, P, P, P, I32, I32, I32, P, P], True),
     "lps_f32_to_f16": (C.c_int, [P, P, I64, P], True),
     "lps_moe_layer_scratch_bytes": (SZ, [C.POINTER(MoEDesc)], False),
     "lps_moe_layer_decode": (C.c_int, [C.POINTER(MoEDesc), P, P, SZ, P], True),
     "lps_counters": (C.c_int, [C.POINTER(Counters)], True),
+    "lps_timer_start": (C.c_int, [I32, I32], True),
+    "lps_timer_stop": (C.c_int, [C.POINTER(C.c_float), I32, PI32], True),
     "lps_counters_reset": (C.c_int, [], True),
 }
 
@@ -162,6 +165,13 @@ def stage_plan_counts(n_layers, counts):
 
 def stage_of(fence, layer):
     return lps_stage_of(i32_array(fence), len(fence) - 1, layer)  # noqa: F821
+
+
+def timer_stop(cap=1 << 16):
+    buf = (C.c_float * cap)()
+    n = C.c_int32()
+    lps_timer_stop(buf, cap, C.byref(n))  # noqa: F821
+    return [buf[i] for i in range(n.value)]
 
 
 def counters() -> dict:

@@ -236,10 +236,7 @@ __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(GemvP p) {
 // ---- launch configuration ---------------------------------------------------
 static int max_blocks() { return 256 * 8; }
 
-// The activation vector can exceed 64 KiB (K up to 40960 f32 in 160 KiB of LDS).
-static bool allow_big_lds(const void* fn) {
-  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess;
-}
+
 
 template <int WT, int EPI, bool NORM>
 static int launch_t(const GemvP& p, hipStream_t st) {
@@ -253,12 +250,12 @@ static int launch_t(const GemvP& p, hipStream_t st) {
   const int per_lane = (p.K / CH + WAVE - 1) / WAVE;
   // keep up to 8 chunk loads per row in flight per lane
   if (per_lane <= 4) {
-    static bool attr = allow_big_lds((const void*)k_gemv<WT, EPI, 4, NORM>);
-    (void)attr;
+    int rc = ensure_lds((const void*)k_gemv<WT, EPI, 4, NORM>, lds);
+    if (rc) return rc;
     hipLaunchKernelGGL((k_gemv<WT, EPI, 4, NORM>), dim3(grid), dim3(GEMV_THREADS), lds, st, p);
   } else {
-    static bool attr = allow_big_lds((const void*)k_gemv<WT, EPI, 8, NORM>);
-    (void)attr;
+    int rc = ensure_lds((const void*)k_gemv<WT, EPI, 8, NORM>, lds);
+    if (rc) return rc;
     hipLaunchKernelGGL((k_gemv<WT, EPI, 8, NORM>), dim3(grid), dim3(GEMV_THREADS), lds, st, p);
   }
   LPS_HIP(hipGetLastError());

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <mutex>
 #include <cstdarg>
 #include <cstdlib>
 #include <cstring>
@@ -30,6 +31,50 @@ void count_send() { c_sends.fetch_add(1, std::memory_order_relaxed); }
 void count_recv() { c_recvs.fetch_add(1, std::memory_order_relaxed); }
 void count_pieces(int64_t n) { c_pieces.fetch_add(n, std::memory_order_relaxed); }
 void count_drain() { c_drains.fetch_add(1, std::memory_order_relaxed); }
+
+int ensure_lds(const void* fn, size_t bytes) {
+  if (bytes <= 65536) return LPS_OK;
+  static std::mutex mu;
+  static std::vector<std::pair<const void*, size_t>> done;
+  std::lock_guard<std::mutex> lk(mu);
+  for (auto& e : done)
+    if (e.first == fn && e.second >= bytes) return LPS_OK;
+  hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
+  if (err != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(LPS_EUNSUP, "ensure_lds: %zu bytes of LDS refused: %s", bytes, hipGetErrorString(err));
+  }
+  done.emplace_back(fn, bytes);
+  return LPS_OK;
+}
+
+// ---- benchmark timer ---------------------------------------------------------------
+struct Timer {
+  std::mutex mu;
+  std::atomic<int> kind{0};
+  std::vector<hipEvent_t> ev;   // 2 per launch
+  int used = 0;
+  bool open = false;
+};
+static Timer g_timer;
+
+void timer_begin(int kind, hipStream_t st) {
+  if (g_timer.kind.load(std::memory_order_relaxed) != kind) return;
+  std::lock_guard<std::mutex> lk(g_timer.mu);
+  if (!g_timer.open && g_timer.used * 2 < int(g_timer.ev.size())) {
+    (void)hipEventRecord(g_timer.ev[2 * g_timer.used], st);
+    g_timer.open = true;
+  }
+}
+void timer_end(int kind, hipStream_t st) {
+  if (g_timer.kind.load(std::memory_order_relaxed) != kind) return;
+  std::lock_guard<std::mutex> lk(g_timer.mu);
+  if (g_timer.open) {
+    (void)hipEventRecord(g_timer.ev[2 * g_timer.used + 1], st);
+    g_timer.open = false;
+    ++g_timer.used;
+  }
+}
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
@@ -91,18 +136,29 @@ static int layer_forward(const lps_layer_desc* L, float* x, int pos, void* scrat
   float* m = reinterpret_cast<float*>(sc + s.m);
   void* at = sc + s.attn;
   QkvArgs qa{L, x, pos, q, reinterpret_cast<int*>(at), attn_counters(L->nkv)};
+  timer_begin(LPS_KIND_QKV, st);
   int rc = launch_qkv(qa, st);
+  timer_end(LPS_KIND_QKV, st);
   if (rc) return rc;
+  timer_begin(LPS_KIND_ATTN, st);
   rc = launch_attention(L->nq, L->nkv, L->hd, L->kvdtype, L->k_cache, L->v_cache, L->ctx_max,
                         pos + 1, q, o, at, true, st);
+  timer_end(LPS_KIND_ATTN, st);
   if (rc) return rc;
+  timer_begin(LPS_KIND_OPROJ, st);
   rc = launch_gemv(L->wdtype, L->w_o, L->s_o, L->d, L->nq * L->hd, o, nullptr, 0.f, x,
                    LPS_EPI_ADD, st);
+  timer_end(LPS_KIND_OPROJ, st);
   if (rc) return rc;
+  timer_begin(LPS_KIND_GATEUP, st);
   rc = launch_gemv(L->wdtype, L->w_gu, L->s_gu, 2 * L->ff, L->d, x, L->g_ffn, L->eps, m,
                    LPS_EPI_SWIGLU, st);
+  timer_end(LPS_KIND_GATEUP, st);
   if (rc) return rc;
-  return launch_gemv(L->wdtype, L->w_d, L->s_d, L->d, L->ff, m, nullptr, 0.f, x, LPS_EPI_ADD, st);
+  timer_begin(LPS_KIND_DOWN, st);
+  rc = launch_gemv(L->wdtype, L->w_d, L->s_d, L->d, L->ff, m, nullptr, 0.f, x, LPS_EPI_ADD, st);
+  timer_end(LPS_KIND_DOWN, st);
+  return rc;
 }
 
 static int check_fence(const int32_t* fence, int32_t n_stages, int32_t n_layers, const char* who) {
@@ -370,7 +426,55 @@ int lps_head_forward(const lps_head_desc* h, const float* x, float* logits, int3
               "lps_head_forward: weights, gain and x must be 16-byte aligned");
   LPS_REQUIRE(scratch_bytes >= head_scratch(h), LPS_EINVAL, "lps_head_forward: scratch %zu < %zu",
               scratch_bytes, head_scratch(h));
-  return launch_head(h, x, logits, tok_out, scratch, scratch_bytes, as_stream(stream));
+  timer_begin(LPS_KIND_HEAD, as_stream(stream));
+  int rc = launch_head(h, x, logits, tok_out, scratch, scratch_bytes, as_stream(stream));
+  timer_end(LPS_KIND_HEAD, as_stream(stream));
+  return rc;
+}
+
+// ---- benchmark timer ----------------------------------------------------------------------
+int lps_timer_start(int32_t kind, int32_t capacity) {
+  LPS_REQUIRE(kind >= LPS_KIND_QKV && kind <= LPS_KIND_HEAD, LPS_EINVAL, "lps_timer_start: kind %d", kind);
+  LPS_REQUIRE(capacity >= 1 && capacity <= 1 << 16, LPS_EINVAL, "lps_timer_start: capacity %d", capacity);
+  std::lock_guard<std::mutex> lk(g_timer.mu);
+  LPS_REQUIRE(g_timer.kind.load() == 0, LPS_ESTATE, "lps_timer_start: a timer is already running");
+  g_timer.ev.assign(size_t(2) * capacity, nullptr);
+  for (auto& e : g_timer.ev) {
+    if (hipEventCreate(&e) != hipSuccess) {
+      for (auto& f : g_timer.ev)
+        if (f) (void)hipEventDestroy(f);
+      g_timer.ev.clear();
+      return fail(LPS_EHIP, "lps_timer_start: hipEventCreate failed");
+    }
+  }
+  g_timer.used = 0;
+  g_timer.open = false;
+  g_timer.kind.store(kind);
+  return LPS_OK;
+}
+
+int lps_timer_stop(float* ms_out, int32_t cap, int32_t* n_out) {
+  LPS_REQUIRE(n_out && (cap == 0 || ms_out), LPS_EINVAL, "lps_timer_stop: null output");
+  std::lock_guard<std::mutex> lk(g_timer.mu);
+  LPS_REQUIRE(g_timer.kind.load() != 0, LPS_ESTATE, "lps_timer_stop: no timer is running");
+  g_timer.kind.store(0);
+  int rc = LPS_OK;
+  int n = 0;
+  for (int i = 0; i < g_timer.used; ++i) {
+    float ms = 0.f;
+    if (hipEventSynchronize(g_timer.ev[2 * i + 1]) != hipSuccess ||
+        hipEventElapsedTime(&ms, g_timer.ev[2 * i], g_timer.ev[2 * i + 1]) != hipSuccess) {
+      rc = fail(LPS_EHIP, "lps_timer_stop: reading event pair %d failed", i);
+      break;
+    }
+    if (n < cap) ms_out[n] = ms;
+    ++n;
+  }
+  for (auto& e : g_timer.ev) (void)hipEventDestroy(e);
+  g_timer.ev.clear();
+  g_timer.used = 0;
+  *n_out = n < cap ? n : cap;
+  return rc;
 }
 
 // ---- A14 boundaries ----------------------------------------------------------------------

@@ -37,6 +37,14 @@ void count_drain();
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// Kernels whose dynamic LDS exceeds the default 64 KiB window must opt in once
+// per function (gfx950 has 160 KiB per workgroup).  Returns a status.
+int ensure_lds(const void* fn, size_t bytes);
+
+// Benchmark timer: brackets launches of one kind with events (no-op when off).
+void timer_begin(int kind, hipStream_t st);
+void timer_end(int kind, hipStream_t st);
+
 // ---- scratch carving ------------------------------------------------------------
 inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 

@@ -58,14 +58,15 @@ __global__ void k_f16_to_f32(const uint16_t* src, float* dst, long long lo, long
        i += (long long)gridDim.x * blockDim.x)
     dst[i] = static_cast<float>(__builtin_bit_cast(_Float16, src[i]));
 }
-// x = f32(x + ((shared + local) + bo)); bo may be the same buffer as local: every
-// element is read before it is written, by the same thread.
-__global__ void k_combine(float* x, const float* shared, const float* local, const float* bo,
-                          long long n) {
+// out = f32(x + ((shared + local) + bo)); out may be bo or x (no __restrict__):
+// every element is read before it is written, by the same thread.
+__global__ void k_combine(float* out, const float* x, const float* shared, const float* local,
+                          const float* bo, long long n) {
   for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n;
        i += (long long)gridDim.x * blockDim.x) {
     const float y = (shared[i] + local[i]) + bo[i];
-    x[i] = x[i] + y;
+    const float v = x[i] + y;
+    out[i] = v;
   }
 }
 
@@ -131,14 +132,17 @@ extern "C" int lps_f32_to_f16(const float* src, uint16_t* dst, int64_t n, void* 
 // strata PR #3648, Approach (sums; the combine kernel; piece bounds): the FP16
 // sums are widened into bo one piece at a time on the remote stream, an event
 // after each piece; the main stream waits the last event and then combines.
-extern "C" int lps_moe_combine(float* x, const float* shared, const float* local,
-                               const uint16_t* remote16, float* bo, int32_t T, int32_t d,
-                               int32_t n_pieces, void* s_remote, void* s_main) {
+extern "C" int lps_moe_combine(float* out, const float* x, const float* shared,
+                               const float* local, const uint16_t* remote16, float* bo, int32_t T,
+                               int32_t d, int32_t n_pieces, void* s_remote, void* s_main) {
   LPS_REQUIRE(T >= 0 && d > 0, LPS_EINVAL, "lps_moe_combine: T %d / d %d", T, d);
   LPS_REQUIRE(n_pieces >= 1 && n_pieces <= 64, LPS_EINVAL,
               "lps_moe_combine: n_pieces %d outside [1, 64]", n_pieces);
   if (T == 0) return LPS_OK;
-  LPS_REQUIRE(x && shared && local && remote16 && bo, LPS_EINVAL, "lps_moe_combine: null pointer");
+  LPS_REQUIRE(out && x && shared && local && remote16 && bo, LPS_EINVAL,
+              "lps_moe_combine: null pointer");
+  LPS_REQUIRE(bo != local && bo != shared && (const void*)bo != (const void*)remote16, LPS_EINVAL,
+              "lps_moe_combine: bo must not be shared, local or remote16 (they are read after bo is written)");
   hipStream_t sr = as_stream(s_remote), sm = as_stream(s_main);
   hipEvent_t start, done;
   LPS_HIP(hipEventCreateWithFlags(&start, hipEventDisableTiming));
@@ -160,7 +164,7 @@ extern "C" int lps_moe_combine(float* x, const float* shared, const float* local
   LPS_HIP(hipEventRecord(done, sr));
   LPS_HIP(hipStreamWaitEvent(sm, done, 0));
   const long long n = (long long)T * d;
-  hipLaunchKernelGGL(k_combine, grid_for(n), dim3(256), 0, sm, x, shared, local, bo, n);
+  hipLaunchKernelGGL(k_combine, grid_for(n), dim3(256), 0, sm, out, x, shared, local, bo, n);
   LPS_HIP(hipGetLastError());
   // events are released once they have fired (the runtime keeps them alive)
   LPS_HIP(hipEventDestroy(start));

@@ -285,9 +285,6 @@ static int check_moe(const lps_moe_desc* m, const char* who) {
   return LPS_OK;
 }
 
-static bool allow_lds(const void* fn) {
-  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess;
-}
 
 }  // namespace lps
 
@@ -307,8 +304,8 @@ extern "C" int lps_moe_route(const lps_moe_desc* m, const float* x, int32_t T, i
   LPS_REQUIRE(x && idx && w && scratch, LPS_EINVAL, "lps_moe_route: null pointer");
   LPS_REQUIRE(scratch_bytes >= lps_moe_route_scratch_bytes(m, T), LPS_EINVAL,
               "lps_moe_route: scratch %zu < %zu", scratch_bytes, lps_moe_route_scratch_bytes(m, T));
-  static bool a = allow_lds((const void*)k_route);
-  (void)a;
+  rc = ensure_lds((const void*)k_route, size_t(m->d) * 4);
+  if (rc) return rc;
   char* s = static_cast<char*>(scratch);
   return launch_route(m, x, T, idx, w, reinterpret_cast<float*>(s + align256(size_t(T) * 4)),
                       reinterpret_cast<int*>(s), as_stream(stream));
@@ -332,10 +329,10 @@ extern "C" int lps_moe_layer_decode(const lps_moe_desc* m, float* x, void* scrat
   int32_t* idx = reinterpret_cast<int32_t*>(sc + s.idx);
   float* wts = reinterpret_cast<float*>(sc + s.w);
   float* mbuf = reinterpret_cast<float*>(sc + s.mbuf);
-  static bool a0 = allow_lds((const void*)k_route);
-  static bool a1 = allow_lds((const void*)k_moe_gu<4>);
-  static bool a2 = allow_lds((const void*)k_moe_down);
-  (void)a0, (void)a1, (void)a2;
+  if ((rc = ensure_lds((const void*)k_route, size_t(m->d) * 4)) ||
+      (rc = ensure_lds((const void*)k_moe_gu<4>, size_t(m->d) * 4)) ||
+      (rc = ensure_lds((const void*)k_moe_down, size_t(m->top_k + 1) * m->ff * 4)))
+    return rc;
   rc = launch_route(m, x, 1, idx, wts, reinterpret_cast<float*>(sc + s.logits),
                     reinterpret_cast<int*>(sc + s.cnt), st);
   if (rc) return rc;

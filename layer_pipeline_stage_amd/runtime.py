@@ -131,8 +131,10 @@ class DeviceDecoder:
         if fence is None:
             fence = lps.stage_plan(cfg.n_layers, 1)
         fence = list(fence)
-        # validated by the library (raises on an invalid plan)
-        lps.stage_plan(cfg.n_layers, len(fence) - 1, fence[1:-1])
+        # the library validates the cuts; the ends must be 0 and n_layers
+        plan = lps.stage_plan(cfg.n_layers, len(fence) - 1, fence[1:-1]) if len(fence) >= 2 else None
+        if plan != fence:
+            raise lps.LpsError(lps.LPS_EINVAL, f"fence {fence} is not a plan of {cfg.n_layers} layers")
         self.fence = fence
         self.n_stages = n = len(fence) - 1
         self._fence_c = lps.i32_array(fence)

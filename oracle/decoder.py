@@ -66,14 +66,26 @@ def silu(z):
 
 def matvec_grouped(W, h, group=32):
     """y = W h summed over K in ascending groups of 32 columns (the MXFP4 scale
-    groups), so that zero groups appended at the end of K leave y unchanged."""
+    groups): each group's 32 products are summed, then the group sums are
+    accumulated left to right (a cumulative sum is strictly sequential), so
+    zero groups appended at the end of K leave y unchanged."""
     N, K = W.shape
     Wg = W.reshape(N, K // group, group)
     hg = np.asarray(h, dtype=np.float64).reshape(K // group, group)
-    acc = np.zeros(N, dtype=np.float64)
-    for j in range(K // group):
-        acc += (Wg[:, j, :] * hg[j]).sum(axis=1)
-    return acc
+    part = (Wg * hg).sum(axis=2)                 # [N, K/32]
+    return np.cumsum(part, axis=1)[:, -1]
+
+
+_POOL = None
+
+
+def _pool():
+    global _POOL
+    if _POOL is None:
+        import os
+        from concurrent.futures import ThreadPoolExecutor
+        _POOL = ThreadPoolExecutor(max(1, min(16, len(os.sched_getaffinity(0)))))
+    return _POOL
 
 
 class Decoder:
@@ -114,10 +126,27 @@ class Decoder:
         return w
 
     def mv(self, l, name, h):
+        if self.cfg.wdtype == "mxfp4" and self._wc is None:
+            return self._mv_mxfp4_rows(l, name, h)
         W = self.W(l, name)
         if self.cfg.wdtype == "mxfp4":
             return matvec_grouped(W, h)
         return W @ h
+
+    def _mv_mxfp4_rows(self, l, name, h, rows=1024):
+        """Same result as matvec_grouped(widen(W), h) (every row is computed
+        alone); rows are widened a block at a time on a thread pool so the whole
+        f64 matrix never exists at once."""
+        codes, scales = self.m["layers"][l][name] if l >= 0 else self.m[name]
+        N = codes.shape[0]
+        y = np.empty(N, dtype=np.float64)
+
+        def block(i):
+            lo, hi = i * rows, min(N, (i + 1) * rows)
+            y[lo:hi] = matvec_grouped(widen_weight((codes[lo:hi], scales[lo:hi]), "mxfp4"), h)
+
+        list(_pool().map(block, range((N + rows - 1) // rows)))
+        return y
 
     # ---- one layer ---------------------------------------------------------
     def layer(self, l, x32, p):

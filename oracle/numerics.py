@@ -73,6 +73,10 @@ def e8m0_value(s) -> np.ndarray:
     return np.where(s == 255, np.nan, v)
 
 
+# element pair (low nibble, high nibble) of every byte value
+_PAIR = np.stack([E2M1[np.arange(256) & 0x0F], E2M1[np.arange(256) >> 4]], axis=1)
+
+
 def mxfp4_to_f64(codes, scales) -> np.ndarray:
     """codes u8 [N, K/2], scales u8 [N, K/32] -> f64 [N, K].
 
@@ -80,11 +84,11 @@ def mxfp4_to_f64(codes, scales) -> np.ndarray:
     codes = np.asarray(codes, dtype=np.uint8)
     N, Kh = codes.shape
     K = 2 * Kh
-    el = np.empty((N, K), dtype=np.float64)
-    el[:, 0::2] = E2M1[codes & 0x0F]
-    el[:, 1::2] = E2M1[codes >> 4]
+    el = _PAIR[codes].reshape(N, K)                # [N, K/2, 2] -> elements 2b, 2b+1
     sc = e8m0_value(scales)                        # [N, K/32]
-    return (el.reshape(N, K // 32, 32) * sc[..., None]).reshape(N, K)
+    el = el.reshape(N, K // 32, 32)
+    el *= sc[..., None]
+    return el.reshape(N, K)
 
 
 def widen_weight(w, wdtype: str) -> np.ndarray:

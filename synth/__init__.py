@@ -17,6 +17,6 @@ from .gen import (  # noqa: F401
 )
 from .models import (  # noqa: F401
     DecoderConfig, MoEConfig,
-    make_tiny, make_dense, make_moe, make_pad,
+    make_tiny, make_dense, make_moe, make_pad, make_pad_pair,
     TINY, TINY_N4, DENSE8B, MOE, PAD,
 )

@@ -158,7 +158,12 @@ def _pad_cols(cs, n_zero_k):
     return np.concatenate([codes, zc], axis=1), np.concatenate([scales, zs], axis=1)
 
 
-def make_pad(cfg: DecoderConfig = PAD, padded: bool = True) -> dict:
+def make_pad_pair(cfg: DecoderConfig = PAD):
+    """(padded, unpadded) models sharing one draw of the real weights."""
+    return make_pad(cfg, padded=True, _both=True)
+
+
+def make_pad(cfg: DecoderConfig = PAD, padded: bool = True, _both: bool = False):
     """MXFP4 decoder whose real part is shared by the padded and the unpadded
     model.  Padded: dummy q/kv heads and FFN rows/columns appended at the end of
     every padded axis (codes 0x00, scales 0x7F = 2^0)."""
@@ -167,6 +172,7 @@ def make_pad(cfg: DecoderConfig = PAD, padded: bool = True) -> dict:
     d, hd = cfg.d, cfg.hd
     out_cfg = cfg if padded else real
     m = {"cfg": out_cfg, "layers": []}
+    um = {"cfg": real, "layers": []}
     dq, dkv, dff = cfg.nq - real.nq, cfg.nkv - real.nkv, cfg.ff - real.ff
     for l in range(cfg.n_layers):
         wq = _mx(cfg, f"l{l}/q", (real.nq * hd, d))
@@ -178,6 +184,13 @@ def make_pad(cfg: DecoderConfig = PAD, padded: bool = True) -> dict:
         wd = _mx(cfg, f"l{l}/down", (d, real.ff))
         kp = bf16_bits(normal_f32(cfg.seed, f"{cfg.name}/l{l}/k_prefix", (real.nkv, cfg.prefix, hd)))
         vp = bf16_bits(normal_f32(cfg.seed, f"{cfg.name}/l{l}/v_prefix", (real.nkv, cfg.prefix, hd)))
+        cat = lambda *ts: (np.concatenate([t[0] for t in ts]), np.concatenate([t[1] for t in ts]))
+        if _both:
+            um["layers"].append({
+                "g_attn": np.ones(d, np.float32), "w_qkv": cat(wq, wk, wv), "w_o": wo,
+                "g_ffn": np.ones(d, np.float32), "w_gu": cat(wg, wu), "w_d": wd,
+                "k_prefix": kp, "v_prefix": vp,
+            })
         if padded:
             wq, wk, wv = _pad_rows(wq, dq * hd), _pad_rows(wk, dkv * hd), _pad_rows(wv, dkv * hd)
             wo = _pad_cols(wo, dq * hd)
@@ -185,7 +198,6 @@ def make_pad(cfg: DecoderConfig = PAD, padded: bool = True) -> dict:
             wd = _pad_cols(wd, dff)
             z = np.zeros((dkv, cfg.prefix, hd), np.uint16)
             kp, vp = np.concatenate([kp, z]), np.concatenate([vp, z])
-        cat = lambda *ts: (np.concatenate([t[0] for t in ts]), np.concatenate([t[1] for t in ts]))
         m["layers"].append({
             "g_attn": np.ones(d, np.float32),
             "w_qkv": cat(wq, wk, wv),
@@ -197,6 +209,9 @@ def make_pad(cfg: DecoderConfig = PAD, padded: bool = True) -> dict:
             "v_prefix": vp,
         })
     m["x_in"] = normal_f32(cfg.seed, f"{cfg.name}/x_in", (cfg.steps, d), 1.0)
+    if _both:
+        um["x_in"] = m["x_in"]
+        return m, um
     return m
 
 

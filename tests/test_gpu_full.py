@@ -1,0 +1,103 @@
+"""The workloads at their full sizes, in the launch configuration the benchmark
+times: the dense 8B-class slice (N = 4 even split vs N = 1), the padded-head
+MXFP4 model (padded vs unpadded) and the MoE stack at decode.  The oracle is
+run on a few steps each (it takes seconds per step at these sizes)."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle.decoder import Decoder
+from oracle.moe import MoEStack
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def rt():
+    from layer_pipeline_stage_amd import runtime, lps
+    lps.load()
+    assert torch.cuda.is_available(), "GPU tests need a visible ROCm GPU"
+    return runtime
+
+
+@pytest.fixture(scope="module")
+def dense():
+    return synth.make_dense(replace(synth.DENSE8B, steps=15))
+
+
+def test_dense_staged_equals_unstaged_and_oracle(rt, dense):
+    from layer_pipeline_stage_amd import lps
+    cfg = dense["cfg"]
+    dd = rt.DeviceDecoder(dense)
+    start = [int(dense["prompt"][0])]
+    ref = dd.run_tokens(start, cfg.steps)
+    dd.set_fence(lps.stage_plan(cfg.n_layers, 4))
+    assert dd.fence == [0, 2, 4, 6, 8]
+    dd.reset()
+    lps.lps_counters_reset()
+    got = dd.run_tokens(start, cfg.steps)
+    c = lps.counters()
+    n = cfg.steps + 1
+    assert c["stage_walks"] == 4 * n and c["boundary_sends"] == 3 * n
+    assert got.argmax == ref.argmax
+    assert all(np.array_equal(a, b) for a, b in zip(got.logits, ref.logits))
+    dd.close()
+    # teacher-forced oracle on the first 2 steps (bf16 weights: 2e-3 of the logit scale)
+    dec = Decoder(dense, weight_cache=False)
+    _, am, lg = dec.greedy([], 0, feed=got.fed[:2])
+    for i in range(2):
+        tol = 2e-3 * np.abs(lg[i]).max()
+        assert np.max(np.abs(got.logits[i] - lg[i])) <= tol
+        if got.argmax[i] != am[i]:
+            top2 = np.sort(lg[i])[-2:]
+            assert top2[1] - top2[0] <= 2 * tol
+
+
+@pytest.fixture(scope="module")
+def pad_models():
+    return synth.make_pad_pair(replace(synth.PAD, steps=3))
+
+
+def test_padded_mxfp4_equals_unpadded(rt, pad_models):
+    """TP3 zero-padded dummy heads plan: 36 q / 6 kv heads of 256 with 12 q and
+    2 kv zero dummies, down_proj K = 17472 (not a multiple of 128).  The GPU's
+    padded output is bit-identical to the unpadded model's (every K chunk lands
+    on the same lane whatever K is), and both match the oracle."""
+    pm, um = pad_models
+    outs = []
+    for m in (pm, um):
+        dd = rt.DeviceDecoder(m)
+        outs.append(dd.run_hidden(m["x_in"]))
+        dd.close()
+    assert np.array_equal(outs[0], outs[1])
+    dec = Decoder(um, weight_cache=False)
+    for t in range(1):
+        ref = dec.step(um["x_in"][t], um["cfg"].prefix + t)
+        tol = 2e-3 * np.abs(ref).max()
+        assert np.max(np.abs(outs[0][t] - ref)) <= tol, (t, np.max(np.abs(outs[0][t] - ref)))
+
+
+def test_padded_mxfp4_staged(rt, pad_models):
+    pm, _ = pad_models
+    a = rt.DeviceDecoder(pm)
+    ra = a.run_hidden(pm["x_in"])
+    a.close()
+    b = rt.DeviceDecoder(pm, fence=[0, 2, 4])
+    rb = b.run_hidden(pm["x_in"])
+    b.close()
+    assert np.array_equal(ra, rb)
+
+
+def test_moe_decode_full_size(rt):
+    cfg = replace(synth.MOE, steps=3, prefill_T=0)
+    m = synth.make_moe(cfg)
+    st = rt.DeviceMoEStack(m)
+    got = st.decode(m["x_in"])
+    ref_st = MoEStack(m)
+    for t in range(2):
+        ref = ref_st.forward(m["x_in"][t])
+        tol = 2e-3 * np.abs(ref).max()
+        assert np.max(np.abs(got[t] - ref)) <= tol, (t, np.max(np.abs(got[t] - ref)))

@@ -166,7 +166,8 @@ def test_rmsnorm_and_embed(L):
     x = rng.standard_normal(d).astype(np.float32)
     g = (1 + 0.1 * rng.standard_normal(d)).astype(np.float32)
     yd = torch.zeros(d, dtype=torch.float32, device=DEV)
-    L.lps_rmsnorm(ptr(dev(x)), ptr(dev(g)), 1e-6, d, ptr(yd), stream())
+    xd, gd = dev(x), dev(g)          # keep the inputs alive until the kernel has run
+    L.lps_rmsnorm(ptr(xd), ptr(gd), 1e-6, d, ptr(yd), stream())
     ref = rmsnorm(x.astype(np.float64), g, 1e-6)
     assert np.max(np.abs(yd.cpu().numpy() - ref)) <= 1e-6 * np.abs(ref).max()
     for wd in ("f32", "bf16"):
@@ -207,8 +208,9 @@ def test_attention_parity(L, nq, nkv, hd, kvd, ns):
     for n in ns:
         q = rng.standard_normal((nq, hd)).astype(np.float32)
         od = torch.zeros(nq * hd, dtype=torch.float32, device=DEV)
+        qd = dev(q)
         L.lps_attention_decode(nq, nkv, hd, L.DTYPES[kvd], ptr(Kd), ptr(Vd), ctx_max, n,
-                               ptr(dev(q)), ptr(od), ptr(scratch), sb, stream())
+                               ptr(qd), ptr(od), ptr(scratch), sb, stream())
         ref = attend(q.astype(np.float64), Kw[:, :n], Vw[:, :n])
         got = od.cpu().numpy().reshape(nq, hd)
         # softmax weights carry ~(hd/16 + 8) ulps from the score dots and exp;
@@ -218,7 +220,7 @@ def test_attention_parity(L, nq, nkv, hd, kvd, ns):
     # counters are left at zero: a second identical call gives identical bits
     o1 = od.clone()
     L.lps_attention_decode(nq, nkv, hd, L.DTYPES[kvd], ptr(Kd), ptr(Vd), ctx_max, ns[-1],
-                           ptr(dev(q)), ptr(od), ptr(scratch), sb, stream())
+                           ptr(qd), ptr(od), ptr(scratch), sb, stream())
     assert torch.equal(o1, od)
 
 
@@ -251,7 +253,8 @@ def test_qkv_rope_append(L, cfg):
     for pos in (0, 3, cfg.ctx_max - 1):
         x = rng.standard_normal(cfg.d).astype(np.float32)
         qd = torch.zeros(cfg.nq * cfg.hd, dtype=torch.float32, device=DEV)
-        L.lps_qkv_rope_append(C.byref(desc), ptr(dev(x)), pos, ptr(qd), stream())
+        xd = dev(x)
+        L.lps_qkv_rope_append(C.byref(desc), ptr(xd), pos, ptr(qd), stream())
         h = rmsnorm(x.astype(np.float64), Lw["g_attn"], cfg.eps)
         qkv = W @ h
         nq, nkv, hd = cfg.nq, cfg.nkv, cfg.hd
@@ -288,7 +291,8 @@ def test_head_argmax(L):
         lg = torch.zeros(V, dtype=torch.float32, device=DEV)
         tk = torch.zeros(1, dtype=torch.int32, device=DEV)
         for rep in range(2):
-            L.lps_head_forward(C.byref(hdsc), ptr(dev(x)), ptr(lg), ptr(tk), ptr(sc), sb, stream())
+            xd = dev(x)
+            L.lps_head_forward(C.byref(hdsc), ptr(xd), ptr(lg), ptr(tk), ptr(sc), sb, stream())
             got = lg.cpu().numpy()
             assert int(tk.item()) == int(np.argmax(got))      # exact on the GPU's own logits
             W64 = onum.widen_weight(W, wd)
@@ -306,7 +310,8 @@ def test_head_argmax(L):
     hdsc.w_lm = ptr(Wd)
     gd = dev(np.ones(d, np.float32))
     hdsc.g_out = ptr(gd)
-    L.lps_head_forward(C.byref(hdsc), ptr(dev(x)), ptr(lg), ptr(tk), ptr(sc), sb, stream())
+    xd = dev(x)
+    L.lps_head_forward(C.byref(hdsc), ptr(xd), ptr(lg), ptr(tk), ptr(sc), sb, stream())
     assert int(tk.item()) == 7
 
 
@@ -371,21 +376,26 @@ def test_f16_pieces_and_combine(L):
     T, d = 37, 2048
     rem = (rng.standard_normal((T, d)) * np.exp(rng.uniform(-6, 6, (T, 1)))).astype(np.float32)
     r16 = torch.zeros((T, d), dtype=torch.int16, device=DEV)
-    L.lps_f32_to_f16(ptr(dev(rem)), ptr(r16), T * d, stream())
+    remd = dev(rem)
+    L.lps_f32_to_f16(ptr(remd), ptr(r16), T * d, stream())
     assert np.array_equal(r16.cpu().numpy().view(np.uint16),
                           rem.astype(np.float16).view(np.uint16))
     x0, sh, lo = (rng.standard_normal((T, d)).astype(np.float32) for _ in range(3))
     sr, sm = torch.cuda.Stream(), torch.cuda.Stream()
     outs = []
-    for P, alias in ((1, False), (8, False), (8, True), (3, False), (37, False)):
+    shd, lod = dev(sh), dev(lo)
+    for P, alias in ((1, None), (8, None), (8, "bo"), (8, "x"), (3, None), (37, None)):
         x = dev(x0)
-        lod = dev(lo)
-        bo = lod if alias else torch.full((T, d), float("nan"), device=DEV)
+        bo = torch.full((T, d), float("nan"), device=DEV)      # poisoned, as a reused buffer
+        out = {"bo": bo, "x": x, None: torch.full((T, d), float("nan"), device=DEV)}[alias]
         torch.cuda.synchronize()
-        L.lps_moe_combine(ptr(x), ptr(dev(sh)), ptr(lod), ptr(r16), ptr(bo), T, d, P,
+        L.lps_moe_combine(ptr(out), ptr(x), ptr(shd), ptr(lod), ptr(r16), ptr(bo), T, d, P,
                           sr.cuda_stream, sm.cuda_stream)
         torch.cuda.synchronize()
-        outs.append(x.cpu().numpy())
+        outs.append(out.cpu().numpy())
+    with pytest.raises(L.LpsError):      # bo may not be an input that is read after it
+        L.lps_moe_combine(ptr(out), ptr(x), ptr(shd), ptr(lod), ptr(r16), ptr(lod), T, d, 8,
+                          sr.cuda_stream, sm.cuda_stream)
     for o in outs[1:]:
         assert np.array_equal(o, outs[0])
     r32 = f16_pieces_to_f32(rem, 8)
@@ -409,7 +419,8 @@ def test_moe_route_parity(L):
     sc = torch.zeros(sb, dtype=torch.uint8, device=DEV)
     idx = torch.zeros((T, 8), dtype=torch.int32, device=DEV)
     w = torch.zeros((T, 8), dtype=torch.float32, device=DEV)
-    L.lps_moe_route(C.byref(desc), ptr(dev(X)), T, ptr(idx), ptr(w), ptr(sc), sb, stream())
+    Xd = dev(X)
+    L.lps_moe_route(C.byref(desc), ptr(Xd), T, ptr(idx), ptr(w), ptr(sc), sb, stream())
     gi, gw = idx.cpu().numpy(), w.cpu().numpy()
     h = rmsnorm(X.astype(np.float64), Lw["g_ffn"], cfg.eps)
     r = h @ onum.bf16_to_f64(Lw["w_r"]).T

@@ -273,3 +273,26 @@ def test_pad_generator_geometry_matches_page():
     wd_c, wd_s = pm["layers"][0]["w_d"]
     assert not np.any(wd_c[:, SMALL_PAD.ff_real // 2:]) and np.all(wd_s[:, SMALL_PAD.ff_real // 32:] == 0x7F)
     assert not np.any(wd_s == 0xFF)
+
+
+def test_pad_pair_matches_separate_builds():
+    pm, um = synth.make_pad_pair(SMALL_PAD)
+    pm2 = synth.make_pad(SMALL_PAD, padded=True)
+    um2 = synth.make_pad(SMALL_PAD, padded=False)
+    for a, b in ((pm, pm2), (um, um2)):
+        assert a["cfg"] == b["cfg"]
+        for La, Lb in zip(a["layers"], b["layers"]):
+            for k in La:
+                va, vb = La[k], Lb[k]
+                if isinstance(va, tuple):
+                    assert all(np.array_equal(x, y) for x, y in zip(va, vb))
+                else:
+                    assert np.array_equal(va, vb)
+
+
+def test_mxfp4_row_blocks_equal_whole_matrix():
+    pm = synth.make_pad(SMALL_PAD, padded=True)
+    a, b = Decoder(pm, weight_cache=True), Decoder(pm, weight_cache=False)
+    x = pm["x_in"][0]
+    h = rmsnorm(x.astype(np.float64), pm["layers"][0]["g_attn"], SMALL_PAD.eps)
+    assert np.array_equal(a.mv(0, "w_gu", h), b._mv_mxfp4_rows(0, "w_gu", h, rows=7))
