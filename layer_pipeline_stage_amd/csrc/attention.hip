@@ -7,9 +7,9 @@
 // G query heads of the group; scores are reduced across the lanes of a row by
 // wavefront shuffles, the chunk softmax (max, sum) by wave reductions, and the
 // V-weighted sums across rows by shuffles and a small LDS tree.  Each tile
-// writes (m, l, o) partials; the last tile of a kv head to finish (a counter
-// bumped after a device-scope fence) merges all chunks of that head in chunk
-// order, so the result does not depend on which tile finishes last.
+// writes (m, l, o) partials; a second small launch merges every q head's chunks
+// in chunk order, so the result does not depend on the order the tiles ran in
+// (and no tile waits on, or fences for, another).
 #include "dev.h"
 #include "internal.h"
 
@@ -30,7 +30,6 @@ struct AttnP {
   float* pm;   // [nkv, nch, G]
   float* pl;   // [nkv, nch, G]
   float* po;   // [nkv, nch, G, HD]
-  int* cnt;    // [nkv]
   int G, ctx_max, n, nch;
   float scale;
 };
@@ -72,7 +71,6 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attn(AttnP p) {
   __shared__ float qs[ATT_MAXG][HD];
   __shared__ float sc[ATT_MAXG][ATT_CH];
   __shared__ float red[ATT_NW][ATT_MAXG][HD];
-  __shared__ int is_last;
 
   const int chunk = blockIdx.x, g = blockIdx.y;
   const int G = p.G;
@@ -174,52 +172,62 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attn(AttnP p) {
     for (int w = 1; w < ATT_NW; ++w) v += red[w][h][e];
     p.po[ob + i] = v;
   }
-  // ---- the last tile of this kv head merges all chunks in chunk order ----
-  __threadfence();
+}
+
+// Merge of the chunk partials of one q head, in chunk order: M = max m_c,
+// L = sum_c l_c e^(m_c - M), o = sum_c o_c e^(m_c - M) / L.  A separate launch:
+// the partials of all tiles are complete when it starts (stream order), so no
+// device-scope fence or counter is needed.
+template <int HD>
+__global__ __launch_bounds__(HD) void k_attn_merge(AttnP p) {
+  const int hq = blockIdx.x;               // q head
+  const int g = hq / p.G, h = hq - g * p.G;
+  const int e = threadIdx.x;
+  __shared__ float wsh[1024];               // e^(m_c - M) per chunk, chunk-tiled
+  float M = -INFINITY;
+  for (int c = e; c < p.nch; c += HD) M = fmaxf(M, p.pm[((long long)g * p.nch + c) * p.G + h]);
+  // block max over the per-thread maxima (HD threads)
+  __shared__ float red[HD / WAVE];
+  M = wave_max(M);
+  if ((e & (WAVE - 1)) == 0) red[e / WAVE] = M;
   __syncthreads();
-  if (tid == 0) {
-    const int prev = atomicAdd(p.cnt + g, 1);
-    is_last = (prev == p.nch - 1);
-  }
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  for (int i = tid; i < G * HD; i += ATT_THREADS) {
-    const int h = i / HD;
-    float M = -INFINITY;
-    for (int c = 0; c < p.nch; ++c) M = fmaxf(M, p.pm[((long long)g * p.nch + c) * G + h]);
-    float L = 0.f, O = 0.f;
-    for (int c = 0; c < p.nch; ++c) {
-      const long long pi = ((long long)g * p.nch + c) * G + h;
-      const float w = expf(p.pm[pi] - M);
+  M = red[0];
+#pragma unroll
+  for (int i = 1; i < HD / WAVE; ++i) M = fmaxf(M, red[i]);
+  float L = 0.f, O = 0.f;
+  for (int c0 = 0; c0 < p.nch; c0 += 1024) {
+    const int n = min(1024, p.nch - c0);
+    __syncthreads();
+    for (int c = e; c < n; c += HD)
+      wsh[c] = expf(p.pm[((long long)g * p.nch + c0 + c) * p.G + h] - M);
+    __syncthreads();
+    for (int c = 0; c < n; ++c) {
+      const long long pi = ((long long)g * p.nch + c0 + c) * p.G + h;
+      const float w = wsh[c];
       L = fmaf(w, p.pl[pi], L);
-      O = fmaf(w, p.po[pi * HD + (i % HD)], O);
+      O = fmaf(w, p.po[pi * HD + e], O);
     }
-    p.o[(long long)(g * G) * HD + i] = O / L;
   }
-  if (tid == 0) p.cnt[g] = 0;
+  p.o[(long long)hq * HD + e] = O / L;
 }
 
 static int nchunks(int rows) { return (rows + ATT_CH - 1) / ATT_CH; }
 
-int attn_counters(int nkv) { return nkv; }
-
 size_t attn_scratch(int nq, int nkv, int hd, int ctx_max) {
   const size_t nch = nchunks(ctx_max);
   const int G = nq / nkv;
-  return align256(size_t(nkv) * 4) + 2 * align256(size_t(nkv) * nch * G * 4) +
-         align256(size_t(nkv) * nch * G * hd * 4);
+  return 2 * align256(size_t(nkv) * nch * G * 4) + align256(size_t(nkv) * nch * G * hd * 4);
 }
 
 template <int HD, int KVT>
 static void go(const AttnP& p, int nkv, hipStream_t st) {
   hipLaunchKernelGGL((k_attn<HD, KVT>), dim3(p.nch, nkv), dim3(ATT_THREADS), 0, st, p);
+  hipLaunchKernelGGL((k_attn_merge<HD>), dim3(nkv * p.G), dim3(HD), 0, st, p);
 }
 
 int launch_attention(int nq, int nkv, int hd, int kvdtype, const void* kc, const void* vc,
                      int ctx_max, int n_rows, const float* q, float* o, void* scratch,
-                     bool counters_zeroed, hipStream_t st) {
-  (void)counters_zeroed;
+                     hipStream_t st) {
   AttnP p{};
   p.kc = kc;
   p.vc = vc;
@@ -232,8 +240,6 @@ int launch_attention(int nq, int nkv, int hd, int kvdtype, const void* kc, const
   p.scale = 1.0f / sqrtf(float(hd));
   const size_t nch_max = nchunks(ctx_max);
   char* s = static_cast<char*>(scratch);
-  p.cnt = reinterpret_cast<int*>(s);
-  s += align256(size_t(nkv) * 4);
   p.pm = reinterpret_cast<float*>(s);
   s += align256(size_t(nkv) * nch_max * p.G * 4);
   p.pl = reinterpret_cast<float*>(s);

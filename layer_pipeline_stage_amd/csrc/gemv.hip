@@ -27,8 +27,7 @@
 
 namespace lps {
 
-enum { EPI_STORE = LPS_EPI_STORE, EPI_ADD = LPS_EPI_ADD, EPI_SWIGLU = LPS_EPI_SWIGLU,
-       EPI_QKV = 3, EPI_LOGITS = 4 };
+enum { EPI_STORE = LPS_EPI_STORE, EPI_ADD = LPS_EPI_ADD, EPI_SWIGLU = LPS_EPI_SWIGLU, EPI_QKV = 3 };
 
 struct GemvP {
   const uint8_t* w;
@@ -45,13 +44,6 @@ struct GemvP {
   float base;
   void* kc;
   void* vc;
-  int* zero_ptr;
-  int n_zero;
-  // LM-head epilogue
-  float* pval;
-  int* pidx;
-  int* done;
-  int* tok;
 };
 
 template <int EPI>
@@ -78,8 +70,7 @@ __device__ __forceinline__ void store_kv(void* base, int kvdtype, long long off,
 }
 
 template <int EPI>
-__device__ __forceinline__ void epilogue(const GemvP& p, int u, int r0, int r1, float a0, float a1,
-                                         float& best, int& bidx) {
+__device__ __forceinline__ void epilogue(const GemvP& p, int u, int r0, int r1, float a0, float a1) {
   if constexpr (EPI == EPI_STORE) {
     p.y[r0] = a0;
     if (r1 >= 0) p.y[r1] = a1;
@@ -88,13 +79,6 @@ __device__ __forceinline__ void epilogue(const GemvP& p, int u, int r0, int r1, 
     if (r1 >= 0) p.y[r1] += a1;
   } else if constexpr (EPI == EPI_SWIGLU) {
     p.y[u] = silu(a0) * a1;
-  } else if constexpr (EPI == EPI_LOGITS) {
-    p.y[r0] = a0;
-    if (a0 > best) { best = a0; bidx = r0; }
-    if (r1 >= 0) {
-      p.y[r1] = a1;
-      if (a1 > best) { best = a1; bidx = r1; }
-    }
   } else {  // QKV: rotate q and k heads at pos, store q, append k and v to the caches
     const int half = p.hd >> 1;
     const int hh = u / half, i = u - hh * half;
@@ -124,17 +108,12 @@ __device__ __forceinline__ void epilogue(const GemvP& p, int u, int r0, int r1, 
 template <int WT, int EPI, int U, bool NORM>
 __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(GemvP p) {
   extern __shared__ float xs[];
-  if constexpr (EPI == EPI_QKV) {
-    if (blockIdx.x == 0 && int(threadIdx.x) < p.n_zero) p.zero_ptr[threadIdx.x] = 0;
-  }
   stage_x<NORM>(p.x, p.g, p.eps, p.K, xs);
   constexpr int CH = Fmt<WT>::CH;
   const int lane = threadIdx.x & (WAVE - 1);
   const int wv = threadIdx.x / WAVE;
   constexpr int NW = GEMV_THREADS / WAVE;
   const int nck = p.K / CH;
-  float best = -INFINITY;
-  int bidx = 0x7fffffff;
   for (int u = blockIdx.x * NW + wv; u < p.units; u += gridDim.x * NW) {
     int r0, r1;
     unit_rows<EPI>(p, u, r0, r1);
@@ -179,57 +158,36 @@ __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(GemvP p) {
     }
     a0 = wave_sum(a0);
     a1 = wave_sum(a1);
-    if (lane == 0) epilogue<EPI>(p, u, r0, r1, a0, a1, best, bidx);
+    if (lane == 0) epilogue<EPI>(p, u, r0, r1, a0, a1);
   }
-  if constexpr (EPI == EPI_LOGITS) {
-    __shared__ float bv[NW];
-    __shared__ int bi[NW];
-    __shared__ int is_last;
-    if (lane == 0) {
-      bv[wv] = best;
-      bi[wv] = bidx;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      float b = bv[0];
-      int ix = bi[0];
-      for (int i = 1; i < NW; ++i)
-        if (bv[i] > b || (bv[i] == b && bi[i] < ix)) { b = bv[i]; ix = bi[i]; }
-      p.pval[blockIdx.x] = b;
-      p.pidx[blockIdx.x] = ix;
-      __threadfence();
-      const int prev = atomicAdd(p.done, 1);
-      is_last = (prev == int(gridDim.x) - 1);
-    }
-    __syncthreads();
-    if (is_last) {
-      __threadfence();
-      // max with lowest-index ties is an exact selection: any order gives the same answer
-      float b = -INFINITY;
-      int ix = 0x7fffffff;
-      for (int i = threadIdx.x; i < int(gridDim.x); i += GEMV_THREADS) {
-        const float v = __hip_atomic_load(p.pval + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const int j = __hip_atomic_load(p.pidx + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (v > b || (v == b && j < ix)) { b = v; ix = j; }
-      }
+}
+
+// A16 argmax: the lowest index of the maximum of n values, one workgroup of
+// 1024 threads (a selection: exact in any order).  Runs as its own launch
+// after the LM head, so it needs no fence or counter.
+__global__ __launch_bounds__(1024) void k_argmax(const float* v, int n, int* out) {
+  float b = -INFINITY;
+  int ix = 0x7fffffff;
+  for (int i = threadIdx.x; i < n; i += 1024) {
+    const float x = v[i];
+    if (x > b) { b = x; ix = i; }          // ascending i: the first maximum stays
+  }
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ob = __shfl_xor(b, o, WAVE);
-        const int oi = __shfl_xor(ix, o, WAVE);
-        if (ob > b || (ob == b && oi < ix)) { b = ob; ix = oi; }
-      }
-      if (lane == 0) {
-        bv[wv] = b;
-        bi[wv] = ix;
-      }
-      __syncthreads();
-      if (threadIdx.x == 0) {
-        for (int i = 1; i < NW; ++i)
-          if (bv[i] > bv[0] || (bv[i] == bv[0] && bi[i] < bi[0])) { bv[0] = bv[i]; bi[0] = bi[i]; }
-        *p.tok = bi[0];
-        *p.done = 0;   // ready for the next launch
-      }
-    }
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ob = __shfl_xor(b, o, WAVE);
+    const int oi = __shfl_xor(ix, o, WAVE);
+    if (ob > b || (ob == b && oi < ix)) { b = ob; ix = oi; }
+  }
+  __shared__ float bv[16];
+  __shared__ int bi[16];
+  const int wv = threadIdx.x / WAVE;
+  if ((threadIdx.x & (WAVE - 1)) == 0) { bv[wv] = b; bi[wv] = ix; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int i = 1; i < 16; ++i)
+      if (bv[i] > b || (bv[i] == b && bi[i] < ix)) { b = bv[i]; ix = bi[i]; }
+    // no maximum (all NaN): report 0 rather than an index outside the vocabulary
+    *out = ix == 0x7fffffff ? 0 : ix;
   }
 }
 
@@ -243,7 +201,6 @@ static int launch_t(const GemvP& p, hipStream_t st) {
   const int NW = GEMV_THREADS / WAVE;
   int grid = (p.units + NW - 1) / NW;
   if (grid > max_blocks()) grid = max_blocks();
-  if (EPI == EPI_LOGITS && grid > 4096) grid = 4096;
   if (grid < 1) grid = 1;
   const size_t lds = size_t(p.K) * sizeof(float);
   constexpr int CH = Fmt<WT>::CH;
@@ -322,36 +279,25 @@ int launch_qkv(const QkvArgs& a, hipStream_t st) {
   p.base = L->rope_base;
   p.kc = L->k_cache;
   p.vc = L->v_cache;
-  p.zero_ptr = a.zero_ptr;
-  p.n_zero = a.zero_ptr ? a.n_zero : 0;
   set_rows(p, L->wdtype, L->d);
   return launch_wt<EPI_QKV, true>(L->wdtype, p, st);
 }
 
 size_t head_scratch(const lps_head_desc* h) {
   (void)h;
-  return align256(256) + align256(4096 * 4) * 2;
+  return 256;
 }
 
 int launch_head(const lps_head_desc* h, const float* x, float* logits, int32_t* tok, void* scratch,
                 size_t bytes, hipStream_t st) {
+  (void)scratch;
   (void)bytes;
-  GemvP p{};
-  p.w = static_cast<const uint8_t*>(h->w_lm);
-  p.N = h->vocab;
-  p.K = h->d;
-  p.x = x;
-  p.g = h->g_out;
-  p.eps = h->eps;
-  p.y = logits;
-  p.units = (h->vocab + 1) / 2;
-  char* sc = static_cast<char*>(scratch);
-  p.done = reinterpret_cast<int*>(sc);
-  p.pval = reinterpret_cast<float*>(sc + align256(256));
-  p.pidx = reinterpret_cast<int*>(sc + align256(256) + align256(4096 * 4));
-  p.tok = tok;
-  set_rows(p, h->wdtype, h->d);
-  return launch_wt<EPI_LOGITS, true>(h->wdtype, p, st);
+  int rc = launch_gemv(h->wdtype, h->w_lm, nullptr, h->vocab, h->d, x, h->g_out, h->eps, logits,
+                       EPI_STORE, st);
+  if (rc) return rc;
+  hipLaunchKernelGGL(k_argmax, dim3(1), dim3(1024), 0, st, logits, h->vocab, tok);
+  LPS_HIP(hipGetLastError());
+  return LPS_OK;
 }
 
 }  // namespace lps

@@ -135,14 +135,14 @@ static int layer_forward(const lps_layer_desc* L, float* x, int pos, void* scrat
   float* o = reinterpret_cast<float*>(sc + s.o);
   float* m = reinterpret_cast<float*>(sc + s.m);
   void* at = sc + s.attn;
-  QkvArgs qa{L, x, pos, q, reinterpret_cast<int*>(at), attn_counters(L->nkv)};
+  QkvArgs qa{L, x, pos, q};
   timer_begin(LPS_KIND_QKV, st);
   int rc = launch_qkv(qa, st);
   timer_end(LPS_KIND_QKV, st);
   if (rc) return rc;
   timer_begin(LPS_KIND_ATTN, st);
   rc = launch_attention(L->nq, L->nkv, L->hd, L->kvdtype, L->k_cache, L->v_cache, L->ctx_max,
-                        pos + 1, q, o, at, true, st);
+                        pos + 1, q, o, at, st);
   timer_end(LPS_KIND_ATTN, st);
   if (rc) return rc;
   timer_begin(LPS_KIND_OPROJ, st);
@@ -381,7 +381,7 @@ int lps_qkv_rope_append(const lps_layer_desc* L, const float* x, int32_t pos, fl
   LPS_REQUIRE(x && q && aligned16(x), LPS_EINVAL, "lps_qkv_rope_append: null or unaligned x / q");
   LPS_REQUIRE(pos >= 0 && pos < L->ctx_max, LPS_ERANGE,
               "lps_qkv_rope_append: pos %d outside [0, %d)", pos, L->ctx_max);
-  QkvArgs qa{L, x, pos, q, nullptr, 0};
+  QkvArgs qa{L, x, pos, q};
   return launch_qkv(qa, as_stream(stream));
 }
 
@@ -407,7 +407,7 @@ int lps_attention_decode(int32_t nq, int32_t nkv, int32_t hd, int32_t kvdtype, c
               "lps_attention_decode: scratch %zu < %zu", scratch_bytes,
               attn_scratch(nq, nkv, hd, ctx_max));
   return launch_attention(nq, nkv, hd, kvdtype, k_cache, v_cache, ctx_max, n_rows, q, o, scratch,
-                          false, as_stream(stream));
+                          as_stream(stream));
 }
 
 size_t lps_head_scratch_bytes(const lps_head_desc* h) { return h ? head_scratch(h) : 0; }

@@ -54,8 +54,6 @@ struct QkvArgs {
   const float* x;
   int pos;
   float* q;
-  int* zero_ptr;   // ints to clear before the attention kernel runs (may be null)
-  int n_zero;
 };
 int launch_gemv(int wdtype, const void* w, const uint8_t* s, int N, int K, const float* x,
                 const float* g, float eps, float* y, int mode, hipStream_t st);
@@ -65,10 +63,9 @@ int launch_head(const lps_head_desc* h, const float* x, float* logits, int32_t* 
 size_t head_scratch(const lps_head_desc* h);
 
 size_t attn_scratch(int nq, int nkv, int hd, int ctx_max);
-int attn_counters(int nkv);  // number of leading int counters in the attention scratch
 int launch_attention(int nq, int nkv, int hd, int kvdtype, const void* kc, const void* vc,
                      int ctx_max, int n_rows, const float* q, float* o, void* scratch,
-                     bool counters_zeroed, hipStream_t st);
+                     hipStream_t st);
 
 int launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t st);
 
