@@ -19,7 +19,6 @@ namespace lps {
 
 constexpr int ATT_THREADS = 256;
 constexpr int ATT_NW = ATT_THREADS / WAVE;
-constexpr int ATT_MAXG = 8;
 constexpr int ATT_CH = 64;  // cache rows per tile
 
 struct AttnP {
@@ -44,9 +43,8 @@ struct AttnCfg {
   static_assert(LPR <= WAVE && ATT_CH % RPP == 0, "unsupported head dim / cache dtype");
 };
 
-template <int KVT, int E16>
-__device__ __forceinline__ void load_row(const void* base, long long elem_off, float* out) {
-  const u32x4 v = ld16(static_cast<const char*>(base) + elem_off * (KVT == LPS_F32 ? 4 : 2));
+template <int KVT>
+__device__ __forceinline__ void widen16(const u32x4 v, float* out) {
   if constexpr (KVT == LPS_F32) {
     out[0] = __uint_as_float(v.x);
     out[1] = __uint_as_float(v.y);
@@ -64,45 +62,57 @@ __device__ __forceinline__ void load_row(const void* base, long long elem_off, f
   }
 }
 
-template <int HD, int KVT>
+template <int HD, int KVT, int G>
 __global__ __launch_bounds__(ATT_THREADS) void k_attn(AttnP p) {
   using C = AttnCfg<HD, KVT>;
   constexpr int E16 = C::E16, LPR = C::LPR, RPP = C::RPP;
-  __shared__ float qs[ATT_MAXG][HD];
-  __shared__ float sc[ATT_MAXG][ATT_CH];
-  __shared__ float red[ATT_NW][ATT_MAXG][HD];
+  constexpr int NP = ATT_CH / RPP;          // rows per thread
+  constexpr int ESZ = C::ESZ;
+  __shared__ float qs[G][HD];
+  __shared__ float sc[G][ATT_CH];
+  __shared__ float red[ATT_NW][G][HD];
 
   const int chunk = blockIdx.x, g = blockIdx.y;
-  const int G = p.G;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wv = tid / WAVE;
   const int li = tid % LPR, rr = tid / LPR;
   const int row0 = chunk * ATT_CH;
+  const long long head_base = (long long)g * p.ctx_max * HD;
 
+  // every K and V load of the tile goes out first: one HBM round trip
+  u32x4 kraw[NP], vraw[NP];
+#pragma unroll
+  for (int ps = 0; ps < NP; ++ps) {
+    const int j = row0 + ps * RPP + rr;
+    if (j < p.n) {
+      const long long off = (head_base + (long long)j * HD + li * E16) * ESZ;
+      kraw[ps] = ld16(static_cast<const char*>(p.kc) + off);
+      vraw[ps] = ld16(static_cast<const char*>(p.vc) + off);
+    } else {
+      kraw[ps] = vraw[ps] = u32x4{0, 0, 0, 0};
+    }
+  }
   for (int i = tid; i < G * HD; i += ATT_THREADS) qs[i / HD][i % HD] = p.q[(g * G) * HD + i];
   __syncthreads();
 
-  const long long head_base = (long long)g * p.ctx_max * HD;
   // ---- scores s[h][j] = q_h . k_j * scale ----
 #pragma unroll
-  for (int pass = 0; pass < ATT_CH / RPP; ++pass) {
-    const int jl = pass * RPP + rr;
+  for (int ps = 0; ps < NP; ++ps) {
+    const int jl = ps * RPP + rr;
     const int j = row0 + jl;
     float kv[E16];
-    if (j < p.n) {
-      load_row<KVT, E16>(p.kc, head_base + (long long)j * HD + li * E16, kv);
-    } else {
+    widen16<KVT>(kraw[ps], kv);
+    float s[G];
 #pragma unroll
-      for (int e = 0; e < E16; ++e) kv[e] = 0.f;
+    for (int h = 0; h < G; ++h) {
+      s[h] = 0.f;
+#pragma unroll
+      for (int e = 0; e < E16; ++e) s[h] = fmaf(kv[e], qs[h][li * E16 + e], s[h]);
     }
 #pragma unroll
-    for (int h = 0; h < ATT_MAXG; ++h) {
-      if (h < G) {
-        float s = 0.f;
+    for (int h = 0; h < G; ++h) s[h] = group_sum<LPR>(s[h]);
+    if (li == 0) {
 #pragma unroll
-        for (int e = 0; e < E16; ++e) s = fmaf(kv[e], qs[h][li * E16 + e], s);
-        s = group_sum<LPR>(s);
-        if (li == 0) sc[h][jl] = (j < p.n) ? s * p.scale : -INFINITY;
-      }
+      for (int h = 0; h < G; ++h) sc[h][jl] = (j < p.n) ? s[h] * p.scale : -INFINITY;
     }
   }
   __syncthreads();
@@ -121,47 +131,35 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attn(AttnP p) {
   }
   __syncthreads();
   // ---- o[h] = sum_j p[h][j] v_j ----
-  float acc[ATT_MAXG][E16];
+  float acc[G][E16];
 #pragma unroll
-  for (int h = 0; h < ATT_MAXG; ++h)
+  for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int e = 0; e < E16; ++e) acc[h][e] = 0.f;
 #pragma unroll
-  for (int pass = 0; pass < ATT_CH / RPP; ++pass) {
-    const int jl = pass * RPP + rr;
-    const int j = row0 + jl;
-    if (j < p.n) {
-      float vv[E16];
-      load_row<KVT, E16>(p.vc, head_base + (long long)j * HD + li * E16, vv);
+  for (int ps = 0; ps < NP; ++ps) {
+    const int jl = ps * RPP + rr;
+    float vv[E16];
+    widen16<KVT>(vraw[ps], vv);       // rows past n hold zeros and weight 0
 #pragma unroll
-      for (int h = 0; h < ATT_MAXG; ++h) {
-        if (h < G) {
-          const float w = sc[h][jl];
+    for (int h = 0; h < G; ++h) {
+      const float w = sc[h][jl];
 #pragma unroll
-          for (int e = 0; e < E16; ++e) acc[h][e] = fmaf(w, vv[e], acc[h][e]);
-        }
-      }
+      for (int e = 0; e < E16; ++e) acc[h][e] = fmaf(w, vv[e], acc[h][e]);
     }
   }
-  // rows of one wave: lanes li + LPR*r; sum over r by shuffles
+  // rows of one wave: lanes li + LPR*r; sum over r across lanes
+  if constexpr (LPR < WAVE) {
 #pragma unroll
-  for (int h = 0; h < ATT_MAXG; ++h) {
-    if (h < G) {
+    for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < E16; ++e) {
-        float v = acc[h][e];
-#pragma unroll
-        for (int o = LPR; o < WAVE; o <<= 1) v += __shfl_xor(v, o, WAVE);
-        acc[h][e] = v;
-      }
-    }
+      for (int e = 0; e < E16; ++e) acc[h][e] = strided_sum<LPR>(acc[h][e]);
   }
   if (lane < LPR) {
 #pragma unroll
-    for (int h = 0; h < ATT_MAXG; ++h)
-      if (h < G)
+    for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int e = 0; e < E16; ++e) red[wv][h][li * E16 + e] = acc[h][e];
+      for (int e = 0; e < E16; ++e) red[wv][h][li * E16 + e] = acc[h][e];
   }
   __syncthreads();
   const long long ob = ((long long)g * p.nch + chunk) * G * HD;
@@ -177,38 +175,68 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attn(AttnP p) {
 // Merge of the chunk partials of one q head, in chunk order: M = max m_c,
 // L = sum_c l_c e^(m_c - M), o = sum_c o_c e^(m_c - M) / L.  A separate launch:
 // the partials of all tiles are complete when it starts (stream order), so no
-// device-scope fence or counter is needed.
+// device-scope fence or counter is needed.  1024 threads per head: thread
+// (part, e) sums the chunks c = part (mod P) for element e, with all of its
+// loads in flight at once, and the P partial sums are added in part order.
+constexpr int MERGE_THREADS = 1024;
+constexpr int MERGE_CH = 1024;   // chunk weights staged in LDS per round
+
 template <int HD>
-__global__ __launch_bounds__(HD) void k_attn_merge(AttnP p) {
+__global__ __launch_bounds__(MERGE_THREADS) void k_attn_merge(AttnP p) {
+  constexpr int P = MERGE_THREADS / HD;
+  constexpr int NWM = MERGE_THREADS / WAVE;
   const int hq = blockIdx.x;               // q head
   const int g = hq / p.G, h = hq - g * p.G;
-  const int e = threadIdx.x;
-  __shared__ float wsh[1024];               // e^(m_c - M) per chunk, chunk-tiled
+  const int t = threadIdx.x, e = t % HD, part = t / HD;
+  __shared__ float wsh[MERGE_CH];
+  __shared__ float red[NWM];
+  __shared__ float opart[P][HD];
+  const long long base = (long long)g * p.nch;
   float M = -INFINITY;
-  for (int c = e; c < p.nch; c += HD) M = fmaxf(M, p.pm[((long long)g * p.nch + c) * p.G + h]);
-  // block max over the per-thread maxima (HD threads)
-  __shared__ float red[HD / WAVE];
+  for (int c = t; c < p.nch; c += MERGE_THREADS) M = fmaxf(M, p.pm[(base + c) * p.G + h]);
   M = wave_max(M);
-  if ((e & (WAVE - 1)) == 0) red[e / WAVE] = M;
+  if ((t & (WAVE - 1)) == 0) red[t / WAVE] = M;
   __syncthreads();
   M = red[0];
 #pragma unroll
-  for (int i = 1; i < HD / WAVE; ++i) M = fmaxf(M, red[i]);
-  float L = 0.f, O = 0.f;
-  for (int c0 = 0; c0 < p.nch; c0 += 1024) {
-    const int n = min(1024, p.nch - c0);
+  for (int i = 1; i < NWM; ++i) M = fmaxf(M, red[i]);
+  float Lp = 0.f, O = 0.f;
+  const long long step = (long long)p.G * HD;
+  for (int c0 = 0; c0 < p.nch; c0 += MERGE_CH) {
+    const int n = min(MERGE_CH, p.nch - c0);
     __syncthreads();
-    for (int c = e; c < n; c += HD)
-      wsh[c] = expf(p.pm[((long long)g * p.nch + c0 + c) * p.G + h] - M);
-    __syncthreads();
-    for (int c = 0; c < n; ++c) {
-      const long long pi = ((long long)g * p.nch + c0 + c) * p.G + h;
-      const float w = wsh[c];
-      L = fmaf(w, p.pl[pi], L);
-      O = fmaf(w, p.po[pi * HD + e], O);
+    for (int c = t; c < n; c += MERGE_THREADS) {
+      const long long pi = (base + c0 + c) * p.G + h;
+      const float w = expf(p.pm[pi] - M);
+      wsh[c] = w;
+      Lp = fmaf(w, p.pl[pi], Lp);
     }
+    __syncthreads();
+    const float* po = p.po + ((base + c0) * p.G + h) * HD + e;
+    int c = part;
+    for (; c + 7 * P < n; c += 8 * P) {
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = po[(c + k * P) * step];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) O = fmaf(wsh[c + k * P], v[k], O);
+    }
+    for (; c < n; c += P) O = fmaf(wsh[c], po[c * step], O);
   }
-  p.o[(long long)hq * HD + e] = O / L;
+  opart[part][e] = O;
+  __syncthreads();
+  Lp = wave_sum(Lp);
+  if ((t & (WAVE - 1)) == 0) red[t / WAVE] = Lp;
+  __syncthreads();
+  if (t < HD) {
+    float L = 0.f;
+#pragma unroll
+    for (int i = 0; i < NWM; ++i) L += red[i];
+    float o = opart[0][e];
+#pragma unroll
+    for (int q = 1; q < P; ++q) o += opart[q][e];
+    p.o[(long long)hq * HD + e] = o / L;
+  }
 }
 
 static int nchunks(int rows) { return (rows + ATT_CH - 1) / ATT_CH; }
@@ -220,9 +248,18 @@ size_t attn_scratch(int nq, int nkv, int hd, int ctx_max) {
 }
 
 template <int HD, int KVT>
-static void go(const AttnP& p, int nkv, hipStream_t st) {
-  hipLaunchKernelGGL((k_attn<HD, KVT>), dim3(p.nch, nkv), dim3(ATT_THREADS), 0, st, p);
-  hipLaunchKernelGGL((k_attn_merge<HD>), dim3(nkv * p.G), dim3(HD), 0, st, p);
+static int go(const AttnP& p, int nkv, hipStream_t st) {
+  const dim3 grid(p.nch, nkv), blk(ATT_THREADS);
+  switch (p.G) {
+    case 1: hipLaunchKernelGGL((k_attn<HD, KVT, 1>), grid, blk, 0, st, p); break;
+    case 2: hipLaunchKernelGGL((k_attn<HD, KVT, 2>), grid, blk, 0, st, p); break;
+    case 4: hipLaunchKernelGGL((k_attn<HD, KVT, 4>), grid, blk, 0, st, p); break;
+    case 6: hipLaunchKernelGGL((k_attn<HD, KVT, 6>), grid, blk, 0, st, p); break;
+    case 8: hipLaunchKernelGGL((k_attn<HD, KVT, 8>), grid, blk, 0, st, p); break;
+    default: return fail(LPS_EUNSUP, "attention: %d q heads per kv head not built (1, 2, 4, 6, 8)", p.G);
+  }
+  hipLaunchKernelGGL((k_attn_merge<HD>), dim3(nkv * p.G), dim3(MERGE_THREADS), 0, st, p);
+  return LPS_OK;
 }
 
 int launch_attention(int nq, int nkv, int hd, int kvdtype, const void* kc, const void* vc,
@@ -246,12 +283,14 @@ int launch_attention(int nq, int nkv, int hd, int kvdtype, const void* kc, const
   s += align256(size_t(nkv) * nch_max * p.G * 4);
   p.po = reinterpret_cast<float*>(s);
   const bool f32 = kvdtype == LPS_F32;
+  int rc;
   switch (hd) {
-    case 64: f32 ? go<64, LPS_F32>(p, nkv, st) : go<64, LPS_BF16>(p, nkv, st); break;
-    case 128: f32 ? go<128, LPS_F32>(p, nkv, st) : go<128, LPS_BF16>(p, nkv, st); break;
-    case 256: f32 ? go<256, LPS_F32>(p, nkv, st) : go<256, LPS_BF16>(p, nkv, st); break;
+    case 64: rc = f32 ? go<64, LPS_F32>(p, nkv, st) : go<64, LPS_BF16>(p, nkv, st); break;
+    case 128: rc = f32 ? go<128, LPS_F32>(p, nkv, st) : go<128, LPS_BF16>(p, nkv, st); break;
+    case 256: rc = f32 ? go<256, LPS_F32>(p, nkv, st) : go<256, LPS_BF16>(p, nkv, st); break;
     default: return fail(LPS_EUNSUP, "attention: head dim %d not built (64, 128, 256)", hd);
   }
+  if (rc) return rc;
   LPS_HIP(hipGetLastError());
   return LPS_OK;
 }

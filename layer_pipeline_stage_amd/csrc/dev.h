@@ -34,23 +34,62 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return uint16_t(u >> 16);
 }
 
-// Sum over the 64 lanes of a wave; every lane receives the same total (the
-// butterfly applies one fixed tree, and a + b == b + a exactly).
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
-  return v;
+// Cross-lane steps.  Inside a 16-lane row: DPP permutations (a VALU operand
+// modifier, no LDS).  Across rows: DPP row broadcasts for whole-wave totals, and
+// LDS-crossbar shuffles (ds_bpermute) where every lane needs its own partner.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp(float v, float old = 0.f) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                                               __builtin_bit_cast(int, v), CTRL,
+                                                               ROW_MASK, 0xF, false));
 }
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
-  return v;
+constexpr int DPP_XOR1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141; // lane i <-> 7 - i within 8
+constexpr int DPP_MIRROR = 0x140;      // lane i <-> 15 - i within 16
+constexpr int DPP_ROR8 = 0x128;        // lane i <- (i + 8) % 16, i.e. i ^ 8
+constexpr int DPP_BCAST15 = 0x142;     // rows 1, 3 <- lane 15 of rows 0, 2
+constexpr int DPP_BCAST31 = 0x143;     // rows 2, 3 <- lane 31
+
+__device__ __forceinline__ float lane63(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
-// Sum over aligned groups of `width` lanes (width a power of two <= 64).
+
+// Sum over aligned groups of W lanes (W a power of two <= 64).  Every lane of a
+// group receives the same total: each step adds two partial sums that are
+// equal on both partner lanes, and a + b == b + a exactly, so one fixed tree.
 template <int W>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  if constexpr (W >= 2) v += dpp<DPP_XOR1>(v);
+  if constexpr (W >= 4) v += dpp<DPP_XOR2>(v);
+  if constexpr (W >= 8) v += dpp<DPP_HALF_MIRROR>(v);
+  if constexpr (W >= 16) v += dpp<DPP_MIRROR>(v);
+  if constexpr (W == 32) v += __shfl_xor(v, 16, WAVE);
+  if constexpr (W == 64) {
+    // row sums -> rows 1, 3 hold S0 + S1, S2 + S3 -> row 3 holds the total
+    v += dpp<DPP_BCAST15, 0xA>(v);
+    v += dpp<DPP_BCAST31, 0xC>(v);
+    v = lane63(v);
+  }
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp<DPP_XOR1>(v));
+  v = fmaxf(v, dpp<DPP_XOR2>(v));
+  v = fmaxf(v, dpp<DPP_HALF_MIRROR>(v));
+  v = fmaxf(v, dpp<DPP_MIRROR>(v));
+  v = fmaxf(v, dpp<DPP_BCAST15, 0xA>(v, v));   // rows left unwritten keep their own value
+  v = fmaxf(v, dpp<DPP_BCAST31, 0xC>(v, v));
+  return lane63(v);
+}
+// Sum over the lanes l, l + S, l + 2S, ... (S a power of two >= 8): the
+// per-row partial sums of lanes that own the same columns.
+template <int S>
+__device__ __forceinline__ float strided_sum(float v) {
+  if constexpr (S <= 8) v += dpp<DPP_ROR8>(v);
+  if constexpr (S <= 16) v += __shfl_xor(v, 16, WAVE);
+  if constexpr (S <= 32) v += __shfl_xor(v, 32, WAVE);
   return v;
 }
 

@@ -41,9 +41,10 @@ struct GemvP {
   float* y;
   // QKV epilogue
   int nq, nkv, hd, pos, ctx_max, kvdtype;
-  float base;
   void* kc;
   void* vc;
+  // cos / sin of pos * base^(-2i/hd) for i < hd/2, formed on the host in double
+  float rope[2 * 128];
 };
 
 template <int EPI>
@@ -84,12 +85,9 @@ __device__ __forceinline__ void epilogue(const GemvP& p, int u, int r0, int r1, 
     const int hh = u / half, i = u - hh * half;
     float o0 = a0, o1 = a1;
     if (hh < p.nq + p.nkv) {
-      const double theta = pow(double(p.base), -2.0 * double(i) / double(p.hd));
-      const double ang = double(p.pos) * theta;
-      double sn, cs;
-      sincos(ang, &sn, &cs);
-      o0 = float(double(a0) * cs - double(a1) * sn);
-      o1 = float(double(a0) * sn + double(a1) * cs);
+      const float cs = p.rope[2 * i], sn = p.rope[2 * i + 1];
+      o0 = a0 * cs - a1 * sn;
+      o1 = a0 * sn + a1 * cs;
     }
     if (hh < p.nq) {
       p.y[r0] = o0;
@@ -110,9 +108,9 @@ __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(GemvP p) {
   extern __shared__ float xs[];
   stage_x<NORM>(p.x, p.g, p.eps, p.K, xs);
   constexpr int CH = Fmt<WT>::CH;
+  constexpr int NW = GEMV_THREADS / WAVE;
   const int lane = threadIdx.x & (WAVE - 1);
   const int wv = threadIdx.x / WAVE;
-  constexpr int NW = GEMV_THREADS / WAVE;
   const int nck = p.K / CH;
   for (int u = blockIdx.x * NW + wv; u < p.units; u += gridDim.x * NW) {
     int r0, r1;
@@ -205,8 +203,9 @@ static int launch_t(const GemvP& p, hipStream_t st) {
   const size_t lds = size_t(p.K) * sizeof(float);
   constexpr int CH = Fmt<WT>::CH;
   const int per_lane = (p.K / CH + WAVE - 1) / WAVE;
-  // keep up to 8 chunk loads per row in flight per lane
-  if (per_lane <= 4) {
+  // keep up to 8 (bf16 / f32) or 4 (MXFP4, whose decode needs more registers)
+  // chunk loads per row in flight per lane
+  if (per_lane <= 4 || WT == LPS_MXFP4) {
     int rc = ensure_lds((const void*)k_gemv<WT, EPI, 4, NORM>, lds);
     if (rc) return rc;
     hipLaunchKernelGGL((k_gemv<WT, EPI, 4, NORM>), dim3(grid), dim3(GEMV_THREADS), lds, st, p);
@@ -276,7 +275,14 @@ int launch_qkv(const QkvArgs& a, hipStream_t st) {
   p.pos = a.pos;
   p.ctx_max = L->ctx_max;
   p.kvdtype = L->kvdtype;
-  p.base = L->rope_base;
+  // the rotation angle pos * theta_i reaches ~1e4 rad: form it and its cos / sin
+  // in double, once per launch, and hand the f32 values to every block
+  for (int i = 0; i < L->hd / 2; ++i) {
+    const double theta = std::pow(double(L->rope_base), -2.0 * double(i) / double(L->hd));
+    const double ang = double(a.pos) * theta;
+    p.rope[2 * i] = float(std::cos(ang));
+    p.rope[2 * i + 1] = float(std::sin(ang));
+  }
   p.kc = L->k_cache;
   p.vc = L->v_cache;
   set_rows(p, L->wdtype, L->d);

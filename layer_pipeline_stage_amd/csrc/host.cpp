@@ -80,15 +80,17 @@ static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 static int chunk_of(int wdtype) { return wdtype == LPS_F32 ? 4 : wdtype == LPS_BF16 ? 8 : 32; }
 
+// q heads per kv head that the attention kernel is instantiated for
+static bool gqa_built(int g) { return g == 1 || g == 2 || g == 4 || g == 6 || g == 8; }
+
 int check_layer(const lps_layer_desc* L, const char* who) {
   LPS_REQUIRE(L, LPS_EINVAL, "%s: null layer descriptor", who);
   LPS_REQUIRE(L->d > 0 && L->nq > 0 && L->nkv > 0 && L->hd > 0 && L->ff > 0, LPS_EINVAL,
               "%s: d/nq/nkv/hd/ff must be > 0 (got %d/%d/%d/%d/%d)", who, L->d, L->nq, L->nkv,
               L->hd, L->ff);
-  LPS_REQUIRE(L->nq % L->nkv == 0 && L->nq / L->nkv <= 8, LPS_EUNSUP,
-              "%s: nq %d must be a multiple of nkv %d with at most 8 q heads per kv head", who,
+  LPS_REQUIRE(L->nq % L->nkv == 0 && gqa_built(L->nq / L->nkv), LPS_EUNSUP, "%s: nq / nkv = %d/%d: 1, 2, 4, 6 or 8 q heads per kv head are built", who,
               L->nq, L->nkv);
-  LPS_REQUIRE(L->hd == 64 || L->hd == 128 || L->hd == 256, LPS_EUNSUP,
+  LPS_REQUIRE(L->hd == 64 || L->hd == 128 || L->hd == 256, LPS_EUNSUP,  // RoPE table: hd/2 <= 128
               "%s: head dim %d not built (64, 128, 256)", who, L->hd);
   LPS_REQUIRE(L->wdtype == LPS_F32 || L->wdtype == LPS_BF16 || L->wdtype == LPS_MXFP4, LPS_EINVAL,
               "%s: wdtype %d", who, L->wdtype);
@@ -393,8 +395,8 @@ size_t lps_attention_scratch_bytes(int32_t nq, int32_t nkv, int32_t hd, int32_t 
 int lps_attention_decode(int32_t nq, int32_t nkv, int32_t hd, int32_t kvdtype, const void* k_cache,
                          const void* v_cache, int32_t ctx_max, int32_t n_rows, const float* q,
                          float* o, void* scratch, size_t scratch_bytes, void* stream) {
-  LPS_REQUIRE(nq > 0 && nkv > 0 && nq % nkv == 0 && nq / nkv <= 8, LPS_EUNSUP,
-              "lps_attention_decode: nq %d / nkv %d (nq %% nkv == 0, at most 8 per group)", nq, nkv);
+  LPS_REQUIRE(nq > 0 && nkv > 0 && nq % nkv == 0, LPS_EUNSUP,
+              "lps_attention_decode: nq %d must be a multiple of nkv %d", nq, nkv);
   LPS_REQUIRE(hd == 64 || hd == 128 || hd == 256, LPS_EUNSUP, "lps_attention_decode: head dim %d", hd);
   LPS_REQUIRE(kvdtype == LPS_F32 || kvdtype == LPS_BF16, LPS_EINVAL, "lps_attention_decode: kvdtype %d",
               kvdtype);
