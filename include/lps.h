@@ -265,6 +265,21 @@ int lps_moe_combine(float* out, const float* x, const float* shared, const float
 /* f32 -> f16 bits (round to nearest even) of n values: the remote half's
  * "sums_to_f16" step (strata PR #3648, Approach: sums). */
 int lps_f32_to_f16(const float* src, uint16_t* dst, int64_t n, void* stream);
+/* A13: one whole MoE layer over a prefill chunk of T tokens; x (dev [T, d] f32)
+ * is updated in place.  Route (as above) per token; group the (token, expert)
+ * pairs per expert in token order (a stable counting sort); run the experts as
+ * grouped GEMMs on the bf16 matrix cores: the normed rows and the SwiGLU output
+ * are rounded to bf16 as matrix inputs, accumulation is f32; the shared expert
+ * is one more group over all T rows; per token, the gate-weighted expert terms
+ * are added in ascending expert id within each half, the remote half rounded to
+ * f16 and widened back in n_pieces pieces on s_remote, and x += (shared + local)
+ * + remote (lps_moe_combine).  Built for n_experts <= 64, top_k <= 16, d a
+ * multiple of 128, ff a multiple of 64.  scratch (dev) of
+ * lps_moe_prefill_scratch_bytes(m, T) bytes; its contents on entry do not
+ * matter.  Work is enqueued on s_main (and the pieces on s_remote). */
+size_t lps_moe_prefill_scratch_bytes(const lps_moe_desc* m, int32_t T);
+int lps_moe_prefill(const lps_moe_desc* m, float* x, int32_t T, int32_t n_pieces, void* scratch,
+                    size_t scratch_bytes, void* s_main, void* s_remote);
 /* One whole MoE layer for one token (decode): x (dev [d]) updated in place. */
 size_t lps_moe_layer_scratch_bytes(const lps_moe_desc* m);
 int lps_moe_layer_decode(const lps_moe_desc* m, float* x, void* scratch, size_t scratch_bytes,

@@ -96,6 +96,8 @@ SIGS = {
     "lps_moe_route": (C.c_int, [C.POINTER(MoEDesc), P, I32, P, P, P, SZ, P], True),
     "lps_moe_combine": (C.c_int, [P, P, P, P, P, P, I32, I32, I32, P, P], True),
     "lps_f32_to_f16": (C.c_int, [P, P, I64, P], True),
+    "lps_moe_prefill_scratch_bytes": (SZ, [C.POINTER(MoEDesc), I32], False),
+    "lps_moe_prefill": (C.c_int, [C.POINTER(MoEDesc), P, I32, I32, P, SZ, P, P], True),
     "lps_moe_layer_scratch_bytes": (SZ, [C.POINTER(MoEDesc)], False),
     "lps_moe_layer_decode": (C.c_int, [C.POINTER(MoEDesc), P, P, SZ, P], True),
     "lps_counters": (C.c_int, [C.POINTER(Counters)], True),

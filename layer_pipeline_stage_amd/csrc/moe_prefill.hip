@@ -1,0 +1,471 @@
+// MoE FFN layer over a prefill chunk of T tokens on gfx950.
+//
+// strata PR #3648 (Problem and result; Approach): every MoE layer of a prompt
+// chunk routes its tokens, groups them per expert, runs the experts, and
+// combines per-token sums where one half of the experts returns FP16 sums in
+// pieces, converted exactly and added in a fixed order.  Here all experts run
+// on one GPU: the expert matmuls are grouped GEMMs on the bf16 matrix cores.
+//
+// Steps (each its own launch, in stream order, so no kernel waits on another):
+//  1. route: per 8-token tile, RMSNorm rows (f32), bf16 copy of the normed rows
+//     for the expert GEMMs, router logits from the f32 rows (the same lane /
+//     chunk split as the decode router), softmax, top-k by logit with ties to
+//     the lower id, weights renormalised over the k.
+//  2. group: per expert, the tokens that selected it, in token order (a stable
+//     counting sort: each expert's list is a compaction of the token sequence).
+//  3. tiles: per-expert offsets and the list of 128-row tiles (experts in
+//     ascending id, then the shared expert over all tokens).
+//  4. GEMM1: [rows x d] x [d x 2ff] on MFMA 32x32x16 bf16 -> f32; the gate and
+//     up columns of one output sit in the same lanes, so SwiGLU is applied in
+//     registers; the product is rounded to bf16 for GEMM2.
+//  5. GEMM2: [rows x ff] x [ff x d] -> f32, scaled by the token's gate weight
+//     and written to the token's slot (the shared expert to its own buffer).
+//  6. halves: per token, the selected experts' terms in ascending expert id:
+//     local (f32) and remote, the latter rounded to f16.
+//  7. combine (lps_moe_combine): the f16 sums widened piece by piece on the
+//     second stream, then x += (shared + local) + remote.
+#include "dev.h"
+#include "gemv_core.h"
+#include "internal.h"
+
+#include <cmath>
+
+namespace lps {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int PF_TOK = 8;      // tokens per routing tile
+constexpr int PF_MAXE = 64;    // experts the tile router is built for
+constexpr int PF_MAXK = 16;
+constexpr int GM = 128, GN = 128, GK = 32, GKP = GK + 8;  // GEMM tile; LDS row pad
+
+struct PfP {
+  const float* x;        // [T, d] residual
+  const float* g;
+  float eps;
+  const uint16_t* wr;    // [E, d]
+  const uint16_t* w_gu_e;
+  const uint16_t* w_d_e;
+  const uint16_t* w_gu_s;
+  const uint16_t* w_d_s;
+  int T, d, E, k, ff, remote_from;
+  uint16_t* xb;          // [T, d] bf16 normed rows
+  int32_t* idx;          // [T, k]
+  float* w;              // [T, k]
+  int32_t* cnt;          // [E + 1]
+  int32_t* off;          // [E + 1]
+  int32_t* lst;          // [E, T] tokens per expert
+  int32_t* lslot;        // [E, T] slot of the expert in the token's top-k
+  float* lw;             // [E, T] gate weight
+  int32_t* tiles;        // [max_tiles] packed (expert << 20) | m0
+  int32_t* n_tiles;      // [1]
+  uint16_t* act;         // [T*k + T, ff] bf16 SwiGLU outputs, rows by (off[e] + i)
+  float* z;              // [T, k, d] weighted expert outputs by slot
+  float* shared;         // [T, d]
+  float* local;          // [T, d]
+  uint16_t* remote16;    // [T, d]
+};
+
+__device__ __forceinline__ uint16_t bf16_rne(float f) { return f32_to_bf16(f); }
+
+// ---- 1. route ------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_pf_route(PfP p) {
+  extern __shared__ float hs[];            // [PF_TOK][d] normed rows (f32)
+  __shared__ float lg[PF_TOK][PF_MAXE];
+  const int t0 = blockIdx.x * PF_TOK;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x / 64;
+  const int d = p.d;
+  // each wave normalises two rows
+  for (int q = 0; q < 2; ++q) {
+    const int r = wv * 2 + q, t = t0 + r;
+    float* h = hs + r * d;
+    if (t < p.T) {
+      const float* xr = p.x + (long long)t * d;
+      float ss = 0.f;
+      for (int c = lane * 4; c < d; c += 256) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(xr + c);
+        *reinterpret_cast<f32x4*>(h + c) = v;
+        ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+      }
+      ss = wave_sum(ss);
+      const float rinv = 1.0f / sqrtf(ss / float(d) + p.eps);
+      for (int c = lane * 4; c < d; c += 256) {
+        f32x4 v = *reinterpret_cast<f32x4*>(h + c);
+        const f32x4 gg = *reinterpret_cast<const f32x4*>(p.g + c);
+        v.x = v.x * rinv * gg.x;
+        v.y = v.y * rinv * gg.y;
+        v.z = v.z * rinv * gg.z;
+        v.w = v.w * rinv * gg.w;
+        *reinterpret_cast<f32x4*>(h + c) = v;
+        const uint32_t lo = uint32_t(bf16_rne(v.x)) | (uint32_t(bf16_rne(v.y)) << 16);
+        const uint32_t hi = uint32_t(bf16_rne(v.z)) | (uint32_t(bf16_rne(v.w)) << 16);
+        *reinterpret_cast<uint2*>(p.xb + (long long)t * d + c) = make_uint2(lo, hi);
+      }
+    } else {
+      for (int c = lane * 4; c < d; c += 256) *reinterpret_cast<f32x4*>(h + c) = f32x4{0, 0, 0, 0};
+    }
+  }
+  __syncthreads();
+  // router logits: wave wv takes experts wv, wv + 4, ...; the lane / chunk split of
+  // a row is the decode router's (chunk c of 8 values on lane c % 64)
+  const int nck = d / 8;
+  for (int e = wv; e < p.E; e += 4) {
+    float a[PF_TOK];
+#pragma unroll
+    for (int r = 0; r < PF_TOK; ++r) a[r] = 0.f;
+    const uint16_t* row = p.wr + (long long)e * d;
+    for (int c = lane; c < nck; c += 64) {
+      const u32x4 v = ld16(row + (long long)c * 8);
+#pragma unroll
+      for (int r = 0; r < PF_TOK; ++r) acc_chunk<LPS_BF16>(v, 0, hs + r * d + c * 8, a[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < PF_TOK; ++r) {
+      const float s = wave_sum(a[r]);
+      if (lane == 0) lg[r][e] = s;
+    }
+  }
+  __syncthreads();
+  // top-k: wave wv selects for tokens 2wv, 2wv + 1; lane = expert id
+  for (int q = 0; q < 2; ++q) {
+    const int r = wv * 2 + q, t = t0 + r;
+    if (t >= p.T) continue;
+    float v = lane < p.E ? lg[r][lane] : -INFINITY;
+    const float m = wave_max(v);
+    const float z = wave_sum(lane < p.E ? expf(v - m) : 0.f);
+    float ssum = 0.f;
+    float pis = 0.f;   // this lane's selected pi, if selected
+    int slot = -1;
+    for (int j = 0; j < p.k; ++j) {
+      const float mx = wave_max(v);
+      const unsigned long long msk = __ballot(v == mx && lane < p.E);
+      const int sel = msk ? __ffsll((long long)msk) - 1 : j;     // no finite logit: slot id
+      const float pi = msk ? expf(mx - m) / z : __uint_as_float(0x7FC00000u);
+      if (lane == sel) {
+        v = -INFINITY;
+        pis = pi;
+        slot = j;
+      }
+      ssum += pi;
+      if (lane == 0) p.idx[(long long)t * p.k + j] = sel;
+    }
+    if (slot >= 0) p.w[(long long)t * p.k + slot] = pis / ssum;
+  }
+}
+
+// ---- 2. group: stable per-expert token lists ------------------------------------------
+__global__ __launch_bounds__(256) void k_pf_group(PfP p) {
+  const int e = blockIdx.x;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x / 64;
+  __shared__ int wtot[4];
+  int base = 0;
+  for (int t0 = 0; t0 < p.T; t0 += 256) {
+    const int t = t0 + threadIdx.x;
+    int slot = -1;
+    if (t < p.T)
+      for (int j = 0; j < p.k; ++j)
+        if (p.idx[(long long)t * p.k + j] == e) { slot = j; break; }
+    const unsigned long long msk = __ballot(slot >= 0);
+    const int before = __popcll(msk & ((1ull << lane) - 1ull));
+    if (lane == 0) wtot[wv] = __popcll(msk);
+    __syncthreads();
+    int wbase = 0;
+    for (int i = 0; i < wv; ++i) wbase += wtot[i];
+    if (slot >= 0) {
+      const long long pos = (long long)e * p.T + base + wbase + before;
+      p.lst[pos] = t;
+      p.lslot[pos] = slot;
+      p.lw[pos] = p.w[(long long)t * p.k + slot];
+    }
+    base += wtot[0] + wtot[1] + wtot[2] + wtot[3];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) p.cnt[e] = base;
+}
+
+// ---- 3. tiles ----------------------------------------------------------------------
+__global__ void k_pf_tiles(PfP p) {
+  if (threadIdx.x != 0) return;
+  int off = 0, n = 0;
+  for (int e = 0; e <= p.E; ++e) {
+    const int c = e < p.E ? p.cnt[e] : p.T;   // the shared expert takes every token
+    p.off[e] = off;
+    if (e == p.E) p.cnt[e] = c;
+    for (int m0 = 0; m0 < c; m0 += GM) p.tiles[n++] = (e << 20) | m0;
+    off += c;
+  }
+  *p.n_tiles = n;
+}
+
+// ---- 4/5. grouped GEMM on MFMA -----------------------------------------------------------
+// C[m, n] = sum_k A[m, k] B[n, k]: A rows are gathered activation rows (bf16),
+// B rows are weight rows (bf16, K contiguous).  128 x 128 tile, 4 waves of 64 x 64
+// (2 x 2 MFMA 32x32x16), K in steps of 32 through double-buffered LDS.
+template <bool FIRST>
+__global__ __launch_bounds__(256) void k_pf_gemm(PfP p) {
+  const int tile = blockIdx.y;
+  if (tile >= *p.n_tiles) return;
+  const int packed = p.tiles[tile];
+  const int e = packed >> 20, m0 = packed & 0xFFFFF;
+  const bool shared_e = e == p.E;
+  const int cnt = p.cnt[e];
+  const int K = FIRST ? p.d : p.ff;
+  const int n0 = FIRST ? blockIdx.x * 64 : blockIdx.x * GN;
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][GM][GKP];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][GN][GKP];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid / 64;
+  const int wm = wv >> 1, wn = wv & 1;
+  // the two 16-byte chunks this thread stages per K step: row c / 4, column 8 (c % 4)
+  const uint16_t* arow[2];
+  const uint16_t* brow[2];
+  int srow[2], scol[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = tid + 256 * i;
+    srow[i] = c >> 2;
+    scol[i] = (c & 3) * 8;
+    const int r = m0 + srow[i];
+    const int rr = r < cnt ? r : m0;          // rows past the list repeat a valid row
+    if (FIRST) {
+      const int tok = shared_e ? rr : p.lst[(long long)e * p.T + rr];
+      arow[i] = p.xb + (long long)tok * p.d;
+    } else {
+      arow[i] = p.act + (long long)(p.off[e] + rr) * p.ff;
+    }
+    const int br = srow[i];
+    long long wrow;
+    const uint16_t* wbase;
+    if (FIRST) {
+      // B rows of wave column wn: 32 gate rows then 32 up rows
+      const int wcol = br >> 6, jj = (br >> 5) & 1, cc = br & 31;
+      wrow = (long long)(jj ? p.ff : 0) + n0 + 32 * wcol + cc;
+      wbase = shared_e ? p.w_gu_s : p.w_gu_e + (long long)e * 2 * p.ff * p.d;
+    } else {
+      wrow = n0 + br;
+      wbase = shared_e ? p.w_d_s : p.w_d_e + (long long)e * p.d * p.ff;
+    }
+    brow[i] = wbase + wrow * K;
+  }
+  u32x4 ra[2], rb[2];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      ra[i] = ld16(arow[i] + k0 + scol[i]);
+      rb[i] = ld_stream16(brow[i] + k0 + scol[i]);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      *reinterpret_cast<u32x4*>(&As[buf][srow[i]][scol[i]]) = ra[i];
+      *reinterpret_cast<u32x4*>(&Bs[buf][srow[i]][scol[i]]) = rb[i];
+    }
+  };
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = K / GK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * GK);
+#pragma unroll
+    for (int ks = 0; ks < GK / 16; ++ks) {
+      bf16x8 a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        a[i] = *reinterpret_cast<const bf16x8*>(&As[buf][64 * wm + 32 * i + (lane & 31)][16 * ks + 8 * (lane >> 5)]);
+        b[i] = *reinterpret_cast<const bf16x8*>(&Bs[buf][64 * wn + 32 * i + (lane & 31)][16 * ks + 8 * (lane >> 5)]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) {
+      sstore(buf ^ 1);
+      __syncthreads();
+    }
+  }
+  // epilogue: acc[i][j][r] is C[64 wm + 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4][64 wn + 32 j + lane % 32]
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      const int m = m0 + row;
+      if (m >= cnt) continue;
+      if (FIRST) {
+        const float gt = acc[i][0][r], up = acc[i][1][r];
+        const int col = n0 + 32 * wn + (lane & 31);
+        p.act[(long long)(p.off[e] + m) * p.ff + col] = bf16_rne(silu(gt) * up);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int col = n0 + 64 * wn + 32 * j + (lane & 31);
+          if (shared_e) {
+            p.shared[(long long)m * p.d + col] = acc[i][j][r];
+          } else {
+            const long long li = (long long)e * p.T + m;
+            const int t = p.lst[li];
+            p.z[((long long)t * p.k + p.lslot[li]) * p.d + col] = p.lw[li] * acc[i][j][r];
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---- 6. per-token halves in ascending expert id -------------------------------------------
+__global__ __launch_bounds__(256) void k_pf_halves(PfP p) {
+  const int t = blockIdx.x;
+  __shared__ int ids[PF_MAXK];
+  __shared__ int order[PF_MAXK];
+  if (threadIdx.x < p.k) ids[threadIdx.x] = p.idx[(long long)t * p.k + threadIdx.x];
+  __syncthreads();
+  if (threadIdx.x < p.k) {
+    int rank = 0;
+    for (int j = 0; j < p.k; ++j)
+      rank += ids[j] < ids[threadIdx.x] || (ids[j] == ids[threadIdx.x] && j < int(threadIdx.x));
+    order[rank] = threadIdx.x;
+  }
+  __syncthreads();
+  for (int c = threadIdx.x * 4; c < p.d; c += 256 * 4) {
+    f32x4 lo = {0, 0, 0, 0}, re = {0, 0, 0, 0};
+    for (int n = 0; n < p.k; ++n) {
+      const int j = order[n];
+      const f32x4 v = *reinterpret_cast<const f32x4*>(p.z + ((long long)t * p.k + j) * p.d + c);
+      if (ids[j] < p.remote_from) {
+        lo.x += v.x; lo.y += v.y; lo.z += v.z; lo.w += v.w;
+      } else {
+        re.x += v.x; re.y += v.y; re.z += v.z; re.w += v.w;
+      }
+    }
+    *reinterpret_cast<f32x4*>(p.local + (long long)t * p.d + c) = lo;
+    const _Float16 h0 = static_cast<_Float16>(re.x), h1 = static_cast<_Float16>(re.y);
+    const _Float16 h2 = static_cast<_Float16>(re.z), h3 = static_cast<_Float16>(re.w);
+    const uint32_t a = uint32_t(__builtin_bit_cast(uint16_t, h0)) | (uint32_t(__builtin_bit_cast(uint16_t, h1)) << 16);
+    const uint32_t b = uint32_t(__builtin_bit_cast(uint16_t, h2)) | (uint32_t(__builtin_bit_cast(uint16_t, h3)) << 16);
+    *reinterpret_cast<uint2*>(p.remote16 + (long long)t * p.d + c) = make_uint2(a, b);
+  }
+}
+
+// ---- scratch -----------------------------------------------------------------------------
+struct PfScratch {
+  size_t xb, idx, w, cnt, off, lst, lslot, lw, tiles, ntiles, act, z, shared, local, remote16, bo,
+      total;
+  int max_tiles;
+};
+static PfScratch pf_scratch(const lps_moe_desc* m, int T) {
+  PfScratch s{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o += align256(bytes); return r; };
+  const size_t Tk = size_t(T) * m->top_k;
+  s.max_tiles = int((Tk + GM - 1) / GM + m->n_experts + (size_t(T) + GM - 1) / GM + 1);
+  s.xb = take(size_t(T) * m->d * 2);
+  s.idx = take(Tk * 4);
+  s.w = take(Tk * 4);
+  s.cnt = take(size_t(m->n_experts + 1) * 4);
+  s.off = take(size_t(m->n_experts + 1) * 4);
+  s.lst = take(size_t(m->n_experts) * T * 4);
+  s.lslot = take(size_t(m->n_experts) * T * 4);
+  s.lw = take(size_t(m->n_experts) * T * 4);
+  s.tiles = take(size_t(s.max_tiles) * 4);
+  s.ntiles = take(4);
+  s.act = take((Tk + T) * m->ff * 2);
+  s.z = take(Tk * m->d * 4);
+  s.shared = take(size_t(T) * m->d * 4);
+  s.local = take(size_t(T) * m->d * 4);
+  s.remote16 = take(size_t(T) * m->d * 2);
+  s.bo = take(size_t(T) * m->d * 4);
+  s.total = o;
+  return s;
+}
+
+}  // namespace lps
+
+using namespace lps;
+
+extern "C" size_t lps_moe_prefill_scratch_bytes(const lps_moe_desc* m, int32_t T) {
+  if (!m || T <= 0) return 0;
+  return pf_scratch(m, T).total;
+}
+
+extern "C" int lps_moe_prefill(const lps_moe_desc* m, float* x, int32_t T, int32_t n_pieces,
+                               void* scratch, size_t scratch_bytes, void* s_main, void* s_remote) {
+  LPS_REQUIRE(m, LPS_EINVAL, "lps_moe_prefill: null MoE descriptor");
+  LPS_REQUIRE(T >= 1 && T <= (1 << 20) - 1, LPS_EINVAL, "lps_moe_prefill: T %d outside [1, 2^20)", T);
+  LPS_REQUIRE(m->n_experts >= 1 && m->n_experts <= PF_MAXE, LPS_EUNSUP,
+              "lps_moe_prefill: n_experts %d outside [1, %d]", m->n_experts, PF_MAXE);
+  LPS_REQUIRE(m->top_k >= 1 && m->top_k <= PF_MAXK && m->top_k <= m->n_experts, LPS_EUNSUP,
+              "lps_moe_prefill: top_k %d", m->top_k);
+  LPS_REQUIRE(m->d % GN == 0 && m->d % GK == 0 && m->ff % 64 == 0 && m->ff % GK == 0, LPS_EUNSUP,
+              "lps_moe_prefill: d %d must be a multiple of %d and ff %d of 64", m->d, GN, m->ff);
+  LPS_REQUIRE(size_t(PF_TOK) * m->d * 4 <= 160 * 1024, LPS_EUNSUP, "lps_moe_prefill: d %d too wide", m->d);
+  LPS_REQUIRE(m->remote_from >= 0 && m->remote_from <= m->n_experts, LPS_EINVAL,
+              "lps_moe_prefill: remote_from %d", m->remote_from);
+  LPS_REQUIRE(m->g_ffn && m->w_r && m->w_gu_e && m->w_d_e && m->w_gu_s && m->w_d_s && x && scratch,
+              LPS_EINVAL, "lps_moe_prefill: null pointer");
+  const PfScratch s = pf_scratch(m, T);
+  LPS_REQUIRE(scratch_bytes >= s.total, LPS_EINVAL, "lps_moe_prefill: scratch %zu < %zu",
+              scratch_bytes, s.total);
+  char* sc = static_cast<char*>(scratch);
+  PfP p{};
+  p.x = x;
+  p.g = m->g_ffn;
+  p.eps = m->eps;
+  p.wr = static_cast<const uint16_t*>(m->w_r);
+  p.w_gu_e = static_cast<const uint16_t*>(m->w_gu_e);
+  p.w_d_e = static_cast<const uint16_t*>(m->w_d_e);
+  p.w_gu_s = static_cast<const uint16_t*>(m->w_gu_s);
+  p.w_d_s = static_cast<const uint16_t*>(m->w_d_s);
+  p.T = T;
+  p.d = m->d;
+  p.E = m->n_experts;
+  p.k = m->top_k;
+  p.ff = m->ff;
+  p.remote_from = m->remote_from;
+  p.xb = reinterpret_cast<uint16_t*>(sc + s.xb);
+  p.idx = reinterpret_cast<int32_t*>(sc + s.idx);
+  p.w = reinterpret_cast<float*>(sc + s.w);
+  p.cnt = reinterpret_cast<int32_t*>(sc + s.cnt);
+  p.off = reinterpret_cast<int32_t*>(sc + s.off);
+  p.lst = reinterpret_cast<int32_t*>(sc + s.lst);
+  p.lslot = reinterpret_cast<int32_t*>(sc + s.lslot);
+  p.lw = reinterpret_cast<float*>(sc + s.lw);
+  p.tiles = reinterpret_cast<int32_t*>(sc + s.tiles);
+  p.n_tiles = reinterpret_cast<int32_t*>(sc + s.ntiles);
+  p.act = reinterpret_cast<uint16_t*>(sc + s.act);
+  p.z = reinterpret_cast<float*>(sc + s.z);
+  p.shared = reinterpret_cast<float*>(sc + s.shared);
+  p.local = reinterpret_cast<float*>(sc + s.local);
+  p.remote16 = reinterpret_cast<uint16_t*>(sc + s.remote16);
+  float* bo = reinterpret_cast<float*>(sc + s.bo);
+  hipStream_t st = as_stream(s_main);
+  int rc = ensure_lds((const void*)k_pf_route, size_t(PF_TOK) * m->d * 4);
+  if (rc) return rc;
+  hipLaunchKernelGGL(k_pf_route, dim3((T + PF_TOK - 1) / PF_TOK), dim3(256), size_t(PF_TOK) * m->d * 4,
+                     st, p);
+  LPS_HIP(hipGetLastError());
+  hipLaunchKernelGGL(k_pf_group, dim3(m->n_experts), dim3(256), 0, st, p);
+  LPS_HIP(hipGetLastError());
+  hipLaunchKernelGGL(k_pf_tiles, dim3(1), dim3(64), 0, st, p);
+  LPS_HIP(hipGetLastError());
+  hipLaunchKernelGGL(k_pf_gemm<true>, dim3(m->ff / 64, s.max_tiles), dim3(256), 0, st, p);
+  LPS_HIP(hipGetLastError());
+  hipLaunchKernelGGL(k_pf_gemm<false>, dim3(m->d / GN, s.max_tiles), dim3(256), 0, st, p);
+  LPS_HIP(hipGetLastError());
+  hipLaunchKernelGGL(k_pf_halves, dim3(T), dim3(256), 0, st, p);
+  LPS_HIP(hipGetLastError());
+  return lps_moe_combine(x, x, p.shared, p.local, p.remote16, bo, T, m->d, n_pieces, s_remote, s_main);
+}

@@ -305,6 +305,27 @@ class DeviceMoEStack:
             lps.lps_moe_layer_decode(C.byref(d), ptr(self.x), ptr(self.scratch), self.scratch_bytes, st)
         lps.lps_copy_f32(ptr(self.x), out_ptr, cfg.d, st)
 
+    def prefill(self, X: np.ndarray, n_pieces: int = 8, remote_stream=None) -> np.ndarray:
+        """All layers over a chunk of T rows (the grouped-GEMM path); returns
+        the output rows [T, d]."""
+        cfg, dev = self.cfg, self.device
+        T = X.shape[0]
+        x = to_dev(np.ascontiguousarray(X, dtype=np.float32), dev)
+        sb = lps.lps_moe_prefill_scratch_bytes(C.byref(self.descs[0]), T)
+        if getattr(self, "_pf_scratch", None) is None or self._pf_scratch.numel() < sb:
+            self._pf_scratch = torch.empty(sb, dtype=torch.uint8, device=dev)
+        rs = remote_stream or torch.cuda.Stream(device=dev)
+        torch.cuda.synchronize(dev)
+        self.prefill_dev(x, T, n_pieces, rs)
+        torch.cuda.synchronize(dev)
+        return x.cpu().numpy()
+
+    def prefill_dev(self, x, T, n_pieces, remote_stream):
+        """Enqueue the layers over device rows x [T, d] (in place)."""
+        for d in self.descs:
+            lps.lps_moe_prefill(C.byref(d), ptr(x), T, n_pieces, ptr(self._pf_scratch),
+                                self._pf_scratch.numel(), sp(self.stream), sp(remote_stream))
+
     def decode(self, xs: np.ndarray) -> np.ndarray:
         cfg, dev = self.cfg, self.device
         xin = to_dev(np.ascontiguousarray(xs, dtype=np.float32), dev)

@@ -142,3 +142,27 @@ def test_moe_decode_small_matches_oracle(rt):
         ref = ref_st.forward(m["x_in"][t], traces=traces)
         tol = 2e-3 * np.abs(ref).max()
         assert np.max(np.abs(got[t] - ref)) <= tol
+
+
+def test_moe_prefill_small_matches_oracle_and_pieces(rt):
+    """Grouped-GEMM prefill over a ragged chunk (T = 300: tiles of 128 rows plus
+    a tail, per-expert groups of uneven size): every row within the bf16
+    tolerance of the oracle (which rounds the GEMM inputs to bf16 the same
+    way), and the 8-piece FP16 transfer bit-identical to the 1-piece one."""
+    from oracle.moe import MoEStack
+    cfg = synth.MoEConfig("moe-gpu-pf", n_layers=2, d=512, n_experts=16, top_k=4, ff=128,
+                          remote_from=8, prefill_T=300, steps=0)
+    m = synth.make_moe(cfg)
+    st = rt.DeviceMoEStack(m)
+    X = m["x_prefill"]
+    got8 = st.prefill(X, n_pieces=8)
+    got1 = st.prefill(X, n_pieces=1)
+    assert np.array_equal(got8, got1)
+    ref = MoEStack(m).forward(X, prefill=True, n_pieces=8)
+    tol = 2e-3 * np.abs(ref).max()
+    err = np.abs(got8 - ref).max(axis=1)
+    assert np.all(err <= tol), (int(np.argmax(err)), float(err.max()), tol)
+    # a single row through the chunk path equals its decode (one-token) path within tolerance
+    dec = st.decode(X[:3])
+    ref_dec = MoEStack(m).forward(X[:3])
+    assert np.max(np.abs(dec - ref_dec)) <= 2e-3 * np.abs(ref_dec).max()

@@ -101,3 +101,23 @@ def test_moe_decode_full_size(rt):
         ref = ref_st.forward(m["x_in"][t])
         tol = 2e-3 * np.abs(ref).max()
         assert np.max(np.abs(got[t] - ref)) <= tol, (t, np.max(np.abs(got[t] - ref)))
+
+
+def test_moe_prefill_full_chunk(rt):
+    """The 16,384-token chunk through the 4 MoE layers: 8 FP16 pieces equal one
+    piece bit for bit (strata PR #3648: exact conversion, fixed add order), and
+    sampled rows match the oracle (rows are independent, so the oracle runs
+    only those rows)."""
+    cfg = replace(synth.MOE, steps=0)
+    m = synth.make_moe(cfg)
+    st = rt.DeviceMoEStack(m)
+    X = m["x_prefill"]
+    got8 = st.prefill(X, n_pieces=8)
+    got1 = st.prefill(X, n_pieces=1)
+    assert np.array_equal(got8, got1)
+    rows = np.random.default_rng(0).choice(X.shape[0], 48, replace=False)
+    rows = np.sort(np.concatenate([rows, [0, X.shape[0] - 1]]))
+    ref = MoEStack(m).forward(X[rows], prefill=True, n_pieces=8)
+    tol = 2e-3 * np.abs(ref).max()
+    err = np.abs(got8[rows] - ref).max(axis=1)
+    assert np.all(err <= tol), (int(rows[np.argmax(err)]), float(err.max()), tol)
