@@ -301,10 +301,11 @@ int lps_counters_reset(void);
 
 /* ---- kernel timing (benchmarks) -------------------------------------------
  * While a timer runs, every launch of the chosen kind made by lps_layer_forward,
- * lps_stage_forward or lps_head_forward is bracketed by a pair of hipEvents
- * recorded on the launching stream (so the durations are those of that kernel
- * on that stream).  capacity bounds the pairs recorded (later launches are not
- * timed).  One timer at a time per process. */
+ * lps_stage_forward or lps_head_forward carries a pair of hipEvents that the
+ * dispatch itself stamps at its start and end (hipExtLaunchKernelGGL), so the
+ * durations are those of the kernels on their stream, without launch gaps.
+ * capacity bounds the pairs recorded (later launches are not timed).  One timer
+ * at a time per process. */
 enum {
   LPS_KIND_QKV = 1,     /* RMSNorm + QKV GEMV + RoPE + KV append */
   LPS_KIND_ATTN = 2,    /* decode attention incl. the chunk merge */

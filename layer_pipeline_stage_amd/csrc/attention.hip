@@ -248,23 +248,25 @@ size_t attn_scratch(int nq, int nkv, int hd, int ctx_max) {
 }
 
 template <int HD, int KVT>
-static int go(const AttnP& p, int nkv, hipStream_t st) {
+static int go(const AttnP& p, int nkv, hipStream_t st, Stamp sp) {
   const dim3 grid(p.nch, nkv), blk(ATT_THREADS);
+  hipEvent_t a = sp.start;
   switch (p.G) {
-    case 1: hipLaunchKernelGGL((k_attn<HD, KVT, 1>), grid, blk, 0, st, p); break;
-    case 2: hipLaunchKernelGGL((k_attn<HD, KVT, 2>), grid, blk, 0, st, p); break;
-    case 4: hipLaunchKernelGGL((k_attn<HD, KVT, 4>), grid, blk, 0, st, p); break;
-    case 6: hipLaunchKernelGGL((k_attn<HD, KVT, 6>), grid, blk, 0, st, p); break;
-    case 8: hipLaunchKernelGGL((k_attn<HD, KVT, 8>), grid, blk, 0, st, p); break;
+    case 1: hipExtLaunchKernelGGL((k_attn<HD, KVT, 1>), grid, blk, 0, st, a, nullptr, 0, p); break;
+    case 2: hipExtLaunchKernelGGL((k_attn<HD, KVT, 2>), grid, blk, 0, st, a, nullptr, 0, p); break;
+    case 4: hipExtLaunchKernelGGL((k_attn<HD, KVT, 4>), grid, blk, 0, st, a, nullptr, 0, p); break;
+    case 6: hipExtLaunchKernelGGL((k_attn<HD, KVT, 6>), grid, blk, 0, st, a, nullptr, 0, p); break;
+    case 8: hipExtLaunchKernelGGL((k_attn<HD, KVT, 8>), grid, blk, 0, st, a, nullptr, 0, p); break;
     default: return fail(LPS_EUNSUP, "attention: %d q heads per kv head not built (1, 2, 4, 6, 8)", p.G);
   }
-  hipLaunchKernelGGL((k_attn_merge<HD>), dim3(nkv * p.G), dim3(MERGE_THREADS), 0, st, p);
+  hipExtLaunchKernelGGL((k_attn_merge<HD>), dim3(nkv * p.G), dim3(MERGE_THREADS), 0, st, nullptr,
+                        sp.stop, 0, p);
   return LPS_OK;
 }
 
 int launch_attention(int nq, int nkv, int hd, int kvdtype, const void* kc, const void* vc,
                      int ctx_max, int n_rows, const float* q, float* o, void* scratch,
-                     hipStream_t st) {
+                     hipStream_t st, Stamp sp) {
   AttnP p{};
   p.kc = kc;
   p.vc = vc;
@@ -285,9 +287,9 @@ int launch_attention(int nq, int nkv, int hd, int kvdtype, const void* kc, const
   const bool f32 = kvdtype == LPS_F32;
   int rc;
   switch (hd) {
-    case 64: rc = f32 ? go<64, LPS_F32>(p, nkv, st) : go<64, LPS_BF16>(p, nkv, st); break;
-    case 128: rc = f32 ? go<128, LPS_F32>(p, nkv, st) : go<128, LPS_BF16>(p, nkv, st); break;
-    case 256: rc = f32 ? go<256, LPS_F32>(p, nkv, st) : go<256, LPS_BF16>(p, nkv, st); break;
+    case 64: rc = f32 ? go<64, LPS_F32>(p, nkv, st, sp) : go<64, LPS_BF16>(p, nkv, st, sp); break;
+    case 128: rc = f32 ? go<128, LPS_F32>(p, nkv, st, sp) : go<128, LPS_BF16>(p, nkv, st, sp); break;
+    case 256: rc = f32 ? go<256, LPS_F32>(p, nkv, st, sp) : go<256, LPS_BF16>(p, nkv, st, sp); break;
     default: return fail(LPS_EUNSUP, "attention: head dim %d not built (64, 128, 256)", hd);
   }
   if (rc) return rc;

@@ -195,7 +195,7 @@ static int max_blocks() { return 256 * 8; }
 
 
 template <int WT, int EPI, bool NORM>
-static int launch_t(const GemvP& p, hipStream_t st) {
+static int launch_t(const GemvP& p, hipStream_t st, Stamp sp) {
   const int NW = GEMV_THREADS / WAVE;
   int grid = (p.units + NW - 1) / NW;
   if (grid > max_blocks()) grid = max_blocks();
@@ -208,22 +208,24 @@ static int launch_t(const GemvP& p, hipStream_t st) {
   if (per_lane <= 4 || WT == LPS_MXFP4) {
     int rc = ensure_lds((const void*)k_gemv<WT, EPI, 4, NORM>, lds);
     if (rc) return rc;
-    hipLaunchKernelGGL((k_gemv<WT, EPI, 4, NORM>), dim3(grid), dim3(GEMV_THREADS), lds, st, p);
+    hipExtLaunchKernelGGL((k_gemv<WT, EPI, 4, NORM>), dim3(grid), dim3(GEMV_THREADS), lds, st,
+                          sp.start, sp.stop, 0, p);
   } else {
     int rc = ensure_lds((const void*)k_gemv<WT, EPI, 8, NORM>, lds);
     if (rc) return rc;
-    hipLaunchKernelGGL((k_gemv<WT, EPI, 8, NORM>), dim3(grid), dim3(GEMV_THREADS), lds, st, p);
+    hipExtLaunchKernelGGL((k_gemv<WT, EPI, 8, NORM>), dim3(grid), dim3(GEMV_THREADS), lds, st,
+                          sp.start, sp.stop, 0, p);
   }
   LPS_HIP(hipGetLastError());
   return LPS_OK;
 }
 
 template <int EPI, bool NORM>
-static int launch_wt(int wdtype, const GemvP& p, hipStream_t st) {
+static int launch_wt(int wdtype, const GemvP& p, hipStream_t st, Stamp sp) {
   switch (wdtype) {
-    case LPS_F32: return launch_t<LPS_F32, EPI, NORM>(p, st);
-    case LPS_BF16: return launch_t<LPS_BF16, EPI, NORM>(p, st);
-    case LPS_MXFP4: return launch_t<LPS_MXFP4, EPI, NORM>(p, st);
+    case LPS_F32: return launch_t<LPS_F32, EPI, NORM>(p, st, sp);
+    case LPS_BF16: return launch_t<LPS_BF16, EPI, NORM>(p, st, sp);
+    case LPS_MXFP4: return launch_t<LPS_MXFP4, EPI, NORM>(p, st, sp);
   }
   return fail(LPS_EINVAL, "gemv: unknown wdtype %d", wdtype);
 }
@@ -235,7 +237,7 @@ static void set_rows(GemvP& p, int wdtype, int K) {
 }
 
 int launch_gemv(int wdtype, const void* w, const uint8_t* s, int N, int K, const float* x,
-                const float* g, float eps, float* y, int mode, hipStream_t st) {
+                const float* g, float eps, float* y, int mode, hipStream_t st, Stamp sp) {
   GemvP p{};
   p.w = static_cast<const uint8_t*>(w);
   p.s = s;
@@ -249,15 +251,15 @@ int launch_gemv(int wdtype, const void* w, const uint8_t* s, int N, int K, const
   const bool norm = g != nullptr;
   if (mode == EPI_SWIGLU) {
     p.units = N / 2;
-    return norm ? launch_wt<EPI_SWIGLU, true>(wdtype, p, st) : launch_wt<EPI_SWIGLU, false>(wdtype, p, st);
+    return norm ? launch_wt<EPI_SWIGLU, true>(wdtype, p, st, sp) : launch_wt<EPI_SWIGLU, false>(wdtype, p, st, sp);
   }
   p.units = (N + 1) / 2;
   if (mode == EPI_ADD)
-    return norm ? launch_wt<EPI_ADD, true>(wdtype, p, st) : launch_wt<EPI_ADD, false>(wdtype, p, st);
-  return norm ? launch_wt<EPI_STORE, true>(wdtype, p, st) : launch_wt<EPI_STORE, false>(wdtype, p, st);
+    return norm ? launch_wt<EPI_ADD, true>(wdtype, p, st, sp) : launch_wt<EPI_ADD, false>(wdtype, p, st, sp);
+  return norm ? launch_wt<EPI_STORE, true>(wdtype, p, st, sp) : launch_wt<EPI_STORE, false>(wdtype, p, st, sp);
 }
 
-int launch_qkv(const QkvArgs& a, hipStream_t st) {
+int launch_qkv(const QkvArgs& a, hipStream_t st, Stamp sp) {
   const lps_layer_desc* L = a.L;
   GemvP p{};
   p.w = static_cast<const uint8_t*>(L->w_qkv);
@@ -286,7 +288,7 @@ int launch_qkv(const QkvArgs& a, hipStream_t st) {
   p.kc = L->k_cache;
   p.vc = L->v_cache;
   set_rows(p, L->wdtype, L->d);
-  return launch_wt<EPI_QKV, true>(L->wdtype, p, st);
+  return launch_wt<EPI_QKV, true>(L->wdtype, p, st, sp);
 }
 
 size_t head_scratch(const lps_head_desc* h) {
@@ -295,13 +297,14 @@ size_t head_scratch(const lps_head_desc* h) {
 }
 
 int launch_head(const lps_head_desc* h, const float* x, float* logits, int32_t* tok, void* scratch,
-                size_t bytes, hipStream_t st) {
+                size_t bytes, hipStream_t st, Stamp sp) {
   (void)scratch;
   (void)bytes;
   int rc = launch_gemv(h->wdtype, h->w_lm, nullptr, h->vocab, h->d, x, h->g_out, h->eps, logits,
-                       EPI_STORE, st);
+                       EPI_STORE, st, Stamp{sp.start, nullptr});
   if (rc) return rc;
-  hipLaunchKernelGGL(k_argmax, dim3(1), dim3(1024), 0, st, logits, h->vocab, tok);
+  hipExtLaunchKernelGGL(k_argmax, dim3(1), dim3(1024), 0, st, nullptr, sp.stop, 0, logits,
+                        h->vocab, tok);
   LPS_HIP(hipGetLastError());
   return LPS_OK;
 }

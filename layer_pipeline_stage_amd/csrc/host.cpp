@@ -54,26 +54,15 @@ struct Timer {
   std::atomic<int> kind{0};
   std::vector<hipEvent_t> ev;   // 2 per launch
   int used = 0;
-  bool open = false;
 };
 static Timer g_timer;
 
-void timer_begin(int kind, hipStream_t st) {
-  if (g_timer.kind.load(std::memory_order_relaxed) != kind) return;
+Stamp timer_take(int kind) {
+  if (g_timer.kind.load(std::memory_order_relaxed) != kind) return {};
   std::lock_guard<std::mutex> lk(g_timer.mu);
-  if (!g_timer.open && g_timer.used * 2 < int(g_timer.ev.size())) {
-    (void)hipEventRecord(g_timer.ev[2 * g_timer.used], st);
-    g_timer.open = true;
-  }
-}
-void timer_end(int kind, hipStream_t st) {
-  if (g_timer.kind.load(std::memory_order_relaxed) != kind) return;
-  std::lock_guard<std::mutex> lk(g_timer.mu);
-  if (g_timer.open) {
-    (void)hipEventRecord(g_timer.ev[2 * g_timer.used + 1], st);
-    g_timer.open = false;
-    ++g_timer.used;
-  }
+  if (g_timer.kind.load() != kind || g_timer.used * 2 >= int(g_timer.ev.size())) return {};
+  const int i = g_timer.used++;
+  return Stamp{g_timer.ev[2 * i], g_timer.ev[2 * i + 1]};
 }
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -138,29 +127,19 @@ static int layer_forward(const lps_layer_desc* L, float* x, int pos, void* scrat
   float* m = reinterpret_cast<float*>(sc + s.m);
   void* at = sc + s.attn;
   QkvArgs qa{L, x, pos, q};
-  timer_begin(LPS_KIND_QKV, st);
-  int rc = launch_qkv(qa, st);
-  timer_end(LPS_KIND_QKV, st);
+  int rc = launch_qkv(qa, st, timer_take(LPS_KIND_QKV));
   if (rc) return rc;
-  timer_begin(LPS_KIND_ATTN, st);
   rc = launch_attention(L->nq, L->nkv, L->hd, L->kvdtype, L->k_cache, L->v_cache, L->ctx_max,
-                        pos + 1, q, o, at, st);
-  timer_end(LPS_KIND_ATTN, st);
+                        pos + 1, q, o, at, st, timer_take(LPS_KIND_ATTN));
   if (rc) return rc;
-  timer_begin(LPS_KIND_OPROJ, st);
   rc = launch_gemv(L->wdtype, L->w_o, L->s_o, L->d, L->nq * L->hd, o, nullptr, 0.f, x,
-                   LPS_EPI_ADD, st);
-  timer_end(LPS_KIND_OPROJ, st);
+                   LPS_EPI_ADD, st, timer_take(LPS_KIND_OPROJ));
   if (rc) return rc;
-  timer_begin(LPS_KIND_GATEUP, st);
   rc = launch_gemv(L->wdtype, L->w_gu, L->s_gu, 2 * L->ff, L->d, x, L->g_ffn, L->eps, m,
-                   LPS_EPI_SWIGLU, st);
-  timer_end(LPS_KIND_GATEUP, st);
+                   LPS_EPI_SWIGLU, st, timer_take(LPS_KIND_GATEUP));
   if (rc) return rc;
-  timer_begin(LPS_KIND_DOWN, st);
-  rc = launch_gemv(L->wdtype, L->w_d, L->s_d, L->d, L->ff, m, nullptr, 0.f, x, LPS_EPI_ADD, st);
-  timer_end(LPS_KIND_DOWN, st);
-  return rc;
+  return launch_gemv(L->wdtype, L->w_d, L->s_d, L->d, L->ff, m, nullptr, 0.f, x, LPS_EPI_ADD, st,
+                     timer_take(LPS_KIND_DOWN));
 }
 
 static int check_fence(const int32_t* fence, int32_t n_stages, int32_t n_layers, const char* who) {
@@ -428,10 +407,8 @@ int lps_head_forward(const lps_head_desc* h, const float* x, float* logits, int3
               "lps_head_forward: weights, gain and x must be 16-byte aligned");
   LPS_REQUIRE(scratch_bytes >= head_scratch(h), LPS_EINVAL, "lps_head_forward: scratch %zu < %zu",
               scratch_bytes, head_scratch(h));
-  timer_begin(LPS_KIND_HEAD, as_stream(stream));
-  int rc = launch_head(h, x, logits, tok_out, scratch, scratch_bytes, as_stream(stream));
-  timer_end(LPS_KIND_HEAD, as_stream(stream));
-  return rc;
+  return launch_head(h, x, logits, tok_out, scratch, scratch_bytes, as_stream(stream),
+                     timer_take(LPS_KIND_HEAD));
 }
 
 // ---- benchmark timer ----------------------------------------------------------------------
@@ -450,7 +427,6 @@ int lps_timer_start(int32_t kind, int32_t capacity) {
     }
   }
   g_timer.used = 0;
-  g_timer.open = false;
   g_timer.kind.store(kind);
   return LPS_OK;
 }

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <cstdint>
 #include <cstdio>
@@ -41,9 +42,13 @@ inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s);
 // per function (gfx950 has 160 KiB per workgroup).  Returns a status.
 int ensure_lds(const void* fn, size_t bytes);
 
-// Benchmark timer: brackets launches of one kind with events (no-op when off).
-void timer_begin(int kind, hipStream_t st);
-void timer_end(int kind, hipStream_t st);
+// Benchmark timer: a pair of events the next launch of `kind` hands to
+// hipExtLaunchKernelGGL, which stamps them with that dispatch's own start and
+// end (nulls when no timer runs for this kind).
+struct Stamp {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+Stamp timer_take(int kind);
 
 // ---- scratch carving ------------------------------------------------------------
 inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
@@ -56,16 +61,16 @@ struct QkvArgs {
   float* q;
 };
 int launch_gemv(int wdtype, const void* w, const uint8_t* s, int N, int K, const float* x,
-                const float* g, float eps, float* y, int mode, hipStream_t st);
-int launch_qkv(const QkvArgs& a, hipStream_t st);
+                const float* g, float eps, float* y, int mode, hipStream_t st, Stamp sp = {});
+int launch_qkv(const QkvArgs& a, hipStream_t st, Stamp sp = {});
 int launch_head(const lps_head_desc* h, const float* x, float* logits, int32_t* tok,
-                void* scratch, size_t bytes, hipStream_t st);
+                void* scratch, size_t bytes, hipStream_t st, Stamp sp = {});
 size_t head_scratch(const lps_head_desc* h);
 
 size_t attn_scratch(int nq, int nkv, int hd, int ctx_max);
 int launch_attention(int nq, int nkv, int hd, int kvdtype, const void* kc, const void* vc,
                      int ctx_max, int n_rows, const float* q, float* o, void* scratch,
-                     hipStream_t st);
+                     hipStream_t st, Stamp sp = {});
 
 int launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t st);
 
