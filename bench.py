@@ -131,6 +131,9 @@ def main():
     ap.add_argument("--steps", type=int, default=128)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--stages", type=int, default=4)
+    ap.add_argument("--streams", choices=("single", "per-stage"), default="single",
+                    help="stage streams: one shared stream (the same-stream seam; greedy "
+                         "decode cannot overlap stages) or one stream per stage")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-steps", type=int, default=2)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -169,7 +172,7 @@ def main():
     model = synth.make_dense(cfg)
     t_gen = time.perf_counter() - t0
     fence = lps.stage_plan(cfg.n_layers, a.stages)
-    dd = runtime.DeviceDecoder(model, fence=fence)
+    dd = runtime.DeviceDecoder(model, fence=fence, streams=a.streams)
     start_tok = [int(model["prompt"][0])]
 
     # warmup
@@ -221,7 +224,8 @@ def main():
         "config": {
             "workload": "dense 8B-class slice decode: 8 layers, n_embd 4096, 32q/8kv x 128, "
                         "SwiGLU 14336, vocab 32000, bf16 weights, f32 hidden, KV context 4096 + "
-                        f"{K} steps, batch 1, {a.stages} stages (even split) on one GPU, "
+                        f"{K} steps, batch 1, {a.stages} stages (even split) on one GPU "
+                        f"({a.streams} stream{'s' if a.streams == 'per-stage' else ''}), "
                         "deferred logits readback",
             "global_batch": 1, "seq_len": cfg.prefix + K, "stages": fence,
         },

@@ -186,9 +186,13 @@ int lps_attention_decode(int32_t nq, int32_t nkv, int32_t hd, int32_t kvdtype,
  * double-buffered slots with ev_tx / ev_rx per slot; fn pp2_overlap: the slots
  * alternate per step.  Slot k = step & 1.
  *  send(step t): the producer stream waits ev_rx[k] (slot k drained by the
- *    recv of step t-2), copies x -> slot[k], records ev_tx[k].
- *  recv(step t): the consumer stream waits ev_tx[k], copies slot[k] -> x,
- *    records ev_rx[k].
+ *    recv of step t-2) and copies x -> slot[k].
+ *  recv(step t): ev_tx[k] is recorded on the producer stream (after the send's
+ *    copy and whatever the host enqueued there since), the consumer stream waits
+ *    it, copies slot[k] -> x and records ev_rx[k].
+ * When producer and consumer are the same stream (memra pp docs, fn
+ * pp2_streams_off: the same-stream seam), stream order already gives both
+ * orderings and no event is recorded or waited.
  * Steps must be sent in order 0, 1, 2, ... and received in the same order;
  * a recv of a step that was not sent, or out of order, is LPS_ESTATE.
  * The two slots (dev [n_elems] f32 each) are the caller's. */

@@ -5,8 +5,8 @@
 // weights).  One workgroup takes one (kv head, 64-row chunk) tile: the chunk's
 // K and V rows are streamed once from HBM with 16-byte loads and reused by all
 // G query heads of the group; scores are reduced across the lanes of a row by
-// wavefront shuffles, the chunk softmax (max, sum) by wave reductions, and the
-// V-weighted sums across rows by shuffles and a small LDS tree.  Each tile
+// DPP row operations, the chunk softmax (max, sum) by wave reductions, and the
+// V tile is staged in LDS so that each thread forms whole output columns.  Each tile
 // writes (m, l, o) partials; a second small launch merges every q head's chunks
 // in chunk order, so the result does not depend on the order the tiles ran in
 // (and no tile waits on, or fences for, another).
@@ -62,15 +62,18 @@ __device__ __forceinline__ void widen16(const u32x4 v, float* out) {
   }
 }
 
+// at head dim 256 the tile's K rows and the G query heads compete for registers:
+// ask for at least 3 waves per SIMD
 template <int HD, int KVT, int G>
-__global__ __launch_bounds__(ATT_THREADS) void k_attn(AttnP p) {
+__global__ __launch_bounds__(ATT_THREADS, HD >= 256 ? 3 : 1) void k_attn(AttnP p) {
   using C = AttnCfg<HD, KVT>;
   constexpr int E16 = C::E16, LPR = C::LPR, RPP = C::RPP;
   constexpr int NP = ATT_CH / RPP;          // rows per thread
   constexpr int ESZ = C::ESZ;
+  constexpr int VROW = HD * ESZ + 16;       // LDS bytes per V row (padded against bank conflicts)
   __shared__ float qs[G][HD];
   __shared__ float sc[G][ATT_CH];
-  __shared__ float red[ATT_NW][G][HD];
+  __shared__ __attribute__((aligned(16))) char vs[ATT_CH * VROW];
 
   const int chunk = blockIdx.x, g = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wv = tid / WAVE;
@@ -88,13 +91,17 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attn(AttnP p) {
       kraw[ps] = ld16(static_cast<const char*>(p.kc) + off);
       vraw[ps] = ld16(static_cast<const char*>(p.vc) + off);
     } else {
-      kraw[ps] = vraw[ps] = u32x4{0, 0, 0, 0};
+      kraw[ps] = vraw[ps] = u32x4{0, 0, 0, 0};   // rows past n: zero V, -inf score
     }
   }
   for (int i = tid; i < G * HD; i += ATT_THREADS) qs[i / HD][i % HD] = p.q[(g * G) * HD + i];
+  // the V tile is staged in LDS for the weighted sum (read there by output column)
+#pragma unroll
+  for (int ps = 0; ps < NP; ++ps)
+    *reinterpret_cast<u32x4*>(vs + (ps * RPP + rr) * VROW + li * 16) = vraw[ps];
   __syncthreads();
 
-  // ---- scores s[h][j] = q_h . k_j * scale ----
+  // ---- scores s[h][j] = q_h . k_j * scale: LPR lanes per row, DPP sums ----
 #pragma unroll
   for (int ps = 0; ps < NP; ++ps) {
     const int jl = ps * RPP + rr;
@@ -130,45 +137,28 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attn(AttnP p) {
     }
   }
   __syncthreads();
-  // ---- o[h] = sum_j p[h][j] v_j ----
-  float acc[G][E16];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < E16; ++e) acc[h][e] = 0.f;
-#pragma unroll
-  for (int ps = 0; ps < NP; ++ps) {
-    const int jl = ps * RPP + rr;
-    float vv[E16];
-    widen16<KVT>(vraw[ps], vv);       // rows past n hold zeros and weight 0
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float w = sc[h][jl];
-#pragma unroll
-      for (int e = 0; e < E16; ++e) acc[h][e] = fmaf(w, vv[e], acc[h][e]);
-    }
-  }
-  // rows of one wave: lanes li + LPR*r; sum over r across lanes
-  if constexpr (LPR < WAVE) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < E16; ++e) acc[h][e] = strided_sum<LPR>(acc[h][e]);
-  }
-  if (lane < LPR) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < E16; ++e) red[wv][h][li * E16 + e] = acc[h][e];
-  }
-  __syncthreads();
+  // ---- o[h][e] = sum_j p[h][j] v_j[e]: one thread per (head, column pair) ----
   const long long ob = ((long long)g * p.nch + chunk) * G * HD;
-  for (int i = tid; i < G * HD; i += ATT_THREADS) {
-    const int h = i / HD, e = i % HD;
-    float v = red[0][h][e];
-#pragma unroll
-    for (int w = 1; w < ATT_NW; ++w) v += red[w][h][e];
-    p.po[ob + i] = v;
+  for (int idx = tid; idx < G * (HD / 2); idx += ATT_THREADS) {
+    const int h = idx / (HD / 2), e2 = idx - h * (HD / 2);
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll 8
+    for (int j = 0; j < ATT_CH; ++j) {
+      const float w = sc[h][j];
+      float v0, v1;
+      if constexpr (KVT == LPS_F32) {
+        const f32x2 v = *reinterpret_cast<const f32x2*>(vs + j * VROW + e2 * 8);
+        v0 = v.x;
+        v1 = v.y;
+      } else {
+        const uint32_t v = *reinterpret_cast<const uint32_t*>(vs + j * VROW + e2 * 4);
+        v0 = bf16_lo(v);
+        v1 = bf16_hi(v);
+      }
+      a0 = fmaf(w, v0, a0);
+      a1 = fmaf(w, v1, a1);
+    }
+    *reinterpret_cast<f32x2*>(p.po + ob + h * HD + 2 * e2) = f32x2{a0, a1};
   }
 }
 
@@ -192,8 +182,14 @@ __global__ __launch_bounds__(MERGE_THREADS) void k_attn_merge(AttnP p) {
   __shared__ float red[NWM];
   __shared__ float opart[P][HD];
   const long long base = (long long)g * p.nch;
-  float M = -INFINITY;
-  for (int c = t; c < p.nch; c += MERGE_THREADS) M = fmaxf(M, p.pm[(base + c) * p.G + h]);
+  // one read of every chunk's (m, l): the first MERGE_CH chunks stay in registers
+  float mreg = -INFINITY, lreg = 0.f;
+  if (t < p.nch) {
+    mreg = p.pm[(base + t) * p.G + h];
+    lreg = p.pl[(base + t) * p.G + h];
+  }
+  float M = mreg;
+  for (int c = t + MERGE_THREADS; c < p.nch; c += MERGE_THREADS) M = fmaxf(M, p.pm[(base + c) * p.G + h]);
   M = wave_max(M);
   if ((t & (WAVE - 1)) == 0) red[t / WAVE] = M;
   __syncthreads();
@@ -207,9 +203,10 @@ __global__ __launch_bounds__(MERGE_THREADS) void k_attn_merge(AttnP p) {
     __syncthreads();
     for (int c = t; c < n; c += MERGE_THREADS) {
       const long long pi = (base + c0 + c) * p.G + h;
-      const float w = expf(p.pm[pi] - M);
+      const bool first = c0 == 0 && c == t;
+      const float w = expf((first ? mreg : p.pm[pi]) - M);
       wsh[c] = w;
-      Lp = fmaf(w, p.pl[pi], Lp);
+      Lp = fmaf(w, first ? lreg : p.pl[pi], Lp);
     }
     __syncthreads();
     const float* po = p.po + ((base + c0) * p.G + h) * HD + e;

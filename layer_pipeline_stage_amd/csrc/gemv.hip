@@ -27,7 +27,8 @@
 
 namespace lps {
 
-enum { EPI_STORE = LPS_EPI_STORE, EPI_ADD = LPS_EPI_ADD, EPI_SWIGLU = LPS_EPI_SWIGLU, EPI_QKV = 3 };
+enum { EPI_STORE = LPS_EPI_STORE, EPI_ADD = LPS_EPI_ADD, EPI_SWIGLU = LPS_EPI_SWIGLU, EPI_QKV = 3,
+       EPI_LOGITS = 4 };
 
 struct GemvP {
   const uint8_t* w;
@@ -45,6 +46,9 @@ struct GemvP {
   void* vc;
   // cos / sin of pos * base^(-2i/hd) for i < hd/2, formed on the host in double
   float rope[2 * 128];
+  // LM-head epilogue: every wave's (max, lowest index of it) over its rows
+  float* pval;
+  int* pidx;
 };
 
 template <int EPI>
@@ -72,7 +76,7 @@ __device__ __forceinline__ void store_kv(void* base, int kvdtype, long long off,
 
 template <int EPI>
 __device__ __forceinline__ void epilogue(const GemvP& p, int u, int r0, int r1, float a0, float a1) {
-  if constexpr (EPI == EPI_STORE) {
+  if constexpr (EPI == EPI_STORE || EPI == EPI_LOGITS) {
     p.y[r0] = a0;
     if (r1 >= 0) p.y[r1] = a1;
   } else if constexpr (EPI == EPI_ADD) {
@@ -103,72 +107,132 @@ __device__ __forceinline__ void epilogue(const GemvP& p, int u, int r0, int r1, 
   }
 }
 
-template <int WT, int EPI, int U, bool NORM>
-__global__ __launch_bounds__(GEMV_THREADS) void k_gemv(GemvP p) {
+// threads per GEMV workgroup and the grid cap (workgroups); a block stages the
+// activation vector once for all of its waves
+#ifndef LPS_GEMV_NT
+#define LPS_GEMV_NT 256
+#endif
+#ifndef LPS_GEMV_MAXB
+#define LPS_GEMV_MAXB 2048
+#endif
+constexpr int GEMV_NT = LPS_GEMV_NT;
+
+// Loads of one batch (U chunks of both rows of a unit), then its FMAs.  Kept as
+// macros over local arrays: the compiler then issues all 2U loads of a batch
+// before the first wait.
+#define GEMV_LOAD(J0)                                              \
+  _Pragma("unroll") for (int i = 0; i < U; ++i) {                  \
+    const int c = (J0) + WAVE * i;                                 \
+    if (c < nck) {                                                 \
+      v0[i] = ld_stream16(w0 + (long long)c * 16);                 \
+      v1[i] = ld_stream16(w1 + (long long)c * 16);                 \
+      if constexpr (WT == LPS_MXFP4) {                             \
+        sc0[i] = s0[c];                                            \
+        sc1[i] = s1[c];                                            \
+      } else {                                                     \
+        sc0[i] = sc1[i] = 0;                                       \
+      }                                                            \
+    } else {                                                       \
+      v0[i] = v1[i] = u32x4{0, 0, 0, 0};                           \
+      sc0[i] = sc1[i] = 127;                                       \
+    }                                                              \
+  }
+#define GEMV_FMA(J0)                                               \
+  _Pragma("unroll") for (int i = 0; i < U; ++i) {                  \
+    const int c = (J0) + WAVE * i;                                 \
+    if (c < nck) {                                                 \
+      acc_chunk<WT>(v0[i], sc0[i], xs + c * CH, a0);               \
+      acc_chunk<WT>(v1[i], sc1[i], xs + c * CH, a1);               \
+    }                                                              \
+  }
+#define GEMV_ROWS(UU)                                              \
+  int r0, r1;                                                      \
+  unit_rows<EPI>(p, (UU), r0, r1);                                 \
+  const int rr1 = r1 >= 0 ? r1 : r0;                               \
+  const uint8_t* w0 = p.w + (long long)r0 * p.wrow;                \
+  const uint8_t* w1 = p.w + (long long)rr1 * p.wrow;               \
+  const uint8_t* s0 = nullptr;                                     \
+  const uint8_t* s1 = nullptr;                                     \
+  if constexpr (WT == LPS_MXFP4) {                                 \
+    s0 = p.s + (long long)r0 * p.srow;                             \
+    s1 = p.s + (long long)rr1 * p.srow;                            \
+  }
+
+template <int EPI>
+__device__ __forceinline__ void finish(const GemvP& p, int u, int r0, int r1, float a0, float a1,
+                                       int lane, float& best, int& bidx) {
+  a0 = wave_sum(a0);
+  a1 = wave_sum(a1);
+  if (lane == 0) epilogue<EPI>(p, u, r0, r1, a0, a1);
+  if constexpr (EPI == EPI_LOGITS) {
+    if (a0 > best) { best = a0; bidx = r0; }
+    if (r1 >= 0 && a1 > best) { best = a1; bidx = r1; }
+  }
+}
+
+// PF: for launches where a wave's first unit fits one batch (K <= 64 U chunks),
+// that batch is loaded before the activation vector is staged, so its HBM
+// latency overlaps the staging and the norm; further units take the plain path.
+template <int WT, int EPI, int U, bool NORM, bool PF>
+__global__ __launch_bounds__(GEMV_NT) void k_gemv(GemvP p) {
   extern __shared__ float xs[];
-  stage_x<NORM>(p.x, p.g, p.eps, p.K, xs);
   constexpr int CH = Fmt<WT>::CH;
-  constexpr int NW = GEMV_THREADS / WAVE;
+  constexpr int NW = GEMV_NT / WAVE;
   const int lane = threadIdx.x & (WAVE - 1);
   const int wv = threadIdx.x / WAVE;
   const int nck = p.K / CH;
-  for (int u = blockIdx.x * NW + wv; u < p.units; u += gridDim.x * NW) {
-    int r0, r1;
-    unit_rows<EPI>(p, u, r0, r1);
-    const int rr1 = r1 >= 0 ? r1 : r0;
-    const uint8_t* w0 = p.w + (long long)r0 * p.wrow;
-    const uint8_t* w1 = p.w + (long long)rr1 * p.wrow;
-    const uint8_t* s0 = nullptr;
-    const uint8_t* s1 = nullptr;
-    if constexpr (WT == LPS_MXFP4) {
-      s0 = p.s + (long long)r0 * p.srow;
-      s1 = p.s + (long long)rr1 * p.srow;
+  float best = -INFINITY;   // EPI_LOGITS: rows rise with u, so '>' keeps the first maximum
+  int bidx = 0x7fffffff;
+  int u = blockIdx.x * NW + wv;
+  if constexpr (PF) {
+    const int uu = u < p.units ? u : p.units - 1;   // waves without a unit load a valid row
+    GEMV_ROWS(uu)
+    u32x4 v0[U], v1[U];
+    uint32_t sc0[U], sc1[U];
+    GEMV_LOAD(lane)
+    stage_x<NORM, GEMV_NT>(p.x, p.g, p.eps, p.K, xs);
+    if (u < p.units) {
+      float a0 = 0.f, a1 = 0.f;
+      GEMV_FMA(lane)
+      finish<EPI>(p, u, r0, r1, a0, a1, lane, best, bidx);
     }
+    u += gridDim.x * NW;
+  } else {
+    stage_x<NORM, GEMV_NT>(p.x, p.g, p.eps, p.K, xs);
+  }
+  for (; u < p.units; u += gridDim.x * NW) {
+    GEMV_ROWS(u)
     float a0 = 0.f, a1 = 0.f;
     for (int j0 = lane; j0 < nck; j0 += WAVE * U) {
       u32x4 v0[U], v1[U];
       uint32_t sc0[U], sc1[U];
-#pragma unroll
-      for (int i = 0; i < U; ++i) {
-        const int c = j0 + WAVE * i;
-        if (c < nck) {
-          v0[i] = ld_stream16(w0 + (long long)c * 16);
-          v1[i] = ld_stream16(w1 + (long long)c * 16);
-          if constexpr (WT == LPS_MXFP4) {
-            sc0[i] = s0[c];
-            sc1[i] = s1[c];
-          } else {
-            sc0[i] = sc1[i] = 0;
-          }
-        } else {
-          v0[i] = v1[i] = u32x4{0, 0, 0, 0};
-          sc0[i] = sc1[i] = 127;
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < U; ++i) {
-        const int c = j0 + WAVE * i;
-        if (c < nck) {
-          acc_chunk<WT>(v0[i], sc0[i], xs + c * CH, a0);
-          acc_chunk<WT>(v1[i], sc1[i], xs + c * CH, a1);
-        }
-      }
+      GEMV_LOAD(j0)
+      GEMV_FMA(j0)
     }
-    a0 = wave_sum(a0);
-    a1 = wave_sum(a1);
-    if (lane == 0) epilogue<EPI>(p, u, r0, r1, a0, a1);
+    finish<EPI>(p, u, r0, r1, a0, a1, lane, best, bidx);
+  }
+  if constexpr (EPI == EPI_LOGITS) {
+    if (lane == 0) {
+      p.pval[blockIdx.x * NW + wv] = best;
+      p.pidx[blockIdx.x * NW + wv] = bidx;
+    }
   }
 }
+#undef GEMV_LOAD
+#undef GEMV_FMA
+#undef GEMV_ROWS
 
-// A16 argmax: the lowest index of the maximum of n values, one workgroup of
-// 1024 threads (a selection: exact in any order).  Runs as its own launch
-// after the LM head, so it needs no fence or counter.
-__global__ __launch_bounds__(1024) void k_argmax(const float* v, int n, int* out) {
+// A16 argmax over the LM head's per-wave partials (value, lowest index with
+// that value), one workgroup: max with ties to the lower index is an exact
+// selection, so any order gives the same answer.  Its own launch after the head
+// GEMV: no fence or counter is needed.
+__global__ __launch_bounds__(1024) void k_argmax(const float* pval, const int* pidx, int n, int* out) {
   float b = -INFINITY;
   int ix = 0x7fffffff;
   for (int i = threadIdx.x; i < n; i += 1024) {
-    const float x = v[i];
-    if (x > b) { b = x; ix = i; }          // ascending i: the first maximum stays
+    const float v = pval[i];
+    const int j = pidx[i];
+    if (v > b || (v == b && j < ix)) { b = v; ix = j; }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -190,13 +254,13 @@ __global__ __launch_bounds__(1024) void k_argmax(const float* v, int n, int* out
 }
 
 // ---- launch configuration ---------------------------------------------------
-static int max_blocks() { return 256 * 8; }
+static int max_blocks() { return LPS_GEMV_MAXB; }
 
 
 
 template <int WT, int EPI, bool NORM>
 static int launch_t(const GemvP& p, hipStream_t st, Stamp sp) {
-  const int NW = GEMV_THREADS / WAVE;
+  const int NW = GEMV_NT / WAVE;
   int grid = (p.units + NW - 1) / NW;
   if (grid > max_blocks()) grid = max_blocks();
   if (grid < 1) grid = 1;
@@ -204,18 +268,24 @@ static int launch_t(const GemvP& p, hipStream_t st, Stamp sp) {
   constexpr int CH = Fmt<WT>::CH;
   const int per_lane = (p.K / CH + WAVE - 1) / WAVE;
   // keep up to 8 (bf16 / f32) or 4 (MXFP4, whose decode needs more registers)
-  // chunk loads per row in flight per lane
+  // chunk loads per row in flight per lane; prefetch under the staging when a
+  // wave has at most two units
+  const bool pf = per_lane <= (per_lane <= 4 || WT == LPS_MXFP4 ? 4 : 8) && p.units <= 2 * grid * NW;
+#define LPS_GO(UU, PFV)                                                                     \
+  do {                                                                                      \
+    int rc_ = ensure_lds((const void*)k_gemv<WT, EPI, UU, NORM, PFV>, lds);                 \
+    if (rc_) return rc_;                                                                    \
+    hipExtLaunchKernelGGL((k_gemv<WT, EPI, UU, NORM, PFV>), dim3(grid), dim3(GEMV_NT), lds, \
+                          st, sp.start, sp.stop, 0, p);                                     \
+  } while (0)
   if (per_lane <= 4 || WT == LPS_MXFP4) {
-    int rc = ensure_lds((const void*)k_gemv<WT, EPI, 4, NORM>, lds);
-    if (rc) return rc;
-    hipExtLaunchKernelGGL((k_gemv<WT, EPI, 4, NORM>), dim3(grid), dim3(GEMV_THREADS), lds, st,
-                          sp.start, sp.stop, 0, p);
+    if (pf) LPS_GO(4, true);
+    else LPS_GO(4, false);
   } else {
-    int rc = ensure_lds((const void*)k_gemv<WT, EPI, 8, NORM>, lds);
-    if (rc) return rc;
-    hipExtLaunchKernelGGL((k_gemv<WT, EPI, 8, NORM>), dim3(grid), dim3(GEMV_THREADS), lds, st,
-                          sp.start, sp.stop, 0, p);
+    if (pf) LPS_GO(8, true);
+    else LPS_GO(8, false);
   }
+#undef LPS_GO
   LPS_HIP(hipGetLastError());
   return LPS_OK;
 }
@@ -293,18 +363,32 @@ int launch_qkv(const QkvArgs& a, hipStream_t st, Stamp sp) {
 
 size_t head_scratch(const lps_head_desc* h) {
   (void)h;
-  return 256;
+  return 2 * align256(size_t(LPS_GEMV_MAXB) * (GEMV_NT / WAVE) * 4);
 }
 
 int launch_head(const lps_head_desc* h, const float* x, float* logits, int32_t* tok, void* scratch,
                 size_t bytes, hipStream_t st, Stamp sp) {
-  (void)scratch;
   (void)bytes;
-  int rc = launch_gemv(h->wdtype, h->w_lm, nullptr, h->vocab, h->d, x, h->g_out, h->eps, logits,
-                       EPI_STORE, st, Stamp{sp.start, nullptr});
+  GemvP p{};
+  p.w = static_cast<const uint8_t*>(h->w_lm);
+  p.N = h->vocab;
+  p.K = h->d;
+  p.x = x;
+  p.g = h->g_out;
+  p.eps = h->eps;
+  p.y = logits;
+  p.units = (h->vocab + 1) / 2;
+  set_rows(p, h->wdtype, h->d);
+  char* sc = static_cast<char*>(scratch);
+  p.pval = reinterpret_cast<float*>(sc);
+  p.pidx = reinterpret_cast<int*>(sc + align256(size_t(LPS_GEMV_MAXB) * (GEMV_NT / WAVE) * 4));
+  int rc = launch_wt<EPI_LOGITS, true>(h->wdtype, p, st, Stamp{sp.start, nullptr});
   if (rc) return rc;
-  hipExtLaunchKernelGGL(k_argmax, dim3(1), dim3(1024), 0, st, nullptr, sp.stop, 0, logits,
-                        h->vocab, tok);
+  const int NW = GEMV_NT / WAVE;
+  int grid = (p.units + NW - 1) / NW;
+  if (grid > max_blocks()) grid = max_blocks();
+  hipExtLaunchKernelGGL(k_argmax, dim3(1), dim3(1024), 0, st, nullptr, sp.stop, 0, p.pval, p.pidx,
+                        grid * NW, tok);
   LPS_HIP(hipGetLastError());
   return LPS_OK;
 }

@@ -67,25 +67,25 @@ __device__ __forceinline__ void acc_chunk(const u32x4 v, uint32_t sb, const floa
 }
 
 // Stage the activation vector in LDS; with NORM, as RMSNorm(x) * g.
-template <bool NORM>
+template <bool NORM, int NT = GEMV_THREADS>
 __device__ __forceinline__ void stage_x(const float* x, const float* g, float eps, int K, float* xs) {
   const int tid = threadIdx.x;
   float ss = 0.f;
-  for (int k = tid * 4; k < K; k += GEMV_THREADS * 4) {
+  for (int k = tid * 4; k < K; k += NT * 4) {
     const f32x4 v = *reinterpret_cast<const f32x4*>(x + k);
     *reinterpret_cast<f32x4*>(xs + k) = v;
     if (NORM) ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
   }
   if (NORM) {
-    __shared__ float red[GEMV_THREADS / WAVE];
+    __shared__ float red[NT / WAVE];
     ss = wave_sum(ss);
     if ((tid & (WAVE - 1)) == 0) red[tid / WAVE] = ss;
     __syncthreads();
     float tot = 0.f;
 #pragma unroll
-    for (int i = 0; i < GEMV_THREADS / WAVE; ++i) tot += red[i];
+    for (int i = 0; i < NT / WAVE; ++i) tot += red[i];
     const float r = 1.0f / sqrtf(tot / float(K) + eps);
-    for (int k = tid * 4; k < K; k += GEMV_THREADS * 4) {
+    for (int k = tid * 4; k < K; k += NT * 4) {
       f32x4 v = *reinterpret_cast<f32x4*>(xs + k);
       const f32x4 gg = *reinterpret_cast<const f32x4*>(g + k);
       v.x = v.x * r * gg.x;

@@ -170,6 +170,8 @@ struct lps_boundary {
   hipEvent_t ev_rx[2];
   bool tx_recorded[2];
   bool rx_recorded[2];
+  hipStream_t tx_stream[2];   // stream of the slot's last send
+  hipStream_t rx_stream[2];   // stream of the slot's last receive
   int64_t next_send;
   int64_t next_recv;
 };
@@ -472,6 +474,7 @@ int lps_boundary_create(int32_t n_elems, float* slot0, float* slot1, lps_boundar
   b->next_recv = 0;
   for (int k = 0; k < 2; ++k) {
     b->tx_recorded[k] = b->rx_recorded[k] = false;
+    b->tx_stream[k] = b->rx_stream[k] = nullptr;
     hipError_t e1 = hipEventCreateWithFlags(&b->ev_tx[k], hipEventDisableTiming);
     hipError_t e2 = hipEventCreateWithFlags(&b->ev_rx[k], hipEventDisableTiming);
     if (e1 != hipSuccess || e2 != hipSuccess) {
@@ -494,11 +497,15 @@ int lps_boundary_send(lps_boundary* b, const float* x, int64_t step, void* produ
               (long long)step, int(step & 1), (long long)(step - 2));
   const int k = int(step & 1);
   hipStream_t st = as_stream(producer);
-  if (b->rx_recorded[k]) LPS_HIP(hipStreamWaitEvent(st, b->ev_rx[k], 0));
+  // a wait on the own stream is implied by stream order (the same-stream seam)
+  if (b->rx_recorded[k] && b->rx_stream[k] != st) LPS_HIP(hipStreamWaitEvent(st, b->ev_rx[k], 0));
   int rc = launch_copy_f32(x, b->slot[k], b->n, st);
   if (rc) return rc;
-  LPS_HIP(hipEventRecord(b->ev_tx[k], st));
-  b->tx_recorded[k] = true;
+  // ev_tx is recorded by the receive, on this stream, when the consumer turns out to
+  // be another stream: a marker after all work enqueued here so far, which covers
+  // the copy above (nothing in between can un-write the slot)
+  b->tx_recorded[k] = false;
+  b->tx_stream[k] = st;
   b->next_send = step + 1;
   count_send();
   return LPS_OK;
@@ -514,11 +521,21 @@ int lps_boundary_recv(lps_boundary* b, float* x, int64_t step, void* consumer) {
               (long long)step);
   const int k = int(step & 1);
   hipStream_t st = as_stream(consumer);
-  LPS_HIP(hipStreamWaitEvent(st, b->ev_tx[k], 0));
+  if (b->tx_stream[k] != st) {
+    LPS_HIP(hipEventRecord(b->ev_tx[k], b->tx_stream[k]));
+    b->tx_recorded[k] = true;
+    LPS_HIP(hipStreamWaitEvent(st, b->ev_tx[k], 0));
+  }
   int rc = launch_copy_f32(b->slot[k], x, b->n, st);
   if (rc) return rc;
-  LPS_HIP(hipEventRecord(b->ev_rx[k], st));
-  b->rx_recorded[k] = true;
+  // the producer's next use of slot k waits this event only from another stream
+  if (b->tx_stream[k] != st) {
+    LPS_HIP(hipEventRecord(b->ev_rx[k], st));
+    b->rx_recorded[k] = true;
+  } else {
+    b->rx_recorded[k] = false;
+  }
+  b->rx_stream[k] = st;
   b->next_recv = step + 1;
   count_recv();
   return LPS_OK;

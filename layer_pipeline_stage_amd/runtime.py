@@ -244,7 +244,8 @@ class DeviceDecoder:
             lps.lps_head_forward(C.byref(self.head), ptr(self.x[-1]), ptr(self.logits_ring[k]),
                                  ptr(self.tok_ring) + 4 * k, ptr(self.head_scratch),
                                  self.head_scratch.numel(), sp(stl))
-            done[k].record(stl)
+            if stl is not st0:
+                done[k].record(stl)
             h = C.c_void_p()
             lps.lps_logits_defer(ptr(self.logits_ring[k]), ptr(self.tok_ring) + 4 * k, cfg.vocab,
                                  sp(stl), sp(self.readback), ptr(self.host_logits[k]),
