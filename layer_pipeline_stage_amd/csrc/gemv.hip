@@ -5,14 +5,18 @@
 // byte, so these kernels are HBM-bound (ninfer "Multi-GPU: layer pipeline
 // stages", What it is and is not: decode is weight-bandwidth-bound).  Design:
 //  - one wave (64 lanes) computes one "unit" of two rows; lane l takes the
-//    16-byte chunks l, l+64, l+128, ... of both rows, so a wave issues fully
-//    coalesced 1 KiB loads per instruction and keeps U of them in flight per
-//    row; every chunk of a row always lands on the same lane in the same order
-//    whatever the row length, so zero chunks appended at the end of K (the
-//    padded dummy columns) leave each lane's partial sum, and the result,
-//    bit for bit unchanged;
+//    16-byte chunks l, l+64, l+128, ... of both rows, so every load instruction
+//    of a wave moves 1 KiB of one row, fully coalesced; every chunk of a row
+//    always lands on the same lane in the same order whatever the row length,
+//    so zero chunks appended at the end of K (the padded dummy columns) leave
+//    each lane's partial sum, and the result, bit for bit unchanged;
+//  - a wave walks its units in batches of U chunks per lane and row, and issues
+//    the loads of the next batch before the FMAs of the current one (double
+//    buffering in registers), through buffer resources sized to the row, so a
+//    ragged last batch needs no per-lane branch;
 //  - the activation vector (f32, optionally RMS-normalised on the way in) sits
-//    in LDS, read once per block from L2 and shared by the block's waves;
+//    in LDS, copied there by the LDS DMA path, read once per block from L2 and
+//    shared by the block's waves;
 //  - the two rows of a unit are chosen so that the epilogue has what it needs:
 //    rows (i, i + hd/2) of one head for RoPE, rows (i, ff + i) for SwiGLU;
 //  - MXFP4 chunks are 16 bytes of codes = one 32-value e8m0 group, decoded by
@@ -107,56 +111,36 @@ __device__ __forceinline__ void epilogue(const GemvP& p, int u, int r0, int r1, 
   }
 }
 
-// threads per GEMV workgroup and the grid cap (workgroups); a block stages the
-// activation vector once for all of its waves
-#ifndef LPS_GEMV_NT
-#define LPS_GEMV_NT 256
+// Launch shapes: threads per workgroup, workgroup cap and U (chunks per lane
+// and row in one batch).  Every workgroup stages the activation vector once, so
+// staging costs grid * 4K bytes of L2 reads next to the N * K weight bytes.
+//  - f32 / bf16 rows: 256 threads, up to 2048 groups, U = 4;
+//  - MXFP4 rows (0.53 bytes per weight, so the f32 vector is large next to a
+//    row): U is the row's chunks per lane rounded up to 3, 5 or 9, so one batch
+//    holds a whole row; 512-thread groups for short rows (many units per wave,
+//    double-buffered), 640-thread groups, one per CU, for long rows (about one
+//    unit per wave, all of it in flight at once).
+#ifndef LPS_BF_NT
+#define LPS_BF_NT 256
 #endif
-#ifndef LPS_GEMV_MAXB
-#define LPS_GEMV_MAXB 2048
+#ifndef LPS_BF_MAXB
+#define LPS_BF_MAXB 2048
 #endif
-constexpr int GEMV_NT = LPS_GEMV_NT;
-
-// Loads of one batch (U chunks of both rows of a unit), then its FMAs.  Kept as
-// macros over local arrays: the compiler then issues all 2U loads of a batch
-// before the first wait.
-#define GEMV_LOAD(J0)                                              \
-  _Pragma("unroll") for (int i = 0; i < U; ++i) {                  \
-    const int c = (J0) + WAVE * i;                                 \
-    if (c < nck) {                                                 \
-      v0[i] = ld_stream16(w0 + (long long)c * 16);                 \
-      v1[i] = ld_stream16(w1 + (long long)c * 16);                 \
-      if constexpr (WT == LPS_MXFP4) {                             \
-        sc0[i] = s0[c];                                            \
-        sc1[i] = s1[c];                                            \
-      } else {                                                     \
-        sc0[i] = sc1[i] = 0;                                       \
-      }                                                            \
-    } else {                                                       \
-      v0[i] = v1[i] = u32x4{0, 0, 0, 0};                           \
-      sc0[i] = sc1[i] = 127;                                       \
-    }                                                              \
-  }
-#define GEMV_FMA(J0)                                               \
-  _Pragma("unroll") for (int i = 0; i < U; ++i) {                  \
-    const int c = (J0) + WAVE * i;                                 \
-    if (c < nck) {                                                 \
-      acc_chunk<WT>(v0[i], sc0[i], xs + c * CH, a0);               \
-      acc_chunk<WT>(v1[i], sc1[i], xs + c * CH, a1);               \
-    }                                                              \
-  }
-#define GEMV_ROWS(UU)                                              \
-  int r0, r1;                                                      \
-  unit_rows<EPI>(p, (UU), r0, r1);                                 \
-  const int rr1 = r1 >= 0 ? r1 : r0;                               \
-  const uint8_t* w0 = p.w + (long long)r0 * p.wrow;                \
-  const uint8_t* w1 = p.w + (long long)rr1 * p.wrow;               \
-  const uint8_t* s0 = nullptr;                                     \
-  const uint8_t* s1 = nullptr;                                     \
-  if constexpr (WT == LPS_MXFP4) {                                 \
-    s0 = p.s + (long long)r0 * p.srow;                             \
-    s1 = p.s + (long long)rr1 * p.srow;                            \
-  }
+#ifndef LPS_BF_U
+#define LPS_BF_U 4
+#endif
+#ifndef LPS_MX_NT
+#define LPS_MX_NT 512
+#endif
+#ifndef LPS_MX_MAXB
+#define LPS_MX_MAXB 512
+#endif
+#ifndef LPS_MX_NTL
+#define LPS_MX_NTL 640
+#endif
+#ifndef LPS_MX_MAXBL
+#define LPS_MX_MAXBL 256
+#endif
 
 template <int EPI>
 __device__ __forceinline__ void finish(const GemvP& p, int u, int r0, int r1, float a0, float a1,
@@ -170,46 +154,125 @@ __device__ __forceinline__ void finish(const GemvP& p, int u, int r0, int r1, fl
   }
 }
 
-// PF: for launches where a wave's first unit fits one batch (K <= 64 U chunks),
-// that batch is loaded before the activation vector is staged, so its HBM
-// latency overlaps the staging and the norm; further units take the plain path.
-template <int WT, int EPI, int U, bool NORM, bool PF>
-__global__ __launch_bounds__(GEMV_NT) void k_gemv(GemvP p) {
+// A wave walks a flat sequence of
+// batches (unit u, chunk base b0 = 0, 64U, 128U, ...; both the same on every
+// lane) and issues the loads of the next batch, possibly of its next unit,
+// before the FMAs of the current one, so one batch's HBM latency hides behind
+// the previous batch's arithmetic.  Each row is read through a buffer resource
+// whose size is the row length: a chunk past the row end (the ragged last
+// batch) loads as zeros without a memory access, and the batch after the last
+// one gets a zero-size resource, so the loop has no per-lane branches and the
+// waits on the current batch never cover the next one.  Such lanes multiply the
+// zeros by a zero chunk of the staged vector (placed after its K values), which
+// adds exactly +0.  The per-lane chunk set and order are those of k_gemv.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+constexpr int BUF_DW3 = 0x00020000;   // gfx9 buffer descriptor word 3 (32-bit data format)
+constexpr int BUF_NT = 2;             // non-temporal load
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const uint8_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, bytes, BUF_DW3);
+}
+
+#define BUF_LOAD(V0, V1, S0, S1, UU, B0, LIVE)                                          \
+  {                                                                                     \
+    const int uu_ = (LIVE) ? (UU) : 0;                                                  \
+    int r0_, r1_;                                                                       \
+    unit_rows<EPI>(p, uu_, r0_, r1_);                                                   \
+    const int rr1_ = r1_ >= 0 ? r1_ : r0_;                                              \
+    const int wb_ = (LIVE) ? (int)p.wrow : 0;                                           \
+    const auto w0_ = row_rsrc(p.w + (long long)r0_ * p.wrow, wb_);                      \
+    const auto w1_ = row_rsrc(p.w + (long long)rr1_ * p.wrow, wb_);                     \
+    _Pragma("unroll") for (int i = 0; i < U; ++i) {                                     \
+      const int off = ((B0) + lane + WAVE * i) * 16;                                    \
+      V0[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w0_, off, 0, BUF_NT)); \
+      V1[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w1_, off, 0, BUF_NT)); \
+    }                                                                                   \
+    if constexpr (WT == LPS_MXFP4) {                                                    \
+      const int sb_ = (LIVE) ? (int)p.srow : 0;                                         \
+      const auto s0_ = row_rsrc(p.s + (long long)r0_ * p.srow, sb_);                    \
+      const auto s1_ = row_rsrc(p.s + (long long)rr1_ * p.srow, sb_);                   \
+      _Pragma("unroll") for (int i = 0; i < U; ++i) {                                   \
+        const int c = (B0) + lane + WAVE * i;                                           \
+        S0[i] = __builtin_amdgcn_raw_buffer_load_b8(s0_, c, 0, 0);                      \
+        S1[i] = __builtin_amdgcn_raw_buffer_load_b8(s1_, c, 0, 0);                      \
+      }                                                                                 \
+    } else {                                                                            \
+      _Pragma("unroll") for (int i = 0; i < U; ++i) S0[i] = S1[i] = 0;                  \
+    }                                                                                   \
+  }
+#define BUF_FMA(V0, V1, S0, S1, B0)                                \
+  _Pragma("unroll") for (int i = 0; i < U; ++i) {                  \
+    int c = (B0) + lane + WAVE * i;                                \
+    c = c < nck ? c : nck;                                         \
+    acc_chunk<WT>(V0[i], S0[i], xs + c * XS, a0);                  \
+    acc_chunk<WT>(V1[i], S1[i], xs + c * XS, a1);                  \
+  }
+#define BUF_STEP(CV0, CV1, CS0, CS1, NV0, NV1, NS0, NS1)           \
+  {                                                                \
+    int nu = u, nb = b0 + WAVE * U;                                \
+    if (nb >= nck) { nu = u + stride; nb = 0; }                    \
+    const bool more = nu < p.units;                                \
+    BUF_LOAD(NV0, NV1, NS0, NS1, nu, nb, more)                     \
+    BUF_FMA(CV0, CV1, CS0, CS1, b0)                                \
+    if (nu != u) {                                                 \
+      int r0, r1;                                                  \
+      unit_rows<EPI>(p, u, r0, r1);                                \
+      finish<EPI>(p, u, r0, r1, a0, a1, lane, best, bidx);         \
+      a0 = a1 = 0.f;                                               \
+    }                                                              \
+    if (!more) break;                                              \
+    u = nu;                                                        \
+    b0 = nb;                                                       \
+  }
+
+template <int WT, int EPI, int U, bool NORM, int NT, bool DB>
+__global__ __launch_bounds__(NT) void k_gemv_buf(GemvP p) {
   extern __shared__ float xs[];
   constexpr int CH = Fmt<WT>::CH;
-  constexpr int NW = GEMV_NT / WAVE;
+  constexpr int XS = WT == LPS_MXFP4 ? MX_XS : CH;   // staged floats per chunk
+  constexpr int NW = NT / WAVE;
   const int lane = threadIdx.x & (WAVE - 1);
-  const int wv = threadIdx.x / WAVE;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
   const int nck = p.K / CH;
-  float best = -INFINITY;   // EPI_LOGITS: rows rise with u, so '>' keeps the first maximum
+  const int stride = gridDim.x * NW;
+  float best = -INFINITY;
   int bidx = 0x7fffffff;
   int u = blockIdx.x * NW + wv;
-  if constexpr (PF) {
-    const int uu = u < p.units ? u : p.units - 1;   // waves without a unit load a valid row
-    GEMV_ROWS(uu)
-    u32x4 v0[U], v1[U];
-    uint32_t sc0[U], sc1[U];
-    GEMV_LOAD(lane)
-    stage_x<NORM, GEMV_NT>(p.x, p.g, p.eps, p.K, xs);
-    if (u < p.units) {
-      float a0 = 0.f, a1 = 0.f;
-      GEMV_FMA(lane)
-      finish<EPI>(p, u, r0, r1, a0, a1, lane, best, bidx);
-    }
-    u += gridDim.x * NW;
+  int b0 = 0;
+  u32x4 va0[U], va1[U], vb0[U], vb1[U];
+  uint32_t sa0[U], sa1[U], sb0[U], sb1[U];
+  BUF_LOAD(va0, va1, sa0, sa1, u, 0, u < p.units)
+  if constexpr (WT == LPS_MXFP4) {
+    stage_x_mx<NORM, NT>(p.x, p.g, p.eps, p.K, xs);
   } else {
-    stage_x<NORM, GEMV_NT>(p.x, p.g, p.eps, p.K, xs);
+    if (threadIdx.x < CH) xs[p.K + threadIdx.x] = 0.f;   // zero chunk
+    stage_x<NORM, NT>(p.x, p.g, p.eps, p.K, xs);
   }
-  for (; u < p.units; u += gridDim.x * NW) {
-    GEMV_ROWS(u)
+  if (u < p.units) {
     float a0 = 0.f, a1 = 0.f;
-    for (int j0 = lane; j0 < nck; j0 += WAVE * U) {
-      u32x4 v0[U], v1[U];
-      uint32_t sc0[U], sc1[U];
-      GEMV_LOAD(j0)
-      GEMV_FMA(j0)
+    if constexpr (DB) {
+      for (;;) {
+        BUF_STEP(va0, va1, sa0, sa1, vb0, vb1, sb0, sb1)
+        BUF_STEP(vb0, vb1, sb0, sb1, va0, va1, sa0, sa1)
+      }
+    } else {
+      // one batch in flight per wave, for launches where a wave meets one batch
+      for (;;) {
+        BUF_FMA(va0, va1, sa0, sa1, b0)
+        int nu = u, nb = b0 + WAVE * U;
+        if (nb >= nck) { nu = u + stride; nb = 0; }
+        if (nu != u) {
+          int r0, r1;
+          unit_rows<EPI>(p, u, r0, r1);
+          finish<EPI>(p, u, r0, r1, a0, a1, lane, best, bidx);
+          a0 = a1 = 0.f;
+        }
+        if (nu >= p.units) break;
+        u = nu;
+        b0 = nb;
+        BUF_LOAD(va0, va1, sa0, sa1, u, b0, true)
+      }
     }
-    finish<EPI>(p, u, r0, r1, a0, a1, lane, best, bidx);
   }
   if constexpr (EPI == EPI_LOGITS) {
     if (lane == 0) {
@@ -218,9 +281,9 @@ __global__ __launch_bounds__(GEMV_NT) void k_gemv(GemvP p) {
     }
   }
 }
-#undef GEMV_LOAD
-#undef GEMV_FMA
-#undef GEMV_ROWS
+#undef BUF_LOAD
+#undef BUF_FMA
+#undef BUF_STEP
 
 // A16 argmax over the LM head's per-wave partials (value, lowest index with
 // that value), one workgroup: max with ties to the lower index is an exact
@@ -254,48 +317,52 @@ __global__ __launch_bounds__(1024) void k_argmax(const float* pval, const int* p
 }
 
 // ---- launch configuration ---------------------------------------------------
-static int max_blocks() { return LPS_GEMV_MAXB; }
-
-
-
+// DB: several batches per wave (double-buffered walk); otherwise each wave meets
+// at most one batch and keeps a single set of registers.
 template <int WT, int EPI, bool NORM>
-static int launch_t(const GemvP& p, hipStream_t st, Stamp sp) {
-  const int NW = GEMV_NT / WAVE;
-  int grid = (p.units + NW - 1) / NW;
-  if (grid > max_blocks()) grid = max_blocks();
-  if (grid < 1) grid = 1;
-  const size_t lds = size_t(p.K) * sizeof(float);
+static int launch_t(const GemvP& p, hipStream_t st, Stamp sp, int* waves) {
   constexpr int CH = Fmt<WT>::CH;
   const int per_lane = (p.K / CH + WAVE - 1) / WAVE;
-  // keep up to 8 (bf16 / f32) or 4 (MXFP4, whose decode needs more registers)
-  // chunk loads per row in flight per lane; prefetch under the staging when a
-  // wave has at most two units
-  const bool pf = per_lane <= (per_lane <= 4 || WT == LPS_MXFP4 ? 4 : 8) && p.units <= 2 * grid * NW;
-#define LPS_GO(UU, PFV)                                                                     \
-  do {                                                                                      \
-    int rc_ = ensure_lds((const void*)k_gemv<WT, EPI, UU, NORM, PFV>, lds);                 \
-    if (rc_) return rc_;                                                                    \
-    hipExtLaunchKernelGGL((k_gemv<WT, EPI, UU, NORM, PFV>), dim3(grid), dim3(GEMV_NT), lds, \
-                          st, sp.start, sp.stop, 0, p);                                     \
+  const size_t lds = WT == LPS_MXFP4 ? size_t(p.K / CH + 1) * MX_XS * sizeof(float)
+                                     : (size_t(p.K) + CH) * sizeof(float);
+#define LPS_GOB(UU, NTV, MAXBV)                                                                  \
+  do {                                                                                           \
+    constexpr int NW_ = (NTV) / WAVE;                                                            \
+    int grid = (p.units + NW_ - 1) / NW_;                                                        \
+    if (grid > (MAXBV)) grid = (MAXBV);                                                          \
+    if (grid < 1) grid = 1;                                                                      \
+    const bool db = p.units > grid * NW_ || per_lane > (UU);                                     \
+    if (waves) *waves = grid * NW_;                                                              \
+    const void* fn_ = db ? (const void*)k_gemv_buf<WT, EPI, UU, NORM, NTV, true>                 \
+                         : (const void*)k_gemv_buf<WT, EPI, UU, NORM, NTV, false>;               \
+    int rc_ = ensure_lds(fn_, lds);                                                              \
+    if (rc_) return rc_;                                                                         \
+    if (db)                                                                                      \
+      hipExtLaunchKernelGGL((k_gemv_buf<WT, EPI, UU, NORM, NTV, true>), dim3(grid), dim3(NTV),   \
+                            lds, st, sp.start, sp.stop, 0, p);                                   \
+    else                                                                                         \
+      hipExtLaunchKernelGGL((k_gemv_buf<WT, EPI, UU, NORM, NTV, false>), dim3(grid), dim3(NTV),  \
+                            lds, st, sp.start, sp.stop, 0, p);                                   \
   } while (0)
-  if (per_lane <= 4 || WT == LPS_MXFP4) {
-    if (pf) LPS_GO(4, true);
-    else LPS_GO(4, false);
+  if constexpr (WT == LPS_MXFP4) {
+    if (per_lane <= 3) LPS_GOB(3, LPS_MX_NT, LPS_MX_MAXB);
+    else if (per_lane <= 5) LPS_GOB(5, LPS_MX_NTL, LPS_MX_MAXBL);
+    else if (per_lane <= 9) LPS_GOB(9, LPS_MX_NTL, LPS_MX_MAXBL);
+    else LPS_GOB(4, LPS_MX_NT, LPS_MX_MAXB);
   } else {
-    if (pf) LPS_GO(8, true);
-    else LPS_GO(8, false);
+    LPS_GOB(LPS_BF_U, LPS_BF_NT, LPS_BF_MAXB);
   }
-#undef LPS_GO
+#undef LPS_GOB
   LPS_HIP(hipGetLastError());
   return LPS_OK;
 }
 
 template <int EPI, bool NORM>
-static int launch_wt(int wdtype, const GemvP& p, hipStream_t st, Stamp sp) {
+static int launch_wt(int wdtype, const GemvP& p, hipStream_t st, Stamp sp, int* waves = nullptr) {
   switch (wdtype) {
-    case LPS_F32: return launch_t<LPS_F32, EPI, NORM>(p, st, sp);
-    case LPS_BF16: return launch_t<LPS_BF16, EPI, NORM>(p, st, sp);
-    case LPS_MXFP4: return launch_t<LPS_MXFP4, EPI, NORM>(p, st, sp);
+    case LPS_F32: return launch_t<LPS_F32, EPI, NORM>(p, st, sp, waves);
+    case LPS_BF16: return launch_t<LPS_BF16, EPI, NORM>(p, st, sp, waves);
+    case LPS_MXFP4: return launch_t<LPS_MXFP4, EPI, NORM>(p, st, sp, waves);
   }
   return fail(LPS_EINVAL, "gemv: unknown wdtype %d", wdtype);
 }
@@ -361,9 +428,12 @@ int launch_qkv(const QkvArgs& a, hipStream_t st, Stamp sp) {
   return launch_wt<EPI_QKV, true>(L->wdtype, p, st, sp);
 }
 
+// most per-wave (value, index) partials an LM-head launch can write
+static size_t head_waves_max() { return size_t(LPS_BF_MAXB) * (LPS_BF_NT / WAVE); }
+
 size_t head_scratch(const lps_head_desc* h) {
   (void)h;
-  return 2 * align256(size_t(LPS_GEMV_MAXB) * (GEMV_NT / WAVE) * 4);
+  return 2 * align256(head_waves_max() * 4);
 }
 
 int launch_head(const lps_head_desc* h, const float* x, float* logits, int32_t* tok, void* scratch,
@@ -381,14 +451,12 @@ int launch_head(const lps_head_desc* h, const float* x, float* logits, int32_t* 
   set_rows(p, h->wdtype, h->d);
   char* sc = static_cast<char*>(scratch);
   p.pval = reinterpret_cast<float*>(sc);
-  p.pidx = reinterpret_cast<int*>(sc + align256(size_t(LPS_GEMV_MAXB) * (GEMV_NT / WAVE) * 4));
-  int rc = launch_wt<EPI_LOGITS, true>(h->wdtype, p, st, Stamp{sp.start, nullptr});
+  p.pidx = reinterpret_cast<int*>(sc + align256(head_waves_max() * 4));
+  int waves = 0;
+  int rc = launch_wt<EPI_LOGITS, true>(h->wdtype, p, st, Stamp{sp.start, nullptr}, &waves);
   if (rc) return rc;
-  const int NW = GEMV_NT / WAVE;
-  int grid = (p.units + NW - 1) / NW;
-  if (grid > max_blocks()) grid = max_blocks();
   hipExtLaunchKernelGGL(k_argmax, dim3(1), dim3(1024), 0, st, nullptr, sp.stop, 0, p.pval, p.pidx,
-                        grid * NW, tok);
+                        waves, tok);
   LPS_HIP(hipGetLastError());
   return LPS_OK;
 }

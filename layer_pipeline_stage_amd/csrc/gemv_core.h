@@ -15,11 +15,12 @@ template <> struct Fmt<LPS_MXFP4> { static constexpr int CH = 32; };
 
 constexpr int GEMV_THREADS = 256;
 
-// e8m0 byte -> f32 scale 2^(s-127) (0 -> 2^-127 subnormal, 255 -> NaN).
+// e8m0 byte -> f32 scale 2^(s-127) (0 -> 2^-127 subnormal, 255 -> NaN), without
+// branches: s << 23 is the exponent field; bit 22 turns 0 into the subnormal
+// 2^-127 and the all-ones exponent into a quiet NaN.
 __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
-  if (s == 0) return __uint_as_float(0x00400000u);
-  if (s == 255) return __uint_as_float(0x7FC00000u);
-  return __uint_as_float(s << 23);
+  const uint32_t edge = ((s + 1u) & 0xFFu) < 2u ? 0x00400000u : 0u;
+  return __uint_as_float((s << 23) | edge);
 }
 
 template <int WT>
@@ -66,24 +67,37 @@ __device__ __forceinline__ void acc_chunk(const u32x4 v, uint32_t sb, const floa
   }
 }
 
-// Stage the activation vector in LDS; with NORM, as RMSNorm(x) * g.
+// Stage the activation vector in LDS; with NORM, as RMSNorm(x) * g.  The copy
+// uses the LDS DMA path (global_load_lds_dwordx4: each lane's 16 bytes land at
+// the wave's LDS base + 16 * lane, no VGPRs): every wave issues all of its
+// 1 KiB pieces back to back, so staging costs one L2 round trip rather than one
+// per piece.  x must be 16-byte aligned and K a multiple of 4.
 template <bool NORM, int NT = GEMV_THREADS>
 __device__ __forceinline__ void stage_x(const float* x, const float* g, float eps, int K, float* xs) {
+  constexpr int NW = NT / WAVE;
   const int tid = threadIdx.x;
-  float ss = 0.f;
-  for (int k = tid * 4; k < K; k += NT * 4) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(x + k);
-    *reinterpret_cast<f32x4*>(xs + k) = v;
-    if (NORM) ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  const int lane = tid & (WAVE - 1);
+  const int wv = tid / WAVE;
+  for (int b = wv * 256; b < K; b += NW * 256) {
+    if (b + 4 * lane < K)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(x + b + 4 * lane),
+                                       (__attribute__((address_space(3))) void*)(xs + b), 16, 0, 0);
   }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
   if (NORM) {
-    __shared__ float red[NT / WAVE];
+    __shared__ float red[NW];
+    float ss = 0.f;
+    for (int k = tid * 4; k < K; k += NT * 4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(xs + k);
+      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
     ss = wave_sum(ss);
-    if ((tid & (WAVE - 1)) == 0) red[tid / WAVE] = ss;
+    if (lane == 0) red[wv] = ss;
     __syncthreads();
     float tot = 0.f;
 #pragma unroll
-    for (int i = 0; i < NT / WAVE; ++i) tot += red[i];
+    for (int i = 0; i < NW; ++i) tot += red[i];
     const float r = 1.0f / sqrtf(tot / float(K) + eps);
     for (int k = tid * 4; k < K; k += NT * 4) {
       f32x4 v = *reinterpret_cast<f32x4*>(xs + k);
@@ -94,8 +108,63 @@ __device__ __forceinline__ void stage_x(const float* x, const float* g, float ep
       v.w = v.w * r * gg.w;
       *reinterpret_cast<f32x4*>(xs + k) = v;
     }
+    __syncthreads();
   }
+}
+
+// Stage x for the MXFP4 GEMV, 32-value chunks (8 groups of 16 bytes) placed at
+// a stride of 9 groups (144 bytes).  Lane l of a wave reads the chunk of its
+// own weight chunk, so lanes are one chunk apart: at the packed 128-byte stride
+// every lane of a ds_read_b128 falls on the same four LDS banks, at 144 bytes
+// eight consecutive lanes cover 32 distinct banks.  The chunk after the last
+// (index K / 32) is zero.  Same LDS DMA copy and RMSNorm as stage_x; the x
+// values themselves, their order of use and the norm arithmetic are unchanged.
+constexpr int MX_XS = 36;   // floats per staged MXFP4 chunk (32 values + 4 pad)
+
+template <bool NORM, int NT>
+__device__ __forceinline__ void stage_x_mx(const float* x, const float* g, float eps, int K, float* xs) {
+  constexpr int NW = NT / WAVE;
+  const int tid = threadIdx.x;
+  const int lane = tid & (WAVE - 1);
+  const int wv = tid / WAVE;
+  const int ng = K / 4;              // data groups
+  const int np = (K / 32) * 9;       // physical groups
+  for (int b = wv * WAVE; b < np; b += NW * WAVE) {
+    const int P = b + lane;
+    const int c = P / 9, q = P - 9 * c;
+    if (P < np && q < 8)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(x + 4 * (8 * c + q)),
+                                       (__attribute__((address_space(3))) void*)(xs + 4 * b), 16, 0, 0);
+  }
+  if (tid < 32) xs[4 * np + tid] = 0.f;   // zero chunk
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  if (NORM) {
+    __shared__ float red[NW];
+    float ss = 0.f;
+    for (int G = tid; G < ng; G += NT) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(xs + 4 * (G + (G >> 3)));
+      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) red[wv] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) tot += red[i];
+    const float r = 1.0f / sqrtf(tot / float(K) + eps);
+    for (int G = tid; G < ng; G += NT) {
+      float* px = xs + 4 * (G + (G >> 3));
+      f32x4 v = *reinterpret_cast<f32x4*>(px);
+      const f32x4 gg = *reinterpret_cast<const f32x4*>(g + 4 * G);
+      v.x = v.x * r * gg.x;
+      v.y = v.y * r * gg.y;
+      v.z = v.z * r * gg.z;
+      v.w = v.w * r * gg.w;
+      *reinterpret_cast<f32x4*>(px) = v;
+    }
+    __syncthreads();
+  }
 }
 
 }  // namespace lps

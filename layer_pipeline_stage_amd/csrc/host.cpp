@@ -401,8 +401,8 @@ int lps_head_forward(const lps_head_desc* h, const float* x, float* logits, int3
   LPS_REQUIRE(h->d > 0 && h->vocab > 0, LPS_EINVAL, "lps_head_forward: d %d / vocab %d", h->d, h->vocab);
   LPS_REQUIRE(h->wdtype == LPS_F32 || h->wdtype == LPS_BF16, LPS_EINVAL,
               "lps_head_forward: wdtype %d (f32 or bf16)", h->wdtype);
-  LPS_REQUIRE(h->d % chunk_of(h->wdtype) == 0 && size_t(h->d) * 4 <= 160 * 1024, LPS_EINVAL,
-              "lps_head_forward: d %d", h->d);
+  LPS_REQUIRE(h->d % chunk_of(h->wdtype) == 0 && h->d <= 8192, LPS_EINVAL,
+              "lps_head_forward: d %d (a multiple of the weight chunk, at most 8192)", h->d);
   LPS_REQUIRE(h->g_out && h->w_lm && x && logits && tok_out && scratch, LPS_EINVAL,
               "lps_head_forward: null pointer");
   LPS_REQUIRE(aligned16(h->w_lm) && aligned16(h->g_out) && aligned16(x), LPS_EINVAL,
