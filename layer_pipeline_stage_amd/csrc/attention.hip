@@ -6,7 +6,7 @@
 // K and V rows are streamed once from HBM with 16-byte loads and reused by all
 // G query heads of the group; scores are reduced across the lanes of a row by
 // DPP row operations, the chunk softmax (max, sum) by wave reductions, and the
-// V tile is staged in LDS so that each thread forms whole output columns.  Each tile
+// weighted V sum is formed in registers and summed over row slots in LDS.  Each tile
 // writes (m, l, o) partials; a second small launch merges every q head's chunks
 // in chunk order, so the result does not depend on the order the tiles ran in
 // (and no tile waits on, or fences for, another).
@@ -17,9 +17,16 @@
 
 namespace lps {
 
-constexpr int ATT_THREADS = 256;
+#ifndef LPS_ATT_THREADS
+#define LPS_ATT_THREADS 256
+#endif
+#ifndef LPS_ATT_CH
+#define LPS_ATT_CH 128
+#endif
+constexpr int ATT_THREADS = LPS_ATT_THREADS;
 constexpr int ATT_NW = ATT_THREADS / WAVE;
-constexpr int ATT_CH = 64;  // cache rows per tile
+constexpr int ATT_CH = LPS_ATT_CH;  // cache rows per tile
+constexpr int ATT_RPL = ATT_CH / WAVE;   // rows per lane in the tile softmax
 
 struct AttnP {
   const void* kc;
@@ -62,18 +69,21 @@ __device__ __forceinline__ void widen16(const u32x4 v, float* out) {
   }
 }
 
-// at head dim 256 the tile's K rows and the G query heads compete for registers:
-// ask for at least 3 waves per SIMD
+// Thread (li, rr) of a tile owns elements li*E16 .. li*E16 + E16 - 1 of the rows
+// rr, rr + RPP, rr + 2 RPP, ...: its K and V loads are 16 bytes each and all
+// of them go out first (one HBM round trip per tile).  The G query heads'
+// matching elements stay in registers.  Scores are summed over the LPR lanes of
+// a row with DPP steps; the chunk softmax (max, sum) is one wave per head over
+// the 64 rows; the weighted V sum is formed in registers from the thread's own
+// V rows and summed over the RPP row slots through LDS, in slot order.
 template <int HD, int KVT, int G>
-__global__ __launch_bounds__(ATT_THREADS, HD >= 256 ? 3 : 1) void k_attn(AttnP p) {
+__global__ __launch_bounds__(ATT_THREADS) void k_attn(AttnP p) {
   using C = AttnCfg<HD, KVT>;
   constexpr int E16 = C::E16, LPR = C::LPR, RPP = C::RPP;
   constexpr int NP = ATT_CH / RPP;          // rows per thread
   constexpr int ESZ = C::ESZ;
-  constexpr int VROW = HD * ESZ + 16;       // LDS bytes per V row (padded against bank conflicts)
-  __shared__ float qs[G][HD];
   __shared__ float sc[G][ATT_CH];
-  __shared__ __attribute__((aligned(16))) char vs[ATT_CH * VROW];
+  extern __shared__ float red[];            // [RPP][G][HD]
 
   const int chunk = blockIdx.x, g = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wv = tid / WAVE;
@@ -81,7 +91,6 @@ __global__ __launch_bounds__(ATT_THREADS, HD >= 256 ? 3 : 1) void k_attn(AttnP p
   const int row0 = chunk * ATT_CH;
   const long long head_base = (long long)g * p.ctx_max * HD;
 
-  // every K and V load of the tile goes out first: one HBM round trip
   u32x4 kraw[NP], vraw[NP];
 #pragma unroll
   for (int ps = 0; ps < NP; ++ps) {
@@ -94,14 +103,21 @@ __global__ __launch_bounds__(ATT_THREADS, HD >= 256 ? 3 : 1) void k_attn(AttnP p
       kraw[ps] = vraw[ps] = u32x4{0, 0, 0, 0};   // rows past n: zero V, -inf score
     }
   }
-  for (int i = tid; i < G * HD; i += ATT_THREADS) qs[i / HD][i % HD] = p.q[(g * G) * HD + i];
-  // the V tile is staged in LDS for the weighted sum (read there by output column)
+  float qv[G][E16];
 #pragma unroll
-  for (int ps = 0; ps < NP; ++ps)
-    *reinterpret_cast<u32x4*>(vs + (ps * RPP + rr) * VROW + li * 16) = vraw[ps];
-  __syncthreads();
+  for (int h = 0; h < G; ++h) {
+    const float* qh = p.q + (long long)(g * G + h) * HD + li * E16;
+#pragma unroll
+    for (int e = 0; e < E16; e += 4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(qh + e);
+      qv[h][e] = v.x;
+      qv[h][e + 1] = v.y;
+      qv[h][e + 2] = v.z;
+      qv[h][e + 3] = v.w;
+    }
+  }
 
-  // ---- scores s[h][j] = q_h . k_j * scale: LPR lanes per row, DPP sums ----
+  // ---- scores s[h][j] = q_h . k_j * scale ----
 #pragma unroll
   for (int ps = 0; ps < NP; ++ps) {
     const int jl = ps * RPP + rr;
@@ -113,7 +129,7 @@ __global__ __launch_bounds__(ATT_THREADS, HD >= 256 ? 3 : 1) void k_attn(AttnP p
     for (int h = 0; h < G; ++h) {
       s[h] = 0.f;
 #pragma unroll
-      for (int e = 0; e < E16; ++e) s[h] = fmaf(kv[e], qs[h][li * E16 + e], s[h]);
+      for (int e = 0; e < E16; ++e) s[h] = fmaf(kv[e], qv[h][e], s[h]);
     }
 #pragma unroll
     for (int h = 0; h < G; ++h) s[h] = group_sum<LPR>(s[h]);
@@ -123,13 +139,24 @@ __global__ __launch_bounds__(ATT_THREADS, HD >= 256 ? 3 : 1) void k_attn(AttnP p
     }
   }
   __syncthreads();
-  // ---- chunk softmax: one wave per head, one row per lane ----
+  // ---- chunk softmax: one wave per head, ATT_RPL rows per lane ----
   for (int h = wv; h < G; h += ATT_NW) {
-    const float v = sc[h][lane];
-    const float m = wave_max(v);
-    const float e = (v == -INFINITY) ? 0.f : expf(v - m);
-    const float l = wave_sum(e);
-    sc[h][lane] = e;
+    float v[ATT_RPL];
+    float m = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < ATT_RPL; ++r) {
+      v[r] = sc[h][lane + WAVE * r];
+      m = fmaxf(m, v[r]);
+    }
+    m = wave_max(m);
+    float l = 0.f;
+#pragma unroll
+    for (int r = 0; r < ATT_RPL; ++r) {
+      const float e = (v[r] == -INFINITY) ? 0.f : expf(v[r] - m);
+      sc[h][lane + WAVE * r] = e;
+      l += e;
+    }
+    l = wave_sum(l);
     if (lane == 0) {
       const long long pi = ((long long)g * p.nch + chunk) * G + h;
       p.pm[pi] = m;
@@ -137,102 +164,125 @@ __global__ __launch_bounds__(ATT_THREADS, HD >= 256 ? 3 : 1) void k_attn(AttnP p
     }
   }
   __syncthreads();
-  // ---- o[h][e] = sum_j p[h][j] v_j[e]: one thread per (head, column pair) ----
+  // ---- o[h][e] = sum_j p[h][j] v_j[e]: per thread over its rows, then over slots ----
+  float acc[G][E16];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < E16; ++e) acc[h][e] = 0.f;
+#pragma unroll
+  for (int ps = 0; ps < NP; ++ps) {
+    const int jl = ps * RPP + rr;
+    float vv[E16];
+    widen16<KVT>(vraw[ps], vv);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float w = sc[h][jl];
+#pragma unroll
+      for (int e = 0; e < E16; ++e) acc[h][e] = fmaf(w, vv[e], acc[h][e]);
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < E16; e += 4)
+      *reinterpret_cast<f32x4*>(red + (rr * G + h) * HD + li * E16 + e) =
+          f32x4{acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]};
+  __syncthreads();
   const long long ob = ((long long)g * p.nch + chunk) * G * HD;
   for (int idx = tid; idx < G * (HD / 2); idx += ATT_THREADS) {
     const int h = idx / (HD / 2), e2 = idx - h * (HD / 2);
-    float a0 = 0.f, a1 = 0.f;
-#pragma unroll 8
-    for (int j = 0; j < ATT_CH; ++j) {
-      const float w = sc[h][j];
-      float v0, v1;
-      if constexpr (KVT == LPS_F32) {
-        const f32x2 v = *reinterpret_cast<const f32x2*>(vs + j * VROW + e2 * 8);
-        v0 = v.x;
-        v1 = v.y;
-      } else {
-        const uint32_t v = *reinterpret_cast<const uint32_t*>(vs + j * VROW + e2 * 4);
-        v0 = bf16_lo(v);
-        v1 = bf16_hi(v);
-      }
-      a0 = fmaf(w, v0, a0);
-      a1 = fmaf(w, v1, a1);
+    f32x2 o = *reinterpret_cast<const f32x2*>(red + h * HD + 2 * e2);
+#pragma unroll
+    for (int r = 1; r < RPP; ++r) {
+      const f32x2 v = *reinterpret_cast<const f32x2*>(red + (r * G + h) * HD + 2 * e2);
+      o.x += v.x;
+      o.y += v.y;
     }
-    *reinterpret_cast<f32x2*>(p.po + ob + h * HD + 2 * e2) = f32x2{a0, a1};
+    *reinterpret_cast<f32x2*>(p.po + ob + h * HD + 2 * e2) = o;
   }
 }
 
-// Merge of the chunk partials of one q head, in chunk order: M = max m_c,
-// L = sum_c l_c e^(m_c - M), o = sum_c o_c e^(m_c - M) / L.  A separate launch:
-// the partials of all tiles are complete when it starts (stream order), so no
-// device-scope fence or counter is needed.  1024 threads per head: thread
-// (part, e) sums the chunks c = part (mod P) for element e, with all of its
-// loads in flight at once, and the P partial sums are added in part order.
+// Merge of the chunk partials of one q head: M = max m_c, L = sum_c l_c
+// e^(m_c - M), o = sum_c o_c e^(m_c - M) / L.  A separate launch: the partials
+// of all tiles are complete when it starts (stream order), so no device-scope
+// fence or counter is needed.  One workgroup per q head; thread (part, e2) owns
+// output columns 2 e2, 2 e2 + 1 and the chunks c = part (mod P).  It loads the
+// (m, l, o) of up to MERGE_B of its chunks at once, so a typical context costs
+// one L2 round trip, and keeps a running maximum with rescaling.  The P part
+// results are combined in part order: the result does not depend on timing.
 constexpr int MERGE_THREADS = 1024;
-constexpr int MERGE_CH = 1024;   // chunk weights staged in LDS per round
+constexpr int MERGE_B = 8;   // chunks per thread in flight
 
 template <int HD>
 __global__ __launch_bounds__(MERGE_THREADS) void k_attn_merge(AttnP p) {
-  constexpr int P = MERGE_THREADS / HD;
-  constexpr int NWM = MERGE_THREADS / WAVE;
+  constexpr int TPH = HD / 2;                  // threads per part
+  constexpr int P = MERGE_THREADS / TPH;
   const int hq = blockIdx.x;               // q head
   const int g = hq / p.G, h = hq - g * p.G;
-  const int t = threadIdx.x, e = t % HD, part = t / HD;
-  __shared__ float wsh[MERGE_CH];
-  __shared__ float red[NWM];
-  __shared__ float opart[P][HD];
+  const int t = threadIdx.x, e2 = t % TPH, part = t / TPH;
+  __shared__ float sM[P], sL[P];
+  __shared__ f32x2 sO[P][TPH];
   const long long base = (long long)g * p.nch;
-  // one read of every chunk's (m, l): the first MERGE_CH chunks stay in registers
-  float mreg = -INFINITY, lreg = 0.f;
-  if (t < p.nch) {
-    mreg = p.pm[(base + t) * p.G + h];
-    lreg = p.pl[(base + t) * p.G + h];
-  }
-  float M = mreg;
-  for (int c = t + MERGE_THREADS; c < p.nch; c += MERGE_THREADS) M = fmaxf(M, p.pm[(base + c) * p.G + h]);
-  M = wave_max(M);
-  if ((t & (WAVE - 1)) == 0) red[t / WAVE] = M;
-  __syncthreads();
-  M = red[0];
-#pragma unroll
-  for (int i = 1; i < NWM; ++i) M = fmaxf(M, red[i]);
-  float Lp = 0.f, O = 0.f;
   const long long step = (long long)p.G * HD;
-  for (int c0 = 0; c0 < p.nch; c0 += MERGE_CH) {
-    const int n = min(MERGE_CH, p.nch - c0);
-    __syncthreads();
-    for (int c = t; c < n; c += MERGE_THREADS) {
-      const long long pi = (base + c0 + c) * p.G + h;
-      const bool first = c0 == 0 && c == t;
-      const float w = expf((first ? mreg : p.pm[pi]) - M);
-      wsh[c] = w;
-      Lp = fmaf(w, first ? lreg : p.pl[pi], Lp);
-    }
-    __syncthreads();
-    const float* po = p.po + ((base + c0) * p.G + h) * HD + e;
-    int c = part;
-    for (; c + 7 * P < n; c += 8 * P) {
-      float v[8];
+  const float* po = p.po + (base * p.G + h) * HD + 2 * e2;
+  float M = -INFINITY, L = 0.f;
+  f32x2 O = {0.f, 0.f};
+  for (int c0 = part; c0 < p.nch; c0 += MERGE_B * P) {
+    float mv[MERGE_B], lv[MERGE_B];
+    f32x2 ov[MERGE_B];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = po[(c + k * P) * step];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) O = fmaf(wsh[c + k * P], v[k], O);
+    for (int k = 0; k < MERGE_B; ++k) {
+      const int c = c0 + k * P;
+      if (c < p.nch) {
+        const long long pi = (base + c) * p.G + h;
+        mv[k] = p.pm[pi];
+        lv[k] = p.pl[pi];
+        ov[k] = *reinterpret_cast<const f32x2*>(po + c * step);
+      } else {
+        mv[k] = -INFINITY;
+        lv[k] = 0.f;
+        ov[k] = f32x2{0.f, 0.f};
+      }
     }
-    for (; c < n; c += P) O = fmaf(wsh[c], po[c * step], O);
+    float Mn = M;
+#pragma unroll
+    for (int k = 0; k < MERGE_B; ++k) Mn = fmaxf(Mn, mv[k]);
+    if (Mn != -INFINITY) {
+      const float r = M == -INFINITY ? 0.f : expf(M - Mn);
+      L *= r;
+      O.x *= r;
+      O.y *= r;
+#pragma unroll
+      for (int k = 0; k < MERGE_B; ++k) {
+        const float w = mv[k] == -INFINITY ? 0.f : expf(mv[k] - Mn);
+        L = fmaf(w, lv[k], L);
+        O.x = fmaf(w, ov[k].x, O.x);
+        O.y = fmaf(w, ov[k].y, O.y);
+      }
+      M = Mn;
+    }
   }
-  opart[part][e] = O;
+  sO[part][e2] = O;
+  if (e2 == 0) {
+    sM[part] = M;
+    sL[part] = L;
+  }
   __syncthreads();
-  Lp = wave_sum(Lp);
-  if ((t & (WAVE - 1)) == 0) red[t / WAVE] = Lp;
-  __syncthreads();
-  if (t < HD) {
-    float L = 0.f;
+  if (t < TPH) {
+    float Mt = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < NWM; ++i) L += red[i];
-    float o = opart[0][e];
+    for (int q = 0; q < P; ++q) Mt = fmaxf(Mt, sM[q]);
+    float Lt = 0.f;
+    f32x2 o = {0.f, 0.f};
 #pragma unroll
-    for (int q = 1; q < P; ++q) o += opart[q][e];
-    p.o[(long long)hq * HD + e] = o / L;
+    for (int q = 0; q < P; ++q) {
+      const float w = sM[q] == -INFINITY ? 0.f : expf(sM[q] - Mt);
+      Lt = fmaf(w, sL[q], Lt);
+      o.x = fmaf(w, sO[q][t].x, o.x);
+      o.y = fmaf(w, sO[q][t].y, o.y);
+    }
+    *reinterpret_cast<f32x2*>(p.o + (long long)hq * HD + 2 * t) = f32x2{o.x / Lt, o.y / Lt};
   }
 }
 
@@ -244,18 +294,28 @@ size_t attn_scratch(int nq, int nkv, int hd, int ctx_max) {
   return 2 * align256(size_t(nkv) * nch * G * 4) + align256(size_t(nkv) * nch * G * hd * 4);
 }
 
+template <int HD, int KVT, int G>
+static int go_g(const AttnP& p, int nkv, hipStream_t st, hipEvent_t start) {
+  const size_t lds = size_t(AttnCfg<HD, KVT>::RPP) * G * HD * sizeof(float);
+  int rc = ensure_lds((const void*)k_attn<HD, KVT, G>, lds);
+  if (rc) return rc;
+  hipExtLaunchKernelGGL((k_attn<HD, KVT, G>), dim3(p.nch, nkv), dim3(ATT_THREADS), lds, st, start,
+                        nullptr, 0, p);
+  return LPS_OK;
+}
+
 template <int HD, int KVT>
 static int go(const AttnP& p, int nkv, hipStream_t st, Stamp sp) {
-  const dim3 grid(p.nch, nkv), blk(ATT_THREADS);
-  hipEvent_t a = sp.start;
+  int rc;
   switch (p.G) {
-    case 1: hipExtLaunchKernelGGL((k_attn<HD, KVT, 1>), grid, blk, 0, st, a, nullptr, 0, p); break;
-    case 2: hipExtLaunchKernelGGL((k_attn<HD, KVT, 2>), grid, blk, 0, st, a, nullptr, 0, p); break;
-    case 4: hipExtLaunchKernelGGL((k_attn<HD, KVT, 4>), grid, blk, 0, st, a, nullptr, 0, p); break;
-    case 6: hipExtLaunchKernelGGL((k_attn<HD, KVT, 6>), grid, blk, 0, st, a, nullptr, 0, p); break;
-    case 8: hipExtLaunchKernelGGL((k_attn<HD, KVT, 8>), grid, blk, 0, st, a, nullptr, 0, p); break;
+    case 1: rc = go_g<HD, KVT, 1>(p, nkv, st, sp.start); break;
+    case 2: rc = go_g<HD, KVT, 2>(p, nkv, st, sp.start); break;
+    case 4: rc = go_g<HD, KVT, 4>(p, nkv, st, sp.start); break;
+    case 6: rc = go_g<HD, KVT, 6>(p, nkv, st, sp.start); break;
+    case 8: rc = go_g<HD, KVT, 8>(p, nkv, st, sp.start); break;
     default: return fail(LPS_EUNSUP, "attention: %d q heads per kv head not built (1, 2, 4, 6, 8)", p.G);
   }
+  if (rc) return rc;
   hipExtLaunchKernelGGL((k_attn_merge<HD>), dim3(nkv * p.G), dim3(MERGE_THREADS), 0, st, nullptr,
                         sp.stop, 0, p);
   return LPS_OK;

@@ -79,13 +79,14 @@ __device__ __forceinline__ void store_kv(void* base, int kvdtype, long long off,
 }
 
 template <int EPI>
-__device__ __forceinline__ void epilogue(const GemvP& p, int u, int r0, int r1, float a0, float a1) {
+__device__ __forceinline__ void epilogue(const GemvP& p, int u, int r0, int r1, float a0, float a1,
+                                         float y0, float y1) {
   if constexpr (EPI == EPI_STORE || EPI == EPI_LOGITS) {
     p.y[r0] = a0;
     if (r1 >= 0) p.y[r1] = a1;
-  } else if constexpr (EPI == EPI_ADD) {
-    p.y[r0] += a0;
-    if (r1 >= 0) p.y[r1] += a1;
+  } else if constexpr (EPI == EPI_ADD) {   // y0, y1: the rows' residual values, loaded early
+    p.y[r0] = y0 + a0;
+    if (r1 >= 0) p.y[r1] = y1 + a1;
   } else if constexpr (EPI == EPI_SWIGLU) {
     p.y[u] = silu(a0) * a1;
   } else {  // QKV: rotate q and k heads at pos, store q, append k and v to the caches
@@ -144,10 +145,10 @@ __device__ __forceinline__ void epilogue(const GemvP& p, int u, int r0, int r1, 
 
 template <int EPI>
 __device__ __forceinline__ void finish(const GemvP& p, int u, int r0, int r1, float a0, float a1,
-                                       int lane, float& best, int& bidx) {
+                                       float y0, float y1, int lane, float& best, int& bidx) {
   a0 = wave_sum(a0);
   a1 = wave_sum(a1);
-  if (lane == 0) epilogue<EPI>(p, u, r0, r1, a0, a1);
+  if (lane == 0) epilogue<EPI>(p, u, r0, r1, a0, a1, y0, y1);
   if constexpr (EPI == EPI_LOGITS) {
     if (a0 > best) { best = a0; bidx = r0; }
     if (r1 >= 0 && a1 > best) { best = a1; bidx = r1; }
@@ -173,12 +174,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const uint8_t* base, 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, bytes, BUF_DW3);
 }
 
-#define BUF_LOAD(V0, V1, S0, S1, UU, B0, LIVE)                                          \
+#define BUF_LOAD(V0, V1, S0, S1, Y0, Y1, UU, B0, LIVE)                                  \
   {                                                                                     \
     const int uu_ = (LIVE) ? (UU) : 0;                                                  \
     int r0_, r1_;                                                                       \
     unit_rows<EPI>(p, uu_, r0_, r1_);                                                   \
     const int rr1_ = r1_ >= 0 ? r1_ : r0_;                                              \
+    if constexpr (EPI == EPI_ADD) {                                                     \
+      Y0 = p.y[r0_];                                                                    \
+      Y1 = p.y[rr1_];                                                                   \
+    }                                                                                   \
     const int wb_ = (LIVE) ? (int)p.wrow : 0;                                           \
     const auto w0_ = row_rsrc(p.w + (long long)r0_ * p.wrow, wb_);                      \
     const auto w1_ = row_rsrc(p.w + (long long)rr1_ * p.wrow, wb_);                     \
@@ -207,17 +212,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const uint8_t* base, 
     acc_chunk<WT>(V0[i], S0[i], xs + c * XS, a0);                  \
     acc_chunk<WT>(V1[i], S1[i], xs + c * XS, a1);                  \
   }
-#define BUF_STEP(CV0, CV1, CS0, CS1, NV0, NV1, NS0, NS1)           \
+// One step of the double-buffered walk: issue the loads of the batch after the
+// current one (into buffer N), then consume the current batch (buffer C).  A
+// unit is finished when the next batch belongs to another unit.
+#define BUF_STEP(CV0, CV1, CS0, CS1, CY0, CY1, NV0, NV1, NS0, NS1, NY0, NY1) \
   {                                                                \
     int nu = u, nb = b0 + WAVE * U;                                \
     if (nb >= nck) { nu = u + stride; nb = 0; }                    \
     const bool more = nu < p.units;                                \
-    BUF_LOAD(NV0, NV1, NS0, NS1, nu, nb, more)                     \
+    BUF_LOAD(NV0, NV1, NS0, NS1, NY0, NY1, nu, nb, more)           \
     BUF_FMA(CV0, CV1, CS0, CS1, b0)                                \
     if (nu != u) {                                                 \
       int r0, r1;                                                  \
       unit_rows<EPI>(p, u, r0, r1);                                \
-      finish<EPI>(p, u, r0, r1, a0, a1, lane, best, bidx);         \
+      finish<EPI>(p, u, r0, r1, a0, a1, CY0, CY1, lane, best, bidx); \
       a0 = a1 = 0.f;                                               \
     }                                                              \
     if (!more) break;                                              \
@@ -241,7 +249,8 @@ __global__ __launch_bounds__(NT) void k_gemv_buf(GemvP p) {
   int b0 = 0;
   u32x4 va0[U], va1[U], vb0[U], vb1[U];
   uint32_t sa0[U], sa1[U], sb0[U], sb1[U];
-  BUF_LOAD(va0, va1, sa0, sa1, u, 0, u < p.units)
+  float ya0 = 0.f, ya1 = 0.f, yb0 = 0.f, yb1 = 0.f;   // residual rows (EPI_ADD)
+  BUF_LOAD(va0, va1, sa0, sa1, ya0, ya1, u, 0, u < p.units)
   if constexpr (WT == LPS_MXFP4) {
     stage_x_mx<NORM, NT>(p.x, p.g, p.eps, p.K, xs);
   } else {
@@ -252,8 +261,8 @@ __global__ __launch_bounds__(NT) void k_gemv_buf(GemvP p) {
     float a0 = 0.f, a1 = 0.f;
     if constexpr (DB) {
       for (;;) {
-        BUF_STEP(va0, va1, sa0, sa1, vb0, vb1, sb0, sb1)
-        BUF_STEP(vb0, vb1, sb0, sb1, va0, va1, sa0, sa1)
+        BUF_STEP(va0, va1, sa0, sa1, ya0, ya1, vb0, vb1, sb0, sb1, yb0, yb1)
+        BUF_STEP(vb0, vb1, sb0, sb1, yb0, yb1, va0, va1, sa0, sa1, ya0, ya1)
       }
     } else {
       // one batch in flight per wave, for launches where a wave meets one batch
@@ -264,13 +273,13 @@ __global__ __launch_bounds__(NT) void k_gemv_buf(GemvP p) {
         if (nu != u) {
           int r0, r1;
           unit_rows<EPI>(p, u, r0, r1);
-          finish<EPI>(p, u, r0, r1, a0, a1, lane, best, bidx);
+          finish<EPI>(p, u, r0, r1, a0, a1, ya0, ya1, lane, best, bidx);
           a0 = a1 = 0.f;
         }
         if (nu >= p.units) break;
         u = nu;
         b0 = nb;
-        BUF_LOAD(va0, va1, sa0, sa1, u, b0, true)
+        BUF_LOAD(va0, va1, sa0, sa1, ya0, ya1, u, b0, true)
       }
     }
   }

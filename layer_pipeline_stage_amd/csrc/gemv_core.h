@@ -67,6 +67,18 @@ __device__ __forceinline__ void acc_chunk(const u32x4 v, uint32_t sb, const floa
   }
 }
 
+constexpr int GPRE = 8;   // norm-gain float4s per thread held in registers
+
+// v = v * r * g, in that order (the rounding the oracle's RMSNorm reading fixes)
+__device__ __forceinline__ void scale4(float* px, float r, const f32x4 gg) {
+  f32x4 v = *reinterpret_cast<f32x4*>(px);
+  v.x = v.x * r * gg.x;
+  v.y = v.y * r * gg.y;
+  v.z = v.z * r * gg.z;
+  v.w = v.w * r * gg.w;
+  *reinterpret_cast<f32x4*>(px) = v;
+}
+
 // Stage the activation vector in LDS; with NORM, as RMSNorm(x) * g.  The copy
 // uses the LDS DMA path (global_load_lds_dwordx4: each lane's 16 bytes land at
 // the wave's LDS base + 16 * lane, no VGPRs): every wave issues all of its
@@ -78,6 +90,15 @@ __device__ __forceinline__ void stage_x(const float* x, const float* g, float ep
   const int tid = threadIdx.x;
   const int lane = tid & (WAVE - 1);
   const int wv = tid / WAVE;
+  // the norm gain goes out with the copy (same wait), for K <= NT * 4 * GPRE
+  f32x4 gpre[GPRE];
+  if (NORM) {
+#pragma unroll
+    for (int i = 0; i < GPRE; ++i) {
+      const int k = (tid + i * NT) * 4;
+      gpre[i] = k < K ? *reinterpret_cast<const f32x4*>(g + k) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
   for (int b = wv * 256; b < K; b += NW * 256) {
     if (b + 4 * lane < K)
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(x + b + 4 * lane),
@@ -99,15 +120,13 @@ __device__ __forceinline__ void stage_x(const float* x, const float* g, float ep
 #pragma unroll
     for (int i = 0; i < NW; ++i) tot += red[i];
     const float r = 1.0f / sqrtf(tot / float(K) + eps);
-    for (int k = tid * 4; k < K; k += NT * 4) {
-      f32x4 v = *reinterpret_cast<f32x4*>(xs + k);
-      const f32x4 gg = *reinterpret_cast<const f32x4*>(g + k);
-      v.x = v.x * r * gg.x;
-      v.y = v.y * r * gg.y;
-      v.z = v.z * r * gg.z;
-      v.w = v.w * r * gg.w;
-      *reinterpret_cast<f32x4*>(xs + k) = v;
+#pragma unroll
+    for (int i = 0; i < GPRE; ++i) {
+      const int k = (tid + i * NT) * 4;
+      if (k < K) scale4(xs + k, r, gpre[i]);
     }
+    for (int k = (tid + GPRE * NT) * 4; k < K; k += NT * 4)
+      scale4(xs + k, r, *reinterpret_cast<const f32x4*>(g + k));
     __syncthreads();
   }
 }
@@ -129,6 +148,14 @@ __device__ __forceinline__ void stage_x_mx(const float* x, const float* g, float
   const int wv = tid / WAVE;
   const int ng = K / 4;              // data groups
   const int np = (K / 32) * 9;       // physical groups
+  f32x4 gpre[GPRE];
+  if (NORM) {
+#pragma unroll
+    for (int i = 0; i < GPRE; ++i) {
+      const int G = tid + i * NT;
+      gpre[i] = G < ng ? *reinterpret_cast<const f32x4*>(g + 4 * G) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
   for (int b = wv * WAVE; b < np; b += NW * WAVE) {
     const int P = b + lane;
     const int c = P / 9, q = P - 9 * c;
@@ -153,16 +180,13 @@ __device__ __forceinline__ void stage_x_mx(const float* x, const float* g, float
 #pragma unroll
     for (int i = 0; i < NW; ++i) tot += red[i];
     const float r = 1.0f / sqrtf(tot / float(K) + eps);
-    for (int G = tid; G < ng; G += NT) {
-      float* px = xs + 4 * (G + (G >> 3));
-      f32x4 v = *reinterpret_cast<f32x4*>(px);
-      const f32x4 gg = *reinterpret_cast<const f32x4*>(g + 4 * G);
-      v.x = v.x * r * gg.x;
-      v.y = v.y * r * gg.y;
-      v.z = v.z * r * gg.z;
-      v.w = v.w * r * gg.w;
-      *reinterpret_cast<f32x4*>(px) = v;
+#pragma unroll
+    for (int i = 0; i < GPRE; ++i) {
+      const int G = tid + i * NT;
+      if (G < ng) scale4(xs + 4 * (G + (G >> 3)), r, gpre[i]);
     }
+    for (int G = tid + GPRE * NT; G < ng; G += NT)
+      scale4(xs + 4 * (G + (G >> 3)), r, *reinterpret_cast<const f32x4*>(g + 4 * G));
     __syncthreads();
   }
 }
