@@ -420,8 +420,10 @@ int lps_timer_start(int32_t kind, int32_t capacity) {
   std::lock_guard<std::mutex> lk(g_timer.mu);
   LPS_REQUIRE(g_timer.kind.load() == 0, LPS_ESTATE, "lps_timer_start: a timer is already running");
   g_timer.ev.assign(size_t(2) * capacity, nullptr);
+  // timing-only events: no system-scope fence (cache writeback / invalidate) when
+  // they complete, which would otherwise be timed with, and slow, the kernels
   for (auto& e : g_timer.ev) {
-    if (hipEventCreate(&e) != hipSuccess) {
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) {
       for (auto& f : g_timer.ev)
         if (f) (void)hipEventDestroy(f);
       g_timer.ev.clear();
