@@ -91,6 +91,28 @@ KERNEL_BYTES = {
 }
 
 
+def hbm_achievable_gbs(torch, lps, gib=4, reps=10):
+    """Read bandwidth this GPU actually reaches: lps_hbm_stream_read (16-byte
+    nontemporal loads, the GEMVs' pattern) over a 4 GiB buffer, 10 launches timed
+    with events on the launching stream."""
+    n = gib << 30
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    sink = torch.empty(lps.STREAM_SINK, dtype=torch.int32, device="cuda:0")
+    st = torch.cuda.current_stream()
+    for _ in range(2):
+        lps.lps_hbm_stream_read(buf.data_ptr(), n, sink.data_ptr(), st.cuda_stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(reps):
+        lps.lps_hbm_stream_read(buf.data_ptr(), n, sink.data_ptr(), st.cuda_stream)
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del buf
+    torch.cuda.empty_cache()
+    return n / (ms * 1e-3) / 1e9
+
+
 def cpu_baseline(model, first_token, n_steps=2):
     """The float64 oracle as it is, on this host, on the first n_steps of the
     same greedy run (teacher-forced to the GPU's tokens is not needed: the
@@ -207,6 +229,7 @@ def main():
                          "gbs": round(float(np.sum(byts) / (np.sum(ms) * 1e-3) / 1e9), 1)}
     gk = kernels["gateup"]
     achieved = gateup_bytes(cfg) / (gk["avg_us"] * 1e-6) / 1e9
+    achievable = hbm_achievable_gbs(torch, lps)
 
     out = {
         "metric": METRIC,
@@ -232,10 +255,13 @@ def main():
         "hbm_bytes_per_token": int(bytes_tok),
         "hbm_gbs": round(gbs, 1),
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "hbm_achievable_gbs": round(achievable, 1),
+        "hbm_frac_of_achievable": round(gbs / achievable, 4),
         "roofline": {
             "bound": "hbm", "kernel": "rmsnorm+gate_up GEMV+SwiGLU (bf16 [28672, 4096])",
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": gateup_traffic(),
+            "frac_of_achievable": round(achieved / achievable, 4),
             "avg_us": gk["avg_us"], "bytes_per_launch": gateup_bytes(cfg),
         },
         "kernels": kernels,

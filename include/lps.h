@@ -203,6 +203,17 @@ int lps_boundary_recv(lps_boundary* b, float* x, int64_t step, void* consumer);
 /* Synchronizes the boundary's events, then frees the handle. */
 int lps_boundary_destroy(lps_boundary* b);
 
+/* Achievable HBM read bandwidth, the calibration of every GB/s figure (TP3
+ * zero-padded dummy heads plan, File-level changes (AR work) and AR phasing &
+ * gates: a bandwidth microbenchmark is run before anything is tuned on it): reads
+ * `bytes` (a positive
+ * multiple of 16) at `src` (dev, 16-byte aligned) once, with the GEMVs' load
+ * pattern, on `stream`.  sink (dev, LPS_STREAM_SINK uint32) receives per-block
+ * XOR folds of the 32-bit words: their XOR is the XOR of the whole buffer.
+ * Errors: LPS_EINVAL on null / unaligned pointers or a bad size. */
+#define LPS_STREAM_SINK 2048
+int lps_hbm_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream);
+
 /* A copy of n f32 values on `stream` (the slot transport, also usable alone). */
 int lps_copy_f32(const float* src, float* dst, int64_t n, void* stream);
 

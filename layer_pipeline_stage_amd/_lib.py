@@ -62,6 +62,8 @@ I32, I64, F32, SZ = C.c_int32, C.c_int64, C.c_float, C.c_size_t
 PI32 = C.POINTER(C.c_int32)
 PP = C.POINTER(C.c_void_p)
 
+STREAM_SINK = 2048   # LPS_STREAM_SINK: uint32 entries lps_hbm_stream_read writes
+
 # name: (restype, argtypes, checked)  -- checked: raise on a negative int status
 SIGS = {
     "lps_last_error": (C.c_char_p, [], False),
@@ -88,6 +90,7 @@ SIGS = {
     "lps_boundary_recv": (C.c_int, [P, P, I64, P], True),
     "lps_boundary_destroy": (C.c_int, [P], True),
     "lps_copy_f32": (C.c_int, [P, P, I64, P], True),
+    "lps_hbm_stream_read": (C.c_int, [P, I64, P, P], True),
     "lps_logits_defer": (C.c_int, [P, P, I32, P, P, P, P, PP], True),
     "lps_pending_order": (C.c_int, [P, P], True),
     "lps_pending_wait": (C.c_int, [P], True),

@@ -98,7 +98,13 @@ def test_validation_before_enqueue(L):
         L.lps_attention_decode(4, 2, 64, 0, 16, 16, 8, 9, 16, 16, 16, 1 << 20, None)  # n_rows > ctx
     with pytest.raises(L.LpsError):
         L.lps_moe_combine(16, 16, 16, 16, 16, 16, 4, 64, 0, None, None)    # 0 pieces
+    with pytest.raises(L.LpsError) as e:
+        L.lps_hbm_stream_read(16, 24, 16, None)                 # bytes not a multiple of 16
+    assert e.value.code == L.LPS_EINVAL
+    with pytest.raises(L.LpsError):
+        L.lps_hbm_stream_read(8, 32, 16, None)                  # unaligned source
     assert L.lps_attention_scratch_bytes(32, 8, 128, 4224) > 0
+
     assert L.lps_attention_scratch_bytes(3, 2, 128, 10) == 0
 
 

@@ -315,6 +315,20 @@ def test_head_argmax(L):
     assert int(tk.item()) == 7
 
 
+@pytest.mark.parametrize("n16", [1, 4097, (1 << 22) + 333])
+def test_hbm_stream_read_touches_every_word(L, n16):
+    """The read-bandwidth calibration reads every 16-byte chunk exactly once: the
+    XOR of its per-block folds equals the XOR of all 32-bit words (exact, any
+    order), also for sizes that leave a ragged grid-stride tail."""
+    rng = np.random.default_rng(n16)
+    words = rng.integers(0, 2**32, size=4 * n16, dtype=np.uint64).astype(np.uint32)
+    src = dev(words.view(np.int32))
+    sink = torch.zeros(L.STREAM_SINK, dtype=torch.int32, device=DEV)
+    L.lps_hbm_stream_read(ptr(src), 16 * n16, ptr(sink), stream())
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert int(got) == int(np.bitwise_xor.reduce(words))
+
+
 def test_boundary_protocol(L):
     d = 5120
     s0 = torch.full((d,), float("nan"), device=DEV)
