@@ -13,7 +13,7 @@
 //     the lower id, weights renormalised over the k.
 //  2. group: per expert, the tokens that selected it, in token order (a stable
 //     counting sort: each expert's list is a compaction of the token sequence).
-//  3. tiles: per-expert offsets and the list of 128-row tiles (experts in
+//  3. tiles: per-expert offsets and the list of 256-row tiles (experts in
 //     ascending id, then the shared expert over all tokens).
 //  4. GEMM1: [rows x d] x [d x 2ff] on MFMA 32x32x16 bf16 -> f32; the gate and
 //     up columns of one output sit in the same lanes, so SwiGLU is applied in
@@ -38,7 +38,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int PF_TOK = 8;      // tokens per routing tile
 constexpr int PF_MAXE = 64;    // experts the tile router is built for
 constexpr int PF_MAXK = 16;
-constexpr int GM = 128, GN = 128, GK = 32, GKP = GK + 8;  // GEMM tile; LDS row pad
+// grouped GEMM tile: BM token rows x BN weight rows, K in steps of BK; LDS rows padded
+// by 16 bytes (144-byte stride: the eight lanes of a ds_read_b128 phase hit distinct banks)
+constexpr int GM = 256, GBN = 256, GBK = 64, GKP = GBK + 8;
+constexpr int GEMM_THREADS = 512;
 
 struct PfP {
   const float* x;        // [T, d] residual
@@ -199,11 +202,18 @@ __global__ void k_pf_tiles(PfP p) {
 }
 
 // ---- 4/5. grouped GEMM on MFMA -----------------------------------------------------------
-// C[m, n] = sum_k A[m, k] B[n, k]: A rows are gathered activation rows (bf16),
-// B rows are weight rows (bf16, K contiguous).  128 x 128 tile, 4 waves of 64 x 64
-// (2 x 2 MFMA 32x32x16), K in steps of 32 through double-buffered LDS.
+// C[m, n] = sum_k A[m, k] B[n, k]: A rows are gathered activation rows (bf16), B
+// rows weight rows (bf16, K contiguous).  A 256 x 256 tile per workgroup of 8 waves
+// (2 x 4, two per SIMD), each wave 128 x 64 as 4 x 2 MFMA 32x32x16 blocks.  K walks
+// in steps of 64 through two LDS buffers, and the global loads run two steps ahead
+// in two register sets: at step k the loads of step k + 2 go out, step k is
+// multiplied from LDS, and step k + 1 (loaded during step k - 1) is written to the
+// other buffer; one barrier per step.  The step count is even, so the loop handles
+// steps in pairs with fixed buffers and no branch; near the end the loads repeat the
+// last step (valid memory, never stored to a buffer that is read).
 template <bool FIRST>
-__global__ __launch_bounds__(256) void k_pf_gemm(PfP p) {
+__global__ __launch_bounds__(GEMM_THREADS) void k_pf_gemm(PfP p) {
+  constexpr int NJ = 4;                      // 16-byte chunks per thread and operand per step
   const int tile = blockIdx.y;
   if (tile >= *p.n_tiles) return;
   const int packed = p.tiles[tile];
@@ -211,117 +221,129 @@ __global__ __launch_bounds__(256) void k_pf_gemm(PfP p) {
   const bool shared_e = e == p.E;
   const int cnt = p.cnt[e];
   const int K = FIRST ? p.d : p.ff;
-  const int n0 = FIRST ? blockIdx.x * 64 : blockIdx.x * GN;
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][GM][GKP];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][GN][GKP];
+  const int n0 = FIRST ? blockIdx.x * (GBN / 2) : blockIdx.x * GBN;
+  extern __shared__ __attribute__((aligned(16))) uint16_t gsm[];
+  uint16_t* As0 = gsm;                       // [GM][GKP]
+  uint16_t* Bs0 = As0 + GM * GKP;            // [GBN][GKP]
+  uint16_t* As1 = Bs0 + GBN * GKP;
+  uint16_t* Bs1 = As1 + GM * GKP;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid / 64;
-  const int wm = wv >> 1, wn = wv & 1;
-  // the two 16-byte chunks this thread stages per K step: row c / 4, column 8 (c % 4)
-  const uint16_t* arow[2];
-  const uint16_t* brow[2];
-  int srow[2], scol[2];
+  const int wm = wv >> 2, wn = wv & 3;
+  // A and B through buffer resources: one 32-bit byte offset per staged row (rows
+  // tid / 8 + 64 j, column 8 (tid % 8)), the K step as the scalar offset
+  const int scol = (tid & 7) * 8;
+  const uint16_t* abase = FIRST ? p.xb : p.act;
+  const uint16_t* bbase = FIRST ? (shared_e ? p.w_gu_s : p.w_gu_e + (long long)e * 2 * p.ff * p.d)
+                                : (shared_e ? p.w_d_s : p.w_d_e + (long long)e * p.d * p.ff);
+  const long long abytes = FIRST ? (long long)p.T * p.d * 2 : ((long long)p.T * p.k + p.T) * p.ff * 2;
+  const long long bbytes = FIRST ? 2LL * p.ff * p.d * 2 : (long long)p.d * p.ff * 2;
+  const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(abase), (short)0, (int)(abytes < 0x7FFFFFFF ? abytes : 0x7FFFFFFF), 0x00020000);
+  const __amdgpu_buffer_rsrc_t bres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(bbase), (short)0, (int)(bbytes < 0x7FFFFFFF ? bbytes : 0x7FFFFFFF), 0x00020000);
+  int aoff[NJ], boff[NJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = tid + 256 * i;
-    srow[i] = c >> 2;
-    scol[i] = (c & 3) * 8;
-    const int r = m0 + srow[i];
+  for (int j = 0; j < NJ; ++j) {
+    const int sr = (tid >> 3) + 64 * j;
+    const int r = m0 + sr;
     const int rr = r < cnt ? r : m0;          // rows past the list repeat a valid row
     if (FIRST) {
       const int tok = shared_e ? rr : p.lst[(long long)e * p.T + rr];
-      arow[i] = p.xb + (long long)tok * p.d;
+      aoff[j] = (tok * p.d + scol) * 2;
     } else {
-      arow[i] = p.act + (long long)(p.off[e] + rr) * p.ff;
+      aoff[j] = ((p.off[e] + rr) * p.ff + scol) * 2;
     }
-    const int br = srow[i];
-    long long wrow;
-    const uint16_t* wbase;
+    int wrow;
     if (FIRST) {
-      // B rows of wave column wn: 32 gate rows then 32 up rows
-      const int wcol = br >> 6, jj = (br >> 5) & 1, cc = br & 31;
-      wrow = (long long)(jj ? p.ff : 0) + n0 + 32 * wcol + cc;
-      wbase = shared_e ? p.w_gu_s : p.w_gu_e + (long long)e * 2 * p.ff * p.d;
+      // B rows of wave column wc: 32 gate rows then 32 up rows of the same outputs
+      const int wc = sr >> 6, jj = (sr >> 5) & 1, cc = sr & 31;
+      wrow = (jj ? p.ff : 0) + n0 + 32 * wc + cc;
     } else {
-      wrow = n0 + br;
-      wbase = shared_e ? p.w_d_s : p.w_d_e + (long long)e * p.d * p.ff;
+      wrow = n0 + sr;
     }
-    brow[i] = wbase + wrow * K;
+    boff[j] = (wrow * K + scol) * 2;
   }
-  u32x4 ra[2], rb[2];
-  auto gload = [&](int k0) {
+  const int soff = (tid >> 3) * GKP + scol;   // LDS element offset of chunk j = 0
+
+  f32x16 acc[4][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      ra[i] = ld16(arow[i] + k0 + scol[i]);
-      rb[i] = ld_stream16(brow[i] + k0 + scol[i]);
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      *reinterpret_cast<u32x4*>(&As[buf][srow[i]][scol[i]]) = ra[i];
-      *reinterpret_cast<u32x4*>(&Bs[buf][srow[i]][scol[i]]) = rb[i];
-    }
-  };
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nk = K / GK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * GK);
-#pragma unroll
-    for (int ks = 0; ks < GK / 16; ++ks) {
-      bf16x8 a[2], b[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        a[i] = *reinterpret_cast<const bf16x8*>(&As[buf][64 * wm + 32 * i + (lane & 31)][16 * ks + 8 * (lane >> 5)]);
-        b[i] = *reinterpret_cast<const bf16x8*>(&Bs[buf][64 * wn + 32 * i + (lane & 31)][16 * ks + 8 * (lane >> 5)]);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) {
-      sstore(buf ^ 1);
-      __syncthreads();
-    }
+#define PF_LOAD(RA, RB, K0)                                                                       \
+  _Pragma("unroll") for (int j = 0; j < NJ; ++j) {                                                \
+    RA[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ares, aoff[j], 2 * (K0), 0)); \
+    RB[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(bres, boff[j], 2 * (K0), 2)); \
   }
-  // epilogue: acc[i][j][r] is C[64 wm + 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4][64 wn + 32 j + lane % 32]
+#define PF_STORE(RA, RB, AS, BS)                                         \
+  _Pragma("unroll") for (int j = 0; j < NJ; ++j) {                       \
+    *reinterpret_cast<u32x4*>(AS + soff + 64 * j * GKP) = RA[j];         \
+    *reinterpret_cast<u32x4*>(BS + soff + 64 * j * GKP) = RB[j];         \
+  }
+#define PF_MMA(AS, BS)                                                                          \
+  _Pragma("unroll") for (int ks = 0; ks < GBK / 16; ++ks) {                                      \
+    bf16x8 a[4], b[2];                                                                           \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                \
+      a[i] = *reinterpret_cast<const bf16x8*>(AS + (128 * wm + 32 * i + (lane & 31)) * GKP +      \
+                                              16 * ks + 8 * (lane >> 5));                        \
+    _Pragma("unroll") for (int j = 0; j < 2; ++j)                                                \
+      b[j] = *reinterpret_cast<const bf16x8*>(BS + (64 * wn + 32 * j + (lane & 31)) * GKP +       \
+                                              16 * ks + 8 * (lane >> 5));                        \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                \
+      _Pragma("unroll") for (int j = 0; j < 2; ++j)                                              \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);     \
+  }
+
+  const int nk = K / GBK;                    // even (checked on the host)
+  u32x4 ra0[NJ], rb0[NJ], ra1[NJ], rb1[NJ];
+  PF_LOAD(ra0, rb0, 0)
+  PF_LOAD(ra1, rb1, GBK)
+  PF_STORE(ra0, rb0, As0, Bs0)
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    const int s2 = min(kt + 2, nk - 1), s3 = min(kt + 3, nk - 1);
+    PF_LOAD(ra0, rb0, s2 * GBK)               // step kt + 2
+    PF_MMA(As0, Bs0)                          // step kt
+    PF_STORE(ra1, rb1, As1, Bs1)              // step kt + 1
+    __syncthreads();
+    PF_LOAD(ra1, rb1, s3 * GBK)               // step kt + 3
+    PF_MMA(As1, Bs1)                          // step kt + 1
+    PF_STORE(ra0, rb0, As0, Bs0)              // step kt + 2 (unread after the last pair)
+    __syncthreads();
+  }
+#undef PF_LOAD
+#undef PF_STORE
+#undef PF_MMA
+  // epilogue: acc[i][j][r] is C[128 wm + 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4][64 wn + 32 j + lane % 32]
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int row = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      const int row = 128 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
       const int m = m0 + row;
-      if (m >= cnt) continue;
-      if (FIRST) {
-        const float gt = acc[i][0][r], up = acc[i][1][r];
-        const int col = n0 + 32 * wn + (lane & 31);
-        p.act[(long long)(p.off[e] + m) * p.ff + col] = bf16_rne(silu(gt) * up);
-      } else {
+      if (m < cnt) {
+        if (FIRST) {
+          const float gt = acc[i][0][r], up = acc[i][1][r];
+          const int col = n0 + 32 * wn + (lane & 31);
+          p.act[(long long)(p.off[e] + m) * p.ff + col] = bf16_rne(silu(gt) * up);
+        } else {
+          const long long li = (long long)e * p.T + m;
+          const int t = shared_e ? m : p.lst[li];
+          const float wgt = shared_e ? 1.f : p.lw[li];
+          float* dst = shared_e ? p.shared + (long long)m * p.d
+                                : p.z + ((long long)t * p.k + p.lslot[li]) * p.d;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int col = n0 + 64 * wn + 32 * j + (lane & 31);
-          if (shared_e) {
-            p.shared[(long long)m * p.d + col] = acc[i][j][r];
-          } else {
-            const long long li = (long long)e * p.T + m;
-            const int t = p.lst[li];
-            p.z[((long long)t * p.k + p.lslot[li]) * p.d + col] = p.lw[li] * acc[i][j][r];
+          for (int j = 0; j < 2; ++j) {
+            const int col = n0 + 64 * wn + 32 * j + (lane & 31);
+            dst[col] = shared_e ? acc[i][j][r] : wgt * acc[i][j][r];
           }
         }
       }
+      __builtin_amdgcn_sched_barrier(0);   // one row at a time: keeps the epilogue's live range short
     }
   }
 }
@@ -409,8 +431,10 @@ extern "C" int lps_moe_prefill(const lps_moe_desc* m, float* x, int32_t T, int32
               "lps_moe_prefill: n_experts %d outside [1, %d]", m->n_experts, PF_MAXE);
   LPS_REQUIRE(m->top_k >= 1 && m->top_k <= PF_MAXK && m->top_k <= m->n_experts, LPS_EUNSUP,
               "lps_moe_prefill: top_k %d", m->top_k);
-  LPS_REQUIRE(m->d % GN == 0 && m->d % GK == 0 && m->ff % 64 == 0 && m->ff % GK == 0, LPS_EUNSUP,
-              "lps_moe_prefill: d %d must be a multiple of %d and ff %d of 64", m->d, GN, m->ff);
+  LPS_REQUIRE(m->d % GBN == 0 && m->ff % (GBN / 2) == 0 && m->d % (2 * GBK) == 0 &&
+                  m->ff % (2 * GBK) == 0, LPS_EUNSUP,
+              "lps_moe_prefill: d %d must be a multiple of %d and ff %d of %d", m->d, GBN, m->ff,
+              GBN / 2);
   LPS_REQUIRE(size_t(PF_TOK) * m->d * 4 <= 160 * 1024, LPS_EUNSUP, "lps_moe_prefill: d %d too wide", m->d);
   LPS_REQUIRE(m->remote_from >= 0 && m->remote_from <= m->n_experts, LPS_EINVAL,
               "lps_moe_prefill: remote_from %d", m->remote_from);
@@ -461,9 +485,15 @@ extern "C" int lps_moe_prefill(const lps_moe_desc* m, float* x, int32_t T, int32
   LPS_HIP(hipGetLastError());
   hipLaunchKernelGGL(k_pf_tiles, dim3(1), dim3(64), 0, st, p);
   LPS_HIP(hipGetLastError());
-  hipLaunchKernelGGL(k_pf_gemm<true>, dim3(m->ff / 64, s.max_tiles), dim3(256), 0, st, p);
+  const size_t glds = size_t(2) * (GM + GBN) * GKP * sizeof(uint16_t);
+  rc = ensure_lds((const void*)k_pf_gemm<true>, glds);
+  if (rc) return rc;
+  rc = ensure_lds((const void*)k_pf_gemm<false>, glds);
+  if (rc) return rc;
+  hipLaunchKernelGGL(k_pf_gemm<true>, dim3(m->ff / (GBN / 2), s.max_tiles), dim3(GEMM_THREADS), glds,
+                     st, p);
   LPS_HIP(hipGetLastError());
-  hipLaunchKernelGGL(k_pf_gemm<false>, dim3(m->d / GN, s.max_tiles), dim3(256), 0, st, p);
+  hipLaunchKernelGGL(k_pf_gemm<false>, dim3(m->d / GBN, s.max_tiles), dim3(GEMM_THREADS), glds, st, p);
   LPS_HIP(hipGetLastError());
   hipLaunchKernelGGL(k_pf_halves, dim3(T), dim3(256), 0, st, p);
   LPS_HIP(hipGetLastError());
