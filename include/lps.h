@@ -262,7 +262,8 @@ typedef struct lps_moe_desc {
 } lps_moe_desc;
 
 /* A10: for T rows of x (dev [T, d] f32): idx (dev [T, top_k] int32), w (dev
- * [T, top_k] f32).  top_k <= 16, n_experts <= 256. */
+ * [T, top_k] f32).  top_k <= 16, n_experts <= 256, d <= 4096.  scratch (dev) of
+ * lps_moe_route_scratch_bytes(m, T) bytes receives the router logits [T, E]. */
 size_t lps_moe_route_scratch_bytes(const lps_moe_desc* m, int32_t T);
 int lps_moe_route(const lps_moe_desc* m, const float* x, int32_t T, int32_t* idx, float* w,
                   void* scratch, size_t scratch_bytes, void* stream);

@@ -32,7 +32,7 @@
 namespace lps {
 
 enum { EPI_STORE = LPS_EPI_STORE, EPI_ADD = LPS_EPI_ADD, EPI_SWIGLU = LPS_EPI_SWIGLU, EPI_QKV = 3,
-       EPI_LOGITS = 4 };
+       EPI_LOGITS = 4, EPI_MOEGU = 5 };
 
 struct GemvP {
   const uint8_t* w;
@@ -53,11 +53,21 @@ struct GemvP {
   // LM-head epilogue: every wave's (max, lowest index of it) over its rows
   float* pval;
   int* pidx;
+  // MoE gate/up: unit u = (slot j, i) of slot j's fused [2ff, d] matrix; slots
+  // j < kslots are expert eidx[j] (w + eidx[j] * estride), slot kslots the shared w_s
+  const uint8_t* w_s;
+  const int32_t* eidx;
+  long long estride;
+  int kslots, ff, E;
 };
 
 template <int EPI>
 __device__ __forceinline__ void unit_rows(const GemvP& p, int u, int& r0, int& r1) {
-  if constexpr (EPI == EPI_SWIGLU) {
+  if constexpr (EPI == EPI_MOEGU) {
+    const int j = u / p.ff;
+    r0 = u - j * p.ff;
+    r1 = r0 + p.ff;
+  } else if constexpr (EPI == EPI_SWIGLU) {
     r0 = u;
     r1 = u + (p.N >> 1);
   } else if constexpr (EPI == EPI_QKV) {
@@ -68,6 +78,19 @@ __device__ __forceinline__ void unit_rows(const GemvP& p, int u, int& r0, int& r
   } else {
     r0 = 2 * u;
     r1 = (2 * u + 1 < p.N) ? 2 * u + 1 : -1;
+  }
+}
+
+// first weight row of the matrix unit u belongs to
+template <int EPI>
+__device__ __forceinline__ const uint8_t* unit_base(const GemvP& p, int u) {
+  if constexpr (EPI == EPI_MOEGU) {
+    const int j = u / p.ff;
+    if (j >= p.kslots) return p.w_s;
+    const int e = min(max(p.eidx[j], 0), p.E - 1);   // indices are device data
+    return p.w + (long long)e * p.estride;
+  } else {
+    return p.w;
   }
 }
 
@@ -87,7 +110,7 @@ __device__ __forceinline__ void epilogue(const GemvP& p, int u, int r0, int r1, 
   } else if constexpr (EPI == EPI_ADD) {   // y0, y1: the rows' residual values, loaded early
     p.y[r0] = y0 + a0;
     if (r1 >= 0) p.y[r1] = y1 + a1;
-  } else if constexpr (EPI == EPI_SWIGLU) {
+  } else if constexpr (EPI == EPI_SWIGLU || EPI == EPI_MOEGU) {
     p.y[u] = silu(a0) * a1;
   } else {  // QKV: rotate q and k heads at pos, store q, append k and v to the caches
     const int half = p.hd >> 1;
@@ -185,8 +208,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const uint8_t* base, 
       Y1 = p.y[rr1_];                                                                   \
     }                                                                                   \
     const int wb_ = (LIVE) ? (int)p.wrow : 0;                                           \
-    const auto w0_ = row_rsrc(p.w + (long long)r0_ * p.wrow, wb_);                      \
-    const auto w1_ = row_rsrc(p.w + (long long)rr1_ * p.wrow, wb_);                     \
+    const uint8_t* ub_ = unit_base<EPI>(p, uu_);                                        \
+    const auto w0_ = row_rsrc(ub_ + (long long)r0_ * p.wrow, wb_);                      \
+    const auto w1_ = row_rsrc(ub_ + (long long)rr1_ * p.wrow, wb_);                     \
     _Pragma("unroll") for (int i = 0; i < U; ++i) {                                     \
       const int off = ((B0) + lane + WAVE * i) * 16;                                    \
       V0[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w0_, off, 0, BUF_NT)); \
@@ -403,6 +427,27 @@ int launch_gemv(int wdtype, const void* w, const uint8_t* s, int N, int K, const
   if (mode == EPI_ADD)
     return norm ? launch_wt<EPI_ADD, true>(wdtype, p, st, sp) : launch_wt<EPI_ADD, false>(wdtype, p, st, sp);
   return norm ? launch_wt<EPI_STORE, true>(wdtype, p, st, sp) : launch_wt<EPI_STORE, false>(wdtype, p, st, sp);
+}
+
+int launch_moe_gu(const void* w_e, const void* w_s, const int32_t* eidx, int E, int kslots, int ff,
+                  int d, const float* x, const float* g, float eps, float* y, hipStream_t st) {
+  GemvP p{};
+  p.w = static_cast<const uint8_t*>(w_e);
+  p.w_s = static_cast<const uint8_t*>(w_s);
+  p.eidx = eidx;
+  p.E = E;
+  p.kslots = kslots;
+  p.ff = ff;
+  p.estride = 2LL * ff * d * 2;
+  p.N = 2 * ff;
+  p.K = d;
+  p.x = x;
+  p.g = g;
+  p.eps = eps;
+  p.y = y;
+  p.units = (kslots + 1) * ff;
+  set_rows(p, LPS_BF16, d);
+  return launch_wt<EPI_MOEGU, true>(LPS_BF16, p, st, Stamp{});
 }
 
 int launch_qkv(const QkvArgs& a, hipStream_t st, Stamp sp) {

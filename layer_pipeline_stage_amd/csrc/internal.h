@@ -63,6 +63,10 @@ struct QkvArgs {
 int launch_gemv(int wdtype, const void* w, const uint8_t* s, int N, int K, const float* x,
                 const float* g, float eps, float* y, int mode, hipStream_t st, Stamp sp = {});
 int launch_qkv(const QkvArgs& a, hipStream_t st, Stamp sp = {});
+// MoE decode gate/up + SwiGLU over the k selected experts (eidx, device) and the
+// shared one: y[(j, i)] = silu(gate) * up for slot j <= k, row i < ff
+int launch_moe_gu(const void* w_e, const void* w_s, const int32_t* eidx, int E, int kslots, int ff,
+                  int d, const float* x, const float* g, float eps, float* y, hipStream_t st);
 int launch_head(const lps_head_desc* h, const float* x, float* logits, int32_t* tok,
                 void* scratch, size_t bytes, hipStream_t st, Stamp sp = {});
 size_t head_scratch(const lps_head_desc* h);

@@ -20,57 +20,59 @@ constexpr int MOE_MAXK = 16;
 constexpr int MOE_MAXE = 256;
 
 // ---- A10: router logits, softmax, top-k ------------------------------------------
-// grid (ceil(E / 8), T): each workgroup computes 8 experts' logits for one token
-// (2 per wave); the last workgroup of that token selects the top k.
+// Two launches.  k_route_logits: grid (ceil(E / 4), T), one expert per wave, every
+// chunk load of the expert row in flight before the normed row is staged (the router
+// weights are spread over many CUs: one workgroup cannot pull E * d * 2 bytes fast).
+// k_route_topk: one wave per token selects the top k.  Stream order joins them, so
+// no fence or counter is needed.
+constexpr int ROUTE_EPB = 4;   // experts (waves) per logits workgroup
 struct RouteP {
   const float* x;      // [T, d]
   const float* g;
   float eps;
   const uint16_t* wr;  // [E, d] bf16
   int d, E, k;
-  float* logits;       // scratch [T, E]
-  int* cnt;            // scratch [T], zero on entry, left zero
+  float* logits;       // [T, E]
   int32_t* idx;        // [T, k]
   float* w;            // [T, k]
 };
 
-__device__ __forceinline__ float bf16_dot_row(const uint16_t* row, const float* xs, int d, int lane) {
-  float a = 0.f;
-  const int nck = d / 8;
-  for (int c = lane; c < nck; c += WAVE) {
-    const u32x4 v = ld16(row + (long long)c * 8);
-    acc_chunk<LPS_BF16>(v, 0, xs + c * 8, a);
-  }
-  return wave_sum(a);
-}
-
-__global__ __launch_bounds__(256) void k_route(RouteP p) {
+// lane l takes the 16-byte chunks l, l + 64, ... of the expert row in ascending
+// order (the same per-lane split and order as the prefill router), then a wave sum
+template <int CPL>
+__global__ __launch_bounds__(ROUTE_EPB * WAVE) void k_route_logits(RouteP p) {
   extern __shared__ float xs[];
   const int t = blockIdx.y;
-  stage_x<true>(p.x + (long long)t * p.d, p.g, p.eps, p.d, xs);
-  const int lane = threadIdx.x & 63, wv = threadIdx.x / 64;
-  for (int q = 0; q < 2; ++q) {
-    const int e = blockIdx.x * 8 + wv * 2 + q;
-    if (e < p.E) {
-      const float r = bf16_dot_row(p.wr + (long long)e * p.d, xs, p.d, lane);
-      if (lane == 0) p.logits[(long long)t * p.E + e] = r;
-    }
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  const int e = blockIdx.x * ROUTE_EPB + wv;
+  const int nck = p.d / 8;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(p.wr + (long long)(e < p.E ? e : 0) * p.d), (short)0,
+      e < p.E ? p.d * 2 : 0, 0x00020000);
+  u32x4 v[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c)
+    v[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (lane + WAVE * c) * 16, 0, 0));
+  stage_x<true, ROUTE_EPB * WAVE>(p.x + (long long)t * p.d, p.g, p.eps, p.d, xs);
+  float a = 0.f;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int ch = lane + WAVE * c;
+    if (ch < nck) acc_chunk<LPS_BF16>(v[c], 0, xs + ch * 8, a);
   }
-  __shared__ int is_last;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) is_last = atomicAdd(p.cnt + t, 1) == int(gridDim.x) - 1;
-  __syncthreads();
-  if (!is_last || wv != 0) return;
-  __threadfence();
-  // one wave: lane holds logits e = lane + 64 q
+  a = wave_sum(a);
+  if (lane == 0 && e < p.E) p.logits[(long long)t * p.E + e] = a;
+}
+
+__global__ __launch_bounds__(WAVE) void k_route_topk(RouteP p) {
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x;
+  // lane holds logits e = lane + 64 q
   float r[MOE_MAXE / 64];
 #pragma unroll
   for (int q = 0; q < MOE_MAXE / 64; ++q) {
     const int e = lane + 64 * q;
-    r[q] = e < p.E ? __hip_atomic_load(p.logits + (long long)t * p.E + e, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT)
-                   : -INFINITY;
+    r[q] = e < p.E ? p.logits[(long long)t * p.E + e] : -INFINITY;
   }
   float m = -INFINITY;
 #pragma unroll
@@ -85,19 +87,19 @@ __global__ __launch_bounds__(256) void k_route(RouteP p) {
   __shared__ int sel_id[MOE_MAXK];
   float ssum = 0.f;
   for (int j = 0; j < p.k; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
+    // the largest logit (DPP max), then the lowest expert id holding it (DPP max of
+    // -id over the candidates): exact selections, so ties go to the lower id
+    float lv = -INFINITY;
+    int li = 0x7fffffff;
 #pragma unroll
     for (int q = 0; q < MOE_MAXE / 64; ++q) {
       const int e = lane + 64 * q;
-      if (e < p.E && (r[q] > bv || (r[q] == bv && e < bi))) { bv = r[q]; bi = e; }
+      if (e < p.E && (r[q] > lv || (r[q] == lv && e < li))) { lv = r[q]; li = e; }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-    }
+    const float bv = wave_max(lv);
+    const float key = (lv == bv && li < p.E) ? -float(li) : -INFINITY;
+    const float kb = wave_max(key);
+    int bi = kb == -INFINITY ? 0x7fffffff : int(-kb);
     // non-finite router inputs leave nothing selectable: fall back to slot id j
     // with a NaN weight, so the step is poisoned loudly but every index stays valid
     const bool none = bi >= p.E;
@@ -117,12 +119,11 @@ __global__ __launch_bounds__(256) void k_route(RouteP p) {
       p.idx[(long long)t * p.k + j] = sel_id[j];
       p.w[(long long)t * p.k + j] = sel_pi[j] / ssum;
     }
-    p.cnt[t] = 0;
   }
 }
 
-static int launch_route(const lps_moe_desc* m, const float* x, int T, int32_t* idx, float* w,
-                        float* logits, int* cnt, hipStream_t st) {
+static int launch_route(const lps_moe_desc* m, const float* x, int T, float* logits, int32_t* idx,
+                        float* w, hipStream_t st) {
   RouteP p{};
   p.x = x;
   p.g = m->g_ffn;
@@ -132,66 +133,38 @@ static int launch_route(const lps_moe_desc* m, const float* x, int T, int32_t* i
   p.E = m->n_experts;
   p.k = m->top_k;
   p.logits = logits;
-  p.cnt = cnt;
   p.idx = idx;
   p.w = w;
-  hipLaunchKernelGGL(k_route, dim3((m->n_experts + 7) / 8, T), dim3(256), size_t(m->d) * 4, st, p);
+  const int cpl = (m->d / 8 + WAVE - 1) / WAVE;
+  const size_t lds = size_t(m->d) * 4;
+  const dim3 grid((m->n_experts + ROUTE_EPB - 1) / ROUTE_EPB, T);
+  int rc;
+#define LPS_ROUTE(C)                                                                  \
+  do {                                                                                \
+    if ((rc = ensure_lds((const void*)k_route_logits<C>, lds))) return rc;           \
+    hipLaunchKernelGGL(k_route_logits<C>, grid, dim3(ROUTE_EPB * WAVE), lds, st, p);  \
+  } while (0)
+  if (cpl <= 1) LPS_ROUTE(1);
+  else if (cpl <= 2) LPS_ROUTE(2);
+  else if (cpl <= 4) LPS_ROUTE(4);
+  else LPS_ROUTE(8);
+#undef LPS_ROUTE
+  LPS_HIP(hipGetLastError());
+  hipLaunchKernelGGL(k_route_topk, dim3(T), dim3(WAVE), 0, st, p);
   LPS_HIP(hipGetLastError());
   return LPS_OK;
 }
 
 // ---- A11: gate/up + SwiGLU for the k selected experts and the shared one ----------
-// unit u = (slot j, i): rows i and ff + i of slot j's fused gate/up matrix.
-struct MoeGuP {
-  const float* x;
-  const float* g;
-  float eps;
-  const uint16_t* w_e;   // [E, 2ff, d]
-  const uint16_t* w_s;   // [2ff, d]
-  const int32_t* idx;    // [k]
-  int d, ff, k, units, E;
-  float* mbuf;           // [(k+1), ff]
-};
-
-template <int U>
-__global__ __launch_bounds__(256) void k_moe_gu(MoeGuP p) {
-  extern __shared__ float xs[];
-  stage_x<true>(p.x, p.g, p.eps, p.d, xs);
-  const int lane = threadIdx.x & 63, wv = threadIdx.x / 64;
-  const int nck = p.d / 8;
-  for (int u = blockIdx.x * 4 + wv; u < p.units; u += gridDim.x * 4) {
-    const int j = u / p.ff, i = u - j * p.ff;
-    const int e = j < p.k ? min(max(p.idx[j], 0), p.E - 1) : 0;   // indices are device data
-    const uint16_t* base = j < p.k ? p.w_e + (long long)e * 2 * p.ff * p.d : p.w_s;
-    const uint16_t* w0 = base + (long long)i * p.d;
-    const uint16_t* w1 = base + (long long)(p.ff + i) * p.d;
-    float a0 = 0.f, a1 = 0.f;
-    for (int j0 = lane; j0 < nck; j0 += 64 * U) {
-      u32x4 v0[U], v1[U];
-#pragma unroll
-      for (int q = 0; q < U; ++q) {
-        const int c = j0 + 64 * q;
-        if (c < nck) {
-          v0[q] = ld_stream16(w0 + (long long)c * 8);
-          v1[q] = ld_stream16(w1 + (long long)c * 8);
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < U; ++q) {
-        const int c = j0 + 64 * q;
-        if (c < nck) {
-          acc_chunk<LPS_BF16>(v0[q], 0, xs + c * 8, a0);
-          acc_chunk<LPS_BF16>(v1[q], 0, xs + c * 8, a1);
-        }
-      }
-    }
-    a0 = wave_sum(a0);
-    a1 = wave_sum(a1);
-    if (lane == 0) p.mbuf[(long long)j * p.ff + i] = silu(a0) * a1;
-  }
-}
+// launch_moe_gu (the weight-streaming GEMV with an expert-table row map).
 
 // ---- A11 + A12: down projections of all slots and the fixed-order combine ----------
+// One wave per output row r: the rows r of every slot's down matrix (k selected
+// experts, then the shared one) are loaded at once through row-sized buffer
+// resources (slots past k get a zero-size resource: no access, zeros), dotted with
+// the slots' SwiGLU outputs staged in LDS (lane l: chunks l, l + 64, ... of each
+// row), and lane 0 adds the k weighted terms in ascending expert id within each
+// half: y = (shared + local) + f32(f16(remote)), x[r] += y.
 struct MoeDownP {
   const uint16_t* w_e;   // [E, d, ff]
   const uint16_t* w_s;   // [d, ff]
@@ -201,20 +174,51 @@ struct MoeDownP {
   float* x;              // [d] residual, updated
   int d, ff, k, remote_from, E;
 };
+constexpr int DOWN_THREADS = 512;
+constexpr int DOWN_NW = DOWN_THREADS / WAVE;
+constexpr int DOWN_K1 = MOE_MAXK + 1;
 
-__global__ __launch_bounds__(256) void k_moe_down(MoeDownP p) {
-  extern __shared__ float ms[];  // (k+1) * ff
+template <int CPL>
+__global__ __launch_bounds__(DOWN_THREADS) void k_moe_down(MoeDownP p) {
+  extern __shared__ float ms[];  // (k+1) * ff, then one zero chunk
   __shared__ int ids[MOE_MAXK];
   __shared__ float wts[MOE_MAXK];
   __shared__ int order[MOE_MAXK];   // slots sorted by ascending expert id
-  __shared__ float accs[4][MOE_MAXK + 1];
   const int nm = (p.k + 1) * p.ff;
-  for (int i = threadIdx.x * 4; i < nm; i += 256 * 4)
-    *reinterpret_cast<f32x4*>(ms + i) = *reinterpret_cast<const f32x4*>(p.mbuf + i);
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  const int nck = p.ff / 8;
+  const int rowb = p.ff * 2;
+  // every slot's down-matrix row r, loaded through a row-sized buffer resource
+  u32x4 v[DOWN_K1][CPL];
+  // the slots' expert ids in one batch of scalar loads (the idx area holds 16 words)
+  int ev[MOE_MAXK];
+#pragma unroll
+  for (int j = 0; j < MOE_MAXK; ++j) ev[j] = min(max(p.idx[j], 0), p.E - 1);
+  auto load_row = [&](int r) {
+#pragma unroll
+    for (int j = 0; j < DOWN_K1; ++j) {
+      const bool live = j <= p.k;
+      const int ej = j < p.k ? ev[j] : 0;
+      const uint16_t* base = j < p.k ? p.w_e + (long long)ej * p.d * p.ff : p.w_s;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(base + (long long)r * p.ff), (short)0, live ? rowb : 0, 0x00020000);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c)
+        v[j][c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (lane + WAVE * c) * 16, 0, 2));
+    }
+  };
+  int r = blockIdx.x * DOWN_NW + wv;
+  if (r < p.d) load_row(r);   // the first row's weights go out before the staging
+  for (int b = wv * 256; b < nm; b += DOWN_NW * 256)
+    if (b + 4 * lane < nm)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(p.mbuf + b + 4 * lane),
+                                       (__attribute__((address_space(3))) void*)(ms + b), 16, 0, 0);
+  if (threadIdx.x < 8) ms[nm + threadIdx.x] = 0.f;
   if (threadIdx.x < p.k) {
     ids[threadIdx.x] = min(max(p.idx[threadIdx.x], 0), p.E - 1);   // indices are device data
     wts[threadIdx.x] = p.wts[threadIdx.x];
   }
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x < p.k) {
     // rank of this slot by (expert id, slot): a permutation even if ids repeat
@@ -224,47 +228,54 @@ __global__ __launch_bounds__(256) void k_moe_down(MoeDownP p) {
     order[rank] = threadIdx.x;
   }
   __syncthreads();
-  const int lane = threadIdx.x & 63, wv = threadIdx.x / 64;
-  const int nck = p.ff / 8;
-  for (int r = blockIdx.x * 4 + wv; r < p.d; r += gridDim.x * 4) {
-    for (int j = 0; j <= p.k; ++j) {
-      const uint16_t* row = (j < p.k ? p.w_e + (long long)ids[j] * p.d * p.ff : p.w_s) +
-                            (long long)r * p.ff;
-      float a = 0.f;
-      for (int c = lane; c < nck; c += 64) {
-        const u32x4 v = ld_stream16(row + (long long)c * 8);
-        acc_chunk<LPS_BF16>(v, 0, ms + j * p.ff + c * 8, a);
+  for (; r < p.d; r += gridDim.x * DOWN_NW) {
+    if (r != int(blockIdx.x * DOWN_NW + wv)) load_row(r);
+    float a[DOWN_K1];
+#pragma unroll
+    for (int j = 0; j < DOWN_K1; ++j) {
+      a[j] = 0.f;
+      if (j <= p.k) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          const int ch = lane + WAVE * c;
+          const float* xp = ch < nck ? ms + j * p.ff + ch * 8 : ms + nm;   // past the row: zero chunk
+          acc_chunk<LPS_BF16>(v[j][c], 0, xp, a[j]);
+        }
+        a[j] = wave_sum(a[j]);
       }
-      a = wave_sum(a);
-      if (lane == 0) accs[wv][j] = a;
     }
     if (lane == 0) {
       // ascending expert id within each half
       float local = 0.f, remote = 0.f;
       for (int n = 0; n < p.k; ++n) {
         const int j = order[n];
-        const float term = wts[j] * accs[wv][j];
+        float aj = 0.f;
+#pragma unroll
+        for (int q = 0; q < DOWN_K1; ++q) aj = q == j ? a[q] : aj;
+        const float term = wts[j] * aj;
         if (ids[j] < p.remote_from) local += term;
         else remote += term;
       }
+      float ash = 0.f;
+#pragma unroll
+      for (int q = 0; q < DOWN_K1; ++q) ash = q == p.k ? a[q] : ash;
       const float r32 = static_cast<float>(static_cast<_Float16>(remote));
-      const float y = (accs[wv][p.k] + local) + r32;
+      const float y = (ash + local) + r32;
       p.x[r] = p.x[r] + y;
     }
   }
 }
 
 struct MoeScratch {
-  size_t logits, cnt, idx, w, mbuf, total;
+  size_t idx, w, logits, mbuf, total;
 };
 static MoeScratch moe_scratch(const lps_moe_desc* m) {
   MoeScratch s{};
-  s.cnt = 0;
-  s.logits = align256(4);
-  s.idx = s.logits + align256(size_t(m->n_experts) * 4);
-  s.w = s.idx + align256(size_t(m->top_k) * 4);
-  s.mbuf = s.w + align256(size_t(m->top_k) * 4);
-  s.total = s.mbuf + align256(size_t(m->top_k + 1) * m->ff * 4);
+  s.idx = 0;                                            // read as 16 words: keep 256 bytes
+  s.w = s.idx + align256(size_t(MOE_MAXK) * 4);
+  s.logits = s.w + align256(size_t(m->top_k) * 4);
+  s.mbuf = s.logits + align256(size_t(m->n_experts) * 4);
+  s.total = s.mbuf + align256((size_t(m->top_k + 1) * m->ff + 8) * 4);
   return s;
 }
 
@@ -292,7 +303,7 @@ using namespace lps;
 
 extern "C" size_t lps_moe_route_scratch_bytes(const lps_moe_desc* m, int32_t T) {
   if (check_moe(m, "lps_moe_route_scratch_bytes") || T < 0) return 0;
-  return align256(size_t(T) * 4) + align256(size_t(T) * m->n_experts * 4);
+  return align256(size_t(T) * m->n_experts * 4);
 }
 
 extern "C" int lps_moe_route(const lps_moe_desc* m, const float* x, int32_t T, int32_t* idx,
@@ -304,11 +315,8 @@ extern "C" int lps_moe_route(const lps_moe_desc* m, const float* x, int32_t T, i
   LPS_REQUIRE(x && idx && w && scratch, LPS_EINVAL, "lps_moe_route: null pointer");
   LPS_REQUIRE(scratch_bytes >= lps_moe_route_scratch_bytes(m, T), LPS_EINVAL,
               "lps_moe_route: scratch %zu < %zu", scratch_bytes, lps_moe_route_scratch_bytes(m, T));
-  rc = ensure_lds((const void*)k_route, size_t(m->d) * 4);
-  if (rc) return rc;
-  char* s = static_cast<char*>(scratch);
-  return launch_route(m, x, T, idx, w, reinterpret_cast<float*>(s + align256(size_t(T) * 4)),
-                      reinterpret_cast<int*>(s), as_stream(stream));
+  LPS_REQUIRE(m->d <= 4096, LPS_EUNSUP, "lps_moe_route: d %d > 4096", m->d);
+  return launch_route(m, x, T, static_cast<float*>(scratch), idx, w, as_stream(stream));
 }
 
 extern "C" size_t lps_moe_layer_scratch_bytes(const lps_moe_desc* m) {
@@ -329,30 +337,18 @@ extern "C" int lps_moe_layer_decode(const lps_moe_desc* m, float* x, void* scrat
   int32_t* idx = reinterpret_cast<int32_t*>(sc + s.idx);
   float* wts = reinterpret_cast<float*>(sc + s.w);
   float* mbuf = reinterpret_cast<float*>(sc + s.mbuf);
-  if ((rc = ensure_lds((const void*)k_route, size_t(m->d) * 4)) ||
-      (rc = ensure_lds((const void*)k_moe_gu<4>, size_t(m->d) * 4)) ||
-      (rc = ensure_lds((const void*)k_moe_down, size_t(m->top_k + 1) * m->ff * 4)))
-    return rc;
-  rc = launch_route(m, x, 1, idx, wts, reinterpret_cast<float*>(sc + s.logits),
-                    reinterpret_cast<int*>(sc + s.cnt), st);
+  const size_t dlds = (size_t(m->top_k + 1) * m->ff + 8) * 4;
+  const int cpl = (m->ff / 8 + WAVE - 1) / WAVE;
+  LPS_REQUIRE(cpl <= 4, LPS_EUNSUP, "lps_moe_layer_decode: ff %d > 2048", m->ff);
+  const void* down = cpl <= 1 ? (const void*)k_moe_down<1> : cpl <= 2 ? (const void*)k_moe_down<2>
+                                                                     : (const void*)k_moe_down<4>;
+  LPS_REQUIRE(m->d <= 4096, LPS_EUNSUP, "lps_moe_layer_decode: d %d > 4096", m->d);
+  if ((rc = ensure_lds(down, dlds))) return rc;
+  rc = launch_route(m, x, 1, reinterpret_cast<float*>(sc + s.logits), idx, wts, st);
   if (rc) return rc;
-  MoeGuP g{};
-  g.x = x;
-  g.g = m->g_ffn;
-  g.eps = m->eps;
-  g.w_e = static_cast<const uint16_t*>(m->w_gu_e);
-  g.w_s = static_cast<const uint16_t*>(m->w_gu_s);
-  g.idx = idx;
-  g.d = m->d;
-  g.ff = m->ff;
-  g.k = m->top_k;
-  g.units = (m->top_k + 1) * m->ff;
-  g.E = m->n_experts;
-  g.mbuf = mbuf;
-  int grid = (g.units + 3) / 4;
-  if (grid > 2048) grid = 2048;
-  hipLaunchKernelGGL(k_moe_gu<4>, dim3(grid), dim3(256), size_t(m->d) * 4, st, g);
-  LPS_HIP(hipGetLastError());
+  rc = launch_moe_gu(m->w_gu_e, m->w_gu_s, idx, m->n_experts, m->top_k, m->ff, m->d, x, m->g_ffn,
+                     m->eps, mbuf, st);
+  if (rc) return rc;
   MoeDownP dn{};
   dn.w_e = static_cast<const uint16_t*>(m->w_d_e);
   dn.w_s = static_cast<const uint16_t*>(m->w_d_s);
@@ -365,8 +361,13 @@ extern "C" int lps_moe_layer_decode(const lps_moe_desc* m, float* x, void* scrat
   dn.k = m->top_k;
   dn.remote_from = m->remote_from;
   dn.E = m->n_experts;
-  int gd = (m->d + 3) / 4;
-  hipLaunchKernelGGL(k_moe_down, dim3(gd), dim3(256), size_t(m->top_k + 1) * m->ff * 4, st, dn);
+  const int gd = (m->d + DOWN_NW - 1) / DOWN_NW;
+  if (cpl <= 1)
+    hipLaunchKernelGGL(k_moe_down<1>, dim3(gd), dim3(DOWN_THREADS), dlds, st, dn);
+  else if (cpl <= 2)
+    hipLaunchKernelGGL(k_moe_down<2>, dim3(gd), dim3(DOWN_THREADS), dlds, st, dn);
+  else
+    hipLaunchKernelGGL(k_moe_down<4>, dim3(gd), dim3(DOWN_THREADS), dlds, st, dn);
   LPS_HIP(hipGetLastError());
   return LPS_OK;
 }
