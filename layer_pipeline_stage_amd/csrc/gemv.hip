@@ -32,7 +32,7 @@
 namespace lps {
 
 enum { EPI_STORE = LPS_EPI_STORE, EPI_ADD = LPS_EPI_ADD, EPI_SWIGLU = LPS_EPI_SWIGLU, EPI_QKV = 3,
-       EPI_LOGITS = 4, EPI_MOEGU = 5 };
+       EPI_LOGITS = 4, EPI_MOEGU = 5, EPI_MOEDN = 6 };
 
 struct GemvP {
   const uint8_t* w;
@@ -59,6 +59,9 @@ struct GemvP {
   const int32_t* eidx;
   long long estride;
   int kslots, ff, E;
+  // MoE down: unit u = (slot j, row pair i) of slot j's [rps, K] matrix, dotted with
+  // activation row j of x ([kslots + 1, K], all staged); out y[j * rps + row]
+  int rps;
 };
 
 template <int EPI>
@@ -67,6 +70,11 @@ __device__ __forceinline__ void unit_rows(const GemvP& p, int u, int& r0, int& r
     const int j = u / p.ff;
     r0 = u - j * p.ff;
     r1 = r0 + p.ff;
+  } else if constexpr (EPI == EPI_MOEDN) {
+    const int half = p.rps >> 1;
+    const int j = u / half;
+    r0 = 2 * (u - j * half);
+    r1 = r0 + 1;
   } else if constexpr (EPI == EPI_SWIGLU) {
     r0 = u;
     r1 = u + (p.N >> 1);
@@ -84,14 +92,25 @@ __device__ __forceinline__ void unit_rows(const GemvP& p, int u, int& r0, int& r
 // first weight row of the matrix unit u belongs to
 template <int EPI>
 __device__ __forceinline__ const uint8_t* unit_base(const GemvP& p, int u) {
-  if constexpr (EPI == EPI_MOEGU) {
-    const int j = u / p.ff;
+  if constexpr (EPI == EPI_MOEGU || EPI == EPI_MOEDN) {
+    const int j = EPI == EPI_MOEGU ? u / p.ff : u / (p.rps >> 1);
     if (j >= p.kslots) return p.w_s;
     const int e = min(max(p.eidx[j], 0), p.E - 1);   // indices are device data
     return p.w + (long long)e * p.estride;
   } else {
     return p.w;
   }
+}
+
+// offset of unit u's activation row in the staged vector, and the staged length
+template <int EPI>
+__device__ __forceinline__ int unit_xoff(const GemvP& p, int u) {
+  if constexpr (EPI == EPI_MOEDN) return (u / (p.rps >> 1)) * p.K;
+  else return 0;
+}
+template <int EPI>
+__host__ __device__ __forceinline__ int staged_len(const GemvP& p) {
+  return EPI == EPI_MOEDN ? (p.kslots + 1) * p.K : p.K;
 }
 
 __device__ __forceinline__ void store_kv(void* base, int kvdtype, long long off, float v) {
@@ -112,6 +131,10 @@ __device__ __forceinline__ void epilogue(const GemvP& p, int u, int r0, int r1, 
     if (r1 >= 0) p.y[r1] = y1 + a1;
   } else if constexpr (EPI == EPI_SWIGLU || EPI == EPI_MOEGU) {
     p.y[u] = silu(a0) * a1;
+  } else if constexpr (EPI == EPI_MOEDN) {
+    const int j = u / (p.rps >> 1);
+    p.y[(long long)j * p.rps + r0] = a0;
+    if (r1 < p.rps) p.y[(long long)j * p.rps + r1] = a1;
   } else {  // QKV: rotate q and k heads at pos, store q, append k and v to the caches
     const int half = p.hd >> 1;
     const int hh = u / half, i = u - hh * half;
@@ -229,12 +252,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const uint8_t* base, 
       _Pragma("unroll") for (int i = 0; i < U; ++i) S0[i] = S1[i] = 0;                  \
     }                                                                                   \
   }
-#define BUF_FMA(V0, V1, S0, S1, B0)                                \
+#define BUF_FMA(V0, V1, S0, S1, B0, XO)                            \
   _Pragma("unroll") for (int i = 0; i < U; ++i) {                  \
-    int c = (B0) + lane + WAVE * i;                                \
-    c = c < nck ? c : nck;                                         \
-    acc_chunk<WT>(V0[i], S0[i], xs + c * XS, a0);                  \
-    acc_chunk<WT>(V1[i], S1[i], xs + c * XS, a1);                  \
+    const int c = (B0) + lane + WAVE * i;                          \
+    const int xi = c < nck ? (XO) + c * XS : zoff;                 \
+    acc_chunk<WT>(V0[i], S0[i], xs + xi, a0);                      \
+    acc_chunk<WT>(V1[i], S1[i], xs + xi, a1);                      \
   }
 // One step of the double-buffered walk: issue the loads of the batch after the
 // current one (into buffer N), then consume the current batch (buffer C).  A
@@ -245,7 +268,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const uint8_t* base, 
     if (nb >= nck) { nu = u + stride; nb = 0; }                    \
     const bool more = nu < p.units;                                \
     BUF_LOAD(NV0, NV1, NS0, NS1, NY0, NY1, nu, nb, more)           \
-    BUF_FMA(CV0, CV1, CS0, CS1, b0)                                \
+    BUF_FMA(CV0, CV1, CS0, CS1, b0, unit_xoff<EPI>(p, u))          \
     if (nu != u) {                                                 \
       int r0, r1;                                                  \
       unit_rows<EPI>(p, u, r0, r1);                                \
@@ -275,11 +298,13 @@ __global__ __launch_bounds__(NT) void k_gemv_buf(GemvP p) {
   uint32_t sa0[U], sa1[U], sb0[U], sb1[U];
   float ya0 = 0.f, ya1 = 0.f, yb0 = 0.f, yb1 = 0.f;   // residual rows (EPI_ADD)
   BUF_LOAD(va0, va1, sa0, sa1, ya0, ya1, u, 0, u < p.units)
+  // a chunk past the row end (zero weights) reads the zero chunk after the staged vector
+  const int zoff = WT == LPS_MXFP4 ? nck * XS : staged_len<EPI>(p);
   if constexpr (WT == LPS_MXFP4) {
     stage_x_mx<NORM, NT>(p.x, p.g, p.eps, p.K, xs);
   } else {
-    if (threadIdx.x < CH) xs[p.K + threadIdx.x] = 0.f;   // zero chunk
-    stage_x<NORM, NT>(p.x, p.g, p.eps, p.K, xs);
+    if (threadIdx.x < CH) xs[zoff + threadIdx.x] = 0.f;   // zero chunk
+    stage_x<NORM, NT>(p.x, p.g, p.eps, staged_len<EPI>(p), xs);
   }
   if (u < p.units) {
     float a0 = 0.f, a1 = 0.f;
@@ -291,7 +316,7 @@ __global__ __launch_bounds__(NT) void k_gemv_buf(GemvP p) {
     } else {
       // one batch in flight per wave, for launches where a wave meets one batch
       for (;;) {
-        BUF_FMA(va0, va1, sa0, sa1, b0)
+        BUF_FMA(va0, va1, sa0, sa1, b0, unit_xoff<EPI>(p, u))
         int nu = u, nb = b0 + WAVE * U;
         if (nb >= nck) { nu = u + stride; nb = 0; }
         if (nu != u) {
@@ -357,7 +382,7 @@ static int launch_t(const GemvP& p, hipStream_t st, Stamp sp, int* waves) {
   constexpr int CH = Fmt<WT>::CH;
   const int per_lane = (p.K / CH + WAVE - 1) / WAVE;
   const size_t lds = WT == LPS_MXFP4 ? size_t(p.K / CH + 1) * MX_XS * sizeof(float)
-                                     : (size_t(p.K) + CH) * sizeof(float);
+                                     : (size_t(staged_len<EPI>(p)) + CH) * sizeof(float);
 #define LPS_GOB(UU, NTV, MAXBV)                                                                  \
   do {                                                                                           \
     constexpr int NW_ = (NTV) / WAVE;                                                            \
@@ -383,7 +408,8 @@ static int launch_t(const GemvP& p, hipStream_t st, Stamp sp, int* waves) {
     else if (per_lane <= 9) LPS_GOB(9, LPS_MX_NTL, LPS_MX_MAXBL);
     else LPS_GOB(4, LPS_MX_NT, LPS_MX_MAXB);
   } else {
-    LPS_GOB(LPS_BF_U, LPS_BF_NT, LPS_BF_MAXB);
+    if (per_lane <= 2) LPS_GOB(2, LPS_BF_NT, LPS_BF_MAXB);   // short rows: no empty chunk slots
+    else LPS_GOB(LPS_BF_U, LPS_BF_NT, LPS_BF_MAXB);
   }
 #undef LPS_GOB
   LPS_HIP(hipGetLastError());
@@ -448,6 +474,25 @@ int launch_moe_gu(const void* w_e, const void* w_s, const int32_t* eidx, int E, 
   p.units = (kslots + 1) * ff;
   set_rows(p, LPS_BF16, d);
   return launch_wt<EPI_MOEGU, true>(LPS_BF16, p, st, Stamp{});
+}
+
+int launch_moe_down(const void* w_e, const void* w_s, const int32_t* eidx, int E, int kslots,
+                    int d, int ff, const float* m, float* z, hipStream_t st) {
+  GemvP p{};
+  p.w = static_cast<const uint8_t*>(w_e);
+  p.w_s = static_cast<const uint8_t*>(w_s);
+  p.eidx = eidx;
+  p.E = E;
+  p.kslots = kslots;
+  p.rps = d;
+  p.estride = (long long)d * ff * 2;
+  p.N = d;
+  p.K = ff;
+  p.x = m;
+  p.y = z;
+  p.units = (kslots + 1) * (d / 2);
+  set_rows(p, LPS_BF16, ff);
+  return launch_wt<EPI_MOEDN, false>(LPS_BF16, p, st, Stamp{});
 }
 
 int launch_qkv(const QkvArgs& a, hipStream_t st, Stamp sp) {

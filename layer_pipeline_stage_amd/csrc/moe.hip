@@ -159,66 +159,26 @@ static int launch_route(const lps_moe_desc* m, const float* x, int T, float* log
 // launch_moe_gu (the weight-streaming GEMV with an expert-table row map).
 
 // ---- A11 + A12: down projections of all slots and the fixed-order combine ----------
-// One wave per output row r: the rows r of every slot's down matrix (k selected
-// experts, then the shared one) are loaded at once through row-sized buffer
-// resources (slots past k get a zero-size resource: no access, zeros), dotted with
-// the slots' SwiGLU outputs staged in LDS (lane l: chunks l, l + 64, ... of each
-// row), and lane 0 adds the k weighted terms in ascending expert id within each
-// half: y = (shared + local) + f32(f16(remote)), x[r] += y.
-struct MoeDownP {
-  const uint16_t* w_e;   // [E, d, ff]
-  const uint16_t* w_s;   // [d, ff]
+// launch_moe_down (the weight-streaming GEMV over every slot's down matrix, each
+// slot's SwiGLU row staged side by side) writes z[j, r]; k_moe_combine then adds,
+// per output row r, the k weighted terms in ascending expert id within each half:
+// y = (shared + local) + f32(f16(remote)), x[r] += y.
+struct MoeCombP {
   const int32_t* idx;    // [k]
   const float* wts;      // [k]
-  const float* mbuf;     // [(k+1), ff]
+  const float* z;        // [(k+1), d]
   float* x;              // [d] residual, updated
-  int d, ff, k, remote_from, E;
+  int d, k, remote_from, E;
 };
-constexpr int DOWN_THREADS = 512;
-constexpr int DOWN_NW = DOWN_THREADS / WAVE;
-constexpr int DOWN_K1 = MOE_MAXK + 1;
 
-template <int CPL>
-__global__ __launch_bounds__(DOWN_THREADS) void k_moe_down(MoeDownP p) {
-  extern __shared__ float ms[];  // (k+1) * ff, then one zero chunk
+__global__ __launch_bounds__(256) void k_moe_combine(MoeCombP p) {
   __shared__ int ids[MOE_MAXK];
   __shared__ float wts[MOE_MAXK];
   __shared__ int order[MOE_MAXK];   // slots sorted by ascending expert id
-  const int nm = (p.k + 1) * p.ff;
-  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
-  const int nck = p.ff / 8;
-  const int rowb = p.ff * 2;
-  // every slot's down-matrix row r, loaded through a row-sized buffer resource
-  u32x4 v[DOWN_K1][CPL];
-  // the slots' expert ids in one batch of scalar loads (the idx area holds 16 words)
-  int ev[MOE_MAXK];
-#pragma unroll
-  for (int j = 0; j < MOE_MAXK; ++j) ev[j] = min(max(p.idx[j], 0), p.E - 1);
-  auto load_row = [&](int r) {
-#pragma unroll
-    for (int j = 0; j < DOWN_K1; ++j) {
-      const bool live = j <= p.k;
-      const int ej = j < p.k ? ev[j] : 0;
-      const uint16_t* base = j < p.k ? p.w_e + (long long)ej * p.d * p.ff : p.w_s;
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint16_t*>(base + (long long)r * p.ff), (short)0, live ? rowb : 0, 0x00020000);
-#pragma unroll
-      for (int c = 0; c < CPL; ++c)
-        v[j][c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (lane + WAVE * c) * 16, 0, 2));
-    }
-  };
-  int r = blockIdx.x * DOWN_NW + wv;
-  if (r < p.d) load_row(r);   // the first row's weights go out before the staging
-  for (int b = wv * 256; b < nm; b += DOWN_NW * 256)
-    if (b + 4 * lane < nm)
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(p.mbuf + b + 4 * lane),
-                                       (__attribute__((address_space(3))) void*)(ms + b), 16, 0, 0);
-  if (threadIdx.x < 8) ms[nm + threadIdx.x] = 0.f;
   if (threadIdx.x < p.k) {
     ids[threadIdx.x] = min(max(p.idx[threadIdx.x], 0), p.E - 1);   // indices are device data
     wts[threadIdx.x] = p.wts[threadIdx.x];
   }
-  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x < p.k) {
     // rank of this slot by (expert id, slot): a permutation even if ids repeat
@@ -228,54 +188,31 @@ __global__ __launch_bounds__(DOWN_THREADS) void k_moe_down(MoeDownP p) {
     order[rank] = threadIdx.x;
   }
   __syncthreads();
-  for (; r < p.d; r += gridDim.x * DOWN_NW) {
-    if (r != int(blockIdx.x * DOWN_NW + wv)) load_row(r);
-    float a[DOWN_K1];
-#pragma unroll
-    for (int j = 0; j < DOWN_K1; ++j) {
-      a[j] = 0.f;
-      if (j <= p.k) {
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-          const int ch = lane + WAVE * c;
-          const float* xp = ch < nck ? ms + j * p.ff + ch * 8 : ms + nm;   // past the row: zero chunk
-          acc_chunk<LPS_BF16>(v[j][c], 0, xp, a[j]);
-        }
-        a[j] = wave_sum(a[j]);
-      }
-    }
-    if (lane == 0) {
-      // ascending expert id within each half
-      float local = 0.f, remote = 0.f;
-      for (int n = 0; n < p.k; ++n) {
-        const int j = order[n];
-        float aj = 0.f;
-#pragma unroll
-        for (int q = 0; q < DOWN_K1; ++q) aj = q == j ? a[q] : aj;
-        const float term = wts[j] * aj;
-        if (ids[j] < p.remote_from) local += term;
-        else remote += term;
-      }
-      float ash = 0.f;
-#pragma unroll
-      for (int q = 0; q < DOWN_K1; ++q) ash = q == p.k ? a[q] : ash;
-      const float r32 = static_cast<float>(static_cast<_Float16>(remote));
-      const float y = (ash + local) + r32;
-      p.x[r] = p.x[r] + y;
-    }
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= p.d) return;
+  float local = 0.f, remote = 0.f;
+  for (int n = 0; n < p.k; ++n) {
+    const int j = order[n];
+    const float term = wts[j] * p.z[(long long)j * p.d + r];
+    if (ids[j] < p.remote_from) local += term;
+    else remote += term;
   }
+  const float r32 = static_cast<float>(static_cast<_Float16>(remote));
+  const float y = (p.z[(long long)p.k * p.d + r] + local) + r32;
+  p.x[r] = p.x[r] + y;
 }
 
 struct MoeScratch {
-  size_t idx, w, logits, mbuf, total;
+  size_t idx, w, logits, mbuf, z, total;
 };
 static MoeScratch moe_scratch(const lps_moe_desc* m) {
   MoeScratch s{};
-  s.idx = 0;                                            // read as 16 words: keep 256 bytes
+  s.idx = 0;
   s.w = s.idx + align256(size_t(MOE_MAXK) * 4);
   s.logits = s.w + align256(size_t(m->top_k) * 4);
   s.mbuf = s.logits + align256(size_t(m->n_experts) * 4);
-  s.total = s.mbuf + align256((size_t(m->top_k + 1) * m->ff + 8) * 4);
+  s.z = s.mbuf + align256(size_t(m->top_k + 1) * m->ff * 4);
+  s.total = s.z + align256(size_t(m->top_k + 1) * m->d * 4);
   return s;
 }
 
@@ -289,7 +226,7 @@ static int check_moe(const lps_moe_desc* m, const char* who) {
               "%s: top_k %d outside [1, min(%d, n_experts)]", who, m->top_k, MOE_MAXK);
   LPS_REQUIRE(m->remote_from >= 0 && m->remote_from <= m->n_experts, LPS_EINVAL,
               "%s: remote_from %d outside [0, n_experts]", who, m->remote_from);
-  LPS_REQUIRE(size_t(m->d) * 4 <= 160 * 1024 && size_t(m->top_k + 1) * m->ff * 4 <= 160 * 1024,
+  LPS_REQUIRE(size_t(m->d) * 4 <= 160 * 1024 && (size_t(m->top_k + 1) * m->ff + 8) * 4 <= 160 * 1024,
               LPS_EUNSUP, "%s: activations exceed 160 KiB of LDS", who);
   LPS_REQUIRE(m->g_ffn && m->w_r && m->w_gu_e && m->w_d_e && m->w_gu_s && m->w_d_s, LPS_EINVAL,
               "%s: null weight pointer", who);
@@ -337,37 +274,26 @@ extern "C" int lps_moe_layer_decode(const lps_moe_desc* m, float* x, void* scrat
   int32_t* idx = reinterpret_cast<int32_t*>(sc + s.idx);
   float* wts = reinterpret_cast<float*>(sc + s.w);
   float* mbuf = reinterpret_cast<float*>(sc + s.mbuf);
-  const size_t dlds = (size_t(m->top_k + 1) * m->ff + 8) * 4;
-  const int cpl = (m->ff / 8 + WAVE - 1) / WAVE;
-  LPS_REQUIRE(cpl <= 4, LPS_EUNSUP, "lps_moe_layer_decode: ff %d > 2048", m->ff);
-  const void* down = cpl <= 1 ? (const void*)k_moe_down<1> : cpl <= 2 ? (const void*)k_moe_down<2>
-                                                                     : (const void*)k_moe_down<4>;
-  LPS_REQUIRE(m->d <= 4096, LPS_EUNSUP, "lps_moe_layer_decode: d %d > 4096", m->d);
-  if ((rc = ensure_lds(down, dlds))) return rc;
+  LPS_REQUIRE(m->d <= 4096 && m->d % 2 == 0, LPS_EUNSUP, "lps_moe_layer_decode: d %d (even, <= 4096)",
+              m->d);
   rc = launch_route(m, x, 1, reinterpret_cast<float*>(sc + s.logits), idx, wts, st);
   if (rc) return rc;
   rc = launch_moe_gu(m->w_gu_e, m->w_gu_s, idx, m->n_experts, m->top_k, m->ff, m->d, x, m->g_ffn,
                      m->eps, mbuf, st);
   if (rc) return rc;
-  MoeDownP dn{};
-  dn.w_e = static_cast<const uint16_t*>(m->w_d_e);
-  dn.w_s = static_cast<const uint16_t*>(m->w_d_s);
-  dn.idx = idx;
-  dn.wts = wts;
-  dn.mbuf = mbuf;
-  dn.x = x;
-  dn.d = m->d;
-  dn.ff = m->ff;
-  dn.k = m->top_k;
-  dn.remote_from = m->remote_from;
-  dn.E = m->n_experts;
-  const int gd = (m->d + DOWN_NW - 1) / DOWN_NW;
-  if (cpl <= 1)
-    hipLaunchKernelGGL(k_moe_down<1>, dim3(gd), dim3(DOWN_THREADS), dlds, st, dn);
-  else if (cpl <= 2)
-    hipLaunchKernelGGL(k_moe_down<2>, dim3(gd), dim3(DOWN_THREADS), dlds, st, dn);
-  else
-    hipLaunchKernelGGL(k_moe_down<4>, dim3(gd), dim3(DOWN_THREADS), dlds, st, dn);
+  float* z = reinterpret_cast<float*>(sc + s.z);
+  rc = launch_moe_down(m->w_d_e, m->w_d_s, idx, m->n_experts, m->top_k, m->d, m->ff, mbuf, z, st);
+  if (rc) return rc;
+  MoeCombP cp{};
+  cp.idx = idx;
+  cp.wts = wts;
+  cp.z = z;
+  cp.x = x;
+  cp.d = m->d;
+  cp.k = m->top_k;
+  cp.remote_from = m->remote_from;
+  cp.E = m->n_experts;
+  hipLaunchKernelGGL(k_moe_combine, dim3((m->d + 255) / 256), dim3(256), 0, st, cp);
   LPS_HIP(hipGetLastError());
   return LPS_OK;
 }
