@@ -75,6 +75,24 @@ int lps_stage_plan_counts(int32_t n_layers, int32_t n_stages, const int32_t* cou
  * for an invalid fence or a layer outside [0, fence[n_stages]). (fn stage_of) */
 int lps_stage_of(const int32_t* fence, int32_t n_stages, int32_t layer);
 
+/* Memory-balancing split (host only): ninfer "Multi-GPU: layer pipeline
+ * stages", How it works (solve_stage_plan: the most KV page groups every stage
+ * can hold, then the least-full stage) and Verification (a brute-force partition
+ * oracle).  Bytes, host arrays: stage_free[s] > 0 and stage_overhead[s] >= 0
+ * (n_stages each: what the device has free and what the stage needs besides its
+ * layers, e.g. the head on the head stage), layer_fixed[l] (weights and fixed
+ * state) and layer_kv[l] (KV bytes per page group), n_layers each.  Every stage
+ * holds the same number P of page groups of its own layers' KV; the split
+ * maximises P (capped at max_groups, which a stage without KV layers reports),
+ * then minimises the largest (overhead + fixed + P * kv) / free, then takes the
+ * lexicographically smallest fence.  Writes fence_out (n_stages + 1 int32) and
+ * *groups_out = P.  LPS_EINVAL on bad arguments, LPS_EUNSUP if no split holds
+ * even the layers' fixed bytes. */
+int lps_stage_solve(int32_t n_layers, int32_t n_stages, const int64_t* stage_free,
+                    const int64_t* stage_overhead, const int64_t* layer_fixed,
+                    const int64_t* layer_kv, int64_t max_groups, int32_t* fence_out,
+                    int64_t* groups_out);
+
 /* ---- A2-A9, A17: one decoder layer ----------------------------------------
  * The pre-norm block: h = RMSNorm(x)*g_attn; [q|k|v] = W_qkv h; RoPE on the
  * pairs (i, i+hd/2) of every q and k head at position pos; k, v stored at row

@@ -60,6 +60,7 @@ class Counters(C.Structure):
 P = C.c_void_p
 I32, I64, F32, SZ = C.c_int32, C.c_int64, C.c_float, C.c_size_t
 PI32 = C.POINTER(C.c_int32)
+PI64 = C.POINTER(C.c_int64)
 PP = C.POINTER(C.c_void_p)
 
 STREAM_SINK = 2048   # LPS_STREAM_SINK: uint32 entries lps_hbm_stream_read writes
@@ -71,6 +72,7 @@ SIGS = {
     "lps_stage_plan": (C.c_int, [I32, I32, PI32, I32, PI32], True),
     "lps_stage_plan_counts": (C.c_int, [I32, I32, PI32, PI32], True),
     "lps_stage_of": (C.c_int, [PI32, I32, I32], True),
+    "lps_stage_solve": (C.c_int, [I32, I32, PI64, PI64, PI64, PI64, I64, PI32, PI64], True),
     "lps_layer_scratch_bytes": (SZ, [C.POINTER(LayerDesc)], False),
     "lps_layer_forward": (C.c_int, [C.POINTER(LayerDesc), P, I32, P, SZ, P], True),
     "lps_model_create": (C.c_int, [C.POINTER(LayerDesc), I32, PP], True),
@@ -177,6 +179,21 @@ def timer_stop(cap=1 << 16):
     n = C.c_int32()
     lps_timer_stop(buf, cap, C.byref(n))  # noqa: F821
     return [buf[i] for i in range(n.value)]
+
+
+def stage_solve(free, overhead, fixed, kv, n_stages, max_groups):
+    """lps_stage_solve with Python lists -> (fence, page groups)."""
+    L = len(fixed)
+    A = C.c_int64 * max(1, n_stages)
+    B = C.c_int64 * max(1, L)
+    fence = (C.c_int32 * (n_stages + 1))()
+    g = C.c_int64(0)
+    lib = load()
+    rc = lib.lps_stage_solve(L, n_stages, A(*free), A(*overhead), B(*fixed), B(*kv), max_groups,
+                             fence, C.byref(g))
+    if rc < 0:
+        raise LpsError(rc, lib.lps_last_error().decode())
+    return list(fence), g.value
 
 
 def counters() -> dict:

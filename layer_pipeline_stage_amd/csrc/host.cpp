@@ -247,6 +247,111 @@ int lps_stage_of(const int32_t* fence, int32_t n_stages, int32_t layer) {
   return fail(LPS_ERANGE, "lps_stage_of: unreachable");
 }
 
+// ---- memory-balancing split (ninfer "Multi-GPU: layer pipeline stages", How it works:
+// the most page groups every stage can hold, then the least-full stage) -------------
+// Exact dynamic programs over contiguous splits, backward so that the forward
+// reconstruction can take, stage by stage, the smallest cut that still completes
+// an optimal split (the lexicographically smallest optimal fence):
+//  1. P = max over splits of min over stages of the groups a stage can hold;
+//  2. among splits where every stage holds P groups, minimise the largest fill
+//     (overhead + fixed + P * kv) / free, compared exactly as fractions.
+int lps_stage_solve(int32_t n_layers, int32_t n_stages, const int64_t* stage_free,
+                    const int64_t* stage_overhead, const int64_t* layer_fixed,
+                    const int64_t* layer_kv, int64_t max_groups, int32_t* fence_out,
+                    int64_t* groups_out) {
+  LPS_REQUIRE(n_layers >= 1 && n_layers <= 4096, LPS_EINVAL, "lps_stage_solve: n_layers %d", n_layers);
+  LPS_REQUIRE(n_stages >= 1 && n_stages <= n_layers, LPS_EINVAL,
+              "lps_stage_solve: n_stages %d outside [1, n_layers %d]", n_stages, n_layers);
+  LPS_REQUIRE(stage_free && stage_overhead && layer_fixed && layer_kv && fence_out && groups_out,
+              LPS_EINVAL, "lps_stage_solve: null pointer");
+  LPS_REQUIRE(max_groups >= 0 && max_groups <= (int64_t(1) << 40), LPS_EINVAL,
+              "lps_stage_solve: max_groups %lld outside [0, 2^40]", (long long)max_groups);
+  const int L = n_layers, N = n_stages;
+  for (int s = 0; s < N; ++s)
+    LPS_REQUIRE(stage_free[s] > 0 && stage_free[s] <= (int64_t(1) << 50) && stage_overhead[s] >= 0 &&
+                    stage_overhead[s] <= (int64_t(1) << 50),
+                LPS_EINVAL, "lps_stage_solve: stage %d free %lld / overhead %lld", s,
+                (long long)stage_free[s], (long long)stage_overhead[s]);
+  for (int l = 0; l < L; ++l)
+    LPS_REQUIRE(layer_fixed[l] >= 0 && layer_fixed[l] <= (int64_t(1) << 40) && layer_kv[l] >= 0 &&
+                    layer_kv[l] <= (int64_t(1) << 40),
+                LPS_EINVAL, "lps_stage_solve: layer %d fixed %lld / kv %lld", l,
+                (long long)layer_fixed[l], (long long)layer_kv[l]);
+  std::vector<int64_t> pf(L + 1, 0), pk(L + 1, 0);   // prefix sums (< 2^52)
+  for (int l = 0; l < L; ++l) {
+    pf[l + 1] = pf[l] + layer_fixed[l];
+    pk[l + 1] = pk[l] + layer_kv[l];
+  }
+  auto groups = [&](int s, int a, int b) -> int64_t {   // page groups stage s holds for [a, b)
+    const int64_t need = stage_overhead[s] + pf[b] - pf[a];
+    if (need > stage_free[s]) return -1;
+    const int64_t per = pk[b] - pk[a];
+    if (per == 0) return max_groups;
+    const int64_t g = (stage_free[s] - need) / per;
+    return g < max_groups ? g : max_groups;
+  };
+  const int64_t NEG = -2;
+  // best1[s][a]: max over splits of [a, L) into stages s..N-1 of the min groups
+  std::vector<int64_t> best1(size_t(N + 1) * (L + 1), NEG);
+  auto B1 = [&](int s, int a) -> int64_t& { return best1[size_t(s) * (L + 1) + a]; };
+  B1(N, L) = max_groups;
+  for (int s = N - 1; s >= 0; --s)
+    for (int a = s; a <= L - (N - s); ++a) {
+      int64_t best = NEG;
+      for (int b = a + 1; b <= L - (N - s - 1); ++b) {
+        const int64_t rest = B1(s + 1, b);
+        if (rest == NEG) continue;
+        const int64_t g = groups(s, a, b);
+        const int64_t v = g < rest ? g : rest;
+        if (v > best) best = v;
+      }
+      B1(s, a) = best;
+    }
+  const int64_t P = B1(0, 0);
+  LPS_REQUIRE(P >= 0, LPS_EUNSUP, "lps_stage_solve: no split of %d layers over %d stages fits", L, N);
+  // fill of stage s over [a, b) at P groups as a fraction num / den (den = free > 0)
+  struct Frac { __int128 num, den; };
+  auto less = [](const Frac& x, const Frac& y) { return x.num * y.den < y.num * x.den; };
+  auto fill = [&](int s, int a, int b) {
+    return Frac{__int128(stage_overhead[s] + pf[b] - pf[a]) + __int128(P) * (pk[b] - pk[a]),
+                __int128(stage_free[s])};
+  };
+  // best2[s][a]: min over P-feasible splits of [a, L) of the largest fill (den 0: none)
+  std::vector<Frac> best2(size_t(N + 1) * (L + 1), Frac{0, 0});
+  auto B2 = [&](int s, int a) -> Frac& { return best2[size_t(s) * (L + 1) + a]; };
+  B2(N, L) = Frac{0, 1};
+  for (int s = N - 1; s >= 0; --s)
+    for (int a = s; a <= L - (N - s); ++a) {
+      Frac best{0, 0};
+      for (int b = a + 1; b <= L - (N - s - 1); ++b) {
+        const Frac rest = B2(s + 1, b);
+        if (rest.den == 0 || groups(s, a, b) < P) continue;
+        const Frac f = fill(s, a, b);
+        const Frac v = less(f, rest) ? rest : f;
+        if (best.den == 0 || less(v, best)) best = v;
+      }
+      B2(s, a) = best;
+    }
+  // forward: the smallest cut whose stage stays within the optimum F and whose
+  // remainder can (the lexicographically smallest of the optimal fences)
+  const Frac F = B2(0, 0);
+  fence_out[0] = 0;
+  int a = 0;
+  for (int s = 0; s < N; ++s) {
+    int pick = -1;
+    for (int b = a + 1; b <= L - (N - s - 1); ++b) {
+      const Frac rest = B2(s + 1, b);
+      if (rest.den == 0 || groups(s, a, b) < P) continue;
+      if (!less(F, fill(s, a, b)) && !less(F, rest)) { pick = b; break; }
+    }
+    LPS_REQUIRE(pick > 0, LPS_ESTATE, "lps_stage_solve: reconstruction failed at stage %d", s);
+    fence_out[s + 1] = pick;
+    a = pick;
+  }
+  *groups_out = P;
+  return LPS_OK;
+}
+
 // ---- counters ---------------------------------------------------------------------
 int lps_counters(lps_counters_t* out) {
   LPS_REQUIRE(out, LPS_EINVAL, "lps_counters: null out");

@@ -55,6 +55,31 @@ def _weight(w, device):
     return to_dev(w, device), None
 
 
+def _row_bytes(wdtype: str, k: int) -> int:
+    """Bytes of one weight row of length k (MXFP4: k/2 codes + k/32 scales)."""
+    return {"f32": 4 * k, "bf16": 2 * k, "mxfp4": k // 2 + k // 32}[wdtype]
+
+
+def memory_balanced_fence(n_layers, d, nq, nkv, hd, ff, vocab, wdtype, kvdtype, n_stages,
+                          free_bytes, page_tokens=16, stage_overhead=0, max_groups=1 << 30):
+    """Split for devices with free_bytes[s] each, by lps_stage_solve (ninfer
+    "Multi-GPU: layer pipeline stages", How it works: the most KV page groups
+    every stage can hold, then the least-full stage).  A layer's fixed bytes are
+    its weights and norm gains; its KV bytes per page group are K and V rows of
+    page_tokens positions.  The embedding counts on stage 0 and the final norm
+    and LM head on the last stage (where this path runs them), plus
+    stage_overhead on every stage.  Returns (fence, page groups)."""
+    layer_w = ((nq + 2 * nkv) * hd * _row_bytes(wdtype, d) + d * _row_bytes(wdtype, nq * hd)
+               + 2 * ff * _row_bytes(wdtype, d) + d * _row_bytes(wdtype, ff) + 2 * d * 4)
+    kv = 2 * nkv * hd * page_tokens * (4 if kvdtype == "f32" else 2)
+    emb = vocab * _row_bytes("bf16" if wdtype == "mxfp4" else wdtype, d)
+    over = [stage_overhead] * n_stages
+    over[0] += emb
+    over[-1] += emb + d * 4
+    return lps.stage_solve(list(free_bytes), over, [layer_w] * n_layers, [kv] * n_layers,
+                           n_stages, max_groups)
+
+
 @dataclass
 class StepResult:
     fed: list

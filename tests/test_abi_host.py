@@ -5,6 +5,7 @@ import ctypes as C
 import os
 import re
 
+import numpy as np
 import pytest
 
 from oracle.plan import stage_plan as oracle_plan
@@ -114,3 +115,54 @@ def test_error_text_is_thread_local_and_cleared(L):
     assert "n_stages" in L.last_error()
     L.stage_plan(4, 2)
     assert L.last_error() == ""
+
+
+def test_stage_solver_matches_the_brute_force_oracle(L):
+    """lps_stage_solve (exact DP) against the oracle's enumeration of every fence,
+    on seeded random instances that include zero-KV layers, head overheads, tight
+    memory and max_groups caps; infeasible instances must be refused by both."""
+    from oracle.plan import solve_stage_plan
+    rng = np.random.default_rng(20261202)
+    checked = 0
+    for _ in range(400):
+        nl = int(rng.integers(1, 10))
+        ns = int(rng.integers(1, min(nl, 4) + 1))
+        fixed = [int(v) for v in rng.integers(0, 50, nl)]
+        kv = [int(v) * int(rng.random() < 0.8) for v in rng.integers(0, 8, nl)]
+        free = [int(v) for v in rng.integers(20, 400, ns)]
+        over = [int(v) for v in rng.integers(0, 60, ns)]
+        mg = int(rng.choice([0, 3, 50, 10**6]))
+        try:
+            want = solve_stage_plan(free, over, fixed, kv, ns, mg)
+        except ValueError:
+            with pytest.raises(L.LpsError) as e:
+                L.stage_solve(free, over, fixed, kv, ns, mg)
+            assert e.value.code == L.LPS_EUNSUP
+            continue
+        assert L.stage_solve(free, over, fixed, kv, ns, mg) == (want[0], want[1]), (
+            free, over, fixed, kv, ns, mg)
+        checked += 1
+    assert checked > 150
+
+
+def test_stage_solver_refuses_bad_arguments(L):
+    with pytest.raises(L.LpsError) as e:
+        L.stage_solve([100], [0], [1, 1], [1, 1], 3, 10)          # more stages than layers
+    assert e.value.code == L.LPS_EINVAL
+    with pytest.raises(L.LpsError):
+        L.stage_solve([0, 100], [0, 0], [1, 1], [1, 1], 2, 10)    # a stage with no free bytes
+    with pytest.raises(L.LpsError):
+        L.stage_solve([100, 100], [0, 0], [1, -1], [1, 1], 2, 10)  # negative size
+
+
+def test_memory_balanced_fence_for_the_dense_slice():
+    """The dense 8B-class slice (8 layers, bf16) over four equal 288 GB devices:
+    the embedding sits on stage 0 and the head on stage 3 (equal sizes), so the
+    split is even; giving stage 0 half the memory moves layers off it."""
+    from layer_pipeline_stage_amd.runtime import memory_balanced_fence
+    geo = dict(n_layers=8, d=4096, nq=32, nkv=8, hd=128, ff=14336, vocab=32000, wdtype="bf16",
+               kvdtype="bf16")
+    fence, groups = memory_balanced_fence(n_stages=4, free_bytes=[288 << 30] * 4, **geo)
+    assert fence == [0, 2, 4, 6, 8] and groups > 0
+    fence2, groups2 = memory_balanced_fence(n_stages=4, free_bytes=[144 << 30] + [288 << 30] * 3, **geo)
+    assert fence2[1] - fence2[0] < 2 and groups2 < groups
