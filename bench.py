@@ -156,6 +156,9 @@ def main():
     ap.add_argument("--streams", choices=("single", "per-stage"), default="single",
                     help="stage streams: one shared stream (the same-stream seam; greedy "
                          "decode cannot overlap stages) or one stream per stage")
+    ap.add_argument("--mode", choices=("graph", "eager"), default="graph",
+                    help="graph: the whole step captured once and replayed, position and "
+                         "next id advanced on the device; eager: every launch from the host")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-steps", type=int, default=2)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -200,13 +203,25 @@ def main():
     # warmup
     dd.reset()
     dd.run_tokens(start_tok, W - 1)
-    # timed region: K steps (the start token + K-1 greedy steps), all on the device
+    # timed region: K steps (the start token + K-1 greedy steps), all on the device,
+    # through the host-side readback of every step's id and logits
     dd.reset()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    res = dd.run_tokens(start_tok, K - 1)
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
+    if a.mode == "graph":
+        dd.run_tokens_graph(start_tok, W - 1)
+        dd.reset()
+        clock = {}
+
+        def timer(start):
+            clock["t0" if start else "t1"] = time.perf_counter()
+
+        res = dd.run_tokens_graph(start_tok, K - 1, timer=timer)
+        dt = clock["t1"] - clock["t0"]
+    else:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        res = dd.run_tokens(start_tok, K - 1)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
     tok_s = K / dt
     rows = [cfg.prefix + 1 + i for i in range(K)]
     b = [algorithmic_bytes(cfg, n) for n in rows]
@@ -249,7 +264,10 @@ def main():
                         "SwiGLU 14336, vocab 32000, bf16 weights, f32 hidden, KV context 4096 + "
                         f"{K} steps, batch 1, {a.stages} stages (even split) on one GPU "
                         f"({a.streams} stream{'s' if a.streams == 'per-stage' else ''}), "
-                        "deferred logits readback",
+                        + ("the whole step as one replayed hipGraph, " if a.mode == "graph"
+                           else "eager launches, ")
+                        + "deferred logits readback",
+            "mode": a.mode,
             "global_batch": 1, "seq_len": cfg.prefix + K, "stages": fence,
         },
         "hbm_bytes_per_token": int(bytes_tok),

@@ -121,6 +121,8 @@ typedef struct lps_layer_desc {
   const void* w_d;   const uint8_t* s_d;     /* (dev) [d, ff] */
   void* k_cache;     /* (dev) [nkv, ctx_max, hd] kvdtype, owned by this layer's stage */
   void* v_cache;     /* (dev) [nkv, ctx_max, hd] kvdtype */
+  const float* rope_cs;  /* (dev, optional) [ctx_max, hd/2, 2] f32: cos, sin of pos * theta_i
+                          * (lps_rope_table); required by the device-position entry points */
 } lps_layer_desc;
 
 /* Scratch bytes lps_layer_forward needs for this layer (0 on invalid desc). */
@@ -150,6 +152,69 @@ size_t lps_model_scratch_bytes(const lps_model* m);
  * stage_walks counter.  (ninfer pipeline stages, How it works: run_staged.) */
 int lps_stage_forward(const lps_model* m, const int32_t* fence, int32_t n_stages, int32_t stage,
                       float* x, int32_t pos, void* scratch, size_t scratch_bytes, void* stream);
+
+/* ---- device-position walk, step state and whole-pass graphs ----------------
+ * ninfer pipeline stages, How it works (StageLink): the small control values
+ * the layers read (the position among them) travel as device data, and decode
+ * captures the whole staged pass into one graph.  A replayed step can only
+ * differ from the last through device memory, so these entry points read the
+ * position from the device and advance it there.
+ *
+ * lps_stage_forward_dpos: lps_stage_forward with the position read on the
+ * device from *pos_dev (dev int32, 4-byte aligned) by every kernel of the
+ * walk.  Each walked layer needs its rope_cs table (lps_rope_table, uploaded
+ * by the caller).  The kernels clamp the position into [0, ctx_max - 1], so a
+ * stale value cannot address memory outside the caches; keeping it in range is
+ * the caller's (lps_step_advance stops it at pos_limit).  Attention is launched
+ * over all ctx_max rows' chunks and the chunks past the position exit at once. */
+int lps_stage_forward_dpos(const lps_model* m, const int32_t* fence, int32_t n_stages,
+                           int32_t stage, float* x, const int32_t* pos_dev, void* scratch,
+                           size_t scratch_bytes, void* stream);
+
+/* host_out (host) [n_pos, hd/2, 2] f32 = cos, sin of p * base^(-2i/hd) for
+ * p < n_pos, i < hd/2: formed in double and rounded once, the same values the
+ * by-value QKV launch uses at position p (so both walks agree bit for bit).
+ * Errors: LPS_EINVAL for a null output, odd or non-positive hd, n_pos < 1 or a
+ * non-positive base.  Host only. */
+int lps_rope_table(int32_t hd, float rope_base, int32_t n_pos, float* host_out);
+
+/* Advances a decode step's device state, on `stream`, after the head wrote
+ * this step's argmax.  state (dev int32 [3]): [0] position, [1] step, [2] flags
+ * (bit 0: the position reached pos_limit - 1 and stayed there).  With s =
+ * state[1]:
+ *  - tok_hist[s] = *argmax when s < hist_cap (tok_hist dev, may be NULL when
+ *    hist_cap is 0);
+ *  - logits_hist[s * vocab ...] = logits[0 .. vocab) when logits_hist is not
+ *    NULL and s < hist_cap (the copy precedes the advance in stream order);
+ *  - *tok_cur = feed[s + 1] while s + 1 < n_feed (teacher-forced ids, dev),
+ *    else *argmax: the next step's input token (read by lps_embed);
+ *  - state[0] += 1 unless that reaches pos_limit (then flag bit 0); state[1] += 1.
+ * Errors: LPS_EINVAL for null required pointers, pos_limit < 1 or
+ * inconsistent feed / history arguments. */
+int lps_step_advance(int32_t* state, int32_t pos_limit, const int32_t* argmax, int32_t* tok_cur,
+                     const int32_t* feed, int32_t n_feed, int32_t* tok_hist, int32_t hist_cap,
+                     const float* logits, int32_t vocab, float* logits_hist, void* stream);
+
+/* Whole-pass graph capture.  lps_graph_begin starts a relaxed-mode capture on
+ * `stream` (not the null stream; LPS_ESTATE while a kernel timer runs or the
+ * stream already captures).  Everything then enqueued on it, and on every
+ * stream that joins through an event (a boundary receive on another stream
+ * joins it), is recorded rather than run.  lps_graph_end joins each stream of
+ * `join` (host array of n_join streams; streams that never joined are skipped)
+ * back into `stream`, ends the capture, and instantiates the graph into *out.
+ * It always ends the capture, also when a captured call failed (it then
+ * returns that failure's status and *out = NULL).
+ * Boundaries in a capture: a wait targets only a record made in the same
+ * context (eager, or that capture).  Ordering eager work against a graph
+ * launch, in either direction, is the caller's (e.g. a stream or device
+ * synchronize between them).
+ * lps_graph_launch enqueues one replay on `stream`; replays on one stream run
+ * one after the other.  lps_graph_destroy frees the graph (NULL is a no-op). */
+typedef struct lps_graph lps_graph;
+int lps_graph_begin(void* stream);
+int lps_graph_end(void* stream, void* const* join, int32_t n_join, lps_graph** out);
+int lps_graph_launch(lps_graph* g, void* stream);
+int lps_graph_destroy(lps_graph* g);
 
 /* ---- A2: embedding gather ------------------------------------------------
  * x[0..d) = E[*tok] widened to f32; tok (dev int32) is read on the device so a

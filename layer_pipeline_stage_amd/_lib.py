@@ -36,7 +36,7 @@ class LayerDesc(C.Structure):
         ("g_ffn", C.c_void_p),
         ("w_gu", C.c_void_p), ("s_gu", C.c_void_p),
         ("w_d", C.c_void_p), ("s_d", C.c_void_p),
-        ("k_cache", C.c_void_p), ("v_cache", C.c_void_p),
+        ("k_cache", C.c_void_p), ("v_cache", C.c_void_p), ("rope_cs", C.c_void_p),
     ]
 
 
@@ -79,6 +79,13 @@ SIGS = {
     "lps_model_destroy": (C.c_int, [P], True),
     "lps_model_scratch_bytes": (SZ, [P], False),
     "lps_stage_forward": (C.c_int, [P, PI32, I32, I32, P, I32, P, SZ, P], True),
+    "lps_stage_forward_dpos": (C.c_int, [P, PI32, I32, I32, P, P, P, SZ, P], True),
+    "lps_rope_table": (C.c_int, [I32, F32, I32, P], True),
+    "lps_step_advance": (C.c_int, [P, I32, P, P, P, I32, P, I32, P, I32, P, P], True),
+    "lps_graph_begin": (C.c_int, [P], True),
+    "lps_graph_end": (C.c_int, [P, PP, I32, PP], True),
+    "lps_graph_launch": (C.c_int, [P, P], True),
+    "lps_graph_destroy": (C.c_int, [P], True),
     "lps_embed": (C.c_int, [P, I32, I32, I32, P, P, P], True),
     "lps_head_scratch_bytes": (SZ, [C.POINTER(HeadDesc)], False),
     "lps_head_forward": (C.c_int, [C.POINTER(HeadDesc), P, P, P, P, SZ, P], True),
@@ -179,6 +186,14 @@ def timer_stop(cap=1 << 16):
     n = C.c_int32()
     lps_timer_stop(buf, cap, C.byref(n))  # noqa: F821
     return [buf[i] for i in range(n.value)]
+
+
+def rope_table(hd, base, n_pos):
+    """lps_rope_table -> numpy f32 [n_pos, hd/2, 2] (host only)."""
+    import numpy as np
+    out = np.zeros((n_pos, hd // 2, 2), dtype=np.float32)
+    lps_rope_table(hd, base, n_pos, out.ctypes.data)  # noqa: F821
+    return out
 
 
 def stage_solve(free, overhead, fixed, kv, n_stages, max_groups):

@@ -36,9 +36,17 @@ struct AttnP {
   float* pm;   // [nkv, nch, G]
   float* pl;   // [nkv, nch, G]
   float* po;   // [nkv, nch, G, HD]
-  int G, ctx_max, n, nch;
+  int G, ctx_max, n, nch;   // rows and chunks (with pos_dev: read on the device)
+  int nstride;              // chunks per kv head in the partial arrays
+  const int32_t* pos_dev;   // device position: rows 0 .. *pos_dev
   float scale;
 };
+
+// rows n and chunks nch of this launch
+__device__ __forceinline__ void attn_rows(const AttnP& p, int& n, int& nch) {
+  n = p.pos_dev ? min(max(*p.pos_dev, 0), p.ctx_max - 1) + 1 : p.n;   // clamped like the QKV store
+  nch = p.pos_dev ? (n + ATT_CH - 1) / ATT_CH : p.nch;
+}
 
 template <int HD, int KVT>
 struct AttnCfg {
@@ -86,6 +94,9 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attn(AttnP p) {
   extern __shared__ float red[];            // [RPP][G][HD]
 
   const int chunk = blockIdx.x, g = blockIdx.y;
+  int n_rows, nch;
+  attn_rows(p, n_rows, nch);
+  if (chunk >= nch) return;   // a device-position launch covers ctx_max rows
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wv = tid / WAVE;
   const int li = tid % LPR, rr = tid / LPR;
   const int row0 = chunk * ATT_CH;
@@ -95,7 +106,7 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attn(AttnP p) {
 #pragma unroll
   for (int ps = 0; ps < NP; ++ps) {
     const int j = row0 + ps * RPP + rr;
-    if (j < p.n) {
+    if (j < n_rows) {
       const long long off = (head_base + (long long)j * HD + li * E16) * ESZ;
       kraw[ps] = ld16(static_cast<const char*>(p.kc) + off);
       vraw[ps] = ld16(static_cast<const char*>(p.vc) + off);
@@ -135,7 +146,7 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attn(AttnP p) {
     for (int h = 0; h < G; ++h) s[h] = group_sum<LPR>(s[h]);
     if (li == 0) {
 #pragma unroll
-      for (int h = 0; h < G; ++h) sc[h][jl] = (j < p.n) ? s[h] * p.scale : -INFINITY;
+      for (int h = 0; h < G; ++h) sc[h][jl] = (j < n_rows) ? s[h] * p.scale : -INFINITY;
     }
   }
   __syncthreads();
@@ -158,7 +169,7 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attn(AttnP p) {
     }
     l = wave_sum(l);
     if (lane == 0) {
-      const long long pi = ((long long)g * p.nch + chunk) * G + h;
+      const long long pi = ((long long)g * p.nstride + chunk) * G + h;
       p.pm[pi] = m;
       p.pl[pi] = l;
     }
@@ -189,7 +200,7 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attn(AttnP p) {
       *reinterpret_cast<f32x4*>(red + (rr * G + h) * HD + li * E16 + e) =
           f32x4{acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]};
   __syncthreads();
-  const long long ob = ((long long)g * p.nch + chunk) * G * HD;
+  const long long ob = ((long long)g * p.nstride + chunk) * G * HD;
   for (int idx = tid; idx < G * (HD / 2); idx += ATT_THREADS) {
     const int h = idx / (HD / 2), e2 = idx - h * (HD / 2);
     f32x2 o = *reinterpret_cast<const f32x2*>(red + h * HD + 2 * e2);
@@ -223,18 +234,20 @@ __global__ __launch_bounds__(MERGE_THREADS) void k_attn_merge(AttnP p) {
   const int t = threadIdx.x, e2 = t % TPH, part = t / TPH;
   __shared__ float sM[P], sL[P];
   __shared__ f32x2 sO[P][TPH];
-  const long long base = (long long)g * p.nch;
+  int n_rows, nch;
+  attn_rows(p, n_rows, nch);
+  const long long base = (long long)g * p.nstride;
   const long long step = (long long)p.G * HD;
   const float* po = p.po + (base * p.G + h) * HD + 2 * e2;
   float M = -INFINITY, L = 0.f;
   f32x2 O = {0.f, 0.f};
-  for (int c0 = part; c0 < p.nch; c0 += MERGE_B * P) {
+  for (int c0 = part; c0 < nch; c0 += MERGE_B * P) {
     float mv[MERGE_B], lv[MERGE_B];
     f32x2 ov[MERGE_B];
 #pragma unroll
     for (int k = 0; k < MERGE_B; ++k) {
       const int c = c0 + k * P;
-      if (c < p.nch) {
+      if (c < nch) {
         const long long pi = (base + c) * p.G + h;
         mv[k] = p.pm[pi];
         lv[k] = p.pl[pi];
@@ -299,8 +312,7 @@ static int go_g(const AttnP& p, int nkv, hipStream_t st, hipEvent_t start) {
   const size_t lds = size_t(AttnCfg<HD, KVT>::RPP) * G * HD * sizeof(float);
   int rc = ensure_lds((const void*)k_attn<HD, KVT, G>, lds);
   if (rc) return rc;
-  hipExtLaunchKernelGGL((k_attn<HD, KVT, G>), dim3(p.nch, nkv), dim3(ATT_THREADS), lds, st, start,
-                        nullptr, 0, p);
+  LPS_LAUNCH((k_attn<HD, KVT, G>), dim3(p.nch, nkv), dim3(ATT_THREADS), lds, st, start, nullptr, p);
   return LPS_OK;
 }
 
@@ -316,14 +328,13 @@ static int go(const AttnP& p, int nkv, hipStream_t st, Stamp sp) {
     default: return fail(LPS_EUNSUP, "attention: %d q heads per kv head not built (1, 2, 4, 6, 8)", p.G);
   }
   if (rc) return rc;
-  hipExtLaunchKernelGGL((k_attn_merge<HD>), dim3(nkv * p.G), dim3(MERGE_THREADS), 0, st, nullptr,
-                        sp.stop, 0, p);
+  LPS_LAUNCH((k_attn_merge<HD>), dim3(nkv * p.G), dim3(MERGE_THREADS), 0, st, nullptr, sp.stop, p);
   return LPS_OK;
 }
 
 int launch_attention(int nq, int nkv, int hd, int kvdtype, const void* kc, const void* vc,
                      int ctx_max, int n_rows, const float* q, float* o, void* scratch,
-                     hipStream_t st, Stamp sp) {
+                     hipStream_t st, Stamp sp, const int32_t* pos_dev) {
   AttnP p{};
   p.kc = kc;
   p.vc = vc;
@@ -331,8 +342,10 @@ int launch_attention(int nq, int nkv, int hd, int kvdtype, const void* kc, const
   p.o = o;
   p.G = nq / nkv;
   p.ctx_max = ctx_max;
-  p.n = n_rows;
-  p.nch = nchunks(n_rows);
+  p.pos_dev = pos_dev;
+  p.n = pos_dev ? ctx_max : n_rows;
+  p.nch = nchunks(p.n);            // the grid; blocks past the device row count exit
+  p.nstride = pos_dev ? nchunks(ctx_max) : p.nch;
   p.scale = 1.0f / sqrtf(float(hd));
   const size_t nch_max = nchunks(ctx_max);
   char* s = static_cast<char*>(scratch);

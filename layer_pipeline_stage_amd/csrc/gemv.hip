@@ -50,6 +50,9 @@ struct GemvP {
   void* vc;
   // cos / sin of pos * base^(-2i/hd) for i < hd/2, formed on the host in double
   float rope[2 * 128];
+  // device position: pos read from pos_dev, cos / sin from the table rope_cs[pos]
+  const int32_t* pos_dev;
+  const float* rope_cs;
   // LM-head epilogue: every wave's (max, lowest index of it) over its rows
   float* pval;
   int* pidx;
@@ -138,9 +141,19 @@ __device__ __forceinline__ void epilogue(const GemvP& p, int u, int r0, int r1, 
   } else {  // QKV: rotate q and k heads at pos, store q, append k and v to the caches
     const int half = p.hd >> 1;
     const int hh = u / half, i = u - hh * half;
+    // a device position is clamped into the cache, so a stale one cannot write outside it
+    const int pos = p.pos_dev ? min(max(*p.pos_dev, 0), p.ctx_max - 1) : p.pos;
     float o0 = a0, o1 = a1;
     if (hh < p.nq + p.nkv) {
-      const float cs = p.rope[2 * i], sn = p.rope[2 * i + 1];
+      float cs, sn;
+      if (p.pos_dev) {
+        const f32x2 t = *reinterpret_cast<const f32x2*>(p.rope_cs + 2 * ((long long)pos * half + i));
+        cs = t.x;
+        sn = t.y;
+      } else {
+        cs = p.rope[2 * i];
+        sn = p.rope[2 * i + 1];
+      }
       o0 = a0 * cs - a1 * sn;
       o1 = a0 * sn + a1 * cs;
     }
@@ -150,7 +163,7 @@ __device__ __forceinline__ void epilogue(const GemvP& p, int u, int r0, int r1, 
     } else {
       const bool is_k = hh < p.nq + p.nkv;
       const int gkv = is_k ? hh - p.nq : hh - p.nq - p.nkv;
-      const long long off = ((long long)gkv * p.ctx_max + p.pos) * p.hd + i;
+      const long long off = ((long long)gkv * p.ctx_max + pos) * p.hd + i;
       void* base = is_k ? p.kc : p.vc;
       store_kv(base, p.kvdtype, off, o0);
       store_kv(base, p.kvdtype, off + half, o1);
@@ -396,11 +409,11 @@ static int launch_t(const GemvP& p, hipStream_t st, Stamp sp, int* waves) {
     int rc_ = ensure_lds(fn_, lds);                                                              \
     if (rc_) return rc_;                                                                         \
     if (db)                                                                                      \
-      hipExtLaunchKernelGGL((k_gemv_buf<WT, EPI, UU, NORM, NTV, true>), dim3(grid), dim3(NTV),   \
-                            lds, st, sp.start, sp.stop, 0, p);                                   \
+      LPS_LAUNCH((k_gemv_buf<WT, EPI, UU, NORM, NTV, true>), dim3(grid), dim3(NTV), lds, st,     \
+                 sp.start, sp.stop, p);                                                          \
     else                                                                                         \
-      hipExtLaunchKernelGGL((k_gemv_buf<WT, EPI, UU, NORM, NTV, false>), dim3(grid), dim3(NTV),  \
-                            lds, st, sp.start, sp.stop, 0, p);                                   \
+      LPS_LAUNCH((k_gemv_buf<WT, EPI, UU, NORM, NTV, false>), dim3(grid), dim3(NTV), lds, st,    \
+                 sp.start, sp.stop, p);                                                          \
   } while (0)
   if constexpr (WT == LPS_MXFP4) {
     if (per_lane <= 3) LPS_GOB(3, LPS_MX_NT, LPS_MX_MAXB);
@@ -495,6 +508,15 @@ int launch_moe_down(const void* w_e, const void* w_s, const int32_t* eidx, int E
   return launch_wt<EPI_MOEDN, false>(LPS_BF16, p, st, Stamp{});
 }
 
+// cos, sin of pos * theta_i, theta_i = base^(-2i / hd), formed in double and
+// rounded once to f32 (the angle reaches ~1e4 rad at long contexts)
+void rope_cos_sin(float base, int hd, int pos, int i, float* cs) {
+  const double theta = std::pow(double(base), -2.0 * double(i) / double(hd));
+  const double ang = double(pos) * theta;
+  cs[0] = float(std::cos(ang));
+  cs[1] = float(std::sin(ang));
+}
+
 int launch_qkv(const QkvArgs& a, hipStream_t st, Stamp sp) {
   const lps_layer_desc* L = a.L;
   GemvP p{};
@@ -514,13 +536,12 @@ int launch_qkv(const QkvArgs& a, hipStream_t st, Stamp sp) {
   p.ctx_max = L->ctx_max;
   p.kvdtype = L->kvdtype;
   // the rotation angle pos * theta_i reaches ~1e4 rad: form it and its cos / sin
-  // in double, once per launch, and hand the f32 values to every block
-  for (int i = 0; i < L->hd / 2; ++i) {
-    const double theta = std::pow(double(L->rope_base), -2.0 * double(i) / double(L->hd));
-    const double ang = double(a.pos) * theta;
-    p.rope[2 * i] = float(std::cos(ang));
-    p.rope[2 * i + 1] = float(std::sin(ang));
-  }
+  // in double, once per launch, and hand the f32 values to every block (with a
+  // device position, the same values come from the table rope_cs)
+  p.pos_dev = a.pos_dev;
+  p.rope_cs = L->rope_cs;
+  for (int i = 0; a.pos_dev == nullptr && i < L->hd / 2; ++i)
+    rope_cos_sin(L->rope_base, L->hd, a.pos, i, &p.rope[2 * i]);
   p.kc = L->k_cache;
   p.vc = L->v_cache;
   set_rows(p, L->wdtype, L->d);
@@ -554,8 +575,7 @@ int launch_head(const lps_head_desc* h, const float* x, float* logits, int32_t* 
   int waves = 0;
   int rc = launch_wt<EPI_LOGITS, true>(h->wdtype, p, st, Stamp{sp.start, nullptr}, &waves);
   if (rc) return rc;
-  hipExtLaunchKernelGGL(k_argmax, dim3(1), dim3(1024), 0, st, nullptr, sp.stop, 0, p.pval, p.pidx,
-                        waves, tok);
+  LPS_LAUNCH(k_argmax, dim3(1), dim3(1024), 0, st, nullptr, sp.stop, p.pval, p.pidx, waves, tok);
   LPS_HIP(hipGetLastError());
   return LPS_OK;
 }

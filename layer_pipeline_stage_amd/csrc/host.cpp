@@ -67,6 +67,17 @@ Stamp timer_take(int kind) {
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// Id of the stream capture `st` takes part in, 0 when it is not capturing.
+static int capture_of(hipStream_t st, unsigned long long* id) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  unsigned long long cid = 0;
+  LPS_HIP(hipStreamGetCaptureInfo(st, &cs, &cid));
+  LPS_REQUIRE(cs != hipStreamCaptureStatusInvalidated, LPS_ESTATE,
+              "stream capture was invalidated by an earlier call");
+  *id = cs == hipStreamCaptureStatusActive ? cid : 0;
+  return LPS_OK;
+}
+
 static int chunk_of(int wdtype) { return wdtype == LPS_F32 ? 4 : wdtype == LPS_BF16 ? 8 : 32; }
 
 // q heads per kv head that the attention kernel is instantiated for
@@ -119,18 +130,20 @@ static LayerScratch layer_scratch(const lps_layer_desc* L) {
   return s;
 }
 
-static int layer_forward(const lps_layer_desc* L, float* x, int pos, void* scratch, hipStream_t st) {
+// pos_dev set: the position is read on the device (pos unused)
+static int layer_forward(const lps_layer_desc* L, float* x, int pos, void* scratch, hipStream_t st,
+                         const int32_t* pos_dev = nullptr) {
   const LayerScratch s = layer_scratch(L);
   char* sc = static_cast<char*>(scratch);
   float* q = reinterpret_cast<float*>(sc + s.q);
   float* o = reinterpret_cast<float*>(sc + s.o);
   float* m = reinterpret_cast<float*>(sc + s.m);
   void* at = sc + s.attn;
-  QkvArgs qa{L, x, pos, q};
+  QkvArgs qa{L, x, pos, q, pos_dev};
   int rc = launch_qkv(qa, st, timer_take(LPS_KIND_QKV));
   if (rc) return rc;
   rc = launch_attention(L->nq, L->nkv, L->hd, L->kvdtype, L->k_cache, L->v_cache, L->ctx_max,
-                        pos + 1, q, o, at, st, timer_take(LPS_KIND_ATTN));
+                        pos + 1, q, o, at, st, timer_take(LPS_KIND_ATTN), pos_dev);
   if (rc) return rc;
   rc = launch_gemv(L->wdtype, L->w_o, L->s_o, L->d, L->nq * L->hd, o, nullptr, 0.f, x,
                    LPS_EPI_ADD, st, timer_take(LPS_KIND_OPROJ));
@@ -172,8 +185,16 @@ struct lps_boundary {
   bool rx_recorded[2];
   hipStream_t tx_stream[2];   // stream of the slot's last send
   hipStream_t rx_stream[2];   // stream of the slot's last receive
+  // capture that made the event's last record (0: an eager record); a wait
+  // only ever targets a record made in the waiting stream's own context
+  unsigned long long tx_cap[2];   // context of the slot's last send
+  unsigned long long rx_cap[2];
   int64_t next_send;
   int64_t next_recv;
+};
+
+struct lps_graph {
+  hipGraphExec_t exec;
 };
 
 struct lps_pending {
@@ -443,6 +464,144 @@ int lps_stage_forward(const lps_model* m, const int32_t* fence, int32_t n_stages
   return LPS_OK;
 }
 
+int lps_stage_forward_dpos(const lps_model* m, const int32_t* fence, int32_t n_stages,
+                           int32_t stage, float* x, const int32_t* pos_dev, void* scratch,
+                           size_t scratch_bytes, void* stream) {
+  LPS_REQUIRE(m, LPS_EINVAL, "lps_stage_forward_dpos: null model");
+  int rc = check_fence(fence, n_stages, int32_t(m->layers.size()), "lps_stage_forward_dpos");
+  if (rc) return rc;
+  LPS_REQUIRE(stage >= 0 && stage < n_stages, LPS_ERANGE,
+              "lps_stage_forward_dpos: stage %d outside [0, %d)", stage, n_stages);
+  LPS_REQUIRE(x && scratch && pos_dev, LPS_EINVAL, "lps_stage_forward_dpos: null x, scratch or pos");
+  LPS_REQUIRE(aligned16(x) && aligned16(scratch) && (reinterpret_cast<uintptr_t>(pos_dev) & 3) == 0,
+              LPS_EINVAL, "lps_stage_forward_dpos: x and scratch must be 16-byte aligned, pos 4");
+  LPS_REQUIRE(scratch_bytes >= m->scratch, LPS_EINVAL,
+              "lps_stage_forward_dpos: scratch %zu < %zu needed", scratch_bytes, m->scratch);
+  for (int l = fence[stage]; l < fence[stage + 1]; ++l) {
+    const float* t = m->layers[l].rope_cs;
+    LPS_REQUIRE(t && (reinterpret_cast<uintptr_t>(t) & 7) == 0, LPS_EINVAL,
+                "lps_stage_forward_dpos: layer %d needs an 8-byte aligned rope_cs table", l);
+  }
+  hipStream_t st = as_stream(stream);
+  for (int l = fence[stage]; l < fence[stage + 1]; ++l) {
+    rc = layer_forward(&m->layers[l], x, 0, scratch, st, pos_dev);
+    if (rc) return rc;
+  }
+  count_stage_walk();
+  return LPS_OK;
+}
+
+int lps_rope_table(int32_t hd, float rope_base, int32_t n_pos, float* host_out) {
+  LPS_REQUIRE(host_out, LPS_EINVAL, "lps_rope_table: null output");
+  LPS_REQUIRE(hd > 0 && hd % 2 == 0, LPS_EINVAL, "lps_rope_table: head dim %d (positive, even)", hd);
+  LPS_REQUIRE(n_pos >= 1, LPS_EINVAL, "lps_rope_table: n_pos %d < 1", n_pos);
+  LPS_REQUIRE(rope_base > 0.f, LPS_EINVAL, "lps_rope_table: base %g must be positive", rope_base);
+  const int half = hd / 2;
+  for (int p = 0; p < n_pos; ++p)
+    for (int i = 0; i < half; ++i) rope_cos_sin(rope_base, hd, p, i, host_out + 2 * (size_t(p) * half + i));
+  return LPS_OK;
+}
+
+int lps_step_advance(int32_t* state, int32_t pos_limit, const int32_t* argmax, int32_t* tok_cur,
+                     const int32_t* feed, int32_t n_feed, int32_t* tok_hist, int32_t hist_cap,
+                     const float* logits, int32_t vocab, float* logits_hist, void* stream) {
+  LPS_REQUIRE(state && argmax && tok_cur, LPS_EINVAL, "lps_step_advance: null state, argmax or tok");
+  LPS_REQUIRE(pos_limit >= 1, LPS_EINVAL, "lps_step_advance: pos_limit %d < 1", pos_limit);
+  LPS_REQUIRE(n_feed >= 0 && (n_feed == 0 || feed), LPS_EINVAL,
+              "lps_step_advance: %d fed ids need a feed array", n_feed);
+  LPS_REQUIRE(hist_cap >= 0 && (hist_cap == 0 || tok_hist), LPS_EINVAL,
+              "lps_step_advance: a history of %d steps needs tok_hist", hist_cap);
+  LPS_REQUIRE(!logits_hist || (logits && vocab > 0), LPS_EINVAL,
+              "lps_step_advance: a logits history needs logits and vocab > 0");
+  return launch_step_advance(state, pos_limit, argmax, tok_cur, feed, n_feed, tok_hist, hist_cap,
+                             logits, vocab, logits_hist, as_stream(stream));
+}
+
+// ---- whole-pass graphs --------------------------------------------------------------------
+int lps_graph_begin(void* stream) {
+  LPS_REQUIRE(g_timer.kind.load() == 0, LPS_ESTATE,
+              "lps_graph_begin: a kernel timer is running (timed launches are not captured)");
+  hipStream_t st = as_stream(stream);
+  LPS_REQUIRE(st != nullptr, LPS_EINVAL, "lps_graph_begin: the null stream cannot be captured");
+  unsigned long long cid = 0;
+  int rc = capture_of(st, &cid);
+  if (rc) return rc;
+  LPS_REQUIRE(cid == 0, LPS_ESTATE, "lps_graph_begin: the stream is already capturing");
+  // relaxed: the walk may call hipFuncSetAttribute the first time a shape runs
+  LPS_HIP(hipStreamBeginCapture(st, hipStreamCaptureModeRelaxed));
+  return LPS_OK;
+}
+
+int lps_graph_end(void* stream, void* const* join, int32_t n_join, lps_graph** out) {
+  LPS_REQUIRE(out, LPS_EINVAL, "lps_graph_end: null out");
+  *out = nullptr;
+  LPS_REQUIRE(n_join >= 0 && (n_join == 0 || join), LPS_EINVAL, "lps_graph_end: bad join list");
+  hipStream_t st = as_stream(stream);
+  unsigned long long cid = 0;
+  int rc = capture_of(st, &cid);
+  hipError_t jerr = hipSuccess;
+  std::vector<hipEvent_t> evs;
+  if (!rc && cid == 0) rc = fail(LPS_ESTATE, "lps_graph_end: the stream is not capturing");
+  // join every forked stream of this capture back into the origin stream
+  for (int i = 0; !rc && jerr == hipSuccess && i < n_join; ++i) {
+    hipStream_t j = as_stream(join[i]);
+    if (j == st || j == nullptr) continue;
+    unsigned long long jc = 0;
+    rc = capture_of(j, &jc);
+    if (rc || jc == 0) continue;   // never forked into the capture: nothing to join
+    if (jc != cid) {
+      rc = fail(LPS_ESTATE, "lps_graph_end: join stream %d is in another capture", i);
+      break;
+    }
+    hipEvent_t e;
+    jerr = hipEventCreateWithFlags(&e, hipEventDisableTiming);
+    if (jerr != hipSuccess) break;
+    evs.push_back(e);
+    jerr = hipEventRecord(e, j);
+    if (jerr == hipSuccess) jerr = hipStreamWaitEvent(st, e, 0);
+  }
+  // the capture always ends here, also after a failure, so the stream is usable again
+  hipGraph_t graph = nullptr;
+  hipError_t eerr = cid ? hipStreamEndCapture(st, &graph) : hipSuccess;
+  for (auto e : evs) (void)hipEventDestroy(e);
+  if (!rc && jerr != hipSuccess) rc = fail(LPS_EHIP, "lps_graph_end: join: %s", hipGetErrorString(jerr));
+  if (!rc && eerr != hipSuccess)
+    rc = fail(LPS_EHIP, "lps_graph_end: hipStreamEndCapture: %s", hipGetErrorString(eerr));
+  if (!rc && graph == nullptr) rc = fail(LPS_EHIP, "lps_graph_end: the capture produced no graph");
+  hipGraphExec_t exec = nullptr;
+  if (!rc) {
+    hipError_t ierr = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    if (ierr != hipSuccess) rc = fail(LPS_EHIP, "lps_graph_end: hipGraphInstantiate: %s", hipGetErrorString(ierr));
+  }
+  if (graph) (void)hipGraphDestroy(graph);
+  if (rc) {
+    (void)hipGetLastError();
+    return rc;
+  }
+  lps_graph* g = new (std::nothrow) lps_graph;
+  if (!g) {
+    (void)hipGraphExecDestroy(exec);
+    return fail(LPS_ENOMEM, "lps_graph_end: out of host memory");
+  }
+  g->exec = exec;
+  *out = g;
+  return LPS_OK;
+}
+
+int lps_graph_launch(lps_graph* g, void* stream) {
+  LPS_REQUIRE(g, LPS_EINVAL, "lps_graph_launch: null graph");
+  LPS_HIP(hipGraphLaunch(g->exec, as_stream(stream)));
+  return LPS_OK;
+}
+
+int lps_graph_destroy(lps_graph* g) {
+  if (!g) return LPS_OK;
+  hipError_t e = hipGraphExecDestroy(g->exec);
+  delete g;
+  if (e != hipSuccess) return fail(LPS_EHIP, "lps_graph_destroy: %s", hipGetErrorString(e));
+  return LPS_OK;
+}
+
 // ---- step-level entry points -----------------------------------------------------------
 int lps_gemv(int32_t wdtype, const void* w, const uint8_t* s, int32_t N, int32_t K, const float* x,
              const float* norm_g, float eps, float* y, int32_t mode, void* stream) {
@@ -582,6 +741,7 @@ int lps_boundary_create(int32_t n_elems, float* slot0, float* slot1, lps_boundar
   for (int k = 0; k < 2; ++k) {
     b->tx_recorded[k] = b->rx_recorded[k] = false;
     b->tx_stream[k] = b->rx_stream[k] = nullptr;
+    b->tx_cap[k] = b->rx_cap[k] = 0;
     hipError_t e1 = hipEventCreateWithFlags(&b->ev_tx[k], hipEventDisableTiming);
     hipError_t e2 = hipEventCreateWithFlags(&b->ev_rx[k], hipEventDisableTiming);
     if (e1 != hipSuccess || e2 != hipSuccess) {
@@ -604,15 +764,22 @@ int lps_boundary_send(lps_boundary* b, const float* x, int64_t step, void* produ
               (long long)step, int(step & 1), (long long)(step - 2));
   const int k = int(step & 1);
   hipStream_t st = as_stream(producer);
-  // a wait on the own stream is implied by stream order (the same-stream seam)
-  if (b->rx_recorded[k] && b->rx_stream[k] != st) LPS_HIP(hipStreamWaitEvent(st, b->ev_rx[k], 0));
-  int rc = launch_copy_f32(x, b->slot[k], b->n, st);
+  unsigned long long cid = 0;
+  int rc = capture_of(st, &cid);
+  if (rc) return rc;
+  // a wait on the own stream is implied by stream order (the same-stream seam);
+  // a receive recorded in another context (eager vs a capture) is not waited:
+  // ordering eager work against a graph launch is the caller's
+  if (b->rx_recorded[k] && b->rx_stream[k] != st && b->rx_cap[k] == cid)
+    LPS_HIP(hipStreamWaitEvent(st, b->ev_rx[k], 0));
+  rc = launch_copy_f32(x, b->slot[k], b->n, st);
   if (rc) return rc;
   // ev_tx is recorded by the receive, on this stream, when the consumer turns out to
   // be another stream: a marker after all work enqueued here so far, which covers
   // the copy above (nothing in between can un-write the slot)
   b->tx_recorded[k] = false;
   b->tx_stream[k] = st;
+  b->tx_cap[k] = cid;
   b->next_send = step + 1;
   count_send();
   return LPS_OK;
@@ -628,12 +795,22 @@ int lps_boundary_recv(lps_boundary* b, float* x, int64_t step, void* consumer) {
               (long long)step);
   const int k = int(step & 1);
   hipStream_t st = as_stream(consumer);
+  unsigned long long ccid = 0, tcid = 0;
+  int rc = capture_of(st, &ccid);
+  if (!rc) rc = capture_of(b->tx_stream[k], &tcid);
+  if (rc) return rc;
+  // send and receive of one step belong to one context: both eager, or both in
+  // one capture (a consumer stream that is not capturing yet joins the
+  // producer's capture through the wait below)
+  LPS_REQUIRE(tcid == b->tx_cap[k] && (ccid == 0 || ccid == tcid), LPS_ESTATE,
+              "lps_boundary_recv: step %lld was sent in another capture context than it is "
+              "received in", (long long)step);
   if (b->tx_stream[k] != st) {
     LPS_HIP(hipEventRecord(b->ev_tx[k], b->tx_stream[k]));
     b->tx_recorded[k] = true;
     LPS_HIP(hipStreamWaitEvent(st, b->ev_tx[k], 0));
   }
-  int rc = launch_copy_f32(b->slot[k], x, b->n, st);
+  rc = launch_copy_f32(b->slot[k], x, b->n, st);
   if (rc) return rc;
   // the producer's next use of slot k waits this event only from another stream
   if (b->tx_stream[k] != st) {
@@ -642,6 +819,7 @@ int lps_boundary_recv(lps_boundary* b, float* x, int64_t step, void* consumer) {
   } else {
     b->rx_recorded[k] = false;
   }
+  b->rx_cap[k] = tcid;   // the consumer now records in the producer's context
   b->rx_stream[k] = st;
   b->next_recv = step + 1;
   count_recv();

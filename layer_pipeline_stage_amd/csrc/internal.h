@@ -50,6 +50,16 @@ struct Stamp {
 };
 Stamp timer_take(int kind);
 
+// A launch that stamps a timer's events when it carries any, and is a plain
+// launch otherwise (the form a stream capture records).
+#define LPS_LAUNCH(K, GRID, BLOCK, LDS, ST, E0, E1, ...)                        \
+  do {                                                                          \
+    if ((E0) != nullptr || (E1) != nullptr)                                     \
+      hipExtLaunchKernelGGL(K, GRID, BLOCK, LDS, ST, E0, E1, 0, __VA_ARGS__);   \
+    else                                                                        \
+      hipLaunchKernelGGL(K, GRID, BLOCK, LDS, ST, __VA_ARGS__);                 \
+  } while (0)
+
 // ---- scratch carving ------------------------------------------------------------
 inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
@@ -59,10 +69,13 @@ struct QkvArgs {
   const float* x;
   int pos;
   float* q;
+  const int32_t* pos_dev = nullptr;   // if set: the position is read here (RoPE from L->rope_cs)
 };
 int launch_gemv(int wdtype, const void* w, const uint8_t* s, int N, int K, const float* x,
                 const float* g, float eps, float* y, int mode, hipStream_t st, Stamp sp = {});
 int launch_qkv(const QkvArgs& a, hipStream_t st, Stamp sp = {});
+// cs[0], cs[1] = f32 cos, sin of pos * base^(-2i / hd) (the QKV launch's own values)
+void rope_cos_sin(float base, int hd, int pos, int i, float* cs);
 // MoE decode gate/up + SwiGLU over the k selected experts (eidx, device) and the
 // shared one: y[(j, i)] = silu(gate) * up for slot j <= k, row i < ff
 int launch_moe_gu(const void* w_e, const void* w_s, const int32_t* eidx, int E, int kslots, int ff,
@@ -76,11 +89,16 @@ int launch_head(const lps_head_desc* h, const float* x, float* logits, int32_t* 
 size_t head_scratch(const lps_head_desc* h);
 
 size_t attn_scratch(int nq, int nkv, int hd, int ctx_max);
+// pos_dev set: the rows are 0 .. *pos_dev (read on the device), n_rows ignored
 int launch_attention(int nq, int nkv, int hd, int kvdtype, const void* kc, const void* vc,
                      int ctx_max, int n_rows, const float* q, float* o, void* scratch,
-                     hipStream_t st, Stamp sp = {});
+                     hipStream_t st, Stamp sp = {}, const int32_t* pos_dev = nullptr);
 
 int launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t st);
+// decode step state (pos, step, flags): see lps_step_advance
+int launch_step_advance(int32_t* state, int32_t pos_limit, const int32_t* argmax, int32_t* tok_cur,
+                        const int32_t* feed, int32_t n_feed, int32_t* tok_hist, int32_t hist_cap,
+                        const float* logits, int32_t vocab, float* logits_hist, hipStream_t st);
 
 // validation helpers shared by entry points
 int check_layer(const lps_layer_desc* L, const char* who);

@@ -113,6 +113,48 @@ __global__ __launch_bounds__(256) void k_stream_read(const u32x4* __restrict__ s
   if (threadIdx.x == 0) sink[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
 }
 
+// ---- device-side step state of a replayed decode step ----------------------------------
+// state[0] = position, state[1] = step, state[2] = flags (bit 0: the position
+// reached its limit and stayed).  Both kernels read the step from state[1], so
+// the copy runs before the advance in stream order.
+__global__ void k_hist_logits(const int32_t* state, const float* logits, int vocab, float* hist,
+                              int cap) {
+  const int s = state[1];
+  if (s < 0 || s >= cap) return;
+  float* dst = hist + (long long)s * vocab;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < vocab; i += gridDim.x * blockDim.x)
+    dst[i] = logits[i];
+}
+
+__global__ void k_step_advance(int32_t* state, int pos_limit, const int32_t* argmax,
+                               int32_t* tok_cur, const int32_t* feed, int n_feed,
+                               int32_t* tok_hist, int cap) {
+  if (threadIdx.x != 0) return;
+  const int s = state[1];
+  const int a = *argmax;
+  if (tok_hist && s >= 0 && s < cap) tok_hist[s] = a;
+  // the next step's input: the fed id while ids remain, else this step's argmax
+  *tok_cur = (s + 1 >= 0 && s + 1 < n_feed) ? feed[s + 1] : a;
+  const int pos = state[0];
+  if (pos + 1 < pos_limit) state[0] = pos + 1;
+  else state[2] = state[2] | 1;
+  state[1] = s + 1;
+}
+
+int launch_step_advance(int32_t* state, int32_t pos_limit, const int32_t* argmax, int32_t* tok_cur,
+                        const int32_t* feed, int32_t n_feed, int32_t* tok_hist, int32_t hist_cap,
+                        const float* logits, int32_t vocab, float* logits_hist, hipStream_t st) {
+  if (logits_hist && hist_cap > 0) {
+    hipLaunchKernelGGL(k_hist_logits, grid_for(vocab / 4 + 1), dim3(256), 0, st, state, logits,
+                       vocab, logits_hist, hist_cap);
+    LPS_HIP(hipGetLastError());
+  }
+  hipLaunchKernelGGL(k_step_advance, dim3(1), dim3(64), 0, st, state, pos_limit, argmax, tok_cur,
+                     feed, n_feed, tok_hist, hist_cap);
+  LPS_HIP(hipGetLastError());
+  return LPS_OK;
+}
+
 int launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t st) {
   if (n == 0) return LPS_OK;
   hipLaunchKernelGGL(k_copy, grid_for(n / 4 + 1), dim3(256), 0, st, src, dst, (long long)n);

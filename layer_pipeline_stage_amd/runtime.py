@@ -102,6 +102,8 @@ class DeviceDecoder:
         kvdt = lps.DTYPES[cfg.kvdtype]
         self.layers = []
         descs = (lps.LayerDesc * cfg.n_layers)()
+        # cos / sin of every cache position, read by the device-position walk
+        self.rope_cs = to_dev(lps.rope_table(cfg.hd, cfg.rope_base, cfg.ctx_max), dev)
         kv_torch = torch.float32 if cfg.kvdtype == "f32" else torch.int16
         for l, L in enumerate(model["layers"]):
             t = {}
@@ -125,6 +127,7 @@ class DeviceDecoder:
             d.w_gu, d.s_gu = ptr(t["w_gu"]), ptr(t["s_gu"])
             d.w_d, d.s_d = ptr(t["w_d"]), ptr(t["s_d"])
             d.k_cache, d.v_cache = ptr(t["k"]), ptr(t["v"])
+            d.rope_cs = ptr(self.rope_cs)
         self.descs = descs
         h = C.c_void_p()
         lps.lps_model_create(descs, cfg.n_layers, C.byref(h))
@@ -145,6 +148,12 @@ class DeviceDecoder:
             self.tok_ring = torch.zeros(ring, dtype=torch.int32, device=dev)
             self.host_logits = torch.zeros((ring, cfg.vocab), dtype=torch.float32).pin_memory()
             self.host_tok = torch.zeros(ring, dtype=torch.int32).pin_memory()
+            # device step state of the graph mode: [pos, step, flags], the next
+            # input id, this step's argmax and logits
+            self.g_state = torch.zeros(4, dtype=torch.int32, device=dev)
+            self.g_tok = torch.zeros(1, dtype=torch.int32, device=dev)
+            self.g_arg = torch.zeros(1, dtype=torch.int32, device=dev)
+            self.g_logits = torch.zeros(cfg.vocab, dtype=torch.float32, device=dev)
         self.readback = torch.cuda.Stream(device=dev)
         self._streams_mode = streams
         self.reset()
@@ -280,6 +289,91 @@ class DeviceDecoder:
             drain(i)
         fed = ids[:P] + [out_tok[i - 1] for i in range(P, total)]
         return StepResult(fed=fed, argmax=out_tok, logits=out_logits)
+
+    # ---- the whole pass as one graph --------------------------------------------
+    def _walk_dpos(self):
+        """Enqueue all stages of one step, the position read from g_state[0]."""
+        n, st = self.n_stages, self.streams
+        t = self.step_no
+        pos_dev = ptr(self.g_state)
+        for s in range(n):
+            if s > 0:
+                lps.lps_boundary_send(self.bounds[s - 1], ptr(self.x[s - 1]), t, sp(st[s - 1]))
+                lps.lps_boundary_recv(self.bounds[s - 1], ptr(self.x[s]), t, sp(st[s]))
+            lps.lps_stage_forward_dpos(self.model, self._fence_c, n, s, ptr(self.x[s]), pos_dev,
+                                       ptr(self.scratch[s]), self.scratch_bytes, sp(st[s]))
+        self.step_no += 1
+
+    def capture_step(self, feed_dev, n_feed, tok_hist, logits_hist, hist_cap):
+        """Capture one decode step (embed, every stage and boundary, head,
+        step advance) into a graph on stage 0's stream; the other stage
+        streams fork into it through the boundary events and are joined back
+        at the end.  Returns the graph handle (lps_graph_destroy frees it)."""
+        cfg = self.cfg
+        st0, stl = self.streams[0], self.streams[-1]
+        torch.cuda.synchronize(self.device)
+        lps.lps_graph_begin(sp(st0))
+        g = C.c_void_p()
+        try:
+            lps.lps_embed(ptr(self.embed), lps.DTYPES[cfg.wdtype], cfg.vocab, cfg.d,
+                          ptr(self.g_tok), ptr(self.x[0]), sp(st0))
+            self._walk_dpos()
+            lps.lps_head_forward(C.byref(self.head), ptr(self.x[-1]), ptr(self.g_logits),
+                                 ptr(self.g_arg), ptr(self.head_scratch),
+                                 self.head_scratch.numel(), sp(stl))
+            lps.lps_step_advance(ptr(self.g_state), cfg.ctx_max, ptr(self.g_arg), ptr(self.g_tok),
+                                 feed_dev, n_feed, tok_hist, hist_cap, ptr(self.g_logits),
+                                 cfg.vocab, logits_hist, sp(stl))
+        finally:
+            join = (C.c_void_p * len(self.streams))(*[sp(s) for s in self.streams])
+            lps.lps_graph_end(sp(st0), join, len(self.streams), C.byref(g))
+        return g
+
+    def run_tokens_graph(self, prompt, n_steps=0, feed=None, p0=None, logits=True,
+                         timer=None) -> StepResult:
+        """run_tokens with the whole step captured once and replayed: the
+        position, the step and the next input id live on the device and are
+        advanced by the graph itself, so the host only launches replays.  Every
+        step's argmax (and, with logits=True, its logits) is kept in a device
+        history that is read back once after the last replay.  timer: an
+        optional callable run around the replays (for the bench)."""
+        cfg = self.cfg
+        assert self.head is not None, "model has no vocabulary"
+        p = cfg.prefix if p0 is None else p0
+        ids = list(prompt) if feed is None else list(feed)
+        P = len(ids)
+        total = P + (0 if feed is not None else n_steps)
+        assert P >= 1 and p + total <= cfg.ctx_max, "cache too short for this run"
+        dev = self.device
+        feed_dev = torch.tensor(ids, dtype=torch.int32, device=dev)
+        tok_hist = torch.zeros(total, dtype=torch.int32, device=dev)
+        lg_hist = (torch.zeros((total, cfg.vocab), dtype=torch.float32, device=dev)
+                   if logits else None)
+        self.g_state.copy_(torch.tensor([p, 0, 0, 0], dtype=torch.int32))
+        self.g_tok.fill_(ids[0])
+        g = self.capture_step(ptr(feed_dev), P, ptr(tok_hist),
+                              ptr(lg_hist) if logits else None, total)
+        try:
+            st0 = self.streams[0]
+            torch.cuda.synchronize(dev)
+            if timer is not None:
+                timer(True)
+            for _ in range(total):
+                lps.lps_graph_launch(g, sp(st0))
+            # the deferred readback: every step's id (and logits) in one drain,
+            # ordered behind the replays on their stream
+            with torch.cuda.stream(st0):
+                toks = tok_hist.cpu().tolist()
+                lg = list(lg_hist.cpu().numpy()) if logits else [None] * total
+            if timer is not None:
+                timer(False)
+        finally:
+            torch.cuda.synchronize(dev)
+            lps.lps_graph_destroy(g)
+        state = self.g_state.cpu().tolist()
+        assert state[1] == total, state
+        fed = ids[:P] + [toks[i - 1] for i in range(P, total)]
+        return StepResult(fed=fed, argmax=toks, logits=lg)
 
     def run_hidden(self, xs: np.ndarray, p0=None) -> np.ndarray:
         """Models without a vocabulary: step t feeds the f32 row xs[t] at position

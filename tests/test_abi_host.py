@@ -166,3 +166,58 @@ def test_memory_balanced_fence_for_the_dense_slice():
     assert fence == [0, 2, 4, 6, 8] and groups > 0
     fence2, groups2 = memory_balanced_fence(n_stages=4, free_bytes=[144 << 30] + [288 << 30] * 3, **geo)
     assert fence2[1] - fence2[0] < 2 and groups2 < groups
+
+
+def test_rope_table_matches_the_oracle_rotation(L):
+    """lps_rope_table (the device-position walk's cos / sin table) against the
+    oracle's rotation applied to unit vectors: rotating e_i at position p
+    yields cos(p theta_i) at i and sin(p theta_i) at i + hd/2.  The table is
+    the f64 values rounded once to f32, so it is within one f32 ulp."""
+    from oracle.decoder import rope
+    for hd, base, n_pos in ((64, 10000.0, 300), (128, 500000.0, 4200)):
+        half = hd // 2
+        tab = L.rope_table(hd, base, n_pos)
+        assert tab.shape == (n_pos, half, 2) and tab.dtype == np.float32
+        eye = np.eye(half, hd)
+        for p in list(range(0, n_pos, 97)) + [n_pos - 1]:
+            r = rope(eye, p, base)
+            want = np.stack([r[np.arange(half), np.arange(half)],
+                             r[np.arange(half), half + np.arange(half)]], axis=-1)
+            ulp = np.spacing(np.abs(want).astype(np.float32))
+            assert np.all(np.abs(tab[p].astype(np.float64) - want) <= ulp), (hd, p)
+        assert np.array_equal(tab[0, :, 0], np.ones(half, np.float32))
+        assert np.array_equal(tab[0, :, 1], np.zeros(half, np.float32))
+
+
+def test_graph_and_device_state_entry_points_refuse_bad_arguments(L):
+    """The whole-pass graph entry points validate on the host first."""
+    for args in ((0, 1e4, 4), (63, 1e4, 4), (64, 1e4, 0), (64, 0.0, 4)):
+        with pytest.raises(L.LpsError) as e:
+            L.lps_rope_table(*args, 16)
+        assert e.value.code == L.LPS_EINVAL
+    with pytest.raises(L.LpsError):
+        L.lps_rope_table(64, 1e4, 4, None)
+    bad_adv = [
+        (None, 8, 16, 16, None, 0, None, 0, None, 0, None, None),   # null state
+        (16, 0, 16, 16, None, 0, None, 0, None, 0, None, None),     # pos_limit < 1
+        (16, 8, 16, 16, None, 3, None, 0, None, 0, None, None),     # feed ids without feed
+        (16, 8, 16, 16, None, 0, None, 4, None, 0, None, None),     # history without tok_hist
+        (16, 8, 16, 16, None, 0, 16, 4, None, 0, 16, None),         # logits history, no logits
+    ]
+    for a in bad_adv:
+        with pytest.raises(L.LpsError) as e:
+            L.lps_step_advance(*a)
+        assert e.value.code == L.LPS_EINVAL, a
+    with pytest.raises(L.LpsError) as e:
+        L.lps_graph_begin(None)                      # the null stream is not captured
+    assert e.value.code == L.LPS_EINVAL
+    with pytest.raises(L.LpsError) as e:
+        L.lps_graph_end(None, None, 0, None)         # null out
+    assert e.value.code == L.LPS_EINVAL
+    with pytest.raises(L.LpsError):
+        L.lps_graph_launch(None, None)
+    assert L.lps_graph_destroy(None) == 0
+    fence = L.i32_array([0, 1])
+    with pytest.raises(L.LpsError) as e:
+        L.lps_stage_forward_dpos(None, fence, 1, 0, 16, 16, 16, 1 << 20, None)
+    assert e.value.code == L.LPS_EINVAL

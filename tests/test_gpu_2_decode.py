@@ -119,6 +119,65 @@ def test_single_stream_seam_equals_per_stage_streams(rt):
     b.close()
 
 
+def _same(a, b):
+    assert a.fed == b.fed and a.argmax == b.argmax
+    assert len(a.logits) == len(b.logits)
+    for i, (x, y) in enumerate(zip(a.logits, b.logits)):
+        assert np.array_equal(x, y), i
+
+
+def test_graph_replay_equals_eager_tiny(rt):
+    """ninfer pipeline stages, How it works (StageLink) and Verification (graphs
+    and eager byte-identical): the whole step captured once and replayed, the
+    position and next id advanced on the device, gives the eager walk's bits,
+    for one stage and for two and three stages on the same-stream seam."""
+    cfg = synth.TINY
+    m = synth.make_tiny(cfg)
+    for fence in ([0, 4], [0, 2, 4], [0, 1, 3, 4]):
+        dd = rt.DeviceDecoder(m, fence=fence, streams="single")
+        ref = dd.run_tokens(m["prompt"], cfg.steps)
+        dd.reset()
+        got = dd.run_tokens_graph(m["prompt"], cfg.steps)
+        _same(got, ref)
+        dd.close()
+
+
+def test_graph_replay_per_stage_streams_and_eager_after(rt):
+    """N = 4 on four streams: the capture forks the later stage streams in
+    through the boundary events and joins them back; replays equal the eager
+    walk at context 32 -> 96, twice with a fresh capture, and an eager walk
+    after the graphs (boundary slots reused across the capture) still gives
+    the same bits; teacher forcing through the graph too."""
+    cfg = synth.TINY_N4
+    m = synth.make_tiny(cfg)
+    dd = rt.DeviceDecoder(m, fence=[0, 1, 2, 3, 4])
+    ref = dd.run_tokens(m["prompt"], cfg.steps)
+    for _ in range(2):
+        dd.reset()
+        _same(dd.run_tokens_graph(m["prompt"], cfg.steps), ref)
+    dd.reset()
+    _same(dd.run_tokens(m["prompt"], cfg.steps), ref)
+    dd.reset()
+    feed = ref.fed[:40]
+    got = dd.run_tokens_graph([], feed=feed)
+    assert got.fed == feed and got.argmax == ref.argmax[:40]
+    assert all(np.array_equal(x, y) for x, y in zip(got.logits, ref.logits[:40]))
+    dd.close()
+
+
+def test_graph_replay_bf16(rt):
+    """The device-position walk on bf16 weights and bf16 caches equals the
+    eager walk bit for bit (the RoPE table holds the by-value launch's own
+    f32 cos / sin values)."""
+    cfg = replace(synth.TINY, wdtype="bf16", kvdtype="bf16", prompt=4, steps=8)
+    m = synth.make_tiny(cfg)
+    dd = rt.DeviceDecoder(m, fence=[0, 2, 4])
+    ref = dd.run_tokens(m["prompt"], cfg.steps)
+    dd.reset()
+    _same(dd.run_tokens_graph(m["prompt"], cfg.steps), ref)
+    dd.close()
+
+
 def test_invalid_fence_refused(rt):
     from layer_pipeline_stage_amd import lps
     m = synth.make_tiny(replace(synth.TINY, prompt=2, steps=1))
