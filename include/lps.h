@@ -119,8 +119,15 @@ typedef struct lps_layer_desc {
   const float* g_ffn;              /* (dev) [d] f32 */
   const void* w_gu;  const uint8_t* s_gu;    /* (dev) [2ff, d] gate rows, then up rows */
   const void* w_d;   const uint8_t* s_d;     /* (dev) [d, ff] */
-  void* k_cache;     /* (dev) [nkv, ctx_max, hd] kvdtype, owned by this layer's stage */
-  void* v_cache;     /* (dev) [nkv, ctx_max, hd] kvdtype */
+  void* k_cache;     /* (dev) kvdtype, owned by this layer's stage.  LPS_F32:
+                      * [nkv, ctx_max, hd].  LPS_BF16: 16-row tiles of 8-dim groups,
+                      * [nkv, ctx_max/16, hd/8, 16, 8]: element (head j, row r, dim e) at
+                      * ((j*(ctx_max/16) + r/16)*(hd/8) + e/8)*128 + (r%16)*8 + e%8 */
+  void* v_cache;     /* (dev) LPS_F32: [nkv, ctx_max, hd].  LPS_BF16: 16-row tiles,
+                      * transposed, [nkv, ctx_max/16, hd, 16]: element (j, r, e) at
+                      * ((j*(ctx_max/16) + r/16)*hd + e)*16 + r%16.  (The bf16 layouts are
+                      * the matrix-core operand order: a 16-row tile of K or V is one
+                      * contiguous block.)  bf16 caches need ctx_max % 16 == 0 */
   const float* rope_cs;  /* (dev, optional) [ctx_max, hd/2, 2] f32: cos, sin of pos * theta_i
                           * (lps_rope_table); required by the device-position entry points */
 } lps_layer_desc;
@@ -256,7 +263,10 @@ int lps_gemv(int32_t wdtype, const void* w, const uint8_t* s, int32_t N, int32_t
 int lps_qkv_rope_append(const lps_layer_desc* L, const float* x, int32_t pos, float* q,
                         void* stream);
 /* A6: o (dev [nq*hd] f32) = softmax(q K^T / sqrt(hd)) V per q head over cache
- * rows 0..n_rows-1 of kv head j/(nq/nkv).  Caches (dev) [nkv, ctx_max, hd].
+ * rows 0..n_rows-1 of kv head j/(nq/nkv).  Caches (dev) in the layouts of
+ * lps_layer_desc.k_cache / v_cache (16-row tiles for LPS_BF16, which also needs
+ * ctx_max % 16 == 0).  Rows at or past n_rows are never used, whatever they
+ * hold.
  * scratch (dev) of lps_attention_scratch_bytes(nq, nkv, hd, ctx_max) bytes. */
 size_t lps_attention_scratch_bytes(int32_t nq, int32_t nkv, int32_t hd, int32_t ctx_max);
 int lps_attention_decode(int32_t nq, int32_t nkv, int32_t hd, int32_t kvdtype,

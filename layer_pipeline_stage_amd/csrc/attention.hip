@@ -214,6 +214,190 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attn(AttnP p) {
   }
 }
 
+// ---- bf16 caches: both products on the matrix cores ---------------------------------
+// Both caches are stored in 16-row tiles laid out as the MFMA operands are read:
+//   K: [nkv, ctx_max/16, hd/8, 16, 8]  (8-dim groups of the tile's 16 rows)
+//   V: [nkv, ctx_max/16, hd, 16]       (the tile transposed: rows contiguous)
+// so one wave's 16 rows of K and of V are each one contiguous 4 KiB block
+// (hd = 128) and every load instruction reads whole 128-byte lines, and the PV
+// product reduces over rows that lie contiguously, as its operands want.  (A
+// plain [hd, ctx] transpose of V spreads a wave's rows over hd DRAM pages and
+// reads at half the rate.)
+// One workgroup of AM_WAVES waves takes one (kv head, ATT_CH-row chunk) tile;
+// wave w owns its 16 rows and keeps everything for them in registers:
+//   S^T[16 rows, 16 cols] = K[16 rows, hd] . Q^T[hd, 16 cols]   (16x16x32 bf16)
+// with the G query heads of the group in columns 0..G-1 (the rest zero) and q
+// split into bf16 hi + lo parts (q - hi - lo is below 2^-16 |q|), so the scores
+// keep nearly f32 accuracy.  Lane (col, grp) then holds the scores of rows
+// 4 grp .. 4 grp + 3 for head col, which is exactly the B operand layout of
+//   O^T[hd, 16 cols] += V^T[hd, 16 rows] . P^T[16 rows, 16 cols]   (16x16x16 bf16)
+// so the softmax weights (again hi + lo) feed PV without leaving the lane.  The
+// wave's softmax max and sum take two cross-lane steps; the AM_WAVES wave
+// partials are merged through LDS into the tile's (m, l, o) partial, the same
+// format the merge launch reads.
+constexpr int AM_WAVES = ATT_CH / 16;
+constexpr int AM_THREADS = AM_WAVES * WAVE;
+static_assert(AM_THREADS <= 1024, "attention tile too large for one workgroup");
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t att_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// hi = bf16(v) (nearest even), lo = bf16(v - hi)
+__device__ __forceinline__ void split_bf16(float v, __bf16& hi, __bf16& lo) {
+  hi = static_cast<__bf16>(v);
+  lo = static_cast<__bf16>(v - static_cast<float>(hi));
+}
+
+template <int HD, int G>
+__global__ __launch_bounds__(AM_THREADS) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void k_attn_mfma(AttnP p) {
+  constexpr int KK = HD / 32;        // QK steps over the head dim
+  constexpr int DT = HD / 16;        // PV tiles of the head dim
+  constexpr int HDP = HD + 4;        // padded LDS row (spreads the heads over the banks)
+  extern __shared__ float red[];     // [AM_WAVES][G][HDP]
+  __shared__ float mw[AM_WAVES][G], lw[AM_WAVES][G];
+
+  const int chunk = blockIdx.x, g = blockIdx.y;
+  int n_rows, nch;
+  attn_rows(p, n_rows, nch);
+  if (chunk >= nch) return;   // a device-position launch covers ctx_max rows
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
+  const int col = lane & 15, grp = lane >> 4;
+  const int row0 = chunk * ATT_CH + 16 * w;          // the wave's first row
+  const bool live = row0 < n_rows;                   // wave-uniform
+
+  // the group's G q heads, staged once per workgroup (one 16-byte load per thread;
+  // threads past the G * HD / 4 loads read a valid address and drop it)
+  static_assert(G * HD / 4 <= AM_THREADS, "q staging takes one load per thread");
+  __shared__ f32x4 qs[G * HD / 4];
+  const int qi = min((int)threadIdx.x, G * HD / 4 - 1);
+  const f32x4 qv = reinterpret_cast<const f32x4*>(p.q + (long long)g * G * HD)[qi];
+  // K tile of rows row0 .. row0 + 15: lane (col, grp) takes row col, dims 32 kk + 8 grp .. + 7
+  const char* kbase = static_cast<const char*>(p.kc) + (long long)g * p.ctx_max * HD * 2;
+  const auto krs = att_rsrc(kbase, live ? p.ctx_max * HD * 2 : 0);
+  u32x4 kr[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk)
+    kr[kk] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           krs, (row0 * HD + (4 * kk + grp) * 128 + col * 8) * 2, 0, 2));
+  // V tile of rows row0 .. row0 + 15: dims 16 dt + col, rows 4 grp .. 4 grp + 3
+  const char* vbase = static_cast<const char*>(p.vc) + (long long)g * HD * p.ctx_max * 2;
+  const auto vrs = att_rsrc(vbase, live ? HD * p.ctx_max * 2 : 0);
+  const int vt = (row0 >> 4) * HD * 16;              // the tile's first element
+  u32x2 vr[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+    vr[dt] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                           vrs, (vt + (16 * dt + col) * 16 + 4 * grp) * 2, 0, 2));
+  // every load is in flight before any arithmetic: one HBM round trip per wave
+  __builtin_amdgcn_sched_barrier(0);
+  if (threadIdx.x < G * HD / 4) qs[threadIdx.x] = qv;
+  __syncthreads();
+
+  // ---- scores ----
+  // B operand: q of head col (zero for the padding columns), dims 32 kk + 8 grp .. + 7
+  const bool hv = col < G;
+  const f32x4* qh = qs + (hv ? col : 0) * (HD / 4) + 2 * grp;
+  bf16x8 qhi[KK], qlo[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    const f32x4 q0 = qh[8 * kk], q1 = qh[8 * kk + 1];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      __bf16 h, l;
+      split_bf16(hv ? (e < 4 ? q0[e] : q1[e - 4]) : 0.f, h, l);
+      qhi[kk][e] = h;
+      qlo[kk][e] = l;
+    }
+  }
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    const bf16x8 a = __builtin_bit_cast(bf16x8, kr[kk]);
+    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qhi[kk], s, 0, 0, 0);
+    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qlo[kk], s, 0, 0, 0);
+  }
+  // ---- the wave's softmax over its 16 rows, per head (lanes col, col+16, col+32, col+48) ----
+  const int rbase = row0 + 4 * grp;
+  float sv[4];
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sv[i] = (rbase + i < n_rows) ? s[i] * p.scale : -INFINITY;
+    m = fmaxf(m, sv[i]);
+  }
+  m = fmaxf(m, __shfl_xor(m, 16, WAVE));
+  m = fmaxf(m, __shfl_xor(m, 32, WAVE));
+  float pv[4], l = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    pv[i] = sv[i] == -INFINITY ? 0.f : expf(sv[i] - m);
+    l += pv[i];
+  }
+  l += __shfl_xor(l, 16, WAVE);
+  l += __shfl_xor(l, 32, WAVE);
+  i16x4 phi, plo;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    __bf16 h, lo;
+    split_bf16(pv[i], h, lo);
+    phi[i] = __builtin_bit_cast(short, h);
+    plo[i] = __builtin_bit_cast(short, lo);
+  }
+  // ---- PV; V^T values of rows at or past n_rows are zeroed bit-wise first ----
+  const int valid = min(max(n_rows - rbase, 0), 4);
+  const unsigned long long vmask = valid >= 4 ? ~0ull : ((1ull << (16 * valid)) - 1ull);
+  f32x4 o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    const unsigned long long bits =
+        ((unsigned long long)vr[dt].y << 32 | vr[dt].x) & vmask;
+    const i16x4 a = __builtin_bit_cast(i16x4, bits);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, phi, acc, 0, 0, 0);
+    o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, plo, acc, 0, 0, 0);
+  }
+  // ---- merge the waves' partials through LDS ----
+  if (hv) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<f32x4*>(red + (w * G + col) * HDP + 16 * dt + 4 * grp) = o[dt];
+    if (grp == 0) {
+      mw[w][col] = m;
+      lw[w][col] = l;
+    }
+  }
+  __syncthreads();
+  const long long pb = (long long)g * p.nstride + chunk;
+  for (int idx = threadIdx.x; idx < G * (HD / 2); idx += AM_THREADS) {
+    const int h = idx / (HD / 2), e2 = idx - h * (HD / 2);
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < AM_WAVES; ++v) M = fmaxf(M, mw[v][h]);
+    float L = 0.f;
+    f32x2 acc = {0.f, 0.f};
+#pragma unroll
+    for (int v = 0; v < AM_WAVES; ++v) {
+      const float sc = mw[v][h] == -INFINITY ? 0.f : expf(mw[v][h] - M);
+      L = fmaf(sc, lw[v][h], L);
+      const f32x2 x = *reinterpret_cast<const f32x2*>(red + (v * G + h) * HDP + 2 * e2);
+      acc.x = fmaf(sc, x.x, acc.x);
+      acc.y = fmaf(sc, x.y, acc.y);
+    }
+    if (e2 == 0) {
+      p.pm[pb * G + h] = M;
+      p.pl[pb * G + h] = L;
+    }
+    *reinterpret_cast<f32x2*>(p.po + (pb * G + h) * HD + 2 * e2) = acc;
+  }
+}
+
 // Merge of the chunk partials of one q head: M = max m_c, L = sum_c l_c
 // e^(m_c - M), o = sum_c o_c e^(m_c - M) / L.  A separate launch: the partials
 // of all tiles are complete when it starts (stream order), so no device-scope
@@ -309,11 +493,19 @@ size_t attn_scratch(int nq, int nkv, int hd, int ctx_max) {
 
 template <int HD, int KVT, int G>
 static int go_g(const AttnP& p, int nkv, hipStream_t st, hipEvent_t start) {
-  const size_t lds = size_t(AttnCfg<HD, KVT>::RPP) * G * HD * sizeof(float);
-  int rc = ensure_lds((const void*)k_attn<HD, KVT, G>, lds);
-  if (rc) return rc;
-  LPS_LAUNCH((k_attn<HD, KVT, G>), dim3(p.nch, nkv), dim3(ATT_THREADS), lds, st, start, nullptr, p);
-  return LPS_OK;
+  if constexpr (KVT == LPS_BF16) {
+    const size_t lds = size_t(AM_WAVES) * G * (HD + 4) * sizeof(float);
+    int rc = ensure_lds((const void*)k_attn_mfma<HD, G>, lds);
+    if (rc) return rc;
+    LPS_LAUNCH((k_attn_mfma<HD, G>), dim3(p.nch, nkv), dim3(AM_THREADS), lds, st, start, nullptr, p);
+    return LPS_OK;
+  } else {
+    const size_t lds = size_t(AttnCfg<HD, KVT>::RPP) * G * HD * sizeof(float);
+    int rc = ensure_lds((const void*)k_attn<HD, KVT, G>, lds);
+    if (rc) return rc;
+    LPS_LAUNCH((k_attn<HD, KVT, G>), dim3(p.nch, nkv), dim3(ATT_THREADS), lds, st, start, nullptr, p);
+    return LPS_OK;
+  }
 }
 
 template <int HD, int KVT>

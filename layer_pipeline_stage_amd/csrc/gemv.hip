@@ -163,10 +163,21 @@ __device__ __forceinline__ void epilogue(const GemvP& p, int u, int r0, int r1, 
     } else {
       const bool is_k = hh < p.nq + p.nkv;
       const int gkv = is_k ? hh - p.nq : hh - p.nq - p.nkv;
-      const long long off = ((long long)gkv * p.ctx_max + pos) * p.hd + i;
-      void* base = is_k ? p.kc : p.vc;
-      store_kv(base, p.kvdtype, off, o0);
-      store_kv(base, p.kvdtype, off + half, o1);
+      const long long tile = (long long)gkv * (p.ctx_max >> 4) + (pos >> 4);
+      if (p.kvdtype == LPS_F32) {            // row pos of [nkv, ctx_max, hd]
+        const long long off = ((long long)gkv * p.ctx_max + pos) * p.hd + i;
+        void* base = is_k ? p.kc : p.vc;
+        store_kv(base, p.kvdtype, off, o0);
+        store_kv(base, p.kvdtype, off + half, o1);
+      } else if (is_k) {                     // bf16 K: [nkv, ctx_max/16, hd/8, 16, 8]
+        const long long off = (tile * (p.hd >> 3) + (i >> 3)) * 128 + (pos & 15) * 8 + (i & 7);
+        store_kv(p.kc, p.kvdtype, off, o0);
+        store_kv(p.kc, p.kvdtype, off + (long long)(half >> 3) * 128, o1);
+      } else {                               // bf16 V: [nkv, ctx_max/16, hd, 16]
+        const long long off = (tile * p.hd + i) * 16 + (pos & 15);
+        store_kv(p.vc, p.kvdtype, off, o0);
+        store_kv(p.vc, p.kvdtype, off + (long long)half * 16, o1);
+      }
     }
   }
 }

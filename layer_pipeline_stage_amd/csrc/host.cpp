@@ -101,6 +101,10 @@ int check_layer(const lps_layer_desc* L, const char* who) {
               "%s: d %d, nq*hd %d and ff %d must be multiples of %d for this weight dtype", who,
               L->d, L->nq * L->hd, L->ff, ch);
   LPS_REQUIRE(L->ctx_max > 0, LPS_EINVAL, "%s: ctx_max %d", who, L->ctx_max);
+  if (L->kvdtype == LPS_BF16)   // whole 16-row V tiles; 32-bit byte offsets per head
+    LPS_REQUIRE(L->ctx_max % 16 == 0 && L->ctx_max <= (1 << 22), LPS_EINVAL,
+                "%s: bf16 caches need ctx_max %d to be a multiple of 16 and at most 4194304", who,
+                L->ctx_max);
   LPS_REQUIRE(L->d * 4 <= 160 * 1024 && L->ff * 4 <= 160 * 1024 && L->nq * L->hd * 4 <= 160 * 1024,
               LPS_EUNSUP, "%s: an activation vector exceeds 160 KiB of LDS", who);
   LPS_REQUIRE(L->g_attn && L->w_qkv && L->w_o && L->g_ffn && L->w_gu && L->w_d && L->k_cache &&
@@ -647,6 +651,9 @@ int lps_attention_decode(int32_t nq, int32_t nkv, int32_t hd, int32_t kvdtype, c
               kvdtype);
   LPS_REQUIRE(n_rows >= 1 && n_rows <= ctx_max, LPS_ERANGE,
               "lps_attention_decode: n_rows %d outside [1, ctx_max=%d]", n_rows, ctx_max);
+  LPS_REQUIRE(kvdtype != LPS_BF16 || (ctx_max % 16 == 0 && ctx_max <= (1 << 22)), LPS_EINVAL,
+              "lps_attention_decode: bf16 caches need ctx_max %d to be a multiple of 16 and at "
+              "most 4194304", ctx_max);
   LPS_REQUIRE(k_cache && v_cache && q && o && scratch, LPS_EINVAL, "lps_attention_decode: null pointer");
   LPS_REQUIRE(aligned16(k_cache) && aligned16(v_cache), LPS_EINVAL,
               "lps_attention_decode: caches must be 16-byte aligned");

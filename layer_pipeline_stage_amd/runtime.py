@@ -24,6 +24,7 @@ import numpy as np
 import torch
 
 from . import _lib as lps
+from . import layout
 
 
 def _need_gpu():
@@ -102,8 +103,12 @@ class DeviceDecoder:
         kvdt = lps.DTYPES[cfg.kvdtype]
         self.layers = []
         descs = (lps.LayerDesc * cfg.n_layers)()
+        # cache rows: bf16 caches are stored in 16-row tiles (layout.py) and need
+        # the row count to be a multiple of 16
+        self.ctx_rows = ctx = (cfg.ctx_max + 15) // 16 * 16
+        self.tiled = cfg.kvdtype == "bf16"
         # cos / sin of every cache position, read by the device-position walk
-        self.rope_cs = to_dev(lps.rope_table(cfg.hd, cfg.rope_base, cfg.ctx_max), dev)
+        self.rope_cs = to_dev(lps.rope_table(cfg.hd, cfg.rope_base, ctx), dev)
         kv_torch = torch.float32 if cfg.kvdtype == "f32" else torch.int16
         for l, L in enumerate(model["layers"]):
             t = {}
@@ -111,15 +116,20 @@ class DeviceDecoder:
             t["g_ffn"] = to_dev(L["g_ffn"], dev)
             for n in ("w_qkv", "w_o", "w_gu", "w_d"):
                 t[n], t["s" + n[1:]] = _weight(L[n], dev)
-            t["k"] = torch.zeros((cfg.nkv, cfg.ctx_max, cfg.hd), dtype=kv_torch, device=dev)
-            t["v"] = torch.zeros_like(t["k"])
+            if self.tiled:
+                kshape = (cfg.nkv, ctx // 16, cfg.hd // 8, 16, 8)
+                vshape = (cfg.nkv, ctx // 16, cfg.hd, 16)
+            else:
+                kshape = vshape = (cfg.nkv, ctx, cfg.hd)
+            t["k"] = torch.zeros(kshape, dtype=kv_torch, device=dev)
+            t["v"] = torch.zeros(vshape, dtype=kv_torch, device=dev)
             if cfg.prefix:
                 t["k_prefix"] = to_dev(L["k_prefix"], dev)
                 t["v_prefix"] = to_dev(L["v_prefix"], dev)
             self.layers.append(t)
             d = descs[l]
             d.d, d.nq, d.nkv, d.hd, d.ff = cfg.d, cfg.nq, cfg.nkv, cfg.hd, cfg.ff
-            d.wdtype, d.kvdtype, d.ctx_max = wdt, kvdt, cfg.ctx_max
+            d.wdtype, d.kvdtype, d.ctx_max = wdt, kvdt, ctx
             d.eps, d.rope_base = cfg.eps, cfg.rope_base
             d.g_attn, d.g_ffn = ptr(t["g_attn"]), ptr(t["g_ffn"])
             d.w_qkv, d.s_qkv = ptr(t["w_qkv"]), ptr(t["s_qkv"])
@@ -204,8 +214,18 @@ class DeviceDecoder:
         for t in self.layers:
             if "k_prefix" in t:
                 P = t["k_prefix"].shape[1]
-                t["k"][:, :P].copy_(t["k_prefix"])
-                t["v"][:, :P].copy_(t["v_prefix"])
+                if self.tiled:
+                    # whole tiles: rows P .. P16 - 1 get zeros (written before read)
+                    P16 = (P + 15) // 16 * 16
+                    for name, to_tiles in (("k", layout.k_to_tiles), ("v", layout.v_to_tiles)):
+                        src = t[name + "_prefix"]
+                        rows = torch.zeros((src.shape[0], P16, src.shape[2]), dtype=src.dtype,
+                                           device=self.device)
+                        rows[:, :P].copy_(src)
+                        t[name][:, :P16 // 16].copy_(to_tiles(rows))
+                else:
+                    t["k"][:, :P].copy_(t["k_prefix"])
+                    t["v"][:, :P].copy_(t["v_prefix"])
         torch.cuda.synchronize(self.device)
 
     def close(self):

@@ -221,3 +221,27 @@ def test_graph_and_device_state_entry_points_refuse_bad_arguments(L):
     with pytest.raises(L.LpsError) as e:
         L.lps_stage_forward_dpos(None, fence, 1, 0, 16, 16, 16, 1 << 20, None)
     assert e.value.code == L.LPS_EINVAL
+
+
+def test_cache_tile_layouts_match_the_documented_offsets():
+    """bf16 caches: K element (head j, row r, dim e) sits at
+    ((j * rows/16 + r/16) * hd/8 + e/8) * 128 + (r % 16) * 8 + e % 8, V at
+    ((j * rows/16 + r/16) * hd + e) * 16 + r % 16; the helpers round-trip
+    for numpy arrays and torch tensors."""
+    import torch
+    from layer_pipeline_stage_amd import layout
+    nkv, rows, hd = 3, 48, 16
+    x = np.arange(nkv * rows * hd).reshape(nkv, rows, hd)
+    kt, vt = layout.k_to_tiles(x), layout.v_to_tiles(x)
+    kf, vf = kt.reshape(-1), vt.reshape(-1)
+    for j, r, e in ((0, 0, 0), (1, 17, 3), (2, 47, 15), (2, 31, 8), (0, 5, 9)):
+        tile = j * (rows // 16) + r // 16
+        assert kf[(tile * (hd // 8) + e // 8) * 128 + (r % 16) * 8 + e % 8] == x[j, r, e]
+        assert vf[(tile * hd + e) * 16 + r % 16] == x[j, r, e]
+    assert np.array_equal(layout.k_from_tiles(kt), x)
+    assert np.array_equal(layout.v_from_tiles(vt), x)
+    xt = torch.from_numpy(x)
+    assert np.array_equal(layout.k_to_tiles(xt).numpy(), kt)
+    assert np.array_equal(layout.v_to_tiles(xt).numpy(), vt)
+    assert np.array_equal(layout.k_from_tiles(layout.k_to_tiles(xt)).numpy(), x)
+    assert np.array_equal(layout.v_from_tiles(layout.v_to_tiles(xt)).numpy(), x)

@@ -13,6 +13,7 @@ import pytest
 import torch
 
 import synth
+from layer_pipeline_stage_amd import layout
 from oracle import numerics as onum
 from oracle.decoder import rmsnorm, rope, attend, silu
 from oracle.moe import softmax, top_k, f16_pieces_to_f32
@@ -195,13 +196,22 @@ ATTN_CASES = [
 
 @pytest.mark.parametrize("nq,nkv,hd,kvd,ns", ATTN_CASES)
 def test_attention_parity(L, nq, nkv, hd, kvd, ns):
+    """Split-context attention against the oracle's softmax; bf16 caches hold V
+    transposed.  The rows past the longest context hold NaN: no row at or past
+    n_rows may reach the result."""
     ctx_max = max(ns) + 3
+    if kvd == "bf16":
+        ctx_max = (ctx_max + 15) // 16 * 16
     rng = np.random.default_rng(nq * hd)
     K32 = rng.standard_normal((nkv, ctx_max, hd)).astype(np.float32)
     V32 = rng.standard_normal((nkv, ctx_max, hd)).astype(np.float32)
     Ks = K32 if kvd == "f32" else synth.bf16_bits(K32)
     Vs = V32 if kvd == "f32" else synth.bf16_bits(V32)
-    Kd, Vd = dev(Ks), dev(Vs)
+    nan = np.float32(np.nan) if kvd == "f32" else np.uint16(0x7FC0)
+    Ks[:, max(ns):] = nan
+    Vs[:, max(ns):] = nan
+    Kd = dev(Ks if kvd == "f32" else layout.k_to_tiles(Ks))
+    Vd = dev(Vs if kvd == "f32" else layout.v_to_tiles(Vs))
     sb = L.lps_attention_scratch_bytes(nq, nkv, hd, ctx_max)
     scratch = torch.zeros(sb, dtype=torch.uint8, device=DEV)
     Kw, Vw = onum.widen_cache(Ks, kvd), onum.widen_cache(Vs, kvd)
@@ -239,14 +249,19 @@ def _layer_desc(L, cfg, t):
 
 @pytest.mark.parametrize("cfg", [synth.TINY, synth.DecoderConfig(
     "qkv-bf16", n_layers=1, d=512, nq=8, nkv=2, hd=128, ff=256, vocab=0, wdtype="bf16",
-    kvdtype="bf16", prefix=4, steps=4)])
+    kvdtype="bf16", prefix=28, steps=4)])
 def test_qkv_rope_append(L, cfg):
     m = synth.make_dense(cfg) if cfg.vocab or cfg.wdtype != "mxfp4" else None
     Lw = m["layers"][0]
     t = {k: dev(Lw[k]) for k in ("g_attn", "g_ffn", "w_qkv", "w_o", "w_gu", "w_d")}
     kvt = torch.float32 if cfg.kvdtype == "f32" else torch.int16
-    t["k"] = torch.zeros((cfg.nkv, cfg.ctx_max, cfg.hd), dtype=kvt, device=DEV)
-    t["v"] = torch.zeros_like(t["k"])
+    if cfg.kvdtype == "bf16":     # 16-row tiles
+        kshape = (cfg.nkv, cfg.ctx_max // 16, cfg.hd // 8, 16, 8)
+        vshape = (cfg.nkv, cfg.ctx_max // 16, cfg.hd, 16)
+    else:
+        kshape = vshape = (cfg.nkv, cfg.ctx_max, cfg.hd)
+    t["k"] = torch.zeros(kshape, dtype=kvt, device=DEV)
+    t["v"] = torch.zeros(vshape, dtype=kvt, device=DEV)
     desc = _layer_desc(L, cfg, t)
     rng = np.random.default_rng(8)
     W = onum.widen_weight(Lw["w_qkv"], cfg.wdtype)
@@ -266,6 +281,8 @@ def test_qkv_rope_append(L, cfg):
         assert np.max(np.abs(qd.cpu().numpy().reshape(nq, hd) - q)) <= tol
         kc = t["k"].cpu().numpy()
         vc = t["v"].cpu().numpy()
+        if cfg.kvdtype == "bf16":
+            kc, vc = layout.k_from_tiles(kc), layout.v_from_tiles(vc)
         if cfg.kvdtype == "bf16":
             kc, vc = kc.view(np.uint16), vc.view(np.uint16)
         kg = onum.widen_cache(kc[:, pos], cfg.kvdtype)
