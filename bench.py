@@ -5,9 +5,11 @@ Workload: the dense 8B-class slice (bf16 weights ~N(0, 0.02), f32 hidden;
 batch-1 greedy decode with a seeded 4096-row random bf16 KV prefix per layer,
 split into N = 4 stages (even split) on one GPU, deferred logits readback.
 A step is one token through all four stages and the LM head (+ argmax on the
-device, which feeds the next step's embedding).
+device, which feeds the next step's embedding).  By default the whole step is
+captured once as a graph and replayed (position, step and next id advanced on
+the device); --mode eager launches every kernel from the host instead.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--mode graph|eager] [--no-cpu]
 
 Prints one JSON line: decode tokens/s, the algorithmic HBM bytes per token
 turned into GB/s and a fraction of MI355X's 8 TB/s, the dominant kernel's
@@ -52,11 +54,11 @@ def algorithmic_bytes(cfg, n_rows: int) -> dict:
 
 
 # HBM traffic of the gate/up GEMV measured by rocprofv3 PMC counters (FETCH_SIZE,
-# WRITE_SIZE, KiB per dispatch) on `python bench.py --no-cpu --steps 16 --warmup 2`,
+# WRITE_SIZE, KiB per dispatch) on `python bench.py --no-cpu --mode eager --steps 16 --warmup 2`,
 # scaled by what the same counters read for the 256 MiB calibration copy
 # (`python bench.py --copy-calibration`: FETCH x 2.0, WRITE x 1.0).  Valid only for
 # the kernel sources it was taken on (hash below); otherwise reported as null.
-GATEUP_TRAFFIC = {"src_sha256_16": "e439d65a1aa211d8", "fetch_kib": 114863.65, "write_kib": 112.03,
+GATEUP_TRAFFIC = {"src_sha256_16": "e7b17313defd0fdb", "fetch_kib": 114863.66, "write_kib": 112.03,
                   "fetch_scale": 2.0, "write_scale": 1.0}
 GEMV_SOURCES = ("layer_pipeline_stage_amd/csrc/gemv.hip", "layer_pipeline_stage_amd/csrc/gemv_core.h",
                 "layer_pipeline_stage_amd/csrc/dev.h")

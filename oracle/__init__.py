@@ -9,9 +9,9 @@ seeded input arrays made by ``synth``.
 What it computes is the plain definition of the decode forward that the
 pages' staged runtime must reproduce bit for bit: the stages, boundary slots,
 FP16 pieces and deferred readback change scheduling, not arithmetic (memra
-``pp`` module docs, header: "scheduling changes, math does not"; strata
-PR #3648, Approach: exact FP16->FP32 conversion with the additions in their
-order).  Everything is evaluated in float64 over the stored operands; the
+``pp`` module docs, header: the deferred arm moves when work runs, not what
+it computes; strata PR #3648, Approach: exact FP16->FP32 conversion with the
+additions in their order).  Everything is evaluated in float64 over the stored operands; the
 rounding points are the storage formats the path itself uses: f32 for the
 residual stream, the cache dtype for K/V rows, f16 for the remote MoE partial
 sums, bf16 for the inputs of the prefill grouped GEMM.
