@@ -19,7 +19,8 @@ sums, bf16 for the inputs of the prefill grouped GEMM.
 Modules
   plan      stage fence, even split / explicit cuts / per-stage counts, stage_of
   numerics  widening of bf16 / f16 / MXFP4 (e2m1 + e8m0) operands, storage roundings
-  decoder   RMSNorm, RoPE, GQA attention, SwiGLU, dense/MXFP4 layer, head, staged walk
+  decoder   RMSNorm, RoPE, GQA attention, SwiGLU, dense/MXFP4 layer, head, staged walk,
+            chunked prefill in matrix form (causal mask, bf16 matrix-core operands)
   moe       router softmax + top-k, experts, fixed-order local/remote sums, FP16 pieces
 
 Pins (each checked by a CPU test against something other than this code):
@@ -27,7 +28,10 @@ Pins (each checked by a CPU test against something other than this code):
   numerics  bf16/f16 against torch's and numpy's own converters; the OCP MX
             v1.0 e2m1 value table and the e8m0 special values (exact)
   decoder   RMSNorm / RoPE / attention special cases and brute force on tiny
-            shapes; staged == unstaged bit for bit; padded == unpadded bit
+            shapes; the prefill matrix form (exact operands) equals the decode
+            steps, chunk and stage splits change nothing, and a planted
+            off-by-one mask is caught; bf16 operand rounding against torch;
+            staged == unstaged bit for bit; padded == unpadded bit
             for bit; a one-token closed form of a whole layer
   moe       top-k against exhaustive subset search; FP16 pieces == one piece
             and aliased == separate combine, bit for bit

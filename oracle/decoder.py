@@ -16,6 +16,15 @@ output gate; RMSNorm y = x / sqrt(mean(x^2) + eps) * g; RoPE rotates the pairs
 (i, i + hd/2) of every q and k head by p * base^(-2i/hd) at the 0-based
 position p; attention is causal over rows 0..p after row p is written, scaled
 by 1/sqrt(hd); silu(z) = z / (1 + e^-z); the argmax takes the first maximum.
+
+Chunked prefill (memra ``pp`` module docs, functions on the prime split; ninfer
+pipeline stages, What is not covered yet: a prefill chunk runs through the
+stages in turn): a chunk of T prompt rows goes through each layer as whole-chunk
+matrix products; its K and V rows are stored first and each row attends
+causally.  Where the pages leave the precision open, the operands the matrix
+cores take are rounded to bf16 (the normed rows, the attention output, the
+SwiGLU output), everything else is as in decode.  With those roundings off the
+matrix form reproduces the decode steps exactly (pinned in the tests).
 """
 from __future__ import annotations
 
@@ -23,7 +32,8 @@ import math
 
 import numpy as np
 
-from .numerics import (to_f32, round_cache, widen_cache, widen_weight)
+from .numerics import (to_f32, round_cache, widen_cache, widen_weight, bf16_to_f64,
+                       f32_to_bf16_bits)
 from .plan import stage_plan
 
 
@@ -62,6 +72,32 @@ def attend(q, K, V):
 
 def silu(z):
     return z / (1.0 + np.exp(-z))
+
+
+def bf16_act(x64):
+    """An activation as a matrix-core operand: f64 -> f32 -> bf16 (nearest even),
+    returned widened to f64."""
+    return bf16_to_f64(f32_to_bf16_bits(to_f32(x64)))
+
+
+def causal_attend(Q, K, V, p0):
+    """Causal attention over a chunk in matrix form.  Q [T, nq, hd] (rows at
+    positions p0 .. p0+T-1); K, V [nkv, p0+T, hd].  Row t sees cache rows
+    0 .. p0+t: S = Q K^T / sqrt(hd) with the rows past p0+t masked out, a row
+    softmax, O = P V.  Returns O [T, nq, hd]."""
+    T, nq, hd = Q.shape
+    nkv, n, _ = K.shape
+    G = nq // nkv
+    visible = np.arange(n)[None, :] <= (p0 + np.arange(T))[:, None]     # [T, n]
+    O = np.empty((T, nq, hd), dtype=np.float64)
+    for h in range(nq):
+        g = h // G
+        S = (Q[:, h, :] @ K[g].T) / math.sqrt(hd)
+        S = np.where(visible, S, -np.inf)
+        W = np.exp(S - S.max(axis=1, keepdims=True))
+        W /= W.sum(axis=1, keepdims=True)
+        O[:, h, :] = W @ V[g]
+    return O
 
 
 def matvec_grouped(W, h, group=32):
@@ -169,6 +205,61 @@ class Decoder:
         gu = self.mv(l, "w_gu", h2)
         mm = silu(gu[:c.ff]) * gu[c.ff:]
         return to_f32(x + self.mv(l, "w_d", mm))
+
+    # ---- a prefill chunk (matrix form) -----------------------------------------
+    def layer_prefill(self, l, X32, p0, act=bf16_act):
+        """One layer over a chunk of T prompt rows at positions p0 .. p0+T-1,
+        written as the whole-chunk matrix products.  The chunk's K and V rows
+        are rotated and stored first; each row then attends causally.  `act`
+        rounds the operands the matrix cores take in prefill: the normed rows,
+        the attention output and the SwiGLU output (bf16); the residual stays
+        f32 between sublayers, every sum is f64.  act=None keeps them exact,
+        which must reproduce the decode steps row by row."""
+        act = act or (lambda a: a)
+        c = self.cfg
+        L = self.m["layers"][l]
+        nq, nkv, hd = c.nq, c.nkv, c.hd
+        X = np.asarray(X32, dtype=np.float32).astype(np.float64)
+        T = X.shape[0]
+        H = act(rmsnorm(X, L["g_attn"], c.eps))
+        QKV = H @ self.W(l, "w_qkv").T                                   # [T, N]
+        Q = np.stack([rope(QKV[t, :nq * hd].reshape(nq, hd), p0 + t, c.rope_base)
+                      for t in range(T)])
+        Kn = np.stack([rope(QKV[t, nq * hd:(nq + nkv) * hd].reshape(nkv, hd), p0 + t,
+                            c.rope_base) for t in range(T)])
+        Vn = QKV[:, (nq + nkv) * hd:].reshape(T, nkv, hd)
+        self.K[l][:, p0:p0 + T] = round_cache(Kn.transpose(1, 0, 2), c.kvdtype)
+        self.V[l][:, p0:p0 + T] = round_cache(Vn.transpose(1, 0, 2), c.kvdtype)
+        Kc = widen_cache(self.K[l][:, :p0 + T], c.kvdtype)
+        Vc = widen_cache(self.V[l][:, :p0 + T], c.kvdtype)
+        O = causal_attend(Q, Kc, Vc, p0).reshape(T, nq * hd)
+        X = to_f32(X + act(O) @ self.W(l, "w_o").T).astype(np.float64)
+        H2 = act(rmsnorm(X, L["g_ffn"], c.eps))
+        GU = H2 @ self.W(l, "w_gu").T
+        M = act(silu(GU[:, :c.ff]) * GU[:, c.ff:])
+        return to_f32(X + M @ self.W(l, "w_d").T)
+
+    def prefill(self, ids, p0=None, fence=None, act=bf16_act):
+        """A chunk of prompt ids through every stage from position p0 (default:
+        just after the cache prefix): embedding rows, each stage's layers over
+        the whole chunk, the [T, d] f32 hidden through a slot between stages,
+        then the head on the last row.  Returns (last logits, argmax, hidden
+        rows [T, d] of the last stage)."""
+        c = self.cfg
+        p = c.prefix if p0 is None else p0
+        if fence is None:
+            fence = stage_plan(c.n_layers, 1)
+        n = len(fence) - 1
+        X = np.stack([self.embed(t) for t in ids])
+        for s in range(n):
+            for l in range(fence[s], fence[s + 1]):
+                X = self.layer_prefill(l, X, p, act)
+            self.counters["stage_walks"] += 1
+            if s < n - 1:
+                X = X.copy()
+                self.counters["boundary_crossings"] += 1
+        logits, a = self.head(X[-1])
+        return logits, a, X
 
     # ---- stages, embedding, head --------------------------------------------
     def embed(self, tok):

@@ -296,3 +296,81 @@ def test_mxfp4_row_blocks_equal_whole_matrix():
     x = pm["x_in"][0]
     h = rmsnorm(x.astype(np.float64), pm["layers"][0]["g_attn"], SMALL_PAD.eps)
     assert np.array_equal(a.mv(0, "w_gu", h), b._mv_mxfp4_rows(0, "w_gu", h, rows=7))
+
+
+# ---- chunked prefill (matrix form) -------------------------------------------------
+PF_BF16 = synth.DecoderConfig("pf-bf16", n_layers=3, d=64, nq=4, nkv=2, hd=16, ff=96, vocab=64,
+                              wdtype="bf16", kvdtype="bf16", prefix=5, prompt=8, steps=0)
+
+
+@pytest.mark.parametrize("cfg", [replace(SMALL8, prefix=4, prompt=7, steps=0), PF_BF16])
+def test_prefill_matrix_form_equals_decode_steps(cfg):
+    """With exact operands (act=None) the whole-chunk matrix form — all K/V rows
+    of the chunk stored first, then a causal mask — reproduces the decode steps
+    fed one id at a time: same last logits, same cache rows."""
+    m = synth.make_tiny(cfg) if cfg.vocab == 1024 else synth.make_dense(cfg)
+    a, b = Decoder(m), Decoder(m)
+    lg, am, X = a.prefill(m["prompt"], act=None)
+    _, dam, dlg = b.greedy(m["prompt"], 0)
+    assert am == dam[-1]
+    assert np.max(np.abs(lg - dlg[-1])) <= 1e-12 * np.abs(dlg[-1]).max()
+    for l in range(cfg.n_layers):
+        assert np.array_equal(a.K[l], b.K[l]) and np.array_equal(a.V[l], b.V[l])
+
+
+def test_prefill_chunks_equal_one_chunk_and_stages_equal_one_stage():
+    """Splitting the prompt into chunks (each from its own position) or the
+    layers into stages changes nothing: rows interact only through the cache,
+    causally."""
+    m = synth.make_dense(PF_BF16)
+    ids = m["prompt"]
+    ref = Decoder(m)
+    lg, am, X = ref.prefill(ids)
+    for chunks in ([3, 5], [1, 1, 6], [7, 1]):
+        d = Decoder(m)
+        p = PF_BF16.prefix
+        for n in chunks:
+            lgc, amc, Xc = d.prefill(ids[:n], p0=p)
+            ids, p = ids[n:], p + n
+        assert amc == am and np.max(np.abs(lgc - lg)) <= 1e-12 * np.abs(lg).max(), chunks
+        ids = m["prompt"]
+    for fence in ([0, 1, 3], [0, 1, 2, 3]):
+        d = Decoder(m)
+        lgs, ams, Xs = d.prefill(ids, fence=fence)
+        assert np.array_equal(lgs, lg) and np.array_equal(Xs, X)
+
+
+def test_prefill_pin_catches_an_off_by_one_mask(monkeypatch):
+    """The decode comparison is not vacuous: a prefill whose row t also sees
+    row p0+t+1 (a planted off-by-one in the oracle) misses it by far."""
+    import oracle.decoder as od
+    m = synth.make_dense(PF_BF16)
+    _, _, dlg = Decoder(m).greedy(m["prompt"], 0)
+    real = od.causal_attend
+
+    def leaky(Q, K, V, p0):
+        T = Q.shape[0]
+        n = K.shape[1]
+        out = np.empty_like(Q)
+        for t in range(T):
+            vis = min(n, p0 + t + 2)
+            out[t] = real(Q[t:t + 1], K[:, :vis], V[:, :vis], vis - 1)[0]
+        return out
+
+    monkeypatch.setattr(od, "causal_attend", leaky)
+    lg, _, _ = Decoder(m).prefill(m["prompt"], act=None)
+    assert np.max(np.abs(lg - dlg[-1])) > 1e-3 * np.abs(dlg[-1]).max()
+
+
+def test_bf16_activation_rounding():
+    """bf16_act rounds to nearest even through f32, as the f32 -> bf16 convert
+    of the matrix-core operands does (torch's conversion as the reference)."""
+    import torch
+    from oracle.decoder import bf16_act
+    rng = np.random.default_rng(3)
+    x = np.concatenate([rng.standard_normal(4096) * 10.0 ** rng.integers(-6, 6, 4096),
+                        [1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -0.0, 2 ** -130]])
+    want = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(bf16_act(x), want)
+    assert bf16_act(np.array([1.0 + 2 ** -8]))[0] == 1.0           # tie -> even
+    assert bf16_act(np.array([1.0 + 3 * 2 ** -8]))[0] == 1.0 + 2 ** -6
