@@ -160,6 +160,31 @@ size_t lps_model_scratch_bytes(const lps_model* m);
 int lps_stage_forward(const lps_model* m, const int32_t* fence, int32_t n_stages, int32_t stage,
                       float* x, int32_t pos, void* scratch, size_t scratch_bytes, void* stream);
 
+/* ---- chunked dense prefill through the stages -------------------------------
+ * memra pp module docs (functions on the prime split: the chunked prompt walk
+ * takes the same per-stage layer ranges as decode) and ninfer pipeline stages
+ * (What is not covered yet: a prefill chunk runs through the stages in turn).
+ * lps_stage_prefill walks layers [fence[stage], fence[stage+1]) over the T rows
+ * of x (dev [T, d] f32, in place) at positions p0 .. p0 + T - 1: per layer the
+ * rows' RMSNorm, the QKV, O, gate/up and down products as bf16 GEMMs on the
+ * matrix cores (the normed rows, the attention output and the SwiGLU output
+ * are rounded to bf16 as their inputs; f32 accumulation and residual), RoPE
+ * from the layer's rope_cs table, the chunk's K and V rows appended to the
+ * caches, and causal attention of row t over cache rows 0 .. p0 + t.  Bumps
+ * the prefill_walks counter.  Needs bf16 weights and bf16 caches, 1, 2, 4 or 8
+ * q heads per kv head, d % 256 == 0, (nq + 2 nkv) hd % 256 == 0, nq hd % 128
+ * == 0, ff % 128 == 0, rope_cs, p0 + T <= ctx_max (LPS_EUNSUP / LPS_EINVAL /
+ * LPS_ERANGE otherwise, before anything is enqueued).  scratch (dev) of at
+ * least lps_prefill_scratch_bytes(m, T) bytes, contents irrelevant. */
+size_t lps_prefill_scratch_bytes(const lps_model* m, int32_t T);
+int lps_stage_prefill(const lps_model* m, const int32_t* fence, int32_t n_stages, int32_t stage,
+                      float* x, int32_t T, int32_t p0, void* scratch, size_t scratch_bytes,
+                      void* stream);
+/* x rows (dev [T, d] f32) = E[tok[t]] for the T ids tok (dev int32), as lps_embed
+ * (an id outside [0, vocab) writes a NaN row); 1 <= T <= 65535. */
+int lps_embed_rows(const void* table, int32_t wdtype, int32_t vocab, int32_t d, const int32_t* tok,
+                   int32_t T, float* x, void* stream);
+
 /* ---- device-position walk, step state and whole-pass graphs ----------------
  * ninfer pipeline stages, How it works (StageLink): the small control values
  * the layers read (the position among them) travel as device data, and decode
@@ -404,6 +429,7 @@ typedef struct lps_counters_t {
   int64_t boundary_recvs;
   int64_t pieces;          /* FP16 pieces converted by lps_moe_combine */
   int64_t drains;          /* pendings waited or dropped */
+  int64_t prefill_walks;   /* lps_stage_prefill calls that enqueued work */
 } lps_counters_t;
 int lps_counters(lps_counters_t* out);
 int lps_counters_reset(void);

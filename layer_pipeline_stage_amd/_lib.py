@@ -54,7 +54,8 @@ class MoEDesc(C.Structure):
 
 class Counters(C.Structure):
     _fields_ = [("stage_walks", C.c_int64), ("boundary_sends", C.c_int64),
-                ("boundary_recvs", C.c_int64), ("pieces", C.c_int64), ("drains", C.c_int64)]
+                ("boundary_recvs", C.c_int64), ("pieces", C.c_int64), ("drains", C.c_int64),
+                ("prefill_walks", C.c_int64)]
 
 
 P = C.c_void_p
@@ -80,6 +81,9 @@ SIGS = {
     "lps_model_scratch_bytes": (SZ, [P], False),
     "lps_stage_forward": (C.c_int, [P, PI32, I32, I32, P, I32, P, SZ, P], True),
     "lps_stage_forward_dpos": (C.c_int, [P, PI32, I32, I32, P, P, P, SZ, P], True),
+    "lps_prefill_scratch_bytes": (SZ, [P, I32], False),
+    "lps_stage_prefill": (C.c_int, [P, PI32, I32, I32, P, I32, I32, P, SZ, P], True),
+    "lps_embed_rows": (C.c_int, [P, I32, I32, I32, P, I32, P, P], True),
     "lps_rope_table": (C.c_int, [I32, F32, I32, P], True),
     "lps_step_advance": (C.c_int, [P, I32, P, P, P, I32, P, I32, P, I32, P, P], True),
     "lps_graph_begin": (C.c_int, [P], True),

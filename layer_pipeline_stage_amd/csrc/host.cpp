@@ -2,6 +2,7 @@
 // slots, deferred logits readback, the model handle and the layer / stage walks.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 #include <cstdarg>
@@ -25,7 +26,9 @@ int fail(int code, const char* fmt, ...) {
 }
 void clear_error() { g_err[0] = 0; }
 
-static std::atomic<long long> c_walks{0}, c_sends{0}, c_recvs{0}, c_pieces{0}, c_drains{0};
+static std::atomic<long long> c_walks{0}, c_sends{0}, c_recvs{0}, c_pieces{0}, c_drains{0},
+    c_prefill{0};
+void count_prefill_walk() { c_prefill.fetch_add(1, std::memory_order_relaxed); }
 void count_stage_walk() { c_walks.fetch_add(1, std::memory_order_relaxed); }
 void count_send() { c_sends.fetch_add(1, std::memory_order_relaxed); }
 void count_recv() { c_recvs.fetch_add(1, std::memory_order_relaxed); }
@@ -385,6 +388,7 @@ int lps_counters(lps_counters_t* out) {
   out->boundary_recvs = c_recvs.load();
   out->pieces = c_pieces.load();
   out->drains = c_drains.load();
+  out->prefill_walks = c_prefill.load();
   return LPS_OK;
 }
 int lps_counters_reset(void) {
@@ -393,6 +397,7 @@ int lps_counters_reset(void) {
   c_recvs = 0;
   c_pieces = 0;
   c_drains = 0;
+  c_prefill = 0;
   return LPS_OK;
 }
 
@@ -493,6 +498,53 @@ int lps_stage_forward_dpos(const lps_model* m, const int32_t* fence, int32_t n_s
   }
   count_stage_walk();
   return LPS_OK;
+}
+
+size_t lps_prefill_scratch_bytes(const lps_model* m, int32_t T) {
+  if (!m || T < 1) return 0;
+  size_t mx = 0;
+  for (const auto& L : m->layers) mx = std::max(mx, prefill_scratch(&L, T).total);
+  return mx;
+}
+
+int lps_stage_prefill(const lps_model* m, const int32_t* fence, int32_t n_stages, int32_t stage,
+                      float* x, int32_t T, int32_t p0, void* scratch, size_t scratch_bytes,
+                      void* stream) {
+  LPS_REQUIRE(m, LPS_EINVAL, "lps_stage_prefill: null model");
+  int rc = check_fence(fence, n_stages, int32_t(m->layers.size()), "lps_stage_prefill");
+  if (rc) return rc;
+  LPS_REQUIRE(stage >= 0 && stage < n_stages, LPS_ERANGE,
+              "lps_stage_prefill: stage %d outside [0, %d)", stage, n_stages);
+  LPS_REQUIRE(x && scratch, LPS_EINVAL, "lps_stage_prefill: null x or scratch");
+  LPS_REQUIRE(aligned16(x) && aligned16(scratch), LPS_EINVAL,
+              "lps_stage_prefill: x and scratch must be 16-byte aligned");
+  LPS_REQUIRE(T >= 1, LPS_EINVAL, "lps_stage_prefill: T %d < 1", T);
+  for (int l = fence[stage]; l < fence[stage + 1]; ++l) {
+    char who[64];
+    snprintf(who, sizeof who, "lps_stage_prefill(layer %d)", l);
+    rc = check_prefill_layer(&m->layers[l], T, p0, who);
+    if (rc) return rc;
+  }
+  const size_t need = lps_prefill_scratch_bytes(m, T);
+  LPS_REQUIRE(scratch_bytes >= need, LPS_EINVAL, "lps_stage_prefill: scratch %zu < %zu needed",
+              scratch_bytes, need);
+  hipStream_t st = as_stream(stream);
+  for (int l = fence[stage]; l < fence[stage + 1]; ++l) {
+    rc = prefill_layer(&m->layers[l], x, T, p0, scratch, st);
+    if (rc) return rc;
+  }
+  count_prefill_walk();
+  return LPS_OK;
+}
+
+int lps_embed_rows(const void* table, int32_t wdtype, int32_t vocab, int32_t d, const int32_t* tok,
+                   int32_t T, float* x, void* stream) {
+  LPS_REQUIRE(table && tok && x, LPS_EINVAL, "lps_embed_rows: null pointer");
+  LPS_REQUIRE(vocab > 0 && d > 0 && T >= 1 && T <= 65535, LPS_EINVAL,
+              "lps_embed_rows: vocab %d, d %d, T %d (1 .. 65535)", vocab, d, T);
+  LPS_REQUIRE(wdtype == LPS_F32 || wdtype == LPS_BF16, LPS_EINVAL,
+              "lps_embed_rows: table dtype %d (f32 or bf16 only)", wdtype);
+  return launch_embed_rows(table, wdtype, vocab, d, tok, T, x, as_stream(stream));
 }
 
 int lps_rope_table(int32_t hd, float rope_base, int32_t n_pos, float* host_out) {

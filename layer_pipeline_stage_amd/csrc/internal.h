@@ -100,6 +100,19 @@ int launch_step_advance(int32_t* state, int32_t pos_limit, const int32_t* argmax
                         const int32_t* feed, int32_t n_feed, int32_t* tok_hist, int32_t hist_cap,
                         const float* logits, int32_t vocab, float* logits_hist, hipStream_t st);
 
+// ---- chunked dense prefill (prefill.hip) ---------------------------------------------
+// scratch of one layer over T rows: bf16 rows [T, max(d, nq hd)] | qkv f32 | SwiGLU bf16
+struct PrefillScratch {
+  size_t xb, qkv, mb, total;
+};
+PrefillScratch prefill_scratch(const lps_layer_desc* L, int T);
+int check_prefill_layer(const lps_layer_desc* L, int T, int p0, const char* who);
+// one layer over the T rows of x [T, d] f32 (in place) at positions p0 .. p0 + T - 1
+int prefill_layer(const lps_layer_desc* L, float* x, int T, int p0, void* scratch, hipStream_t st);
+int launch_embed_rows(const void* table, int wdtype, int vocab, int d, const int32_t* tok, int T,
+                      float* x, hipStream_t st);
+void count_prefill_walk();
+
 // validation helpers shared by entry points
 int check_layer(const lps_layer_desc* L, const char* who);
 

@@ -1,0 +1,492 @@
+// Chunked dense prefill through a stage's layers on gfx950.
+//
+// memra pp module docs (functions on the prime split) and ninfer pipeline
+// stages (What is not covered yet): a prompt chunk runs through the stages in
+// turn, each stage walking its own layers over all T rows of the chunk.  Per
+// layer, each step its own launch, in stream order:
+//  1. rows: RMSNorm of every row, rounded to bf16 (the matrix-core operand);
+//  2. QKV GEMM [T, d] x [d, (nq + 2 nkv) hd] -> f32;
+//  3. RoPE of the q and k heads at positions p0 + t (cos / sin from the layer's
+//     table) and the chunk's K and V rows appended to the caches;
+//  4. causal attention of every row over cache rows 0 .. p0 + t on the matrix
+//     cores, the output rounded to bf16;
+//  5. O GEMM, residual add into x;
+//  6. rows: RMSNorm again, bf16;
+//  7. gate/up GEMM with SwiGLU in registers, rounded to bf16;
+//  8. down GEMM, residual add into x.
+// bf16 weights and bf16 caches (16-row tiles) only: the shapes of the dense
+// model whose prompts run through the stages.
+#include "dev.h"
+#include "internal.h"
+
+#include <cmath>
+
+namespace lps {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// ---- 1/6. per-row RMSNorm -> bf16 -------------------------------------------------------
+__global__ __launch_bounds__(256) void k_pf_rows_norm(const float* x, const float* g, float eps,
+                                                      int d, uint16_t* xb) {
+  const long long t = blockIdx.x;
+  const float* xr = x + t * d;
+  __shared__ float red[4];
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < d; i += 256) ss += xr[i] * xr[i];
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x / 64] = ss;
+  __syncthreads();
+  const float r = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / float(d) + eps);
+  for (int i = threadIdx.x; i < d; i += 256) xb[t * d + i] = f32_to_bf16(xr[i] * r * g[i]);
+}
+
+// ---- 2/5/7/8. dense GEMM on the matrix cores -----------------------------------------------
+// C[m, n] = sum_k A[m, k] B[n, k]; A [T, K] bf16 rows, B [N, K] bf16 weight rows.  A
+// 256 x 256 tile per workgroup of 8 waves (2 x 4), each wave 128 x 64 as 4 x 2 MFMA
+// 32x32x16 blocks; K in steps of 64 through two LDS buffers (rows padded to a
+// 144-byte stride), the global loads two steps ahead in two register sets, one
+// barrier per step, steps taken in pairs (K % 128 == 0).  Rows past T repeat row
+// T - 1 (valid memory, never stored).  Epilogues:
+//   GE_STORE   out[m, n] = C            (f32)
+//   GE_ADD     out[m, n] += C           (f32, the residual)
+//   GE_SWIGLU  out[m, j] = bf16(silu(C[m, j]) * C[m, ff + j]): a workgroup takes
+//              128 outputs, its B rows are 32 gate rows then the 32 matching up
+//              rows per wave column, so both land in the same lanes.
+enum { GE_STORE = 0, GE_ADD = 1, GE_SWIGLU = 2 };
+constexpr int DM = 256, DN = 256, DK = 64, DKP = DK + 8;
+constexpr int DG_THREADS = 512;
+
+struct DgP {
+  const uint16_t* a;
+  const uint16_t* b;
+  void* out;
+  int T, N, K;    // N: output columns (GE_SWIGLU: ff)
+};
+
+template <int EPI>
+__global__ __launch_bounds__(DG_THREADS) void k_dense_gemm(DgP p) {
+  constexpr int NJ = 4;
+  const int m0 = blockIdx.y * DM;
+  const int n0 = EPI == GE_SWIGLU ? blockIdx.x * (DN / 2) : blockIdx.x * DN;
+  const int K = p.K;
+  extern __shared__ __attribute__((aligned(16))) uint16_t dsm[];
+  uint16_t* As0 = dsm;
+  uint16_t* Bs0 = As0 + DM * DKP;
+  uint16_t* As1 = Bs0 + DN * DKP;
+  uint16_t* Bs1 = As1 + DM * DKP;
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid / 64;
+  const int wm = wv >> 2, wn = wv & 3;
+  const int scol = (tid & 7) * 8;
+  const long long abytes = (long long)p.T * K * 2;
+  const long long bbytes = (long long)(EPI == GE_SWIGLU ? 2 * p.N : p.N) * K * 2;
+  const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(p.a), (short)0, (int)abytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t bres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(p.b), (short)0, (int)bbytes, 0x00020000);
+  int aoff[NJ], boff[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int sr = (tid >> 3) + 64 * j;
+    const int r = min(m0 + sr, p.T - 1);
+    aoff[j] = (r * K + scol) * 2;
+    int wrow;
+    if constexpr (EPI == GE_SWIGLU) {
+      const int wc = sr >> 6, jj = (sr >> 5) & 1, cc = sr & 31;
+      wrow = (jj ? p.N : 0) + n0 + 32 * wc + cc;
+    } else {
+      wrow = n0 + sr;
+    }
+    boff[j] = (wrow * K + scol) * 2;
+  }
+  const int soff = (tid >> 3) * DKP + scol;
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+#define DG_LOAD(RA, RB, K0)                                                                       \
+  _Pragma("unroll") for (int j = 0; j < NJ; ++j) {                                                \
+    RA[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ares, aoff[j], 2 * (K0), 0)); \
+    RB[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(bres, boff[j], 2 * (K0), 2)); \
+  }
+#define DG_STORE(RA, RB, AS, BS)                                         \
+  _Pragma("unroll") for (int j = 0; j < NJ; ++j) {                       \
+    *reinterpret_cast<u32x4*>(AS + soff + 64 * j * DKP) = RA[j];         \
+    *reinterpret_cast<u32x4*>(BS + soff + 64 * j * DKP) = RB[j];         \
+  }
+#define DG_MMA(AS, BS)                                                                          \
+  _Pragma("unroll") for (int ks = 0; ks < DK / 16; ++ks) {                                       \
+    bf16x8 a[4], b[2];                                                                           \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                \
+      a[i] = *reinterpret_cast<const bf16x8*>(AS + (128 * wm + 32 * i + (lane & 31)) * DKP +      \
+                                              16 * ks + 8 * (lane >> 5));                        \
+    _Pragma("unroll") for (int j = 0; j < 2; ++j)                                                \
+      b[j] = *reinterpret_cast<const bf16x8*>(BS + (64 * wn + 32 * j + (lane & 31)) * DKP +       \
+                                              16 * ks + 8 * (lane >> 5));                        \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                \
+      _Pragma("unroll") for (int j = 0; j < 2; ++j)                                              \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);     \
+  }
+
+  const int nk = K / DK;
+  u32x4 ra0[NJ], rb0[NJ], ra1[NJ], rb1[NJ];
+  DG_LOAD(ra0, rb0, 0)
+  DG_LOAD(ra1, rb1, DK)
+  DG_STORE(ra0, rb0, As0, Bs0)
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    const int s2 = min(kt + 2, nk - 1), s3 = min(kt + 3, nk - 1);
+    DG_LOAD(ra0, rb0, s2 * DK)
+    DG_MMA(As0, Bs0)
+    DG_STORE(ra1, rb1, As1, Bs1)
+    __syncthreads();
+    DG_LOAD(ra1, rb1, s3 * DK)
+    DG_MMA(As1, Bs1)
+    DG_STORE(ra0, rb0, As0, Bs0)
+    __syncthreads();
+  }
+#undef DG_LOAD
+#undef DG_STORE
+#undef DG_MMA
+  // acc[i][j][r] is C[128 wm + 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4][col(j)]
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + 128 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (m < p.T) {
+        if constexpr (EPI == GE_SWIGLU) {
+          const int col = n0 + 32 * wn + (lane & 31);
+          const float v = silu(acc[i][0][r]) * acc[i][1][r];
+          static_cast<uint16_t*>(p.out)[(long long)m * p.N + col] = f32_to_bf16(v);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int col = n0 + 64 * wn + 32 * j + (lane & 31);
+            float* o = static_cast<float*>(p.out) + (long long)m * p.N + col;
+            if constexpr (EPI == GE_ADD) *o += acc[i][j][r];
+            else *o = acc[i][j][r];
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);   // one row at a time: short live ranges
+    }
+  }
+}
+
+// ---- 3. RoPE + K/V append for the chunk ------------------------------------------------------
+// qkv [T, (nq + 2 nkv) hd] f32 from the GEMM: q heads are rotated in place; k heads
+// rotated and v heads copied into cache row p0 + t (bf16, 16-row tiles).  One
+// thread per (row, head, pair i): elements i and i + hd/2.
+__global__ void k_pf_rope_append(float* qkv, int T, int nq, int nkv, int hd, int p0,
+                                 const float* rope_cs, int ctx_max, uint16_t* kc, uint16_t* vc) {
+  const int half = hd >> 1;
+  const int heads = nq + 2 * nkv;
+  const long long n = (long long)T * heads * half;
+  for (long long u = blockIdx.x * (long long)blockDim.x + threadIdx.x; u < n;
+       u += (long long)gridDim.x * blockDim.x) {
+    const int t = int(u / (heads * half));
+    const int rem = int(u - (long long)t * heads * half);
+    const int hh = rem / half, i = rem - hh * half;
+    const int pos = p0 + t;
+    float* row = qkv + (long long)t * heads * hd + (long long)hh * hd;
+    const float a0 = row[i], a1 = row[i + half];
+    float o0 = a0, o1 = a1;
+    if (hh < nq + nkv) {
+      const f32x2 cs = *reinterpret_cast<const f32x2*>(rope_cs + 2 * ((long long)pos * half + i));
+      o0 = a0 * cs.x - a1 * cs.y;
+      o1 = a0 * cs.y + a1 * cs.x;
+    }
+    if (hh < nq) {
+      row[i] = o0;
+      row[i + half] = o1;
+    } else {
+      const bool is_k = hh < nq + nkv;
+      const int g = is_k ? hh - nq : hh - nq - nkv;
+      const long long tile = (long long)g * (ctx_max >> 4) + (pos >> 4);
+      if (is_k) {
+        const long long off = (tile * (hd >> 3) + (i >> 3)) * 128 + (pos & 15) * 8 + (i & 7);
+        kc[off] = f32_to_bf16(o0);
+        kc[off + (long long)(half >> 3) * 128] = f32_to_bf16(o1);
+      } else {
+        const long long off = (tile * hd + i) * 16 + (pos & 15);
+        vc[off] = f32_to_bf16(o0);
+        vc[off + (long long)half * 16] = f32_to_bf16(o1);
+      }
+    }
+  }
+}
+
+// ---- 4. causal attention of the chunk on the matrix cores -----------------------------------
+// The decode tile kernel's products with 16 query columns per wave: a wave takes
+// kv head g and the 16 / G query rows t0 .. t0 + R - 1, column c = r G + j being
+// q head g G + j of row t0 + r.  It walks the key tiles (16 cache rows each) from
+// row 0 to its last row's position with an online softmax per column:
+//   S^T[16 keys, 16 cols] = K_tile . Q^T   (16x16x32 bf16, q as bf16 hi + lo)
+//   O^T[hd, 16 cols]     += V_tile^T . P^T (16x16x16 bf16, p as bf16 hi + lo)
+// where lane (col, grp) holds the scores of keys 4 grp .. 4 grp + 3 for column col,
+// exactly the B operand of the PV product.  Keys past a column's position are
+// masked.  The next tile's K and V loads go out before the current tile's
+// products.  The output o / l is rounded to bf16 for the O projection.
+struct PaP {
+  const float* q;          // [T, nq, hd] rotated (the q part of qkv: row stride qs)
+  const uint16_t* kc;      // tiled bf16 caches of the layer
+  const uint16_t* vc;
+  uint16_t* ob;            // [T, nq hd] bf16
+  int T, nq, nkv, p0, ctx_max, qs;
+  float scale;
+};
+
+constexpr int PA_WAVES = 4;
+
+template <int HD, int G>
+__global__ __launch_bounds__(PA_WAVES * WAVE) void k_pf_attn(PaP p) {
+  constexpr int KK = HD / 32, DT = HD / 16, R = 16 / G;
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
+  const int col = lane & 15, grp = lane >> 4;
+  const int g = blockIdx.y;
+  const int t0 = (blockIdx.x * PA_WAVES + w) * R;
+  if (t0 >= p.T) return;
+  const int r = col / G, hh = col - r * G;
+  const int t = min(t0 + r, p.T - 1);          // rows past T: duplicate a valid row, never stored
+  const bool tv = t0 + r < p.T;
+  const int pos = p.p0 + t;
+  const int last = p.p0 + min(t0 + R, p.T) - 1;  // the wave's last position
+  const int ntiles = (last >> 4) + 1;
+
+  // B operand of S^T: q of column col, dims 32 kk + 8 grp .. + 7, as bf16 hi + lo
+  const float* qrow = p.q + (long long)t * p.qs + (long long)(g * G + hh) * HD + 8 * grp;
+  bf16x8 qhi[KK], qlo[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    const f32x4 q0 = *reinterpret_cast<const f32x4*>(qrow + 32 * kk);
+    const f32x4 q1 = *reinterpret_cast<const f32x4*>(qrow + 32 * kk + 4);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = e < 4 ? q0[e] : q1[e - 4];
+      const __bf16 h = static_cast<__bf16>(v);
+      qhi[kk][e] = h;
+      qlo[kk][e] = static_cast<__bf16>(v - static_cast<float>(h));
+    }
+  }
+  const long long head = (long long)g * p.ctx_max * HD;     // elements before kv head g
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(p.kc + head), (short)0, p.ctx_max * HD * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(p.vc + head), (short)0, p.ctx_max * HD * 2, 0x00020000);
+
+  u32x4 kr0[KK], kr1[KK];
+  u32x2 vr0[DT], vr1[DT];
+#define PA_LOAD(KR, VR, J)                                                                       \
+  _Pragma("unroll") for (int kk = 0; kk < KK; ++kk)                                              \
+    KR[kk] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(                    \
+        krs, ((J) * 16 * HD + (4 * kk + grp) * 128 + col * 8) * 2, 0, 0));                       \
+  _Pragma("unroll") for (int dt = 0; dt < DT; ++dt)                                              \
+    VR[dt] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(                     \
+        vrs, ((J) * 16 * HD + (16 * dt + col) * 16 + 4 * grp) * 2, 0, 0));
+  // one key tile: the next tile's loads (into the other buffer) go out first
+#define PA_STEP(KR, VR, KN, VN, J)                                                               \
+  {                                                                                              \
+    PA_LOAD(KN, VN, min((J) + 1, ntiles - 1))                                                    \
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};                                                              \
+    _Pragma("unroll") for (int kk = 0; kk < KK; ++kk) {                                          \
+      const bf16x8 a = __builtin_bit_cast(bf16x8, KR[kk]);                                       \
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qhi[kk], s, 0, 0, 0);                       \
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qlo[kk], s, 0, 0, 0);                       \
+    }                                                                                            \
+    const int key0 = 16 * (J) + 4 * grp;                                                         \
+    float sv[4], mt = -INFINITY;                                                                 \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                              \
+      sv[i] = key0 + i <= pos ? s[i] * p.scale : -INFINITY;                                      \
+      mt = fmaxf(mt, sv[i]);                                                                     \
+    }                                                                                            \
+    mt = fmaxf(mt, __shfl_xor(mt, 16, WAVE));                                                    \
+    mt = fmaxf(mt, __shfl_xor(mt, 32, WAVE));                                                    \
+    const float mn = fmaxf(m, mt);                                                               \
+    const float alpha = m == -INFINITY ? 0.f : expf(m - mn);                                     \
+    float pv[4], ls = 0.f;                                                                       \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                              \
+      pv[i] = sv[i] == -INFINITY ? 0.f : expf(sv[i] - mn);                                       \
+      ls += pv[i];                                                                               \
+    }                                                                                            \
+    ls += __shfl_xor(ls, 16, WAVE);                                                              \
+    ls += __shfl_xor(ls, 32, WAVE);                                                              \
+    l = l * alpha + ls;                                                                          \
+    m = mn;                                                                                      \
+    i16x4 phi, plo;                                                                              \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                              \
+      const __bf16 h = static_cast<__bf16>(pv[i]);                                               \
+      phi[i] = __builtin_bit_cast(short, h);                                                     \
+      plo[i] = __builtin_bit_cast(short, static_cast<__bf16>(pv[i] - static_cast<float>(h)));    \
+    }                                                                                            \
+    _Pragma("unroll") for (int dt = 0; dt < DT; ++dt) {                                          \
+      const i16x4 a = __builtin_bit_cast(i16x4, VR[dt]);                                         \
+      f32x4 acc = o[dt] * alpha;                                                                 \
+      acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, phi, acc, 0, 0, 0);                     \
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, plo, acc, 0, 0, 0);                   \
+    }                                                                                            \
+  }
+
+  f32x4 o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;
+
+  PA_LOAD(kr0, vr0, 0)
+  for (int j = 0; j < ntiles; j += 2) {
+    PA_STEP(kr0, vr0, kr1, vr1, j)
+    if (j + 1 < ntiles) PA_STEP(kr1, vr1, kr0, vr0, j + 1)
+  }
+#undef PA_STEP
+#undef PA_LOAD
+  if (tv) {
+    const float inv = 1.0f / l;
+    uint16_t* dst = p.ob + (long long)t * p.nq * HD + (long long)(g * G + hh) * HD + 4 * grp;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const uint32_t lo = f32_to_bf16(o[dt][0] * inv) | (uint32_t)f32_to_bf16(o[dt][1] * inv) << 16;
+      const uint32_t hi = f32_to_bf16(o[dt][2] * inv) | (uint32_t)f32_to_bf16(o[dt][3] * inv) << 16;
+      *reinterpret_cast<u32x2*>(dst + 16 * dt) = u32x2{lo, hi};
+    }
+  }
+}
+
+// ---- host side ---------------------------------------------------------------------------
+static dim3 rows_grid(long long n) {
+  long long b = (n + 255) / 256;
+  return dim3((unsigned)(b < 8192 ? (b < 1 ? 1 : b) : 8192));
+}
+
+template <int EPI>
+static int gemm(const uint16_t* a, const uint16_t* b, void* out, int T, int N, int K, hipStream_t st) {
+  const size_t lds = size_t(2) * (DM + DN) * DKP * 2;
+  int rc = ensure_lds((const void*)k_dense_gemm<EPI>, lds);
+  if (rc) return rc;
+  DgP p{a, b, out, T, N, K};
+  const int nt = EPI == GE_SWIGLU ? N / (DN / 2) : N / DN;
+  hipLaunchKernelGGL((k_dense_gemm<EPI>), dim3(nt, (T + DM - 1) / DM), dim3(DG_THREADS), lds, st, p);
+  LPS_HIP(hipGetLastError());
+  return LPS_OK;
+}
+
+template <int HD>
+static int attn_hd(const PaP& p, int G, hipStream_t st) {
+  const int R = 16 / G;
+  const dim3 grid((p.T + PA_WAVES * R - 1) / (PA_WAVES * R), p.nkv);
+  switch (G) {
+    case 1: hipLaunchKernelGGL((k_pf_attn<HD, 1>), grid, dim3(PA_WAVES * WAVE), 0, st, p); break;
+    case 2: hipLaunchKernelGGL((k_pf_attn<HD, 2>), grid, dim3(PA_WAVES * WAVE), 0, st, p); break;
+    case 4: hipLaunchKernelGGL((k_pf_attn<HD, 4>), grid, dim3(PA_WAVES * WAVE), 0, st, p); break;
+    case 8: hipLaunchKernelGGL((k_pf_attn<HD, 8>), grid, dim3(PA_WAVES * WAVE), 0, st, p); break;
+    default: return fail(LPS_EUNSUP, "prefill attention: %d q heads per kv head (1, 2, 4, 8)", G);
+  }
+  LPS_HIP(hipGetLastError());
+  return LPS_OK;
+}
+
+PrefillScratch prefill_scratch(const lps_layer_desc* L, int T) {
+  PrefillScratch s{};
+  const int nqkv = (L->nq + 2 * L->nkv) * L->hd;
+  const int w = std::max(L->d, L->nq * L->hd);
+  s.xb = 0;                                            // [T, max(d, nq hd)] bf16 (normed rows, o)
+  s.qkv = align256(size_t(T) * w * 2);                 // [T, nqkv] f32
+  s.mb = s.qkv + align256(size_t(T) * nqkv * 4);       // [T, ff] bf16
+  s.total = s.mb + align256(size_t(T) * L->ff * 2);
+  return s;
+}
+
+int check_prefill_layer(const lps_layer_desc* L, int T, int p0, const char* who) {
+  LPS_REQUIRE(L->wdtype == LPS_BF16 && L->kvdtype == LPS_BF16, LPS_EUNSUP,
+              "%s: prefill runs bf16 weights with bf16 caches (got %d / %d)", who, L->wdtype,
+              L->kvdtype);
+  const int G = L->nq / L->nkv;
+  LPS_REQUIRE(G == 1 || G == 2 || G == 4 || G == 8, LPS_EUNSUP,
+              "%s: prefill attention needs 1, 2, 4 or 8 q heads per kv head (got %d)", who, G);
+  LPS_REQUIRE(L->hd == 64 || L->hd == 128 || L->hd == 256, LPS_EUNSUP, "%s: head dim %d", who, L->hd);
+  const int nqkv = (L->nq + 2 * L->nkv) * L->hd;
+  LPS_REQUIRE(L->d % 256 == 0 && nqkv % 256 == 0 && (L->nq * L->hd) % 128 == 0 &&
+                  L->ff % 128 == 0,
+              LPS_EUNSUP,
+              "%s: prefill GEMM tiles need d %% 256, (nq + 2 nkv) hd %% 256, nq hd %% 128 and "
+              "ff %% 128 == 0 (d %d, qkv %d, nq hd %d, ff %d)",
+              who, L->d, nqkv, L->nq * L->hd, L->ff);
+  LPS_REQUIRE(L->rope_cs, LPS_EINVAL, "%s: prefill needs the layer's rope_cs table", who);
+  LPS_REQUIRE(T >= 1 && p0 >= 0 && (long long)p0 + T <= L->ctx_max, LPS_ERANGE,
+              "%s: rows %d .. %d outside the cache [0, %d)", who, p0, p0 + T - 1, L->ctx_max);
+  const long long big = (long long)T * std::max({L->d, L->nq * L->hd, L->ff}) * 2;
+  LPS_REQUIRE(big < (1LL << 31) && (long long)2 * L->ff * L->d * 2 < (1LL << 31) &&
+                  (long long)nqkv * L->d * 2 < (1LL << 31),
+              LPS_EUNSUP, "%s: an operand of 2 GiB or more (32-bit offsets)", who);
+  return LPS_OK;
+}
+
+int prefill_layer(const lps_layer_desc* L, float* x, int T, int p0, void* scratch, hipStream_t st) {
+  const PrefillScratch s = prefill_scratch(L, T);
+  char* sc = static_cast<char*>(scratch);
+  uint16_t* xb = reinterpret_cast<uint16_t*>(sc + s.xb);
+  float* qkv = reinterpret_cast<float*>(sc + s.qkv);
+  uint16_t* mb = reinterpret_cast<uint16_t*>(sc + s.mb);
+  const int d = L->d, nqh = L->nq * L->hd, nqkv = (L->nq + 2 * L->nkv) * L->hd;
+  auto w = [](const void* v) { return static_cast<const uint16_t*>(v); };
+  hipLaunchKernelGGL(k_pf_rows_norm, dim3(T), dim3(256), 0, st, x, L->g_attn, L->eps, d, xb);
+  int rc = gemm<GE_STORE>(xb, w(L->w_qkv), qkv, T, nqkv, d, st);
+  if (rc) return rc;
+  hipLaunchKernelGGL(k_pf_rope_append, rows_grid((long long)T * (nqkv / 2)), dim3(256), 0, st, qkv,
+                     T, L->nq, L->nkv, L->hd, p0, L->rope_cs, L->ctx_max,
+                     static_cast<uint16_t*>(L->k_cache), static_cast<uint16_t*>(L->v_cache));
+  PaP pa{qkv, static_cast<const uint16_t*>(L->k_cache), static_cast<const uint16_t*>(L->v_cache),
+         xb, T, L->nq, L->nkv, p0, L->ctx_max, nqkv, 1.0f / sqrtf(float(L->hd))};
+  const int G = L->nq / L->nkv;
+  switch (L->hd) {
+    case 64: rc = attn_hd<64>(pa, G, st); break;
+    case 128: rc = attn_hd<128>(pa, G, st); break;
+    default: rc = attn_hd<256>(pa, G, st); break;
+  }
+  if (rc) return rc;
+  rc = gemm<GE_ADD>(xb, w(L->w_o), x, T, d, nqh, st);
+  if (rc) return rc;
+  hipLaunchKernelGGL(k_pf_rows_norm, dim3(T), dim3(256), 0, st, x, L->g_ffn, L->eps, d, xb);
+  rc = gemm<GE_SWIGLU>(xb, w(L->w_gu), mb, T, L->ff, d, st);
+  if (rc) return rc;
+  rc = gemm<GE_ADD>(mb, w(L->w_d), x, T, d, L->ff, st);
+  if (rc) return rc;
+  LPS_HIP(hipGetLastError());
+  return LPS_OK;
+}
+
+// x rows = E[tok[t]] widened to f32 (tokens read on the device; outside [0, vocab): NaN)
+template <int WT>
+__global__ void k_embed_rows(const void* table, int vocab, int d, const int32_t* tok, float* x) {
+  const int t = blockIdx.y;
+  const int id = tok[t];
+  const bool ok = id >= 0 && id < vocab;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < d; i += gridDim.x * blockDim.x) {
+    float v;
+    if (!ok) v = __uint_as_float(0x7FC00000u);
+    else if (WT == LPS_F32) v = static_cast<const float*>(table)[(long long)id * d + i];
+    else v = bf16_to_f32(static_cast<const uint16_t*>(table)[(long long)id * d + i]);
+    x[(long long)t * d + i] = v;
+  }
+}
+
+int launch_embed_rows(const void* table, int wdtype, int vocab, int d, const int32_t* tok, int T,
+                      float* x, hipStream_t st) {
+  const dim3 grid((d + 255) / 256, T);
+  if (wdtype == LPS_F32)
+    hipLaunchKernelGGL(k_embed_rows<LPS_F32>, grid, dim3(256), 0, st, table, vocab, d, tok, x);
+  else
+    hipLaunchKernelGGL(k_embed_rows<LPS_BF16>, grid, dim3(256), 0, st, table, vocab, d, tok, x);
+  LPS_HIP(hipGetLastError());
+  return LPS_OK;
+}
+
+}  // namespace lps

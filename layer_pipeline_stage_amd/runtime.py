@@ -204,9 +204,11 @@ class DeviceDecoder:
         torch.cuda.synchronize(dev)
 
     def _close_boundaries(self):
-        for b in getattr(self, "bounds", []):
+        for b in getattr(self, "bounds", []) + getattr(self, "_pf_bounds", []):
             lps.lps_boundary_destroy(b)
         self.bounds = []
+        self._pf_bounds = []
+        self._pf_key = None
 
     def reset(self):
         """Restore every cache to its seeded prefix (rows past it are rewritten
@@ -309,6 +311,71 @@ class DeviceDecoder:
             drain(i)
         fed = ids[:P] + [out_tok[i - 1] for i in range(P, total)]
         return StepResult(fed=fed, argmax=out_tok, logits=out_logits)
+
+    # ---- chunked prefill through the stages ----------------------------------------
+    def _prefill_buffers(self, T):
+        """Per-stage [T, d] hidden rows and prefill scratch, and boundaries whose
+        slots carry a whole chunk; rebuilt when the chunk size or fence changes."""
+        key = (T, tuple(self.fence))
+        if getattr(self, "_pf_key", None) == key:
+            return
+        cfg, dev, n = self.cfg, self.device, self.n_stages
+        for b in getattr(self, "_pf_bounds", []):
+            lps.lps_boundary_destroy(b)
+        self._pf_x = [torch.zeros((T, cfg.d), dtype=torch.float32, device=dev) for _ in range(n)]
+        nb = lps.lps_prefill_scratch_bytes(self.model, T)
+        self._pf_scratch = [torch.zeros(nb, dtype=torch.uint8, device=dev) for _ in range(n)]
+        self._pf_slots, self._pf_bounds = [], []
+        for _ in range(n - 1):
+            s0 = torch.zeros((T, cfg.d), dtype=torch.float32, device=dev)
+            s1 = torch.zeros_like(s0)
+            b = C.c_void_p()
+            lps.lps_boundary_create(T * cfg.d, ptr(s0), ptr(s1), C.byref(b))
+            self._pf_slots.append((s0, s1))
+            self._pf_bounds.append(b)
+        self._pf_step = 0
+        self._pf_key = key
+        torch.cuda.synchronize(dev)
+
+    def prefill(self, ids, chunk=None, p0=None):
+        """Feed the prompt ids as chunks of `chunk` rows (default: all at once)
+        from position p0 (default: right after the cache prefix), each chunk
+        through every stage in turn (a [T, d] f32 block per boundary), then the
+        head on the prompt's last row.  Returns (logits, argmax, last stage's
+        hidden rows of the last chunk)."""
+        cfg = self.cfg
+        assert self.head is not None, "model has no vocabulary"
+        ids = list(ids)
+        p = cfg.prefix if p0 is None else p0
+        chunk = len(ids) if chunk is None else chunk
+        assert ids and p + len(ids) <= cfg.ctx_max, "cache too short for this prompt"
+        self._prefill_buffers(chunk)
+        dev, n, st = self.device, self.n_stages, self.streams
+        tok_dev = torch.tensor(ids, dtype=torch.int32, device=dev)
+        torch.cuda.synchronize(dev)
+        T = 0
+        for c0 in range(0, len(ids), chunk):
+            T = min(chunk, len(ids) - c0)
+            lps.lps_embed_rows(ptr(self.embed), lps.DTYPES[cfg.wdtype], cfg.vocab, cfg.d,
+                               ptr(tok_dev) + 4 * c0, T, ptr(self._pf_x[0]), sp(st[0]))
+            k = self._pf_step
+            for s in range(n):
+                if s > 0:
+                    lps.lps_boundary_send(self._pf_bounds[s - 1], ptr(self._pf_x[s - 1]), k,
+                                          sp(st[s - 1]))
+                    lps.lps_boundary_recv(self._pf_bounds[s - 1], ptr(self._pf_x[s]), k, sp(st[s]))
+                lps.lps_stage_prefill(self.model, self._fence_c, n, s, ptr(self._pf_x[s]), T, p,
+                                      ptr(self._pf_scratch[s]), self._pf_scratch[s].numel(),
+                                      sp(st[s]))
+            self._pf_step += 1
+            p += T
+        last = ptr(self._pf_x[-1]) + 4 * cfg.d * (T - 1)
+        lps.lps_head_forward(C.byref(self.head), last, ptr(self.logits_ring[0]),
+                             ptr(self.tok_ring), ptr(self.head_scratch),
+                             self.head_scratch.numel(), sp(st[-1]))
+        torch.cuda.synchronize(dev)
+        return (self.logits_ring[0].cpu().numpy().copy(), int(self.tok_ring[0]),
+                self._pf_x[-1][:T].cpu().numpy().copy())
 
     # ---- the whole pass as one graph --------------------------------------------
     def _walk_dpos(self):

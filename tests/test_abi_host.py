@@ -221,6 +221,40 @@ def test_graph_and_device_state_entry_points_refuse_bad_arguments(L):
     with pytest.raises(L.LpsError) as e:
         L.lps_stage_forward_dpos(None, fence, 1, 0, 16, 16, 16, 1 << 20, None)
     assert e.value.code == L.LPS_EINVAL
+    with pytest.raises(L.LpsError) as e:
+        L.lps_stage_prefill(None, fence, 1, 0, 16, 4, 0, 16, 1 << 20, None)
+    assert e.value.code == L.LPS_EINVAL
+    assert L.lps_prefill_scratch_bytes(None, 4) == 0
+    for args in ((16, 1, 10, 8, 16, 0, 16), (16, 2, 10, 8, 16, 4, 16), (None, 1, 10, 8, 16, 4, 16)):
+        with pytest.raises(L.LpsError) as e:
+            L.lps_embed_rows(*args, None)           # T 0, wdtype MXFP4, null table
+        assert e.value.code == L.LPS_EINVAL
+
+
+def test_prefill_refuses_unsupported_layers_before_enqueue(L):
+    """A model handle over valid decode layers that the prefill cannot run
+    (f32 weights, a ragged ff) is refused by lps_stage_prefill with the layer
+    named, before any HIP call."""
+    import ctypes
+    d = L.LayerDesc()
+    d.d, d.nq, d.nkv, d.hd, d.ff = 256, 4, 2, 64, 704
+    d.wdtype, d.kvdtype, d.ctx_max = L.LPS_BF16, L.LPS_BF16, 64
+    d.eps, d.rope_base = 1e-6, 1e4
+    for k in ("g_attn", "g_ffn", "w_qkv", "w_o", "w_gu", "w_d", "k_cache", "v_cache", "rope_cs"):
+        setattr(d, k, 256)
+    h = ctypes.c_void_p()
+    L.lps_model_create(ctypes.byref(d), 1, ctypes.byref(h))
+    try:
+        assert L.lps_prefill_scratch_bytes(h, 8) > 0
+        fence = L.i32_array([0, 1])
+        with pytest.raises(L.LpsError) as e:        # ff 704 is not a multiple of 128
+            L.lps_stage_prefill(h, fence, 1, 0, 256, 8, 0, 256, 1 << 30, None)
+        assert e.value.code == L.LPS_EUNSUP and "layer 0" in str(e.value)
+        with pytest.raises(L.LpsError) as e:        # rows past the cache
+            L.lps_stage_prefill(h, fence, 1, 0, 256, 60, 8, 256, 1 << 30, None)
+        assert e.value.code in (L.LPS_EUNSUP, L.LPS_ERANGE)
+    finally:
+        L.lps_model_destroy(h)
 
 
 def test_cache_tile_layouts_match_the_documented_offsets():
