@@ -149,6 +149,41 @@ def _cpu_model():
     return "unknown"
 
 
+def prefill_bench(torch, synth, lps, runtime, T, stages, streams, reps):
+    """The dense slice's prompt path: a T-token chunk through the stages (bf16
+    GEMMs and causal attention on the matrix cores) after the 4096-row prefix,
+    timed from the first embedding to the last stage's output on the device
+    (reps runs after one warmup; the caches are reset between runs, untimed)."""
+    cfg = replace(synth.DENSE8B, prompt=T, steps=0)
+    model = synth.make_dense(cfg)
+    dd = runtime.DeviceDecoder(model, fence=lps.stage_plan(cfg.n_layers, stages), streams=streams)
+    ids = [int(t) for t in model["prompt"]]
+    dd.prefill(ids)
+    times = []
+    for _ in range(reps):
+        dd.reset()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        dd.prefill(ids, hidden=False)   # ends with a device synchronize and the logits readback
+        times.append(time.perf_counter() - t0)
+    dd.close()
+    dt = min(times)
+    c = cfg
+    wparams = (c.nq + 2 * c.nkv) * c.hd * c.d + c.d * c.nq * c.hd + 2 * c.ff * c.d + c.d * c.ff
+    gemm = 2.0 * T * wparams * c.n_layers
+    attn = 4.0 * c.n_layers * c.nq * c.hd * sum(c.prefix + t + 1 for t in range(T))
+    return {"metric": "prefill tokens/s (chunked prompt through the stages), 1 GPU",
+            "value": round(T / dt, 1), "unit": "tok/s", "ms_per_chunk": round(1e3 * dt, 3),
+            "tflops": round((gemm + attn) / dt / 1e12, 1), "gemm_tflop": round(gemm / 1e12, 3),
+            "attn_tflop": round(attn / 1e12, 3), "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"dense 8B-class slice prefill: {T}-token chunk after a "
+                                   f"4096-row prefix, {stages} stages ({streams} "
+                                   f"stream{'s' if streams == 'per-stage' else ''}), bf16 "
+                                   "matrix-core operands, timed from the host to the last "
+                                   "row's logits on the host",
+                       "chunk": T, "stages": stages}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -165,6 +200,9 @@ def main():
     ap.add_argument("--cpu-steps", type=int, default=2)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 256 MiB f32 device copy 8 times (reference for HBM counters)")
+    ap.add_argument("--prefill-only", type=int, default=0, metavar="T",
+                    help="only time the chunked prefill of a T-token prompt through the stages "
+                         "(one chunk, after the 4096-row prefix) and print one JSON line")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py: this path runs on one GPU (stages are streams of that GPU); "
@@ -192,6 +230,10 @@ def main():
         assert torch.equal(src, dst)
         print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n,
                           "launches": 8, "gbs": round(8 * n / dt / 1e9, 1)}))
+        return
+    if a.prefill_only:
+        print(json.dumps(prefill_bench(torch, synth, lps, runtime, a.prefill_only, a.stages,
+                                       a.streams, max(1, a.steps))), flush=True)
         return
     K, W = a.steps, a.warmup
     cfg = replace(synth.DENSE8B, steps=max(K, W, 128) - 1)

@@ -226,16 +226,21 @@ __global__ void k_pf_rope_append(float* qkv, int T, int nq, int nkv, int hd, int
 }
 
 // ---- 4. causal attention of the chunk on the matrix cores -----------------------------------
-// The decode tile kernel's products with 16 query columns per wave: a wave takes
-// kv head g and the 16 / G query rows t0 .. t0 + R - 1, column c = r G + j being
-// q head g G + j of row t0 + r.  It walks the key tiles (16 cache rows each) from
-// row 0 to its last row's position with an online softmax per column:
+// The decode tile kernel's products with 16 query columns per wave: a workgroup
+// takes kv head g and PA_WAVES * R query rows (R = 16 / G), wave w the rows
+// t0 + w R .. t0 + w R + R - 1, its column c = r G + j being q head g G + j of
+// row t0 + w R + r.  The workgroup walks the key tiles (16 cache rows each) from
+// row 0 to its last row's position; each tile of K and V is loaded from HBM / L2
+// once per workgroup into LDS (double-buffered through registers: tile j + 1 is
+// fetched while tile j is multiplied, one barrier per tile) and every wave forms,
+// with an online softmax per column (in base 2: the scale carries log2 e),
 //   S^T[16 keys, 16 cols] = K_tile . Q^T   (16x16x32 bf16, q as bf16 hi + lo)
 //   O^T[hd, 16 cols]     += V_tile^T . P^T (16x16x16 bf16, p as bf16 hi + lo)
-// where lane (col, grp) holds the scores of keys 4 grp .. 4 grp + 3 for column col,
-// exactly the B operand of the PV product.  Keys past a column's position are
-// masked.  The next tile's K and V loads go out before the current tile's
-// products.  The output o / l is rounded to bf16 for the O projection.
+// where lane (col, grp) holds the scores of keys 4 grp .. 4 grp + 3 for column
+// col, exactly the B operand of the PV product.  The tiles sit in LDS in the
+// caches' own order, so each wave's operand reads cover contiguous 1 KiB / 512 B
+// (no bank conflicts).  Keys past a column's position are masked.  The output
+// o / l is rounded to bf16 for the O projection.
 struct PaP {
   const float* q;          // [T, nq, hd] rotated (the q part of qkv: row stride qs)
   const uint16_t* kc;      // tiled bf16 caches of the layer
@@ -245,23 +250,35 @@ struct PaP {
   float scale;
 };
 
-constexpr int PA_WAVES = 4;
+constexpr int PA_WAVES = 8;
+constexpr int PA_THREADS = PA_WAVES * WAVE;
+#ifndef LPS_PA_KT
+#define LPS_PA_KT 4
+#endif
+constexpr int PA_KT = LPS_PA_KT;   // 16-row key tiles per step (one softmax update, one barrier)
 
 template <int HD, int G>
-__global__ __launch_bounds__(PA_WAVES * WAVE) void k_pf_attn(PaP p) {
+__global__ __launch_bounds__(PA_THREADS) void k_pf_attn(PaP p) {
   constexpr int KK = HD / 32, DT = HD / 16, R = 16 / G;
-  const int lane = threadIdx.x & (WAVE - 1);
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
+  constexpr int TILE = 16 * HD;                 // elements of one K (or V) 16-row tile
+  constexpr int NT = PA_KT;                     // tiles per step
+  constexpr int CH = 2 * NT * TILE / 8;         // 16-byte chunks of a step's K + V tiles
+  constexpr int LPT = (CH + PA_THREADS - 1) / PA_THREADS;   // chunks per thread
+  extern __shared__ __attribute__((aligned(16))) uint16_t kv_lds[];   // [2][K tiles | V tiles]
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
   const int col = lane & 15, grp = lane >> 4;
   const int g = blockIdx.y;
-  const int t0 = (blockIdx.x * PA_WAVES + w) * R;
-  if (t0 >= p.T) return;
+  const int tb = blockIdx.x * PA_WAVES * R;     // the workgroup's first row
   const int r = col / G, hh = col - r * G;
-  const int t = min(t0 + r, p.T - 1);          // rows past T: duplicate a valid row, never stored
-  const bool tv = t0 + r < p.T;
+  const int tr = tb + w * R + r;
+  const int t = min(tr, p.T - 1);               // rows past T: a valid row's copy, never stored
   const int pos = p.p0 + t;
-  const int last = p.p0 + min(t0 + R, p.T) - 1;  // the wave's last position
-  const int ntiles = (last >> 4) + 1;
+  const int last = p.p0 + min(tb + PA_WAVES * R, p.T) - 1;   // the workgroup's last position
+  const int nsteps = (last >> 4) / NT + 1;
+  const int tmax = (p.ctx_max >> 4) - 1;        // last tile of the cache
+  // scores in base 2: e^(s / sqrt(hd) - m) = 2^(s log2(e) / sqrt(hd) - m'), one v_exp_f32 each
+  const float scale2 = p.scale * 1.44269504088896341f;
 
   // B operand of S^T: q of column col, dims 32 kk + 8 grp .. + 7, as bf16 hi + lo
   const float* qrow = p.q + (long long)t * p.qs + (long long)(g * G + hh) * HD + 8 * grp;
@@ -283,57 +300,25 @@ __global__ __launch_bounds__(PA_WAVES * WAVE) void k_pf_attn(PaP p) {
       const_cast<uint16_t*>(p.kc + head), (short)0, p.ctx_max * HD * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(p.vc + head), (short)0, p.ctx_max * HD * 2, 0x00020000);
-
-  u32x4 kr0[KK], kr1[KK];
-  u32x2 vr0[DT], vr1[DT];
-#define PA_LOAD(KR, VR, J)                                                                       \
-  _Pragma("unroll") for (int kk = 0; kk < KK; ++kk)                                              \
-    KR[kk] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(                    \
-        krs, ((J) * 16 * HD + (4 * kk + grp) * 128 + col * 8) * 2, 0, 0));                       \
-  _Pragma("unroll") for (int dt = 0; dt < DT; ++dt)                                              \
-    VR[dt] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(                     \
-        vrs, ((J) * 16 * HD + (16 * dt + col) * 16 + 4 * grp) * 2, 0, 0));
-  // one key tile: the next tile's loads (into the other buffer) go out first
-#define PA_STEP(KR, VR, KN, VN, J)                                                               \
-  {                                                                                              \
-    PA_LOAD(KN, VN, min((J) + 1, ntiles - 1))                                                    \
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};                                                              \
-    _Pragma("unroll") for (int kk = 0; kk < KK; ++kk) {                                          \
-      const bf16x8 a = __builtin_bit_cast(bf16x8, KR[kk]);                                       \
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qhi[kk], s, 0, 0, 0);                       \
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qlo[kk], s, 0, 0, 0);                       \
-    }                                                                                            \
-    const int key0 = 16 * (J) + 4 * grp;                                                         \
-    float sv[4], mt = -INFINITY;                                                                 \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                              \
-      sv[i] = key0 + i <= pos ? s[i] * p.scale : -INFINITY;                                      \
-      mt = fmaxf(mt, sv[i]);                                                                     \
-    }                                                                                            \
-    mt = fmaxf(mt, __shfl_xor(mt, 16, WAVE));                                                    \
-    mt = fmaxf(mt, __shfl_xor(mt, 32, WAVE));                                                    \
-    const float mn = fmaxf(m, mt);                                                               \
-    const float alpha = m == -INFINITY ? 0.f : expf(m - mn);                                     \
-    float pv[4], ls = 0.f;                                                                       \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                              \
-      pv[i] = sv[i] == -INFINITY ? 0.f : expf(sv[i] - mn);                                       \
-      ls += pv[i];                                                                               \
-    }                                                                                            \
-    ls += __shfl_xor(ls, 16, WAVE);                                                              \
-    ls += __shfl_xor(ls, 32, WAVE);                                                              \
-    l = l * alpha + ls;                                                                          \
-    m = mn;                                                                                      \
-    i16x4 phi, plo;                                                                              \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                              \
-      const __bf16 h = static_cast<__bf16>(pv[i]);                                               \
-      phi[i] = __builtin_bit_cast(short, h);                                                     \
-      plo[i] = __builtin_bit_cast(short, static_cast<__bf16>(pv[i] - static_cast<float>(h)));    \
-    }                                                                                            \
-    _Pragma("unroll") for (int dt = 0; dt < DT; ++dt) {                                          \
-      const i16x4 a = __builtin_bit_cast(i16x4, VR[dt]);                                         \
-      f32x4 acc = o[dt] * alpha;                                                                 \
-      acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, phi, acc, 0, 0, 0);                     \
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, plo, acc, 0, 0, 0);                   \
-    }                                                                                            \
+  // thread tid stages chunks tid, tid + PA_THREADS, ... of the step's tiles: the NT
+  // K tiles first, then the NT V tiles; tiles past the cache repeat its last tile
+  // (their keys are masked)
+  u32x4 st[LPT];
+#define PA_FETCH(S)                                                                              \
+  _Pragma("unroll") for (int c = 0; c < LPT; ++c) {                                              \
+    const int ch = tid + c * PA_THREADS;                                                         \
+    const int kv = ch >= CH / 2;                                                                 \
+    const int e = (ch - kv * (CH / 2)) * 8;                   /* element in the NT tiles */      \
+    const int tl = min((S) * NT + e / TILE, tmax);                                               \
+    const int off = (tl * TILE + e % TILE) * 2;                                                  \
+    st[c] = ch < CH ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(           \
+                          kv ? vrs : krs, off, 0, 0))                                             \
+                    : u32x4{0u, 0u, 0u, 0u};                                                      \
+  }
+#define PA_PUT(B)                                                                                \
+  _Pragma("unroll") for (int c = 0; c < LPT; ++c) {                                              \
+    const int ch = tid + c * PA_THREADS;                                                         \
+    if (ch < CH) *reinterpret_cast<u32x4*>(kv_lds + (B) * 2 * NT * TILE + ch * 8) = st[c];       \
   }
 
   f32x4 o[DT];
@@ -341,14 +326,74 @@ __global__ __launch_bounds__(PA_WAVES * WAVE) void k_pf_attn(PaP p) {
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.f;
 
-  PA_LOAD(kr0, vr0, 0)
-  for (int j = 0; j < ntiles; j += 2) {
-    PA_STEP(kr0, vr0, kr1, vr1, j)
-    if (j + 1 < ntiles) PA_STEP(kr1, vr1, kr0, vr0, j + 1)
+  PA_FETCH(0)
+  PA_PUT(0)
+  __syncthreads();
+  for (int sj = 0; sj < nsteps; ++sj) {
+    const int b = sj & 1;
+    if (sj + 1 < nsteps) { PA_FETCH(sj + 1) }
+    const uint16_t* kt = kv_lds + b * 2 * NT * TILE;
+    const uint16_t* vt = kt + NT * TILE;
+    // scores of the NT tiles: independent accumulation chains
+    f32x4 s[NT];
+#pragma unroll
+    for (int u = 0; u < NT; ++u) s[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int u = 0; u < NT; ++u) {
+        const bf16x8 a =
+            *reinterpret_cast<const bf16x8*>(kt + u * TILE + (4 * kk + grp) * 128 + col * 8);
+        s[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qhi[kk], s[u], 0, 0, 0);
+        s[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qlo[kk], s[u], 0, 0, 0);
+      }
+    float sv[NT][4], mt = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < NT; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = 16 * (sj * NT + u) + 4 * grp + i;
+        sv[u][i] = key <= pos ? s[u][i] * scale2 : -INFINITY;
+        mt = fmaxf(mt, sv[u][i]);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 16, WAVE));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, WAVE));
+    const float mn = fmaxf(m, mt);
+    const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+    float ls = 0.f;
+    i16x4 phi[NT], plo[NT];
+#pragma unroll
+    for (int u = 0; u < NT; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pv = sv[u][i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[u][i] - mn);
+        ls += pv;
+        const __bf16 h = static_cast<__bf16>(pv);
+        phi[u][i] = __builtin_bit_cast(short, h);
+        plo[u][i] = __builtin_bit_cast(short, static_cast<__bf16>(pv - static_cast<float>(h)));
+      }
+    ls += __shfl_xor(ls, 16, WAVE);
+    ls += __shfl_xor(ls, 32, WAVE);
+    l = l * alpha + ls;
+    m = mn;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      f32x4 acc = o[dt] * alpha;
+#pragma unroll
+      for (int u = 0; u < NT; ++u) {
+        const i16x4 a =
+            *reinterpret_cast<const i16x4*>(vt + u * TILE + (16 * dt + col) * 16 + 4 * grp);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, phi[u], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, plo[u], acc, 0, 0, 0);
+      }
+      o[dt] = acc;
+    }
+    if (sj + 1 < nsteps) { PA_PUT(b ^ 1) }
+    __syncthreads();
   }
-#undef PA_STEP
-#undef PA_LOAD
-  if (tv) {
+#undef PA_FETCH
+#undef PA_PUT
+  if (tr < p.T) {
     const float inv = 1.0f / l;
     uint16_t* dst = p.ob + (long long)t * p.nq * HD + (long long)(g * G + hh) * HD + 4 * grp;
 #pragma unroll
@@ -378,19 +423,27 @@ static int gemm(const uint16_t* a, const uint16_t* b, void* out, int T, int N, i
   return LPS_OK;
 }
 
-template <int HD>
-static int attn_hd(const PaP& p, int G, hipStream_t st) {
+template <int HD, int G>
+static int attn_go(const PaP& p, hipStream_t st) {
   const int R = 16 / G;
   const dim3 grid((p.T + PA_WAVES * R - 1) / (PA_WAVES * R), p.nkv);
-  switch (G) {
-    case 1: hipLaunchKernelGGL((k_pf_attn<HD, 1>), grid, dim3(PA_WAVES * WAVE), 0, st, p); break;
-    case 2: hipLaunchKernelGGL((k_pf_attn<HD, 2>), grid, dim3(PA_WAVES * WAVE), 0, st, p); break;
-    case 4: hipLaunchKernelGGL((k_pf_attn<HD, 4>), grid, dim3(PA_WAVES * WAVE), 0, st, p); break;
-    case 8: hipLaunchKernelGGL((k_pf_attn<HD, 8>), grid, dim3(PA_WAVES * WAVE), 0, st, p); break;
-    default: return fail(LPS_EUNSUP, "prefill attention: %d q heads per kv head (1, 2, 4, 8)", G);
-  }
+  const size_t lds = size_t(2) * 2 * PA_KT * 16 * HD * 2;
+  int rc = ensure_lds((const void*)k_pf_attn<HD, G>, lds);
+  if (rc) return rc;
+  hipLaunchKernelGGL((k_pf_attn<HD, G>), grid, dim3(PA_THREADS), lds, st, p);
   LPS_HIP(hipGetLastError());
   return LPS_OK;
+}
+
+template <int HD>
+static int attn_hd(const PaP& p, int G, hipStream_t st) {
+  switch (G) {
+    case 1: return attn_go<HD, 1>(p, st);
+    case 2: return attn_go<HD, 2>(p, st);
+    case 4: return attn_go<HD, 4>(p, st);
+    case 8: return attn_go<HD, 8>(p, st);
+    default: return fail(LPS_EUNSUP, "prefill attention: %d q heads per kv head (1, 2, 4, 8)", G);
+  }
 }
 
 PrefillScratch prefill_scratch(const lps_layer_desc* L, int T) {

@@ -337,12 +337,12 @@ class DeviceDecoder:
         self._pf_key = key
         torch.cuda.synchronize(dev)
 
-    def prefill(self, ids, chunk=None, p0=None):
+    def prefill(self, ids, chunk=None, p0=None, hidden=True):
         """Feed the prompt ids as chunks of `chunk` rows (default: all at once)
         from position p0 (default: right after the cache prefix), each chunk
         through every stage in turn (a [T, d] f32 block per boundary), then the
         head on the prompt's last row.  Returns (logits, argmax, last stage's
-        hidden rows of the last chunk)."""
+        hidden rows of the last chunk, or None with hidden=False)."""
         cfg = self.cfg
         assert self.head is not None, "model has no vocabulary"
         ids = list(ids)
@@ -374,8 +374,8 @@ class DeviceDecoder:
                              ptr(self.tok_ring), ptr(self.head_scratch),
                              self.head_scratch.numel(), sp(st[-1]))
         torch.cuda.synchronize(dev)
-        return (self.logits_ring[0].cpu().numpy().copy(), int(self.tok_ring[0]),
-                self._pf_x[-1][:T].cpu().numpy().copy())
+        X = self._pf_x[-1][:T].cpu().numpy().copy() if hidden else None
+        return self.logits_ring[0].cpu().numpy().copy(), int(self.tok_ring[0]), X
 
     # ---- the whole pass as one graph --------------------------------------------
     def _walk_dpos(self):
