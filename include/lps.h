@@ -407,10 +407,17 @@ int lps_f32_to_f16(const float* src, uint16_t* dst, int64_t n, void* stream);
  * is one more group over all T rows; per token, the gate-weighted expert terms
  * are added in ascending expert id within each half, the remote half rounded to
  * f16 and widened back in n_pieces pieces on s_remote, and x += (shared + local)
- * + remote (lps_moe_combine).  Built for n_experts <= 64, top_k <= 16, d a
- * multiple of 128, ff a multiple of 64.  scratch (dev) of
- * lps_moe_prefill_scratch_bytes(m, T) bytes; its contents on entry do not
- * matter.  Work is enqueued on s_main (and the pieces on s_remote). */
+ * + remote (lps_moe_combine).  The activation half of the piece transfer
+ * (strata PR #3648, Approach: activations): as soon as the rows are normed, their
+ * bf16 copy goes to the remote half's own buffer in n_pieces row pieces on
+ * s_remote while s_main routes and groups; the remote experts' grouped GEMMs then
+ * run on s_remote from that copy once the tile lists exist, the local experts and
+ * the shared one on s_main, which waits for the remote experts before the
+ * per-token halves.  Both halves read the same values, so every n_pieces (1..64)
+ * gives the same bits.  Bumps act_pieces (and pieces, in the combine).  Built for
+ * n_experts <= 64, top_k <= 16, d a multiple of 128, ff a multiple of 64.
+ * scratch (dev) of lps_moe_prefill_scratch_bytes(m, T) bytes; its contents on
+ * entry do not matter.  Work is enqueued on s_main and s_remote. */
 size_t lps_moe_prefill_scratch_bytes(const lps_moe_desc* m, int32_t T);
 int lps_moe_prefill(const lps_moe_desc* m, float* x, int32_t T, int32_t n_pieces, void* scratch,
                     size_t scratch_bytes, void* s_main, void* s_remote);
@@ -430,6 +437,7 @@ typedef struct lps_counters_t {
   int64_t pieces;          /* FP16 pieces converted by lps_moe_combine */
   int64_t drains;          /* pendings waited or dropped */
   int64_t prefill_walks;   /* lps_stage_prefill calls that enqueued work */
+  int64_t act_pieces;      /* activation row pieces sent to the remote half by lps_moe_prefill */
 } lps_counters_t;
 int lps_counters(lps_counters_t* out);
 int lps_counters_reset(void);

@@ -55,7 +55,7 @@ class MoEDesc(C.Structure):
 class Counters(C.Structure):
     _fields_ = [("stage_walks", C.c_int64), ("boundary_sends", C.c_int64),
                 ("boundary_recvs", C.c_int64), ("pieces", C.c_int64), ("drains", C.c_int64),
-                ("prefill_walks", C.c_int64)]
+                ("prefill_walks", C.c_int64), ("act_pieces", C.c_int64)]
 
 
 P = C.c_void_p

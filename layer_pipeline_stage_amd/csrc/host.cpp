@@ -27,8 +27,9 @@ int fail(int code, const char* fmt, ...) {
 void clear_error() { g_err[0] = 0; }
 
 static std::atomic<long long> c_walks{0}, c_sends{0}, c_recvs{0}, c_pieces{0}, c_drains{0},
-    c_prefill{0};
+    c_prefill{0}, c_act_pieces{0};
 void count_prefill_walk() { c_prefill.fetch_add(1, std::memory_order_relaxed); }
+void count_act_pieces(int64_t n) { c_act_pieces.fetch_add(n, std::memory_order_relaxed); }
 void count_stage_walk() { c_walks.fetch_add(1, std::memory_order_relaxed); }
 void count_send() { c_sends.fetch_add(1, std::memory_order_relaxed); }
 void count_recv() { c_recvs.fetch_add(1, std::memory_order_relaxed); }
@@ -389,6 +390,7 @@ int lps_counters(lps_counters_t* out) {
   out->pieces = c_pieces.load();
   out->drains = c_drains.load();
   out->prefill_walks = c_prefill.load();
+  out->act_pieces = c_act_pieces.load();
   return LPS_OK;
 }
 int lps_counters_reset(void) {
@@ -398,6 +400,7 @@ int lps_counters_reset(void) {
   c_pieces = 0;
   c_drains = 0;
   c_prefill = 0;
+  c_act_pieces = 0;
   return LPS_OK;
 }
 

@@ -112,6 +112,7 @@ int prefill_layer(const lps_layer_desc* L, float* x, int T, int p0, void* scratc
 int launch_embed_rows(const void* table, int wdtype, int vocab, int d, const int32_t* tok, int T,
                       float* x, hipStream_t st);
 void count_prefill_walk();
+void count_act_pieces(int64_t n);
 
 // validation helpers shared by entry points
 int check_layer(const lps_layer_desc* L, const char* who);

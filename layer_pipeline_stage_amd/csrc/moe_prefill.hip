@@ -7,14 +7,22 @@
 // on one GPU: the expert matmuls are grouped GEMMs on the bf16 matrix cores.
 //
 // Steps (each its own launch, in stream order, so no kernel waits on another):
-//  1. route: per 8-token tile, RMSNorm rows (f32), bf16 copy of the normed rows
-//     for the expert GEMMs, router logits from the f32 rows (the same lane /
-//     chunk split as the decode router), softmax, top-k by logit with ties to
-//     the lower id, weights renormalised over the k.
+//  0. norm: per 8-token tile, RMSNorm rows (f32) and their bf16 copy for the
+//     expert GEMMs.  The activation half of the piece transfer starts here: on the
+//     second stream the bf16 rows go to the remote half's own copy in P row
+//     pieces while the main stream routes and groups (strata PR #3648, Approach:
+//     the activations leave before the router; both halves read the same values,
+//     so the pieces change timing, not results).
+//  1. route: the same RMSNorm recomputed per tile (bit for bit), router logits
+//     from the f32 rows (the same lane / chunk split as the decode router),
+//     softmax, top-k by logit with ties to the lower id, weights renormalised
+//     over the k.
 //  2. group: per expert, the tokens that selected it, in token order (a stable
 //     counting sort: each expert's list is a compaction of the token sequence).
-//  3. tiles: per-expert offsets and the list of 256-row tiles (experts in
-//     ascending id, then the shared expert over all tokens).
+//  3. tiles: per-expert offsets and two lists of 256-row tiles: the local
+//     experts in ascending id then the shared expert over all tokens (main
+//     stream), and the remote experts (second stream, reading the remote copy of
+//     the rows once every piece has landed and the lists exist).
 //  4. GEMM1: [rows x d] x [d x 2ff] on MFMA 32x32x16 bf16 -> f32; the gate and
 //     up columns of one output sit in the same lanes, so SwiGLU is applied in
 //     registers; the product is rounded to bf16 for GEMM2.
@@ -61,8 +69,10 @@ struct PfP {
   int32_t* lst;          // [E, T] tokens per expert
   int32_t* lslot;        // [E, T] slot of the expert in the token's top-k
   float* lw;             // [E, T] gate weight
-  int32_t* tiles;        // [max_tiles] packed (expert << 20) | m0
+  int32_t* tiles;        // [max_tiles] packed (expert << 20) | m0: this launch's list
   int32_t* n_tiles;      // [1]
+  int32_t* tiles_r;      // the remote experts' list (built with the local one)
+  int32_t* n_tiles_r;
   uint16_t* act;         // [T*k + T, ff] bf16 SwiGLU outputs, rows by (off[e] + i)
   float* z;              // [T, k, d] weighted expert outputs by slot
   float* shared;         // [T, d]
@@ -73,6 +83,9 @@ struct PfP {
 __device__ __forceinline__ uint16_t bf16_rne(float f) { return f32_to_bf16(f); }
 
 // ---- 1. route ------------------------------------------------------------------
+// ROUTE = false: only the normed rows' bf16 copy (step 0); ROUTE = true: the router
+// on the same f32 rows, recomputed by the same code (step 1)
+template <bool ROUTE>
 __global__ __launch_bounds__(256) void k_pf_route(PfP p) {
   extern __shared__ float hs[];            // [PF_TOK][d] normed rows (f32)
   __shared__ float lg[PF_TOK][PF_MAXE];
@@ -101,14 +114,17 @@ __global__ __launch_bounds__(256) void k_pf_route(PfP p) {
         v.z = v.z * rinv * gg.z;
         v.w = v.w * rinv * gg.w;
         *reinterpret_cast<f32x4*>(h + c) = v;
-        const uint32_t lo = uint32_t(bf16_rne(v.x)) | (uint32_t(bf16_rne(v.y)) << 16);
-        const uint32_t hi = uint32_t(bf16_rne(v.z)) | (uint32_t(bf16_rne(v.w)) << 16);
-        *reinterpret_cast<uint2*>(p.xb + (long long)t * d + c) = make_uint2(lo, hi);
+        if constexpr (!ROUTE) {
+          const uint32_t lo = uint32_t(bf16_rne(v.x)) | (uint32_t(bf16_rne(v.y)) << 16);
+          const uint32_t hi = uint32_t(bf16_rne(v.z)) | (uint32_t(bf16_rne(v.w)) << 16);
+          *reinterpret_cast<uint2*>(p.xb + (long long)t * d + c) = make_uint2(lo, hi);
+        }
       }
     } else {
       for (int c = lane * 4; c < d; c += 256) *reinterpret_cast<f32x4*>(h + c) = f32x4{0, 0, 0, 0};
     }
   }
+  if constexpr (!ROUTE) return;
   __syncthreads();
   // router logits: wave wv takes experts wv, wv + 4, ...; the lane / chunk split of
   // a row is the decode router's (chunk c of 8 values on lane c % 64)
@@ -190,15 +206,20 @@ __global__ __launch_bounds__(256) void k_pf_group(PfP p) {
 // ---- 3. tiles ----------------------------------------------------------------------
 __global__ void k_pf_tiles(PfP p) {
   if (threadIdx.x != 0) return;
-  int off = 0, n = 0;
+  int off = 0, n = 0, nr = 0;
   for (int e = 0; e <= p.E; ++e) {
     const int c = e < p.E ? p.cnt[e] : p.T;   // the shared expert takes every token
     p.off[e] = off;
     if (e == p.E) p.cnt[e] = c;
-    for (int m0 = 0; m0 < c; m0 += GM) p.tiles[n++] = (e << 20) | m0;
+    const bool remote = e >= p.remote_from && e < p.E;
+    for (int m0 = 0; m0 < c; m0 += GM) {
+      if (remote) p.tiles_r[nr++] = (e << 20) | m0;
+      else p.tiles[n++] = (e << 20) | m0;
+    }
     off += c;
   }
   *p.n_tiles = n;
+  *p.n_tiles_r = nr;
 }
 
 // ---- 4/5. grouped GEMM on MFMA -----------------------------------------------------------
@@ -384,8 +405,8 @@ __global__ __launch_bounds__(256) void k_pf_halves(PfP p) {
 
 // ---- scratch -----------------------------------------------------------------------------
 struct PfScratch {
-  size_t xb, idx, w, cnt, off, lst, lslot, lw, tiles, ntiles, act, z, shared, local, remote16, bo,
-      total;
+  size_t xb, xr, idx, w, cnt, off, lst, lslot, lw, tiles, ntiles, tiles_r, ntiles_r, act, z,
+      shared, local, remote16, bo, total;
   int max_tiles;
 };
 static PfScratch pf_scratch(const lps_moe_desc* m, int T) {
@@ -395,6 +416,7 @@ static PfScratch pf_scratch(const lps_moe_desc* m, int T) {
   const size_t Tk = size_t(T) * m->top_k;
   s.max_tiles = int((Tk + GM - 1) / GM + m->n_experts + (size_t(T) + GM - 1) / GM + 1);
   s.xb = take(size_t(T) * m->d * 2);
+  s.xr = take(size_t(T) * m->d * 2);          // the remote half's copy of the bf16 rows
   s.idx = take(Tk * 4);
   s.w = take(Tk * 4);
   s.cnt = take(size_t(m->n_experts + 1) * 4);
@@ -404,6 +426,8 @@ static PfScratch pf_scratch(const lps_moe_desc* m, int T) {
   s.lw = take(size_t(m->n_experts) * T * 4);
   s.tiles = take(size_t(s.max_tiles) * 4);
   s.ntiles = take(4);
+  s.tiles_r = take(size_t(s.max_tiles) * 4);
+  s.ntiles_r = take(4);
   s.act = take((Tk + T) * m->ff * 2);
   s.z = take(Tk * m->d * 4);
   s.shared = take(size_t(T) * m->d * 4);
@@ -469,33 +493,87 @@ extern "C" int lps_moe_prefill(const lps_moe_desc* m, float* x, int32_t T, int32
   p.lw = reinterpret_cast<float*>(sc + s.lw);
   p.tiles = reinterpret_cast<int32_t*>(sc + s.tiles);
   p.n_tiles = reinterpret_cast<int32_t*>(sc + s.ntiles);
+  p.tiles_r = reinterpret_cast<int32_t*>(sc + s.tiles_r);
+  p.n_tiles_r = reinterpret_cast<int32_t*>(sc + s.ntiles_r);
   p.act = reinterpret_cast<uint16_t*>(sc + s.act);
   p.z = reinterpret_cast<float*>(sc + s.z);
   p.shared = reinterpret_cast<float*>(sc + s.shared);
   p.local = reinterpret_cast<float*>(sc + s.local);
   p.remote16 = reinterpret_cast<uint16_t*>(sc + s.remote16);
   float* bo = reinterpret_cast<float*>(sc + s.bo);
-  hipStream_t st = as_stream(s_main);
-  int rc = ensure_lds((const void*)k_pf_route, size_t(PF_TOK) * m->d * 4);
+  LPS_REQUIRE(n_pieces >= 1 && n_pieces <= 64, LPS_EINVAL,
+              "lps_moe_prefill: n_pieces %d outside [1, 64]", n_pieces);
+  hipStream_t st = as_stream(s_main), sr = as_stream(s_remote);
+  uint16_t* xr = reinterpret_cast<uint16_t*>(sc + s.xr);
+  const size_t rlds = size_t(PF_TOK) * m->d * 4;
+  int rc = ensure_lds((const void*)k_pf_route<false>, rlds);
+  if (!rc) rc = ensure_lds((const void*)k_pf_route<true>, rlds);
   if (rc) return rc;
-  hipLaunchKernelGGL(k_pf_route, dim3((T + PF_TOK - 1) / PF_TOK), dim3(256), size_t(PF_TOK) * m->d * 4,
-                     st, p);
-  LPS_HIP(hipGetLastError());
-  hipLaunchKernelGGL(k_pf_group, dim3(m->n_experts), dim3(256), 0, st, p);
-  LPS_HIP(hipGetLastError());
-  hipLaunchKernelGGL(k_pf_tiles, dim3(1), dim3(64), 0, st, p);
-  LPS_HIP(hipGetLastError());
   const size_t glds = size_t(2) * (GM + GBN) * GKP * sizeof(uint16_t);
   rc = ensure_lds((const void*)k_pf_gemm<true>, glds);
+  if (!rc) rc = ensure_lds((const void*)k_pf_gemm<false>, glds);
   if (rc) return rc;
-  rc = ensure_lds((const void*)k_pf_gemm<false>, glds);
+  hipEvent_t ev[3];   // rows normed (main), tile lists built (main), remote experts done
+  for (int i = 0; i < 3; ++i) {
+    if (hipEventCreateWithFlags(&ev[i], hipEventDisableTiming) != hipSuccess) {
+      for (int j = 0; j < i; ++j) (void)hipEventDestroy(ev[j]);
+      return fail(LPS_EHIP, "lps_moe_prefill: hipEventCreate failed");
+    }
+  }
+  const dim3 rgrid((T + PF_TOK - 1) / PF_TOK);
+  hipLaunchKernelGGL(k_pf_route<false>, rgrid, dim3(256), rlds, st, p);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) e = hipEventRecord(ev[0], st);
+  // activation half: the remote copy of the bf16 rows, in P row pieces, on the
+  // second stream while the main stream routes and groups
+  if (e == hipSuccess) e = hipStreamWaitEvent(sr, ev[0], 0);
+  int pieces = 0;
+  for (int pc = 0; e == hipSuccess && pc < n_pieces; ++pc) {
+    const long long lo = (long long)pc * T / n_pieces, hi = (long long)(pc + 1) * T / n_pieces;
+    if (hi == lo) continue;
+    // bf16 rows as 32-bit words (d is even): lo * d / 2 .. hi * d / 2
+    rc = launch_copy_f32(reinterpret_cast<const float*>(p.xb) + lo * m->d / 2,
+                         reinterpret_cast<float*>(xr) + lo * m->d / 2, (hi - lo) * m->d / 2, sr);
+    if (rc) break;
+    ++pieces;
+  }
+  if (e == hipSuccess && !rc) {
+    hipLaunchKernelGGL(k_pf_route<true>, rgrid, dim3(256), rlds, st, p);
+    hipLaunchKernelGGL(k_pf_group, dim3(m->n_experts), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(k_pf_tiles, dim3(1), dim3(64), 0, st, p);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess && !rc) e = hipEventRecord(ev[1], st);
+  // remote experts: their tile list, rows from the remote copy, on the second stream
+  if (e == hipSuccess && !rc) e = hipStreamWaitEvent(sr, ev[1], 0);
+  if (e == hipSuccess && !rc) {
+    PfP pr = p;
+    pr.xb = xr;
+    pr.tiles = p.tiles_r;
+    pr.n_tiles = p.n_tiles_r;
+    hipLaunchKernelGGL(k_pf_gemm<true>, dim3(m->ff / (GBN / 2), s.max_tiles), dim3(GEMM_THREADS),
+                       glds, sr, pr);
+    hipLaunchKernelGGL(k_pf_gemm<false>, dim3(m->d / GBN, s.max_tiles), dim3(GEMM_THREADS), glds,
+                       sr, pr);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess && !rc) e = hipEventRecord(ev[2], sr);
+  // local experts and the shared one on the main stream
+  if (e == hipSuccess && !rc) {
+    hipLaunchKernelGGL(k_pf_gemm<true>, dim3(m->ff / (GBN / 2), s.max_tiles), dim3(GEMM_THREADS),
+                       glds, st, p);
+    hipLaunchKernelGGL(k_pf_gemm<false>, dim3(m->d / GBN, s.max_tiles), dim3(GEMM_THREADS), glds,
+                       st, p);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess && !rc) e = hipStreamWaitEvent(st, ev[2], 0);
+  if (e == hipSuccess && !rc) {
+    hipLaunchKernelGGL(k_pf_halves, dim3(T), dim3(256), 0, st, p);
+    e = hipGetLastError();
+  }
+  for (int i = 0; i < 3; ++i) (void)hipEventDestroy(ev[i]);   // released once fired
   if (rc) return rc;
-  hipLaunchKernelGGL(k_pf_gemm<true>, dim3(m->ff / (GBN / 2), s.max_tiles), dim3(GEMM_THREADS), glds,
-                     st, p);
-  LPS_HIP(hipGetLastError());
-  hipLaunchKernelGGL(k_pf_gemm<false>, dim3(m->d / GBN, s.max_tiles), dim3(GEMM_THREADS), glds, st, p);
-  LPS_HIP(hipGetLastError());
-  hipLaunchKernelGGL(k_pf_halves, dim3(T), dim3(256), 0, st, p);
-  LPS_HIP(hipGetLastError());
+  if (e != hipSuccess) return fail(LPS_EHIP, "lps_moe_prefill: %s", hipGetErrorString(e));
+  count_act_pieces(pieces);
   return lps_moe_combine(x, x, p.shared, p.local, p.remote16, bo, T, m->d, n_pieces, s_remote, s_main);
 }

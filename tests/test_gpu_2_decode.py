@@ -211,12 +211,24 @@ def test_moe_prefill_small_matches_oracle_and_pieces(rt):
     from oracle.moe import MoEStack
     cfg = synth.MoEConfig("moe-gpu-pf", n_layers=2, d=512, n_experts=16, top_k=4, ff=128,
                           remote_from=8, prefill_T=300, steps=0)
+    from layer_pipeline_stage_amd import lps
     m = synth.make_moe(cfg)
     st = rt.DeviceMoEStack(m)
     X = m["x_prefill"]
+    lps.lps_counters_reset()
     got8 = st.prefill(X, n_pieces=8)
+    c = lps.counters()
+    # both halves of the transfer ran in 8 pieces per layer (activations, then sums)
+    assert c["act_pieces"] == 8 * cfg.n_layers and c["pieces"] == 8 * cfg.n_layers, c
     got1 = st.prefill(X, n_pieces=1)
     assert np.array_equal(got8, got1)
+    # one stream for both halves, and more pieces than rows in a tiny chunk
+    got_one_stream = st.prefill(X, n_pieces=8, remote_stream=st.stream)
+    assert np.array_equal(got8, got_one_stream)
+    lps.lps_counters_reset()
+    tiny = st.prefill(X[:5], n_pieces=8)
+    assert lps.counters()["act_pieces"] == 5 * cfg.n_layers
+    assert np.array_equal(tiny, st.prefill(X[:5], n_pieces=1))
     ref = MoEStack(m).forward(X, prefill=True, n_pieces=8)
     tol = 2e-3 * np.abs(ref).max()
     err = np.abs(got8 - ref).max(axis=1)
