@@ -149,7 +149,7 @@ def _cpu_model():
     return "unknown"
 
 
-def prefill_bench(torch, synth, lps, runtime, T, stages, streams, reps):
+def prefill_bench(torch, synth, lps, runtime, T, stages, streams, reps, chunk=None):
     """The dense slice's prompt path: a T-token chunk through the stages (bf16
     GEMMs and causal attention on the matrix cores) after the 4096-row prefix,
     timed from the first embedding to the last stage's output on the device
@@ -158,13 +158,13 @@ def prefill_bench(torch, synth, lps, runtime, T, stages, streams, reps):
     model = synth.make_dense(cfg)
     dd = runtime.DeviceDecoder(model, fence=lps.stage_plan(cfg.n_layers, stages), streams=streams)
     ids = [int(t) for t in model["prompt"]]
-    dd.prefill(ids)
+    dd.prefill(ids, chunk=chunk)
     times = []
     for _ in range(reps):
         dd.reset()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        dd.prefill(ids, hidden=False)   # ends with a device synchronize and the logits readback
+        dd.prefill(ids, chunk=chunk, hidden=False)   # ends with a device sync and the logits readback
         times.append(time.perf_counter() - t0)
     dd.close()
     dt = min(times)
@@ -176,12 +176,13 @@ def prefill_bench(torch, synth, lps, runtime, T, stages, streams, reps):
             "value": round(T / dt, 1), "unit": "tok/s", "ms_per_chunk": round(1e3 * dt, 3),
             "tflops": round((gemm + attn) / dt / 1e12, 1), "gemm_tflop": round(gemm / 1e12, 3),
             "attn_tflop": round(attn / 1e12, 3), "dtype": "bf16", "data": "synthetic",
-            "config": {"workload": f"dense 8B-class slice prefill: {T}-token chunk after a "
+            "config": {"workload": f"dense 8B-class slice prefill: {T}-token prompt "
+                                   f"in chunks of {chunk or T} after a "
                                    f"4096-row prefix, {stages} stages ({streams} "
                                    f"stream{'s' if streams == 'per-stage' else ''}), bf16 "
                                    "matrix-core operands, timed from the host to the last "
                                    "row's logits on the host",
-                       "chunk": T, "stages": stages}}
+                       "prompt": T, "chunk": chunk or T, "stages": stages}}
 
 
 def main():
@@ -202,7 +203,10 @@ def main():
                     help="only run a 256 MiB f32 device copy 8 times (reference for HBM counters)")
     ap.add_argument("--prefill-only", type=int, default=0, metavar="T",
                     help="only time the chunked prefill of a T-token prompt through the stages "
-                         "(one chunk, after the 4096-row prefix) and print one JSON line")
+                         "(after the 4096-row prefix) and print one JSON line")
+    ap.add_argument("--prefill-chunk", type=int, default=0, metavar="C",
+                    help="with --prefill-only: feed the prompt in micro-chunks of C rows (on "
+                         "per-stage streams a later stage runs chunk k while stage 0 runs k + 1)")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py: this path runs on one GPU (stages are streams of that GPU); "
@@ -233,7 +237,8 @@ def main():
         return
     if a.prefill_only:
         print(json.dumps(prefill_bench(torch, synth, lps, runtime, a.prefill_only, a.stages,
-                                       a.streams, max(1, a.steps))), flush=True)
+                                       a.streams, max(1, a.steps), a.prefill_chunk or None)),
+              flush=True)
         return
     K, W = a.steps, a.warmup
     cfg = replace(synth.DENSE8B, steps=max(K, W, 128) - 1)
