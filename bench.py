@@ -19,6 +19,7 @@ and the float64 CPU oracle timed on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import ctypes as C
 import json
 import os
 import platform
@@ -149,6 +150,87 @@ def _cpu_model():
     return "unknown"
 
 
+def _timed(torch, fn):
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    fn()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def pad_bench(torch, synth, lps, runtime, steps):
+    """Padded-head MXFP4 decode (4 layers, n_embd 5120, 36 q / 6 kv heads of 256 of
+    which 12 q and 2 kv are zero dummies, ff 17472, context 8192): `steps` hidden
+    rows in and out, device-resident, one stage and two."""
+    cfg = replace(synth.PAD, steps=steps)
+    model = synth.make_pad(cfg)
+    xs = np.asarray(model["x_in"], np.float32)
+    c = cfg
+    kvb = 2 * c.nkv * c.hd * 2
+    wb = lambda n, k: n * k // 2 + n * k // 32                     # noqa: E731
+    per_tok = c.n_layers * (wb((c.nq + 2 * c.nkv) * c.hd, c.d) + wb(c.d, c.nq * c.hd) +
+                            wb(2 * c.ff, c.d) + wb(c.d, c.ff)) + \
+        c.n_layers * kvb * (c.prefix + steps / 2)
+    out = {"metric": "decode tokens/s, padded-head MXFP4 model, 1 GPU", "unit": "tok/s",
+           "dtype": "mxfp4 weights, bf16 KV, f32 activations", "data": "synthetic",
+           "hbm_bytes_per_token": int(per_tok), "rows": []}
+    for fence in ([0, 4], [0, 2, 4]):
+        dd = runtime.DeviceDecoder(model, fence=fence, streams="single")
+        dd.run_hidden(xs[:4])
+        dd.reset()
+        dt = _timed(torch, lambda: dd.run_hidden(xs)) / steps
+        dd.close()
+        out["rows"].append({"stages": len(fence) - 1, "value": round(1 / dt, 1),
+                            "us_per_token": round(1e6 * dt, 2),
+                            "hbm_gbs": round(per_tok / dt / 1e9, 1),
+                            "hbm_frac": round(per_tok / dt / 1e9 / HBM_PEAK_GBS, 4)})
+    out["value"] = out["rows"][0]["value"]
+    out["config"] = {"workload": "padded-head MXFP4 decode: 4 layers, n_embd 5120, 36 q / 6 kv "
+                                 "heads of 256 (12 q, 2 kv zero dummies), ff 17472, MXFP4 weights, "
+                                 f"context 8192 + {steps} steps, hidden rows in and out "
+                                 "(timed including the per-step row copies, excluding the "
+                                 "final host readback)"}
+    return out
+
+
+def moe_bench(torch, synth, lps, runtime, steps):
+    """The MoE layer stack (4 layers, n_embd 2048, 64 experts top-8 + 1 shared, ff
+    1024): batch-1 decode of `steps` rows, then the 16,384-token prefill chunk in 8
+    pieces (both halves of the piece transfer) — MFMA utilisation of the chunk."""
+    cfg = replace(synth.MOE, steps=steps)
+    model = synth.make_moe(cfg)
+    st = runtime.DeviceMoEStack(model)
+    xs = np.asarray(model["x_in"], np.float32)
+    st.decode(xs[:4])
+    dt = _timed(torch, lambda: st.decode(xs)) / steps
+    c = cfg
+    per_tok = c.n_layers * ((c.top_k + 1) * 3 * c.ff * c.d * 2 + c.n_experts * c.d * 2)
+    X = np.asarray(model["x_prefill"], np.float32)
+    T = X.shape[0]
+    xdev = runtime.to_dev(X, "cuda:0")
+    sb = lps.lps_moe_prefill_scratch_bytes(C.byref(st.descs[0]), T)
+    st._pf_scratch = torch.empty(sb, dtype=torch.uint8, device="cuda:0")
+    rs = torch.cuda.Stream()
+    times = []
+    for _ in range(3):
+        x = xdev.clone()
+        times.append(_timed(torch, lambda: st.prefill_dev(x, T, 8, rs)))
+    tp = min(times[1:])
+    flop = 7.44e12 * T / 16384
+    return {"metric": "decode tokens/s, MoE layer stack, 1 GPU", "value": round(1 / dt, 1),
+            "unit": "tok/s", "us_per_token": round(1e6 * dt, 2),
+            "hbm_bytes_per_token": int(per_tok), "hbm_gbs": round(per_tok / dt / 1e9, 1),
+            "hbm_frac": round(per_tok / dt / 1e9 / HBM_PEAK_GBS, 4),
+            "prefill": {"tokens": T, "ms": round(1e3 * tp, 3), "tok_s": round(T / tp, 1),
+                        "tflops": round(flop / tp / 1e12, 1),
+                        "mfma_frac": round(flop / tp / 1e12 / 2500.0, 4), "pieces": 8},
+            "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "MoE layer stack: 4 layers, n_embd 2048, 64 experts top-8 "
+                                   "+ 1 shared, ff 1024, bf16; decode rows device-resident; "
+                                   "prefill chunk 16,384 tokens, FP16 sums and bf16 "
+                                   "activations in 8 pieces on a second stream"}}
+
+
 def prefill_bench(torch, synth, lps, runtime, T, stages, streams, reps, chunk=None):
     """The dense slice's prompt path: a T-token chunk through the stages (bf16
     GEMMs and causal attention on the matrix cores) after the 4096-row prefix,
@@ -204,6 +286,10 @@ def main():
     ap.add_argument("--prefill-only", type=int, default=0, metavar="T",
                     help="only time the chunked prefill of a T-token prompt through the stages "
                          "(after the 4096-row prefix) and print one JSON line")
+    ap.add_argument("--config", choices=("moe", "pad"), default=None,
+                    help="only time another workload and print one JSON line: moe = the MoE "
+                         "layer stack (batch-1 decode, then the 16,384-token prefill chunk), "
+                         "pad = the padded-head MXFP4 decode at context 8192")
     ap.add_argument("--prefill-chunk", type=int, default=0, metavar="C",
                     help="with --prefill-only: feed the prompt in micro-chunks of C rows (on "
                          "per-stage streams a later stage runs chunk k while stage 0 runs k + 1)")
@@ -234,6 +320,10 @@ def main():
         assert torch.equal(src, dst)
         print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n,
                           "launches": 8, "gbs": round(8 * n / dt / 1e9, 1)}))
+        return
+    if a.config:
+        fn = moe_bench if a.config == "moe" else pad_bench
+        print(json.dumps(fn(torch, synth, lps, runtime, max(8, a.steps))), flush=True)
         return
     if a.prefill_only:
         print(json.dumps(prefill_bench(torch, synth, lps, runtime, a.prefill_only, a.stages,
