@@ -421,7 +421,10 @@ int lps_f32_to_f16(const float* src, uint16_t* dst, int64_t n, void* stream);
 size_t lps_moe_prefill_scratch_bytes(const lps_moe_desc* m, int32_t T);
 int lps_moe_prefill(const lps_moe_desc* m, float* x, int32_t T, int32_t n_pieces, void* scratch,
                     size_t scratch_bytes, void* s_main, void* s_remote);
-/* One whole MoE layer for one token (decode): x (dev [d]) updated in place. */
+/* One whole MoE layer for one token (decode): x (dev [d]) updated in place:
+ * route, the selected experts' and the shared expert's gate/up + SwiGLU and down
+ * GEMVs, the ordered local / remote (f16) combine.  d a multiple of 8, at most
+ * 4096 (LPS_EUNSUP otherwise). */
 size_t lps_moe_layer_scratch_bytes(const lps_moe_desc* m);
 int lps_moe_layer_decode(const lps_moe_desc* m, float* x, void* scratch, size_t scratch_bytes,
                          void* stream);

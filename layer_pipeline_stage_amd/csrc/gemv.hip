@@ -108,12 +108,12 @@ __device__ __forceinline__ const uint8_t* unit_base(const GemvP& p, int u) {
 // offset of unit u's activation row in the staged vector, and the staged length
 template <int EPI>
 __device__ __forceinline__ int unit_xoff(const GemvP& p, int u) {
-  if constexpr (EPI == EPI_MOEDN) return (u / (p.rps >> 1)) * p.K;
+  if constexpr (EPI == EPI_MOEDN) return 0;   // the workgroup staged its own slot's vector
   else return 0;
 }
 template <int EPI>
 __host__ __device__ __forceinline__ int staged_len(const GemvP& p) {
-  return EPI == EPI_MOEDN ? (p.kslots + 1) * p.K : p.K;
+  return p.K;
 }
 
 __device__ __forceinline__ void store_kv(void* base, int kvdtype, long long off, float v) {
@@ -328,7 +328,13 @@ __global__ __launch_bounds__(NT) void k_gemv_buf(GemvP p) {
     stage_x_mx<NORM, NT>(p.x, p.g, p.eps, p.K, xs);
   } else {
     if (threadIdx.x < CH) xs[zoff + threadIdx.x] = 0.f;   // zero chunk
-    stage_x<NORM, NT>(p.x, p.g, p.eps, staged_len<EPI>(p), xs);
+    // MoE down: a workgroup's units all belong to one slot (the launch gives every
+    // wave one unit and a slot's unit count is a multiple of the waves per group),
+    // so it stages only that slot's activations
+    const float* xsrc = p.x;
+    if constexpr (EPI == EPI_MOEDN)
+      xsrc += (long long)((blockIdx.x * NW) / (p.rps >> 1)) * p.K;
+    stage_x<NORM, NT>(xsrc, p.g, p.eps, staged_len<EPI>(p), xs);
   }
   if (u < p.units) {
     float a0 = 0.f, a1 = 0.f;
@@ -411,7 +417,7 @@ static int launch_t(const GemvP& p, hipStream_t st, Stamp sp, int* waves) {
   do {                                                                                           \
     constexpr int NW_ = (NTV) / WAVE;                                                            \
     int grid = (p.units + NW_ - 1) / NW_;                                                        \
-    if (grid > (MAXBV)) grid = (MAXBV);                                                          \
+    if (EPI != EPI_MOEDN && grid > (MAXBV)) grid = (MAXBV);  /* MoE down: one unit per wave */   \
     if (grid < 1) grid = 1;                                                                      \
     const bool db = p.units > grid * NW_ || per_lane > (UU);                                     \
     if (waves) *waves = grid * NW_;                                                              \

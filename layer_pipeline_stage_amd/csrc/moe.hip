@@ -274,7 +274,8 @@ extern "C" int lps_moe_layer_decode(const lps_moe_desc* m, float* x, void* scrat
   int32_t* idx = reinterpret_cast<int32_t*>(sc + s.idx);
   float* wts = reinterpret_cast<float*>(sc + s.w);
   float* mbuf = reinterpret_cast<float*>(sc + s.mbuf);
-  LPS_REQUIRE(m->d <= 4096 && m->d % 2 == 0, LPS_EUNSUP, "lps_moe_layer_decode: d %d (even, <= 4096)",
+  LPS_REQUIRE(m->d <= 4096 && m->d % 8 == 0, LPS_EUNSUP,
+              "lps_moe_layer_decode: d %d (a multiple of 8, <= 4096)",
               m->d);
   rc = launch_route(m, x, 1, reinterpret_cast<float*>(sc + s.logits), idx, wts, st);
   if (rc) return rc;
