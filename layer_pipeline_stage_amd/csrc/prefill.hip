@@ -261,10 +261,16 @@ template <int HD, int G>
 __global__ __launch_bounds__(PA_THREADS) void k_pf_attn(PaP p) {
   constexpr int KK = HD / 32, DT = HD / 16, R = 16 / G;
   constexpr int TILE = 16 * HD;                 // elements of one K (or V) 16-row tile
+  constexpr int VP = 20;                        // LDS row of a V^T tile: 16 keys + 4 pad
+  constexpr int VTILE = HD * VP;                // LDS elements of one V tile
   constexpr int NT = PA_KT;                     // tiles per step
+  constexpr int BUF = NT * (TILE + VTILE);      // LDS elements of one step buffer
   constexpr int CH = 2 * NT * TILE / 8;         // 16-byte chunks of a step's K + V tiles
   constexpr int LPT = (CH + PA_THREADS - 1) / PA_THREADS;   // chunks per thread
-  extern __shared__ __attribute__((aligned(16))) uint16_t kv_lds[];   // [2][K tiles | V tiles]
+  // [2][NT K tiles | NT V tiles]: K tiles as in the cache; V^T rows padded to 40 bytes
+  // so the 16 lanes of a PV operand read (rows 32 bytes apart otherwise) hit
+  // distinct banks
+  extern __shared__ __attribute__((aligned(16))) uint16_t kv_lds[];
   const int tid = threadIdx.x, lane = tid & (WAVE - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
   const int col = lane & 15, grp = lane >> 4;
@@ -318,7 +324,15 @@ __global__ __launch_bounds__(PA_THREADS) void k_pf_attn(PaP p) {
 #define PA_PUT(B)                                                                                \
   _Pragma("unroll") for (int c = 0; c < LPT; ++c) {                                              \
     const int ch = tid + c * PA_THREADS;                                                         \
-    if (ch < CH) *reinterpret_cast<u32x4*>(kv_lds + (B) * 2 * NT * TILE + ch * 8) = st[c];       \
+    if (ch < CH / 2) {                                                                           \
+      *reinterpret_cast<u32x4*>(kv_lds + (B) * BUF + ch * 8) = st[c];                             \
+    } else if (ch < CH) {                                                                        \
+      const int e = (ch - CH / 2) * 8;        /* element in the NT V tiles: half a key row */    \
+      uint16_t* dst = kv_lds + (B) * BUF + NT * TILE + (e / TILE) * VTILE +                      \
+                      ((e % TILE) >> 4) * VP + (e & 15);                                          \
+      *reinterpret_cast<u32x2*>(dst) = u32x2{st[c].x, st[c].y};                                   \
+      *reinterpret_cast<u32x2*>(dst + 4) = u32x2{st[c].z, st[c].w};                               \
+    }                                                                                            \
   }
 
   f32x4 o[DT];
@@ -332,7 +346,7 @@ __global__ __launch_bounds__(PA_THREADS) void k_pf_attn(PaP p) {
   for (int sj = 0; sj < nsteps; ++sj) {
     const int b = sj & 1;
     if (sj + 1 < nsteps) { PA_FETCH(sj + 1) }
-    const uint16_t* kt = kv_lds + b * 2 * NT * TILE;
+    const uint16_t* kt = kv_lds + b * BUF;
     const uint16_t* vt = kt + NT * TILE;
     // scores of the NT tiles: independent accumulation chains
     f32x4 s[NT];
@@ -382,7 +396,7 @@ __global__ __launch_bounds__(PA_THREADS) void k_pf_attn(PaP p) {
 #pragma unroll
       for (int u = 0; u < NT; ++u) {
         const i16x4 a =
-            *reinterpret_cast<const i16x4*>(vt + u * TILE + (16 * dt + col) * 16 + 4 * grp);
+            *reinterpret_cast<const i16x4*>(vt + u * VTILE + (16 * dt + col) * VP + 4 * grp);
         acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, phi[u], acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, plo[u], acc, 0, 0, 0);
       }
@@ -427,7 +441,7 @@ template <int HD, int G>
 static int attn_go(const PaP& p, hipStream_t st) {
   const int R = 16 / G;
   const dim3 grid((p.T + PA_WAVES * R - 1) / (PA_WAVES * R), p.nkv);
-  const size_t lds = size_t(2) * 2 * PA_KT * 16 * HD * 2;
+  const size_t lds = size_t(2) * PA_KT * (16 * HD + 20 * HD) * 2;
   int rc = ensure_lds((const void*)k_pf_attn<HD, G>, lds);
   if (rc) return rc;
   hipLaunchKernelGGL((k_pf_attn<HD, G>), grid, dim3(PA_THREADS), lds, st, p);
