@@ -20,6 +20,7 @@
 #include "internal.h"
 
 #include <cmath>
+#include <type_traits>
 
 namespace lps {
 
@@ -232,15 +233,18 @@ __global__ void k_pf_rope_append(float* qkv, int T, int nq, int nkv, int hd, int
 // row t0 + w R + r.  The workgroup walks the key tiles (16 cache rows each) from
 // row 0 to its last row's position; each tile of K and V is loaded from HBM / L2
 // once per workgroup into LDS (double-buffered through registers: tile j + 1 is
-// fetched while tile j is multiplied, one barrier per tile) and every wave forms,
+// fetched while tile j is multiplied, one barrier per step) and every wave forms,
 // with an online softmax per column (in base 2: the scale carries log2 e),
-//   S^T[16 keys, 16 cols] = K_tile . Q^T   (16x16x32 bf16, q as bf16 hi + lo)
-//   O^T[hd, 16 cols]     += V_tile^T . P^T (16x16x16 bf16, p as bf16 hi + lo)
-// where lane (col, grp) holds the scores of keys 4 grp .. 4 grp + 3 for column
-// col, exactly the B operand of the PV product.  The tiles sit in LDS in the
-// caches' own order, so each wave's operand reads cover contiguous 1 KiB / 512 B
-// (no bank conflicts).  Keys past a column's position are masked.  The output
-// o / l is rounded to bf16 for the O projection.
+//   S^T[16 keys, 16 cols] = K_tile . Q^T          (16x16x32 bf16, q as bf16)
+//   O^T[hd, 16 cols]     += V_pair^T . P_pair^T   (16x16x32 bf16, p as bf16)
+// where lane (col, grp) holds the scores of keys 4 grp .. 4 grp + 3 of a tile
+// for column col.  A pair of tiles (u0, u1) makes one 32-deep PV product: its
+// k index 8 grp + e stands for key 4 grp + e of tile u0 (e < 4) or key
+// 4 grp + e - 4 of tile u1, which is where lane (col, grp) already holds those
+// keys' weights (B operand) and where it reads V^T (A operand), so the weights
+// never leave the lane.  q, K, V and the weights are bf16 operands with f32
+// accumulation; the softmax sum l adds the f32 weights.  Keys past a column's
+// position are masked.  The output o / l is rounded to bf16 for the O projection.
 struct PaP {
   const float* q;          // [T, nq, hd] rotated (the q part of qkv: row stride qs)
   const uint16_t* kc;      // tiled bf16 caches of the layer
@@ -256,17 +260,21 @@ constexpr int PA_THREADS = PA_WAVES * WAVE;
 #define LPS_PA_KT 4
 #endif
 constexpr int PA_KT = LPS_PA_KT;   // 16-row key tiles per step (one softmax update, one barrier)
+static_assert(PA_KT % 2 == 0, "PV takes the key tiles in pairs");
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 template <int HD, int G>
-__global__ __launch_bounds__(PA_THREADS) void k_pf_attn(PaP p) {
+__global__ __launch_bounds__(PA_THREADS) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void k_pf_attn(PaP p) {
   constexpr int KK = HD / 32, DT = HD / 16, R = 16 / G;
   constexpr int TILE = 16 * HD;                 // elements of one K (or V) 16-row tile
   constexpr int VP = 20;                        // LDS row of a V^T tile: 16 keys + 4 pad
   constexpr int VTILE = HD * VP;                // LDS elements of one V tile
   constexpr int NT = PA_KT;                     // tiles per step
   constexpr int BUF = NT * (TILE + VTILE);      // LDS elements of one step buffer
-  constexpr int CH = 2 * NT * TILE / 8;         // 16-byte chunks of a step's K + V tiles
-  constexpr int LPT = (CH + PA_THREADS - 1) / PA_THREADS;   // chunks per thread
+  constexpr int CK = NT * TILE / 8;             // 16-byte chunks of a step's K (and of its V) tiles
+  static_assert(CK % PA_THREADS == 0, "whole chunks of K and of V per thread");
+  constexpr int LPT = CK / PA_THREADS;          // K (and V) chunks per thread per step
   // [2][NT K tiles | NT V tiles]: K tiles as in the cache; V^T rows padded to 40 bytes
   // so the 16 lanes of a PV operand read (rows 32 bytes apart otherwise) hit
   // distinct banks
@@ -282,129 +290,143 @@ __global__ __launch_bounds__(PA_THREADS) void k_pf_attn(PaP p) {
   const int pos = p.p0 + t;
   const int last = p.p0 + min(tb + PA_WAVES * R, p.T) - 1;   // the workgroup's last position
   const int nsteps = (last >> 4) / NT + 1;
-  const int tmax = (p.ctx_max >> 4) - 1;        // last tile of the cache
+  // steps whose keys every row of the workgroup sees (no mask): keys < p0 + tb + 1
+  const int nfree = min((p.p0 + tb + 1) / (16 * NT), nsteps);
   // scores in base 2: e^(s / sqrt(hd) - m) = 2^(s log2(e) / sqrt(hd) - m'), one v_exp_f32 each
   const float scale2 = p.scale * 1.44269504088896341f;
 
-  // B operand of S^T: q of column col, dims 32 kk + 8 grp .. + 7, as bf16 hi + lo
+  // B operand of S^T: q of column col, dims 32 kk + 8 grp .. + 7, as bf16
   const float* qrow = p.q + (long long)t * p.qs + (long long)(g * G + hh) * HD + 8 * grp;
-  bf16x8 qhi[KK], qlo[KK];
+  bf16x8 qb[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
     const f32x4 q0 = *reinterpret_cast<const f32x4*>(qrow + 32 * kk);
     const f32x4 q1 = *reinterpret_cast<const f32x4*>(qrow + 32 * kk + 4);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float v = e < 4 ? q0[e] : q1[e - 4];
-      const __bf16 h = static_cast<__bf16>(v);
-      qhi[kk][e] = h;
-      qlo[kk][e] = static_cast<__bf16>(v - static_cast<float>(h));
-    }
+    for (int e = 0; e < 8; ++e) qb[kk][e] = static_cast<__bf16>(e < 4 ? q0[e] : q1[e - 4]);
   }
   const long long head = (long long)g * p.ctx_max * HD;     // elements before kv head g
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(p.kc + head), (short)0, p.ctx_max * HD * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(p.vc + head), (short)0, p.ctx_max * HD * 2, 0x00020000);
-  // thread tid stages chunks tid, tid + PA_THREADS, ... of the step's tiles: the NT
-  // K tiles first, then the NT V tiles; tiles past the cache repeat its last tile
-  // (their keys are masked)
-  u32x4 st[LPT];
-#define PA_FETCH(S)                                                                              \
-  _Pragma("unroll") for (int c = 0; c < LPT; ++c) {                                              \
-    const int ch = tid + c * PA_THREADS;                                                         \
-    const int kv = ch >= CH / 2;                                                                 \
-    const int e = (ch - kv * (CH / 2)) * 8;                   /* element in the NT tiles */      \
-    const int tl = min((S) * NT + e / TILE, tmax);                                               \
-    const int off = (tl * TILE + e % TILE) * 2;                                                  \
-    st[c] = ch < CH ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(           \
-                          kv ? vrs : krs, off, 0, 0))                                             \
-                    : u32x4{0u, 0u, 0u, 0u};                                                      \
+  // Thread tid stages chunks tid, tid + PA_THREADS, ... of the step's K tiles and the
+  // same chunks of its V tiles.  A step's NT tiles are contiguous in the caches, so
+  // chunk c of step S sits at byte S * NT * TILE * 2 + 16 c; tiles past the cache
+  // read as zeros through the resource bound (their keys are masked).  The LDS
+  // places are the same every step: K chunks packed, V chunks (half a V^T row of
+  // one tile) at their padded row.
+  int vdst[LPT];
+#pragma unroll
+  for (int c = 0; c < LPT; ++c) {
+    const int e = (tid + c * PA_THREADS) * 8;   // element in the NT V tiles
+    vdst[c] = NT * TILE + (e / TILE) * VTILE + ((e % TILE) >> 4) * VP + (e & 15);
   }
-#define PA_PUT(B)                                                                                \
-  _Pragma("unroll") for (int c = 0; c < LPT; ++c) {                                              \
-    const int ch = tid + c * PA_THREADS;                                                         \
-    if (ch < CH / 2) {                                                                           \
-      *reinterpret_cast<u32x4*>(kv_lds + (B) * BUF + ch * 8) = st[c];                             \
-    } else if (ch < CH) {                                                                        \
-      const int e = (ch - CH / 2) * 8;        /* element in the NT V tiles: half a key row */    \
-      uint16_t* dst = kv_lds + (B) * BUF + NT * TILE + (e / TILE) * VTILE +                      \
-                      ((e % TILE) >> 4) * VP + (e & 15);                                          \
-      *reinterpret_cast<u32x2*>(dst) = u32x2{st[c].x, st[c].y};                                   \
-      *reinterpret_cast<u32x2*>(dst + 4) = u32x2{st[c].z, st[c].w};                               \
-    }                                                                                            \
+  u32x4 stk[LPT], stv[LPT];
+#define PA_FETCH(S)                                                                           \
+  _Pragma("unroll") for (int c = 0; c < LPT; ++c) {                                           \
+    const int off = (S) * (NT * TILE * 2) + (tid + c * PA_THREADS) * 16;                      \
+    stk[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0)); \
+    stv[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0)); \
+  }
+#define PA_PUT(B)                                                                             \
+  _Pragma("unroll") for (int c = 0; c < LPT; ++c) {                                           \
+    *reinterpret_cast<u32x4*>(kv_lds + (B) * BUF + (tid + c * PA_THREADS) * 8) = stk[c];       \
+    uint16_t* dst = kv_lds + (B) * BUF + vdst[c];                                             \
+    *reinterpret_cast<u32x2*>(dst) = u32x2{stv[c].x, stv[c].y};                               \
+    *reinterpret_cast<u32x2*>(dst + 4) = u32x2{stv[c].z, stv[c].w};                           \
   }
 
   f32x4 o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;
+  float m2 = -INFINITY, l = 0.f;   // running max of the base-2 scores, sum of weights
 
-  PA_FETCH(0)
-  PA_PUT(0)
-  __syncthreads();
-  for (int sj = 0; sj < nsteps; ++sj) {
+  // One step: NT key tiles.  The first step holds key 0, which every row sees, so
+  // the running max is finite from then on and a masked score (-inf) gives a zero
+  // weight through exp2 without any select.
+  auto step = [&](int sj, auto masked) {
+    constexpr bool MASK = decltype(masked)::value;
     const int b = sj & 1;
     if (sj + 1 < nsteps) { PA_FETCH(sj + 1) }
     const uint16_t* kt = kv_lds + b * BUF;
     const uint16_t* vt = kt + NT * TILE;
-    // scores of the NT tiles: independent accumulation chains
+    bf16x8 ka[NT][KK];
+#pragma unroll
+    for (int u = 0; u < NT; ++u)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        ka[u][kk] = *reinterpret_cast<const bf16x8*>(kt + u * TILE + (4 * kk + grp) * 128 + col * 8);
     f32x4 s[NT];
 #pragma unroll
-    for (int u = 0; u < NT; ++u) s[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < NT; ++u) {
+      s[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
+      for (int kk = 0; kk < KK; ++kk)
+        s[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[u][kk], qb[kk], s[u], 0, 0, 0);
+    }
+    // V operands of the tile pairs, read while the softmax runs
+    bf16x8 va[DT][NT / 2];
 #pragma unroll
-      for (int u = 0; u < NT; ++u) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(kt + u * TILE + (4 * kk + grp) * 128 + col * 8);
-        s[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qhi[kk], s[u], 0, 0, 0);
-        s[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qlo[kk], s[u], 0, 0, 0);
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int v = 0; v < NT / 2; ++v) {
+        const uint16_t* vp = vt + (16 * dt + col) * VP + 4 * grp;
+        const i16x4 a0 = *reinterpret_cast<const i16x4*>(vp + (2 * v) * VTILE);
+        const i16x4 a1 = *reinterpret_cast<const i16x4*>(vp + (2 * v + 1) * VTILE);
+        va[dt][v] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
       }
-    float sv[NT][4], mt = -INFINITY;
+    float mt = -INFINITY;
 #pragma unroll
     for (int u = 0; u < NT; ++u)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int key = 16 * (sj * NT + u) + 4 * grp + i;
-        sv[u][i] = key <= pos ? s[u][i] * scale2 : -INFINITY;
-        mt = fmaxf(mt, sv[u][i]);
+        if constexpr (MASK) {
+          const int key = 16 * (sj * NT + u) + 4 * grp + i;
+          s[u][i] = key <= pos ? s[u][i] : -INFINITY;
+        }
+        mt = fmaxf(mt, s[u][i]);
       }
     mt = fmaxf(mt, __shfl_xor(mt, 16, WAVE));
     mt = fmaxf(mt, __shfl_xor(mt, 32, WAVE));
-    const float mn = fmaxf(m, mt);
-    const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+    const float mn2 = fmaxf(m2, mt * scale2);
+    const float alpha = __builtin_amdgcn_exp2f(m2 - mn2);
     float ls = 0.f;
-    i16x4 phi[NT], plo[NT];
+    i16x4 pb[NT];
 #pragma unroll
     for (int u = 0; u < NT; ++u)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float pv = sv[u][i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[u][i] - mn);
+        const float pv = __builtin_amdgcn_exp2f(fmaf(s[u][i], scale2, -mn2));
         ls += pv;
-        const __bf16 h = static_cast<__bf16>(pv);
-        phi[u][i] = __builtin_bit_cast(short, h);
-        plo[u][i] = __builtin_bit_cast(short, static_cast<__bf16>(pv - static_cast<float>(h)));
+        pb[u][i] = __builtin_bit_cast(short, static_cast<__bf16>(pv));
       }
     ls += __shfl_xor(ls, 16, WAVE);
     ls += __shfl_xor(ls, 32, WAVE);
-    l = l * alpha + ls;
-    m = mn;
+    l = fmaf(l, alpha, ls);
+    m2 = mn2;
+    if (__any(alpha != 1.f)) {   // a column's maximum moved: rescale the sums
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      f32x4 acc = o[dt] * alpha;
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    }
 #pragma unroll
-      for (int u = 0; u < NT; ++u) {
-        const i16x4 a =
-            *reinterpret_cast<const i16x4*>(vt + u * VTILE + (16 * dt + col) * VP + 4 * grp);
-        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, phi[u], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, plo[u], acc, 0, 0, 0);
-      }
-      o[dt] = acc;
+    for (int v = 0; v < NT / 2; ++v) {
+      const bf16x8 pp =
+          __builtin_bit_cast(bf16x8, __builtin_shufflevector(pb[2 * v], pb[2 * v + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt][v], pp, o[dt], 0, 0, 0);
     }
     if (sj + 1 < nsteps) { PA_PUT(b ^ 1) }
     __syncthreads();
-  }
+  };
+
+  PA_FETCH(0)
+  PA_PUT(0)
+  __syncthreads();
+  int sj = 0;
+  for (; sj < nfree; ++sj) step(sj, std::false_type{});
+  for (; sj < nsteps; ++sj) step(sj, std::true_type{});
 #undef PA_FETCH
 #undef PA_PUT
   if (tr < p.T) {

@@ -80,23 +80,29 @@ def bf16_act(x64):
     return bf16_to_f64(f32_to_bf16_bits(to_f32(x64)))
 
 
-def causal_attend(Q, K, V, p0):
+def causal_attend(Q, K, V, p0, act=None):
     """Causal attention over a chunk in matrix form.  Q [T, nq, hd] (rows at
     positions p0 .. p0+T-1); K, V [nkv, p0+T, hd].  Row t sees cache rows
     0 .. p0+t: S = Q K^T / sqrt(hd) with the rows past p0+t masked out, a row
-    softmax, O = P V.  Returns O [T, nq, hd]."""
+    softmax, O = P V.  Returns O [T, nq, hd].
+
+    `act` rounds the two operands the matrix cores take besides the cached K and
+    V: q, and the softmax weights W = e^(S - row max) before they multiply V;
+    the row sum that normalises O adds the unrounded weights.  act=None keeps
+    both exact (O is then the plain softmax(S) V)."""
+    act = act or (lambda a: a)
     T, nq, hd = Q.shape
     nkv, n, _ = K.shape
     G = nq // nkv
     visible = np.arange(n)[None, :] <= (p0 + np.arange(T))[:, None]     # [T, n]
+    Qa = act(Q)
     O = np.empty((T, nq, hd), dtype=np.float64)
     for h in range(nq):
         g = h // G
-        S = (Q[:, h, :] @ K[g].T) / math.sqrt(hd)
+        S = (Qa[:, h, :] @ K[g].T) / math.sqrt(hd)
         S = np.where(visible, S, -np.inf)
         W = np.exp(S - S.max(axis=1, keepdims=True))
-        W /= W.sum(axis=1, keepdims=True)
-        O[:, h, :] = W @ V[g]
+        O[:, h, :] = (act(W) @ V[g]) / W.sum(axis=1, keepdims=True)
     return O
 
 
@@ -214,7 +220,8 @@ class Decoder:
         rounds the operands the matrix cores take in prefill: the normed rows,
         the attention output and the SwiGLU output (bf16); the residual stays
         f32 between sublayers, every sum is f64.  act=None keeps them exact,
-        which must reproduce the decode steps row by row."""
+        which must reproduce the decode steps row by row.  In attention `act`
+        also rounds q and the softmax weights (causal_attend)."""
         act = act or (lambda a: a)
         c = self.cfg
         L = self.m["layers"][l]
@@ -232,7 +239,7 @@ class Decoder:
         self.V[l][:, p0:p0 + T] = round_cache(Vn.transpose(1, 0, 2), c.kvdtype)
         Kc = widen_cache(self.K[l][:, :p0 + T], c.kvdtype)
         Vc = widen_cache(self.V[l][:, :p0 + T], c.kvdtype)
-        O = causal_attend(Q, Kc, Vc, p0).reshape(T, nq * hd)
+        O = causal_attend(Q, Kc, Vc, p0, act).reshape(T, nq * hd)
         X = to_f32(X + act(O) @ self.W(l, "w_o").T).astype(np.float64)
         H2 = act(rmsnorm(X, L["g_ffn"], c.eps))
         GU = H2 @ self.W(l, "w_gu").T
