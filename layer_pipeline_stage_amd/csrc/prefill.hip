@@ -227,13 +227,14 @@ __global__ void k_pf_rope_append(float* qkv, int T, int nq, int nkv, int hd, int
 }
 
 // ---- 4. causal attention of the chunk on the matrix cores -----------------------------------
-// The decode tile kernel's products with 16 query columns per wave: a workgroup
-// takes kv head g and PA_WAVES * R query rows (R = 16 / G), wave w the rows
-// t0 + w R .. t0 + w R + R - 1, its column c = r G + j being q head g G + j of
-// row t0 + w R + r.  The workgroup walks the key tiles (16 cache rows each) from
+// The decode tile kernel's products with CB blocks of 16 query columns per wave
+// (CB = 2, 1 for head dim 256): a workgroup takes kv head g and PA_WAVES CB R
+// query rows (R = 16 / G); block b of wave w has the rows t0 + (w CB + b) R ..
+// + R - 1, its column c = r G + j being q head g G + j of the block's row r.  Each
+// K and V operand read from LDS feeds the products of all CB blocks.  The workgroup walks the key tiles (16 cache rows each) from
 // row 0 to its last row's position; each tile of K and V is loaded from HBM / L2
-// once per workgroup into LDS (double-buffered through registers: tile j + 1 is
-// fetched while tile j is multiplied, one barrier per step) and every wave forms,
+// once per workgroup into LDS (double-buffered through registers: step j + 1 is
+// fetched while step j is multiplied, one barrier per step) and every wave forms,
 // with an online softmax per column (in base 2: the scale carries log2 e),
 //   S^T[16 keys, 16 cols] = K_tile . Q^T          (16x16x32 bf16, q as bf16)
 //   O^T[hd, 16 cols]     += V_pair^T . P_pair^T   (16x16x32 bf16, p as bf16)
@@ -259,18 +260,24 @@ constexpr int PA_THREADS = PA_WAVES * WAVE;
 #ifndef LPS_PA_KT
 #define LPS_PA_KT 4
 #endif
-constexpr int PA_KT = LPS_PA_KT;   // 16-row key tiles per step (one softmax update, one barrier)
-static_assert(PA_KT % 2 == 0, "PV takes the key tiles in pairs");
+// 16-row key tiles per step (one softmax update, one barrier); head dim 256 takes
+// half as many so that a step's operands stay in registers
+constexpr int pa_nt(int hd) { return hd >= 256 ? LPS_PA_KT / 2 : LPS_PA_KT; }
+static_assert(LPS_PA_KT % 4 == 0, "PV takes the key tiles in pairs");
 typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+// column blocks (16 columns each) per wave: two share every K and V operand read
+constexpr int pa_cb(int hd) { return hd >= 256 ? 1 : 2; }
 
 template <int HD, int G>
 __global__ __launch_bounds__(PA_THREADS) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void k_pf_attn(PaP p) {
   constexpr int KK = HD / 32, DT = HD / 16, R = 16 / G;
+  constexpr int CB = pa_cb(HD);                 // column blocks per wave
   constexpr int TILE = 16 * HD;                 // elements of one K (or V) 16-row tile
   constexpr int VP = 20;                        // LDS row of a V^T tile: 16 keys + 4 pad
   constexpr int VTILE = HD * VP;                // LDS elements of one V tile
-  constexpr int NT = PA_KT;                     // tiles per step
+  constexpr int NT = pa_nt(HD);                 // tiles per step
   constexpr int BUF = NT * (TILE + VTILE);      // LDS elements of one step buffer
   constexpr int CK = NT * TILE / 8;             // 16-byte chunks of a step's K (and of its V) tiles
   static_assert(CK % PA_THREADS == 0, "whole chunks of K and of V per thread");
@@ -283,27 +290,33 @@ void k_pf_attn(PaP p) {
   const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
   const int col = lane & 15, grp = lane >> 4;
   const int g = blockIdx.y;
-  const int tb = blockIdx.x * PA_WAVES * R;     // the workgroup's first row
+  const int tb = blockIdx.x * PA_WAVES * CB * R;   // the workgroup's first row
   const int r = col / G, hh = col - r * G;
-  const int tr = tb + w * R + r;
-  const int t = min(tr, p.T - 1);               // rows past T: a valid row's copy, never stored
-  const int pos = p.p0 + t;
-  const int last = p.p0 + min(tb + PA_WAVES * R, p.T) - 1;   // the workgroup's last position
+  int tr[CB], pos[CB];
+#pragma unroll
+  for (int b = 0; b < CB; ++b) {
+    tr[b] = tb + (w * CB + b) * R + r;
+    pos[b] = p.p0 + min(tr[b], p.T - 1);        // rows past T: a valid row's copy, never stored
+  }
+  const int last = p.p0 + min(tb + PA_WAVES * CB * R, p.T) - 1;   // the workgroup's last position
   const int nsteps = (last >> 4) / NT + 1;
   // steps whose keys every row of the workgroup sees (no mask): keys < p0 + tb + 1
   const int nfree = min((p.p0 + tb + 1) / (16 * NT), nsteps);
   // scores in base 2: e^(s / sqrt(hd) - m) = 2^(s log2(e) / sqrt(hd) - m'), one v_exp_f32 each
   const float scale2 = p.scale * 1.44269504088896341f;
 
-  // B operand of S^T: q of column col, dims 32 kk + 8 grp .. + 7, as bf16
-  const float* qrow = p.q + (long long)t * p.qs + (long long)(g * G + hh) * HD + 8 * grp;
-  bf16x8 qb[KK];
+  // B operands of S^T: q of column col of each block, dims 32 kk + 8 grp .. + 7, as bf16
+  bf16x8 qb[CB][KK];
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
-    const f32x4 q0 = *reinterpret_cast<const f32x4*>(qrow + 32 * kk);
-    const f32x4 q1 = *reinterpret_cast<const f32x4*>(qrow + 32 * kk + 4);
+  for (int b = 0; b < CB; ++b) {
+    const float* qrow = p.q + (long long)(pos[b] - p.p0) * p.qs + (long long)(g * G + hh) * HD + 8 * grp;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qb[kk][e] = static_cast<__bf16>(e < 4 ? q0[e] : q1[e - 4]);
+    for (int kk = 0; kk < KK; ++kk) {
+      const f32x4 q0 = *reinterpret_cast<const f32x4*>(qrow + 32 * kk);
+      const f32x4 q1 = *reinterpret_cast<const f32x4*>(qrow + 32 * kk + 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qb[b][kk][e] = static_cast<__bf16>(e < 4 ? q0[e] : q1[e - 4]);
+    }
   }
   const long long head = (long long)g * p.ctx_max * HD;     // elements before kv head g
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
@@ -329,44 +342,92 @@ void k_pf_attn(PaP p) {
     stk[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0)); \
     stv[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0)); \
   }
-#define PA_PUT(B)                                                                             \
+#define PA_PUT(BUFI)                                                                          \
   _Pragma("unroll") for (int c = 0; c < LPT; ++c) {                                           \
-    *reinterpret_cast<u32x4*>(kv_lds + (B) * BUF + (tid + c * PA_THREADS) * 8) = stk[c];       \
-    uint16_t* dst = kv_lds + (B) * BUF + vdst[c];                                             \
+    *reinterpret_cast<u32x4*>(kv_lds + (BUFI) * BUF + (tid + c * PA_THREADS) * 8) = stk[c];    \
+    uint16_t* dst = kv_lds + (BUFI) * BUF + vdst[c];                                          \
     *reinterpret_cast<u32x2*>(dst) = u32x2{stv[c].x, stv[c].y};                               \
     *reinterpret_cast<u32x2*>(dst + 4) = u32x2{stv[c].z, stv[c].w};                           \
   }
 
-  f32x4 o[DT];
+  f32x4 o[CB][DT];
+  float m2[CB], l[CB];   // running max of the base-2 scores, sum of weights
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m2 = -INFINITY, l = 0.f;   // running max of the base-2 scores, sum of weights
+  for (int b = 0; b < CB; ++b) {
+    m2[b] = -INFINITY;
+    l[b] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[b][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   // One step: NT key tiles.  The first step holds key 0, which every row sees, so
   // the running max is finite from then on and a masked score (-inf) gives a zero
   // weight through exp2 without any select.
   auto step = [&](int sj, auto masked) {
     constexpr bool MASK = decltype(masked)::value;
-    const int b = sj & 1;
+    const int bi = sj & 1;
     if (sj + 1 < nsteps) { PA_FETCH(sj + 1) }
-    const uint16_t* kt = kv_lds + b * BUF;
+    const uint16_t* kt = kv_lds + bi * BUF;
     const uint16_t* vt = kt + NT * TILE;
-    bf16x8 ka[NT][KK];
-#pragma unroll
-    for (int u = 0; u < NT; ++u)
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-        ka[u][kk] = *reinterpret_cast<const bf16x8*>(kt + u * TILE + (4 * kk + grp) * 128 + col * 8);
-    f32x4 s[NT];
+    f32x4 s[CB][NT];
 #pragma unroll
     for (int u = 0; u < NT; ++u) {
-      s[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-        s[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[u][kk], qb[kk], s[u], 0, 0, 0);
+      for (int b = 0; b < CB; ++b) s[b][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + u * TILE + (4 * kk + grp) * 128 + col * 8);
+#pragma unroll
+        for (int b = 0; b < CB; ++b)
+          s[b][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[b][kk], s[b][u], 0, 0, 0);
+      }
     }
-    // V operands of the tile pairs, read while the softmax runs
-    bf16x8 va[DT][NT / 2];
+    bf16x8 pp[CB][NT / 2];   // B operands of the tile pairs
+    bool moved = false;
+    float alpha[CB];
+#pragma unroll
+    for (int b = 0; b < CB; ++b) {
+      float mt = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < NT; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (MASK) {
+            const int key = 16 * (sj * NT + u) + 4 * grp + i;
+            s[b][u][i] = key <= pos[b] ? s[b][u][i] : -INFINITY;
+          }
+          mt = fmaxf(mt, s[b][u][i]);
+        }
+      mt = fmaxf(mt, __shfl_xor(mt, 16, WAVE));
+      mt = fmaxf(mt, __shfl_xor(mt, 32, WAVE));
+      const float mn2 = fmaxf(m2[b], mt * scale2);
+      alpha[b] = __builtin_amdgcn_exp2f(m2[b] - mn2);
+      moved |= alpha[b] != 1.f;
+      float ls = 0.f;
+      i16x4 pb[NT];
+#pragma unroll
+      for (int u = 0; u < NT; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pv = __builtin_amdgcn_exp2f(fmaf(s[b][u][i], scale2, -mn2));
+          ls += pv;
+          pb[u][i] = __builtin_bit_cast(short, static_cast<__bf16>(pv));
+        }
+      ls += __shfl_xor(ls, 16, WAVE);
+      ls += __shfl_xor(ls, 32, WAVE);
+      l[b] = fmaf(l[b], alpha[b], ls);
+      m2[b] = mn2;
+#pragma unroll
+      for (int v = 0; v < NT / 2; ++v)
+        pp[b][v] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(pb[2 * v], pb[2 * v + 1], 0, 1, 2, 3,
+                                                                       4, 5, 6, 7));
+    }
+    if (__any(moved)) {   // a column's maximum moved: rescale the sums
+#pragma unroll
+      for (int b = 0; b < CB; ++b)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[b][dt] *= alpha[b];
+    }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -374,50 +435,12 @@ void k_pf_attn(PaP p) {
         const uint16_t* vp = vt + (16 * dt + col) * VP + 4 * grp;
         const i16x4 a0 = *reinterpret_cast<const i16x4*>(vp + (2 * v) * VTILE);
         const i16x4 a1 = *reinterpret_cast<const i16x4*>(vp + (2 * v + 1) * VTILE);
-        va[dt][v] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int b = 0; b < CB; ++b)
+          o[b][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pp[b][v], o[b][dt], 0, 0, 0);
       }
-    float mt = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < NT; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if constexpr (MASK) {
-          const int key = 16 * (sj * NT + u) + 4 * grp + i;
-          s[u][i] = key <= pos ? s[u][i] : -INFINITY;
-        }
-        mt = fmaxf(mt, s[u][i]);
-      }
-    mt = fmaxf(mt, __shfl_xor(mt, 16, WAVE));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, WAVE));
-    const float mn2 = fmaxf(m2, mt * scale2);
-    const float alpha = __builtin_amdgcn_exp2f(m2 - mn2);
-    float ls = 0.f;
-    i16x4 pb[NT];
-#pragma unroll
-    for (int u = 0; u < NT; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pv = __builtin_amdgcn_exp2f(fmaf(s[u][i], scale2, -mn2));
-        ls += pv;
-        pb[u][i] = __builtin_bit_cast(short, static_cast<__bf16>(pv));
-      }
-    ls += __shfl_xor(ls, 16, WAVE);
-    ls += __shfl_xor(ls, 32, WAVE);
-    l = fmaf(l, alpha, ls);
-    m2 = mn2;
-    if (__any(alpha != 1.f)) {   // a column's maximum moved: rescale the sums
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-    }
-#pragma unroll
-    for (int v = 0; v < NT / 2; ++v) {
-      const bf16x8 pp =
-          __builtin_bit_cast(bf16x8, __builtin_shufflevector(pb[2 * v], pb[2 * v + 1], 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt][v], pp, o[dt], 0, 0, 0);
-    }
-    if (sj + 1 < nsteps) { PA_PUT(b ^ 1) }
+    if (sj + 1 < nsteps) { PA_PUT(bi ^ 1) }
     __syncthreads();
   };
 
@@ -429,14 +452,17 @@ void k_pf_attn(PaP p) {
   for (; sj < nsteps; ++sj) step(sj, std::true_type{});
 #undef PA_FETCH
 #undef PA_PUT
-  if (tr < p.T) {
-    const float inv = 1.0f / l;
-    uint16_t* dst = p.ob + (long long)t * p.nq * HD + (long long)(g * G + hh) * HD + 4 * grp;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const uint32_t lo = f32_to_bf16(o[dt][0] * inv) | (uint32_t)f32_to_bf16(o[dt][1] * inv) << 16;
-      const uint32_t hi = f32_to_bf16(o[dt][2] * inv) | (uint32_t)f32_to_bf16(o[dt][3] * inv) << 16;
-      *reinterpret_cast<u32x2*>(dst + 16 * dt) = u32x2{lo, hi};
+  for (int b = 0; b < CB; ++b) {
+    if (tr[b] < p.T) {
+      const float inv = 1.0f / l[b];
+      uint16_t* dst = p.ob + (long long)tr[b] * p.nq * HD + (long long)(g * G + hh) * HD + 4 * grp;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const uint32_t lo = f32_to_bf16(o[b][dt][0] * inv) | (uint32_t)f32_to_bf16(o[b][dt][1] * inv) << 16;
+        const uint32_t hi = f32_to_bf16(o[b][dt][2] * inv) | (uint32_t)f32_to_bf16(o[b][dt][3] * inv) << 16;
+        *reinterpret_cast<u32x2*>(dst + 16 * dt) = u32x2{lo, hi};
+      }
     }
   }
 }
@@ -461,9 +487,9 @@ static int gemm(const uint16_t* a, const uint16_t* b, void* out, int T, int N, i
 
 template <int HD, int G>
 static int attn_go(const PaP& p, hipStream_t st) {
-  const int R = 16 / G;
-  const dim3 grid((p.T + PA_WAVES * R - 1) / (PA_WAVES * R), p.nkv);
-  const size_t lds = size_t(2) * PA_KT * (16 * HD + 20 * HD) * 2;
+  const int rows = PA_WAVES * pa_cb(HD) * (16 / G);   // rows per workgroup
+  const dim3 grid((p.T + rows - 1) / rows, p.nkv);
+  const size_t lds = size_t(2) * pa_nt(HD) * (16 * HD + 20 * HD) * 2;
   int rc = ensure_lds((const void*)k_pf_attn<HD, G>, lds);
   if (rc) return rc;
   hipLaunchKernelGGL((k_pf_attn<HD, G>), grid, dim3(PA_THREADS), lds, st, p);

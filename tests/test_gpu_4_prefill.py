@@ -59,16 +59,30 @@ def _argmax_ok(a, logits, tol=TOL):
     return top2[1] - top2[0] <= 2 * scale and logits[a] >= top2[1] - 2 * scale
 
 
-def test_prefill_matches_oracle(rt, small):
-    dd = rt.DeviceDecoder(small)
-    lg, am, X = dd.prefill(small["prompt"])
-    olg, oam, OX = Decoder(small).prefill(small["prompt"])
-    elg, _, EX = Decoder(small).prefill(small["prompt"], act=None)
+def _check_prefill(rt, m):
+    dd = rt.DeviceDecoder(m)
+    lg, am, X = dd.prefill(m["prompt"])
+    olg, oam, OX = Decoder(m).prefill(m["prompt"])
+    elg, _, EX = Decoder(m).prefill(m["prompt"], act=None)
     for got, want, exact, what in ((X, OX, EX, "hidden rows"), (lg, olg, elg, "logits")):
         err = float(np.max(np.abs(np.asarray(got, np.float64) - want)))
         assert err <= _pf_tol(exact, want), (what, err, _pf_tol(exact, want))
     assert am == oam or _argmax_ok(am, olg, 2 * _pf_tol(elg, olg) / np.abs(olg).max())
     dd.close()
+
+
+def test_prefill_matches_oracle(rt, small):
+    _check_prefill(rt, small)
+
+
+# the other built head dims and group sizes of the attention kernel: head dim 256
+# with 8 q heads per kv head (two key tiles per step, V operands read when used),
+# head dim 128 with one; ragged prompts after ragged prefixes
+@pytest.mark.parametrize("hd,nq,nkv,prefix,prompt", [(256, 8, 1, 21, 39), (128, 2, 2, 50, 70)])
+def test_prefill_other_head_shapes_match_oracle(rt, hd, nq, nkv, prefix, prompt):
+    cfg = replace(PF, name=f"pf-hd{hd}-g{nq // nkv}", n_layers=2, nq=nq, nkv=nkv, hd=hd,
+                  prefix=prefix, prompt=prompt)
+    _check_prefill(rt, synth.make_dense(cfg))
 
 
 @pytest.mark.parametrize("streams", ["single", "per-stage"])
