@@ -279,7 +279,10 @@ int lps_rmsnorm(const float* x, const float* g, float eps, int32_t d, float* y, 
  *  mode LPS_EPI_SWIGLU: y[i] = silu(r_i) * r_{N/2+i}, i < N/2, r = W x' (N even)
  * W (dev) [N, K] of wdtype, s (dev) its e8m0 scales for LPS_MXFP4.  x (dev)
  * [K] f32.  The K tail is handled per 32-value group for MXFP4 (no read past a
- * row's end whatever K % 128 is: TP3 plan, Implementation status, item 1). */
+ * row's end whatever K % 128 is: TP3 plan, Implementation status, item 1).
+ * MXFP4 rows meet x' as an f16 operand (rounded once to nearest; f32
+ * accumulation), f32 and bf16 rows meet it in f32.  MXFP4 K is at most 24576
+ * (LPS_EUNSUP beyond). */
 int lps_gemv(int32_t wdtype, const void* w, const uint8_t* s, int32_t N, int32_t K,
              const float* x, const float* norm_g, float eps, float* y, int32_t mode, void* stream);
 /* A3+A4+A5: q (dev [nq*hd] f32) = RoPE(W_q h); RoPE(W_k h) and W_v h are written

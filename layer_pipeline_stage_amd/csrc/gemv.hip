@@ -280,8 +280,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const uint8_t* base, 
   _Pragma("unroll") for (int i = 0; i < U; ++i) {                  \
     const int c = (B0) + lane + WAVE * i;                          \
     const int xi = c < nck ? (XO) + c * XS : zoff;                 \
-    acc_chunk<WT>(V0[i], S0[i], xs + xi, a0);                      \
-    acc_chunk<WT>(V1[i], S1[i], xs + xi, a1);                      \
+    if constexpr (WT == LPS_MXFP4) {                               \
+      acc_chunk_mx16(V0[i], S0[i], xh + xi, a0);                   \
+      acc_chunk_mx16(V1[i], S1[i], xh + xi, a1);                   \
+    } else {                                                       \
+      acc_chunk<WT>(V0[i], S0[i], xs + xi, a0);                    \
+      acc_chunk<WT>(V1[i], S1[i], xs + xi, a1);                    \
+    }                                                              \
   }
 // One step of the double-buffered walk: issue the loads of the batch after the
 // current one (into buffer N), then consume the current batch (buffer C).  A
@@ -308,7 +313,8 @@ template <int WT, int EPI, int U, bool NORM, int NT, bool DB>
 __global__ __launch_bounds__(NT) void k_gemv_buf(GemvP p) {
   extern __shared__ float xs[];
   constexpr int CH = Fmt<WT>::CH;
-  constexpr int XS = WT == LPS_MXFP4 ? MX_XS : CH;   // staged floats per chunk
+  constexpr int XS = WT == LPS_MXFP4 ? MX16_XS : CH;   // staged floats (MXFP4: halves) per chunk
+  _Float16* const xh = reinterpret_cast<_Float16*>(xs);   // the MXFP4 staging (f16)
   constexpr int NW = NT / WAVE;
   const int lane = threadIdx.x & (WAVE - 1);
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
@@ -325,7 +331,7 @@ __global__ __launch_bounds__(NT) void k_gemv_buf(GemvP p) {
   // a chunk past the row end (zero weights) reads the zero chunk after the staged vector
   const int zoff = WT == LPS_MXFP4 ? nck * XS : staged_len<EPI>(p);
   if constexpr (WT == LPS_MXFP4) {
-    stage_x_mx<NORM, NT>(p.x, p.g, p.eps, p.K, xs);
+    stage_x_mx16<NORM, NT, mx16_maxr(U, NT)>(p.x, p.g, p.eps, p.K, xh);
   } else {
     if (threadIdx.x < CH) xs[zoff + threadIdx.x] = 0.f;   // zero chunk
     // MoE down: a workgroup's units all belong to one slot (the launch gives every
@@ -411,11 +417,13 @@ template <int WT, int EPI, bool NORM>
 static int launch_t(const GemvP& p, hipStream_t st, Stamp sp, int* waves) {
   constexpr int CH = Fmt<WT>::CH;
   const int per_lane = (p.K / CH + WAVE - 1) / WAVE;
-  const size_t lds = WT == LPS_MXFP4 ? size_t(p.K / CH + 1) * MX_XS * sizeof(float)
+  const size_t lds = WT == LPS_MXFP4 ? size_t(p.K / CH + 1) * MX16_XS * sizeof(_Float16)
                                      : (size_t(staged_len<EPI>(p)) + CH) * sizeof(float);
 #define LPS_GOB(UU, NTV, MAXBV)                                                                  \
   do {                                                                                           \
     constexpr int NW_ = (NTV) / WAVE;                                                            \
+    if (WT == LPS_MXFP4 && p.K / 4 > mx16_maxr(UU, NTV) * (NTV))                                \
+      return fail(LPS_EUNSUP, "gemv: MXFP4 K %d above %d", p.K, 4 * mx16_maxr(UU, NTV) * (NTV)); \
     int grid = (p.units + NW_ - 1) / NW_;                                                        \
     if (EPI != EPI_MOEDN && grid > (MAXBV)) grid = (MAXBV);  /* MoE down: one unit per wave */   \
     if (grid < 1) grid = 1;                                                                      \

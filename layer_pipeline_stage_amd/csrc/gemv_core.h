@@ -191,4 +191,90 @@ __device__ __forceinline__ void stage_x_mx(const float* x, const float* g, float
   }
 }
 
+// MXFP4 rows against f16 activations.  The activation vector is staged in LDS as
+// f16 (rounded once, to nearest even, after the optional RMSNorm in f32), 32-value
+// chunks at a pitch of 40 halves (80 bytes: lane l reads the x of its own weight
+// chunk, so lanes are a chunk apart; at 80 bytes sixteen consecutive lanes cover
+// distinct 16-byte bank groups).  Each byte of codes becomes two f16 weights in
+// one scaled conversion (exact: an e2m1 value times a power of two), and each
+// pair meets its two activations in one dot2 with f32 accumulation, so a weight
+// costs one VALU operation instead of the f32 path's one and a half.  The chunk
+// after the last (index K / 32) is zero.
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+constexpr int MX16_XS = 40;     // halves per staged MXFP4 chunk (32 values + 8 pad)
+// x float4 groups per thread held across the norm's sum: a launch with U chunks per
+// lane covers rows of up to U * 64 chunks (512 U groups); U = 4 is the launch for
+// longer rows, which holds 12 groups per thread
+constexpr int mx16_maxr(int U, int NT) { return U == 4 ? 12 : (512 * U + NT - 1) / NT; }
+
+__device__ __forceinline__ void acc_chunk_mx16(const u32x4 v, uint32_t sb, const _Float16* xh, float& a) {
+  const float sc = e8m0_to_f32(sb);
+  const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const h8 xv = *reinterpret_cast<const h8*>(xh + 8 * q);
+    // byte b of the word: element 2b (low nibble) then 2b + 1, times the group scale
+    a = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[q], sc, 0),
+                               h2{xv[0], xv[1]}, a, false);
+    a = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[q], sc, 1),
+                               h2{xv[2], xv[3]}, a, false);
+    a = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[q], sc, 2),
+                               h2{xv[4], xv[5]}, a, false);
+    a = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[q], sc, 3),
+                               h2{xv[6], xv[7]}, a, false);
+  }
+}
+
+// Stage x as f16 chunks (see above); with NORM, as RMSNorm(x) * g computed in f32
+// (the same v * r * g order as stage_x) before the rounding.  K % 32 == 0 and
+// K / 4 <= MAXR * NT (the launch checks it).
+template <bool NORM, int NT, int MAXR>
+__device__ __forceinline__ void stage_x_mx16(const float* x, const float* g, float eps, int K,
+                                             _Float16* xs) {
+  constexpr int NW = NT / WAVE;
+  const int tid = threadIdx.x;
+  const int ng = K / 4;
+  f32x4 v[MAXR];
+#pragma unroll
+  for (int i = 0; i < MAXR; ++i) {
+    const int G = tid + i * NT;
+    v[i] = G < ng ? *reinterpret_cast<const f32x4*>(x + 4 * G) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  float r = 1.f;
+  if (NORM) {
+    __shared__ float red[NW];
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXR; ++i) ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+    ss = wave_sum(ss);
+    if ((tid & (WAVE - 1)) == 0) red[tid / WAVE] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) tot += red[i];
+    r = 1.0f / sqrtf(tot / float(K) + eps);
+  }
+#pragma unroll
+  for (int i = 0; i < MAXR; ++i) {
+    const int G = tid + i * NT;
+    if (G < ng) {
+      f32x4 y = v[i];
+      if (NORM) {
+        const f32x4 gg = *reinterpret_cast<const f32x4*>(g + 4 * G);
+        y.x = y.x * r * gg.x;
+        y.y = y.y * r * gg.y;
+        y.z = y.z * r * gg.z;
+        y.w = y.w * r * gg.w;
+      }
+      // float4 G = values 4G .. 4G + 3: chunk G / 8, halves 4 (G % 8) ..
+      _Float16* dst = xs + (G >> 3) * MX16_XS + 4 * (G & 7);
+      *reinterpret_cast<h2*>(dst) = h2{(_Float16)y.x, (_Float16)y.y};
+      *reinterpret_cast<h2*>(dst + 2) = h2{(_Float16)y.z, (_Float16)y.w};
+    }
+  }
+  if (tid < 16) *reinterpret_cast<h2*>(xs + (K / 32) * MX16_XS + 2 * tid) = h2{0, 0};   // zero chunk
+  __syncthreads();
+}
+
 }  // namespace lps

@@ -83,6 +83,11 @@ def test_gemv_parity(L, wdtype, N, K, mode, norm):
     bound = dot_bound(W64, xp)
     if norm:
         bound += 8 * 2.0 ** -24 * (np.abs(W64) @ np.abs(xp))
+    if wdtype == "mxfp4":
+        # MXFP4 rows meet x as f16 operands (one dot2 per weight pair): x is rounded
+        # to nearest once, relative error <= 2^-11 (absolute <= 2^-25 below f16's
+        # normal range)
+        bound += 2.0 ** -11 * (np.abs(W64) @ np.abs(xp)) + 2.0 ** -25 * np.abs(W64).sum(axis=1)
     y0 = rng.standard_normal(N).astype(np.float32)
     if mode == "store":
         ref, n_out = r, N
@@ -159,6 +164,25 @@ def test_mxfp4_builtin_nibble_order(L):
     cd, sd, xd = dev(codes), dev(scales), dev(x)
     L.lps_gemv(L.LPS_MXFP4, ptr(cd), ptr(sd), N, K, ptr(xd), None, 0.0, ptr(yd), 0, stream())
     assert np.array_equal(yd.cpu().numpy(), x[:N])
+
+
+def test_mxfp4_gemv_refuses_rows_past_its_staging(L):
+    """The MXFP4 GEMV stages x from registers held across the norm's sum, so K is
+    bounded (24576); a longer row is refused before anything is enqueued (the
+    buffers are sized for it all the same)."""
+    N, K = 2, 24576 + 32
+    codes = np.zeros((N, K // 2), np.uint8)
+    scales = np.full((N, K // 32), 127, np.uint8)
+    x = np.ones(K, np.float32)
+    yd = torch.zeros(N, dtype=torch.float32, device=DEV)
+    cd, sd, xd = dev(codes), dev(scales), dev(x)
+    with pytest.raises(L.LpsError) as e:
+        L.lps_gemv(L.LPS_MXFP4, ptr(cd), ptr(sd), N, K, ptr(xd), None, 0.0, ptr(yd), 0, stream())
+    assert e.value.code == L.LPS_EUNSUP
+    K = 24576                                            # the longest row runs
+    L.lps_gemv(L.LPS_MXFP4, ptr(cd), ptr(sd), N, K, ptr(xd), None, 0.0, ptr(yd), 0, stream())
+    torch.cuda.synchronize()
+    assert np.array_equal(yd.cpu().numpy(), np.zeros(N, np.float32))
 
 
 def test_rmsnorm_and_embed(L):
