@@ -44,6 +44,12 @@ def test_dense_staged_equals_unstaged_and_oracle(rt, dense):
     assert c["stage_walks"] == 4 * n and c["boundary_sends"] == 3 * n
     assert got.argmax == ref.argmax
     assert all(np.array_equal(a, b) for a, b in zip(got.logits, ref.logits))
+    # the benchmark's launch form: N = 4 on one stream, the whole step captured once
+    # and replayed with the position and next id advanced on the device
+    dd.reset()
+    gr = dd.run_tokens_graph(start, cfg.steps)
+    assert gr.fed == got.fed and gr.argmax == got.argmax
+    assert all(np.array_equal(a, b) for a, b in zip(gr.logits, got.logits))
     dd.close()
     # teacher-forced oracle on the first 2 steps (bf16 weights: 2e-3 of the logit scale)
     dec = Decoder(dense, weight_cache=False)
