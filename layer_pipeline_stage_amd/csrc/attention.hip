@@ -2,14 +2,15 @@
 //
 // q head h reads kv head h / G, G = nq / nkv (TP3 zero-padded dummy heads plan,
 // Implementation status item 2 and Geometry: the GQA map is part of the
-// weights).  One workgroup takes one (kv head, 64-row chunk) tile: the chunk's
-// K and V rows are streamed once from HBM with 16-byte loads and reused by all
-// G query heads of the group; scores are reduced across the lanes of a row by
-// DPP row operations, the chunk softmax (max, sum) by wave reductions, and the
-// weighted V sum is formed in registers and summed over row slots in LDS.  Each tile
-// writes (m, l, o) partials; a second small launch merges every q head's chunks
-// in chunk order, so the result does not depend on the order the tiles ran in
-// (and no tile waits on, or fences for, another).
+// weights).  One workgroup takes one (kv head, ATT_CH-row chunk) tile: the
+// chunk's K and V rows are streamed once from HBM and reused by all G query
+// heads of the group.  bf16 caches (16-row operand-order tiles) run on the
+// matrix cores (k_attn_mfma); f32 caches on the VALU (k_attn: scores reduced
+// across the lanes of a row by DPP row operations, the weighted V sum formed in
+// registers and summed over row slots in LDS).  Each tile writes (m, l, o)
+// partials; a second small launch merges every q head's chunks in chunk order,
+// so the result does not depend on the order the tiles ran in (and no tile
+// waits on, or fences for, another).
 #include "dev.h"
 #include "internal.h"
 
@@ -82,7 +83,7 @@ __device__ __forceinline__ void widen16(const u32x4 v, float* out) {
 // of them go out first (one HBM round trip per tile).  The G query heads'
 // matching elements stay in registers.  Scores are summed over the LPR lanes of
 // a row with DPP steps; the chunk softmax (max, sum) is one wave per head over
-// the 64 rows; the weighted V sum is formed in registers from the thread's own
+// the ATT_CH rows; the weighted V sum is formed in registers from the thread's own
 // V rows and summed over the RPP row slots through LDS, in slot order.
 template <int HD, int KVT, int G>
 __global__ __launch_bounds__(ATT_THREADS) void k_attn(AttnP p) {

@@ -1,6 +1,7 @@
 // Shared pieces of the weight-streaming kernels: chunk formats, the per-chunk
-// multiply-accumulate for f32 / bf16 / MXFP4 weights, and the LDS staging of the
-// (optionally RMS-normalised) activation vector.
+// multiply-accumulate for f32 / bf16 weights (f32 activations) and MXFP4 weights
+// (f16 activations), and the LDS staging of the (optionally RMS-normalised)
+// activation vector.
 #pragma once
 
 #include "dev.h"
@@ -23,8 +24,10 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
   return __uint_as_float((s << 23) | edge);
 }
 
+// one chunk of f32 or bf16 weights against its staged f32 activations (sb unused)
 template <int WT>
 __device__ __forceinline__ void acc_chunk(const u32x4 v, uint32_t sb, const float* xs, float& a) {
+  static_assert(WT == LPS_F32 || WT == LPS_BF16, "MXFP4 chunks: acc_chunk_mx16");
   if constexpr (WT == LPS_F32) {
     const f32x4 xv = *reinterpret_cast<const f32x4*>(xs);
     a = fmaf(__uint_as_float(v.x), xv.x, a);
@@ -42,28 +45,6 @@ __device__ __forceinline__ void acc_chunk(const u32x4 v, uint32_t sb, const floa
     a = fmaf(bf16_hi(v.z), x1.y, a);
     a = fmaf(bf16_lo(v.w), x1.z, a);
     a = fmaf(bf16_hi(v.w), x1.w, a);
-  } else {
-    const float sc = e8m0_to_f32(sb);
-    const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f32x4 xa = *reinterpret_cast<const f32x4*>(xs + 8 * q);
-      const f32x4 xb = *reinterpret_cast<const f32x4*>(xs + 8 * q + 4);
-      // each call converts the two codes of one byte: element 2b (low nibble)
-      // then 2b+1 (high nibble), already multiplied by the group scale
-      const f32x2 e0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[q], sc, 0);
-      const f32x2 e1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[q], sc, 1);
-      const f32x2 e2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[q], sc, 2);
-      const f32x2 e3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[q], sc, 3);
-      a = fmaf(e0.x, xa.x, a);
-      a = fmaf(e0.y, xa.y, a);
-      a = fmaf(e1.x, xa.z, a);
-      a = fmaf(e1.y, xa.w, a);
-      a = fmaf(e2.x, xb.x, a);
-      a = fmaf(e2.y, xb.y, a);
-      a = fmaf(e3.x, xb.z, a);
-      a = fmaf(e3.y, xb.w, a);
-    }
   }
 }
 
@@ -127,66 +108,6 @@ __device__ __forceinline__ void stage_x(const float* x, const float* g, float ep
     }
     for (int k = (tid + GPRE * NT) * 4; k < K; k += NT * 4)
       scale4(xs + k, r, *reinterpret_cast<const f32x4*>(g + k));
-    __syncthreads();
-  }
-}
-
-// Stage x for the MXFP4 GEMV, 32-value chunks (8 groups of 16 bytes) placed at
-// a stride of 9 groups (144 bytes).  Lane l of a wave reads the chunk of its
-// own weight chunk, so lanes are one chunk apart: at the packed 128-byte stride
-// every lane of a ds_read_b128 falls on the same four LDS banks, at 144 bytes
-// eight consecutive lanes cover 32 distinct banks.  The chunk after the last
-// (index K / 32) is zero.  Same LDS DMA copy and RMSNorm as stage_x; the x
-// values themselves, their order of use and the norm arithmetic are unchanged.
-constexpr int MX_XS = 36;   // floats per staged MXFP4 chunk (32 values + 4 pad)
-
-template <bool NORM, int NT>
-__device__ __forceinline__ void stage_x_mx(const float* x, const float* g, float eps, int K, float* xs) {
-  constexpr int NW = NT / WAVE;
-  const int tid = threadIdx.x;
-  const int lane = tid & (WAVE - 1);
-  const int wv = tid / WAVE;
-  const int ng = K / 4;              // data groups
-  const int np = (K / 32) * 9;       // physical groups
-  f32x4 gpre[GPRE];
-  if (NORM) {
-#pragma unroll
-    for (int i = 0; i < GPRE; ++i) {
-      const int G = tid + i * NT;
-      gpre[i] = G < ng ? *reinterpret_cast<const f32x4*>(g + 4 * G) : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-  }
-  for (int b = wv * WAVE; b < np; b += NW * WAVE) {
-    const int P = b + lane;
-    const int c = P / 9, q = P - 9 * c;
-    if (P < np && q < 8)
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(x + 4 * (8 * c + q)),
-                                       (__attribute__((address_space(3))) void*)(xs + 4 * b), 16, 0, 0);
-  }
-  if (tid < 32) xs[4 * np + tid] = 0.f;   // zero chunk
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (NORM) {
-    __shared__ float red[NW];
-    float ss = 0.f;
-    for (int G = tid; G < ng; G += NT) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(xs + 4 * (G + (G >> 3)));
-      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-    }
-    ss = wave_sum(ss);
-    if (lane == 0) red[wv] = ss;
-    __syncthreads();
-    float tot = 0.f;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) tot += red[i];
-    const float r = 1.0f / sqrtf(tot / float(K) + eps);
-#pragma unroll
-    for (int i = 0; i < GPRE; ++i) {
-      const int G = tid + i * NT;
-      if (G < ng) scale4(xs + 4 * (G + (G >> 3)), r, gpre[i]);
-    }
-    for (int G = tid + GPRE * NT; G < ng; G += NT)
-      scale4(xs + 4 * (G + (G >> 3)), r, *reinterpret_cast<const f32x4*>(g + 4 * G));
     __syncthreads();
   }
 }
