@@ -45,6 +45,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int PF_TOK = 8;      // tokens per routing tile
 constexpr int PF_MAXE = 64;    // experts the tile router is built for
+constexpr int PF_RCPL = 10;    // router row chunks per lane (d <= 5120, the LDS bound below)
 constexpr int PF_MAXK = 16;
 // grouped GEMM tile: BM token rows x BN weight rows, K in steps of BK; LDS rows padded
 // by 16 bytes (144-byte stride: the eight lanes of a ds_read_b128 phase hit distinct banks)
@@ -127,24 +128,44 @@ __global__ __launch_bounds__(256) void k_pf_route(PfP p) {
   if constexpr (!ROUTE) return;
   __syncthreads();
   // router logits: wave wv takes experts wv, wv + 4, ...; the lane / chunk split of
-  // a row is the decode router's (chunk c of 8 values on lane c % 64)
+  // a row is the decode router's (chunk c of 8 values on lane c % 64, ascending).
+  // All of an expert row's chunks are loaded at once, and the next expert's row is
+  // in flight while the current one is multiplied (two register sets), so a wave
+  // waits for about one L2 round trip instead of one per chunk.
   const int nck = d / 8;
-  for (int e = wv; e < p.E; e += 4) {
-    float a[PF_TOK];
-#pragma unroll
-    for (int r = 0; r < PF_TOK; ++r) a[r] = 0.f;
-    const uint16_t* row = p.wr + (long long)e * d;
-    for (int c = lane; c < nck; c += 64) {
-      const u32x4 v = ld16(row + (long long)c * 8);
-#pragma unroll
-      for (int r = 0; r < PF_TOK; ++r) acc_chunk<LPS_BF16>(v, 0, hs + r * d + c * 8, a[r]);
-    }
-#pragma unroll
-    for (int r = 0; r < PF_TOK; ++r) {
-      const float s = wave_sum(a[r]);
-      if (lane == 0) lg[r][e] = s;
-    }
+  u32x4 va[PF_RCPL], vb[PF_RCPL];
+#define PF_RLOAD(V, EX)                                                                   \
+  _Pragma("unroll") for (int i = 0; i < PF_RCPL; ++i) {                                  \
+    const int c = lane + 64 * i;                                                         \
+    V[i] = ((EX) < p.E && c < nck) ? ld16(p.wr + (long long)(EX) * d + (long long)c * 8)   \
+                                  : u32x4{0u, 0u, 0u, 0u};                               \
   }
+#define PF_RDOT(V, EX)                                                                    \
+  {                                                                                      \
+    float a[PF_TOK];                                                                     \
+    _Pragma("unroll") for (int r = 0; r < PF_TOK; ++r) a[r] = 0.f;                       \
+    _Pragma("unroll") for (int i = 0; i < PF_RCPL; ++i) {                                \
+      const int c = lane + 64 * i;                                                       \
+      if (c < nck) {                                                                     \
+        _Pragma("unroll") for (int r = 0; r < PF_TOK; ++r)                               \
+          acc_chunk<LPS_BF16>(V[i], 0, hs + r * d + c * 8, a[r]);                        \
+      }                                                                                  \
+    }                                                                                    \
+    _Pragma("unroll") for (int r = 0; r < PF_TOK; ++r) {                                 \
+      const float s_ = wave_sum(a[r]);                                                   \
+      if (lane == 0) lg[r][EX] = s_;                                                      \
+    }                                                                                    \
+  }
+  PF_RLOAD(va, wv)
+  for (int e = wv; e < p.E; e += 8) {
+    PF_RLOAD(vb, e + 4)
+    PF_RDOT(va, e)
+    if (e + 4 >= p.E) break;
+    PF_RLOAD(va, e + 8)
+    PF_RDOT(vb, e + 4)
+  }
+#undef PF_RLOAD
+#undef PF_RDOT
   __syncthreads();
   // top-k: wave wv selects for tokens 2wv, 2wv + 1; lane = expert id
   for (int q = 0; q < 2; ++q) {
