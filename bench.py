@@ -116,7 +116,7 @@ def hbm_achievable_gbs(torch, lps, gib=4, reps=10):
     return n / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(model, first_token, n_steps=2):
+def cpu_baseline(model, first_token, n_steps=6):
     """The float64 oracle as it is, on this host, on the first n_steps of the
     same greedy run (teacher-forced to the GPU's tokens is not needed: the
     oracle's own greedy steps are the same work)."""
@@ -280,7 +280,7 @@ def main():
                     help="graph: the whole step captured once and replayed, position and "
                          "next id advanced on the device; eager: every launch from the host")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-steps", type=int, default=2)
+    ap.add_argument("--cpu-steps", type=int, default=6)   # about 10 s of oracle work
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 256 MiB f32 device copy 8 times (reference for HBM counters)")
     ap.add_argument("--prefill-only", type=int, default=0, metavar="T",
