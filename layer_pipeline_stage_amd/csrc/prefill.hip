@@ -256,6 +256,9 @@ struct PaP {
 };
 
 constexpr int PA_WAVES = 8;
+#ifndef LPS_PA_ORDER
+#define LPS_PA_ORDER 1
+#endif
 constexpr int PA_THREADS = PA_WAVES * WAVE;
 #ifndef LPS_PA_KT
 #define LPS_PA_KT 4
@@ -289,8 +292,19 @@ void k_pf_attn(PaP p) {
   const int tid = threadIdx.x, lane = tid & (WAVE - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
   const int col = lane & 15, grp = lane >> 4;
+  // One linear grid over (row block, kv head): workgroup b takes kv head b % nkv,
+  // so consecutive workgroups, which the dispatcher deals to the 8 XCDs in turn,
+  // keep each head on the same XCDs (its K/V tiles stay in those L2s), and row
+  // block nrb - 1 - b / nkv, so the longest causal walks start first.
+#if LPS_PA_ORDER
+  const int nrb = (p.T + PA_WAVES * CB * R - 1) / (PA_WAVES * CB * R);
+  const int g = blockIdx.x % p.nkv;
+  const int rb = nrb - 1 - (int)blockIdx.x / p.nkv;
+#else
   const int g = blockIdx.y;
-  const int tb = blockIdx.x * PA_WAVES * CB * R;   // the workgroup's first row
+  const int rb = blockIdx.x;
+#endif
+  const int tb = rb * PA_WAVES * CB * R;   // the workgroup's first row
   const int r = col / G, hh = col - r * G;
   int tr[CB], pos[CB];
 #pragma unroll
@@ -488,7 +502,11 @@ static int gemm(const uint16_t* a, const uint16_t* b, void* out, int T, int N, i
 template <int HD, int G>
 static int attn_go(const PaP& p, hipStream_t st) {
   const int rows = PA_WAVES * pa_cb(HD) * (16 / G);   // rows per workgroup
+#if LPS_PA_ORDER
+  const dim3 grid(((p.T + rows - 1) / rows) * p.nkv);
+#else
   const dim3 grid((p.T + rows - 1) / rows, p.nkv);
+#endif
   const size_t lds = size_t(2) * pa_nt(HD) * (16 * HD + 20 * HD) * 2;
   int rc = ensure_lds((const void*)k_pf_attn<HD, G>, lds);
   if (rc) return rc;
