@@ -170,7 +170,9 @@ int lps_stage_forward(const lps_model* m, const int32_t* fence, int32_t n_stages
  * matrix cores (the normed rows, the attention output and the SwiGLU output
  * are rounded to bf16 as their inputs; f32 accumulation and residual), RoPE
  * from the layer's rope_cs table, the chunk's K and V rows appended to the
- * caches, and causal attention of row t over cache rows 0 .. p0 + t.  Bumps
+ * caches, and causal attention of row t over cache rows 0 .. p0 + t on the
+ * matrix cores (q and the unnormalised softmax weights bf16 operands, f32
+ * accumulation, the softmax sum over the f32 weights).  Bumps
  * the prefill_walks counter.  Needs bf16 weights and bf16 caches, 1, 2, 4 or 8
  * q heads per kv head, d % 256 == 0, (nq + 2 nkv) hd % 256 == 0, nq hd % 128
  * == 0, ff % 128 == 0, rope_cs, p0 + T <= ctx_max (LPS_EUNSUP / LPS_EINVAL /
