@@ -83,6 +83,31 @@ struct PfP {
 
 __device__ __forceinline__ uint16_t bf16_rne(float f) { return f32_to_bf16(f); }
 
+// Token t's top k of its E router logits lgr (one wave, lane = expert id):
+// softmax over all E, the k largest (ties to the lower id), weights renormalised.
+__device__ __forceinline__ void pf_select(const PfP& p, const float* lgr, int t, int lane) {
+  float v = lane < p.E ? lgr[lane] : -INFINITY;
+  const float m = wave_max(v);
+  const float z = wave_sum(lane < p.E ? expf(v - m) : 0.f);
+  float ssum = 0.f;
+  float pis = 0.f;   // this lane's selected pi, if selected
+  int slot = -1;
+  for (int j = 0; j < p.k; ++j) {
+    const float mx = wave_max(v);
+    const unsigned long long msk = __ballot(v == mx && lane < p.E);
+    const int sel = msk ? __ffsll((long long)msk) - 1 : j;     // no finite logit: slot id
+    const float pi = msk ? expf(mx - m) / z : __uint_as_float(0x7FC00000u);
+    if (lane == sel) {
+      v = -INFINITY;
+      pis = pi;
+      slot = j;
+    }
+    ssum += pi;
+    if (lane == 0) p.idx[(long long)t * p.k + j] = sel;
+  }
+  if (slot >= 0) p.w[(long long)t * p.k + slot] = pis / ssum;
+}
+
 // ---- 1. route ------------------------------------------------------------------
 // ROUTE = false: only the normed rows' bf16 copy (step 0); ROUTE = true: the router
 // on the same f32 rows, recomputed by the same code (step 1)
@@ -170,27 +195,104 @@ __global__ __launch_bounds__(256) void k_pf_route(PfP p) {
   // top-k: wave wv selects for tokens 2wv, 2wv + 1; lane = expert id
   for (int q = 0; q < 2; ++q) {
     const int r = wv * 2 + q, t = t0 + r;
-    if (t >= p.T) continue;
-    float v = lane < p.E ? lg[r][lane] : -INFINITY;
-    const float m = wave_max(v);
-    const float z = wave_sum(lane < p.E ? expf(v - m) : 0.f);
-    float ssum = 0.f;
-    float pis = 0.f;   // this lane's selected pi, if selected
-    int slot = -1;
-    for (int j = 0; j < p.k; ++j) {
-      const float mx = wave_max(v);
-      const unsigned long long msk = __ballot(v == mx && lane < p.E);
-      const int sel = msk ? __ffsll((long long)msk) - 1 : j;     // no finite logit: slot id
-      const float pi = msk ? expf(mx - m) / z : __uint_as_float(0x7FC00000u);
-      if (lane == sel) {
-        v = -INFINITY;
-        pis = pi;
-        slot = j;
-      }
-      ssum += pi;
-      if (lane == 0) p.idx[(long long)t * p.k + j] = sel;
+    if (t < p.T) pf_select(p, lg[r], t, lane);
+  }
+}
+
+
+// The router on the matrix cores: 16 tokens per workgroup, their normed f32 rows
+// in LDS (row pitch d + 4 floats, so the 16 rows of an operand read fall on
+// distinct banks), logits[t, e] = sum_k h[t, k] Wr[e, k] on v_mfma_f32_16x16x4_f32
+// with f32 operands (the router reads the unrounded rows; bf16 weights widen
+// exactly).  Wave wv takes experts 16 wv .. 16 wv + 15 (as 16 columns); lane
+// (n, g) supplies token n's and expert 16 wv + n's values at k = g d/4 + s for
+// step s, so each lane reads its k range contiguously (4 floats of h per LDS read,
+// 8 bf16 of Wr per global read).  The selection is the tile router's.  d % 32 == 0,
+// E <= 64, d <= 2300 (the 16 rows fit 144 KiB of LDS); wider rows take the tile router.
+constexpr int PF_MTOK = 16;
+constexpr int PF_MUNR = 4;   // 8-value B chunks per lane in flight
+constexpr int PF_MROW = 9;   // float4s per lane of a normed row (d <= 2304)
+
+__global__ __launch_bounds__(256) void k_pf_route_mx(PfP p) {
+  extern __shared__ float hs[];            // [PF_MTOK][d + 4] normed rows (f32)
+  __shared__ float lg[PF_MTOK][PF_MAXE];
+  const int t0 = blockIdx.x * PF_MTOK;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x / 64;
+  const int d = p.d, dp = d + 4;
+  for (int q = 0; q < 4; ++q) {            // each wave normalises four rows
+    const int r = wv * 4 + q, t = t0 + r;
+    float* h = hs + r * dp;
+    // the row's float4s, all in flight at once (rows past T are zero); the sum of
+    // squares and the scaling visit them in the order the tile router does
+    f32x4 v[PF_MROW];
+#pragma unroll
+    for (int i = 0; i < PF_MROW; ++i) {
+      const int c = lane * 4 + 256 * i;
+      v[i] = (t < p.T && c < d) ? *reinterpret_cast<const f32x4*>(p.x + (long long)t * d + c)
+                                : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    if (slot >= 0) p.w[(long long)t * p.k + slot] = pis / ssum;
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < PF_MROW; ++i) ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+    ss = wave_sum(ss);
+    const float rinv = 1.0f / sqrtf(ss / float(d) + p.eps);
+#pragma unroll
+    for (int i = 0; i < PF_MROW; ++i) {
+      const int c = lane * 4 + 256 * i;
+      if (c < d) {
+        f32x4 y = v[i];
+        if (t < p.T) {
+          const f32x4 gg = *reinterpret_cast<const f32x4*>(p.g + c);
+          y.x = y.x * rinv * gg.x;
+          y.y = y.y * rinv * gg.y;
+          y.z = y.z * rinv * gg.z;
+          y.w = y.w * rinv * gg.w;
+        }
+        *reinterpret_cast<f32x4*>(h + c) = y;
+      }
+    }
+  }
+  __syncthreads();
+  const int n = lane & 15, g = lane >> 4;
+  const int e = 16 * wv + n;
+  const int kq = d / 4;                     // k values per lane group
+  const float* ha = hs + n * dp + g * kq;   // A: token n
+  // one descriptor for the whole router matrix (wave-uniform); expert rows past E
+  // lie past its end and read as zeros
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(p.wr), (short)0, p.E * d * 2, 0x00020000);
+  const int boff = (e * d + g * kq) * 2;    // this lane's row and k range, in bytes
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < kq; s0 += 8 * PF_MUNR) {
+    u32x4 bq[PF_MUNR];
+#pragma unroll
+    for (int u = 0; u < PF_MUNR; ++u)
+      bq[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rs, boff + min(s0 + 8 * u, kq - 8) * 2, 0, 0));
+#pragma unroll
+    for (int u = 0; u < PF_MUNR; ++u) {
+      const int s = s0 + 8 * u;
+      if (s < kq) {
+        const f32x4 a0 = *reinterpret_cast<const f32x4*>(ha + s);
+        const f32x4 a1 = *reinterpret_cast<const f32x4*>(ha + s + 4);
+        const uint32_t wd[4] = {bq[u].x, bq[u].y, bq[u].z, bq[u].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(j < 2 ? a0[2 * j] : a1[2 * j - 4], bf16_lo(wd[j]), acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(j < 2 ? a0[2 * j + 1] : a1[2 * j - 3], bf16_hi(wd[j]), acc, 0, 0, 0);
+        }
+      }
+    }
+  }
+  // acc[i] = logits[token 4 g + i][expert 16 wv + n]
+  if (e < p.E) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lg[4 * g + i][e] = acc[i];
+  }
+  __syncthreads();
+  for (int q = 0; q < 4; ++q) {            // wave wv selects for its four tokens
+    const int r = wv * 4 + q, t = t0 + r;
+    if (t < p.T) pf_select(p, lg[r], t, lane);
   }
 }
 
@@ -527,8 +629,12 @@ extern "C" int lps_moe_prefill(const lps_moe_desc* m, float* x, int32_t T, int32
   hipStream_t st = as_stream(s_main), sr = as_stream(s_remote);
   uint16_t* xr = reinterpret_cast<uint16_t*>(sc + s.xr);
   const size_t rlds = size_t(PF_TOK) * m->d * 4;
+  // the matrix-core router where its LDS rows fit (d <= 2296), else the tile router
+  const size_t mlds = size_t(PF_MTOK) * (m->d + 4) * 4;
+  const bool route_mx = m->d % 32 == 0 && m->d <= 256 * PF_MROW && mlds <= 144 * 1024;
   int rc = ensure_lds((const void*)k_pf_route<false>, rlds);
-  if (!rc) rc = ensure_lds((const void*)k_pf_route<true>, rlds);
+  if (!rc) rc = route_mx ? ensure_lds((const void*)k_pf_route_mx, mlds)
+                         : ensure_lds((const void*)k_pf_route<true>, rlds);
   if (rc) return rc;
   const size_t glds = size_t(2) * (GM + GBN) * GKP * sizeof(uint16_t);
   rc = ensure_lds((const void*)k_pf_gemm<true>, glds);
@@ -559,7 +665,10 @@ extern "C" int lps_moe_prefill(const lps_moe_desc* m, float* x, int32_t T, int32
     ++pieces;
   }
   if (e == hipSuccess && !rc) {
-    hipLaunchKernelGGL(k_pf_route<true>, rgrid, dim3(256), rlds, st, p);
+    if (route_mx)
+      hipLaunchKernelGGL(k_pf_route_mx, dim3((T + PF_MTOK - 1) / PF_MTOK), dim3(256), mlds, st, p);
+    else
+      hipLaunchKernelGGL(k_pf_route<true>, rgrid, dim3(256), rlds, st, p);
     hipLaunchKernelGGL(k_pf_group, dim3(m->n_experts), dim3(256), 0, st, p);
     hipLaunchKernelGGL(k_pf_tiles, dim3(1), dim3(64), 0, st, p);
     e = hipGetLastError();

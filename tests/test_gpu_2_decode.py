@@ -237,3 +237,20 @@ def test_moe_prefill_small_matches_oracle_and_pieces(rt):
     dec = st.decode(X[:3])
     ref_dec = MoEStack(m).forward(X[:3])
     assert np.max(np.abs(dec - ref_dec)) <= 2e-3 * np.abs(ref_dec).max()
+
+
+def test_moe_prefill_wide_rows_tile_router(rt):
+    """Rows too wide for the matrix-core router's LDS tile (d = 2560: 16 f32 rows
+    exceed it) take the 8-token tile router; the chunk still matches the oracle
+    row by row, with a ragged last tile (T = 45)."""
+    from oracle.moe import MoEStack
+    cfg = synth.MoEConfig("moe-gpu-wide", n_layers=1, d=2560, n_experts=16, top_k=4, ff=128,
+                          remote_from=8, prefill_T=45, steps=0)
+    m = synth.make_moe(cfg)
+    st = rt.DeviceMoEStack(m)
+    X = m["x_prefill"]
+    got = st.prefill(X, n_pieces=3)
+    ref = MoEStack(m).forward(X, prefill=True, n_pieces=3)
+    tol = 2e-3 * np.abs(ref).max()
+    err = np.abs(got - ref).max(axis=1)
+    assert np.all(err <= tol), (int(np.argmax(err)), float(err.max()), tol)
