@@ -297,52 +297,101 @@ __global__ __launch_bounds__(256) void k_pf_route_mx(PfP p) {
 }
 
 // ---- 2. group: stable per-expert token lists ------------------------------------------
+// Each thread takes one token of every 256: its KW 16-byte words of indices and of
+// weights for B such steps are loaded at once (one round trip per 256 B tokens), then
+// the B steps take their ballots and prefix sums from registers.  The per-step totals
+// alternate between two LDS rows, so one barrier per step keeps them apart.
+template <int KW, int B>
 __global__ __launch_bounds__(256) void k_pf_group(PfP p) {
   const int e = blockIdx.x;
   const int lane = threadIdx.x & 63, wv = threadIdx.x / 64;
-  __shared__ int wtot[4];
+  __shared__ int wtot[2][4];
+  const int bytes = p.T * p.k * 4;
+  const __amdgpu_buffer_rsrc_t ri = __builtin_amdgcn_make_buffer_rsrc(p.idx, (short)0, bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(p.w, (short)0, bytes, 0x00020000);
   int base = 0;
-  for (int t0 = 0; t0 < p.T; t0 += 256) {
-    const int t = t0 + threadIdx.x;
-    int slot = -1;
-    if (t < p.T)
-      for (int j = 0; j < p.k; ++j)
-        if (p.idx[(long long)t * p.k + j] == e) { slot = j; break; }
-    const unsigned long long msk = __ballot(slot >= 0);
-    const int before = __popcll(msk & ((1ull << lane) - 1ull));
-    if (lane == 0) wtot[wv] = __popcll(msk);
-    __syncthreads();
-    int wbase = 0;
-    for (int i = 0; i < wv; ++i) wbase += wtot[i];
-    if (slot >= 0) {
-      const long long pos = (long long)e * p.T + base + wbase + before;
-      p.lst[pos] = t;
-      p.lslot[pos] = slot;
-      p.lw[pos] = p.w[(long long)t * p.k + slot];
+  for (int t0 = 0; t0 < p.T; t0 += 256 * B) {
+    u32x4 vi[B][KW], vw[B][KW];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const int off = (t0 + 256 * b + threadIdx.x) * p.k * 4;   // past T: zeros, masked below
+#pragma unroll
+      for (int q = 0; q < KW; ++q) {
+        vi[b][q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ri, off + 16 * q, 0, 0));
+        vw[b][q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, off + 16 * q, 0, 0));
+      }
     }
-    base += wtot[0] + wtot[1] + wtot[2] + wtot[3];
-    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const int t = t0 + 256 * b + threadIdx.x;
+      int slot = -1;
+      uint32_t wbits = 0;
+      if (t < p.T) {
+#pragma unroll
+        for (int j = 0; j < 4 * KW; ++j) {
+          const uint32_t id = vi[b][j / 4][j % 4];
+          if (j < p.k && slot < 0 && int(id) == e) {
+            slot = j;
+            wbits = vw[b][j / 4][j % 4];
+          }
+        }
+      }
+      const unsigned long long msk = __ballot(slot >= 0);
+      const int before = __popcll(msk & ((1ull << lane) - 1ull));
+      if (lane == 0) wtot[b & 1][wv] = __popcll(msk);
+      __syncthreads();
+      int wbase = 0;
+      for (int i = 0; i < wv; ++i) wbase += wtot[b & 1][i];
+      if (slot >= 0) {
+        const long long pos = (long long)e * p.T + base + wbase + before;
+        p.lst[pos] = t;
+        p.lslot[pos] = slot;
+        p.lw[pos] = __uint_as_float(wbits);
+      }
+      base += wtot[b & 1][0] + wtot[b & 1][1] + wtot[b & 1][2] + wtot[b & 1][3];
+    }
   }
   if (threadIdx.x == 0) p.cnt[e] = base;
 }
 
 // ---- 3. tiles ----------------------------------------------------------------------
-__global__ void k_pf_tiles(PfP p) {
-  if (threadIdx.x != 0) return;
-  int off = 0, n = 0, nr = 0;
-  for (int e = 0; e <= p.E; ++e) {
-    const int c = e < p.E ? p.cnt[e] : p.T;   // the shared expert takes every token
-    p.off[e] = off;
-    if (e == p.E) p.cnt[e] = c;
-    const bool remote = e >= p.remote_from && e < p.E;
-    for (int m0 = 0; m0 < c; m0 += GM) {
-      if (remote) p.tiles_r[nr++] = (e << 20) | m0;
-      else p.tiles[n++] = (e << 20) | m0;
-    }
-    off += c;
+// One wave: lane e < E takes routed expert e.  Exclusive prefix sums over the lanes
+// give each expert's first row in the grouped buffers (off) and its first entry in
+// the local or the remote tile list; the shared expert (every token) follows the
+// routed ones, its tiles last in the local list.  Lists hold (expert << 20) | m0.
+// exclusive prefix sum of v over the wave's lanes; *tot = the sum over all lanes
+__device__ __forceinline__ int wave_excl_scan(int v, int lane, int* tot) {
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < WAVE; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
   }
-  *p.n_tiles = n;
-  *p.n_tiles_r = nr;
+  *tot = __shfl(x, WAVE - 1);
+  return x - v;
+}
+__global__ __launch_bounds__(WAVE) void k_pf_tiles(PfP p) {
+  const int e = threadIdx.x;
+  const int c = e < p.E ? p.cnt[e] : 0;
+  const int nt = (c + GM - 1) / GM;
+  const bool remote = e >= p.remote_from && e < p.E;
+  int tot, nl, nr;
+  const int off = wave_excl_scan(c, e, &tot);
+  const int sl = wave_excl_scan(remote ? 0 : nt, e, &nl);
+  const int sr = wave_excl_scan(remote ? nt : 0, e, &nr);
+  if (e < p.E) {
+    p.off[e] = off;
+    int32_t* lst = remote ? p.tiles_r + sr : p.tiles + sl;
+    for (int i = 0; i < nt; ++i) lst[i] = (e << 20) | (i * GM);
+  }
+  const int ns = (p.T + GM - 1) / GM;
+  for (int i = e; i < ns; i += WAVE) p.tiles[nl + i] = (p.E << 20) | (i * GM);
+  if (e == 0) {
+    p.off[p.E] = tot;
+    p.cnt[p.E] = p.T;
+    *p.n_tiles = nl + ns;
+    *p.n_tiles_r = nr;
+  }
 }
 
 // ---- 4/5. grouped GEMM on MFMA -----------------------------------------------------------
@@ -669,7 +718,8 @@ extern "C" int lps_moe_prefill(const lps_moe_desc* m, float* x, int32_t T, int32
       hipLaunchKernelGGL(k_pf_route_mx, dim3((T + PF_MTOK - 1) / PF_MTOK), dim3(256), mlds, st, p);
     else
       hipLaunchKernelGGL(k_pf_route<true>, rgrid, dim3(256), rlds, st, p);
-    hipLaunchKernelGGL(k_pf_group, dim3(m->n_experts), dim3(256), 0, st, p);
+    if (m->top_k <= 8) hipLaunchKernelGGL((k_pf_group<2, 4>), dim3(m->n_experts), dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((k_pf_group<4, 2>), dim3(m->n_experts), dim3(256), 0, st, p);
     hipLaunchKernelGGL(k_pf_tiles, dim3(1), dim3(64), 0, st, p);
     e = hipGetLastError();
   }

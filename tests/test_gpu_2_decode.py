@@ -254,3 +254,21 @@ def test_moe_prefill_wide_rows_tile_router(rt):
     tol = 2e-3 * np.abs(ref).max()
     err = np.abs(got - ref).max(axis=1)
     assert np.all(err <= tol), (int(np.argmax(err)), float(err.max()), tol)
+
+
+def test_moe_prefill_top12_matches_oracle(rt):
+    """More selections per token than one pair of 16-byte index words holds (k = 12
+    of 16 experts): the grouping takes four words per token; rows match the oracle
+    and 8 pieces equal one."""
+    from oracle.moe import MoEStack
+    cfg = synth.MoEConfig("moe-gpu-k12", n_layers=1, d=512, n_experts=16, top_k=12, ff=128,
+                          remote_from=8, prefill_T=700, steps=0)
+    m = synth.make_moe(cfg)
+    st = rt.DeviceMoEStack(m)
+    X = m["x_prefill"]
+    got8 = st.prefill(X, n_pieces=8)
+    assert np.array_equal(got8, st.prefill(X, n_pieces=1))
+    ref = MoEStack(m).forward(X, prefill=True, n_pieces=8)
+    tol = 2e-3 * np.abs(ref).max()
+    err = np.abs(got8 - ref).max(axis=1)
+    assert np.all(err <= tol), (int(np.argmax(err)), float(err.max()), tol)
