@@ -296,6 +296,39 @@ __global__ __launch_bounds__(256) void k_pf_route_mx(PfP p) {
   }
 }
 
+// Step 0 for rows up to 256 PF_MROW wide: one wave per row, the row's float4s all in
+// flight, then the tile router's norm (same per-lane order and arithmetic, so the
+// same bits) rounded to the bf16 rows.  No LDS.
+__global__ __launch_bounds__(256) void k_pf_norm_rows(PfP p) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + threadIdx.x / 64;
+  if (t >= p.T) return;
+  const int d = p.d;
+  f32x4 v[PF_MROW];
+#pragma unroll
+  for (int i = 0; i < PF_MROW; ++i) {
+    const int c = lane * 4 + 256 * i;
+    v[i] = c < d ? *reinterpret_cast<const f32x4*>(p.x + (long long)t * d + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < PF_MROW; ++i) ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+  ss = wave_sum(ss);
+  const float rinv = 1.0f / sqrtf(ss / float(d) + p.eps);
+#pragma unroll
+  for (int i = 0; i < PF_MROW; ++i) {
+    const int c = lane * 4 + 256 * i;
+    if (c < d) {
+      const f32x4 gg = *reinterpret_cast<const f32x4*>(p.g + c);
+      const float y0 = v[i].x * rinv * gg.x, y1 = v[i].y * rinv * gg.y;
+      const float y2 = v[i].z * rinv * gg.z, y3 = v[i].w * rinv * gg.w;
+      const uint32_t lo = uint32_t(bf16_rne(y0)) | (uint32_t(bf16_rne(y1)) << 16);
+      const uint32_t hi = uint32_t(bf16_rne(y2)) | (uint32_t(bf16_rne(y3)) << 16);
+      *reinterpret_cast<uint2*>(p.xb + (long long)t * d + c) = make_uint2(lo, hi);
+    }
+  }
+}
+
 // ---- 2. group: stable per-expert token lists ------------------------------------------
 // Each thread takes one token of every 256: its KW 16-byte words of indices and of
 // weights for B such steps are loaded at once (one round trip per 256 B tokens), then
@@ -696,8 +729,11 @@ extern "C" int lps_moe_prefill(const lps_moe_desc* m, float* x, int32_t T, int32
       return fail(LPS_EHIP, "lps_moe_prefill: hipEventCreate failed");
     }
   }
-  const dim3 rgrid((T + PF_TOK - 1) / PF_TOK);
-  hipLaunchKernelGGL(k_pf_route<false>, rgrid, dim3(256), rlds, st, p);
+  if (m->d <= 256 * PF_MROW) {
+    hipLaunchKernelGGL(k_pf_norm_rows, dim3((T + 3) / 4), dim3(256), 0, st, p);
+  } else {
+    hipLaunchKernelGGL(k_pf_route<false>, dim3((T + PF_TOK - 1) / PF_TOK), dim3(256), rlds, st, p);
+  }
   hipError_t e = hipGetLastError();
   if (e == hipSuccess) e = hipEventRecord(ev[0], st);
   // activation half: the remote copy of the bf16 rows, in P row pieces, on the
@@ -717,7 +753,7 @@ extern "C" int lps_moe_prefill(const lps_moe_desc* m, float* x, int32_t T, int32
     if (route_mx)
       hipLaunchKernelGGL(k_pf_route_mx, dim3((T + PF_MTOK - 1) / PF_MTOK), dim3(256), mlds, st, p);
     else
-      hipLaunchKernelGGL(k_pf_route<true>, rgrid, dim3(256), rlds, st, p);
+      hipLaunchKernelGGL(k_pf_route<true>, dim3((T + PF_TOK - 1) / PF_TOK), dim3(256), rlds, st, p);
     if (m->top_k <= 8) hipLaunchKernelGGL((k_pf_group<2, 4>), dim3(m->n_experts), dim3(256), 0, st, p);
     else hipLaunchKernelGGL((k_pf_group<4, 2>), dim3(m->n_experts), dim3(256), 0, st, p);
     hipLaunchKernelGGL(k_pf_tiles, dim3(1), dim3(64), 0, st, p);
