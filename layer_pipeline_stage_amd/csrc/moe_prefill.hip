@@ -7,16 +7,17 @@
 // on one GPU: the expert matmuls are grouped GEMMs on the bf16 matrix cores.
 //
 // Steps (each its own launch, in stream order, so no kernel waits on another):
-//  0. norm: per 8-token tile, RMSNorm rows (f32) and their bf16 copy for the
-//     expert GEMMs.  The activation half of the piece transfer starts here: on the
+//  0. norm: RMSNorm rows (f32) rounded to their bf16 copy for the expert GEMMs,
+//     one wave per row (rows wider than 2304: per 8-token tile).  The activation half of the piece transfer starts here: on the
 //     second stream the bf16 rows go to the remote half's own copy in P row
 //     pieces while the main stream routes and groups (strata PR #3648, Approach:
 //     the activations leave before the router; both halves read the same values,
 //     so the pieces change timing, not results).
 //  1. route: the same RMSNorm recomputed per tile (bit for bit), router logits
-//     from the f32 rows (the same lane / chunk split as the decode router),
-//     softmax, top-k by logit with ties to the lower id, weights renormalised
-//     over the k.
+//     from the f32 rows on the f32 matrix cores for 16 tokens x 64 experts per
+//     workgroup (rows wider than 2300: on the vector ALUs, with the decode
+//     router's lane / chunk split), softmax, top-k by logit with ties to the
+//     lower id, weights renormalised over the k.
 //  2. group: per expert, the tokens that selected it, in token order (a stable
 //     counting sort: each expert's list is a compaction of the token sequence).
 //  3. tiles: per-expert offsets and two lists of 256-row tiles: the local
