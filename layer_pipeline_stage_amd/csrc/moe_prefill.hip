@@ -529,6 +529,28 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_pf_gemm(PfP p) {
   u32x4 ra0[NJ], rb0[NJ], ra1[NJ], rb1[NJ];
   PF_LOAD(ra0, rb0, 0)
   PF_LOAD(ra1, rb1, GBK)
+  // GEMM2: each of the tile's rows' output offset and gate weight, loaded once into
+  // LDS behind the operand buffers while the first operands are in flight (the
+  // epilogue reads them from there; the loop's barriers order them)
+  long long* eoff = reinterpret_cast<long long*>(gsm + 2 * (GM + GBN) * GKP);
+  float* ew = reinterpret_cast<float*>(eoff + GM);
+  if (!FIRST && tid < GM) {
+    const int m = m0 + tid;
+    long long o = 0;
+    float w = 0.f;
+    if (m < cnt) {
+      if (shared_e) {
+        o = (long long)m * p.d;
+        w = 1.f;
+      } else {
+        const long long li = (long long)e * p.T + m;
+        o = ((long long)p.lst[li] * p.k + p.lslot[li]) * p.d;
+        w = p.lw[li];
+      }
+    }
+    eoff[tid] = o;
+    ew[tid] = w;
+  }
   PF_STORE(ra0, rb0, As0, Bs0)
   __syncthreads();
   for (int kt = 0; kt < nk; kt += 2) {
@@ -546,31 +568,49 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_pf_gemm(PfP p) {
 #undef PF_STORE
 #undef PF_MMA
   // epilogue: acc[i][j][r] is C[128 wm + 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4][64 wn + 32 j + lane % 32]
+  if constexpr (FIRST) {
+    // the SwiGLU tile [GM][GBN / 2] (bf16) is assembled in LDS (the operand buffers are
+    // free: every wave passed the loop's last barrier after its last operand read),
+    // then leaves as whole 16-byte pieces of its rows (2-byte stores from the
+    // accumulator layout covered only half a cache line per half-wave)
+    constexpr int OP = GBN / 2 + 8;           // row pitch (bf16): rows 4 apart on other banks
+    uint16_t* ot = gsm;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = 128 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      const int m = m0 + row;
-      if (m < cnt) {
-        if (FIRST) {
-          const float gt = acc[i][0][r], up = acc[i][1][r];
-          const int col = n0 + 32 * wn + (lane & 31);
-          p.act[(long long)(p.off[e] + m) * p.ff + col] = bf16_rne(silu(gt) * up);
-        } else {
-          const long long li = (long long)e * p.T + m;
-          const int t = shared_e ? m : p.lst[li];
-          const float wgt = shared_e ? 1.f : p.lw[li];
-          float* dst = shared_e ? p.shared + (long long)m * p.d
-                                : p.z + ((long long)t * p.k + p.lslot[li]) * p.d;
+      for (int r = 0; r < 16; ++r) {
+        const int row = 128 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        ot[row * OP + 32 * wn + (lane & 31)] = bf16_rne(silu(acc[i][0][r]) * acc[i][1][r]);
+      }
+    }
+    __syncthreads();
+    const long long obase = (long long)(p.off[e] + m0) * p.ff + n0;
+    constexpr int CPR = GBN / 2 / 8;          // 16-byte pieces per row
+#pragma unroll
+    for (int q = 0; q < GM * CPR / GEMM_THREADS; ++q) {
+      const int c = tid + q * GEMM_THREADS;
+      const int row = c / CPR, c8 = (c % CPR) * 8;
+      if (m0 + row < cnt)
+        *reinterpret_cast<u32x4*>(p.act + obase + (long long)row * p.ff + c8) =
+            *reinterpret_cast<const u32x4*>(ot + row * OP + c8);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 128 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (m0 + row < cnt) {
+          const float wgt = ew[row];
+          float* dst = (shared_e ? p.shared : p.z) + eoff[row];
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
             const int col = n0 + 64 * wn + 32 * j + (lane & 31);
             dst[col] = shared_e ? acc[i][j][r] : wgt * acc[i][j][r];
           }
         }
+        __builtin_amdgcn_sched_barrier(0);   // one row at a time: keeps the epilogue's live range short
       }
-      __builtin_amdgcn_sched_barrier(0);   // one row at a time: keeps the epilogue's live range short
     }
   }
 }
@@ -720,8 +760,9 @@ extern "C" int lps_moe_prefill(const lps_moe_desc* m, float* x, int32_t T, int32
                          : ensure_lds((const void*)k_pf_route<true>, rlds);
   if (rc) return rc;
   const size_t glds = size_t(2) * (GM + GBN) * GKP * sizeof(uint16_t);
+  const size_t glds2 = glds + size_t(GM) * (sizeof(long long) + sizeof(float));   // + row table
   rc = ensure_lds((const void*)k_pf_gemm<true>, glds);
-  if (!rc) rc = ensure_lds((const void*)k_pf_gemm<false>, glds);
+  if (!rc) rc = ensure_lds((const void*)k_pf_gemm<false>, glds2);
   if (rc) return rc;
   hipEvent_t ev[3];   // rows normed (main), tile lists built (main), remote experts done
   for (int i = 0; i < 3; ++i) {
@@ -770,7 +811,7 @@ extern "C" int lps_moe_prefill(const lps_moe_desc* m, float* x, int32_t T, int32
     pr.n_tiles = p.n_tiles_r;
     hipLaunchKernelGGL(k_pf_gemm<true>, dim3(m->ff / (GBN / 2), s.max_tiles), dim3(GEMM_THREADS),
                        glds, sr, pr);
-    hipLaunchKernelGGL(k_pf_gemm<false>, dim3(m->d / GBN, s.max_tiles), dim3(GEMM_THREADS), glds,
+    hipLaunchKernelGGL(k_pf_gemm<false>, dim3(m->d / GBN, s.max_tiles), dim3(GEMM_THREADS), glds2,
                        sr, pr);
     e = hipGetLastError();
   }
@@ -779,7 +820,7 @@ extern "C" int lps_moe_prefill(const lps_moe_desc* m, float* x, int32_t T, int32
   if (e == hipSuccess && !rc) {
     hipLaunchKernelGGL(k_pf_gemm<true>, dim3(m->ff / (GBN / 2), s.max_tiles), dim3(GEMM_THREADS),
                        glds, st, p);
-    hipLaunchKernelGGL(k_pf_gemm<false>, dim3(m->d / GBN, s.max_tiles), dim3(GEMM_THREADS), glds,
+    hipLaunchKernelGGL(k_pf_gemm<false>, dim3(m->d / GBN, s.max_tiles), dim3(GEMM_THREADS), glds2,
                        st, p);
     e = hipGetLastError();
   }
