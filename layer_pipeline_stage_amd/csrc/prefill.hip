@@ -158,27 +158,62 @@ __global__ __launch_bounds__(DG_THREADS) void k_dense_gemm(DgP p) {
 #undef DG_STORE
 #undef DG_MMA
   // acc[i][j][r] is C[128 wm + 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4][col(j)]
+  if constexpr (EPI == GE_SWIGLU) {
+    // the bf16 tile [DM][DN / 2] is assembled in LDS (free: every wave passed the
+    // loop's last barrier after its last operand read) and leaves as whole 16-byte
+    // pieces of its rows (2-byte stores from the accumulator layout covered half a
+    // cache line per half-wave)
+    constexpr int OP = DN / 2 + 8;            // row pitch (bf16): rows 4 apart on other banks
+    uint16_t* ot = dsm;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = m0 + 128 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      if (m < p.T) {
-        if constexpr (EPI == GE_SWIGLU) {
-          const int col = n0 + 32 * wn + (lane & 31);
-          const float v = silu(acc[i][0][r]) * acc[i][1][r];
-          static_cast<uint16_t*>(p.out)[(long long)m * p.N + col] = f32_to_bf16(v);
-        } else {
+      for (int r = 0; r < 16; ++r) {
+        const int row = 128 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        ot[row * OP + 32 * wn + (lane & 31)] = f32_to_bf16(silu(acc[i][0][r]) * acc[i][1][r]);
+      }
+    }
+    __syncthreads();
+    constexpr int CPR = DN / 2 / 8;           // 16-byte pieces per row
+#pragma unroll
+    for (int q = 0; q < DM * CPR / DG_THREADS; ++q) {
+      const int c = tid + q * DG_THREADS;
+      const int row = c / CPR, c8 = (c % CPR) * 8;
+      if (m0 + row < p.T)
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.out) + (long long)(m0 + row) * p.N + n0 + c8) =
+            *reinterpret_cast<const u32x4*>(ot + row * OP + c8);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // GE_ADD: the 16 rows' residual values of this block all in flight at once,
+      // then the sums (one round trip per block instead of one per row)
+      float old[16][2];
+      if constexpr (EPI == GE_ADD) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + 128 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int col = n0 + 64 * wn + 32 * j + (lane & 31);
+            old[r][j] = m < p.T ? static_cast<const float*>(p.out)[(long long)m * p.N + col] : 0.f;
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + 128 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (m < p.T) {
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
             const int col = n0 + 64 * wn + 32 * j + (lane & 31);
             float* o = static_cast<float*>(p.out) + (long long)m * p.N + col;
-            if constexpr (EPI == GE_ADD) *o += acc[i][j][r];
+            if constexpr (EPI == GE_ADD) *o = old[r][j] + acc[i][j][r];
             else *o = acc[i][j][r];
           }
         }
+        __builtin_amdgcn_sched_barrier(0);   // one row at a time: short live ranges
       }
-      __builtin_amdgcn_sched_barrier(0);   // one row at a time: short live ranges
     }
   }
 }
