@@ -32,10 +32,33 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 // ---- 1/6. per-row RMSNorm -> bf16 -------------------------------------------------------
 __global__ __launch_bounds__(256) void k_pf_rows_norm(const float* x, const float* g, float eps,
                                                       int d, uint16_t* xb) {
+  constexpr int NPT = 16;                    // rows up to 4096 wide stay in registers
   const long long t = blockIdx.x;
   const float* xr = x + t * d;
   __shared__ float red[4];
   float ss = 0.f;
+  if (d <= NPT * 256) {
+    // every element of the thread's share in flight at once; the same elements and
+    // summation order as the loop below (zeros past d add nothing)
+    float v[NPT];
+#pragma unroll
+    for (int k = 0; k < NPT; ++k) {
+      const int i = threadIdx.x + 256 * k;
+      v[k] = i < d ? xr[i] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < NPT; ++k) ss += v[k] * v[k];
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x / 64] = ss;
+    __syncthreads();
+    const float r = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / float(d) + eps);
+#pragma unroll
+    for (int k = 0; k < NPT; ++k) {
+      const int i = threadIdx.x + 256 * k;
+      if (i < d) xb[t * d + i] = f32_to_bf16(v[k] * r * g[i]);
+    }
+    return;
+  }
   for (int i = threadIdx.x; i < d; i += 256) ss += xr[i] * xr[i];
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x / 64] = ss;
