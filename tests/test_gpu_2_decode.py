@@ -272,3 +272,22 @@ def test_moe_prefill_top12_matches_oracle(rt):
     tol = 2e-3 * np.abs(ref).max()
     err = np.abs(got8 - ref).max(axis=1)
     assert np.all(err <= tol), (int(np.argmax(err)), float(err.max()), tol)
+
+
+@pytest.mark.parametrize("remote_from", [0, 16])
+def test_moe_prefill_all_remote_or_all_local(rt, remote_from):
+    """Every routed expert on the remote half (the local tile list holds only the
+    shared expert) or none of them (the remote list is empty and its launches find
+    no tile): rows still match the oracle and 8 pieces equal one."""
+    from oracle.moe import MoEStack
+    cfg = synth.MoEConfig("moe-gpu-edge", n_layers=1, d=512, n_experts=16, top_k=4, ff=128,
+                          remote_from=remote_from, prefill_T=260, steps=0)
+    m = synth.make_moe(cfg)
+    st = rt.DeviceMoEStack(m)
+    X = m["x_prefill"]
+    got8 = st.prefill(X, n_pieces=8)
+    assert np.array_equal(got8, st.prefill(X, n_pieces=1))
+    ref = MoEStack(m).forward(X, prefill=True, n_pieces=8)
+    tol = 2e-3 * np.abs(ref).max()
+    err = np.abs(got8 - ref).max(axis=1)
+    assert np.all(err <= tol), (int(np.argmax(err)), float(err.max()), tol)
