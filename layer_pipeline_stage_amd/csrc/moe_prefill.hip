@@ -606,7 +606,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_pf_gemm(PfP p) {
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
             const int col = n0 + 64 * wn + 32 * j + (lane & 31);
-            dst[col] = shared_e ? acc[i][j][r] : wgt * acc[i][j][r];
+            __builtin_nontemporal_store(shared_e ? acc[i][j][r] : wgt * acc[i][j][r], dst + col);
           }
         }
         __builtin_amdgcn_sched_barrier(0);   // one row at a time: keeps the epilogue's live range short
@@ -633,7 +633,8 @@ __global__ __launch_bounds__(256) void k_pf_halves(PfP p) {
     f32x4 lo = {0, 0, 0, 0}, re = {0, 0, 0, 0};
     for (int n = 0; n < p.k; ++n) {
       const int j = order[n];
-      const f32x4 v = *reinterpret_cast<const f32x4*>(p.z + ((long long)t * p.k + j) * p.d + c);
+      // read once: nontemporal, so the stream does not evict what the combine reads next
+      const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p.z + ((long long)t * p.k + j) * p.d + c));
       if (ids[j] < p.remote_from) {
         lo.x += v.x; lo.y += v.y; lo.z += v.z; lo.w += v.w;
       } else {
