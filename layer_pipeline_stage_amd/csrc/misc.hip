@@ -70,6 +70,25 @@ __global__ void k_combine(float* out, const float* x, const float* shared, const
   }
 }
 
+// The same, four elements per thread access (all five buffers 16-byte aligned, n a
+// multiple of 4); shared, local and bo are last uses and stream past the caches.
+__global__ void k_combine4(float* out, const float* x, const float* shared, const float* local,
+                           const float* bo, long long n4) {
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n4;
+       i += (long long)gridDim.x * blockDim.x) {
+    const f32x4 sv = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(shared) + i);
+    const f32x4 lv = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(local) + i);
+    const f32x4 bv = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(bo) + i);
+    const f32x4 xv = reinterpret_cast<const f32x4*>(x)[i];
+    f32x4 v;
+    v.x = xv.x + ((sv.x + lv.x) + bv.x);
+    v.y = xv.y + ((sv.y + lv.y) + bv.y);
+    v.z = xv.z + ((sv.z + lv.z) + bv.z);
+    v.w = xv.w + ((sv.w + lv.w) + bv.w);
+    reinterpret_cast<f32x4*>(out)[i] = v;
+  }
+}
+
 static dim3 grid_for(long long n, int threads = 256) {
   long long b = (n + threads - 1) / threads;
   if (b < 1) b = 1;
@@ -254,7 +273,11 @@ extern "C" int lps_moe_combine(float* out, const float* x, const float* shared,
   LPS_HIP(hipEventRecord(done, sr));
   LPS_HIP(hipStreamWaitEvent(sm, done, 0));
   const long long n = (long long)T * d;
-  hipLaunchKernelGGL(k_combine, grid_for(n), dim3(256), 0, sm, out, x, shared, local, bo, n);
+  const auto a16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+  if (n % 4 == 0 && a16(out) && a16(x) && a16(shared) && a16(local) && a16(bo))
+    hipLaunchKernelGGL(k_combine4, grid_for(n / 4), dim3(256), 0, sm, out, x, shared, local, bo, n / 4);
+  else
+    hipLaunchKernelGGL(k_combine, grid_for(n), dim3(256), 0, sm, out, x, shared, local, bo, n);
   LPS_HIP(hipGetLastError());
   // events are released once they have fired (the runtime keeps them alive)
   LPS_HIP(hipEventDestroy(start));

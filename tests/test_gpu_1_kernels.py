@@ -426,9 +426,10 @@ def test_pending_readback(L):
     torch.cuda.synchronize()
 
 
-def test_f16_pieces_and_combine(L):
+@pytest.mark.parametrize("d", [2048, 2047])   # 16-byte accesses; odd element count: scalar
+def test_f16_pieces_and_combine(L, d):
     rng = np.random.default_rng(14)
-    T, d = 37, 2048
+    T = 37
     rem = (rng.standard_normal((T, d)) * np.exp(rng.uniform(-6, 6, (T, 1)))).astype(np.float32)
     r16 = torch.zeros((T, d), dtype=torch.int16, device=DEV)
     remd = dev(rem)
