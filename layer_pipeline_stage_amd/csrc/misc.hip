@@ -70,6 +70,20 @@ __global__ void k_combine(float* out, const float* x, const float* shared, const
   }
 }
 
+// f16 -> f32 over [lo, hi), eight halves per thread access (lo, hi multiples of 8, both
+// buffers 16-byte aligned); the halves are a last use and stream past the caches.
+__global__ void k_f16_to_f32_8(const uint16_t* src, float* dst, long long lo, long long hi) {
+  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+  const long long n8 = (hi - lo) / 8;
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n8;
+       i += (long long)gridDim.x * blockDim.x) {
+    const long long e = lo + 8 * i;
+    const h8 v = __builtin_bit_cast(h8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + e)));
+    reinterpret_cast<f32x4*>(dst + e)[0] = f32x4{float(v[0]), float(v[1]), float(v[2]), float(v[3])};
+    reinterpret_cast<f32x4*>(dst + e)[1] = f32x4{float(v[4]), float(v[5]), float(v[6]), float(v[7])};
+  }
+}
+
 // The same, four elements per thread access (all five buffers 16-byte aligned, n a
 // multiple of 4); shared, local and bo are last uses and stream past the caches.
 __global__ void k_combine4(float* out, const float* x, const float* shared, const float* local,
@@ -265,7 +279,10 @@ extern "C" int lps_moe_combine(float* out, const float* x, const float* shared,
     const long long lo = (long long)pc * T / n_pieces, hi = (long long)(pc + 1) * T / n_pieces;
     if (hi > lo) {
       const long long a = lo * d, b = hi * d;
-      hipLaunchKernelGGL(k_f16_to_f32, grid_for(b - a), dim3(256), 0, sr, remote16, bo, a, b);
+      if (a % 8 == 0 && b % 8 == 0 && ((reinterpret_cast<uintptr_t>(remote16) | reinterpret_cast<uintptr_t>(bo)) & 15) == 0)
+        hipLaunchKernelGGL(k_f16_to_f32_8, grid_for((b - a) / 8), dim3(256), 0, sr, remote16, bo, a, b);
+      else
+        hipLaunchKernelGGL(k_f16_to_f32, grid_for(b - a), dim3(256), 0, sr, remote16, bo, a, b);
       LPS_HIP(hipGetLastError());
       ++pieces;
     }
