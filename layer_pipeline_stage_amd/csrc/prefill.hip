@@ -243,42 +243,104 @@ __global__ __launch_bounds__(DG_THREADS) void k_dense_gemm(DgP p) {
 
 // ---- 3. RoPE + K/V append for the chunk ------------------------------------------------------
 // qkv [T, (nq + 2 nkv) hd] f32 from the GEMM: q heads are rotated in place; k heads
-// rotated and v heads copied into cache row p0 + t (bf16, 16-row tiles).  One
-// thread per (row, head, pair i): elements i and i + hd/2.
-__global__ void k_pf_rope_append(float* qkv, int T, int nq, int nkv, int hd, int p0,
-                                 const float* rope_cs, int ctx_max, uint16_t* kc, uint16_t* vc) {
-  const int half = hd >> 1;
+// rotated and v heads copied into cache rows p0 .. p0 + T - 1 (bf16, 16-row tiles).
+
+// q heads: rotated in place, one thread per (row, head, 4 dims of the first half) and
+// their partners i + hd/2 (16-byte accesses)
+__global__ void k_pf_rope_q(float* qkv, int T, int nq, int nkv, int hd, int p0, const float* rope_cs) {
+  const int half = hd >> 1, h4 = half >> 2;
   const int heads = nq + 2 * nkv;
-  const long long n = (long long)T * heads * half;
+  const long long n = (long long)T * nq * h4;
   for (long long u = blockIdx.x * (long long)blockDim.x + threadIdx.x; u < n;
        u += (long long)gridDim.x * blockDim.x) {
-    const int t = int(u / (heads * half));
-    const int rem = int(u - (long long)t * heads * half);
-    const int hh = rem / half, i = rem - hh * half;
+    const int t = int(u / (nq * h4));
+    const int rem = int(u - (long long)t * nq * h4);
+    const int hh = rem / h4, i0 = 4 * (rem - hh * h4);
     const int pos = p0 + t;
     float* row = qkv + (long long)t * heads * hd + (long long)hh * hd;
-    const float a0 = row[i], a1 = row[i + half];
-    float o0 = a0, o1 = a1;
-    if (hh < nq + nkv) {
-      const f32x2 cs = *reinterpret_cast<const f32x2*>(rope_cs + 2 * ((long long)pos * half + i));
-      o0 = a0 * cs.x - a1 * cs.y;
-      o1 = a0 * cs.y + a1 * cs.x;
+    const f32x4 a0 = *reinterpret_cast<const f32x4*>(row + i0);
+    const f32x4 a1 = *reinterpret_cast<const f32x4*>(row + half + i0);
+    const float* cs = rope_cs + 2 * ((long long)pos * half + i0);
+    const f32x4 c01 = *reinterpret_cast<const f32x4*>(cs), c23 = *reinterpret_cast<const f32x4*>(cs + 4);
+    const float c[4] = {c01.x, c01.z, c23.x, c23.z}, sn[4] = {c01.y, c01.w, c23.y, c23.w};
+    const float x0[4] = {a0.x, a0.y, a0.z, a0.w}, x1[4] = {a1.x, a1.y, a1.z, a1.w};
+    float o0[4], o1[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      o0[e] = x0[e] * c[e] - x1[e] * sn[e];
+      o1[e] = x0[e] * sn[e] + x1[e] * c[e];
     }
-    if (hh < nq) {
-      row[i] = o0;
-      row[i + half] = o1;
-    } else {
-      const bool is_k = hh < nq + nkv;
-      const int g = is_k ? hh - nq : hh - nq - nkv;
+    *reinterpret_cast<f32x4*>(row + i0) = f32x4{o0[0], o0[1], o0[2], o0[3]};
+    *reinterpret_cast<f32x4*>(row + half + i0) = f32x4{o1[0], o1[1], o1[2], o1[3]};
+  }
+}
+
+// k and v heads into the cache tiles with whole 16-byte pieces.  Units [0, nk): one
+// thread per (row, kv head, group of 8 dims of the first half): the 8 dims and their
+// rotation partners i + hd/2, each group's 8 bf16 of one row contiguous in the K tile.
+// Units [nk, nk + nv): one thread per (kv head, dim, 16-row tile the chunk touches):
+// that dim's 16 rows of the V^T tile (32 bytes) when the chunk covers the whole tile,
+// else only its own rows.
+__global__ void k_pf_kv_append(const float* qkv, int T, int nq, int nkv, int hd, int p0,
+                               const float* rope_cs, int ctx_max, uint16_t* kc, uint16_t* vc) {
+  const int half = hd >> 1, hg = half >> 3;
+  const int heads = nq + 2 * nkv;
+  const int tb = p0 >> 4, ntl = ((p0 + T - 1) >> 4) - tb + 1;
+  const long long nk = (long long)T * nkv * hg, nv = (long long)nkv * hd * ntl;
+  for (long long u = blockIdx.x * (long long)blockDim.x + threadIdx.x; u < nk + nv;
+       u += (long long)gridDim.x * blockDim.x) {
+    if (u < nk) {
+      const int t = int(u / (nkv * hg));
+      const int rem = int(u - (long long)t * nkv * hg);
+      const int g = rem / hg, j = rem - g * hg, i0 = 8 * j;
+      const int pos = p0 + t;
+      const float* row = qkv + (long long)t * heads * hd + (long long)(nq + g) * hd;
+      const float* cs = rope_cs + 2 * ((long long)pos * half + i0);
+      uint32_t w0[4], w1[4];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const f32x4 a0 = *reinterpret_cast<const f32x4*>(row + i0 + 4 * q);
+        const f32x4 a1 = *reinterpret_cast<const f32x4*>(row + half + i0 + 4 * q);
+        const f32x4 c01 = *reinterpret_cast<const f32x4*>(cs + 8 * q);       // cos, sin of i0 + 4q, + 1
+        const f32x4 c23 = *reinterpret_cast<const f32x4*>(cs + 8 * q + 4);   // of i0 + 4q + 2, + 3
+        const float c[4] = {c01.x, c01.z, c23.x, c23.z}, sn[4] = {c01.y, c01.w, c23.y, c23.w};
+        const float x0[4] = {a0.x, a0.y, a0.z, a0.w}, x1[4] = {a1.x, a1.y, a1.z, a1.w};
+        uint16_t o0[4], o1[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o0[e] = f32_to_bf16(x0[e] * c[e] - x1[e] * sn[e]);
+          o1[e] = f32_to_bf16(x0[e] * sn[e] + x1[e] * c[e]);
+        }
+        w0[2 * q] = o0[0] | (uint32_t)o0[1] << 16;
+        w0[2 * q + 1] = o0[2] | (uint32_t)o0[3] << 16;
+        w1[2 * q] = o1[0] | (uint32_t)o1[1] << 16;
+        w1[2 * q + 1] = o1[2] | (uint32_t)o1[3] << 16;
+      }
       const long long tile = (long long)g * (ctx_max >> 4) + (pos >> 4);
-      if (is_k) {
-        const long long off = (tile * (hd >> 3) + (i >> 3)) * 128 + (pos & 15) * 8 + (i & 7);
-        kc[off] = f32_to_bf16(o0);
-        kc[off + (long long)(half >> 3) * 128] = f32_to_bf16(o1);
+      const long long off = (tile * (hd >> 3) + j) * 128 + (pos & 15) * 8;
+      *reinterpret_cast<u32x4*>(kc + off) = u32x4{w0[0], w0[1], w0[2], w0[3]};
+      *reinterpret_cast<u32x4*>(kc + off + (long long)hg * 128) = u32x4{w1[0], w1[1], w1[2], w1[3]};
+    } else {
+      const long long v = u - nk;
+      const int i = int(v % hd);
+      const long long r2 = v / hd;
+      const int k = int(r2 % ntl), g = int(r2 / ntl);
+      const int tp0 = (tb + k) << 4;                       // the tile's first row
+      const int lo = max(tp0, p0), hi = min(tp0 + 16, p0 + T);
+      const float* col = qkv + (long long)(nq + nkv + g) * hd + i;   // v dim i, row stride heads hd
+      const long long base = (((long long)g * (ctx_max >> 4) + (tb + k)) * hd + i) * 16;
+      if (lo == tp0 && hi == tp0 + 16) {
+        uint32_t wv[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const long long t0 = (long long)(tp0 + 2 * r - p0) * heads * hd;
+          wv[r] = f32_to_bf16(col[t0]) | (uint32_t)f32_to_bf16(col[t0 + (long long)heads * hd]) << 16;
+        }
+        *reinterpret_cast<u32x4*>(vc + base) = u32x4{wv[0], wv[1], wv[2], wv[3]};
+        *reinterpret_cast<u32x4*>(vc + base + 8) = u32x4{wv[4], wv[5], wv[6], wv[7]};
       } else {
-        const long long off = (tile * hd + i) * 16 + (pos & 15);
-        vc[off] = f32_to_bf16(o0);
-        vc[off + (long long)half * 16] = f32_to_bf16(o1);
+        for (int pos = lo; pos < hi; ++pos)
+          vc[base + (pos & 15)] = f32_to_bf16(col[(long long)(pos - p0) * heads * hd]);
       }
     }
   }
@@ -631,9 +693,17 @@ int prefill_layer(const lps_layer_desc* L, float* x, int T, int p0, void* scratc
   hipLaunchKernelGGL(k_pf_rows_norm, dim3(T), dim3(256), 0, st, x, L->g_attn, L->eps, d, xb);
   int rc = gemm<GE_STORE>(xb, w(L->w_qkv), qkv, T, nqkv, d, st);
   if (rc) return rc;
-  hipLaunchKernelGGL(k_pf_rope_append, rows_grid((long long)T * (nqkv / 2)), dim3(256), 0, st, qkv,
-                     T, L->nq, L->nkv, L->hd, p0, L->rope_cs, L->ctx_max,
-                     static_cast<uint16_t*>(L->k_cache), static_cast<uint16_t*>(L->v_cache));
+  {
+    const int hd = L->hd, nkv = L->nkv;
+    const long long nq_units = (long long)T * L->nq * (hd / 8);
+    const long long nkv_units = (long long)T * nkv * (hd / 16) +
+                                (long long)nkv * hd * (((p0 + T - 1) >> 4) - (p0 >> 4) + 1);
+    hipLaunchKernelGGL(k_pf_rope_q, rows_grid(nq_units), dim3(256), 0, st, qkv, T, L->nq, nkv, hd, p0,
+                       L->rope_cs);
+    hipLaunchKernelGGL(k_pf_kv_append, rows_grid(nkv_units), dim3(256), 0, st, qkv, T, L->nq, nkv, hd,
+                       p0, L->rope_cs, L->ctx_max, static_cast<uint16_t*>(L->k_cache),
+                       static_cast<uint16_t*>(L->v_cache));
+  }
   PaP pa{qkv, static_cast<const uint16_t*>(L->k_cache), static_cast<const uint16_t*>(L->v_cache),
          xb, T, L->nq, L->nkv, p0, L->ctx_max, nqkv, 1.0f / sqrtf(float(L->hd))};
   const int G = L->nq / L->nkv;
