@@ -31,10 +31,16 @@ Pins (each checked by a CPU test against something other than this code):
             shapes; the prefill matrix form (exact operands) equals the decode
             steps, chunk and stage splits change nothing, and a planted
             off-by-one mask is caught; bf16 operand rounding against torch;
+            every prefill rounding point (normed rows, attention output,
+            normed rows, SwiGLU output) and the gate/up order by closed forms
+            on hand-built layers, each with a planted removal that fails;
             staged == unstaged bit for bit; padded == unpadded bit
             for bit; a one-token closed form of a whole layer
   moe       top-k against exhaustive subset search; FP16 pieces == one piece
-            and aliased == separate combine, bit for bit
+            and aliased == separate combine, bit for bit; a whole layer (router,
+            experts' gate/up order, the prefill bf16 rounding points, the f16
+            remote sum) by closed forms on a hand-built layer, with planted
+            removals of each rounding point
 Absolute logits of a whole model have no printed worked example on the pages:
 they are pinned only through the rows above (parity unpinned beyond that).
 """

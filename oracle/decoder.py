@@ -23,7 +23,8 @@ stages in turn): a chunk of T prompt rows goes through each layer as whole-chunk
 matrix products; its K and V rows are stored first and each row attends
 causally.  Where the pages leave the precision open, the operands the matrix
 cores take are rounded to bf16 (the normed rows, the attention output, the
-SwiGLU output), everything else is as in decode.  With those roundings off the
+SwiGLU output), everything else is as in decode: attention takes q and its
+softmax weights exact, as the decode step does.  With those roundings off the
 matrix form reproduces the decode steps exactly (pinned in the tests).
 """
 from __future__ import annotations
@@ -80,29 +81,26 @@ def bf16_act(x64):
     return bf16_to_f64(f32_to_bf16_bits(to_f32(x64)))
 
 
-def causal_attend(Q, K, V, p0, act=None):
+def causal_attend(Q, K, V, p0):
     """Causal attention over a chunk in matrix form.  Q [T, nq, hd] (rows at
     positions p0 .. p0+T-1); K, V [nkv, p0+T, hd].  Row t sees cache rows
     0 .. p0+t: S = Q K^T / sqrt(hd) with the rows past p0+t masked out, a row
     softmax, O = P V.  Returns O [T, nq, hd].
 
-    `act` rounds the two operands the matrix cores take besides the cached K and
-    V: q, and the softmax weights W = e^(S - row max) before they multiply V;
-    the row sum that normalises O adds the unrounded weights.  act=None keeps
-    both exact (O is then the plain softmax(S) V)."""
-    act = act or (lambda a: a)
+    q and the softmax weights are not rounding points: the chunk's attention is
+    the plain definition, as in the decode step (the cached K and V rows carry
+    the cache dtype's rounding)."""
     T, nq, hd = Q.shape
     nkv, n, _ = K.shape
     G = nq // nkv
     visible = np.arange(n)[None, :] <= (p0 + np.arange(T))[:, None]     # [T, n]
-    Qa = act(Q)
     O = np.empty((T, nq, hd), dtype=np.float64)
     for h in range(nq):
         g = h // G
-        S = (Qa[:, h, :] @ K[g].T) / math.sqrt(hd)
+        S = (Q[:, h, :] @ K[g].T) / math.sqrt(hd)
         S = np.where(visible, S, -np.inf)
         W = np.exp(S - S.max(axis=1, keepdims=True))
-        O[:, h, :] = (act(W) @ V[g]) / W.sum(axis=1, keepdims=True)
+        O[:, h, :] = (W @ V[g]) / W.sum(axis=1, keepdims=True)
     return O
 
 
@@ -220,8 +218,8 @@ class Decoder:
         rounds the operands the matrix cores take in prefill: the normed rows,
         the attention output and the SwiGLU output (bf16); the residual stays
         f32 between sublayers, every sum is f64.  act=None keeps them exact,
-        which must reproduce the decode steps row by row.  In attention `act`
-        also rounds q and the softmax weights (causal_attend)."""
+        which must reproduce the decode steps row by row.  Attention itself
+        takes q and the softmax weights exact (causal_attend)."""
         act = act or (lambda a: a)
         c = self.cfg
         L = self.m["layers"][l]
@@ -239,7 +237,7 @@ class Decoder:
         self.V[l][:, p0:p0 + T] = round_cache(Vn.transpose(1, 0, 2), c.kvdtype)
         Kc = widen_cache(self.K[l][:, :p0 + T], c.kvdtype)
         Vc = widen_cache(self.V[l][:, :p0 + T], c.kvdtype)
-        O = causal_attend(Q, Kc, Vc, p0, act).reshape(T, nq * hd)
+        O = causal_attend(Q, Kc, Vc, p0).reshape(T, nq * hd)
         X = to_f32(X + act(O) @ self.W(l, "w_o").T).astype(np.float64)
         H2 = act(rmsnorm(X, L["g_ffn"], c.eps))
         GU = H2 @ self.W(l, "w_gu").T

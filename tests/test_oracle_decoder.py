@@ -348,13 +348,13 @@ def test_prefill_pin_catches_an_off_by_one_mask(monkeypatch):
     _, _, dlg = Decoder(m).greedy(m["prompt"], 0)
     real = od.causal_attend
 
-    def leaky(Q, K, V, p0, act=None):
+    def leaky(Q, K, V, p0):
         T = Q.shape[0]
         n = K.shape[1]
         out = np.empty_like(Q)
         for t in range(T):
             vis = min(n, p0 + t + 2)
-            out[t] = real(Q[t:t + 1], K[:, :vis], V[:, :vis], vis - 1, act)[0]
+            out[t] = real(Q[t:t + 1], K[:, :vis], V[:, :vis], vis - 1)[0]
         return out
 
     monkeypatch.setattr(od, "causal_attend", leaky)
@@ -376,32 +376,23 @@ def test_bf16_activation_rounding():
     assert bf16_act(np.array([1.0 + 3 * 2 ** -8]))[0] == 1.0 + 2 ** -6
 
 
-def test_causal_attend_operand_rounding_closed_forms():
-    """causal_attend's rounded operands against hand-solvable cases, with torch's
-    bf16 conversion as the rounding reference: (a) K = 0 makes every weight
-    e^0 = 1 (exact in bf16), so each row's output is the plain mean of the V rows
-    it sees, rounded or not; (b) one query against two keys, where the second
-    key's weight e^(-q0) is not a bf16 value and q0 itself is not either: the
-    rounded form takes bf16(q0) into the score and bf16(weight) into the PV
-    product, and divides by the unrounded weight sum."""
-    import torch
-    from oracle.decoder import bf16_act, causal_attend
-
-    def bf(x):
-        return float(torch.tensor(x, dtype=torch.float32).to(torch.bfloat16).to(torch.float64))
-
+def test_causal_attend_closed_forms():
+    """causal_attend against hand-solvable cases: (a) K = 0 makes every weight
+    e^0 = 1, so each row's output is the plain mean of the V rows it sees (the
+    GQA map h // G picks the kv head); (b) one query against two keys, the
+    second one's score -q0: the output is (v0 + e^(-q0) v1) / (1 + e^(-q0))."""
+    from oracle.decoder import causal_attend
     rng = np.random.default_rng(11)
     T, nq, nkv, hd, p0 = 5, 4, 2, 8, 3
     Q = rng.standard_normal((T, nq, hd))
     K = np.zeros((nkv, p0 + T, hd))
     V = rng.standard_normal((nkv, p0 + T, hd))
-    for act in (None, bf16_act):
-        O = causal_attend(Q, K, V, p0, act)
-        for t in range(T):
-            for h in range(nq):
-                want = V[h // 2, :p0 + t + 1].mean(axis=0)
-                assert np.max(np.abs(O[t, h] - want)) <= 1e-14
-    q0 = 1.0 + 3 * 2.0 ** -9                       # bf16: 1 + 2^-7
+    O = causal_attend(Q, K, V, p0)
+    for t in range(T):
+        for h in range(nq):
+            want = V[h // 2, :p0 + t + 1].mean(axis=0)
+            assert np.max(np.abs(O[t, h] - want)) <= 1e-14
+    q0 = 1.0 + 3 * 2.0 ** -9
     Q = np.zeros((1, 1, 4))
     Q[0, 0, 0] = q0
     K = np.zeros((1, 2, 4))
@@ -409,11 +400,8 @@ def test_causal_attend_operand_rounding_closed_forms():
     V = np.zeros((1, 2, 4))
     V[0, 0, 0] = 1.0
     V[0, 1, 1] = 1.0
-    O = causal_attend(Q, K, V, 1, bf16_act)[0, 0]
-    w1 = math.exp(-bf(q0))
-    assert abs(O[0] - 1.0 / (1.0 + w1)) <= 1e-15
-    assert abs(O[1] - bf(w1) / (1.0 + w1)) <= 1e-15
-    assert bf(w1) != w1 and bf(q0) != q0          # both roundings were live
     O = causal_attend(Q, K, V, 1)[0, 0]
     w1 = math.exp(-q0)
+    assert abs(O[0] - 1.0 / (1.0 + w1)) <= 1e-15
     assert abs(O[1] - w1 / (1.0 + w1)) <= 1e-15
+    assert O[2] == O[3] == 0.0
