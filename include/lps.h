@@ -171,13 +171,17 @@ int lps_stage_forward(const lps_model* m, const int32_t* fence, int32_t n_stages
  * are rounded to bf16 as their inputs; f32 accumulation and residual), RoPE
  * from the layer's rope_cs table, the chunk's K and V rows appended to the
  * caches, and causal attention of row t over cache rows 0 .. p0 + t on the
- * matrix cores (q and the unnormalised softmax weights bf16 operands, f32
- * accumulation, the softmax sum over the f32 weights).  Bumps
- * the prefill_walks counter.  Needs bf16 weights and bf16 caches, 1, 2, 4 or 8
- * q heads per kv head, d % 256 == 0, (nq + 2 nkv) hd % 256 == 0, nq hd % 128
- * == 0, ff % 128 == 0, rope_cs, p0 + T <= ctx_max (LPS_EUNSUP / LPS_EINVAL /
- * LPS_ERANGE otherwise, before anything is enqueued).  scratch (dev) of at
- * least lps_prefill_scratch_bytes(m, T) bytes, contents irrelevant. */
+ * matrix cores (q and the unnormalised softmax weights enter as bf16 operands,
+ * a precision deviation from the plain softmax(S) V of the decode path; f32
+ * accumulation, the softmax sum over the f32 weights).  Cache rows at or past
+ * p0 + T are never used, whatever they hold.  Bumps the prefill_walks counter.
+ * Needs bf16 weights and bf16 caches, 1, 2, 4 or 8 q heads per kv head,
+ * d % 256 == 0, (nq + 2 nkv) hd % 256 == 0, nq hd % 128 == 0, ff % 128 == 0,
+ * rope_cs, p0 + T <= ctx_max, and every operand of the chunk (T rows of bf16
+ * activations, f32 QKV and residual rows; the weights) below 2 GiB, the reach of
+ * the kernels' 32-bit offsets (LPS_EUNSUP / LPS_EINVAL / LPS_ERANGE otherwise,
+ * before anything is enqueued).  scratch (dev) of at least
+ * lps_prefill_scratch_bytes(m, T) bytes, contents irrelevant. */
 size_t lps_prefill_scratch_bytes(const lps_model* m, int32_t T);
 int lps_stage_prefill(const lps_model* m, const int32_t* fence, int32_t n_stages, int32_t stage,
                       float* x, int32_t T, int32_t p0, void* scratch, size_t scratch_bytes,
@@ -260,8 +264,10 @@ int lps_embed(const void* table, int32_t wdtype, int32_t vocab, int32_t d, const
 
 /* ---- A15, A16: final RMSNorm + LM head + argmax --------------------------
  * logits (dev [vocab] f32) = W_lm (RMSNorm(x) * g_out); *tok_out (dev int32) =
- * the lowest index of the maximum logit.  memra pp docs: output_norm and the
- * LM head live with the last stage. */
+ * the lowest index of the maximum logit.  Logits holding a NaN have no maximum:
+ * *tok_out = vocab, an id outside the table, which lps_embed turns into a NaN
+ * row, so a poisoned step poisons the next one instead of feeding a valid id.
+ * memra pp docs: output_norm and the LM head live with the last stage. */
 typedef struct lps_head_desc {
   int32_t d, vocab, wdtype;  /* wdtype LPS_F32 | LPS_BF16 */
   float eps;
@@ -309,13 +315,15 @@ int lps_attention_decode(int32_t nq, int32_t nkv, int32_t hd, int32_t kvdtype,
  * double-buffered slots with ev_tx / ev_rx per slot; fn pp2_overlap: the slots
  * alternate per step.  Slot k = step & 1.
  *  send(step t): the producer stream waits ev_rx[k] (slot k drained by the
- *    recv of step t-2) and copies x -> slot[k].
+ *    recv of step t-2) and copies x -> slot[k].  When that recv ran on its own
+ *    producer's stream (no event was recorded then) and this send comes from
+ *    another stream, ev_rx[k] is recorded first on the receiving stream.
  *  recv(step t): ev_tx[k] is recorded on the producer stream (after the send's
  *    copy and whatever the host enqueued there since), the consumer stream waits
  *    it, copies slot[k] -> x and records ev_rx[k].
  * When producer and consumer are the same stream (memra pp docs, fn
  * pp2_streams_off: the same-stream seam), stream order already gives both
- * orderings and no event is recorded or waited.
+ * orderings and no event is recorded or waited for that step.
  * Steps must be sent in order 0, 1, 2, ... and received in the same order;
  * a recv of a step that was not sent, or out of order, is LPS_ESTATE.
  * The two slots (dev [n_elems] f32 each) are the caller's. */
@@ -350,17 +358,21 @@ int lps_copy_f32(const float* src, float* dst, int64_t n, void* stream);
  * (host; pinned for a truly asynchronous copy), and records a drained event.
  * The caller must not overwrite the device buffers until the pending is
  * drained: lps_pending_order(p, stream) makes `stream` wait the drained event.
+ * *out is an opaque token, not an address: exactly one lps_pending_wait or
+ * lps_pending_drop consumes it; any later use of the token (a second wait, a
+ * drop after a wait, an order after either), or a token the library never
+ * issued, is LPS_ESTATE (memra pp docs, fn pp_multi_stream_same_device: refuse
+ * loudly rather than return silently-wrong logits).
  */
 typedef struct lps_pending lps_pending;
 int lps_logits_defer(const float* logits, const int32_t* tok, int32_t vocab, void* last_stage,
                      void* readback, float* host_logits, int32_t* host_tok, lps_pending** out);
 /* Makes `stream` wait until the pending's copies are done (no host block). */
 int lps_pending_order(lps_pending* p, void* stream);
-/* Blocks the host until host_logits / host_tok hold the step; then frees p.
- * A second wait on a freed handle is undefined (the handle is gone). */
+/* Blocks the host until host_logits / host_tok hold the step; consumes p. */
 int lps_pending_wait(lps_pending* p);
-/* Frees p without waiting: its copies still complete on the readback stream;
- * the events are released once they have fired. */
+/* Consumes p without waiting: its copies still complete on the readback
+ * stream; the events are released once they have fired. */
 int lps_pending_drop(lps_pending* p);
 
 /* ---- A10-A12: MoE FFN layer ------------------------------------------------
@@ -420,7 +432,10 @@ int lps_f32_to_f16(const float* src, uint16_t* dst, int64_t n, void* stream);
  * the shared one on s_main, which waits for the remote experts before the
  * per-token halves.  Both halves read the same values, so every n_pieces (1..64)
  * gives the same bits.  Bumps act_pieces (and pieces, in the combine).  Built for
- * n_experts <= 64, top_k <= 16, d a multiple of 128, ff a multiple of 64.
+ * n_experts <= 64, top_k <= 16, d a multiple of 128, ff a multiple of 64, and
+ * every operand below 2 GiB, the reach of the kernels' 32-bit offsets (e.g. T
+ * <= 32767 at d 2048, top 8: the per-slot expert outputs [T, top_k, d] f32);
+ * LPS_EUNSUP otherwise, before anything is enqueued.
  * scratch (dev) of lps_moe_prefill_scratch_bytes(m, T) bytes; its contents on
  * entry do not matter.  Work is enqueued on s_main and s_remote. */
 size_t lps_moe_prefill_scratch_bytes(const lps_moe_desc* m, int32_t T);

@@ -105,17 +105,6 @@ __device__ __forceinline__ const uint8_t* unit_base(const GemvP& p, int u) {
   }
 }
 
-// offset of unit u's activation row in the staged vector, and the staged length
-template <int EPI>
-__device__ __forceinline__ int unit_xoff(const GemvP& p, int u) {
-  if constexpr (EPI == EPI_MOEDN) return 0;   // the workgroup staged its own slot's vector
-  else return 0;
-}
-template <int EPI>
-__host__ __device__ __forceinline__ int staged_len(const GemvP& p) {
-  return p.K;
-}
-
 __device__ __forceinline__ void store_kv(void* base, int kvdtype, long long off, float v) {
   if (kvdtype == LPS_F32)
     reinterpret_cast<float*>(base)[off] = v;
@@ -219,9 +208,9 @@ __device__ __forceinline__ void finish(const GemvP& p, int u, int r0, int r1, fl
   a0 = wave_sum(a0);
   a1 = wave_sum(a1);
   if (lane == 0) epilogue<EPI>(p, u, r0, r1, a0, a1, y0, y1);
-  if constexpr (EPI == EPI_LOGITS) {
-    if (a0 > best) { best = a0; bidx = r0; }
-    if (r1 >= 0 && a1 > best) { best = a1; bidx = r1; }
+  if constexpr (EPI == EPI_LOGITS) {   // a NaN logit sticks: the step has no argmax
+    if (a0 > best || a0 != a0) { best = a0; bidx = r0; }
+    if (r1 >= 0 && (a1 > best || a1 != a1)) { best = a1; bidx = r1; }
   }
 }
 
@@ -297,7 +286,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const uint8_t* base, 
     if (nb >= nck) { nu = u + stride; nb = 0; }                    \
     const bool more = nu < p.units;                                \
     BUF_LOAD(NV0, NV1, NS0, NS1, NY0, NY1, nu, nb, more)           \
-    BUF_FMA(CV0, CV1, CS0, CS1, b0, unit_xoff<EPI>(p, u))          \
+    BUF_FMA(CV0, CV1, CS0, CS1, b0, 0)            \
     if (nu != u) {                                                 \
       int r0, r1;                                                  \
       unit_rows<EPI>(p, u, r0, r1);                                \
@@ -329,7 +318,7 @@ __global__ __launch_bounds__(NT) void k_gemv_buf(GemvP p) {
   float ya0 = 0.f, ya1 = 0.f, yb0 = 0.f, yb1 = 0.f;   // residual rows (EPI_ADD)
   BUF_LOAD(va0, va1, sa0, sa1, ya0, ya1, u, 0, u < p.units)
   // a chunk past the row end (zero weights) reads the zero chunk after the staged vector
-  const int zoff = WT == LPS_MXFP4 ? nck * XS : staged_len<EPI>(p);
+  const int zoff = WT == LPS_MXFP4 ? nck * XS : p.K;
   if constexpr (WT == LPS_MXFP4) {
     stage_x_mx16<NORM, NT, mx16_maxr(U, NT)>(p.x, p.g, p.eps, p.K, xh);
   } else {
@@ -340,7 +329,7 @@ __global__ __launch_bounds__(NT) void k_gemv_buf(GemvP p) {
     const float* xsrc = p.x;
     if constexpr (EPI == EPI_MOEDN)
       xsrc += (long long)((blockIdx.x * NW) / (p.rps >> 1)) * p.K;
-    stage_x<NORM, NT>(xsrc, p.g, p.eps, staged_len<EPI>(p), xs);
+    stage_x<NORM, NT>(xsrc, p.g, p.eps, p.K, xs);
   }
   if (u < p.units) {
     float a0 = 0.f, a1 = 0.f;
@@ -352,7 +341,7 @@ __global__ __launch_bounds__(NT) void k_gemv_buf(GemvP p) {
     } else {
       // one batch in flight per wave, for launches where a wave meets one batch
       for (;;) {
-        BUF_FMA(va0, va1, sa0, sa1, b0, unit_xoff<EPI>(p, u))
+        BUF_FMA(va0, va1, sa0, sa1, b0, 0)
         int nu = u, nb = b0 + WAVE * U;
         if (nb >= nck) { nu = u + stride; nb = 0; }
         if (nu != u) {
@@ -382,20 +371,28 @@ __global__ __launch_bounds__(NT) void k_gemv_buf(GemvP p) {
 // A16 argmax over the LM head's per-wave partials (value, lowest index with
 // that value), one workgroup: max with ties to the lower index is an exact
 // selection, so any order gives the same answer.  Its own launch after the head
-// GEMV: no fence or counter is needed.
-__global__ __launch_bounds__(1024) void k_argmax(const float* pval, const int* pidx, int n, int* out) {
+// GEMV: no fence or counter is needed.  A NaN partial (some logit of the step is
+// NaN) beats every number, and then, as when no partial holds a maximum at all,
+// the id written is `vocab`, outside the table: the next embedding gather turns
+// it into a NaN row, so a poisoned step stays poisoned instead of feeding id 0.
+__device__ __forceinline__ bool argmax_better(float v, int j, float b, int ix) {
+  if (b != b) return false;            // a NaN holds its place
+  return v != v || v > b || (v == b && j < ix);
+}
+__global__ __launch_bounds__(1024) void k_argmax(const float* pval, const int* pidx, int n,
+                                                 int vocab, int* out) {
   float b = -INFINITY;
   int ix = 0x7fffffff;
   for (int i = threadIdx.x; i < n; i += 1024) {
     const float v = pval[i];
     const int j = pidx[i];
-    if (v > b || (v == b && j < ix)) { b = v; ix = j; }
+    if (argmax_better(v, j, b, ix)) { b = v; ix = j; }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const float ob = __shfl_xor(b, o, WAVE);
     const int oi = __shfl_xor(ix, o, WAVE);
-    if (ob > b || (ob == b && oi < ix)) { b = ob; ix = oi; }
+    if (argmax_better(ob, oi, b, ix)) { b = ob; ix = oi; }
   }
   __shared__ float bv[16];
   __shared__ int bi[16];
@@ -404,9 +401,8 @@ __global__ __launch_bounds__(1024) void k_argmax(const float* pval, const int* p
   __syncthreads();
   if (threadIdx.x == 0) {
     for (int i = 1; i < 16; ++i)
-      if (bv[i] > b || (bv[i] == b && bi[i] < ix)) { b = bv[i]; ix = bi[i]; }
-    // no maximum (all NaN): report 0 rather than an index outside the vocabulary
-    *out = ix == 0x7fffffff ? 0 : ix;
+      if (argmax_better(bv[i], bi[i], b, ix)) { b = bv[i]; ix = bi[i]; }
+    *out = (b != b || ix == 0x7fffffff) ? vocab : ix;
   }
 }
 
@@ -418,7 +414,7 @@ static int launch_t(const GemvP& p, hipStream_t st, Stamp sp, int* waves) {
   constexpr int CH = Fmt<WT>::CH;
   const int per_lane = (p.K / CH + WAVE - 1) / WAVE;
   const size_t lds = WT == LPS_MXFP4 ? size_t(p.K / CH + 1) * MX16_XS * sizeof(_Float16)
-                                     : (size_t(staged_len<EPI>(p)) + CH) * sizeof(float);
+                                     : (size_t(p.K) + CH) * sizeof(float);
 #define LPS_GOB(UU, NTV, MAXBV)                                                                  \
   do {                                                                                           \
     constexpr int NW_ = (NTV) / WAVE;                                                            \
@@ -600,7 +596,8 @@ int launch_head(const lps_head_desc* h, const float* x, float* logits, int32_t* 
   int waves = 0;
   int rc = launch_wt<EPI_LOGITS, true>(h->wdtype, p, st, Stamp{sp.start, nullptr}, &waves);
   if (rc) return rc;
-  LPS_LAUNCH(k_argmax, dim3(1), dim3(1024), 0, st, nullptr, sp.stop, p.pval, p.pidx, waves, tok);
+  LPS_LAUNCH(k_argmax, dim3(1), dim3(1024), 0, st, nullptr, sp.stop, p.pval, p.pidx, waves,
+             h->vocab, tok);
   LPS_HIP(hipGetLastError());
   return LPS_OK;
 }

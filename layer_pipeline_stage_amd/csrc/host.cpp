@@ -205,10 +205,39 @@ struct lps_graph {
   hipGraphExec_t exec;
 };
 
-struct lps_pending {
-  hipEvent_t drained;
-  hipStream_t readback;
+// A pending readback is a token, not an address: (generation << 32) | (slot + 1)
+// into a table of slots.  A wait or a drop frees the slot and bumps its
+// generation, so a second wait or drop on the same token (or one on a token
+// that was never issued) is refused instead of touching freed state.
+namespace lps {
+struct PendingSlot {
+  hipEvent_t drained = nullptr;
+  uint32_t gen = 1;
+  bool live = false;
 };
+static std::mutex g_pend_mu;
+static std::vector<PendingSlot> g_pend;
+static std::vector<uint32_t> g_pend_free;
+
+static lps_pending* pending_token(uint32_t slot, uint32_t gen) {
+  return reinterpret_cast<lps_pending*>((uintptr_t(gen) << 32) | uintptr_t(slot + 1));
+}
+// Takes the live slot a token names (marking it finished) and returns its event;
+// nullptr when the token is not a live pending.
+static hipEvent_t pending_take(lps_pending* p) {
+  const uintptr_t v = reinterpret_cast<uintptr_t>(p);
+  const uint32_t slot = uint32_t(v & 0xffffffffu) - 1u, gen = uint32_t(v >> 32);
+  std::lock_guard<std::mutex> lk(g_pend_mu);
+  if (slot >= g_pend.size() || !g_pend[slot].live || g_pend[slot].gen != gen) return nullptr;
+  PendingSlot& e = g_pend[slot];
+  hipEvent_t ev = e.drained;
+  e.drained = nullptr;
+  e.live = false;
+  e.gen = e.gen == 0xffffffffu ? 1u : e.gen + 1u;
+  g_pend_free.push_back(slot);
+  return ev;
+}
+}  // namespace lps
 
 using namespace lps;
 
@@ -831,9 +860,23 @@ int lps_boundary_send(lps_boundary* b, const float* x, int64_t step, void* produ
   if (rc) return rc;
   // a wait on the own stream is implied by stream order (the same-stream seam);
   // a receive recorded in another context (eager vs a capture) is not waited:
-  // ordering eager work against a graph launch is the caller's
-  if (b->rx_recorded[k] && b->rx_stream[k] != st && b->rx_cap[k] == cid)
+  // ordering eager work against a graph launch is the caller's.  A receive made
+  // on its producer's stream recorded no event; when the slot's next producer is
+  // another stream, ev_rx is recorded now on the receiving stream, after all its
+  // work so far, which covers that receive's copy.
+  if (b->rx_stream[k] && b->rx_stream[k] != st && b->rx_cap[k] == cid) {
+    if (!b->rx_recorded[k]) {
+      unsigned long long rcid = 0;
+      rc = capture_of(b->rx_stream[k], &rcid);
+      if (rc) return rc;
+      LPS_REQUIRE(rcid == cid, LPS_ESTATE,
+                  "lps_boundary_send: slot %d's last receive stream is in another capture context",
+                  k);
+      LPS_HIP(hipEventRecord(b->ev_rx[k], b->rx_stream[k]));
+      b->rx_recorded[k] = true;
+    }
     LPS_HIP(hipStreamWaitEvent(st, b->ev_rx[k], 0));
+  }
   rc = launch_copy_f32(x, b->slot[k], b->n, st);
   if (rc) return rc;
   // ev_tx is recorded by the receive, on this stream, when the consumer turns out to
@@ -910,42 +953,59 @@ int lps_logits_defer(const float* logits, const int32_t* tok, int32_t vocab, voi
   LPS_REQUIRE(!logits || (host_logits && vocab > 0), LPS_EINVAL,
               "lps_logits_defer: logits need host_logits and vocab > 0");
   LPS_REQUIRE(!tok || host_tok, LPS_EINVAL, "lps_logits_defer: tok needs host_tok");
+  *out = nullptr;
   hipStream_t ls = as_stream(last_stage), rb = as_stream(readback);
-  hipEvent_t done;
-  LPS_HIP(hipEventCreateWithFlags(&done, hipEventDisableTiming));
-  lps_pending* p = new (std::nothrow) lps_pending;
-  if (!p) {
-    (void)hipEventDestroy(done);
-    return fail(LPS_ENOMEM, "lps_logits_defer: out of host memory");
-  }
-  p->readback = rb;
-  hipError_t e = hipEventCreateWithFlags(&p->drained, hipEventDisableTiming);
+  hipEvent_t done = nullptr, drained = nullptr;
+  hipError_t e = hipEventCreateWithFlags(&done, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&drained, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventRecord(done, ls);
   if (e == hipSuccess) e = hipStreamWaitEvent(rb, done, 0);
   if (e == hipSuccess && logits)
     e = hipMemcpyAsync(host_logits, logits, size_t(vocab) * 4, hipMemcpyDeviceToHost, rb);
   if (e == hipSuccess && tok) e = hipMemcpyAsync(host_tok, tok, 4, hipMemcpyDeviceToHost, rb);
-  if (e == hipSuccess) e = hipEventRecord(p->drained, rb);
-  (void)hipEventDestroy(done);
+  if (e == hipSuccess) e = hipEventRecord(drained, rb);
+  if (done) (void)hipEventDestroy(done);
   if (e != hipSuccess) {
-    delete p;
+    if (drained) (void)hipEventDestroy(drained);
     return fail(LPS_EHIP, "lps_logits_defer: %s", hipGetErrorString(e));
   }
-  *out = p;
+  std::lock_guard<std::mutex> lk(g_pend_mu);
+  uint32_t slot;
+  if (!g_pend_free.empty()) {
+    slot = g_pend_free.back();
+    g_pend_free.pop_back();
+  } else {
+    if (g_pend.size() >= 0xfffffffeu) {
+      (void)hipEventDestroy(drained);
+      return fail(LPS_ENOMEM, "lps_logits_defer: too many pending readbacks");
+    }
+    slot = uint32_t(g_pend.size());
+    g_pend.emplace_back();
+  }
+  g_pend[slot].drained = drained;
+  g_pend[slot].live = true;
+  *out = pending_token(slot, g_pend[slot].gen);
   return LPS_OK;
 }
 
 int lps_pending_order(lps_pending* p, void* stream) {
   LPS_REQUIRE(p, LPS_EINVAL, "lps_pending_order: null pending");
-  LPS_HIP(hipStreamWaitEvent(as_stream(stream), p->drained, 0));
+  const uintptr_t v = reinterpret_cast<uintptr_t>(p);
+  const uint32_t slot = uint32_t(v & 0xffffffffu) - 1u, gen = uint32_t(v >> 32);
+  std::lock_guard<std::mutex> lk(g_pend_mu);
+  LPS_REQUIRE(slot < g_pend.size() && g_pend[slot].live && g_pend[slot].gen == gen, LPS_ESTATE,
+              "lps_pending_order: the pending was already waited or dropped (or never issued)");
+  LPS_HIP(hipStreamWaitEvent(as_stream(stream), g_pend[slot].drained, 0));
   return LPS_OK;
 }
 
 int lps_pending_wait(lps_pending* p) {
   LPS_REQUIRE(p, LPS_EINVAL, "lps_pending_wait: null pending");
-  hipError_t e = hipEventSynchronize(p->drained);
-  (void)hipEventDestroy(p->drained);
-  delete p;
+  hipEvent_t ev = pending_take(p);
+  LPS_REQUIRE(ev, LPS_ESTATE,
+              "lps_pending_wait: the pending was already waited or dropped (or never issued)");
+  hipError_t e = hipEventSynchronize(ev);
+  (void)hipEventDestroy(ev);
   count_drain();
   if (e != hipSuccess) return fail(LPS_EHIP, "lps_pending_wait: %s", hipGetErrorString(e));
   return LPS_OK;
@@ -953,9 +1013,11 @@ int lps_pending_wait(lps_pending* p) {
 
 int lps_pending_drop(lps_pending* p) {
   LPS_REQUIRE(p, LPS_EINVAL, "lps_pending_drop: null pending");
+  hipEvent_t ev = pending_take(p);
+  LPS_REQUIRE(ev, LPS_ESTATE,
+              "lps_pending_drop: the pending was already waited or dropped (or never issued)");
   // the copies stay enqueued; destroying the event defers its release until it fires
-  (void)hipEventDestroy(p->drained);
-  delete p;
+  (void)hipEventDestroy(ev);
   count_drain();
   return LPS_OK;
 }

@@ -711,6 +711,18 @@ extern "C" int lps_moe_prefill(const lps_moe_desc* m, float* x, int32_t T, int32
               "lps_moe_prefill: remote_from %d", m->remote_from);
   LPS_REQUIRE(m->g_ffn && m->w_r && m->w_gu_e && m->w_d_e && m->w_gu_s && m->w_d_s && x && scratch,
               LPS_EINVAL, "lps_moe_prefill: null pointer");
+  {
+    // every kernel addresses its operands with 32-bit byte offsets (buffer
+    // resources, int row offsets): each operand stays below 2 GiB, else the chunk
+    // is refused before anything is enqueued (e.g. T >= 32768 at d 2048, top 8:
+    // the per-slot expert outputs [T, k, d] f32)
+    const long long Tk = (long long)T * m->top_k;
+    const long long big = std::max({(long long)T * m->d * 4, Tk * m->d * 4, (Tk + T) * m->ff * 2,
+                                    4LL * m->ff * m->d, (long long)m->n_experts * T * 4});
+    LPS_REQUIRE(big < (1LL << 31), LPS_EUNSUP,
+                "lps_moe_prefill: a %lld-byte operand at T %d (the kernels address below 2 GiB "
+                "with 32-bit offsets; split the chunk)", big, T);
+  }
   const PfScratch s = pf_scratch(m, T);
   LPS_REQUIRE(scratch_bytes >= s.total, LPS_EINVAL, "lps_moe_prefill: scratch %zu < %zu",
               scratch_bytes, s.total);

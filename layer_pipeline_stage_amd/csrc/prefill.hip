@@ -363,9 +363,14 @@ __global__ void k_pf_kv_append(const float* qkv, int T, int nq, int nkv, int hd,
 // k index 8 grp + e stands for key 4 grp + e of tile u0 (e < 4) or key
 // 4 grp + e - 4 of tile u1, which is where lane (col, grp) already holds those
 // keys' weights (B operand) and where it reads V^T (A operand), so the weights
-// never leave the lane.  q, K, V and the weights are bf16 operands with f32
-// accumulation; the softmax sum l adds the f32 weights.  Keys past a column's
-// position are masked.  The output o / l is rounded to bf16 for the O projection.
+// never leave the lane.  K and V are the bf16 cache rows; q and the unnormalised
+// weights enter as single bf16 operands (relative error up to 2^-9 each, a
+// deviation from the plain softmax(S) V that the decode kernel does not take: it
+// splits both into bf16 hi + lo); accumulation is f32 and the softmax sum l adds
+// the f32 weights.  Keys past a column's position are masked, and V rows past the
+// workgroup's last position (stale cache rows, possibly never written) are
+// zeroed as they are staged, so whatever they hold cannot reach the output
+// through a zero weight.  The output o / l is rounded to bf16 for the O projection.
 struct PaP {
   const float* q;          // [T, nq, hd] rotated (the q part of qkv: row stride qs)
   const uint16_t* kc;      // tiled bf16 caches of the layer
@@ -476,6 +481,22 @@ void k_pf_attn(PaP p) {
     stk[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0)); \
     stv[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0)); \
   }
+  // V elements of keys past `last` in the staged step S: the chunk's 8 elements are
+  // 8 consecutive keys of one V^T row, two per 32-bit word (the lower key in the low half)
+  auto zero_stale_v = [&](int S) {
+#pragma unroll
+    for (int c = 0; c < LPT; ++c) {
+      const int e = (tid + c * PA_THREADS) * 8;
+      const int key0 = 16 * (S * NT + e / TILE) + (e & 15);
+      uint32_t wv[4] = {stv[c].x, stv[c].y, stv[c].z, stv[c].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (key0 + 2 * j > last) wv[j] = 0u;
+        else if (key0 + 2 * j + 1 > last) wv[j] &= 0xFFFFu;
+      }
+      stv[c] = u32x4{wv[0], wv[1], wv[2], wv[3]};
+    }
+  };
 #define PA_PUT(BUFI)                                                                          \
   _Pragma("unroll") for (int c = 0; c < LPT; ++c) {                                           \
     *reinterpret_cast<u32x4*>(kv_lds + (BUFI) * BUF + (tid + c * PA_THREADS) * 8) = stk[c];    \
@@ -574,11 +595,15 @@ void k_pf_attn(PaP p) {
         for (int b = 0; b < CB; ++b)
           o[b][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pp[b][v], o[b][dt], 0, 0, 0);
       }
-    if (sj + 1 < nsteps) { PA_PUT(bi ^ 1) }
+    if (sj + 1 < nsteps) {
+      if (sj + 2 == nsteps) zero_stale_v(sj + 1);
+      PA_PUT(bi ^ 1)
+    }
     __syncthreads();
   };
 
   PA_FETCH(0)
+  if (nsteps == 1) zero_stale_v(0);
   PA_PUT(0)
   __syncthreads();
   int sj = 0;
@@ -675,10 +700,15 @@ int check_prefill_layer(const lps_layer_desc* L, int T, int p0, const char* who)
   LPS_REQUIRE(L->rope_cs, LPS_EINVAL, "%s: prefill needs the layer's rope_cs table", who);
   LPS_REQUIRE(T >= 1 && p0 >= 0 && (long long)p0 + T <= L->ctx_max, LPS_ERANGE,
               "%s: rows %d .. %d outside the cache [0, %d)", who, p0, p0 + T - 1, L->ctx_max);
-  const long long big = (long long)T * std::max({L->d, L->nq * L->hd, L->ff}) * 2;
-  LPS_REQUIRE(big < (1LL << 31) && (long long)2 * L->ff * L->d * 2 < (1LL << 31) &&
-                  (long long)nqkv * L->d * 2 < (1LL << 31),
-              LPS_EUNSUP, "%s: an operand of 2 GiB or more (32-bit offsets)", who);
+  // the GEMMs address their operands through buffer resources with 32-bit byte
+  // offsets: every operand (bf16 rows, f32 QKV and residual rows, weights) stays
+  // below 2 GiB, else the chunk is refused before anything is enqueued
+  const long long big = std::max({(long long)T * std::max({L->d, L->nq * L->hd, L->ff}) * 2,
+                                  (long long)T * nqkv * 4, (long long)T * L->d * 4,
+                                  (long long)2 * L->ff * L->d * 2, (long long)nqkv * L->d * 2});
+  LPS_REQUIRE(big < (1LL << 31), LPS_EUNSUP,
+              "%s: a %lld-byte operand at T %d (the kernels address below 2 GiB with 32-bit "
+              "offsets; split the chunk)", who, big, T);
   return LPS_OK;
 }
 

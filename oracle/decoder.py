@@ -15,7 +15,9 @@ Readings where the pages are silent: no biases, no QK norm, no attention
 output gate; RMSNorm y = x / sqrt(mean(x^2) + eps) * g; RoPE rotates the pairs
 (i, i + hd/2) of every q and k head by p * base^(-2i/hd) at the 0-based
 position p; attention is causal over rows 0..p after row p is written, scaled
-by 1/sqrt(hd); silu(z) = z / (1 + e^-z); the argmax takes the first maximum.
+by 1/sqrt(hd); silu(z) = z / (1 + e^-z); the argmax takes the first maximum,
+and a step whose logits hold a NaN has none: its id is vocab, which the next
+embedding turns into a NaN row (a poisoned step stays poisoned).
 
 Chunked prefill (memra ``pp`` module docs, functions on the prime split; ninfer
 pipeline stages, What is not covered yet: a prefill chunk runs through the
@@ -268,11 +270,19 @@ class Decoder:
 
     # ---- stages, embedding, head --------------------------------------------
     def embed(self, tok):
+        """The embedding row of an id; an id outside the table has no row: a NaN
+        row stands for it, so a poisoned step stays poisoned."""
+        if not 0 <= int(tok) < self.cfg.vocab:
+            return np.full(self.cfg.d, np.nan, dtype=np.float32)
         return to_f32(widen_weight(self.m["embed"][int(tok)], self.cfg.wdtype))
 
     def head(self, x32):
+        """Logits and the first maximum; logits holding a NaN have no maximum and
+        give the id vocab (outside the table)."""
         hf = rmsnorm(np.asarray(x32, np.float32).astype(np.float64), self.m["g_out"], self.cfg.eps)
         logits = self.mv(-1, "w_lm", hf)
+        if np.isnan(logits).any():
+            return logits, self.cfg.vocab
         return logits, int(np.argmax(logits))
 
     def walk(self, x32, p, fence=None):

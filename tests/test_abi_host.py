@@ -279,3 +279,52 @@ def test_cache_tile_layouts_match_the_documented_offsets():
     assert np.array_equal(layout.v_to_tiles(xt).numpy(), vt)
     assert np.array_equal(layout.k_from_tiles(layout.k_to_tiles(xt)).numpy(), x)
     assert np.array_equal(layout.v_from_tiles(layout.v_to_tiles(xt)).numpy(), x)
+
+
+def test_chunks_past_32_bit_offsets_are_refused_before_enqueue(L):
+    """The prefill kernels address every operand with 32-bit byte offsets: a chunk
+    whose largest operand reaches 2 GiB is refused (LPS_EUNSUP) with the size in
+    the text, before any HIP call.  Dense: T = 140,000 rows of f32 QKV at the 8B
+    slice's width; MoE: T = 40,000 at d 2048, top 8 (the [T, 8, d] f32 expert
+    outputs)."""
+    import ctypes
+    d = L.LayerDesc()
+    d.d, d.nq, d.nkv, d.hd, d.ff = 4096, 32, 8, 128, 14336
+    d.wdtype, d.kvdtype, d.ctx_max = L.LPS_BF16, L.LPS_BF16, 1 << 18
+    d.eps, d.rope_base = 1e-6, 1e4
+    for k in ("g_attn", "g_ffn", "w_qkv", "w_o", "w_gu", "w_d", "k_cache", "v_cache", "rope_cs"):
+        setattr(d, k, 256)
+    h = ctypes.c_void_p()
+    L.lps_model_create(ctypes.byref(d), 1, ctypes.byref(h))
+    try:
+        fence = L.i32_array([0, 1])
+        with pytest.raises(L.LpsError) as e:
+            L.lps_stage_prefill(h, fence, 1, 0, 256, 140000, 0, 256, 1 << 62, None)
+        assert e.value.code == L.LPS_EUNSUP and "2 GiB" in str(e.value)
+    finally:
+        L.lps_model_destroy(h)
+    m = L.MoEDesc()
+    m.d, m.n_experts, m.top_k, m.ff, m.remote_from, m.eps = 2048, 64, 8, 1024, 32, 1e-6
+    for k in ("g_ffn", "w_r", "w_gu_e", "w_d_e", "w_gu_s", "w_d_s"):
+        setattr(m, k, 256)
+    with pytest.raises(L.LpsError) as e:
+        L.lps_moe_prefill(ctypes.byref(m), 256, 40000, 8, 256, 1 << 62, None, None)
+    assert e.value.code == L.LPS_EUNSUP and "2 GiB" in str(e.value)
+    # the workload's own chunk (16,384 rows) stays below the limit: it fails later,
+    # on the scratch size, not on the offsets
+    with pytest.raises(L.LpsError) as e:
+        L.lps_moe_prefill(ctypes.byref(m), 256, 16384, 8, 256, 16, None, None)
+    assert e.value.code == L.LPS_EINVAL and "scratch" in str(e.value)
+
+
+def test_pending_tokens_refuse_a_second_use(L):
+    """A pending readback handle is a token that one wait or drop consumes; a
+    token the library never issued (or one already consumed) is refused with
+    LPS_ESTATE, before any HIP call."""
+    for fn in (L.lps_pending_wait, L.lps_pending_drop):
+        with pytest.raises(L.LpsError) as e:
+            fn((7 << 32) | 3)
+        assert e.value.code == L.LPS_ESTATE and "already waited or dropped" in str(e.value)
+    with pytest.raises(L.LpsError) as e:
+        L.lps_pending_order((1 << 32) | 1, None)
+    assert e.value.code == L.LPS_ESTATE

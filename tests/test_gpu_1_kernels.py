@@ -354,6 +354,25 @@ def test_head_argmax(L):
     xd = dev(x)
     L.lps_head_forward(C.byref(hdsc), ptr(xd), ptr(lg), ptr(tk), ptr(sc), sb, stream())
     assert int(tk.item()) == 7
+    # a NaN logit (one poisoned weight row), or a NaN input (every logit NaN):
+    # the step has no argmax and the id is vocab, outside the table, which the
+    # next embedding gather turns into a NaN row
+    W[50, 0] = np.nan
+    Wd = dev(W)
+    hdsc.w_lm = ptr(Wd)
+    L.lps_head_forward(C.byref(hdsc), ptr(xd), ptr(lg), ptr(tk), ptr(sc), sb, stream())
+    assert np.isnan(lg.cpu().numpy()[50]) and int(tk.item()) == V
+    W[50, 0] = 0.0
+    Wd = dev(W)
+    hdsc.w_lm = ptr(Wd)
+    x[3] = np.nan
+    xd = dev(x)
+    L.lps_head_forward(C.byref(hdsc), ptr(xd), ptr(lg), ptr(tk), ptr(sc), sb, stream())
+    assert np.all(np.isnan(lg.cpu().numpy()[:V])) and int(tk.item()) == V
+    emb = dev(np.ones((V, d), np.float32))
+    out = torch.zeros(d, dtype=torch.float32, device=DEV)
+    L.lps_embed(ptr(emb), L.LPS_F32, V, d, ptr(tk), ptr(out), stream())
+    assert torch.all(torch.isnan(out))
 
 
 @pytest.mark.parametrize("n16", [1, 4097, (1 << 22) + 333])
@@ -424,6 +443,44 @@ def test_pending_readback(L):
                        ptr(hl), None, C.byref(p2))
     L.lps_pending_drop(p2)          # safe without waiting
     torch.cuda.synchronize()
+    # a handle is consumed by its wait or drop: a second use is refused
+    for fn in (L.lps_pending_wait, L.lps_pending_drop):
+        with pytest.raises(L.LpsError) as e:
+            fn(p)
+        assert e.value.code == L.LPS_ESTATE
+    with pytest.raises(L.LpsError) as e:
+        L.lps_pending_order(p2, rb.cuda_stream)
+    assert e.value.code == L.LPS_ESTATE
+
+
+def test_boundary_orders_a_same_stream_receive_before_another_producer(L):
+    """Step 0 is sent and received on stream A behind a long read (its receive
+    records no event: same stream); step 2 is then sent from stream B into the
+    same slot.  B must wait for A's receive copy: the value received for step 0
+    is step 0's, not step 2's."""
+    d = 1 << 20
+    s0 = torch.full((d,), float("nan"), device=DEV)
+    s1 = torch.full((d,), float("nan"), device=DEV)
+    b = C.c_void_p()
+    L.lps_boundary_create(d, ptr(s0), ptr(s1), C.byref(b))
+    A, B = torch.cuda.Stream(), torch.cuda.Stream()
+    xs = [torch.full((d,), float(t + 1), device=DEV) for t in range(3)]
+    ys = [torch.zeros(d, device=DEV) for _ in range(3)]
+    busy = torch.empty(1 << 30, dtype=torch.uint8, device=DEV)
+    sink = torch.zeros(L.STREAM_SINK, dtype=torch.int32, device=DEV)
+    torch.cuda.synchronize()
+    L.lps_boundary_send(b, ptr(xs[0]), 0, A.cuda_stream)
+    for _ in range(4):     # ~0.6 ms of HBM reads ahead of the receive on A
+        L.lps_hbm_stream_read(ptr(busy), busy.numel(), ptr(sink), A.cuda_stream)
+    L.lps_boundary_recv(b, ptr(ys[0]), 0, A.cuda_stream)
+    L.lps_boundary_send(b, ptr(xs[1]), 1, B.cuda_stream)
+    L.lps_boundary_recv(b, ptr(ys[1]), 1, B.cuda_stream)
+    L.lps_boundary_send(b, ptr(xs[2]), 2, B.cuda_stream)
+    L.lps_boundary_recv(b, ptr(ys[2]), 2, B.cuda_stream)
+    torch.cuda.synchronize()
+    for t in range(3):
+        assert torch.equal(ys[t], xs[t]), t
+    L.lps_boundary_destroy(b)
 
 
 @pytest.mark.parametrize("d", [2048, 2047])   # 16-byte accesses; odd element count: scalar

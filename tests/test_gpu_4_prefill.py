@@ -15,23 +15,35 @@ from oracle.decoder import Decoder
 
 pytestmark = pytest.mark.gpu
 
-TOL = 2e-3   # bf16 weights: of the output scale, per step
+TOL = 2e-3   # bf16 weights, f32 activations (decode): of the output scale, per step
 
-# Prefill rounds the matrix-core operands (normed rows, attention output, SwiGLU
-# output) to bf16 at every layer.  Two implementations that round the same values
-# at the same points but form them with different accumulation orders (f32 on the
-# GPU, f64 in the oracle) take opposite sides of a rounding midpoint now and then,
-# and a flipped operand perturbs the next layer's inputs, so their rounding
-# errors decorrelate over the layers.  The bar therefore comes from the oracle
-# itself: the GPU may sit at most twice as far from the bf16-operand oracle as
-# that oracle sits from the exact-operand one (the size of the rounding effect),
-# plus the bf16-weight bar.  A real mistake (a mask, a position, a layout) moves
-# the result by far more: the split identities below are exact.
+# Prefill bar, fixed.  A chunk rounds five operands per layer to bf16 (unit
+# roundoff u = 2^-9): the normed rows, the cached K and V rows, the attention
+# output, the normed rows again and the SwiGLU output; and the attention kernel
+# takes q and its softmax weights as bf16 operands (a stated deviation from the
+# plain softmax(S) V of the oracle).  The GPU forms the values it rounds with f32
+# accumulation, the oracle in f64, so a fraction of the roundings falls on the
+# other side of a midpoint; a flipped operand moves the next rounding's inputs,
+# and over a few rounding points the two sides' rounding errors decorrelate.
+# Each side then lies within the rounding effect E of the exact-operand result
+# (E <= 1.8 u measured on the oracle at these shapes) and the kernel's bf16 q
+# and weights add up to about 2.2 u more (measured by rounding them in a copy of
+# the oracle), so the two may lie up to about 5 u apart: PF_TOL = 1e-2 of the
+# output scale.  What the bar cannot see (it is larger than E) is checked
+# bit-wise where no cascade has started: layer 0's cache rows of the chunk
+# (test_prefill_first_layer_cache_rows_round_like_the_oracle).
+PF_TOL = 1e-2
+# The 8B slice (8 layers, sums over 4096 and 14336 terms, a 4096-row prefix): the
+# oracle's rounding effect E there is 1.6e-2 of the logit scale (rounded vs exact
+# operands, both in the oracle) and rounding q and the weights in a copy of the
+# oracle moves the logits by 1.4e-2: the two sides may lie about 2 E apart.
+PF_TOL_8B = 3e-2
 
 
-def _pf_tol(exact, rounded):
-    exact, rounded = np.asarray(exact, np.float64), np.asarray(rounded, np.float64)
-    return 2.0 * float(np.abs(exact - rounded).max()) + TOL * float(np.abs(rounded).max())
+def _rel_err(got, want):
+    want = np.asarray(want, np.float64)
+    return float(np.max(np.abs(np.asarray(got, np.float64) - want)) / np.abs(want).max())
+
 
 PF = synth.DecoderConfig("pf-small", n_layers=4, d=256, nq=4, nkv=2, hd=64, ff=768, vocab=1024,
                          wdtype="bf16", kvdtype="bf16", prefix=37, prompt=45, steps=6)
@@ -63,11 +75,11 @@ def _check_prefill(rt, m):
     dd = rt.DeviceDecoder(m)
     lg, am, X = dd.prefill(m["prompt"])
     olg, oam, OX = Decoder(m).prefill(m["prompt"])
-    elg, _, EX = Decoder(m).prefill(m["prompt"], act=None)
-    for got, want, exact, what in ((X, OX, EX, "hidden rows"), (lg, olg, elg, "logits")):
-        err = float(np.max(np.abs(np.asarray(got, np.float64) - want)))
-        assert err <= _pf_tol(exact, want), (what, err, _pf_tol(exact, want))
-    assert am == oam or _argmax_ok(am, olg, 2 * _pf_tol(elg, olg) / np.abs(olg).max())
+    for got, want, what in ((X, OX, "hidden rows"), (lg, olg, "logits")):
+        err = _rel_err(got, want)
+        print(f"{m['cfg'].name} prefill {what}: max err {err:.2e} of scale (bar {PF_TOL:.0e})")
+        assert err <= PF_TOL, (what, err)
+    assert am == oam or _argmax_ok(am, olg, PF_TOL)
     dd.close()
 
 
@@ -111,23 +123,83 @@ def test_prefill_stage_and_chunk_splits_bit_identical(rt, small, streams):
     dd.close()
 
 
+def _gpu_cache_rows(dd, l, n):
+    """Layer l's K and V cache rows 0..n-1 from the device, as [nkv, n, hd] bits."""
+    from layer_pipeline_stage_amd import layout
+    t = dd.layers[l]
+    k = layout.k_from_tiles(t["k"].cpu()).numpy().view(np.uint16)
+    v = layout.v_from_tiles(t["v"].cpu()).numpy().view(np.uint16)
+    return k[:, :n], v[:, :n]
+
+
+def test_prefill_first_layer_cache_rows_round_like_the_oracle(rt, small):
+    """Layer 0 sees the same f32 embedding rows on both sides, so its chunk K/V
+    rows (normed rows rounded to bf16, f32 GEMM, RoPE, bf16 cache) differ from
+    the oracle's only where f32 and f64 accumulation straddle a bf16 midpoint:
+    at least 99 % bit-identical and the rest one bf16 step apart.  A missing or
+    truncating rounding of the normed rows, or a truncating cache store, moves a
+    quarter or more of them."""
+    cfg = small["cfg"]
+    P = len(small["prompt"])
+    dd = rt.DeviceDecoder(small)
+    dd.prefill(small["prompt"])
+    gk, gv = _gpu_cache_rows(dd, 0, cfg.prefix + P)
+    dd.close()
+    dec = Decoder(small)
+    dec.prefill(small["prompt"])
+    for got, want, what in ((gk, dec.K[0], "K"), (gv, dec.V[0], "V")):
+        got = got[:, cfg.prefix:cfg.prefix + P].astype(np.int64)
+        want = want[:, cfg.prefix:cfg.prefix + P].astype(np.int64)
+        same = float(np.mean(got == want))
+        print(f"layer 0 {what} rows of the chunk: {same:.4%} bit-identical")
+        assert same >= 0.99, (what, same)
+        assert np.max(np.abs(got - want)) <= 1, what       # same sign: one bf16 step
+
+
+def test_prefill_ignores_stale_cache_rows(rt, small):
+    """Cache rows at and past the chunk's end (never written, or left by a poisoned
+    step) hold NaN: the prefill output is bit-identical to the run over zeroed
+    rows (masked keys get weight 0 and their V rows are not multiplied)."""
+    cfg = small["cfg"]
+    P = len(small["prompt"])
+    end = cfg.prefix + P
+    dd = rt.DeviceDecoder(small)
+    ref = dd.prefill(small["prompt"])
+    dd.reset()
+    from layer_pipeline_stage_amd import layout
+    for t in dd.layers:
+        for name, back, to in (("k", layout.k_from_tiles, layout.k_to_tiles),
+                               ("v", layout.v_from_tiles, layout.v_to_tiles)):
+            rows = back(t[name])
+            rows[:, end:] = 0x7FC0                              # bf16 NaN
+            t[name].copy_(to(rows))
+    torch.cuda.synchronize()
+    got = dd.prefill(small["prompt"])
+    dd.close()
+    assert got[1] == ref[1] and np.array_equal(got[0], ref[0]) and np.array_equal(got[2], ref[2])
+
+
 def test_decode_continues_from_the_prefilled_cache(rt, small):
+    """Decode steps after a prefill read the chunk's rows from the caches: the
+    oracle, given the device's own prefilled cache rows, matches every step's
+    logits at the decode bar."""
     cfg = small["cfg"]
     P = len(small["prompt"])
     dd = rt.DeviceDecoder(small, fence=[0, 2, 4])
     lg, am, _ = dd.prefill(small["prompt"])
+    olg, oam, _ = Decoder(small).prefill(small["prompt"])
+    assert am == oam or _argmax_ok(am, olg, PF_TOL)
+    rows = [_gpu_cache_rows(dd, l, cfg.prefix + P) for l in range(cfg.n_layers)]
     res = dd.run_tokens([am], cfg.steps - 1, p0=cfg.prefix + P)
-    dec, ex = Decoder(small), Decoder(small)
-    olg, oam, _ = dec.prefill(small["prompt"])
-    elg, _, _ = ex.prefill(small["prompt"], act=None)
-    rel = _pf_tol(elg, olg) / np.abs(olg).max()
-    assert am == oam or _argmax_ok(am, olg, rel)
-    # the decode steps read the prefilled caches: same bar, from the same two oracles
-    _, _, olgs = dec.greedy([], 0, p0=cfg.prefix + P, feed=res.fed)
-    _, _, elgs = ex.greedy([], 0, p0=cfg.prefix + P, feed=res.fed)
-    for i, (a, b, e) in enumerate(zip(res.logits, olgs, elgs)):
-        err = float(np.max(np.abs(a - b)))
-        assert err <= _pf_tol(e, b), (i, err, _pf_tol(e, b))
+    dec = Decoder(small)
+    for l, (k, v) in enumerate(rows):
+        dec.K[l][:, :cfg.prefix + P] = k
+        dec.V[l][:, :cfg.prefix + P] = v
+    _, oams, olgs = dec.greedy([], 0, p0=cfg.prefix + P, feed=res.fed)
+    for i, (a, b) in enumerate(zip(res.logits, olgs)):
+        err = _rel_err(a, b)
+        assert err <= TOL, (i, err)
+        assert res.argmax[i] == oams[i] or _argmax_ok(res.argmax[i], b)
     dd.close()
 
 
@@ -145,8 +217,8 @@ def test_prefill_dense8b_slice_full_size(rt):
     assert am1 == am and np.array_equal(lg1, lg) and np.array_equal(X1, X)
     dd.close()
     olg, oam, OX = Decoder(m, weight_cache=False).prefill(m["prompt"])
-    elg, _, EX = Decoder(m, weight_cache=False).prefill(m["prompt"], act=None)
-    for got, want, exact, what in ((lg, olg, elg, "logits"), (X[-1], OX[-1], EX[-1], "last row")):
-        err = float(np.max(np.abs(np.asarray(got, np.float64) - want)))
-        assert err <= _pf_tol(exact, want), (what, err, _pf_tol(exact, want))
-    assert am == oam or _argmax_ok(am, olg, 2 * _pf_tol(elg, olg) / np.abs(olg).max())
+    for got, want, what in ((lg, olg, "logits"), (X[-1], OX[-1], "last row")):
+        err = _rel_err(got, want)
+        print(f"8B slice prefill {what}: max err {err:.2e} of scale (bar {PF_TOL_8B:.0e})")
+        assert err <= PF_TOL_8B, (what, err)
+    assert am == oam or _argmax_ok(am, olg, PF_TOL_8B)

@@ -405,3 +405,15 @@ def test_causal_attend_closed_forms():
     assert abs(O[0] - 1.0 / (1.0 + w1)) <= 1e-15
     assert abs(O[1] - w1 / (1.0 + w1)) <= 1e-15
     assert O[2] == O[3] == 0.0
+
+
+def test_poisoned_step_stays_poisoned():
+    """An id outside the table embeds as a NaN row; NaN logits have no argmax
+    and give the out-of-table id vocab, so the poison carries to the next step."""
+    m = synth.make_tiny(replace(synth.TINY, prompt=2, steps=1))
+    d = Decoder(m)
+    V = m["cfg"].vocab
+    assert np.all(np.isnan(d.embed(V))) and np.all(np.isnan(d.embed(-1)))
+    logits, a = d.step(V, 0)
+    assert np.all(np.isnan(logits)) and a == V
+    assert not np.isnan(d.embed(V - 1)).any()
