@@ -160,6 +160,20 @@ size_t lps_model_scratch_bytes(const lps_model* m);
 int lps_stage_forward(const lps_model* m, const int32_t* fence, int32_t n_stages, int32_t stage,
                       float* x, int32_t pos, void* scratch, size_t scratch_bytes, void* stream);
 
+/* lps_stage_forward without caller scratch, for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  The layer scratch is a static device buffer inside the
+ * library, 8 MiB, one per GPU, held until the process ends; its address is
+ * looked up on the first call on each device.  Nothing is allocated and
+ * nothing in it needs clearing (every scratch value is written before it is
+ * read).  A model whose layers need more scratch than the buffer holds
+ * (lps_model_scratch_bytes(m) > 8 MiB) is refused with LPS_ERANGE before
+ * anything is enqueued.  Every call on one GPU shares that GPU's buffer: calls
+ * whose work overlaps on one GPU (other streams, or other threads) race on it;
+ * the caller keeps them ordered. */
+int lps_stage_forward_static(const lps_model* m, const int32_t* fence, int32_t n_stages,
+                             int32_t stage, float* x, int32_t pos, void* stream);
+
 /* ---- chunked dense prefill through the stages -------------------------------
  * memra pp module docs (functions on the prime split: the chunked prompt walk
  * takes the same per-stage layer ranges as decode) and ninfer pipeline stages

@@ -532,6 +532,53 @@ int lps_stage_forward_dpos(const lps_model* m, const int32_t* fence, int32_t n_s
   return LPS_OK;
 }
 
+}  // extern "C"
+
+// ---- the stage walk without caller scratch ---------------------------------------------
+// For callers that cannot allocate (code under graph capture, tight serving loops):
+// the layer scratch lives in this file-scope device array instead, one copy per GPU,
+// held until the process ends.  In host code `scratch` names a host-side stand-in,
+// never the device memory: its device address is looked up once per device with
+// hipGetSymbolAddress (with that device current) and only that address is used.
+namespace lps {
+constexpr size_t kStaticScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+static std::mutex g_static_mu;
+static std::vector<void*> g_static_ptr;   // per device ordinal, nullptr until looked up
+
+static int static_scratch(void** out) {
+  int dev = -1;
+  LPS_HIP(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lk(g_static_mu);
+  if (size_t(dev) >= g_static_ptr.size()) g_static_ptr.resize(size_t(dev) + 1, nullptr);
+  if (!g_static_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(LPS_EHIP, "lps_stage_forward_static: hipGetSymbolAddress(scratch) on device %d: %s",
+                  dev, hipGetErrorString(e));
+    g_static_ptr[dev] = ptr;
+  }
+  *out = g_static_ptr[dev];
+  return LPS_OK;
+}
+}  // namespace lps
+
+extern "C" {
+
+int lps_stage_forward_static(const lps_model* m, const int32_t* fence, int32_t n_stages,
+                             int32_t stage, float* x, int32_t pos, void* stream) {
+  LPS_REQUIRE(m, LPS_EINVAL, "lps_stage_forward_static: null model");
+  LPS_REQUIRE(m->scratch <= kStaticScratchBytes, LPS_ERANGE,
+              "lps_stage_forward_static: the model's layers need %zu bytes of scratch, more than "
+              "the %zu bytes of the library's static buffer (use lps_stage_forward)",
+              m->scratch, kStaticScratchBytes);
+  void* sc = nullptr;
+  int rc = static_scratch(&sc);
+  if (rc) return rc;
+  return lps_stage_forward(m, fence, n_stages, stage, x, pos, sc, kStaticScratchBytes, stream);
+}
+
 size_t lps_prefill_scratch_bytes(const lps_model* m, int32_t T) {
   if (!m || T < 1) return 0;
   size_t mx = 0;
