@@ -102,7 +102,15 @@ int lps_stage_solve(int32_t n_layers, int32_t n_stages, const int64_t* stage_fre
  * dummy heads plan, Geometry and Weight-padding design for the GQA map and the
  * padded-head layout; ninfer pipeline stages, Tensor parallelism: status, for
  * the gate-then-up row order.)
+ * A layer with nq == 0 has no attention sublayer (the attention fields are then
+ * ignored): an FFN-only block, as in the MoE layer stack.  ffn_kind LPS_FFN_MOE
+ * replaces the dense FFN by the MoE FFN of *moe (its own norm gain; the dense
+ * FFN fields are then ignored): x += MoE(RMSNorm(x)) as lps_moe_layer_decode
+ * computes it (strata PR #3648, Problem and result: MoE layers whose sums cross
+ * a stage; memra pp docs, header: any layer range is a stage).
  */
+struct lps_moe_desc;
+enum { LPS_FFN_DENSE = 0, LPS_FFN_MOE = 1 };
 typedef struct lps_layer_desc {
   int32_t d;          /* n_embd */
   int32_t nq, nkv;    /* q heads, kv heads (nq % nkv == 0) */
@@ -130,6 +138,9 @@ typedef struct lps_layer_desc {
                       * contiguous block.)  bf16 caches need ctx_max % 16 == 0 */
   const float* rope_cs;  /* (dev, optional) [ctx_max, hd/2, 2] f32: cos, sin of pos * theta_i
                           * (lps_rope_table); required by the device-position entry points */
+  int32_t ffn_kind;      /* LPS_FFN_DENSE (0: g_ffn, w_gu, w_d, ff) | LPS_FFN_MOE (moe) */
+  const struct lps_moe_desc* moe;   /* (host) LPS_FFN_MOE: the layer's MoE FFN; copied by
+                                     * lps_model_create, read during the call otherwise */
 } lps_layer_desc;
 
 /* Scratch bytes lps_layer_forward needs for this layer (0 on invalid desc). */
@@ -147,8 +158,8 @@ int lps_layer_forward(const lps_layer_desc* L, float* x, int32_t pos, void* scra
 
 /* ---- a model handle and the stage walk ----------------------------------- */
 typedef struct lps_model lps_model;
-/* Copies the n_layers descriptors (the device buffers they point at stay the
- * caller's).  *out receives the handle. */
+/* Copies the n_layers descriptors, and the MoE descriptors they point at (the
+ * device buffers they point at stay the caller's).  *out receives the handle. */
 int lps_model_create(const lps_layer_desc* layers, int32_t n_layers, lps_model** out);
 int lps_model_destroy(lps_model* m);
 /* Max scratch over the model's layers. */

@@ -16,6 +16,7 @@ LPS_OK, LPS_EINVAL, LPS_ERANGE, LPS_ESTATE, LPS_EHIP, LPS_ENOMEM, LPS_EUNSUP = 0
 LPS_F32, LPS_BF16, LPS_MXFP4 = 0, 1, 2
 LPS_EPI_STORE, LPS_EPI_ADD, LPS_EPI_SWIGLU = 0, 1, 2
 KINDS = {"qkv": 1, "attn": 2, "oproj": 3, "gateup": 4, "down": 5, "head": 6}
+LPS_FFN_DENSE, LPS_FFN_MOE = 0, 1
 DTYPES = {"f32": LPS_F32, "bf16": LPS_BF16, "mxfp4": LPS_MXFP4}
 
 
@@ -37,6 +38,7 @@ class LayerDesc(C.Structure):
         ("w_gu", C.c_void_p), ("s_gu", C.c_void_p),
         ("w_d", C.c_void_p), ("s_d", C.c_void_p),
         ("k_cache", C.c_void_p), ("v_cache", C.c_void_p), ("rope_cs", C.c_void_p),
+        ("ffn_kind", C.c_int32), ("moe", C.c_void_p),
     ]
 
 

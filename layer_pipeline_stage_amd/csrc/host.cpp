@@ -89,52 +89,78 @@ static bool gqa_built(int g) { return g == 1 || g == 2 || g == 4 || g == 6 || g 
 
 int check_layer(const lps_layer_desc* L, const char* who) {
   LPS_REQUIRE(L, LPS_EINVAL, "%s: null layer descriptor", who);
-  LPS_REQUIRE(L->d > 0 && L->nq > 0 && L->nkv > 0 && L->hd > 0 && L->ff > 0, LPS_EINVAL,
-              "%s: d/nq/nkv/hd/ff must be > 0 (got %d/%d/%d/%d/%d)", who, L->d, L->nq, L->nkv,
-              L->hd, L->ff);
-  LPS_REQUIRE(L->nq % L->nkv == 0 && gqa_built(L->nq / L->nkv), LPS_EUNSUP, "%s: nq / nkv = %d/%d: 1, 2, 4, 6 or 8 q heads per kv head are built", who,
-              L->nq, L->nkv);
-  LPS_REQUIRE(L->hd == 64 || L->hd == 128 || L->hd == 256, LPS_EUNSUP,  // RoPE table: hd/2 <= 128
-              "%s: head dim %d not built (64, 128, 256)", who, L->hd);
+  LPS_REQUIRE(L->ffn_kind == LPS_FFN_DENSE || L->ffn_kind == LPS_FFN_MOE, LPS_EINVAL,
+              "%s: ffn_kind %d", who, L->ffn_kind);
+  LPS_REQUIRE(L->d > 0 && L->nq >= 0, LPS_EINVAL, "%s: d %d must be > 0 and nq %d >= 0", who, L->d,
+              L->nq);
   LPS_REQUIRE(L->wdtype == LPS_F32 || L->wdtype == LPS_BF16 || L->wdtype == LPS_MXFP4, LPS_EINVAL,
               "%s: wdtype %d", who, L->wdtype);
-  LPS_REQUIRE(L->kvdtype == LPS_F32 || L->kvdtype == LPS_BF16, LPS_EINVAL, "%s: kvdtype %d", who,
-              L->kvdtype);
   const int ch = chunk_of(L->wdtype);
-  LPS_REQUIRE(L->d % ch == 0 && (L->nq * L->hd) % ch == 0 && L->ff % ch == 0, LPS_EINVAL,
-              "%s: d %d, nq*hd %d and ff %d must be multiples of %d for this weight dtype", who,
-              L->d, L->nq * L->hd, L->ff, ch);
-  LPS_REQUIRE(L->ctx_max > 0, LPS_EINVAL, "%s: ctx_max %d", who, L->ctx_max);
-  if (L->kvdtype == LPS_BF16)   // whole 16-row V tiles; 32-bit byte offsets per head
-    LPS_REQUIRE(L->ctx_max % 16 == 0 && L->ctx_max <= (1 << 22), LPS_EINVAL,
-                "%s: bf16 caches need ctx_max %d to be a multiple of 16 and at most 4194304", who,
-                L->ctx_max);
-  LPS_REQUIRE(L->d * 4 <= 160 * 1024 && L->ff * 4 <= 160 * 1024 && L->nq * L->hd * 4 <= 160 * 1024,
-              LPS_EUNSUP, "%s: an activation vector exceeds 160 KiB of LDS", who);
-  LPS_REQUIRE(L->g_attn && L->w_qkv && L->w_o && L->g_ffn && L->w_gu && L->w_d && L->k_cache &&
-                  L->v_cache,
-              LPS_EINVAL, "%s: null weight / gain / cache pointer", who);
-  LPS_REQUIRE(aligned16(L->w_qkv) && aligned16(L->w_o) && aligned16(L->w_gu) && aligned16(L->w_d) &&
-                  aligned16(L->g_attn) && aligned16(L->g_ffn) && aligned16(L->k_cache) &&
-                  aligned16(L->v_cache),
-              LPS_EINVAL, "%s: weights, gains and caches must be 16-byte aligned", who);
+  LPS_REQUIRE(L->d * 4 <= 160 * 1024, LPS_EUNSUP, "%s: d %d exceeds 160 KiB of LDS", who, L->d);
+  if (L->nq > 0) {   // the attention sublayer
+    LPS_REQUIRE(L->nkv > 0 && L->hd > 0, LPS_EINVAL, "%s: nkv %d and hd %d must be > 0", who,
+                L->nkv, L->hd);
+    LPS_REQUIRE(L->nq % L->nkv == 0 && gqa_built(L->nq / L->nkv), LPS_EUNSUP,
+                "%s: nq / nkv = %d/%d: 1, 2, 4, 6 or 8 q heads per kv head are built", who, L->nq,
+                L->nkv);
+    LPS_REQUIRE(L->hd == 64 || L->hd == 128 || L->hd == 256, LPS_EUNSUP,  // RoPE table: hd/2 <= 128
+                "%s: head dim %d not built (64, 128, 256)", who, L->hd);
+    LPS_REQUIRE(L->kvdtype == LPS_F32 || L->kvdtype == LPS_BF16, LPS_EINVAL, "%s: kvdtype %d", who,
+                L->kvdtype);
+    LPS_REQUIRE(L->d % ch == 0 && (L->nq * L->hd) % ch == 0, LPS_EINVAL,
+                "%s: d %d and nq*hd %d must be multiples of %d for this weight dtype", who, L->d,
+                L->nq * L->hd, ch);
+    LPS_REQUIRE(L->ctx_max > 0, LPS_EINVAL, "%s: ctx_max %d", who, L->ctx_max);
+    if (L->kvdtype == LPS_BF16)   // whole 16-row V tiles; 32-bit byte offsets per head
+      LPS_REQUIRE(L->ctx_max % 16 == 0 && L->ctx_max <= (1 << 22), LPS_EINVAL,
+                  "%s: bf16 caches need ctx_max %d to be a multiple of 16 and at most 4194304", who,
+                  L->ctx_max);
+    LPS_REQUIRE(L->nq * L->hd * 4 <= 160 * 1024, LPS_EUNSUP,
+                "%s: the attention output exceeds 160 KiB of LDS", who);
+    LPS_REQUIRE(L->g_attn && L->w_qkv && L->w_o && L->k_cache && L->v_cache, LPS_EINVAL,
+                "%s: null attention weight / gain / cache pointer", who);
+    LPS_REQUIRE(aligned16(L->w_qkv) && aligned16(L->w_o) && aligned16(L->g_attn) &&
+                    aligned16(L->k_cache) && aligned16(L->v_cache),
+                LPS_EINVAL, "%s: weights, gains and caches must be 16-byte aligned", who);
+    if (L->wdtype == LPS_MXFP4)
+      LPS_REQUIRE(L->s_qkv && L->s_o, LPS_EINVAL, "%s: MXFP4 weights need their e8m0 scale arrays",
+                  who);
+  }
+  if (L->ffn_kind == LPS_FFN_MOE) {   // the MoE FFN carries its own norm gain and weights
+    LPS_REQUIRE(L->moe, LPS_EINVAL, "%s: ffn_kind MoE with a null moe descriptor", who);
+    LPS_REQUIRE(L->moe->d == L->d, LPS_EINVAL, "%s: moe->d %d differs from d %d", who, L->moe->d,
+                L->d);
+    return check_moe_decode(L->moe, who);
+  }
+  LPS_REQUIRE(L->ff > 0 && L->d % ch == 0 && L->ff % ch == 0, LPS_EINVAL,
+              "%s: d %d and ff %d must be positive multiples of %d for this weight dtype", who, L->d,
+              L->ff, ch);
+  LPS_REQUIRE(L->ff * 4 <= 160 * 1024, LPS_EUNSUP, "%s: ff %d exceeds 160 KiB of LDS", who, L->ff);
+  LPS_REQUIRE(L->g_ffn && L->w_gu && L->w_d, LPS_EINVAL, "%s: null FFN weight / gain pointer", who);
+  LPS_REQUIRE(aligned16(L->w_gu) && aligned16(L->w_d) && aligned16(L->g_ffn), LPS_EINVAL,
+              "%s: weights and gains must be 16-byte aligned", who);
   if (L->wdtype == LPS_MXFP4)
-    LPS_REQUIRE(L->s_qkv && L->s_o && L->s_gu && L->s_d, LPS_EINVAL,
-                "%s: MXFP4 weights need their e8m0 scale arrays", who);
+    LPS_REQUIRE(L->s_gu && L->s_d, LPS_EINVAL, "%s: MXFP4 weights need their e8m0 scale arrays", who);
   return LPS_OK;
 }
 
-// scratch layout of one layer: q | o | m | attention partials
+// scratch layout of one layer: q | o | attention partials (attention sublayer) and
+// m (dense FFN) or the MoE FFN's scratch, each region after the previous one
 struct LayerScratch {
-  size_t q, o, m, attn, total;
+  size_t q, o, attn, m, total;
 };
 static LayerScratch layer_scratch(const lps_layer_desc* L) {
   LayerScratch s{};
-  s.q = 0;
-  s.o = align256(size_t(L->nq) * L->hd * 4);
-  s.m = s.o + align256(size_t(L->nq) * L->hd * 4);
-  s.attn = s.m + align256(size_t(L->ff) * 4);
-  s.total = s.attn + attn_scratch(L->nq, L->nkv, L->hd, L->ctx_max);
+  size_t off = 0;
+  if (L->nq > 0) {
+    s.q = off;
+    s.o = off += align256(size_t(L->nq) * L->hd * 4);
+    s.attn = off += align256(size_t(L->nq) * L->hd * 4);
+    off += align256(attn_scratch(L->nq, L->nkv, L->hd, L->ctx_max));
+  }
+  s.m = off;
+  s.total = off + (L->ffn_kind == LPS_FFN_MOE ? moe_decode_scratch(L->moe)
+                                               : align256(size_t(L->ff) * 4));
   return s;
 }
 
@@ -143,19 +169,23 @@ static int layer_forward(const lps_layer_desc* L, float* x, int pos, void* scrat
                          const int32_t* pos_dev = nullptr) {
   const LayerScratch s = layer_scratch(L);
   char* sc = static_cast<char*>(scratch);
-  float* q = reinterpret_cast<float*>(sc + s.q);
-  float* o = reinterpret_cast<float*>(sc + s.o);
   float* m = reinterpret_cast<float*>(sc + s.m);
-  void* at = sc + s.attn;
-  QkvArgs qa{L, x, pos, q, pos_dev};
-  int rc = launch_qkv(qa, st, timer_take(LPS_KIND_QKV));
-  if (rc) return rc;
-  rc = launch_attention(L->nq, L->nkv, L->hd, L->kvdtype, L->k_cache, L->v_cache, L->ctx_max,
-                        pos + 1, q, o, at, st, timer_take(LPS_KIND_ATTN), pos_dev);
-  if (rc) return rc;
-  rc = launch_gemv(L->wdtype, L->w_o, L->s_o, L->d, L->nq * L->hd, o, nullptr, 0.f, x,
-                   LPS_EPI_ADD, st, timer_take(LPS_KIND_OPROJ));
-  if (rc) return rc;
+  int rc;
+  if (L->nq > 0) {
+    float* q = reinterpret_cast<float*>(sc + s.q);
+    float* o = reinterpret_cast<float*>(sc + s.o);
+    void* at = sc + s.attn;
+    QkvArgs qa{L, x, pos, q, pos_dev};
+    rc = launch_qkv(qa, st, timer_take(LPS_KIND_QKV));
+    if (rc) return rc;
+    rc = launch_attention(L->nq, L->nkv, L->hd, L->kvdtype, L->k_cache, L->v_cache, L->ctx_max,
+                          pos + 1, q, o, at, st, timer_take(LPS_KIND_ATTN), pos_dev);
+    if (rc) return rc;
+    rc = launch_gemv(L->wdtype, L->w_o, L->s_o, L->d, L->nq * L->hd, o, nullptr, 0.f, x,
+                     LPS_EPI_ADD, st, timer_take(LPS_KIND_OPROJ));
+    if (rc) return rc;
+  }
+  if (L->ffn_kind == LPS_FFN_MOE) return moe_decode(L->moe, x, m, st);
   rc = launch_gemv(L->wdtype, L->w_gu, L->s_gu, 2 * L->ff, L->d, x, L->g_ffn, L->eps, m,
                    LPS_EPI_SWIGLU, st, timer_take(LPS_KIND_GATEUP));
   if (rc) return rc;
@@ -181,6 +211,7 @@ static int check_fence(const int32_t* fence, int32_t n_stages, int32_t n_layers,
 
 struct lps_model {
   std::vector<lps_layer_desc> layers;
+  std::vector<lps_moe_desc> moes;   // copies the MoE layers' descriptors point at
   size_t scratch = 0;
 };
 
@@ -446,8 +477,8 @@ int lps_layer_forward(const lps_layer_desc* L, float* x, int32_t pos, void* scra
   LPS_REQUIRE(x && scratch, LPS_EINVAL, "lps_layer_forward: null x or scratch");
   LPS_REQUIRE(aligned16(x) && aligned16(scratch), LPS_EINVAL,
               "lps_layer_forward: x and scratch must be 16-byte aligned");
-  LPS_REQUIRE(pos >= 0 && pos < L->ctx_max, LPS_ERANGE, "lps_layer_forward: pos %d outside [0, %d)",
-              pos, L->ctx_max);
+  LPS_REQUIRE(L->nq == 0 || (pos >= 0 && pos < L->ctx_max), LPS_ERANGE,
+              "lps_layer_forward: pos %d outside [0, %d)", pos, L->ctx_max);
   LPS_REQUIRE(scratch_bytes >= layer_scratch(L).total, LPS_EINVAL,
               "lps_layer_forward: scratch %zu bytes < %zu needed", scratch_bytes,
               layer_scratch(L).total);
@@ -468,6 +499,12 @@ int lps_model_create(const lps_layer_desc* layers, int32_t n_layers, lps_model**
   lps_model* m = new (std::nothrow) lps_model;
   LPS_REQUIRE(m, LPS_ENOMEM, "lps_model_create: out of host memory");
   m->layers.assign(layers, layers + n_layers);
+  m->moes.reserve(size_t(n_layers));   // no reallocation: the layers point into it
+  for (auto& L : m->layers)
+    if (L.ffn_kind == LPS_FFN_MOE) {
+      m->moes.push_back(*L.moe);
+      L.moe = &m->moes.back();
+    }
   m->scratch = mx;
   *out = m;
   return LPS_OK;
@@ -493,7 +530,7 @@ int lps_stage_forward(const lps_model* m, const int32_t* fence, int32_t n_stages
   LPS_REQUIRE(scratch_bytes >= m->scratch, LPS_EINVAL, "lps_stage_forward: scratch %zu < %zu needed",
               scratch_bytes, m->scratch);
   for (int l = fence[stage]; l < fence[stage + 1]; ++l)
-    LPS_REQUIRE(pos >= 0 && pos < m->layers[l].ctx_max, LPS_ERANGE,
+    LPS_REQUIRE(m->layers[l].nq == 0 || (pos >= 0 && pos < m->layers[l].ctx_max), LPS_ERANGE,
                 "lps_stage_forward: pos %d outside layer %d's cache [0, %d)", pos, l,
                 m->layers[l].ctx_max);
   hipStream_t st = as_stream(stream);
@@ -519,6 +556,7 @@ int lps_stage_forward_dpos(const lps_model* m, const int32_t* fence, int32_t n_s
   LPS_REQUIRE(scratch_bytes >= m->scratch, LPS_EINVAL,
               "lps_stage_forward_dpos: scratch %zu < %zu needed", scratch_bytes, m->scratch);
   for (int l = fence[stage]; l < fence[stage + 1]; ++l) {
+    if (m->layers[l].nq == 0) continue;   // no attention: no position is read
     const float* t = m->layers[l].rope_cs;
     LPS_REQUIRE(t && (reinterpret_cast<uintptr_t>(t) & 7) == 0, LPS_EINVAL,
                 "lps_stage_forward_dpos: layer %d needs an 8-byte aligned rope_cs table", l);
@@ -760,6 +798,7 @@ int lps_qkv_rope_append(const lps_layer_desc* L, const float* x, int32_t pos, fl
                         void* stream) {
   int rc = check_layer(L, "lps_qkv_rope_append");
   if (rc) return rc;
+  LPS_REQUIRE(L->nq > 0, LPS_EINVAL, "lps_qkv_rope_append: the layer has no attention (nq 0)");
   LPS_REQUIRE(x && q && aligned16(x), LPS_EINVAL, "lps_qkv_rope_append: null or unaligned x / q");
   LPS_REQUIRE(pos >= 0 && pos < L->ctx_max, LPS_ERANGE,
               "lps_qkv_rope_append: pos %d outside [0, %d)", pos, L->ctx_max);

@@ -116,5 +116,9 @@ void count_act_pieces(int64_t n);
 
 // validation helpers shared by entry points
 int check_layer(const lps_layer_desc* L, const char* who);
+// MoE FFN decode of one token (moe.hip): validation, scratch bytes, the launches
+int check_moe_decode(const lps_moe_desc* m, const char* who);
+size_t moe_decode_scratch(const lps_moe_desc* m);
+int moe_decode(const lps_moe_desc* m, float* x, void* scratch, hipStream_t st);
 
 }  // namespace lps

@@ -261,23 +261,25 @@ extern "C" size_t lps_moe_layer_scratch_bytes(const lps_moe_desc* m) {
   return moe_scratch(m).total;
 }
 
-extern "C" int lps_moe_layer_decode(const lps_moe_desc* m, float* x, void* scratch,
-                                    size_t scratch_bytes, void* stream) {
-  int rc = check_moe(m, "lps_moe_layer_decode");
+namespace lps {
+int check_moe_decode(const lps_moe_desc* m, const char* who) {
+  int rc = check_moe(m, who);
   if (rc) return rc;
-  LPS_REQUIRE(x && scratch, LPS_EINVAL, "lps_moe_layer_decode: null x or scratch");
+  LPS_REQUIRE(m->d <= 4096 && m->d % 8 == 0, LPS_EUNSUP, "%s: d %d (a multiple of 8, <= 4096)", who,
+              m->d);
+  return LPS_OK;
+}
+size_t moe_decode_scratch(const lps_moe_desc* m) { return moe_scratch(m).total; }
+
+// One MoE FFN layer for one token (validated by the caller): route, the selected
+// and the shared expert's gate/up + SwiGLU and down GEMVs, the ordered combine.
+int moe_decode(const lps_moe_desc* m, float* x, void* scratch, hipStream_t st) {
   const MoeScratch s = moe_scratch(m);
-  LPS_REQUIRE(scratch_bytes >= s.total, LPS_EINVAL, "lps_moe_layer_decode: scratch %zu < %zu",
-              scratch_bytes, s.total);
-  hipStream_t st = as_stream(stream);
   char* sc = static_cast<char*>(scratch);
   int32_t* idx = reinterpret_cast<int32_t*>(sc + s.idx);
   float* wts = reinterpret_cast<float*>(sc + s.w);
   float* mbuf = reinterpret_cast<float*>(sc + s.mbuf);
-  LPS_REQUIRE(m->d <= 4096 && m->d % 8 == 0, LPS_EUNSUP,
-              "lps_moe_layer_decode: d %d (a multiple of 8, <= 4096)",
-              m->d);
-  rc = launch_route(m, x, 1, reinterpret_cast<float*>(sc + s.logits), idx, wts, st);
+  int rc = launch_route(m, x, 1, reinterpret_cast<float*>(sc + s.logits), idx, wts, st);
   if (rc) return rc;
   rc = launch_moe_gu(m->w_gu_e, m->w_gu_s, idx, m->n_experts, m->top_k, m->ff, m->d, x, m->g_ffn,
                      m->eps, mbuf, st);
@@ -297,4 +299,16 @@ extern "C" int lps_moe_layer_decode(const lps_moe_desc* m, float* x, void* scrat
   hipLaunchKernelGGL(k_moe_combine, dim3((m->d + 255) / 256), dim3(256), 0, st, cp);
   LPS_HIP(hipGetLastError());
   return LPS_OK;
+}
+}  // namespace lps
+
+extern "C" int lps_moe_layer_decode(const lps_moe_desc* m, float* x, void* scratch,
+                                    size_t scratch_bytes, void* stream) {
+  int rc = check_moe_decode(m, "lps_moe_layer_decode");
+  if (rc) return rc;
+  LPS_REQUIRE(x && scratch, LPS_EINVAL, "lps_moe_layer_decode: null x or scratch");
+  const MoeScratch s = moe_scratch(m);
+  LPS_REQUIRE(scratch_bytes >= s.total, LPS_EINVAL, "lps_moe_layer_decode: scratch %zu < %zu",
+              scratch_bytes, s.total);
+  return moe_decode(m, x, scratch, as_stream(stream));
 }

@@ -683,6 +683,9 @@ PrefillScratch prefill_scratch(const lps_layer_desc* L, int T) {
 }
 
 int check_prefill_layer(const lps_layer_desc* L, int T, int p0, const char* who) {
+  LPS_REQUIRE(L->nq > 0 && L->ffn_kind == LPS_FFN_DENSE, LPS_EUNSUP,
+              "%s: the chunked prefill walks attention layers with a dense FFN (MoE FFN layers "
+              "take lps_moe_prefill)", who);
   LPS_REQUIRE(L->wdtype == LPS_BF16 && L->kvdtype == LPS_BF16, LPS_EUNSUP,
               "%s: prefill runs bf16 weights with bf16 caches (got %d / %d)", who, L->wdtype,
               L->kvdtype);

@@ -483,9 +483,14 @@ class DeviceDecoder:
 
 
 class DeviceMoEStack:
-    """A synth MoE FFN stack resident on one GPU (decode: one token per step)."""
+    """A synth MoE FFN stack resident on one GPU, walked as N stages on N streams:
+    every layer is an FFN-only block (nq 0) whose FFN is the MoE of its lps_moe_desc;
+    the stages and boundaries are those of the dense decoder (lps_stage_forward,
+    lps_boundary_send / recv).  Decode takes one row per step; prefill takes a
+    chunk of rows through each stage's layers (the grouped-GEMM path) with a
+    [T, d] block per boundary."""
 
-    def __init__(self, model: dict, device="cuda:0"):
+    def __init__(self, model: dict, fence=None, device="cuda:0", streams: str = "per-stage"):
         _need_gpu()
         self.cfg = cfg = model["cfg"]
         self.device = dev = torch.device(device)
@@ -500,45 +505,140 @@ class DeviceMoEStack:
             d.w_gu_s, d.w_d_s = ptr(t["w_gu_s"]), ptr(t["w_d_s"])
             self.layers.append(t)
             self.descs.append(d)
-        self.scratch_bytes = lps.lps_moe_layer_scratch_bytes(C.byref(self.descs[0]))
-        self.scratch = torch.zeros(self.scratch_bytes, dtype=torch.uint8, device=dev)
-        self.x = torch.zeros(cfg.d, dtype=torch.float32, device=dev)
-        self.stream = torch.cuda.Stream(device=dev)
+        ld = (lps.LayerDesc * cfg.n_layers)()
+        for l, d in enumerate(self.descs):
+            ld[l].d, ld[l].nq, ld[l].wdtype, ld[l].eps = cfg.d, 0, lps.LPS_BF16, cfg.eps
+            ld[l].ffn_kind, ld[l].moe = lps.LPS_FFN_MOE, C.addressof(d)
+        h = C.c_void_p()
+        lps.lps_model_create(ld, cfg.n_layers, C.byref(h))
+        self.model = h
+        self.scratch_bytes = lps.lps_model_scratch_bytes(h)
+        self.stream = torch.cuda.Stream(device=dev)     # the unstaged prefill's main stream
+        self._streams_mode = streams
+        self.bounds, self._pf_bounds = [], []
+        self._pf_scratch = None
+        self.set_fence(fence)
 
-    def decode_step(self, x_ptr_in: int, out_ptr: int):
-        cfg, st = self.cfg, sp(self.stream)
-        lps.lps_copy_f32(x_ptr_in, ptr(self.x), cfg.d, st)
-        for d in self.descs:
-            lps.lps_moe_layer_decode(C.byref(d), ptr(self.x), ptr(self.scratch), self.scratch_bytes, st)
-        lps.lps_copy_f32(ptr(self.x), out_ptr, cfg.d, st)
-
-    def prefill(self, X: np.ndarray, n_pieces: int = 8, remote_stream=None) -> np.ndarray:
-        """All layers over a chunk of T rows (the grouped-GEMM path); returns
-        the output rows [T, d]."""
+    def set_fence(self, fence=None):
         cfg, dev = self.cfg, self.device
-        T = X.shape[0]
-        x = to_dev(np.ascontiguousarray(X, dtype=np.float32), dev)
-        sb = lps.lps_moe_prefill_scratch_bytes(C.byref(self.descs[0]), T)
-        if getattr(self, "_pf_scratch", None) is None or self._pf_scratch.numel() < sb:
-            self._pf_scratch = torch.empty(sb, dtype=torch.uint8, device=dev)
-        rs = remote_stream or torch.cuda.Stream(device=dev)
+        fence = list(fence) if fence is not None else lps.stage_plan(cfg.n_layers, 1)
+        if lps.stage_plan(cfg.n_layers, len(fence) - 1, fence[1:-1]) != fence:
+            raise lps.LpsError(lps.LPS_EINVAL, f"fence {fence} is not a plan of {cfg.n_layers} layers")
+        self.fence, self.n_stages = fence, len(fence) - 1
+        n = self.n_stages
+        self._fence_c = lps.i32_array(fence)
+        if self._streams_mode == "single":
+            self.streams = [torch.cuda.Stream(device=dev)] * n
+        else:
+            self.streams = [torch.cuda.Stream(device=dev) for _ in range(n)]
+        self.x = [torch.zeros(cfg.d, dtype=torch.float32, device=dev) for _ in range(n)]
+        self.scratch = [torch.zeros(self.scratch_bytes, dtype=torch.uint8, device=dev)
+                        for _ in range(n)]
+        self._close_boundaries()
+        self.slots = []
+        for _ in range(n - 1):
+            s0 = torch.full((cfg.d,), float("nan"), dtype=torch.float32, device=dev)
+            s1 = torch.full((cfg.d,), float("nan"), dtype=torch.float32, device=dev)
+            b = C.c_void_p()
+            lps.lps_boundary_create(cfg.d, ptr(s0), ptr(s1), C.byref(b))
+            self.slots.append((s0, s1))
+            self.bounds.append(b)
+        self.step_no = 0
         torch.cuda.synchronize(dev)
-        self.prefill_dev(x, T, n_pieces, rs)
-        torch.cuda.synchronize(dev)
-        return x.cpu().numpy()
 
-    def prefill_dev(self, x, T, n_pieces, remote_stream):
-        """Enqueue the layers over device rows x [T, d] (in place)."""
-        for d in self.descs:
-            lps.lps_moe_prefill(C.byref(d), ptr(x), T, n_pieces, ptr(self._pf_scratch),
-                                self._pf_scratch.numel(), sp(self.stream), sp(remote_stream))
+    def _close_boundaries(self):
+        for b in self.bounds + self._pf_bounds:
+            lps.lps_boundary_destroy(b)
+        self.bounds, self._pf_bounds, self._pf_key = [], [], None
+
+    def close(self):
+        torch.cuda.synchronize(self.device)
+        self._close_boundaries()
+        if getattr(self, "model", None):
+            lps.lps_model_destroy(self.model)
+            self.model = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _walk(self):
+        n, st, t = self.n_stages, self.streams, self.step_no
+        for s in range(n):
+            if s > 0:
+                lps.lps_boundary_send(self.bounds[s - 1], ptr(self.x[s - 1]), t, sp(st[s - 1]))
+                lps.lps_boundary_recv(self.bounds[s - 1], ptr(self.x[s]), t, sp(st[s]))
+            lps.lps_stage_forward(self.model, self._fence_c, n, s, ptr(self.x[s]), 0,
+                                  ptr(self.scratch[s]), self.scratch_bytes, sp(st[s]))
+        self.step_no += 1
 
     def decode(self, xs: np.ndarray) -> np.ndarray:
+        """Step t feeds the f32 row xs[t] and returns the last stage's rows [steps, d]."""
         cfg, dev = self.cfg, self.device
         xin = to_dev(np.ascontiguousarray(xs, dtype=np.float32), dev)
         out = torch.zeros_like(xin)
         torch.cuda.synchronize(dev)
+        st0, stl = self.streams[0], self.streams[-1]
         for t in range(xs.shape[0]):
-            self.decode_step(ptr(xin) + 4 * cfg.d * t, ptr(out) + 4 * cfg.d * t)
+            lps.lps_copy_f32(ptr(xin) + 4 * cfg.d * t, ptr(self.x[0]), cfg.d, sp(st0))
+            self._walk()
+            lps.lps_copy_f32(ptr(self.x[-1]), ptr(out) + 4 * cfg.d * t, cfg.d, sp(stl))
         torch.cuda.synchronize(dev)
         return out.cpu().numpy()
+
+    def _prefill_scratch(self, T):
+        sb = lps.lps_moe_prefill_scratch_bytes(C.byref(self.descs[0]), T)
+        if self._pf_scratch is None or self._pf_scratch.numel() < sb:
+            self._pf_scratch = torch.empty(sb, dtype=torch.uint8, device=self.device)
+
+    def prefill(self, X: np.ndarray, n_pieces: int = 8, remote_stream=None) -> np.ndarray:
+        """All layers over a chunk of T rows (the grouped-GEMM path), stage by stage
+        with a [T, d] block through each boundary; returns the output rows [T, d]."""
+        cfg, dev, n = self.cfg, self.device, self.n_stages
+        T = X.shape[0]
+        xs = [to_dev(np.ascontiguousarray(X, dtype=np.float32), dev)]
+        xs += [torch.empty((T, cfg.d), dtype=torch.float32, device=dev) for _ in range(n - 1)]
+        self._prefill_scratch(T)
+        if n == 1:
+            rs = remote_stream or torch.cuda.Stream(device=dev)
+            torch.cuda.synchronize(dev)
+            self.prefill_dev(xs[0], T, n_pieces, rs)
+            torch.cuda.synchronize(dev)
+            return xs[0].cpu().numpy()
+        key = (T, tuple(self.fence))
+        if self._pf_key != key:
+            for b in self._pf_bounds:
+                lps.lps_boundary_destroy(b)
+            self._pf_bounds, self._pf_slots = [], []
+            for _ in range(n - 1):
+                s0 = torch.empty((T, cfg.d), dtype=torch.float32, device=dev)
+                s1 = torch.empty_like(s0)
+                b = C.c_void_p()
+                lps.lps_boundary_create(T * cfg.d, ptr(s0), ptr(s1), C.byref(b))
+                self._pf_slots.append((s0, s1))
+                self._pf_bounds.append(b)
+            self._pf_key, self._pf_step = key, 0
+        # one scratch serves every stage: the stages run one after the other here
+        rs = remote_stream or torch.cuda.Stream(device=dev)
+        st = self.streams
+        torch.cuda.synchronize(dev)
+        k = self._pf_step
+        for s in range(n):
+            if s > 0:
+                lps.lps_boundary_send(self._pf_bounds[s - 1], ptr(xs[s - 1]), k, sp(st[s - 1]))
+                lps.lps_boundary_recv(self._pf_bounds[s - 1], ptr(xs[s]), k, sp(st[s]))
+            for l in range(self.fence[s], self.fence[s + 1]):
+                lps.lps_moe_prefill(C.byref(self.descs[l]), ptr(xs[s]), T, n_pieces,
+                                    ptr(self._pf_scratch), self._pf_scratch.numel(), sp(st[s]),
+                                    sp(rs))
+            torch.cuda.synchronize(dev)   # the shared scratch is free for the next stage
+        self._pf_step += 1
+        return xs[-1].cpu().numpy()
+
+    def prefill_dev(self, x, T, n_pieces, remote_stream):
+        """Enqueue every layer over device rows x [T, d] (in place) on self.stream."""
+        for d in self.descs:
+            lps.lps_moe_prefill(C.byref(d), ptr(x), T, n_pieces, ptr(self._pf_scratch),
+                                self._pf_scratch.numel(), sp(self.stream), sp(remote_stream))

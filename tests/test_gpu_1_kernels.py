@@ -555,3 +555,20 @@ def test_moe_route_parity(L, d, E):
         assert gaps.min() <= 2 * err_r[i].max(), (i, gi[i], oi[i])
         near += 1
     assert near <= 3
+    # the selection on the GPU's own router logits (left in the scratch, [T, E]
+    # f32) is exact: the oracle's top-k of the softmax of the same logits, ties to
+    # the lower id, every row, no exceptions; the weights to f32 rounding
+    glog = sc[:T * E * 4].view(torch.float32).reshape(T, E).cpu().numpy().astype(np.float64)
+    ei, ew = top_k(softmax(glog), 8)
+    assert np.array_equal(gi, ei)
+    assert np.max(np.abs(gw - ew)) <= 2e-6
+    # identical logits in a row: the lowest ids win (the tie rule), also on the GPU
+    desc2 = L.MoEDesc()
+    ctypes_fields = [f for f, _ in L.MoEDesc._fields_]
+    for f in ctypes_fields:
+        setattr(desc2, f, getattr(desc, f))
+    wz = torch.zeros_like(t["w_r"])                      # a zero router: every logit 0
+    desc2.w_r = ptr(wz)
+    L.lps_moe_route(C.byref(desc2), ptr(Xd), 4, ptr(idx), ptr(w), ptr(sc), sb, stream())
+    assert np.array_equal(idx.cpu().numpy()[:4], np.tile(np.arange(8, dtype=np.int32), (4, 1)))
+    assert np.allclose(w.cpu().numpy()[:4], 1 / 8, rtol=0, atol=1e-7)

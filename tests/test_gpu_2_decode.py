@@ -291,3 +291,28 @@ def test_moe_prefill_all_remote_or_all_local(rt, remote_from):
     tol = 2e-3 * np.abs(ref).max()
     err = np.abs(got8 - ref).max(axis=1)
     assert np.all(err <= tol), (int(np.argmax(err)), float(err.max()), tol)
+
+
+def test_moe_stack_stages_equal_one_stage_decode_and_prefill(rt):
+    """Every cut set of a 4-layer MoE stack, on per-stage streams: decode rows and a
+    ragged prefill chunk equal the one-stage run bit for bit, with the walks and
+    boundary crossings counted (the staged walk is not vacuous)."""
+    from layer_pipeline_stage_amd import lps
+    cfg = synth.MoEConfig("moe-stages", n_layers=4, d=512, n_experts=16, top_k=4, ff=128,
+                          remote_from=8, prefill_T=200, steps=5)
+    m = synth.make_moe(cfg)
+    st = rt.DeviceMoEStack(m)
+    ref = st.decode(m["x_in"])
+    ref_pf = st.prefill(m["x_prefill"], n_pieces=8)
+    for cuts in ([1], [2], [3], [1, 2], [1, 3], [2, 3], [1, 2, 3]):
+        fence = [0, *cuts, 4]
+        n = len(fence) - 1
+        st.set_fence(fence)
+        lps.lps_counters_reset()
+        got = st.decode(m["x_in"])
+        c = lps.counters()
+        assert c["stage_walks"] == n * cfg.steps and c["boundary_sends"] == (n - 1) * cfg.steps
+        assert np.array_equal(got, ref), fence
+        got_pf = st.prefill(m["x_prefill"], n_pieces=8)
+        assert np.array_equal(got_pf, ref_pf), fence
+    st.close()

@@ -98,12 +98,24 @@ def test_padded_mxfp4_staged(rt, pad_models):
 
 
 def test_moe_decode_full_size(rt):
+    """The MoE layer stack at its full size (4 layers, n_embd 2048, 64 experts top-8
+    + shared, ff 1024): N = 2 stages [0, 2, 4] through a boundary equal N = 1 bit
+    for bit, with the stage walks and boundary sends counted, and every step
+    matches the oracle."""
+    from layer_pipeline_stage_amd import lps
     cfg = replace(synth.MOE, steps=3, prefill_T=0)
     m = synth.make_moe(cfg)
     st = rt.DeviceMoEStack(m)
     got = st.decode(m["x_in"])
+    lps.lps_counters_reset()
+    st.set_fence([0, 2, 4])
+    got2 = st.decode(m["x_in"])
+    c = lps.counters()
+    assert c["stage_walks"] == 2 * cfg.steps and c["boundary_sends"] == cfg.steps
+    assert np.array_equal(got2, got)
+    st.close()
     ref_st = MoEStack(m)
-    for t in range(2):
+    for t in range(cfg.steps):
         ref = ref_st.forward(m["x_in"][t])
         tol = 2e-3 * np.abs(ref).max()
         assert np.max(np.abs(got[t] - ref)) <= tol, (t, np.max(np.abs(got[t] - ref)))
