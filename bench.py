@@ -158,20 +158,62 @@ def _timed(torch, fn):
     return time.perf_counter() - t0
 
 
-def pad_bench(torch, synth, lps, runtime, steps):
+def _kernel_times(lps, kind, cap, run):
+    """Durations (ms) of every launch of one kind during run(), HIP events on the
+    kernels' own stream."""
+    lps.lps_timer_start(kind, cap)
+    run()
+    return lps.timer_stop()
+
+
+def _roofline(bound, kernel, nbytes_or_flops, avg_us, peak, unit, traffic=None, **extra):
+    achieved = nbytes_or_flops / (avg_us * 1e-6) / (1e9 if unit == "GB/s" else 1e12)
+    out = {"bound": bound, "kernel": kernel, "achieved": round(achieved, 1), "peak": peak,
+           "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic,
+           "avg_us": round(avg_us, 2)}
+    out.update(extra)
+    return out
+
+
+def _cpu_info(dt, what):
+    from threadpoolctl import threadpool_info
+    cores = len(os.sched_getaffinity(0))
+    blas = [i.get("num_threads") for i in threadpool_info() if i.get("user_api") == "blas"]
+    return int(blas[0]) if blas else cores, (f"{what} (numpy float64, BLAS threads "
+                                             f"{blas[0] if blas else '?'} of {cores} host cores, "
+                                             f"{dt:.1f} s)")
+
+
+def mx_bytes(n, k):
+    """Bytes of an MXFP4 [n, k] matrix: k/2 code bytes and k/32 scale bytes per row."""
+    return n * k // 2 + n * k // 32
+
+
+PAD_KERNEL_BYTES = {
+    "qkv": lambda c, n: mx_bytes((c.nq + 2 * c.nkv) * c.hd, c.d) + 2 * c.d * 4 + c.nq * c.hd * 4
+    + 2 * c.nkv * c.hd * 2,
+    "attn": lambda c, n: 2 * c.nkv * n * c.hd * 2 + 2 * c.nq * c.hd * 4,
+    "oproj": lambda c, n: mx_bytes(c.d, c.nq * c.hd) + c.nq * c.hd * 4 + 2 * c.d * 4,
+    "gateup": lambda c, n: mx_bytes(2 * c.ff, c.d) + 2 * c.d * 4 + c.ff * 4,
+    "down": lambda c, n: mx_bytes(c.d, c.ff) + c.ff * 4 + 2 * c.d * 4,
+}
+
+
+def pad_bench(torch, synth, lps, runtime, steps, cpu=True):
     """Padded-head MXFP4 decode (4 layers, n_embd 5120, 36 q / 6 kv heads of 256 of
     which 12 q and 2 kv are zero dummies, ff 17472, context 8192): `steps` hidden
-    rows in and out, device-resident, one stage and two."""
+    rows in and out, device-resident, one stage and two; the gate/up GEMV's
+    roofline from a measured pass; the oracle on 4 steps."""
     cfg = replace(synth.PAD, steps=steps)
     model = synth.make_pad(cfg)
     xs = np.asarray(model["x_in"], np.float32)
     c = cfg
-    kvb = 2 * c.nkv * c.hd * 2
-    wb = lambda n, k: n * k // 2 + n * k // 32                     # noqa: E731
-    per_tok = c.n_layers * (wb((c.nq + 2 * c.nkv) * c.hd, c.d) + wb(c.d, c.nq * c.hd) +
-                            wb(2 * c.ff, c.d) + wb(c.d, c.ff)) + \
-        c.n_layers * kvb * (c.prefix + steps / 2)
-    out = {"metric": "decode tokens/s, padded-head MXFP4 model, 1 GPU", "unit": "tok/s",
+    per_tok = c.n_layers * (mx_bytes((c.nq + 2 * c.nkv) * c.hd, c.d) + mx_bytes(c.d, c.nq * c.hd) +
+                            mx_bytes(2 * c.ff, c.d) + mx_bytes(c.d, c.ff)) + \
+        c.n_layers * 2 * c.nkv * c.hd * 2 * (c.prefix + steps / 2)
+    out = {"metric": "decode tokens/s + achieved HBM GB/s (% of MI355X peak), 1 GPU",
+           "unit": "tok/s", "n_gpus": 1, "steps": steps, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None,
            "dtype": "mxfp4 weights, bf16 KV, f32 activations", "data": "synthetic",
            "hbm_bytes_per_token": int(per_tok), "rows": []}
     for fence in ([0, 4], [0, 2, 4]):
@@ -179,24 +221,58 @@ def pad_bench(torch, synth, lps, runtime, steps):
         dd.run_hidden(xs[:4])
         dd.reset()
         dt = _timed(torch, lambda: dd.run_hidden(xs)) / steps
+        if len(fence) == 2:
+            kernels = {}
+            rows = [c.prefix + 1 + i for i in range(steps)]
+            for name, kind in lps.KINDS.items():
+                if name == "head":
+                    continue
+                dd.reset()
+                ms = _kernel_times(lps, kind, 8 * steps + 8, lambda: dd.run_hidden(xs))
+                n_rows = np.repeat(rows, c.n_layers)[:len(ms)]
+                byts = np.array([PAD_KERNEL_BYTES[name](c, n) for n in n_rows], np.float64)
+                kernels[name] = {"launches": len(ms), "avg_us": round(1e3 * float(np.mean(ms)), 2),
+                                 "gbs": round(float(np.sum(byts) / (np.sum(ms) * 1e-3) / 1e9), 1)}
+            out["kernels"] = kernels
         dd.close()
         out["rows"].append({"stages": len(fence) - 1, "value": round(1 / dt, 1),
                             "us_per_token": round(1e6 * dt, 2),
                             "hbm_gbs": round(per_tok / dt / 1e9, 1),
                             "hbm_frac": round(per_tok / dt / 1e9 / HBM_PEAK_GBS, 4)})
     out["value"] = out["rows"][0]["value"]
+    out["ms_per_step"] = round(1e-3 * out["rows"][0]["us_per_token"], 4)
+    out["hbm_gbs"] = out["rows"][0]["hbm_gbs"]
+    out["hbm_frac"] = out["rows"][0]["hbm_frac"]
+    g = out["kernels"]["gateup"]
+    out["roofline"] = _roofline("hbm", "rmsnorm + MXFP4 gate/up GEMV + SwiGLU ([34944, 5120], "
+                                "e2m1 + e8m0 per 32)", PAD_KERNEL_BYTES["gateup"](c, 0),
+                                g["avg_us"], HBM_PEAK_GBS, "GB/s",
+                                bytes_per_launch=PAD_KERNEL_BYTES["gateup"](c, 0))
     out["config"] = {"workload": "padded-head MXFP4 decode: 4 layers, n_embd 5120, 36 q / 6 kv "
                                  "heads of 256 (12 q, 2 kv zero dummies), ff 17472, MXFP4 weights, "
                                  f"context 8192 + {steps} steps, hidden rows in and out "
                                  "(timed including the per-step row copies, excluding the "
-                                 "final host readback)"}
+                                 "final host readback), 1 stage (a 2-stage row beside it)"}
+    if cpu:
+        from oracle.decoder import Decoder
+        dec = Decoder(model, weight_cache=False)
+        n = 4
+        t0 = time.perf_counter()
+        for t in range(n):
+            dec.step(xs[t], c.prefix + t)
+        dt = time.perf_counter() - t0
+        cores, sample = _cpu_info(dt, f"{n} decode steps of the same padded model at context 8192")
+        out["cpu_baseline"] = {"value": round(n / dt, 4), "unit": "tok/s", "cores": cores,
+                               "kind": "oracle", "sample": sample}
     return out
 
 
-def moe_bench(torch, synth, lps, runtime, steps):
+def moe_bench(torch, synth, lps, runtime, steps, cpu=True):
     """The MoE layer stack (4 layers, n_embd 2048, 64 experts top-8 + 1 shared, ff
-    1024): batch-1 decode of `steps` rows, then the 16,384-token prefill chunk in 8
-    pieces (both halves of the piece transfer) — MFMA utilisation of the chunk."""
+    1024): batch-1 decode of `steps` rows (its expert gate/up GEMV's roofline),
+    then the 16,384-token prefill chunk in 8 pieces (both halves of the piece
+    transfer; MFMA utilisation of the chunk and of each grouped GEMM launch);
+    the oracle on 16 decode steps and a 1,024-token prefill slice."""
     cfg = replace(synth.MOE, steps=steps)
     model = synth.make_moe(cfg)
     st = runtime.DeviceMoEStack(model)
@@ -204,12 +280,20 @@ def moe_bench(torch, synth, lps, runtime, steps):
     st.decode(xs[:4])
     dt = _timed(torch, lambda: st.decode(xs)) / steps
     c = cfg
-    per_tok = c.n_layers * ((c.top_k + 1) * 3 * c.ff * c.d * 2 + c.n_experts * c.d * 2)
+    k1 = c.top_k + 1
+    per_tok = c.n_layers * (k1 * 3 * c.ff * c.d * 2 + c.n_experts * c.d * 2)
+    gu_bytes = k1 * 2 * c.ff * c.d * 2 + 2 * c.d * 4 + k1 * c.ff * 4
+    dn_bytes = k1 * c.d * c.ff * 2 + k1 * c.ff * 4 + k1 * c.d * 4
+    kernels = {}
+    for name, kind, nb in (("moe_gateup", 7, gu_bytes), ("moe_down", 8, dn_bytes)):
+        ms = _kernel_times(lps, kind, 8 * steps + 8, lambda: st.decode(xs))
+        avg = 1e3 * float(np.mean(ms))
+        kernels[name] = {"launches": len(ms), "avg_us": round(avg, 2),
+                         "gbs": round(nb / (avg * 1e-6) / 1e9, 1)}
     X = np.asarray(model["x_prefill"], np.float32)
     T = X.shape[0]
     xdev = runtime.to_dev(X, "cuda:0")
-    sb = lps.lps_moe_prefill_scratch_bytes(C.byref(st.descs[0]), T)
-    st._pf_scratch = torch.empty(sb, dtype=torch.uint8, device="cuda:0")
+    st._prefill_scratch(T)
     rs = torch.cuda.Stream()
     times = []
     for _ in range(3):
@@ -217,18 +301,63 @@ def moe_bench(torch, synth, lps, runtime, steps):
         times.append(_timed(torch, lambda: st.prefill_dev(x, T, 8, rs)))
     tp = min(times[1:])
     flop = 7.44e12 * T / 16384
-    return {"metric": "decode tokens/s, MoE layer stack, 1 GPU", "value": round(1 / dt, 1),
-            "unit": "tok/s", "us_per_token": round(1e6 * dt, 2),
-            "hbm_bytes_per_token": int(per_tok), "hbm_gbs": round(per_tok / dt / 1e9, 1),
-            "hbm_frac": round(per_tok / dt / 1e9 / HBM_PEAK_GBS, 4),
-            "prefill": {"tokens": T, "ms": round(1e3 * tp, 3), "tok_s": round(T / tp, 1),
-                        "tflops": round(flop / tp / 1e12, 1),
-                        "mfma_frac": round(flop / tp / 1e12 / 2500.0, 4), "pieces": 8},
-            "dtype": "bf16", "data": "synthetic",
-            "config": {"workload": "MoE layer stack: 4 layers, n_embd 2048, 64 experts top-8 "
-                                   "+ 1 shared, ff 1024, bf16; decode rows device-resident; "
-                                   "prefill chunk 16,384 tokens, FP16 sums and bf16 "
-                                   "activations in 8 pieces on a second stream"}}
+    # per launch, on one stream (the halves one after the other): algorithmic flops
+    # of each grouped GEMM over its launch time
+    g1 = _kernel_times(lps, 9, 64, lambda: st.prefill_dev(xdev.clone(), T, 8, st.stream))
+    g2 = _kernel_times(lps, 10, 64, lambda: st.prefill_dev(xdev.clone(), T, 8, st.stream))
+    gemm_flop = {"moe_gemm1": 2.0 * (T * c.top_k + T) * 2 * c.ff * c.d,
+                 "moe_gemm2": 2.0 * (T * c.top_k + T) * c.ff * c.d}
+    for name, ms in (("moe_gemm1", g1), ("moe_gemm2", g2)):
+        # 2 launches per layer (remote half, then local + shared): their durations
+        # summed per layer carry the layer's flops
+        per_layer = [ms[i] + ms[i + 1] for i in range(0, len(ms) - 1, 2)]
+        avg = 1e3 * float(np.mean(per_layer))
+        kernels[name] = {"launches": len(ms), "avg_us_per_layer": round(avg, 2),
+                         "tflops": round(gemm_flop[name] / (avg * 1e-6) / 1e12, 1),
+                         "mfma_frac": round(gemm_flop[name] / (avg * 1e-6) / 1e12 / 2500.0, 4)}
+    out = {"metric": "decode tokens/s + achieved HBM GB/s (% of MI355X peak), 1 GPU",
+           "value": round(1 / dt, 1), "unit": "tok/s", "n_gpus": 1, "steps": steps,
+           "ms_per_step": round(1e3 * dt, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "us_per_token": round(1e6 * dt, 2),
+           "hbm_bytes_per_token": int(per_tok), "hbm_gbs": round(per_tok / dt / 1e9, 1),
+           "hbm_frac": round(per_tok / dt / 1e9 / HBM_PEAK_GBS, 4),
+           "roofline": _roofline("hbm", "rmsnorm + gate/up GEMV + SwiGLU of the 8 selected "
+                                 "experts and the shared one (9 x [2048, 2048] bf16)", gu_bytes,
+                                 kernels["moe_gateup"]["avg_us"], HBM_PEAK_GBS, "GB/s",
+                                 bytes_per_launch=gu_bytes),
+           "kernels": kernels,
+           "prefill": {"tokens": T, "ms": round(1e3 * tp, 3), "tok_s": round(T / tp, 1),
+                       "tflops": round(flop / tp / 1e12, 1),
+                       "mfma_frac": round(flop / tp / 1e12 / 2500.0, 4), "pieces": 8,
+                       "roofline": {"bound": "mfma", "kernel": "the whole chunk (grouped GEMMs, "
+                                    "router, grouping, halves, combine)",
+                                    "achieved": round(flop / tp / 1e12, 1), "peak": 2500.0,
+                                    "unit": "TFLOP/s", "frac": round(flop / tp / 1e12 / 2500.0, 4),
+                                    "traffic": None}},
+           "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "MoE layer stack: 4 layers, n_embd 2048, 64 experts top-8 "
+                                  "+ 1 shared, ff 1024, bf16; decode rows device-resident; "
+                                  "prefill chunk 16,384 tokens, FP16 sums and bf16 "
+                                  "activations in 8 pieces on a second stream"}}
+    st.close()
+    if cpu:
+        from oracle.moe import MoEStack
+        ref = MoEStack(model)
+        n = 16
+        t0 = time.perf_counter()
+        for t in range(n):
+            ref.forward(xs[t % len(xs)])
+        dt_dec = time.perf_counter() - t0
+        Tp = 1024
+        t0 = time.perf_counter()
+        ref.forward(X[:Tp], prefill=True, n_pieces=8)
+        dt_pf = time.perf_counter() - t0
+        cores, sample = _cpu_info(dt_dec + dt_pf, f"{n} decode steps and a {Tp}-token prefill "
+                                  "slice of the same MoE stack")
+        out["cpu_baseline"] = {"value": round(n / dt_dec, 4), "unit": "tok/s", "cores": cores,
+                               "kind": "oracle", "sample": sample,
+                               "prefill_tok_s": round(Tp / dt_pf, 1)}
+    return out
 
 
 def prefill_bench(torch, synth, lps, runtime, T, stages, streams, reps, chunk=None):
@@ -323,7 +452,8 @@ def main():
         return
     if a.config:
         fn = moe_bench if a.config == "moe" else pad_bench
-        print(json.dumps(fn(torch, synth, lps, runtime, max(8, a.steps))), flush=True)
+        print(json.dumps(fn(torch, synth, lps, runtime, max(8, a.steps), cpu=not a.no_cpu)),
+              flush=True)
         return
     if a.prefill_only:
         print(json.dumps(prefill_bench(torch, synth, lps, runtime, a.prefill_only, a.stages,

@@ -492,7 +492,8 @@ int lps_counters_reset(void);
 
 /* ---- kernel timing (benchmarks) -------------------------------------------
  * While a timer runs, every launch of the chosen kind made by lps_layer_forward,
- * lps_stage_forward or lps_head_forward carries a pair of hipEvents that the
+ * lps_stage_forward, lps_head_forward, lps_moe_layer_decode or lps_moe_prefill
+ * carries a pair of hipEvents that the
  * dispatch itself stamps at its start and end (hipExtLaunchKernelGGL), so the
  * durations are those of the kernels on their stream, without launch gaps.
  * capacity bounds the pairs recorded (later launches are not timed).  One timer
@@ -503,7 +504,11 @@ enum {
   LPS_KIND_OPROJ = 3,   /* O projection + residual */
   LPS_KIND_GATEUP = 4,  /* RMSNorm + gate/up GEMV + SwiGLU */
   LPS_KIND_DOWN = 5,    /* down projection + residual */
-  LPS_KIND_HEAD = 6     /* final RMSNorm + LM head + argmax */
+  LPS_KIND_HEAD = 6,    /* final RMSNorm + LM head + argmax */
+  LPS_KIND_MOE_GU = 7,  /* MoE decode: RMSNorm + the selected and shared experts' gate/up + SwiGLU */
+  LPS_KIND_MOE_DOWN = 8,   /* MoE decode: every slot's down projection */
+  LPS_KIND_MOE_GEMM1 = 9,  /* MoE prefill: grouped gate/up GEMM + SwiGLU (each half's launch) */
+  LPS_KIND_MOE_GEMM2 = 10  /* MoE prefill: grouped down GEMM (each half's launch) */
 };
 int lps_timer_start(int32_t kind, int32_t capacity);
 /* Synchronizes the recorded events, writes up to cap durations (milliseconds)

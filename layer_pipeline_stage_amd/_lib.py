@@ -16,6 +16,7 @@ LPS_OK, LPS_EINVAL, LPS_ERANGE, LPS_ESTATE, LPS_EHIP, LPS_ENOMEM, LPS_EUNSUP = 0
 LPS_F32, LPS_BF16, LPS_MXFP4 = 0, 1, 2
 LPS_EPI_STORE, LPS_EPI_ADD, LPS_EPI_SWIGLU = 0, 1, 2
 KINDS = {"qkv": 1, "attn": 2, "oproj": 3, "gateup": 4, "down": 5, "head": 6}
+MOE_KINDS = {"moe_gateup": 7, "moe_down": 8, "moe_gemm1": 9, "moe_gemm2": 10}
 LPS_FFN_DENSE, LPS_FFN_MOE = 0, 1
 DTYPES = {"f32": LPS_F32, "bf16": LPS_BF16, "mxfp4": LPS_MXFP4}
 

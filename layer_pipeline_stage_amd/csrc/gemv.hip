@@ -490,7 +490,8 @@ int launch_gemv(int wdtype, const void* w, const uint8_t* s, int N, int K, const
 }
 
 int launch_moe_gu(const void* w_e, const void* w_s, const int32_t* eidx, int E, int kslots, int ff,
-                  int d, const float* x, const float* g, float eps, float* y, hipStream_t st) {
+                  int d, const float* x, const float* g, float eps, float* y, hipStream_t st,
+                  Stamp sp) {
   GemvP p{};
   p.w = static_cast<const uint8_t*>(w_e);
   p.w_s = static_cast<const uint8_t*>(w_s);
@@ -507,11 +508,11 @@ int launch_moe_gu(const void* w_e, const void* w_s, const int32_t* eidx, int E, 
   p.y = y;
   p.units = (kslots + 1) * ff;
   set_rows(p, LPS_BF16, d);
-  return launch_wt<EPI_MOEGU, true>(LPS_BF16, p, st, Stamp{});
+  return launch_wt<EPI_MOEGU, true>(LPS_BF16, p, st, sp);
 }
 
 int launch_moe_down(const void* w_e, const void* w_s, const int32_t* eidx, int E, int kslots,
-                    int d, int ff, const float* m, float* z, hipStream_t st) {
+                    int d, int ff, const float* m, float* z, hipStream_t st, Stamp sp) {
   GemvP p{};
   p.w = static_cast<const uint8_t*>(w_e);
   p.w_s = static_cast<const uint8_t*>(w_s);
@@ -526,7 +527,7 @@ int launch_moe_down(const void* w_e, const void* w_s, const int32_t* eidx, int E
   p.y = z;
   p.units = (kslots + 1) * (d / 2);
   set_rows(p, LPS_BF16, ff);
-  return launch_wt<EPI_MOEDN, false>(LPS_BF16, p, st, Stamp{});
+  return launch_wt<EPI_MOEDN, false>(LPS_BF16, p, st, sp);
 }
 
 // cos, sin of pos * theta_i, theta_i = base^(-2i / hd), formed in double and

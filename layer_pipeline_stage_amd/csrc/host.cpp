@@ -856,7 +856,8 @@ int lps_head_forward(const lps_head_desc* h, const float* x, float* logits, int3
 
 // ---- benchmark timer ----------------------------------------------------------------------
 int lps_timer_start(int32_t kind, int32_t capacity) {
-  LPS_REQUIRE(kind >= LPS_KIND_QKV && kind <= LPS_KIND_HEAD, LPS_EINVAL, "lps_timer_start: kind %d", kind);
+  LPS_REQUIRE(kind >= LPS_KIND_QKV && kind <= LPS_KIND_MOE_GEMM2, LPS_EINVAL, "lps_timer_start: kind %d",
+              kind);
   LPS_REQUIRE(capacity >= 1 && capacity <= 1 << 16, LPS_EINVAL, "lps_timer_start: capacity %d", capacity);
   std::lock_guard<std::mutex> lk(g_timer.mu);
   LPS_REQUIRE(g_timer.kind.load() == 0, LPS_ESTATE, "lps_timer_start: a timer is already running");

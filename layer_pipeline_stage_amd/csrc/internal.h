@@ -79,11 +79,11 @@ void rope_cos_sin(float base, int hd, int pos, int i, float* cs);
 // MoE decode gate/up + SwiGLU over the k selected experts (eidx, device) and the
 // shared one: y[(j, i)] = silu(gate) * up for slot j <= k, row i < ff
 int launch_moe_gu(const void* w_e, const void* w_s, const int32_t* eidx, int E, int kslots, int ff,
-                  int d, const float* x, const float* g, float eps, float* y, hipStream_t st);
+                  int d, const float* x, const float* g, float eps, float* y, hipStream_t st, Stamp sp = {});
 // MoE decode down projections: z[j * d + r] = W_j[r, :] . m[j, :] for slot j <= k
 // (k selected experts by eidx, then the shared one); d even
 int launch_moe_down(const void* w_e, const void* w_s, const int32_t* eidx, int E, int kslots,
-                    int d, int ff, const float* m, float* z, hipStream_t st);
+                    int d, int ff, const float* m, float* z, hipStream_t st, Stamp sp = {});
 int launch_head(const lps_head_desc* h, const float* x, float* logits, int32_t* tok,
                 void* scratch, size_t bytes, hipStream_t st, Stamp sp = {});
 size_t head_scratch(const lps_head_desc* h);

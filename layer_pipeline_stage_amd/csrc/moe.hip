@@ -282,10 +282,11 @@ int moe_decode(const lps_moe_desc* m, float* x, void* scratch, hipStream_t st) {
   int rc = launch_route(m, x, 1, reinterpret_cast<float*>(sc + s.logits), idx, wts, st);
   if (rc) return rc;
   rc = launch_moe_gu(m->w_gu_e, m->w_gu_s, idx, m->n_experts, m->top_k, m->ff, m->d, x, m->g_ffn,
-                     m->eps, mbuf, st);
+                     m->eps, mbuf, st, timer_take(LPS_KIND_MOE_GU));
   if (rc) return rc;
   float* z = reinterpret_cast<float*>(sc + s.z);
-  rc = launch_moe_down(m->w_d_e, m->w_d_s, idx, m->n_experts, m->top_k, m->d, m->ff, mbuf, z, st);
+  rc = launch_moe_down(m->w_d_e, m->w_d_s, idx, m->n_experts, m->top_k, m->d, m->ff, mbuf, z, st,
+                       timer_take(LPS_KIND_MOE_DOWN));
   if (rc) return rc;
   MoeCombP cp{};
   cp.idx = idx;

@@ -822,19 +822,21 @@ extern "C" int lps_moe_prefill(const lps_moe_desc* m, float* x, int32_t T, int32
     pr.xb = xr;
     pr.tiles = p.tiles_r;
     pr.n_tiles = p.n_tiles_r;
-    hipLaunchKernelGGL(k_pf_gemm<true>, dim3(m->ff / (GBN / 2), s.max_tiles), dim3(GEMM_THREADS),
-                       glds, sr, pr);
-    hipLaunchKernelGGL(k_pf_gemm<false>, dim3(m->d / GBN, s.max_tiles), dim3(GEMM_THREADS), glds2,
-                       sr, pr);
+    Stamp t1 = timer_take(LPS_KIND_MOE_GEMM1), t2 = timer_take(LPS_KIND_MOE_GEMM2);
+    LPS_LAUNCH(k_pf_gemm<true>, dim3(m->ff / (GBN / 2), s.max_tiles), dim3(GEMM_THREADS), glds, sr,
+               t1.start, t1.stop, pr);
+    LPS_LAUNCH(k_pf_gemm<false>, dim3(m->d / GBN, s.max_tiles), dim3(GEMM_THREADS), glds2, sr,
+               t2.start, t2.stop, pr);
     e = hipGetLastError();
   }
   if (e == hipSuccess && !rc) e = hipEventRecord(ev[2], sr);
   // local experts and the shared one on the main stream
   if (e == hipSuccess && !rc) {
-    hipLaunchKernelGGL(k_pf_gemm<true>, dim3(m->ff / (GBN / 2), s.max_tiles), dim3(GEMM_THREADS),
-                       glds, st, p);
-    hipLaunchKernelGGL(k_pf_gemm<false>, dim3(m->d / GBN, s.max_tiles), dim3(GEMM_THREADS), glds2,
-                       st, p);
+    Stamp t1 = timer_take(LPS_KIND_MOE_GEMM1), t2 = timer_take(LPS_KIND_MOE_GEMM2);
+    LPS_LAUNCH(k_pf_gemm<true>, dim3(m->ff / (GBN / 2), s.max_tiles), dim3(GEMM_THREADS), glds, st,
+               t1.start, t1.stop, p);
+    LPS_LAUNCH(k_pf_gemm<false>, dim3(m->d / GBN, s.max_tiles), dim3(GEMM_THREADS), glds2, st,
+               t2.start, t2.stop, p);
     e = hipGetLastError();
   }
   if (e == hipSuccess && !rc) e = hipStreamWaitEvent(st, ev[2], 0);
