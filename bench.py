@@ -55,11 +55,11 @@ def algorithmic_bytes(cfg, n_rows: int) -> dict:
 
 
 # HBM traffic of the gate/up GEMV measured by rocprofv3 PMC counters (FETCH_SIZE,
-# WRITE_SIZE, KiB per dispatch) on `python bench.py --no-cpu --mode eager --steps 16 --warmup 2`,
+# WRITE_SIZE, KiB per dispatch) on `python bench.py --no-cpu --mode eager --steps 8 --warmup 2`,
 # scaled by what the same counters read for the 256 MiB calibration copy
 # (`python bench.py --copy-calibration`: FETCH x 2.0, WRITE x 1.0).  Valid only for
 # the kernel sources it was taken on (hash below); otherwise reported as null.
-GATEUP_TRAFFIC = {"src_sha256_16": "494cc801f6a59c4d", "fetch_kib": 114863.64, "write_kib": 112.03,
+GATEUP_TRAFFIC = {"src_sha256_16": "b44027b551511e72", "fetch_kib": 114863.5, "write_kib": 112.0,
                   "fetch_scale": 2.0, "write_scale": 1.0}
 GEMV_SOURCES = ("layer_pipeline_stage_amd/csrc/gemv.hip", "layer_pipeline_stage_amd/csrc/gemv_core.h",
                 "layer_pipeline_stage_amd/csrc/dev.h")
