@@ -220,7 +220,15 @@ def pad_bench(torch, synth, lps, runtime, steps, cpu=True):
         dd = runtime.DeviceDecoder(model, fence=fence, streams="single")
         dd.run_hidden(xs[:4])
         dd.reset()
-        dt = _timed(torch, lambda: dd.run_hidden(xs)) / steps
+        dt_eager = _timed(torch, lambda: dd.run_hidden(xs)) / steps
+        dd.reset()
+        dd.run_hidden_graph(xs[:4])
+        dd.reset()
+        clock = {}
+        dd.run_hidden_graph(xs, timer=lambda start: clock.__setitem__("t0" if start else "t1",
+                                                                        time.perf_counter()))
+        dt_graph = (clock["t1"] - clock["t0"]) / steps
+        dt = dt_eager        # the faster launch form here: the step is kernel-bound
         if len(fence) == 2:
             kernels = {}
             rows = [c.prefix + 1 + i for i in range(steps)]
@@ -238,7 +246,8 @@ def pad_bench(torch, synth, lps, runtime, steps, cpu=True):
         out["rows"].append({"stages": len(fence) - 1, "value": round(1 / dt, 1),
                             "us_per_token": round(1e6 * dt, 2),
                             "hbm_gbs": round(per_tok / dt / 1e9, 1),
-                            "hbm_frac": round(per_tok / dt / 1e9 / HBM_PEAK_GBS, 4)})
+                            "hbm_frac": round(per_tok / dt / 1e9 / HBM_PEAK_GBS, 4),
+                            "graph_value": round(1 / dt_graph, 1)})
     out["value"] = out["rows"][0]["value"]
     out["ms_per_step"] = round(1e-3 * out["rows"][0]["us_per_token"], 4)
     out["hbm_gbs"] = out["rows"][0]["hbm_gbs"]
@@ -252,7 +261,10 @@ def pad_bench(torch, synth, lps, runtime, steps, cpu=True):
                                  "heads of 256 (12 q, 2 kv zero dummies), ff 17472, MXFP4 weights, "
                                  f"context 8192 + {steps} steps, hidden rows in and out "
                                  "(timed including the per-step row copies, excluding the "
-                                 "final host readback), 1 stage (a 2-stage row beside it)"}
+                                 "final host readback), eager launches (the whole step as one "
+                                 "replayed hipGraph beside it: graph_value), 1 stage (a 2-stage "
+                                 "row beside it)",
+                     "mode": "eager"}
     if cpu:
         from oracle.decoder import Decoder
         dec = Decoder(model, weight_cache=False)
@@ -278,7 +290,13 @@ def moe_bench(torch, synth, lps, runtime, steps, cpu=True):
     st = runtime.DeviceMoEStack(model)
     xs = np.asarray(model["x_in"], np.float32)
     st.decode(xs[:4])
-    dt = _timed(torch, lambda: st.decode(xs)) / steps
+    dt_eager = _timed(torch, lambda: st.decode(xs)) / steps
+    st.decode_graph(xs[:4])
+    clock = {}
+    st.decode_graph(xs, timer=lambda start: clock.__setitem__("t0" if start else "t1",
+                                                              time.perf_counter()))
+    dt_graph = (clock["t1"] - clock["t0"]) / steps
+    dt = dt_eager            # the faster launch form here: the step is kernel-bound
     c = cfg
     k1 = c.top_k + 1
     per_tok = c.n_layers * (k1 * 3 * c.ff * c.d * 2 + c.n_experts * c.d * 2)
@@ -319,6 +337,7 @@ def moe_bench(torch, synth, lps, runtime, steps, cpu=True):
            "value": round(1 / dt, 1), "unit": "tok/s", "n_gpus": 1, "steps": steps,
            "ms_per_step": round(1e3 * dt, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "us_per_token": round(1e6 * dt, 2),
+           "graph_value": round(1 / dt_graph, 1),
            "hbm_bytes_per_token": int(per_tok), "hbm_gbs": round(per_tok / dt / 1e9, 1),
            "hbm_frac": round(per_tok / dt / 1e9 / HBM_PEAK_GBS, 4),
            "roofline": _roofline("hbm", "rmsnorm + gate/up GEMV + SwiGLU of the 8 selected "
@@ -336,9 +355,11 @@ def moe_bench(torch, synth, lps, runtime, steps, cpu=True):
                                     "traffic": None}},
            "dtype": "bf16", "data": "synthetic",
            "config": {"workload": "MoE layer stack: 4 layers, n_embd 2048, 64 experts top-8 "
-                                  "+ 1 shared, ff 1024, bf16; decode rows device-resident; "
-                                  "prefill chunk 16,384 tokens, FP16 sums and bf16 "
-                                  "activations in 8 pieces on a second stream"}}
+                                  "+ 1 shared, ff 1024, bf16; decode rows device-resident, "
+                                  "eager launches (the whole step as one replayed hipGraph "
+                                  "beside it: graph_value); prefill chunk 16,384 tokens, FP16 "
+                                  "sums and bf16 activations in 8 pieces on a second stream",
+                      "mode": "eager"}}
     st.close()
     if cpu:
         from oracle.moe import MoEStack

@@ -242,7 +242,8 @@ int lps_stage_forward_dpos(const lps_model* m, const int32_t* fence, int32_t n_s
 int lps_rope_table(int32_t hd, float rope_base, int32_t n_pos, float* host_out);
 
 /* Advances a decode step's device state, on `stream`, after the head wrote
- * this step's argmax.  state (dev int32 [3]): [0] position, [1] step, [2] flags
+ * this step's argmax (models without a vocabulary pass argmax = tok_cur = NULL,
+ * n_feed 0 and no histories: only the position and the step advance).  state (dev int32 [3]): [0] position, [1] step, [2] flags
  * (bit 0: the position reached pos_limit - 1 and stayed there).  With s =
  * state[1]:
  *  - tok_hist[s] = *argmax when s < hist_cap (tok_hist dev, may be NULL when
@@ -257,6 +258,16 @@ int lps_rope_table(int32_t hd, float rope_base, int32_t n_pos, float* host_out);
 int lps_step_advance(int32_t* state, int32_t pos_limit, const int32_t* argmax, int32_t* tok_cur,
                      const int32_t* feed, int32_t n_feed, int32_t* tok_hist, int32_t hist_cap,
                      const float* logits, int32_t vocab, float* logits_hist, void* stream);
+
+/* The hidden-row input and output of a replayed step for models without a
+ * vocabulary: with s = state[1] (dev int32, the step of lps_step_advance)
+ * clamped into [0, n_rows - 1], dst[s * dst_stride + i] = src[s * src_stride + i]
+ * for i < n, on `stream` (all dev f32).  A stride of 0 pins that side: src rows
+ * [n_rows, src_stride] -> the stage-0 hidden (dst_stride 0) before the walk; the
+ * last stage's hidden (src_stride 0) -> output rows after it.  Errors: LPS_EINVAL
+ * for null pointers, n or n_rows < 1, or a nonzero stride below n. */
+int lps_row_at_step(const int32_t* state, const float* src, int64_t src_stride, float* dst,
+                    int64_t dst_stride, int32_t n, int32_t n_rows, void* stream);
 
 /* Whole-pass graph capture.  lps_graph_begin starts a relaxed-mode capture on
  * `stream` (not the null stream; LPS_ESTATE while a kernel timer runs or the

@@ -678,7 +678,11 @@ int lps_rope_table(int32_t hd, float rope_base, int32_t n_pos, float* host_out) 
 int lps_step_advance(int32_t* state, int32_t pos_limit, const int32_t* argmax, int32_t* tok_cur,
                      const int32_t* feed, int32_t n_feed, int32_t* tok_hist, int32_t hist_cap,
                      const float* logits, int32_t vocab, float* logits_hist, void* stream) {
-  LPS_REQUIRE(state && argmax && tok_cur, LPS_EINVAL, "lps_step_advance: null state, argmax or tok");
+  LPS_REQUIRE(state, LPS_EINVAL, "lps_step_advance: null state");
+  LPS_REQUIRE((argmax == nullptr) == (tok_cur == nullptr), LPS_EINVAL,
+              "lps_step_advance: argmax and tok_cur go together (both NULL: no token chain)");
+  LPS_REQUIRE(argmax || (n_feed == 0 && !tok_hist && !logits_hist), LPS_EINVAL,
+              "lps_step_advance: fed ids and histories need the token chain");
   LPS_REQUIRE(pos_limit >= 1, LPS_EINVAL, "lps_step_advance: pos_limit %d < 1", pos_limit);
   LPS_REQUIRE(n_feed >= 0 && (n_feed == 0 || feed), LPS_EINVAL,
               "lps_step_advance: %d fed ids need a feed array", n_feed);
@@ -688,6 +692,18 @@ int lps_step_advance(int32_t* state, int32_t pos_limit, const int32_t* argmax, i
               "lps_step_advance: a logits history needs logits and vocab > 0");
   return launch_step_advance(state, pos_limit, argmax, tok_cur, feed, n_feed, tok_hist, hist_cap,
                              logits, vocab, logits_hist, as_stream(stream));
+}
+
+int lps_row_at_step(const int32_t* state, const float* src, int64_t src_stride, float* dst,
+                    int64_t dst_stride, int32_t n, int32_t n_rows, void* stream) {
+  LPS_REQUIRE(state && src && dst, LPS_EINVAL, "lps_row_at_step: null state, src or dst");
+  LPS_REQUIRE(n >= 1 && n_rows >= 1, LPS_EINVAL, "lps_row_at_step: n %d and n_rows %d must be >= 1", n,
+              n_rows);
+  LPS_REQUIRE(src_stride >= 0 && dst_stride >= 0 && (src_stride == 0 || src_stride >= n) &&
+                  (dst_stride == 0 || dst_stride >= n),
+              LPS_EINVAL, "lps_row_at_step: strides %lld / %lld (0, or at least n %d)",
+              (long long)src_stride, (long long)dst_stride, n);
+  return launch_row_at_step(state, src, src_stride, dst, dst_stride, n, n_rows, as_stream(stream));
 }
 
 // ---- whole-pass graphs --------------------------------------------------------------------

@@ -164,10 +164,12 @@ __global__ void k_step_advance(int32_t* state, int pos_limit, const int32_t* arg
                                int32_t* tok_hist, int cap) {
   if (threadIdx.x != 0) return;
   const int s = state[1];
-  const int a = *argmax;
-  if (tok_hist && s >= 0 && s < cap) tok_hist[s] = a;
-  // the next step's input: the fed id while ids remain, else this step's argmax
-  *tok_cur = (s + 1 >= 0 && s + 1 < n_feed) ? feed[s + 1] : a;
+  if (argmax) {   // a model with a vocabulary: the token chain
+    const int a = *argmax;
+    if (tok_hist && s >= 0 && s < cap) tok_hist[s] = a;
+    // the next step's input: the fed id while ids remain, else this step's argmax
+    *tok_cur = (s + 1 >= 0 && s + 1 < n_feed) ? feed[s + 1] : a;
+  }
   const int pos = state[0];
   if (pos + 1 < pos_limit) state[0] = pos + 1;
   else state[2] = state[2] | 1;
@@ -184,6 +186,24 @@ int launch_step_advance(int32_t* state, int32_t pos_limit, const int32_t* argmax
   }
   hipLaunchKernelGGL(k_step_advance, dim3(1), dim3(64), 0, st, state, pos_limit, argmax, tok_cur,
                      feed, n_feed, tok_hist, hist_cap);
+  LPS_HIP(hipGetLastError());
+  return LPS_OK;
+}
+
+// dst[s * dst_stride + i] = src[s * src_stride + i], i < n, at the device step
+// s = state[1] clamped into [0, n_rows - 1] (a stride of 0 pins that side)
+__global__ void k_row_at_step(const int32_t* state, const float* src, long long src_stride,
+                              float* dst, long long dst_stride, int n, int n_rows) {
+  const int s = min(max(state[1], 0), n_rows - 1);
+  const float* a = src + (long long)s * src_stride;
+  float* b = dst + (long long)s * dst_stride;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) b[i] = a[i];
+}
+
+int launch_row_at_step(const int32_t* state, const float* src, int64_t src_stride, float* dst,
+                       int64_t dst_stride, int32_t n, int32_t n_rows, hipStream_t st) {
+  hipLaunchKernelGGL(k_row_at_step, grid_for(n), dim3(256), 0, st, state, src,
+                     (long long)src_stride, dst, (long long)dst_stride, n, n_rows);
   LPS_HIP(hipGetLastError());
   return LPS_OK;
 }

@@ -158,12 +158,12 @@ class DeviceDecoder:
             self.tok_ring = torch.zeros(ring, dtype=torch.int32, device=dev)
             self.host_logits = torch.zeros((ring, cfg.vocab), dtype=torch.float32).pin_memory()
             self.host_tok = torch.zeros(ring, dtype=torch.int32).pin_memory()
-            # device step state of the graph mode: [pos, step, flags], the next
-            # input id, this step's argmax and logits
-            self.g_state = torch.zeros(4, dtype=torch.int32, device=dev)
+            # the graph mode's next input id, this step's argmax and logits
             self.g_tok = torch.zeros(1, dtype=torch.int32, device=dev)
             self.g_arg = torch.zeros(1, dtype=torch.int32, device=dev)
             self.g_logits = torch.zeros(cfg.vocab, dtype=torch.float32, device=dev)
+        # device step state of the graph mode: [pos, step, flags]
+        self.g_state = torch.zeros(4, dtype=torch.int32, device=dev)
         self.readback = torch.cuda.Stream(device=dev)
         self._streams_mode = streams
         self.reset()
@@ -462,6 +462,49 @@ class DeviceDecoder:
         fed = ids[:P] + [toks[i - 1] for i in range(P, total)]
         return StepResult(fed=fed, argmax=toks, logits=lg)
 
+    def run_hidden_graph(self, xs: np.ndarray, p0=None, timer=None) -> np.ndarray:
+        """run_hidden with the whole step captured once and replayed: the input row
+        of step s (xs[s]) is copied in and the last stage's hidden copied out at the
+        device step, and the position advances on the device.  timer: an optional
+        callable run around the replays (for the bench)."""
+        cfg = self.cfg
+        p = cfg.prefix if p0 is None else p0
+        T = xs.shape[0]
+        assert T >= 1 and p + T <= cfg.ctx_max
+        dev = self.device
+        xin = to_dev(np.ascontiguousarray(xs, dtype=np.float32), dev)
+        out = torch.zeros((T, cfg.d), dtype=torch.float32, device=dev)
+        self.g_state.copy_(torch.tensor([p, 0, 0, 0], dtype=torch.int32))
+        st0, stl = self.streams[0], self.streams[-1]
+        torch.cuda.synchronize(dev)
+        lps.lps_graph_begin(sp(st0))
+        g = C.c_void_p()
+        try:
+            lps.lps_row_at_step(ptr(self.g_state), ptr(xin), cfg.d, ptr(self.x[0]), 0, cfg.d, T,
+                                sp(st0))
+            self._walk_dpos()
+            lps.lps_row_at_step(ptr(self.g_state), ptr(self.x[-1]), 0, ptr(out), cfg.d, cfg.d, T,
+                                sp(stl))
+            lps.lps_step_advance(ptr(self.g_state), cfg.ctx_max, None, None, None, 0, None, 0,
+                                 None, 0, None, sp(stl))
+        finally:
+            join = (C.c_void_p * len(self.streams))(*[sp(x) for x in self.streams])
+            lps.lps_graph_end(sp(st0), join, len(self.streams), C.byref(g))
+        try:
+            torch.cuda.synchronize(dev)
+            if timer is not None:
+                timer(True)
+            for _ in range(T):
+                lps.lps_graph_launch(g, sp(st0))
+            torch.cuda.synchronize(dev)
+            if timer is not None:
+                timer(False)
+        finally:
+            torch.cuda.synchronize(dev)
+            lps.lps_graph_destroy(g)
+        assert self.g_state.cpu().tolist()[1] == T
+        return out.cpu().numpy()
+
     def run_hidden(self, xs: np.ndarray, p0=None) -> np.ndarray:
         """Models without a vocabulary: step t feeds the f32 row xs[t] at position
         p0 + t and returns the last stage's hidden rows [steps, d]."""
@@ -514,6 +557,7 @@ class DeviceMoEStack:
         self.model = h
         self.scratch_bytes = lps.lps_model_scratch_bytes(h)
         self.stream = torch.cuda.Stream(device=dev)     # the unstaged prefill's main stream
+        self.g_state = torch.zeros(4, dtype=torch.int32, device=dev)   # [pos, step, flags]
         self._streams_mode = streams
         self.bounds, self._pf_bounds = [], []
         self._pf_scratch = None
@@ -586,6 +630,44 @@ class DeviceMoEStack:
             self._walk()
             lps.lps_copy_f32(ptr(self.x[-1]), ptr(out) + 4 * cfg.d * t, cfg.d, sp(stl))
         torch.cuda.synchronize(dev)
+        return out.cpu().numpy()
+
+    def decode_graph(self, xs: np.ndarray, timer=None) -> np.ndarray:
+        """decode with the whole step (row in, every stage and boundary, row out,
+        step advance) captured once and replayed once per row."""
+        cfg, dev = self.cfg, self.device
+        T = xs.shape[0]
+        xin = to_dev(np.ascontiguousarray(xs, dtype=np.float32), dev)
+        out = torch.zeros_like(xin)
+        self.g_state.zero_()
+        st0, stl = self.streams[0], self.streams[-1]
+        torch.cuda.synchronize(dev)
+        lps.lps_graph_begin(sp(st0))
+        g = C.c_void_p()
+        try:
+            lps.lps_row_at_step(ptr(self.g_state), ptr(xin), cfg.d, ptr(self.x[0]), 0, cfg.d, T,
+                                sp(st0))
+            self._walk()
+            lps.lps_row_at_step(ptr(self.g_state), ptr(self.x[-1]), 0, ptr(out), cfg.d, cfg.d, T,
+                                sp(stl))
+            lps.lps_step_advance(ptr(self.g_state), 1 << 30, None, None, None, 0, None, 0, None, 0,
+                                 None, sp(stl))
+        finally:
+            join = (C.c_void_p * len(self.streams))(*[sp(x) for x in self.streams])
+            lps.lps_graph_end(sp(st0), join, len(self.streams), C.byref(g))
+        try:
+            torch.cuda.synchronize(dev)
+            if timer is not None:
+                timer(True)
+            for _ in range(T):
+                lps.lps_graph_launch(g, sp(st0))
+            torch.cuda.synchronize(dev)
+            if timer is not None:
+                timer(False)
+        finally:
+            torch.cuda.synchronize(dev)
+            lps.lps_graph_destroy(g)
+        assert self.g_state.cpu().tolist()[1] == T
         return out.cpu().numpy()
 
     def _prefill_scratch(self, T):

@@ -94,8 +94,28 @@ def test_padded_mxfp4_staged(rt, pad_models):
     a.close()
     b = rt.DeviceDecoder(pm, fence=[0, 2, 4])
     rb = b.run_hidden(pm["x_in"])
+    # the whole step captured once and replayed (rows in and out at the device
+    # step, position advanced on the device): the same bits as the eager walk
+    b.reset()
+    rg = b.run_hidden_graph(pm["x_in"])
     b.close()
     assert np.array_equal(ra, rb)
+    assert np.array_equal(rg, rb)
+
+
+def test_moe_decode_graph_replay_equals_eager(rt):
+    """The MoE layer stack's decode captured as one graph per step (row in, each
+    stage and boundary, row out, step advance) and replayed: bit-identical to the
+    eager walk, on one stage and on two with per-stage streams."""
+    cfg = replace(synth.MOE, steps=4, prefill_T=0)
+    m = synth.make_moe(cfg)
+    st = rt.DeviceMoEStack(m)
+    ref = st.decode(m["x_in"])
+    assert np.array_equal(st.decode_graph(m["x_in"]), ref)
+    st.set_fence([0, 2, 4])
+    assert np.array_equal(st.decode_graph(m["x_in"]), ref)
+    assert np.array_equal(st.decode(m["x_in"]), ref)      # eager again after the replays
+    st.close()
 
 
 def test_moe_decode_full_size(rt):
