@@ -10,7 +10,8 @@ import ctypes as C
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liblps.so")
+# LPS_LIB_PATH selects another build of the same library (the host-sanitizer build)
+LIB_PATH = os.environ.get("LPS_LIB_PATH") or os.path.join(_HERE, "liblps.so")
 
 LPS_OK, LPS_EINVAL, LPS_ERANGE, LPS_ESTATE, LPS_EHIP, LPS_ENOMEM, LPS_EUNSUP = 0, -1, -2, -3, -4, -5, -6
 LPS_F32, LPS_BF16, LPS_MXFP4 = 0, 1, 2

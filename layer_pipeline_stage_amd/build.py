@@ -33,19 +33,41 @@ FLAGS = [
 ]
 
 
+# Host-only sanitizers (AddressSanitizer + UndefinedBehaviorSanitizer) for the
+# library's CPU paths: each -fsanitize= applies to the host pass alone; the device
+# code is built as usual.  The result is loaded with the ASan runtime preloaded.
+SAN_FLAGS = [
+    "-O1", "-g", "-fno-omit-frame-pointer", "-shared-libsan",
+    "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+]
+SAN_BUILD = os.path.join(PKG, "_build_san")
+SAN_OUT = os.path.join(SAN_BUILD, "liblps_san.so")
+
+
+def asan_runtime() -> str:
+    """The clang ASan runtime that a sanitized liblps needs preloaded."""
+    import glob
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not hits:
+        raise RuntimeError("the clang ASan runtime is not installed under /opt/rocm/llvm")
+    return hits[-1]
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
                   if f.endswith((".hip", ".cpp")))
 
 
-def build(jobs: int | None = None, verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int | None = None, verbose: bool = False, sanitize: bool = False) -> str:
+    out_dir, out = (SAN_BUILD, SAN_OUT) if sanitize else (BUILD, OUT)
+    os.makedirs(out_dir, exist_ok=True)
     cc = hipcc()
     srcs = sources()
+    flags = [f for f in FLAGS if f != "-O3"] + SAN_FLAGS if sanitize else FLAGS
 
     def compile_one(src):
-        obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-        cmd = [cc, *FLAGS, "-c", src, "-o", obj]
+        obj = os.path.join(out_dir, os.path.basename(src) + ".o")
+        cmd = [cc, *flags, "-c", src, "-o", obj]
         if src.endswith(".cpp"):
             cmd[1:1] = ["-x", "hip"]
         r = subprocess.run(cmd, capture_output=True, text=True)
@@ -59,18 +81,22 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
 
     with ThreadPoolExecutor(jobs or min(8, os.cpu_count() or 1)) as ex:
         objs = list(ex.map(compile_one, srcs))
-    tmp = OUT + ".tmp"
-    r = subprocess.run([cc, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs],
-                       capture_output=True, text=True)
+    tmp = out + ".tmp"
+    link = [cc, "-shared", f"--offload-arch={ARCH}"]
+    if sanitize:
+        link += ["-shared-libsan", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined"]
+    r = subprocess.run([*link, "-o", tmp, *objs], capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, OUT)
-    return OUT
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=None)
     ap.add_argument("-v", "--verbose", action="store_true")
+    ap.add_argument("--sanitize", action="store_true",
+                    help="build _build_san/liblps_san.so with host ASan + UBSan")
     a = ap.parse_args()
-    print(build(a.jobs, a.verbose))
+    print(build(a.jobs, a.verbose, a.sanitize))

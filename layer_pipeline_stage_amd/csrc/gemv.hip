@@ -290,7 +290,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const uint8_t* base, 
     if (nu != u) {                                                 \
       int r0, r1;                                                  \
       unit_rows<EPI>(p, u, r0, r1);                                \
-      finish<EPI>(p, u, r0, r1, a0, a1, CY0, CY1, lane, best, bidx); \
+      finish<EPI>(p, u, r0, r1, a0 * xback, a1 * xback, CY0, CY1, lane, best, bidx); \
       a0 = a1 = 0.f;                                               \
     }                                                              \
     if (!more) break;                                              \
@@ -300,7 +300,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const uint8_t* base, 
 
 template <int WT, int EPI, int U, bool NORM, int NT, bool DB>
 __global__ __launch_bounds__(NT) void k_gemv_buf(GemvP p) {
-  extern __shared__ float xs[];
+  extern __shared__ __attribute__((aligned(16))) float xs[];
   constexpr int CH = Fmt<WT>::CH;
   constexpr int XS = WT == LPS_MXFP4 ? MX16_XS : CH;   // staged floats (MXFP4: halves) per chunk
   _Float16* const xh = reinterpret_cast<_Float16*>(xs);   // the MXFP4 staging (f16)
@@ -319,8 +319,9 @@ __global__ __launch_bounds__(NT) void k_gemv_buf(GemvP p) {
   BUF_LOAD(va0, va1, sa0, sa1, ya0, ya1, u, 0, u < p.units)
   // a chunk past the row end (zero weights) reads the zero chunk after the staged vector
   const int zoff = WT == LPS_MXFP4 ? nck * XS : p.K;
+  float xback = 1.f;   // MXFP4: the power of two the staged vector was scaled down by
   if constexpr (WT == LPS_MXFP4) {
-    stage_x_mx16<NORM, NT, mx16_maxr(U, NT)>(p.x, p.g, p.eps, p.K, xh);
+    xback = stage_x_mx16<NORM, NT, mx16_maxr(U, NT)>(p.x, p.g, p.eps, p.K, xh);
   } else {
     if (threadIdx.x < CH) xs[zoff + threadIdx.x] = 0.f;   // zero chunk
     // MoE down: a workgroup's units all belong to one slot (the launch gives every
@@ -347,7 +348,7 @@ __global__ __launch_bounds__(NT) void k_gemv_buf(GemvP p) {
         if (nu != u) {
           int r0, r1;
           unit_rows<EPI>(p, u, r0, r1);
-          finish<EPI>(p, u, r0, r1, a0, a1, ya0, ya1, lane, best, bidx);
+          finish<EPI>(p, u, r0, r1, a0 * xback, a1 * xback, ya0, ya1, lane, best, bidx);
           a0 = a1 = 0.f;
         }
         if (nu >= p.units) break;

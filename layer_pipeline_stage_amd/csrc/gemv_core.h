@@ -150,9 +150,14 @@ __device__ __forceinline__ void acc_chunk_mx16(const u32x4 v, uint32_t sb, const
 // Stage x as f16 chunks (see above); with NORM, as RMSNorm(x) * g computed in f32
 // (the same v * r * g order as stage_x) before the rounding.  K % 32 == 0 and
 // K / 4 <= MAXR * NT (the launch checks it).
+// Without NORM the vector's magnitude is not bounded (the attention output, the
+// SwiGLU output): when its largest |x| passes 2^15 the staged values are x * 2^-e,
+// e the smallest power that brings it to at most 2^15, so none rounds to an f16
+// infinity; the return value 2^e scales the products back (exact powers of two,
+// and 1 for every vector below 2^15, where the staging is unchanged).
 template <bool NORM, int NT, int MAXR>
-__device__ __forceinline__ void stage_x_mx16(const float* x, const float* g, float eps, int K,
-                                             _Float16* xs) {
+__device__ __forceinline__ float stage_x_mx16(const float* x, const float* g, float eps, int K,
+                                              _Float16* xs) {
   constexpr int NW = NT / WAVE;
   const int tid = threadIdx.x;
   const int ng = K / 4;
@@ -176,6 +181,16 @@ __device__ __forceinline__ void stage_x_mx16(const float* x, const float* g, flo
     for (int i = 0; i < NW; ++i) tot += red[i];
     r = 1.0f / sqrtf(tot / float(K) + eps);
   }
+  // without NORM each wave records its largest |x| (read after the staging barrier)
+  __shared__ float mx[NW];
+  if (!NORM) {
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXR; ++i)
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+    m = wave_max(m);
+    if ((tid & (WAVE - 1)) == 0) mx[tid / WAVE] = m;
+  }
 #pragma unroll
   for (int i = 0; i < MAXR; ++i) {
     const int G = tid + i * NT;
@@ -196,6 +211,27 @@ __device__ __forceinline__ void stage_x_mx16(const float* x, const float* g, flo
   }
   if (tid < 16) *reinterpret_cast<h2*>(xs + (K / 32) * MX16_XS + 2 * tid) = h2{0, 0};   // zero chunk
   __syncthreads();
+  float back = 1.f;
+  if (!NORM) {
+    float am = 0.f;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) am = fmaxf(am, mx[i]);
+    // the same value on every thread: the restaging below (x read again, scaled)
+    // is taken by the whole workgroup or by none of it
+    if (am > 32768.f && am <= 3.0e38f) {   // finite and past 2^15 (inf passes as is)
+      const int e = ilogbf(am) - 14;         // am * 2^-e < 2^15
+      const float sc = ldexpf(1.f, -e);
+      back = ldexpf(1.f, e);
+      for (int G = tid; G < ng; G += NT) {
+        const f32x4 y = *reinterpret_cast<const f32x4*>(x + 4 * G);
+        _Float16* dst = xs + (G >> 3) * MX16_XS + 4 * (G & 7);
+        *reinterpret_cast<h2*>(dst) = h2{(_Float16)(y.x * sc), (_Float16)(y.y * sc)};
+        *reinterpret_cast<h2*>(dst + 2) = h2{(_Float16)(y.z * sc), (_Float16)(y.w * sc)};
+      }
+      __syncthreads();
+    }
+  }
+  return back;
 }
 
 }  // namespace lps

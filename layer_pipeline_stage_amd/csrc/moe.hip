@@ -41,7 +41,7 @@ struct RouteP {
 // order (the same per-lane split and order as the prefill router), then a wave sum
 template <int CPL>
 __global__ __launch_bounds__(ROUTE_EPB * WAVE) void k_route_logits(RouteP p) {
-  extern __shared__ float xs[];
+  extern __shared__ __attribute__((aligned(16))) float xs[];
   const int t = blockIdx.y;
   const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
   const int e = blockIdx.x * ROUTE_EPB + wv;

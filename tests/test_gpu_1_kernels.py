@@ -112,6 +112,40 @@ def test_gemv_parity(L, wdtype, N, K, mode, norm):
     assert np.all(err <= bound + 1e-30), (err.max(), bound[np.argmax(err - bound)])
 
 
+@pytest.mark.parametrize("K", [5120, 17472])
+def test_mxfp4_gemv_unnormed_vector_past_f16_range(L, K):
+    """An un-normed MXFP4 GEMV input (the attention output, the SwiGLU output)
+    whose values pass f16's largest finite value: the staging scales the vector by
+    a power of two so no operand rounds to infinity, and the products are scaled
+    back: every output finite and within the same f16-operand bound of the oracle
+    as an ordinary vector; a vector below 2^15 gives the same bits as before the
+    scaling existed (it is staged unchanged: scaling by 2^e is exact, so the
+    2^e-scaled vector gives the 2^e-scaled result)."""
+    N = 66
+    w, W64, s = _weights("mxfp4", N, K, seed=K + 5)
+    rng = np.random.default_rng(K + 1)
+    x = (rng.standard_normal(K) * 1e5).astype(np.float32)       # |x| up to ~5e5
+    x[17] = 3.0e6
+    wd, sd, xd = dev(w), dev(s), dev(x)
+    yd = dev(np.zeros(N, np.float32))
+    L.lps_gemv(L.LPS_MXFP4, ptr(wd), ptr(sd), N, K, ptr(xd), None, 1e-6, ptr(yd), 0, stream())
+    got = yd.cpu().numpy().astype(np.float64)
+    xp = x.astype(np.float64)
+    ref = W64 @ xp
+    bound = dot_bound(W64, xp) + 2.0 ** -11 * (np.abs(W64) @ np.abs(xp))
+    assert np.all(np.isfinite(got))
+    assert np.all(np.abs(got - ref) <= bound), np.max(np.abs(got - ref) - bound)
+    # scaling a small vector by 2^e scales the result by exactly 2^e
+    xs = rng.standard_normal(K) * 10
+    xs = (np.sign(xs) * np.maximum(np.abs(xs), 1e-3)).astype(np.float32)   # no f16 subnormals
+    y1 = dev(np.zeros(N, np.float32))
+    L.lps_gemv(L.LPS_MXFP4, ptr(wd), ptr(sd), N, K, ptr(dev(xs)), None, 1e-6, ptr(y1), 0, stream())
+    y2 = dev(np.zeros(N, np.float32))
+    L.lps_gemv(L.LPS_MXFP4, ptr(wd), ptr(sd), N, K, ptr(dev(xs * np.float32(2.0 ** 20))), None,
+               1e-6, ptr(y2), 0, stream())
+    assert torch.equal(y2, y1 * 2.0 ** 20)
+
+
 def test_gemv_k_tail_reads_no_next_row(L):
     """K = 17472 (= 136 * 128 + 64): rows are laid out back to back, so a kernel
     that read whole 128-wide slabs past the end of a row would pull in the next
