@@ -513,6 +513,23 @@ def main():
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
     tok_s = K / dt
+    # the same graph-mode run with one stream per stage: every boundary hop is the
+    # event-ordered send / receive (ev_tx / ev_rx) instead of the same-stream seam
+    per_stage = None
+    if a.mode == "graph" and a.streams == "single" and a.stages > 1:
+        dd._streams_mode = "per-stage"
+        dd.set_fence(fence)
+        dd.reset()
+        dd.run_tokens_graph(start_tok, W - 1)
+        dd.reset()
+        clock2 = {}
+        dd.run_tokens_graph(start_tok, K - 1, timer=lambda st_: clock2.__setitem__(
+            "t0" if st_ else "t1", time.perf_counter()))
+        dt2 = clock2["t1"] - clock2["t0"]
+        per_stage = {"value": round(K / dt2, 2), "ms_per_step": round(1e3 * dt2 / K, 4),
+                     "streams": "per-stage", "boundary_hops_per_step": a.stages - 1}
+        dd._streams_mode = "single"
+        dd.set_fence(fence)
     rows = [cfg.prefix + 1 + i for i in range(K)]
     b = [algorithmic_bytes(cfg, n) for n in rows]
     bytes_tok = sum(x["weights"] + x["kv"] + x["io"] for x in b) / K
@@ -556,7 +573,8 @@ def main():
                         f"({a.streams} stream{'s' if a.streams == 'per-stage' else ''}), "
                         + ("the whole step as one replayed hipGraph, " if a.mode == "graph"
                            else "eager launches, ")
-                        + "deferred logits readback",
+                        + "per-step deferred logits readback (a pinned host ring drained "
+                          "on its own stream)",
             "mode": a.mode,
             "global_batch": 1, "seq_len": cfg.prefix + K, "stages": fence,
         },
@@ -573,6 +591,7 @@ def main():
             "avg_us": gk["avg_us"], "bytes_per_launch": gateup_bytes(cfg),
         },
         "kernels": kernels,
+        "per_stage_streams": per_stage,
         "first_tokens": res.fed[:8],
         "gen_s": round(t_gen, 1),
     }

@@ -421,9 +421,12 @@ class DeviceDecoder:
         """run_tokens with the whole step captured once and replayed: the
         position, the step and the next input id live on the device and are
         advanced by the graph itself, so the host only launches replays.  Every
-        step's argmax (and, with logits=True, its logits) is kept in a device
-        history that is read back once after the last replay.  timer: an
-        optional callable run around the replays (for the bench)."""
+        step's argmax (and, with logits=True, its logits) goes into a device
+        history slot of its own; after each replay that step's slot is handed to
+        the deferred readback (lps_logits_defer on the readback stream into a
+        pinned host ring of `ring` entries), and the host drains step t - ring
+        while later replays run.  timer: an optional callable run around the
+        replays and their readback (for the bench)."""
         cfg = self.cfg
         assert self.head is not None, "model has no vocabulary"
         p = cfg.prefix if p0 is None else p0
@@ -440,18 +443,34 @@ class DeviceDecoder:
         self.g_tok.fill_(ids[0])
         g = self.capture_step(ptr(feed_dev), P, ptr(tok_hist),
                               ptr(lg_hist) if logits else None, total)
+        R = self.ring
+        pend = [None] * R
+        toks, lg = [None] * total, [None] * total
+
+        def drain(i):
+            lps.lps_pending_wait(pend[i % R])
+            pend[i % R] = None
+            toks[i] = int(self.host_tok[i % R])
+            if logits:
+                lg[i] = self.host_logits[i % R].numpy().copy()
+
         try:
             st0 = self.streams[0]
             torch.cuda.synchronize(dev)
             if timer is not None:
                 timer(True)
-            for _ in range(total):
+            for i in range(total):
+                if i >= R:
+                    drain(i - R)             # frees host ring slot i % R
                 lps.lps_graph_launch(g, sp(st0))
-            # the deferred readback: every step's id (and logits) in one drain,
-            # ordered behind the replays on their stream
-            with torch.cuda.stream(st0):
-                toks = tok_hist.cpu().tolist()
-                lg = list(lg_hist.cpu().numpy()) if logits else [None] * total
+                h = C.c_void_p()
+                lps.lps_logits_defer(ptr(lg_hist) + 4 * cfg.vocab * i if logits else None,
+                                     ptr(tok_hist) + 4 * i, cfg.vocab, sp(st0), sp(self.readback),
+                                     ptr(self.host_logits[i % R]) if logits else None,
+                                     ptr(self.host_tok) + 4 * (i % R), C.byref(h))
+                pend[i % R] = h
+            for i in range(max(0, total - R), total):
+                drain(i)
             if timer is not None:
                 timer(False)
         finally:
