@@ -367,6 +367,12 @@ typedef struct lps_boundary lps_boundary;
 int lps_boundary_create(int32_t n_elems, float* slot0, float* slot1, lps_boundary** out);
 int lps_boundary_send(lps_boundary* b, const float* x, int64_t step, void* producer);
 int lps_boundary_recv(lps_boundary* b, float* x, int64_t step, void* consumer);
+/* The same-stream seam in one call: send(step) and recv(step) with producer ==
+ * consumer == `stream`, as one kernel that writes slot[step & 1] and x_out (dev
+ * [n_elems] f32) from x; the same order rules (step must be the next send and the
+ * next receive), the same waits (for an earlier receive of that slot on another
+ * stream) and counters (a send and a receive) as the two calls. */
+int lps_boundary_hop(lps_boundary* b, const float* x, float* x_out, int64_t step, void* stream);
 /* Synchronizes the boundary's events, then frees the handle. */
 int lps_boundary_destroy(lps_boundary* b);
 

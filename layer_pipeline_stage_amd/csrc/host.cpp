@@ -1034,6 +1034,43 @@ int lps_boundary_recv(lps_boundary* b, float* x, int64_t step, void* consumer) {
   return LPS_OK;
 }
 
+int lps_boundary_hop(lps_boundary* b, const float* x, float* x_out, int64_t step, void* stream) {
+  LPS_REQUIRE(b && x && x_out, LPS_EINVAL, "lps_boundary_hop: null boundary, x or x_out");
+  LPS_REQUIRE(aligned16(x) && aligned16(x_out), LPS_EINVAL,
+              "lps_boundary_hop: x and x_out must be 16-byte aligned");
+  LPS_REQUIRE(step == b->next_send && step == b->next_recv, LPS_ESTATE,
+              "lps_boundary_hop: step %lld out of order (next send %lld, next receive %lld)",
+              (long long)step, (long long)b->next_send, (long long)b->next_recv);
+  const int k = int(step & 1);
+  hipStream_t st = as_stream(stream);
+  unsigned long long cid = 0;
+  int rc = capture_of(st, &cid);
+  if (rc) return rc;
+  // the slot's last receive on another stream: this write waits for it (as a send)
+  if (b->rx_stream[k] && b->rx_stream[k] != st && b->rx_cap[k] == cid) {
+    if (!b->rx_recorded[k]) {
+      unsigned long long rcid = 0;
+      rc = capture_of(b->rx_stream[k], &rcid);
+      if (rc) return rc;
+      LPS_REQUIRE(rcid == cid, LPS_ESTATE,
+                  "lps_boundary_hop: slot %d's last receive stream is in another capture context", k);
+      LPS_HIP(hipEventRecord(b->ev_rx[k], b->rx_stream[k]));
+      b->rx_recorded[k] = true;
+    }
+    LPS_HIP(hipStreamWaitEvent(st, b->ev_rx[k], 0));
+  }
+  rc = launch_copy2_f32(x, b->slot[k], x_out, b->n, st);
+  if (rc) return rc;
+  b->tx_recorded[k] = false;
+  b->tx_stream[k] = b->rx_stream[k] = st;
+  b->tx_cap[k] = b->rx_cap[k] = cid;
+  b->rx_recorded[k] = false;
+  b->next_send = b->next_recv = step + 1;
+  count_send();
+  count_recv();
+  return LPS_OK;
+}
+
 int lps_boundary_destroy(lps_boundary* b) {
   if (!b) return LPS_OK;
   int rc = LPS_OK;

@@ -96,6 +96,7 @@ int launch_attention(int nq, int nkv, int hd, int kvdtype, const void* kc, const
 
 int launch_row_at_step(const int32_t* state, const float* src, int64_t src_stride, float* dst,
                        int64_t dst_stride, int32_t n, int32_t n_rows, hipStream_t st);
+int launch_copy2_f32(const float* src, float* dst0, float* dst1, int64_t n, hipStream_t st);
 int launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t st);
 // decode step state (pos, step, flags): see lps_step_advance
 int launch_step_advance(int32_t* state, int32_t pos_limit, const int32_t* argmax, int32_t* tok_cur,

@@ -45,6 +45,21 @@ __global__ void k_copy(const float* __restrict__ src, float* __restrict__ dst, l
     dst[i] = src[i];
 }
 
+// dst0 = dst1 = src (n floats, 16-byte aligned): the same-stream boundary hop
+__global__ void k_copy2(const float* __restrict__ src, float* __restrict__ dst0,
+                        float* __restrict__ dst1, long long n) {
+  const long long n4 = n / 4;
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n4;
+       i += (long long)gridDim.x * blockDim.x) {
+    const f32x4 v = reinterpret_cast<const f32x4*>(src)[i];
+    reinterpret_cast<f32x4*>(dst0)[i] = v;
+    reinterpret_cast<f32x4*>(dst1)[i] = v;
+  }
+  for (long long i = n4 * 4 + blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n;
+       i += (long long)gridDim.x * blockDim.x)
+    dst0[i] = dst1[i] = src[i];
+}
+
 // ---- A12: f32 -> f16 (RNE), f16 -> f32 (exact) ----------------------------------------
 __global__ void k_f32_to_f16(const float* src, uint16_t* dst, long long n) {
   for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n;
@@ -204,6 +219,13 @@ int launch_row_at_step(const int32_t* state, const float* src, int64_t src_strid
                        int64_t dst_stride, int32_t n, int32_t n_rows, hipStream_t st) {
   hipLaunchKernelGGL(k_row_at_step, grid_for(n), dim3(256), 0, st, state, src,
                      (long long)src_stride, dst, (long long)dst_stride, n, n_rows);
+  LPS_HIP(hipGetLastError());
+  return LPS_OK;
+}
+
+int launch_copy2_f32(const float* src, float* dst0, float* dst1, int64_t n, hipStream_t st) {
+  if (n == 0) return LPS_OK;
+  hipLaunchKernelGGL(k_copy2, grid_for(n / 4 + 1), dim3(256), 0, st, src, dst0, dst1, (long long)n);
   LPS_HIP(hipGetLastError());
   return LPS_OK;
 }

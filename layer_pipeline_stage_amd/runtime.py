@@ -81,6 +81,16 @@ def memory_balanced_fence(n_layers, d, nq, nkv, hd, ff, vocab, wdtype, kvdtype, 
                            n_stages, max_groups)
 
 
+def _hop(b, src, dst, step, producer, consumer):
+    """One boundary crossing: the send and the receive, or on the same-stream seam
+    the single-kernel hop."""
+    if producer is consumer:
+        lps.lps_boundary_hop(b, src, dst, step, sp(producer))
+    else:
+        lps.lps_boundary_send(b, src, step, sp(producer))
+        lps.lps_boundary_recv(b, dst, step, sp(consumer))
+
+
 @dataclass
 class StepResult:
     fed: list
@@ -250,8 +260,7 @@ class DeviceDecoder:
         t = self.step_no
         for s in range(n):
             if s > 0:
-                lps.lps_boundary_send(self.bounds[s - 1], ptr(self.x[s - 1]), t, sp(st[s - 1]))
-                lps.lps_boundary_recv(self.bounds[s - 1], ptr(self.x[s]), t, sp(st[s]))
+                _hop(self.bounds[s - 1], ptr(self.x[s - 1]), ptr(self.x[s]), t, st[s - 1], st[s])
             lps.lps_stage_forward(self.model, self._fence_c, n, s, ptr(self.x[s]), pos,
                                   ptr(self.scratch[s]), self.scratch_bytes, sp(st[s]))
         self.step_no += 1
@@ -385,8 +394,7 @@ class DeviceDecoder:
         pos_dev = ptr(self.g_state)
         for s in range(n):
             if s > 0:
-                lps.lps_boundary_send(self.bounds[s - 1], ptr(self.x[s - 1]), t, sp(st[s - 1]))
-                lps.lps_boundary_recv(self.bounds[s - 1], ptr(self.x[s]), t, sp(st[s]))
+                _hop(self.bounds[s - 1], ptr(self.x[s - 1]), ptr(self.x[s]), t, st[s - 1], st[s])
             lps.lps_stage_forward_dpos(self.model, self._fence_c, n, s, ptr(self.x[s]), pos_dev,
                                        ptr(self.scratch[s]), self.scratch_bytes, sp(st[s]))
         self.step_no += 1
@@ -631,8 +639,7 @@ class DeviceMoEStack:
         n, st, t = self.n_stages, self.streams, self.step_no
         for s in range(n):
             if s > 0:
-                lps.lps_boundary_send(self.bounds[s - 1], ptr(self.x[s - 1]), t, sp(st[s - 1]))
-                lps.lps_boundary_recv(self.bounds[s - 1], ptr(self.x[s]), t, sp(st[s]))
+                _hop(self.bounds[s - 1], ptr(self.x[s - 1]), ptr(self.x[s]), t, st[s - 1], st[s])
             lps.lps_stage_forward(self.model, self._fence_c, n, s, ptr(self.x[s]), 0,
                                   ptr(self.scratch[s]), self.scratch_bytes, sp(st[s]))
         self.step_no += 1

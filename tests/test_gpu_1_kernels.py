@@ -487,6 +487,38 @@ def test_pending_readback(L):
     assert e.value.code == L.LPS_ESTATE
 
 
+def test_boundary_hop_is_send_plus_receive(L):
+    """The same-stream hop writes the slot and the receiver's buffer from the sent
+    row in one kernel, keeps the protocol's order (a hop out of order is refused,
+    as is a hop after a lone send) and counts a send and a receive."""
+    d = 4099
+    s0 = torch.full((d,), float("nan"), device=DEV)
+    s1 = torch.full((d,), float("nan"), device=DEV)
+    b = C.c_void_p()
+    L.lps_boundary_create(d, ptr(s0), ptr(s1), C.byref(b))
+    st = torch.cuda.Stream()
+    rng = np.random.default_rng(21)
+    xs = [dev(rng.standard_normal(d).astype(np.float32)) for _ in range(4)]
+    ys = [torch.full((d,), float("nan"), device=DEV) for _ in range(4)]
+    L.lps_counters_reset()
+    for t in range(3):
+        L.lps_boundary_hop(b, ptr(xs[t]), ptr(ys[t]), t, st.cuda_stream)
+    with pytest.raises(L.LpsError) as e:
+        L.lps_boundary_hop(b, ptr(xs[3]), ptr(ys[3]), 5, st.cuda_stream)
+    assert e.value.code == L.LPS_ESTATE
+    L.lps_boundary_send(b, ptr(xs[3]), 3, st.cuda_stream)
+    with pytest.raises(L.LpsError):
+        L.lps_boundary_hop(b, ptr(xs[3]), ptr(ys[3]), 3, st.cuda_stream)
+    L.lps_boundary_recv(b, ptr(ys[3]), 3, st.cuda_stream)
+    torch.cuda.synchronize()
+    for t in range(4):
+        assert torch.equal(ys[t], xs[t]), t
+    assert torch.equal(s0, xs[2]) and torch.equal(s1, xs[3])
+    c = L.counters()
+    assert c["boundary_sends"] == 4 and c["boundary_recvs"] == 4
+    L.lps_boundary_destroy(b)
+
+
 def test_boundary_orders_a_same_stream_receive_before_another_producer(L):
     """Step 0 is sent and received on stream A behind a long read (its receive
     records no event: same stream); step 2 is then sent from stream B into the
