@@ -48,10 +48,8 @@ constexpr int PF_TOK = 8;      // tokens per routing tile
 constexpr int PF_MAXE = 64;    // experts the tile router is built for
 constexpr int PF_RCPL = 10;    // router row chunks per lane (d <= 5120, the LDS bound below)
 constexpr int PF_MAXK = 16;
-// grouped GEMM tile: BM token rows x BN weight rows, K in steps of BK; LDS rows padded
-// by 16 bytes (144-byte stride: the eight lanes of a ds_read_b128 phase hit distinct banks)
-constexpr int GM = 256, GBN = 256, GBK = 64, GKP = GBK + 8;
-constexpr int GEMM_THREADS = 512;
+// grouped GEMM tile: GM token rows x GBN weight rows; K a multiple of 2 GBK
+constexpr int GM = 256, GBN = 256, GBK = 64;
 
 struct PfP {
   const float* x;        // [T, d] residual
@@ -430,17 +428,70 @@ __global__ __launch_bounds__(WAVE) void k_pf_tiles(PfP p) {
 
 // ---- 4/5. grouped GEMM on MFMA -----------------------------------------------------------
 // C[m, n] = sum_k A[m, k] B[n, k]: A rows are gathered activation rows (bf16), B
-// rows weight rows (bf16, K contiguous).  A 256 x 256 tile per workgroup of 8 waves
-// (2 x 4, two per SIMD), each wave 128 x 64 as 4 x 2 MFMA 32x32x16 blocks.  K walks
-// in steps of 64 through two LDS buffers, and the global loads run two steps ahead
-// in two register sets: at step k the loads of step k + 2 go out, step k is
-// multiplied from LDS, and step k + 1 (loaded during step k - 1) is written to the
-// other buffer; one barrier per step.  The step count is even, so the loop handles
-// steps in pairs with fixed buffers and no branch; near the end the loads repeat the
-// last step (valid memory, never stored to a buffer that is read).
+// rows weight rows (bf16, K contiguous).  A 256 x 256 tile per workgroup of four
+// waves (2 x 2, one per SIMD), each wave 128 x 128 as 4 x 4 MFMA 32x32x16 blocks:
+// per 16-deep sub-step a wave reads 8 KiB of operands from LDS for 16 products,
+// half a KiB per product (a 128 x 64 wave tile reads three quarters), so the LDS
+// reads stay below the matrix cores' time.
+// The operands go from global memory straight into LDS (buffer loads with the LDS
+// as destination: no registers, no LDS store instructions) in K steps of MM_BK,
+// through rings of MM_SA stages for A and MM_SB for B: a step's loads go out
+// MM_SA - 1 (A) and MM_SB - 1 (B) steps before it is multiplied.  A staged row is
+// one step of K (whole 128-byte lines at MM_BK = 64); its 16-byte k chunk c sits
+// at slot c ^ swz(r), so the 16 lanes of each ds_read_b128 phase (16 consecutive
+// rows, one chunk) fall on all 64 banks.
+// Step t: read sub-step 1.. operands while multiplying the previous ones; once the
+// last sub-step's reads are done, wait for this wave's loads of step t + 1; one
+// barrier (every wave has read step t's stages, every wave's loads of step t + 1
+// have landed); load B of step t + MM_SB and A of step t + MM_SA into the freed
+// stages, read step t + 1's first sub-step, multiply the last one.  The last
+// steps' loads repeat the last step into stages that are not read again.
+#ifndef LPS_MM_BK
+#define LPS_MM_BK 64
+#endif
+#ifndef LPS_MM_SA
+#define LPS_MM_SA 3
+#endif
+#ifndef LPS_MM_SB
+#define LPS_MM_SB 2
+#endif
+constexpr int MM_THREADS = 256;
+constexpr int MM_BK = LPS_MM_BK;             // K per step
+constexpr int MM_SA = LPS_MM_SA, MM_SB = LPS_MM_SB;
+constexpr int MM_NS = MM_BK / 16;            // sub-steps per step
+constexpr int MM_CH = MM_BK / 8;             // 16-byte chunks per staged row
+constexpr int MM_ROWB = MM_BK * 2;           // bytes of a staged row
+constexpr int MM_OPB = GM * MM_ROWB;         // bytes per operand stage
+constexpr int MM_RPI = 64 / MM_CH;           // staged rows per load instruction
+constexpr int MM_NI = 64 / MM_RPI;           // load instructions per wave, operand and step
+constexpr int MM_LDS = (MM_SA + MM_SB) * MM_OPB;
+static_assert(GM == 256 && GBN == 256, "the staged tile is 256 x 256");
+static_assert((MM_BK == 32 || MM_BK == 64) && MM_SA == MM_SB + 1 && MM_SB >= 2, "staging shape");
+static_assert(MM_LDS <= 160 * 1024, "staging exceeds the LDS");
+// Load order: during step t the A loads of step t + MM_SA - 1 (into the A stage step
+// t - 1 freed), spread over the step's sub-steps; after step t's barrier the B loads
+// of step t + MM_SB (into the B stage step t freed).  Loads return in order, so at
+// step t's wait (A and B of step t + 1 landed) the loads issued after B of step
+// t + 1 may still be out: step t's A and MM_SB - 2 steps of A and B.
+constexpr int MM_VM_MID = MM_NI + (MM_SB - 2) * 2 * MM_NI;
+constexpr int MM_VM_PRO = (MM_SB - 1) * 2 * MM_NI;
+static_assert(MM_VM_PRO < 64 && MM_VM_MID < 64, "vmcnt range");
+
+// slot of chunk c in staged row r is c ^ mm_swz(r).  The LDS has 64 four-byte banks
+// and serves a ds_read_b128 16 lanes (256 bytes) at a time; an operand read is 16
+// consecutive rows at one chunk, so the 16 rows must cover all 16 16-byte bank
+// groups: 128-byte rows (two per 256 bytes) alternate halves and need 8 slots among
+// same-parity rows, 64-byte rows 4 slots among rows equal mod 4.
+__device__ __forceinline__ int mm_swz(int r) { return MM_CH == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
+// s_waitcnt immediates (gfx9 encoding): vmcnt bits [3:0] and [15:14], lgkmcnt [11:8]
+constexpr int mm_wait(int vm, int lgkm) {
+  return (vm & 15) | (7 << 4) | ((lgkm & 15) << 8) | ((vm >> 4) << 14);
+}
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
 template <bool FIRST>
-__global__ __launch_bounds__(GEMM_THREADS) void k_pf_gemm(PfP p) {
-  constexpr int NJ = 4;                      // 16-byte chunks per thread and operand per step
+__global__ __launch_bounds__(MM_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_pf_gemm(PfP p) {
   const int tile = blockIdx.y;
   if (tile >= *p.n_tiles) return;
   const int packed = p.tiles[tile];
@@ -450,16 +501,13 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_pf_gemm(PfP p) {
   const int K = FIRST ? p.d : p.ff;
   const int n0 = FIRST ? blockIdx.x * (GBN / 2) : blockIdx.x * GBN;
   extern __shared__ __attribute__((aligned(16))) uint16_t gsm[];
-  uint16_t* As0 = gsm;                       // [GM][GKP]
-  uint16_t* Bs0 = As0 + GM * GKP;            // [GBN][GKP]
-  uint16_t* As1 = Bs0 + GBN * GKP;
-  uint16_t* Bs1 = As1 + GM * GKP;
+  char* lds = reinterpret_cast<char*>(gsm);
+  char* ldsA = lds;                          // [MM_SA][GM][MM_ROWB]
+  char* ldsB = lds + MM_SA * MM_OPB;         // [MM_SB][GBN][MM_ROWB]
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid / 64;
-  const int wm = wv >> 2, wn = wv & 3;
-  // A and B through buffer resources: one 32-bit byte offset per staged row (rows
-  // tid / 8 + 64 j, column 8 (tid % 8)), the K step as the scalar offset
-  const int scol = (tid & 7) * 8;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int wm = wv >> 1, wn = wv & 1;
   const uint16_t* abase = FIRST ? p.xb : p.act;
   const uint16_t* bbase = FIRST ? (shared_e ? p.w_gu_s : p.w_gu_e + (long long)e * 2 * p.ff * p.d)
                                 : (shared_e ? p.w_d_s : p.w_d_e + (long long)e * p.d * p.ff);
@@ -469,132 +517,203 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_pf_gemm(PfP p) {
       const_cast<uint16_t*>(abase), (short)0, (int)(abytes < 0x7FFFFFFF ? abytes : 0x7FFFFFFF), 0x00020000);
   const __amdgpu_buffer_rsrc_t bres = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(bbase), (short)0, (int)(bbytes < 0x7FFFFFFF ? bbytes : 0x7FFFFFFF), 0x00020000);
-  int aoff[NJ], boff[NJ];
+  // GEMM2: this thread's tile row's output offset and gate weight, loaded first
+  // (the first operand wait covers them), put in LDS for the epilogue
+  long long eo = 0;
+  float ewt = 0.f;
+  if (!FIRST) {
+    const int m = m0 + tid;
+    if (m < cnt) {
+      if (shared_e) {
+        eo = (long long)m * p.d;
+        ewt = 1.f;
+      } else {
+        const long long li = (long long)e * p.T + m;
+        eo = ((long long)p.lst[li] * p.k + p.lslot[li]) * p.d;
+        ewt = p.lw[li];
+      }
+    }
+  }
+  // the rows this lane stages: rows 64 wv + MM_RPI j + lane / MM_CH (j < MM_NI) of
+  // A and of B, k chunk (lane % MM_CH) ^ swz(row) into slot lane % MM_CH
+  const int lrow = lane / MM_CH;
+  int aoff[MM_NI], boff[MM_NI];
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int sr = (tid >> 3) + 64 * j;
+  for (int j = 0; j < MM_NI; ++j) {
+    const int sr = 64 * wv + MM_RPI * j + lrow;
+    const int gch = (lane % MM_CH) ^ mm_swz(sr);
     const int r = m0 + sr;
     const int rr = r < cnt ? r : m0;          // rows past the list repeat a valid row
     if (FIRST) {
       const int tok = shared_e ? rr : p.lst[(long long)e * p.T + rr];
-      aoff[j] = (tok * p.d + scol) * 2;
+      aoff[j] = (tok * p.d + 8 * gch) * 2;
     } else {
-      aoff[j] = ((p.off[e] + rr) * p.ff + scol) * 2;
+      aoff[j] = ((p.off[e] + rr) * p.ff + 8 * gch) * 2;
     }
     int wrow;
     if (FIRST) {
-      // B rows of wave column wc: 32 gate rows then 32 up rows of the same outputs
-      const int wc = sr >> 6, jj = (sr >> 5) & 1, cc = sr & 31;
-      wrow = (jj ? p.ff : 0) + n0 + 32 * wc + cc;
+      // staged B rows of wave column wc = sr / 128: blocks of 32 gate rows and 32 up
+      // rows of the same outputs, alternating, so gate and up of an output share lanes
+      const int wc = sr >> 7, jb = (sr >> 5) & 3, cc = sr & 31;
+      wrow = ((jb & 1) ? p.ff : 0) + n0 + 64 * wc + 32 * (jb >> 1) + cc;
     } else {
       wrow = n0 + sr;
     }
-    boff[j] = (wrow * K + scol) * 2;
+    boff[j] = (wrow * K + 8 * gch) * 2;
   }
-  const int soff = (tid >> 3) * GKP + scol;   // LDS element offset of chunk j = 0
+  // operand reads: A rows 128 wm + 32 i + lane % 32, B rows 128 wn + 32 j + lane % 32
+  // (their swizzle is lane % 32's); sub-step ks takes k chunk 2 ks + lane / 32
+  const int fr = lane & 31, fsw = mm_swz(fr), fh = lane >> 5;
+  const int ard = (128 * wm + fr) * MM_ROWB, brd = (128 * wn + fr) * MM_ROWB;
 
-  f32x16 acc[4][2];
+  f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-#define PF_LOAD(RA, RB, K0)                                                                       \
-  _Pragma("unroll") for (int j = 0; j < NJ; ++j) {                                                \
-    RA[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ares, aoff[j], 2 * (K0), 0)); \
-    RB[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(bres, boff[j], 2 * (K0), 2)); \
+#define MM_DMA_B(S, T)                                                                         \
+  _Pragma("unroll") for (int j = 0; j < MM_NI; ++j)                                            \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                  \
+        bres, (lds_ptr_t)(ldsB + (S) * MM_OPB + (64 * wv + MM_RPI * j) * MM_ROWB), 16, boff[j], \
+        (T) * MM_ROWB, 0, 2);
+#define MM_DMA_A1(S, T, J)                                                                     \
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                    \
+      ares, (lds_ptr_t)(ldsA + (S) * MM_OPB + (64 * wv + MM_RPI * (J)) * MM_ROWB), 16, aoff[J], \
+      (T) * MM_ROWB, 0, 0);
+#define MM_READ(R, SA_, SB_, KS)                                                               \
+  {                                                                                            \
+    const int sl = 16 * ((2 * (KS) + fh) ^ fsw);                                               \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                            \
+      R[i] = *reinterpret_cast<const bf16x8*>(ldsA + (SA_) * MM_OPB + ard + 32 * i * MM_ROWB + sl); \
+      R[4 + i] = *reinterpret_cast<const bf16x8*>(ldsB + (SB_) * MM_OPB + brd + 32 * i * MM_ROWB + sl); \
+    }                                                                                          \
   }
-#define PF_STORE(RA, RB, AS, BS)                                         \
-  _Pragma("unroll") for (int j = 0; j < NJ; ++j) {                       \
-    *reinterpret_cast<u32x4*>(AS + soff + 64 * j * GKP) = RA[j];         \
-    *reinterpret_cast<u32x4*>(BS + soff + 64 * j * GKP) = RB[j];         \
-  }
-#define PF_MMA(AS, BS)                                                                          \
-  _Pragma("unroll") for (int ks = 0; ks < GBK / 16; ++ks) {                                      \
-    bf16x8 a[4], b[2];                                                                           \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                \
-      a[i] = *reinterpret_cast<const bf16x8*>(AS + (128 * wm + 32 * i + (lane & 31)) * GKP +      \
-                                              16 * ks + 8 * (lane >> 5));                        \
-    _Pragma("unroll") for (int j = 0; j < 2; ++j)                                                \
-      b[j] = *reinterpret_cast<const bf16x8*>(BS + (64 * wn + 32 * j + (lane & 31)) * GKP +       \
-                                              16 * ks + 8 * (lane >> 5));                        \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                \
-      _Pragma("unroll") for (int j = 0; j < 2; ++j)                                              \
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);     \
-  }
+#define MM_MMA(R)                                                                              \
+  _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                              \
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(R[i], R[4 + j], acc[i][j], 0, 0, 0);
 
-  const int nk = K / GBK;                    // even (checked on the host)
-  u32x4 ra0[NJ], rb0[NJ], ra1[NJ], rb1[NJ];
-  PF_LOAD(ra0, rb0, 0)
-  PF_LOAD(ra1, rb1, GBK)
-  // GEMM2: each of the tile's rows' output offset and gate weight, loaded once into
-  // LDS behind the operand buffers while the first operands are in flight (the
-  // epilogue reads them from there; the loop's barriers order them)
-  long long* eoff = reinterpret_cast<long long*>(gsm + 2 * (GM + GBN) * GKP);
-  float* ew = reinterpret_cast<float*>(eoff + GM);
-  if (!FIRST && tid < GM) {
-    const int m = m0 + tid;
-    long long o = 0;
-    float w = 0.f;
-    if (m < cnt) {
-      if (shared_e) {
-        o = (long long)m * p.d;
-        w = 1.f;
-      } else {
-        const long long li = (long long)e * p.T + m;
-        o = ((long long)p.lst[li] * p.k + p.lslot[li]) * p.d;
-        w = p.lw[li];
-      }
+  const int nk = K / MM_BK;                  // >= 2 (K is a multiple of 128)
+  // prologue: the loads of steps before 0 in the loop's order (during step s the A
+  // loads of step s + MM_SB, after it the B loads of the same step, s = -MM_SB .. -1);
+  // with fewer steps than stages the extra stages get the last step again and are
+  // never read
+#pragma unroll
+  for (int s = 0; s < MM_SB; ++s) {
+#pragma unroll
+    for (int j = 0; j < MM_NI; ++j) MM_DMA_A1(s, min(s, nk - 1), j)
+    MM_DMA_B(s, min(s, nk - 1))
+  }
+  bf16x8 r0[8], r1[8];
+  __builtin_amdgcn_s_waitcnt(mm_wait(MM_VM_PRO, 15));   // this wave's loads of step 0
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  MM_READ(r0, 0, 0, 0)
+  int sa = 0, sb = 0;                        // stages of step kt
+  // With one wave per SIMD the wave's own instruction order decides what overlaps
+  // the products, and its loads queue for the CU's one address unit: each
+  // sub-step's 16 products go out one by one with the next sub-step's 8 operand
+  // reads between the first eight (their LDS latency is covered by the last eight)
+  // and a share of the A loads between the last eight; after the barrier the B
+  // loads go between the last sub-step's products.
+#define MM_PACE_READS()                                                                        \
+  _Pragma("unroll") for (int q = 0; q < 8; ++q) {                                              \
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                         \
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                         \
+  }
+  int fa = MM_SA - 1;                        // the A stage freed by the previous step
+  for (int kt = 0; kt < nk; ++kt) {
+    const int ta = min(kt + MM_SA - 1, nk - 1);   // A loads of this step's spread
+    // sub-step KS: read sub-step KS into RN, issue A loads [J0, J1), multiply RC
+#define MM_SUB(KS, RN, RC)                                                                     \
+    {                                                                                          \
+      constexpr int J0 = ((KS) - 1) * MM_NI / (MM_NS - 1), J1 = (KS) * MM_NI / (MM_NS - 1);    \
+      MM_READ(RN, sa, sb, KS)                                                                  \
+      _Pragma("unroll") for (int j = J0; j < J1; ++j) MM_DMA_A1(fa, ta, j)                     \
+      MM_MMA(RC)                                                                               \
+      MM_PACE_READS()                                                                          \
+      _Pragma("unroll") for (int q = 0; q < J1 - J0; ++q) {                                    \
+        __builtin_amdgcn_sched_group_barrier(0x008, 8 / (J1 - J0), 0);                         \
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                     \
+      }                                                                                        \
+      __builtin_amdgcn_sched_group_barrier(0x008, 8 - (8 / (J1 - J0)) * (J1 - J0) + 0, 0);     \
+      __builtin_amdgcn_sched_barrier(0);                                                       \
     }
-    eoff[tid] = o;
-    ew[tid] = w;
+    MM_SUB(1, r1, r0)
+    if constexpr (MM_NS == 4) {
+      MM_SUB(2, r0, r1)
+      MM_SUB(3, r1, r0)
+    }
+#undef MM_SUB
+    // the reads above are done and this wave's loads of step kt + 1 have landed
+    __builtin_amdgcn_s_waitcnt(mm_wait(MM_VM_MID, 0));
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    const int na = sa + 1 == MM_SA ? 0 : sa + 1, nb = sb + 1 == MM_SB ? 0 : sb + 1;
+    MM_READ(r0, na, nb, 0)
+    MM_DMA_B(sb, min(kt + MM_SB, nk - 1))
+    MM_MMA(r1)                               // MM_NS is even: the last sub-step is in r1
+    MM_PACE_READS()
+#pragma unroll
+    for (int q = 0; q < MM_NI; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 8 / MM_NI, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    fa = sa;
+    sa = na;
+    sb = nb;
   }
-  PF_STORE(ra0, rb0, As0, Bs0)
+#undef MM_PACE_READS
+#undef MM_DMA_A1
+#undef MM_DMA_B
+#undef MM_READ
+#undef MM_MMA
+  // the loads still out only repeat the last step into unread stages: drain them
+  // before the stages are reused below
+  __builtin_amdgcn_s_waitcnt(mm_wait(0, 0));
   __syncthreads();
-  for (int kt = 0; kt < nk; kt += 2) {
-    const int s2 = min(kt + 2, nk - 1), s3 = min(kt + 3, nk - 1);
-    PF_LOAD(ra0, rb0, s2 * GBK)               // step kt + 2
-    PF_MMA(As0, Bs0)                          // step kt
-    PF_STORE(ra1, rb1, As1, Bs1)              // step kt + 1
-    __syncthreads();
-    PF_LOAD(ra1, rb1, s3 * GBK)               // step kt + 3
-    PF_MMA(As1, Bs1)                          // step kt + 1
-    PF_STORE(ra0, rb0, As0, Bs0)              // step kt + 2 (unread after the last pair)
-    __syncthreads();
-  }
-#undef PF_LOAD
-#undef PF_STORE
-#undef PF_MMA
-  // epilogue: acc[i][j][r] is C[128 wm + 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4][64 wn + 32 j + lane % 32]
+  // epilogue: acc[i][j][r] is C[128 wm + 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4][128 wn + 32 j + lane % 32]
   if constexpr (FIRST) {
-    // the SwiGLU tile [GM][GBN / 2] (bf16) is assembled in LDS (the operand buffers are
-    // free: every wave passed the loop's last barrier after its last operand read),
-    // then leaves as whole 16-byte pieces of its rows (2-byte stores from the
-    // accumulator layout covered only half a cache line per half-wave)
+    // blocks j = 0, 2 hold gate and 1, 3 up of outputs 64 wn + 32 (j / 2) + lane % 32;
+    // the SwiGLU tile [GM][GBN / 2] (bf16) is assembled in LDS, then leaves as whole
+    // 16-byte pieces of its rows
     constexpr int OP = GBN / 2 + 8;           // row pitch (bf16): rows 4 apart on other banks
     uint16_t* ot = gsm;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 128 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        ot[row * OP + 32 * wn + (lane & 31)] = bf16_rne(silu(acc[i][0][r]) * acc[i][1][r]);
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 128 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          ot[row * OP + 64 * wn + 32 * h + (lane & 31)] =
+              bf16_rne(silu_fast(acc[i][2 * h][r]) * acc[i][2 * h + 1][r]);
+        }
       }
     }
     __syncthreads();
     const long long obase = (long long)(p.off[e] + m0) * p.ff + n0;
     constexpr int CPR = GBN / 2 / 8;          // 16-byte pieces per row
 #pragma unroll
-    for (int q = 0; q < GM * CPR / GEMM_THREADS; ++q) {
-      const int c = tid + q * GEMM_THREADS;
+    for (int q = 0; q < GM * CPR / MM_THREADS; ++q) {
+      const int c = tid + q * MM_THREADS;
       const int row = c / CPR, c8 = (c % CPR) * 8;
       if (m0 + row < cnt)
         *reinterpret_cast<u32x4*>(p.act + obase + (long long)row * p.ff + c8) =
             *reinterpret_cast<const u32x4*>(ot + row * OP + c8);
     }
   } else {
+    long long* eoff = reinterpret_cast<long long*>(lds);
+    float* ew = reinterpret_cast<float*>(eoff + GM);
+    eoff[tid] = eo;
+    ew[tid] = ewt;
+    __syncthreads();
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -604,8 +723,8 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_pf_gemm(PfP p) {
           const float wgt = ew[row];
           float* dst = (shared_e ? p.shared : p.z) + eoff[row];
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int col = n0 + 64 * wn + 32 * j + (lane & 31);
+          for (int j = 0; j < 4; ++j) {
+            const int col = n0 + 128 * wn + 32 * j + (lane & 31);
             __builtin_nontemporal_store(shared_e ? acc[i][j][r] : wgt * acc[i][j][r], dst + col);
           }
         }
@@ -772,8 +891,7 @@ extern "C" int lps_moe_prefill(const lps_moe_desc* m, float* x, int32_t T, int32
   if (!rc) rc = route_mx ? ensure_lds((const void*)k_pf_route_mx, mlds)
                          : ensure_lds((const void*)k_pf_route<true>, rlds);
   if (rc) return rc;
-  const size_t glds = size_t(2) * (GM + GBN) * GKP * sizeof(uint16_t);
-  const size_t glds2 = glds + size_t(GM) * (sizeof(long long) + sizeof(float));   // + row table
+  const size_t glds = MM_LDS, glds2 = MM_LDS;
   rc = ensure_lds((const void*)k_pf_gemm<true>, glds);
   if (!rc) rc = ensure_lds((const void*)k_pf_gemm<false>, glds2);
   if (rc) return rc;
@@ -823,9 +941,9 @@ extern "C" int lps_moe_prefill(const lps_moe_desc* m, float* x, int32_t T, int32
     pr.tiles = p.tiles_r;
     pr.n_tiles = p.n_tiles_r;
     Stamp t1 = timer_take(LPS_KIND_MOE_GEMM1), t2 = timer_take(LPS_KIND_MOE_GEMM2);
-    LPS_LAUNCH(k_pf_gemm<true>, dim3(m->ff / (GBN / 2), s.max_tiles), dim3(GEMM_THREADS), glds, sr,
+    LPS_LAUNCH(k_pf_gemm<true>, dim3(m->ff / (GBN / 2), s.max_tiles), dim3(MM_THREADS), glds, sr,
                t1.start, t1.stop, pr);
-    LPS_LAUNCH(k_pf_gemm<false>, dim3(m->d / GBN, s.max_tiles), dim3(GEMM_THREADS), glds2, sr,
+    LPS_LAUNCH(k_pf_gemm<false>, dim3(m->d / GBN, s.max_tiles), dim3(MM_THREADS), glds2, sr,
                t2.start, t2.stop, pr);
     e = hipGetLastError();
   }
@@ -833,9 +951,9 @@ extern "C" int lps_moe_prefill(const lps_moe_desc* m, float* x, int32_t T, int32
   // local experts and the shared one on the main stream
   if (e == hipSuccess && !rc) {
     Stamp t1 = timer_take(LPS_KIND_MOE_GEMM1), t2 = timer_take(LPS_KIND_MOE_GEMM2);
-    LPS_LAUNCH(k_pf_gemm<true>, dim3(m->ff / (GBN / 2), s.max_tiles), dim3(GEMM_THREADS), glds, st,
+    LPS_LAUNCH(k_pf_gemm<true>, dim3(m->ff / (GBN / 2), s.max_tiles), dim3(MM_THREADS), glds, st,
                t1.start, t1.stop, p);
-    LPS_LAUNCH(k_pf_gemm<false>, dim3(m->d / GBN, s.max_tiles), dim3(GEMM_THREADS), glds2, st,
+    LPS_LAUNCH(k_pf_gemm<false>, dim3(m->d / GBN, s.max_tiles), dim3(MM_THREADS), glds2, st,
                t2.start, t2.stop, p);
     e = hipGetLastError();
   }
