@@ -36,13 +36,12 @@
 #include "dev.h"
 #include "gemv_core.h"
 #include "internal.h"
+#include "mm_core.h"
 
 #include <cmath>
 
 namespace lps {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int PF_TOK = 8;      // tokens per routing tile
 constexpr int PF_MAXE = 64;    // experts the tile router is built for
@@ -428,66 +427,11 @@ __global__ __launch_bounds__(WAVE) void k_pf_tiles(PfP p) {
 
 // ---- 4/5. grouped GEMM on MFMA -----------------------------------------------------------
 // C[m, n] = sum_k A[m, k] B[n, k]: A rows are gathered activation rows (bf16), B
-// rows weight rows (bf16, K contiguous).  A 256 x 256 tile per workgroup of four
-// waves (2 x 2, one per SIMD), each wave 128 x 128 as 4 x 4 MFMA 32x32x16 blocks:
-// per 16-deep sub-step a wave reads 8 KiB of operands from LDS for 16 products,
-// half a KiB per product (a 128 x 64 wave tile reads three quarters), so the LDS
-// reads stay below the matrix cores' time.
-// The operands go from global memory straight into LDS (buffer loads with the LDS
-// as destination: no registers, no LDS store instructions) in K steps of MM_BK,
-// through rings of MM_SA stages for A and MM_SB for B: a step's loads go out
-// MM_SA - 1 (A) and MM_SB - 1 (B) steps before it is multiplied.  A staged row is
-// one step of K (whole 128-byte lines at MM_BK = 64); its 16-byte k chunk c sits
-// at slot c ^ swz(r), so the 16 lanes of each ds_read_b128 phase (16 consecutive
-// rows, one chunk) fall on all 64 banks.
-// Step t: read sub-step 1.. operands while multiplying the previous ones; once the
-// last sub-step's reads are done, wait for this wave's loads of step t + 1; one
-// barrier (every wave has read step t's stages, every wave's loads of step t + 1
-// have landed); load B of step t + MM_SB and A of step t + MM_SA into the freed
-// stages, read step t + 1's first sub-step, multiply the last one.  The last
-// steps' loads repeat the last step into stages that are not read again.
-#ifndef LPS_MM_BK
-#define LPS_MM_BK 64
-#endif
-#ifndef LPS_MM_SA
-#define LPS_MM_SA 3
-#endif
-#ifndef LPS_MM_SB
-#define LPS_MM_SB 2
-#endif
-constexpr int MM_THREADS = 256;
-constexpr int MM_BK = LPS_MM_BK;             // K per step
-constexpr int MM_SA = LPS_MM_SA, MM_SB = LPS_MM_SB;
-constexpr int MM_NS = MM_BK / 16;            // sub-steps per step
-constexpr int MM_CH = MM_BK / 8;             // 16-byte chunks per staged row
-constexpr int MM_ROWB = MM_BK * 2;           // bytes of a staged row
-constexpr int MM_OPB = GM * MM_ROWB;         // bytes per operand stage
-constexpr int MM_RPI = 64 / MM_CH;           // staged rows per load instruction
-constexpr int MM_NI = 64 / MM_RPI;           // load instructions per wave, operand and step
-constexpr int MM_LDS = (MM_SA + MM_SB) * MM_OPB;
-static_assert(GM == 256 && GBN == 256, "the staged tile is 256 x 256");
-static_assert((MM_BK == 32 || MM_BK == 64) && MM_SA == MM_SB + 1 && MM_SB >= 2, "staging shape");
-static_assert(MM_LDS <= 160 * 1024, "staging exceeds the LDS");
-// Load order: during step t the A loads of step t + MM_SA - 1 (into the A stage step
-// t - 1 freed), spread over the step's sub-steps; after step t's barrier the B loads
-// of step t + MM_SB (into the B stage step t freed).  Loads return in order, so at
-// step t's wait (A and B of step t + 1 landed) the loads issued after B of step
-// t + 1 may still be out: step t's A and MM_SB - 2 steps of A and B.
-constexpr int MM_VM_MID = MM_NI + (MM_SB - 2) * 2 * MM_NI;
-constexpr int MM_VM_PRO = (MM_SB - 1) * 2 * MM_NI;
-static_assert(MM_VM_PRO < 64 && MM_VM_MID < 64, "vmcnt range");
-
-// slot of chunk c in staged row r is c ^ mm_swz(r).  The LDS has 64 four-byte banks
-// and serves a ds_read_b128 16 lanes (256 bytes) at a time; an operand read is 16
-// consecutive rows at one chunk, so the 16 rows must cover all 16 16-byte bank
-// groups: 128-byte rows (two per 256 bytes) alternate halves and need 8 slots among
-// same-parity rows, 64-byte rows 4 slots among rows equal mod 4.
-__device__ __forceinline__ int mm_swz(int r) { return MM_CH == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
-// s_waitcnt immediates (gfx9 encoding): vmcnt bits [3:0] and [15:14], lgkmcnt [11:8]
-constexpr int mm_wait(int vm, int lgkm) {
-  return (vm & 15) | (7 << 4) | ((lgkm & 15) << 8) | ((vm >> 4) << 14);
-}
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
+// rows weight rows (bf16, K contiguous).  A 256 x 256 tile per workgroup, the main
+// loop of mm_core.h (four waves of 128 x 128, LDS DMA staging); this kernel maps the
+// tile's rows (the expert's token list, its rows of the SwiGLU buffer, its weight
+// rows) and applies the epilogue.
+static_assert(GM == MM_TILE && GBN == MM_TILE, "the grouped GEMM tile is the core's");
 
 template <bool FIRST>
 __global__ __launch_bounds__(MM_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -502,8 +446,6 @@ void k_pf_gemm(PfP p) {
   const int n0 = FIRST ? blockIdx.x * (GBN / 2) : blockIdx.x * GBN;
   extern __shared__ __attribute__((aligned(16))) uint16_t gsm[];
   char* lds = reinterpret_cast<char*>(gsm);
-  char* ldsA = lds;                          // [MM_SA][GM][MM_ROWB]
-  char* ldsB = lds + MM_SA * MM_OPB;         // [MM_SB][GBN][MM_ROWB]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -534,14 +476,11 @@ void k_pf_gemm(PfP p) {
       }
     }
   }
-  // the rows this lane stages: rows 64 wv + MM_RPI j + lane / MM_CH (j < MM_NI) of
-  // A and of B, k chunk (lane % MM_CH) ^ swz(row) into slot lane % MM_CH
-  const int lrow = lane / MM_CH;
   int aoff[MM_NI], boff[MM_NI];
 #pragma unroll
   for (int j = 0; j < MM_NI; ++j) {
-    const int sr = 64 * wv + MM_RPI * j + lrow;
-    const int gch = (lane % MM_CH) ^ mm_swz(sr);
+    const int sr = mm_stage_row(wv, lane, j);
+    const int gch = mm_stage_chunk(sr, lane);
     const int r = m0 + sr;
     const int rr = r < cnt ? r : m0;          // rows past the list repeat a valid row
     if (FIRST) {
@@ -561,10 +500,6 @@ void k_pf_gemm(PfP p) {
     }
     boff[j] = (wrow * K + 8 * gch) * 2;
   }
-  // operand reads: A rows 128 wm + 32 i + lane % 32, B rows 128 wn + 32 j + lane % 32
-  // (their swizzle is lane % 32's); sub-step ks takes k chunk 2 ks + lane / 32
-  const int fr = lane & 31, fsw = mm_swz(fr), fh = lane >> 5;
-  const int ard = (128 * wm + fr) * MM_ROWB, brd = (128 * wn + fr) * MM_ROWB;
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -573,111 +508,9 @@ void k_pf_gemm(PfP p) {
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  // A rows (reused by the other column tiles) cached, weight rows streamed
+  mm_tile<0, 2>(ares, bres, aoff, boff, K / MM_BK, lds, acc);
 
-#define MM_DMA_B(S, T)                                                                         \
-  _Pragma("unroll") for (int j = 0; j < MM_NI; ++j)                                            \
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                  \
-        bres, (lds_ptr_t)(ldsB + (S) * MM_OPB + (64 * wv + MM_RPI * j) * MM_ROWB), 16, boff[j], \
-        (T) * MM_ROWB, 0, 2);
-#define MM_DMA_A1(S, T, J)                                                                     \
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                    \
-      ares, (lds_ptr_t)(ldsA + (S) * MM_OPB + (64 * wv + MM_RPI * (J)) * MM_ROWB), 16, aoff[J], \
-      (T) * MM_ROWB, 0, 0);
-#define MM_READ(R, SA_, SB_, KS)                                                               \
-  {                                                                                            \
-    const int sl = 16 * ((2 * (KS) + fh) ^ fsw);                                               \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                            \
-      R[i] = *reinterpret_cast<const bf16x8*>(ldsA + (SA_) * MM_OPB + ard + 32 * i * MM_ROWB + sl); \
-      R[4 + i] = *reinterpret_cast<const bf16x8*>(ldsB + (SB_) * MM_OPB + brd + 32 * i * MM_ROWB + sl); \
-    }                                                                                          \
-  }
-#define MM_MMA(R)                                                                              \
-  _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                              \
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(R[i], R[4 + j], acc[i][j], 0, 0, 0);
-
-  const int nk = K / MM_BK;                  // >= 2 (K is a multiple of 128)
-  // prologue: the loads of steps before 0 in the loop's order (during step s the A
-  // loads of step s + MM_SB, after it the B loads of the same step, s = -MM_SB .. -1);
-  // with fewer steps than stages the extra stages get the last step again and are
-  // never read
-#pragma unroll
-  for (int s = 0; s < MM_SB; ++s) {
-#pragma unroll
-    for (int j = 0; j < MM_NI; ++j) MM_DMA_A1(s, min(s, nk - 1), j)
-    MM_DMA_B(s, min(s, nk - 1))
-  }
-  bf16x8 r0[8], r1[8];
-  __builtin_amdgcn_s_waitcnt(mm_wait(MM_VM_PRO, 15));   // this wave's loads of step 0
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  MM_READ(r0, 0, 0, 0)
-  int sa = 0, sb = 0;                        // stages of step kt
-  // With one wave per SIMD the wave's own instruction order decides what overlaps
-  // the products, and its loads queue for the CU's one address unit: each
-  // sub-step's 16 products go out one by one with the next sub-step's 8 operand
-  // reads between the first eight (their LDS latency is covered by the last eight)
-  // and a share of the A loads between the last eight; after the barrier the B
-  // loads go between the last sub-step's products.
-#define MM_PACE_READS()                                                                        \
-  _Pragma("unroll") for (int q = 0; q < 8; ++q) {                                              \
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                         \
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                         \
-  }
-  int fa = MM_SA - 1;                        // the A stage freed by the previous step
-  for (int kt = 0; kt < nk; ++kt) {
-    const int ta = min(kt + MM_SA - 1, nk - 1);   // A loads of this step's spread
-    // sub-step KS: read sub-step KS into RN, issue A loads [J0, J1), multiply RC
-#define MM_SUB(KS, RN, RC)                                                                     \
-    {                                                                                          \
-      constexpr int J0 = ((KS) - 1) * MM_NI / (MM_NS - 1), J1 = (KS) * MM_NI / (MM_NS - 1);    \
-      MM_READ(RN, sa, sb, KS)                                                                  \
-      _Pragma("unroll") for (int j = J0; j < J1; ++j) MM_DMA_A1(fa, ta, j)                     \
-      MM_MMA(RC)                                                                               \
-      MM_PACE_READS()                                                                          \
-      _Pragma("unroll") for (int q = 0; q < J1 - J0; ++q) {                                    \
-        __builtin_amdgcn_sched_group_barrier(0x008, 8 / (J1 - J0), 0);                         \
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                     \
-      }                                                                                        \
-      __builtin_amdgcn_sched_group_barrier(0x008, 8 - (8 / (J1 - J0)) * (J1 - J0) + 0, 0);     \
-      __builtin_amdgcn_sched_barrier(0);                                                       \
-    }
-    MM_SUB(1, r1, r0)
-    if constexpr (MM_NS == 4) {
-      MM_SUB(2, r0, r1)
-      MM_SUB(3, r1, r0)
-    }
-#undef MM_SUB
-    // the reads above are done and this wave's loads of step kt + 1 have landed
-    __builtin_amdgcn_s_waitcnt(mm_wait(MM_VM_MID, 0));
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    const int na = sa + 1 == MM_SA ? 0 : sa + 1, nb = sb + 1 == MM_SB ? 0 : sb + 1;
-    MM_READ(r0, na, nb, 0)
-    MM_DMA_B(sb, min(kt + MM_SB, nk - 1))
-    MM_MMA(r1)                               // MM_NS is even: the last sub-step is in r1
-    MM_PACE_READS()
-#pragma unroll
-    for (int q = 0; q < MM_NI; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 8 / MM_NI, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    fa = sa;
-    sa = na;
-    sb = nb;
-  }
-#undef MM_PACE_READS
-#undef MM_DMA_A1
-#undef MM_DMA_B
-#undef MM_READ
-#undef MM_MMA
-  // the loads still out only repeat the last step into unread stages: drain them
-  // before the stages are reused below
-  __builtin_amdgcn_s_waitcnt(mm_wait(0, 0));
-  __syncthreads();
   // epilogue: acc[i][j][r] is C[128 wm + 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4][128 wn + 32 j + lane % 32]
   if constexpr (FIRST) {
     // blocks j = 0, 2 hold gate and 1, 3 up of outputs 64 wn + 32 (j / 2) + lane % 32;

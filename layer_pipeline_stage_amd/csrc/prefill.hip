@@ -18,15 +18,14 @@
 // model whose prompts run through the stages.
 #include "dev.h"
 #include "internal.h"
+#include "mm_core.h"
 
 #include <cmath>
 #include <type_traits>
 
 namespace lps {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // ---- 1/6. per-row RMSNorm -> bf16 -------------------------------------------------------
@@ -69,19 +68,16 @@ __global__ __launch_bounds__(256) void k_pf_rows_norm(const float* x, const floa
 
 // ---- 2/5/7/8. dense GEMM on the matrix cores -----------------------------------------------
 // C[m, n] = sum_k A[m, k] B[n, k]; A [T, K] bf16 rows, B [N, K] bf16 weight rows.  A
-// 256 x 256 tile per workgroup of 8 waves (2 x 4), each wave 128 x 64 as 4 x 2 MFMA
-// 32x32x16 blocks; K in steps of 64 through two LDS buffers (rows padded to a
-// 144-byte stride), the global loads two steps ahead in two register sets, one
-// barrier per step, steps taken in pairs (K % 128 == 0).  Rows past T repeat row
-// T - 1 (valid memory, never stored).  Epilogues:
+// 256 x 256 tile per workgroup, the main loop of mm_core.h (four waves of 128 x 128,
+// LDS DMA staging, K % 128 == 0).  Rows past T repeat row T - 1 (valid memory, never
+// stored).  Epilogues:
 //   GE_STORE   out[m, n] = C            (f32)
 //   GE_ADD     out[m, n] += C           (f32, the residual)
 //   GE_SWIGLU  out[m, j] = bf16(silu(C[m, j]) * C[m, ff + j]): a workgroup takes
-//              128 outputs, its B rows are 32 gate rows then the 32 matching up
-//              rows per wave column, so both land in the same lanes.
+//              128 outputs; per wave column its staged B rows alternate blocks of 32
+//              gate rows and the 32 matching up rows, so both land in the same lanes.
 enum { GE_STORE = 0, GE_ADD = 1, GE_SWIGLU = 2 };
-constexpr int DM = 256, DN = 256, DK = 64, DKP = DK + 8;
-constexpr int DG_THREADS = 512;
+constexpr int DM = MM_TILE, DN = MM_TILE;
 
 struct DgP {
   const uint16_t* a;
@@ -91,116 +87,73 @@ struct DgP {
 };
 
 template <int EPI>
-__global__ __launch_bounds__(DG_THREADS) void k_dense_gemm(DgP p) {
-  constexpr int NJ = 4;
+__global__ __launch_bounds__(MM_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_dense_gemm(DgP p) {
   const int m0 = blockIdx.y * DM;
   const int n0 = EPI == GE_SWIGLU ? blockIdx.x * (DN / 2) : blockIdx.x * DN;
   const int K = p.K;
   extern __shared__ __attribute__((aligned(16))) uint16_t dsm[];
-  uint16_t* As0 = dsm;
-  uint16_t* Bs0 = As0 + DM * DKP;
-  uint16_t* As1 = Bs0 + DN * DKP;
-  uint16_t* Bs1 = As1 + DM * DKP;
-
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid / 64;
-  const int wm = wv >> 2, wn = wv & 3;
-  const int scol = (tid & 7) * 8;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int wm = wv >> 1, wn = wv & 1;
   const long long abytes = (long long)p.T * K * 2;
   const long long bbytes = (long long)(EPI == GE_SWIGLU ? 2 * p.N : p.N) * K * 2;
   const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(p.a), (short)0, (int)abytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t bres = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(p.b), (short)0, (int)bbytes, 0x00020000);
-  int aoff[NJ], boff[NJ];
+  int aoff[MM_NI], boff[MM_NI];
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int sr = (tid >> 3) + 64 * j;
+  for (int j = 0; j < MM_NI; ++j) {
+    const int sr = mm_stage_row(wv, lane, j);
+    const int gch = mm_stage_chunk(sr, lane);
     const int r = min(m0 + sr, p.T - 1);
-    aoff[j] = (r * K + scol) * 2;
+    aoff[j] = (r * K + 8 * gch) * 2;
     int wrow;
     if constexpr (EPI == GE_SWIGLU) {
-      const int wc = sr >> 6, jj = (sr >> 5) & 1, cc = sr & 31;
-      wrow = (jj ? p.N : 0) + n0 + 32 * wc + cc;
+      const int wc = sr >> 7, jb = (sr >> 5) & 3, cc = sr & 31;
+      wrow = ((jb & 1) ? p.N : 0) + n0 + 64 * wc + 32 * (jb >> 1) + cc;
     } else {
       wrow = n0 + sr;
     }
-    boff[j] = (wrow * K + scol) * 2;
+    boff[j] = (wrow * K + 8 * gch) * 2;
   }
-  const int soff = (tid >> 3) * DKP + scol;
 
-  f32x16 acc[4][2];
+  f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  // chunk rows (reused by the other column tiles) cached, weight rows streamed
+  mm_tile<0, 2>(ares, bres, aoff, boff, K / MM_BK, reinterpret_cast<char*>(dsm), acc);
 
-#define DG_LOAD(RA, RB, K0)                                                                       \
-  _Pragma("unroll") for (int j = 0; j < NJ; ++j) {                                                \
-    RA[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ares, aoff[j], 2 * (K0), 0)); \
-    RB[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(bres, boff[j], 2 * (K0), 2)); \
-  }
-#define DG_STORE(RA, RB, AS, BS)                                         \
-  _Pragma("unroll") for (int j = 0; j < NJ; ++j) {                       \
-    *reinterpret_cast<u32x4*>(AS + soff + 64 * j * DKP) = RA[j];         \
-    *reinterpret_cast<u32x4*>(BS + soff + 64 * j * DKP) = RB[j];         \
-  }
-#define DG_MMA(AS, BS)                                                                          \
-  _Pragma("unroll") for (int ks = 0; ks < DK / 16; ++ks) {                                       \
-    bf16x8 a[4], b[2];                                                                           \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                \
-      a[i] = *reinterpret_cast<const bf16x8*>(AS + (128 * wm + 32 * i + (lane & 31)) * DKP +      \
-                                              16 * ks + 8 * (lane >> 5));                        \
-    _Pragma("unroll") for (int j = 0; j < 2; ++j)                                                \
-      b[j] = *reinterpret_cast<const bf16x8*>(BS + (64 * wn + 32 * j + (lane & 31)) * DKP +       \
-                                              16 * ks + 8 * (lane >> 5));                        \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                \
-      _Pragma("unroll") for (int j = 0; j < 2; ++j)                                              \
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);     \
-  }
-
-  const int nk = K / DK;
-  u32x4 ra0[NJ], rb0[NJ], ra1[NJ], rb1[NJ];
-  DG_LOAD(ra0, rb0, 0)
-  DG_LOAD(ra1, rb1, DK)
-  DG_STORE(ra0, rb0, As0, Bs0)
-  __syncthreads();
-  for (int kt = 0; kt < nk; kt += 2) {
-    const int s2 = min(kt + 2, nk - 1), s3 = min(kt + 3, nk - 1);
-    DG_LOAD(ra0, rb0, s2 * DK)
-    DG_MMA(As0, Bs0)
-    DG_STORE(ra1, rb1, As1, Bs1)
-    __syncthreads();
-    DG_LOAD(ra1, rb1, s3 * DK)
-    DG_MMA(As1, Bs1)
-    DG_STORE(ra0, rb0, As0, Bs0)
-    __syncthreads();
-  }
-#undef DG_LOAD
-#undef DG_STORE
-#undef DG_MMA
-  // acc[i][j][r] is C[128 wm + 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4][col(j)]
+  // acc[i][j][r] is C[128 wm + 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4][128 wn + 32 j + lane % 32]
   if constexpr (EPI == GE_SWIGLU) {
-    // the bf16 tile [DM][DN / 2] is assembled in LDS (free: every wave passed the
-    // loop's last barrier after its last operand read) and leaves as whole 16-byte
-    // pieces of its rows (2-byte stores from the accumulator layout covered half a
-    // cache line per half-wave)
+    // blocks j = 0, 2 hold gate and 1, 3 up of outputs 64 wn + 32 (j / 2) + lane % 32;
+    // the bf16 tile [DM][DN / 2] is assembled in LDS (free once the main loop
+    // returns) and leaves as whole 16-byte pieces of its rows (2-byte stores from
+    // the accumulator layout covered half a cache line per half-wave)
     constexpr int OP = DN / 2 + 8;            // row pitch (bf16): rows 4 apart on other banks
     uint16_t* ot = dsm;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 128 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        ot[row * OP + 32 * wn + (lane & 31)] = f32_to_bf16(silu(acc[i][0][r]) * acc[i][1][r]);
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 128 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          ot[row * OP + 64 * wn + 32 * h + (lane & 31)] =
+              f32_to_bf16(silu_fast(acc[i][2 * h][r]) * acc[i][2 * h + 1][r]);
+        }
       }
     }
     __syncthreads();
     constexpr int CPR = DN / 2 / 8;           // 16-byte pieces per row
 #pragma unroll
-    for (int q = 0; q < DM * CPR / DG_THREADS; ++q) {
-      const int c = tid + q * DG_THREADS;
+    for (int q = 0; q < DM * CPR / MM_THREADS; ++q) {
+      const int c = tid + q * MM_THREADS;
       const int row = c / CPR, c8 = (c % CPR) * 8;
       if (m0 + row < p.T)
         *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.out) + (long long)(m0 + row) * p.N + n0 + c8) =
@@ -211,14 +164,14 @@ __global__ __launch_bounds__(DG_THREADS) void k_dense_gemm(DgP p) {
     for (int i = 0; i < 4; ++i) {
       // GE_ADD: the 16 rows' residual values of this block all in flight at once,
       // then the sums (one round trip per block instead of one per row)
-      float old[16][2];
+      float old[16][4];
       if constexpr (EPI == GE_ADD) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = m0 + 128 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int col = n0 + 64 * wn + 32 * j + (lane & 31);
+          for (int j = 0; j < 4; ++j) {
+            const int col = n0 + 128 * wn + 32 * j + (lane & 31);
             old[r][j] = m < p.T ? static_cast<const float*>(p.out)[(long long)m * p.N + col] : 0.f;
           }
         }
@@ -228,8 +181,8 @@ __global__ __launch_bounds__(DG_THREADS) void k_dense_gemm(DgP p) {
         const int m = m0 + 128 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         if (m < p.T) {
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int col = n0 + 64 * wn + 32 * j + (lane & 31);
+          for (int j = 0; j < 4; ++j) {
+            const int col = n0 + 128 * wn + 32 * j + (lane & 31);
             float* o = static_cast<float*>(p.out) + (long long)m * p.N + col;
             if constexpr (EPI == GE_ADD) *o = old[r][j] + acc[i][j][r];
             else *o = acc[i][j][r];
@@ -634,12 +587,12 @@ static dim3 rows_grid(long long n) {
 
 template <int EPI>
 static int gemm(const uint16_t* a, const uint16_t* b, void* out, int T, int N, int K, hipStream_t st) {
-  const size_t lds = size_t(2) * (DM + DN) * DKP * 2;
+  const size_t lds = MM_LDS;
   int rc = ensure_lds((const void*)k_dense_gemm<EPI>, lds);
   if (rc) return rc;
   DgP p{a, b, out, T, N, K};
   const int nt = EPI == GE_SWIGLU ? N / (DN / 2) : N / DN;
-  hipLaunchKernelGGL((k_dense_gemm<EPI>), dim3(nt, (T + DM - 1) / DM), dim3(DG_THREADS), lds, st, p);
+  hipLaunchKernelGGL((k_dense_gemm<EPI>), dim3(nt, (T + DM - 1) / DM), dim3(MM_THREADS), lds, st, p);
   LPS_HIP(hipGetLastError());
   return LPS_OK;
 }
