@@ -936,8 +936,10 @@ int lps_boundary_create(int32_t n_elems, float* slot0, float* slot1, lps_boundar
     b->tx_recorded[k] = b->rx_recorded[k] = false;
     b->tx_stream[k] = b->rx_stream[k] = nullptr;
     b->tx_cap[k] = b->rx_cap[k] = 0;
-    hipError_t e1 = hipEventCreateWithFlags(&b->ev_tx[k], hipEventDisableTiming);
-    hipError_t e2 = hipEventCreateWithFlags(&b->ev_rx[k], hipEventDisableTiming);
+    // device-side ordering between the stage streams only: no system-scope fence
+    // (an L2 writeback for the host) when they are recorded
+    hipError_t e1 = hipEventCreateWithFlags(&b->ev_tx[k], hipEventDisableTiming | hipEventDisableSystemFence);
+    hipError_t e2 = hipEventCreateWithFlags(&b->ev_rx[k], hipEventDisableTiming | hipEventDisableSystemFence);
     if (e1 != hipSuccess || e2 != hipSuccess) {
       delete b;
       return fail(LPS_EHIP, "lps_boundary_create: hipEventCreate failed");
@@ -1096,7 +1098,10 @@ int lps_logits_defer(const float* logits, const int32_t* tok, int32_t vocab, voi
   *out = nullptr;
   hipStream_t ls = as_stream(last_stage), rb = as_stream(readback);
   hipEvent_t done = nullptr, drained = nullptr;
-  hipError_t e = hipEventCreateWithFlags(&done, hipEventDisableTiming);
+  // done orders the copies after the step on the device (no system-scope fence on
+  // the last stage's stream); drained is what the host waits on, with the fence that
+  // makes the copied bytes visible to it
+  hipError_t e = hipEventCreateWithFlags(&done, hipEventDisableTiming | hipEventDisableSystemFence);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&drained, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventRecord(done, ls);
   if (e == hipSuccess) e = hipStreamWaitEvent(rb, done, 0);

@@ -310,8 +310,9 @@ extern "C" int lps_moe_combine(float* out, const float* x, const float* shared,
               "lps_moe_combine: bo must not be shared, local or remote16 (they are read after bo is written)");
   hipStream_t sr = as_stream(s_remote), sm = as_stream(s_main);
   hipEvent_t start, done;
-  LPS_HIP(hipEventCreateWithFlags(&start, hipEventDisableTiming));
-  LPS_HIP(hipEventCreateWithFlags(&done, hipEventDisableTiming));
+  // device-side ordering between the two streams only: no system-scope fence
+  LPS_HIP(hipEventCreateWithFlags(&start, hipEventDisableTiming | hipEventDisableSystemFence));
+  LPS_HIP(hipEventCreateWithFlags(&done, hipEventDisableTiming | hipEventDisableSystemFence));
   // the remote stream may only overwrite bo once the main stream's earlier work
   // (which may still read bo or local) is done
   LPS_HIP(hipEventRecord(start, sm));

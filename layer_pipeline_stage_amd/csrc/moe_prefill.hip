@@ -730,7 +730,7 @@ extern "C" int lps_moe_prefill(const lps_moe_desc* m, float* x, int32_t T, int32
   if (rc) return rc;
   hipEvent_t ev[3];   // rows normed (main), tile lists built (main), remote experts done
   for (int i = 0; i < 3; ++i) {
-    if (hipEventCreateWithFlags(&ev[i], hipEventDisableTiming) != hipSuccess) {
+    if (hipEventCreateWithFlags(&ev[i], hipEventDisableTiming | hipEventDisableSystemFence) != hipSuccess) {
       for (int j = 0; j < i; ++j) (void)hipEventDestroy(ev[j]);
       return fail(LPS_EHIP, "lps_moe_prefill: hipEventCreate failed");
     }
