@@ -313,6 +313,26 @@ typedef struct lps_head_desc {
 size_t lps_head_scratch_bytes(const lps_head_desc* h);
 int lps_head_forward(const lps_head_desc* h, const float* x, float* logits, int32_t* tok_out,
                      void* scratch, size_t scratch_bytes, void* stream);
+/* The end of a replayed greedy step (ninfer "Multi-GPU: layer pipeline stages", How
+ * it works: the whole pass as one replayed graph) in three launches instead of
+ * lps_head_forward, lps_step_advance and the next step's lps_embed: the final
+ * RMSNorm and LM head into logits (dev [vocab] f32) as lps_head_forward; with
+ * s = state[1] (dev), the logits copied to logits_hist[s * vocab ..] when
+ * logits_hist is given and s < hist_cap; then one launch takes the lowest-index
+ * argmax (vocab when no finite maximum), stores it to tok_hist[s] (s < hist_cap),
+ * picks the next input id (feed[s + 1] while fed ids remain, else the argmax; to
+ * *tok_cur when tok_cur is not NULL), writes that id's row of the embedding table
+ * (dev, h->vocab rows of h->d values of embed_dtype, LPS_F32 or LPS_BF16; a NaN row
+ * for an id outside it, as lps_embed) to x_next (dev [d] f32; may be x, which the
+ * head has read by then), and advances
+ * the position (unless it would reach pos_limit: flag bit 0 of state[2]) and the
+ * step.  A run seeds x_next with lps_embed before its first replay.  Errors as
+ * lps_head_forward and lps_step_advance (LPS_EINVAL). */
+int lps_step_finish(const lps_head_desc* h, const float* x, float* logits, int32_t* state,
+                    int32_t pos_limit, const int32_t* feed, int32_t n_feed, int32_t* tok_hist,
+                    float* logits_hist, int32_t hist_cap, const void* embed, int32_t embed_dtype,
+                    float* x_next, int32_t* tok_cur, void* scratch, size_t scratch_bytes,
+                    void* stream);
 
 /* ---- step-level entry points (the pieces lps_layer_forward launches) ------ */
 /* A3: y = x / sqrt(mean(x^2) + eps) * g, all (dev) [d] f32. */

@@ -380,8 +380,9 @@ __device__ __forceinline__ bool argmax_better(float v, int j, float b, int ix) {
   if (b != b) return false;            // a NaN holds its place
   return v != v || v > b || (v == b && j < ix);
 }
-__global__ __launch_bounds__(1024) void k_argmax(const float* pval, const int* pidx, int n,
-                                                 int vocab, int* out) {
+// the lowest-index argmax over the head's per-wave partials (vocab when no finite
+// maximum), valid on thread 0 (the caller's block is 1024 threads; all of them call)
+__device__ __forceinline__ int argmax_partials(const float* pval, const int* pidx, int n, int vocab) {
   float b = -INFINITY;
   int ix = 0x7fffffff;
   for (int i = threadIdx.x; i < n; i += 1024) {
@@ -403,7 +404,52 @@ __global__ __launch_bounds__(1024) void k_argmax(const float* pval, const int* p
   if (threadIdx.x == 0) {
     for (int i = 1; i < 16; ++i)
       if (argmax_better(bv[i], bi[i], b, ix)) { b = bv[i]; ix = bi[i]; }
-    *out = (b != b || ix == 0x7fffffff) ? vocab : ix;
+    return (b != b || ix == 0x7fffffff) ? vocab : ix;
+  }
+  return 0;
+}
+
+__global__ __launch_bounds__(1024) void k_argmax(const float* pval, const int* pidx, int n,
+                                                 int vocab, int* out) {
+  const int a = argmax_partials(pval, pidx, n, vocab);
+  if (threadIdx.x == 0) *out = a;
+}
+
+// The token chain at the end of a replayed step (lps_step_finish), one launch: the
+// argmax a; with s = state[1]: tok_hist[s] = a, the next input id t (feed[s + 1]
+// while fed ids remain, else a) to *tok_cur and its embedding row to x_next (NaN for
+// an id outside the table), then the position (unless it reached pos_limit: flag bit
+// 0) and the step advance.  The state and the next id's feed entry are read before
+// the partials are reduced, so their round trips overlap.
+template <int WT>
+__global__ __launch_bounds__(1024) void k_step_finish(const float* pval, const int* pidx, int n,
+                                                      int vocab, int32_t* state, int pos_limit,
+                                                      const int32_t* feed, int n_feed,
+                                                      int32_t* tok_hist, int cap, int32_t* tok_cur,
+                                                      const void* table, int d, float* x_next) {
+  const int s = state[1], pos = state[0];
+  const bool use_feed = s + 1 >= 0 && s + 1 < n_feed;
+  const int fed = use_feed ? feed[s + 1] : -1;
+  const int a = argmax_partials(pval, pidx, n, vocab);
+  __shared__ int nxt;
+  if (threadIdx.x == 0) {
+    if (tok_hist && s >= 0 && s < cap) tok_hist[s] = a;
+    const int t = use_feed ? fed : a;
+    if (tok_cur) *tok_cur = t;
+    nxt = t;
+    if (pos + 1 < pos_limit) state[0] = pos + 1;
+    else state[2] = state[2] | 1;
+    state[1] = s + 1;
+  }
+  __syncthreads();
+  const int t = nxt;
+  const bool ok = t >= 0 && t < vocab;
+  for (int i = threadIdx.x; i < d; i += 1024) {
+    float v;
+    if (!ok) v = __uint_as_float(0x7FC00000u);
+    else if (WT == LPS_F32) v = static_cast<const float*>(table)[(long long)t * d + i];
+    else v = bf16_to_f32(static_cast<const uint16_t*>(table)[(long long)t * d + i]);
+    x_next[i] = v;
   }
 }
 
@@ -600,6 +646,41 @@ int launch_head(const lps_head_desc* h, const float* x, float* logits, int32_t* 
   if (rc) return rc;
   LPS_LAUNCH(k_argmax, dim3(1), dim3(1024), 0, st, nullptr, sp.stop, p.pval, p.pidx, waves,
              h->vocab, tok);
+  LPS_HIP(hipGetLastError());
+  return LPS_OK;
+}
+
+int launch_step_finish(const lps_head_desc* h, const float* x, float* logits, int32_t* state,
+                       int32_t pos_limit, const int32_t* feed, int32_t n_feed, int32_t* tok_hist,
+                       float* logits_hist, int32_t hist_cap, const void* embed, int32_t embed_dtype,
+                       float* x_next, int32_t* tok_cur, void* scratch, hipStream_t st, Stamp sp) {
+  GemvP p{};
+  p.w = static_cast<const uint8_t*>(h->w_lm);
+  p.N = h->vocab;
+  p.K = h->d;
+  p.x = x;
+  p.g = h->g_out;
+  p.eps = h->eps;
+  p.y = logits;
+  p.units = (h->vocab + 1) / 2;
+  set_rows(p, h->wdtype, h->d);
+  char* sc = static_cast<char*>(scratch);
+  p.pval = reinterpret_cast<float*>(sc);
+  p.pidx = reinterpret_cast<int*>(sc + align256(head_waves_max() * 4));
+  int waves = 0;
+  int rc = launch_wt<EPI_LOGITS, true>(h->wdtype, p, st, Stamp{sp.start, nullptr}, &waves);
+  if (rc) return rc;
+  // the history copy reads the step before the finish launch advances it
+  rc = launch_step_advance_hist(state, logits, h->vocab, logits_hist, hist_cap, st);
+  if (rc) return rc;
+  if (embed_dtype == LPS_F32)
+    LPS_LAUNCH(k_step_finish<LPS_F32>, dim3(1), dim3(1024), 0, st, nullptr, sp.stop, p.pval, p.pidx,
+               waves, h->vocab, state, pos_limit, feed, n_feed, tok_hist, hist_cap, tok_cur, embed,
+               h->d, x_next);
+  else
+    LPS_LAUNCH(k_step_finish<LPS_BF16>, dim3(1), dim3(1024), 0, st, nullptr, sp.stop, p.pval, p.pidx,
+               waves, h->vocab, state, pos_limit, feed, n_feed, tok_hist, hist_cap, tok_cur, embed,
+               h->d, x_next);
   LPS_HIP(hipGetLastError());
   return LPS_OK;
 }

@@ -870,6 +870,35 @@ int lps_head_forward(const lps_head_desc* h, const float* x, float* logits, int3
                      timer_take(LPS_KIND_HEAD));
 }
 
+int lps_step_finish(const lps_head_desc* h, const float* x, float* logits, int32_t* state,
+                    int32_t pos_limit, const int32_t* feed, int32_t n_feed, int32_t* tok_hist,
+                    float* logits_hist, int32_t hist_cap, const void* embed, int32_t embed_dtype,
+                    float* x_next, int32_t* tok_cur, void* scratch, size_t scratch_bytes,
+                    void* stream) {
+  LPS_REQUIRE(h, LPS_EINVAL, "lps_step_finish: null head");
+  LPS_REQUIRE(h->d > 0 && h->vocab > 0, LPS_EINVAL, "lps_step_finish: d %d / vocab %d", h->d, h->vocab);
+  LPS_REQUIRE(h->wdtype == LPS_F32 || h->wdtype == LPS_BF16, LPS_EINVAL,
+              "lps_step_finish: wdtype %d (f32 or bf16)", h->wdtype);
+  LPS_REQUIRE(h->d % chunk_of(h->wdtype) == 0 && h->d <= 8192, LPS_EINVAL,
+              "lps_step_finish: d %d (a multiple of the weight chunk, at most 8192)", h->d);
+  LPS_REQUIRE(embed_dtype == LPS_F32 || embed_dtype == LPS_BF16, LPS_EINVAL,
+              "lps_step_finish: embed_dtype %d (f32 or bf16)", embed_dtype);
+  LPS_REQUIRE(h->g_out && h->w_lm && x && logits && state && embed && x_next && scratch, LPS_EINVAL,
+              "lps_step_finish: null pointer");
+  LPS_REQUIRE(aligned16(h->w_lm) && aligned16(h->g_out) && aligned16(x), LPS_EINVAL,
+              "lps_step_finish: weights, gain and x must be 16-byte aligned");
+  LPS_REQUIRE(pos_limit >= 1, LPS_EINVAL, "lps_step_finish: pos_limit %d < 1", pos_limit);
+  LPS_REQUIRE(n_feed >= 0 && (n_feed == 0 || feed), LPS_EINVAL,
+              "lps_step_finish: %d fed ids need a feed array", n_feed);
+  LPS_REQUIRE(hist_cap >= 0 && (hist_cap == 0 || tok_hist), LPS_EINVAL,
+              "lps_step_finish: a history of %d steps needs tok_hist", hist_cap);
+  LPS_REQUIRE(scratch_bytes >= head_scratch(h), LPS_EINVAL, "lps_step_finish: scratch %zu < %zu",
+              scratch_bytes, head_scratch(h));
+  return launch_step_finish(h, x, logits, state, pos_limit, feed, n_feed, tok_hist, logits_hist,
+                            hist_cap, embed, embed_dtype, x_next, tok_cur, scratch, as_stream(stream),
+                            timer_take(LPS_KIND_HEAD));
+}
+
 // ---- benchmark timer ----------------------------------------------------------------------
 int lps_timer_start(int32_t kind, int32_t capacity) {
   LPS_REQUIRE(kind >= LPS_KIND_QKV && kind <= LPS_KIND_MOE_GEMM2, LPS_EINVAL, "lps_timer_start: kind %d",

@@ -191,14 +191,21 @@ __global__ void k_step_advance(int32_t* state, int pos_limit, const int32_t* arg
   state[1] = s + 1;
 }
 
-int launch_step_advance(int32_t* state, int32_t pos_limit, const int32_t* argmax, int32_t* tok_cur,
-                        const int32_t* feed, int32_t n_feed, int32_t* tok_hist, int32_t hist_cap,
-                        const float* logits, int32_t vocab, float* logits_hist, hipStream_t st) {
+int launch_step_advance_hist(const int32_t* state, const float* logits, int32_t vocab,
+                             float* logits_hist, int32_t hist_cap, hipStream_t st) {
   if (logits_hist && hist_cap > 0) {
     hipLaunchKernelGGL(k_hist_logits, grid_for(vocab / 4 + 1), dim3(256), 0, st, state, logits,
                        vocab, logits_hist, hist_cap);
     LPS_HIP(hipGetLastError());
   }
+  return LPS_OK;
+}
+
+int launch_step_advance(int32_t* state, int32_t pos_limit, const int32_t* argmax, int32_t* tok_cur,
+                        const int32_t* feed, int32_t n_feed, int32_t* tok_hist, int32_t hist_cap,
+                        const float* logits, int32_t vocab, float* logits_hist, hipStream_t st) {
+  int rc = launch_step_advance_hist(state, logits, vocab, logits_hist, hist_cap, st);
+  if (rc) return rc;
   hipLaunchKernelGGL(k_step_advance, dim3(1), dim3(64), 0, st, state, pos_limit, argmax, tok_cur,
                      feed, n_feed, tok_hist, hist_cap);
   LPS_HIP(hipGetLastError());

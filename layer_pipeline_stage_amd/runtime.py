@@ -170,7 +170,6 @@ class DeviceDecoder:
             self.host_tok = torch.zeros(ring, dtype=torch.int32).pin_memory()
             # the graph mode's next input id, this step's argmax and logits
             self.g_tok = torch.zeros(1, dtype=torch.int32, device=dev)
-            self.g_arg = torch.zeros(1, dtype=torch.int32, device=dev)
             self.g_logits = torch.zeros(cfg.vocab, dtype=torch.float32, device=dev)
         # device step state of the graph mode: [pos, step, flags]
         self.g_state = torch.zeros(4, dtype=torch.int32, device=dev)
@@ -400,25 +399,24 @@ class DeviceDecoder:
         self.step_no += 1
 
     def capture_step(self, feed_dev, n_feed, tok_hist, logits_hist, hist_cap):
-        """Capture one decode step (embed, every stage and boundary, head,
-        step advance) into a graph on stage 0's stream; the other stage
-        streams fork into it through the boundary events and are joined back
-        at the end.  Returns the graph handle (lps_graph_destroy frees it)."""
+        """Capture one decode step (every stage and boundary, then the head and the
+        token chain in lps_step_finish, which also writes the next step's input row
+        into x[0]) into a graph on stage 0's stream; the other stage streams fork
+        into it through the boundary events and are joined back at the end.  The
+        run seeds x[0] before the first replay.  Returns the graph handle
+        (lps_graph_destroy frees it)."""
         cfg = self.cfg
         st0, stl = self.streams[0], self.streams[-1]
         torch.cuda.synchronize(self.device)
         lps.lps_graph_begin(sp(st0))
         g = C.c_void_p()
         try:
-            lps.lps_embed(ptr(self.embed), lps.DTYPES[cfg.wdtype], cfg.vocab, cfg.d,
-                          ptr(self.g_tok), ptr(self.x[0]), sp(st0))
             self._walk_dpos()
-            lps.lps_head_forward(C.byref(self.head), ptr(self.x[-1]), ptr(self.g_logits),
-                                 ptr(self.g_arg), ptr(self.head_scratch),
-                                 self.head_scratch.numel(), sp(stl))
-            lps.lps_step_advance(ptr(self.g_state), cfg.ctx_max, ptr(self.g_arg), ptr(self.g_tok),
-                                 feed_dev, n_feed, tok_hist, hist_cap, ptr(self.g_logits),
-                                 cfg.vocab, logits_hist, sp(stl))
+            lps.lps_step_finish(C.byref(self.head), ptr(self.x[-1]), ptr(self.g_logits),
+                                ptr(self.g_state), cfg.ctx_max, feed_dev, n_feed, tok_hist,
+                                logits_hist, hist_cap, ptr(self.embed), lps.DTYPES[cfg.wdtype],
+                                ptr(self.x[0]), ptr(self.g_tok), ptr(self.head_scratch),
+                                self.head_scratch.numel(), sp(stl))
         finally:
             join = (C.c_void_p * len(self.streams))(*[sp(s) for s in self.streams])
             lps.lps_graph_end(sp(st0), join, len(self.streams), C.byref(g))
@@ -464,6 +462,9 @@ class DeviceDecoder:
 
         try:
             st0 = self.streams[0]
+            # the first step's input row; every replay writes the next one
+            lps.lps_embed(ptr(self.embed), lps.DTYPES[cfg.wdtype], cfg.vocab, cfg.d,
+                          ptr(self.g_tok), ptr(self.x[0]), sp(st0))
             torch.cuda.synchronize(dev)
             if timer is not None:
                 timer(True)

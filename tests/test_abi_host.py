@@ -208,6 +208,28 @@ def test_graph_and_device_state_entry_points_refuse_bad_arguments(L):
         with pytest.raises(L.LpsError) as e:
             L.lps_step_advance(*a)
         assert e.value.code == L.LPS_EINVAL, a
+    # lps_step_finish: (h, x, logits, state, pos_limit, feed, n_feed, tok_hist,
+    # logits_hist, hist_cap, embed, embed_dtype, x_next, tok_cur, scratch, bytes, stream)
+    hd = L.HeadDesc()
+    hd.d, hd.vocab, hd.wdtype, hd.eps, hd.g_out, hd.w_lm = 256, 100, L.LPS_F32, 1e-6, 16, 16
+    ok = [C.byref(hd), 16, 16, 16, 8, None, 0, None, None, 0, 16, L.LPS_F32, 16, None, 16, 1 << 20, None]
+    bad_fin = [
+        (0, None),              # null head
+        (3, None),              # null state
+        (4, 0),                 # pos_limit < 1
+        (6, 3),                 # feed ids without feed
+        (9, 4),                 # history without tok_hist
+        (10, None),             # null embedding table
+        (11, L.LPS_MXFP4),      # embedding dtype
+        (12, None),             # null x_next
+        (15, 16),               # scratch below the head's
+    ]
+    for i, v in bad_fin:
+        a = list(ok)
+        a[i] = v
+        with pytest.raises(L.LpsError) as e:
+            L.lps_step_finish(*a)
+        assert e.value.code == L.LPS_EINVAL, (i, v)
     with pytest.raises(L.LpsError) as e:
         L.lps_graph_begin(None)                      # the null stream is not captured
     assert e.value.code == L.LPS_EINVAL

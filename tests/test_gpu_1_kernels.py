@@ -409,6 +409,59 @@ def test_head_argmax(L):
     assert torch.all(torch.isnan(out))
 
 
+def test_step_finish_equals_head_advance_embed(L):
+    """lps_step_finish (head, history copy, one launch for argmax + token chain +
+    next embedding row + advance) leaves exactly what lps_head_forward,
+    lps_step_advance and lps_embed leave: logits, history rows, token history, next
+    id, state and the next input row, for a fed step, a greedy step, the position
+    limit, and a step with no finite logit (a NaN row follows)."""
+    rng = np.random.default_rng(5)
+    V, d = 1003, 512
+    W = synth.bf16_bits((rng.standard_normal((V, d)) * 0.05).astype(np.float32))
+    E = synth.bf16_bits(rng.standard_normal((V, d)).astype(np.float32))
+    hd = L.HeadDesc()
+    Wd, gd, Ed = dev(W), dev(np.ones(d, np.float32)), dev(E)
+    hd.d, hd.vocab, hd.wdtype, hd.eps, hd.g_out, hd.w_lm = d, V, L.LPS_BF16, 1e-6, ptr(gd), ptr(Wd)
+    sb = L.lps_head_scratch_bytes(C.byref(hd))
+    feed = dev(np.array([5, 17, 400], np.int32))
+    cap = 4
+
+    def run(fused, x, state0, pos_limit, n_feed):
+        sc = torch.zeros(sb, dtype=torch.uint8, device=DEV)
+        lg = torch.zeros(V, dtype=torch.float32, device=DEV)
+        st = dev(np.array(state0, np.int32))
+        th = torch.full((cap,), -7, dtype=torch.int32, device=DEV)
+        lh = torch.full((cap, V), -7.0, dtype=torch.float32, device=DEV)
+        tok = torch.full((1,), -7, dtype=torch.int32, device=DEV)
+        xn = torch.full((d,), -7.0, dtype=torch.float32, device=DEV)
+        xd = dev(x)
+        if fused:
+            L.lps_step_finish(C.byref(hd), ptr(xd), ptr(lg), ptr(st), pos_limit, ptr(feed), n_feed,
+                              ptr(th), ptr(lh), cap, ptr(Ed), L.LPS_BF16, ptr(xn), ptr(tok),
+                              ptr(sc), sb, stream())
+        else:
+            am = torch.zeros(1, dtype=torch.int32, device=DEV)
+            L.lps_head_forward(C.byref(hd), ptr(xd), ptr(lg), ptr(am), ptr(sc), sb, stream())
+            L.lps_step_advance(ptr(st), pos_limit, ptr(am), ptr(tok), ptr(feed), n_feed, ptr(th),
+                               cap, ptr(lg), V, ptr(lh), stream())
+            L.lps_embed(ptr(Ed), L.LPS_BF16, V, d, ptr(tok), ptr(xn), stream())
+        torch.cuda.synchronize()
+        return [t.cpu().numpy() for t in (lg, st, th, lh, tok, xn)]
+
+    x = rng.standard_normal(d).astype(np.float32)
+    xnan = x.copy()
+    xnan[3] = np.nan
+    cases = [(x, [40, 0, 0, 0], 100, 3),      # fed: the next id is feed[1]
+             (x, [41, 2, 0, 0], 100, 3),      # past the feed: the argmax
+             (x, [99, 1, 0, 0], 100, 0),      # at the position limit: flag set, position kept
+             (xnan, [50, 3, 0, 0], 100, 0)]   # no finite logit: id V, a NaN row next
+    for xi, s0, lim, nf in cases:
+        a, b = run(True, xi, s0, lim, nf), run(False, xi, s0, lim, nf)
+        for u, v in zip(a, b):
+            assert np.array_equal(u, v, equal_nan=True), (s0, nf)
+    assert int(a[4][0]) == V and np.all(np.isnan(a[5]))
+
+
 @pytest.mark.parametrize("n16", [1, 4097, (1 << 22) + 333])
 def test_hbm_stream_read_touches_every_word(L, n16):
     """The read-bandwidth calibration reads every 16-byte chunk exactly once: the
