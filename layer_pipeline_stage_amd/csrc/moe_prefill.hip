@@ -208,7 +208,7 @@ __global__ __launch_bounds__(256) void k_pf_route(PfP p) {
 // 8 bf16 of Wr per global read).  The selection is the tile router's.  d % 32 == 0,
 // E <= 64, d <= 2300 (the 16 rows fit 144 KiB of LDS); wider rows take the tile router.
 constexpr int PF_MTOK = 16;
-constexpr int PF_MUNR = 4;   // 8-value B chunks per lane in flight
+constexpr int PF_MUNR = 8;   // router k steps per lane and batch (two batches in flight)
 constexpr int PF_MROW = 9;   // float4s per lane of a normed row (d <= 2304)
 
 __global__ __launch_bounds__(256) void k_pf_route_mx(PfP p) {
@@ -217,18 +217,25 @@ __global__ __launch_bounds__(256) void k_pf_route_mx(PfP p) {
   const int t0 = blockIdx.x * PF_MTOK;
   const int lane = threadIdx.x & 63, wv = threadIdx.x / 64;
   const int d = p.d, dp = d + 4;
-  for (int q = 0; q < 4; ++q) {            // each wave normalises four rows
-    const int r = wv * 4 + q, t = t0 + r;
-    float* h = hs + r * dp;
-    // the row's float4s, all in flight at once (rows past T are zero); the sum of
-    // squares and the scaling visit them in the order the tile router does
-    f32x4 v[PF_MROW];
+  // each wave normalises four rows; the four rows' float4s all go out at once (rows
+  // past T are zero)
+  f32x4 vq[4][PF_MROW];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int t = t0 + wv * 4 + q;
 #pragma unroll
     for (int i = 0; i < PF_MROW; ++i) {
       const int c = lane * 4 + 256 * i;
-      v[i] = (t < p.T && c < d) ? *reinterpret_cast<const f32x4*>(p.x + (long long)t * d + c)
-                                : f32x4{0.f, 0.f, 0.f, 0.f};
+      vq[q][i] = (t < p.T && c < d) ? *reinterpret_cast<const f32x4*>(p.x + (long long)t * d + c)
+                                    : f32x4{0.f, 0.f, 0.f, 0.f};
     }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = wv * 4 + q, t = t0 + r;
+    float* h = hs + r * dp;
+    // the sum of squares and the scaling visit the row in the order the tile router does
+    f32x4* v = vq[q];
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < PF_MROW; ++i) ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
@@ -251,37 +258,60 @@ __global__ __launch_bounds__(256) void k_pf_route_mx(PfP p) {
     }
   }
   __syncthreads();
+  // logits[t, e] = sum_k h[t, k] Wr[e, k] on v_mfma_f32_16x16x32_bf16: wave wv takes
+  // experts 16 wv .. 16 wv + 15 as columns, the 16 tokens as rows; lane (n, g) supplies
+  // token n's and expert 16 wv + n's values at k = 32 s + 8 g .. + 7 for step s.  The
+  // f32 row values enter as three bf16 parts (hi = the top 8 significant bits, mid the
+  // next 8, lo the rest: hi + mid + lo is the value exactly, each part's product with a
+  // bf16 weight is exact in f32), so the sum is an f32 dot product in another order.
   const int n = lane & 15, g = lane >> 4;
   const int e = 16 * wv + n;
-  const int kq = d / 4;                     // k values per lane group
-  const float* ha = hs + n * dp + g * kq;   // A: token n
+  const float* ha = hs + n * dp + 8 * g;    // A: token n
   // one descriptor for the whole router matrix (wave-uniform); expert rows past E
   // lie past its end and read as zeros
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(p.wr), (short)0, p.E * d * 2, 0x00020000);
-  const int boff = (e * d + g * kq) * 2;    // this lane's row and k range, in bytes
+  const int boff = (e * d + 8 * g) * 2;     // this lane's row and k offset, in bytes
+  const int ns = d / 32;                    // k steps (d % 32 == 0)
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < kq; s0 += 8 * PF_MUNR) {
-    u32x4 bq[PF_MUNR];
-#pragma unroll
-    for (int u = 0; u < PF_MUNR; ++u)
-      bq[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            rs, boff + min(s0 + 8 * u, kq - 8) * 2, 0, 0));
-#pragma unroll
-    for (int u = 0; u < PF_MUNR; ++u) {
-      const int s = s0 + 8 * u;
-      if (s < kq) {
-        const f32x4 a0 = *reinterpret_cast<const f32x4*>(ha + s);
-        const f32x4 a1 = *reinterpret_cast<const f32x4*>(ha + s + 4);
-        const uint32_t wd[4] = {bq[u].x, bq[u].y, bq[u].z, bq[u].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(j < 2 ? a0[2 * j] : a1[2 * j - 4], bf16_lo(wd[j]), acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(j < 2 ? a0[2 * j + 1] : a1[2 * j - 3], bf16_hi(wd[j]), acc, 0, 0, 0);
-        }
-      }
-    }
+  u32x4 bq0[PF_MUNR], bq1[PF_MUNR];
+#define PF_RLOAD_B(BQ, S0)                                                                     \
+  _Pragma("unroll") for (int u = 0; u < PF_MUNR; ++u)                                          \
+    BQ[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(                   \
+                                          rs, boff + min((S0) + u, ns - 1) * 64, 0, 0));
+#define PF_RMMA_B(BQ, S0)                                                                      \
+  _Pragma("unroll") for (int u = 0; u < PF_MUNR; ++u) {                                        \
+    const int st = (S0) + u;                                                                   \
+    if (st < ns) {                                                                             \
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(ha + 32 * st);                          \
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(ha + 32 * st + 4);                      \
+      const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};                    \
+      bf16x8 hi, mid, lo;                                                                      \
+      _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                          \
+        const float xh = __uint_as_float(__float_as_uint(av[j]) & 0xFFFF0000u);                \
+        const float r1 = av[j] - xh;                                                           \
+        const float xm = __uint_as_float(__float_as_uint(r1) & 0xFFFF0000u);                   \
+        const float r2 = r1 - xm;                                                              \
+        hi[j] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(xh) >> 16));             \
+        mid[j] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(xm) >> 16));            \
+        lo[j] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(r2) >> 16));             \
+      }                                                                                        \
+      const bf16x8 b = __builtin_bit_cast(bf16x8, BQ[u]);                                      \
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, b, acc, 0, 0, 0);                      \
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mid, b, acc, 0, 0, 0);                     \
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, b, acc, 0, 0, 0);                      \
+    }                                                                                          \
   }
+  // the router rows stream from L2 in batches of PF_MUNR steps, double-buffered
+  PF_RLOAD_B(bq0, 0)
+  for (int s0 = 0; s0 < ns; s0 += 2 * PF_MUNR) {
+    PF_RLOAD_B(bq1, s0 + PF_MUNR)
+    PF_RMMA_B(bq0, s0)
+    PF_RLOAD_B(bq0, s0 + 2 * PF_MUNR)
+    PF_RMMA_B(bq1, s0 + PF_MUNR)
+  }
+#undef PF_RLOAD_B
+#undef PF_RMMA_B
   // acc[i] = logits[token 4 g + i][expert 16 wv + n]
   if (e < p.E) {
 #pragma unroll
