@@ -28,6 +28,7 @@
 #include "internal.h"
 
 #include <cmath>
+#include <type_traits>
 
 namespace lps {
 
@@ -202,11 +203,12 @@ __device__ __forceinline__ void epilogue(const GemvP& p, int u, int r0, int r1, 
 #define LPS_MX_MAXBL 256
 #endif
 
-template <int EPI>
-__device__ __forceinline__ void finish(const GemvP& p, int u, int r0, int r1, float a0, float a1,
-                                       float y0, float y1, int lane, float& best, int& bidx) {
-  a0 = wave_sum(a0);
-  a1 = wave_sum(a1);
+template <int EPI, typename A>
+__device__ __forceinline__ void finish(const GemvP& p, int u, int r0, int r1, A acc0, A acc1,
+                                       float xback, float y0, float y1, int lane, float& best,
+                                       int& bidx) {
+  float a0 = wave_sum(acc_value(acc0)) * xback;
+  float a1 = wave_sum(acc_value(acc1)) * xback;
   if (lane == 0) epilogue<EPI>(p, u, r0, r1, a0, a1, y0, y1);
   if constexpr (EPI == EPI_LOGITS) {   // a NaN logit sticks: the step has no argmax
     if (a0 > best || a0 != a0) { best = a0; bidx = r0; }
@@ -290,8 +292,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const uint8_t* base, 
     if (nu != u) {                                                 \
       int r0, r1;                                                  \
       unit_rows<EPI>(p, u, r0, r1);                                \
-      finish<EPI>(p, u, r0, r1, a0 * xback, a1 * xback, CY0, CY1, lane, best, bidx); \
-      a0 = a1 = 0.f;                                               \
+      finish<EPI>(p, u, r0, r1, a0, a1, xback, CY0, CY1, lane, best, bidx); \
+      a0 = a1 = AccT{};                                            \
     }                                                              \
     if (!more) break;                                              \
     u = nu;                                                        \
@@ -333,7 +335,9 @@ __global__ __launch_bounds__(NT) void k_gemv_buf(GemvP p) {
     stage_x<NORM, NT>(xsrc, p.g, p.eps, p.K, xs);
   }
   if (u < p.units) {
-    float a0 = 0.f, a1 = 0.f;
+    // MXFP4: matrix-core accumulators (acc_chunk_mx16), one per row
+    using AccT = std::conditional_t<WT == LPS_MXFP4, f32x4m, float>;
+    AccT a0{}, a1{};
     if constexpr (DB) {
       for (;;) {
         BUF_STEP(va0, va1, sa0, sa1, ya0, ya1, vb0, vb1, sb0, sb1, yb0, yb1)
@@ -348,8 +352,8 @@ __global__ __launch_bounds__(NT) void k_gemv_buf(GemvP p) {
         if (nu != u) {
           int r0, r1;
           unit_rows<EPI>(p, u, r0, r1);
-          finish<EPI>(p, u, r0, r1, a0 * xback, a1 * xback, ya0, ya1, lane, best, bidx);
-          a0 = a1 = 0.f;
+          finish<EPI>(p, u, r0, r1, a0, a1, xback, ya0, ya1, lane, best, bidx);
+          a0 = a1 = AccT{};
         }
         if (nu >= p.units) break;
         u = nu;

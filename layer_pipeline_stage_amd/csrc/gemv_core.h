@@ -117,10 +117,9 @@ __device__ __forceinline__ void stage_x(const float* x, const float* g, float ep
 // chunks at a pitch of 40 halves (80 bytes: lane l reads the x of its own weight
 // chunk, so lanes are a chunk apart; at 80 bytes sixteen consecutive lanes cover
 // distinct 16-byte bank groups).  Each byte of codes becomes two f16 weights in
-// one scaled conversion (exact: an e2m1 value times a power of two), and each
-// pair meets its two activations in one dot2 with f32 accumulation, so a weight
-// costs one VALU operation instead of the f32 path's one and a half.  The chunk
-// after the last (index K / 32) is zero.
+// one scaled conversion (exact: an e2m1 value times a power of two); the products
+// with f32 accumulation run on the matrix cores (below).  The chunk after the last
+// (index K / 32) is zero.
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 constexpr int MX16_XS = 40;     // halves per staged MXFP4 chunk (32 values + 8 pad)
@@ -129,22 +128,38 @@ constexpr int MX16_XS = 40;     // halves per staged MXFP4 chunk (32 values + 8 
 // longer rows, which holds 12 groups per thread
 constexpr int mx16_maxr(int U, int NT) { return U == 4 ? 12 : (512 * U + NT - 1) / NT; }
 
-__device__ __forceinline__ void acc_chunk_mx16(const u32x4 v, uint32_t sb, const _Float16* xh, float& a) {
+// A chunk's products on the matrix cores: v_mfma_f32_16x16x32_f16
+// takes the A operand of row m = l % 16, k = 8 (l / 16) .. + 7 from lane l and the B
+// operand of column n = l % 16 at the same k from lane l, so when every lane gives
+// 8 of its own chunk's weights as A and the same 8 staged activations as B, the
+// diagonal element D[m][m] sums those products of lanes m, m + 16, m + 32, m + 48
+// (the other elements mix lanes and are not used).  Four products (the chunk's
+// words q = 0..3: values 8q .. 8q + 7) cover the 32 values; the conversions stay on
+// the vector ALUs, the dot products leave them.  A zero chunk adds exactly +0.
+typedef float f32x4m __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void acc_chunk_mx16(const u32x4 v, uint32_t sb, const _Float16* xh, f32x4m& d) {
   const float sc = e8m0_to_f32(sb);
   const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const h8 xv = *reinterpret_cast<const h8*>(xh + 8 * q);
-    // byte b of the word: element 2b (low nibble) then 2b + 1, times the group scale
-    a = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[q], sc, 0),
-                               h2{xv[0], xv[1]}, a, false);
-    a = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[q], sc, 1),
-                               h2{xv[2], xv[3]}, a, false);
-    a = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[q], sc, 2),
-                               h2{xv[4], xv[5]}, a, false);
-    a = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[q], sc, 3),
-                               h2{xv[6], xv[7]}, a, false);
+    const h2 w0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[q], sc, 0);
+    const h2 w1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[q], sc, 1);
+    const h2 w2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[q], sc, 2);
+    const h2 w3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[q], sc, 3);
+    const h8 wv = {w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
+    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv, xv, d, 0, 0, 0);
   }
+}
+// this lane's share of the row: its diagonal element of D (lanes 20 q .. 20 q + 3 hold
+// D[4 q + i][4 q + i] as element i), zero on the other lanes; a wave sum then gives
+// the row's dot product
+__device__ __forceinline__ float acc_value(float a) { return a; }
+__device__ __forceinline__ float acc_value(f32x4m d) {
+  const int l = threadIdx.x & 63;
+  if ((l >> 4) != ((l & 15) >> 2)) return 0.f;
+  const int i = l & 3;
+  return i == 0 ? d[0] : i == 1 ? d[1] : i == 2 ? d[2] : d[3];
 }
 
 // Stage x as f16 chunks (see above); with NORM, as RMSNorm(x) * g computed in f32
