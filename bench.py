@@ -573,8 +573,11 @@ def main():
                         f"({a.streams} stream{'s' if a.streams == 'per-stage' else ''}), "
                         + ("the whole step as one replayed hipGraph, " if a.mode == "graph"
                            else "eager launches, ")
-                        + "per-step deferred logits readback (a pinned host ring drained "
-                          "on its own stream)",
+                        + ("per-step deferred logits readback (the step's kernels store its "
+                           "logits and id into a pinned host ring, drained by the host "
+                           "R steps later)" if a.mode == "graph"
+                           else "per-step deferred logits readback (a pinned host ring "
+                                "filled on its own stream)"),
             "mode": a.mode,
             "global_batch": 1, "seq_len": cfg.prefix + K, "stages": fence,
         },

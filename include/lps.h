@@ -326,13 +326,30 @@ int lps_head_forward(const lps_head_desc* h, const float* x, float* logits, int3
  * for an id outside it, as lps_embed) to x_next (dev [d] f32; may be x, which the
  * head has read by then), and advances
  * the position (unless it would reach pos_limit: flag bit 0 of state[2]) and the
- * step.  A run seeds x_next with lps_embed before its first replay.  Errors as
- * lps_head_forward and lps_step_advance (LPS_EINVAL). */
+ * step.  A run seeds x_next with lps_embed before its first replay.
+ * ring (may be NULL): the step's own kernels also store its logits to
+ * ring->logits[(s % slots) * vocab ..] and its argmax to ring->tok[s % slots]
+ * (see lps_host_ring), so a replayed step is read back without a copy on another
+ * stream.  Errors as lps_head_forward and lps_step_advance (LPS_EINVAL), also for
+ * a ring with slots < 1, with neither row, or rows that are not pinned host memory. */
+/* A pinned host ring the replayed step writes into (memra pp docs, struct
+ * PendingLogits: the step's logits reach the host later, without blocking it;
+ * ninfer pipeline stages, How it works: StageLink's ring of pinned host slots).
+ * Rows are host memory the device addresses (pinned: hipHostMalloc, a pinned
+ * tensor); logits [slots, vocab] f32 and tok [slots] int32, either may be NULL.
+ * Step s's row is visible to the host once a pending marked after the step
+ * (lps_pending_mark on the step's stream) has been waited; the caller waits step
+ * s before it launches step s + slots, which reuses the row. */
+typedef struct lps_host_ring {
+  float* logits;
+  int32_t* tok;
+  int32_t slots;
+} lps_host_ring;
 int lps_step_finish(const lps_head_desc* h, const float* x, float* logits, int32_t* state,
                     int32_t pos_limit, const int32_t* feed, int32_t n_feed, int32_t* tok_hist,
                     float* logits_hist, int32_t hist_cap, const void* embed, int32_t embed_dtype,
-                    float* x_next, int32_t* tok_cur, void* scratch, size_t scratch_bytes,
-                    void* stream);
+                    float* x_next, int32_t* tok_cur, const lps_host_ring* ring, void* scratch,
+                    size_t scratch_bytes, void* stream);
 
 /* ---- step-level entry points (the pieces lps_layer_forward launches) ------ */
 /* A3: y = x / sqrt(mean(x^2) + eps) * g, all (dev) [d] f32. */
@@ -429,6 +446,12 @@ int lps_copy_f32(const float* src, float* dst, int64_t n, void* stream);
 typedef struct lps_pending lps_pending;
 int lps_logits_defer(const float* logits, const int32_t* tok, int32_t vocab, void* last_stage,
                      void* readback, float* host_logits, int32_t* host_tok, lps_pending** out);
+/* A pending for everything enqueued on `stream` so far (an event with the
+ * system-scope fence that makes the device's stores to host memory visible),
+ * e.g. a replayed step whose kernels wrote an lps_host_ring: lps_pending_wait
+ * then blocks until those rows are on the host.  Consumed and refused as the
+ * pendings of lps_logits_defer. */
+int lps_pending_mark(void* stream, lps_pending** out);
 /* Makes `stream` wait until the pending's copies are done (no host block). */
 int lps_pending_order(lps_pending* p, void* stream);
 /* Blocks the host until host_logits / host_tok hold the step; consumes p. */

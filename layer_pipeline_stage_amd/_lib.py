@@ -49,6 +49,10 @@ class HeadDesc(C.Structure):
                 ("g_out", C.c_void_p), ("w_lm", C.c_void_p)]
 
 
+class HostRing(C.Structure):
+    _fields_ = [("logits", C.c_void_p), ("tok", C.c_void_p), ("slots", C.c_int32)]
+
+
 class MoEDesc(C.Structure):
     _fields_ = [("d", C.c_int32), ("n_experts", C.c_int32), ("top_k", C.c_int32), ("ff", C.c_int32),
                 ("remote_from", C.c_int32), ("eps", C.c_float),
@@ -88,7 +92,7 @@ SIGS = {
     "lps_stage_forward_static": (C.c_int, [P, PI32, I32, I32, P, I32, P], True),
     "lps_row_at_step": (C.c_int, [P, P, I64, P, I64, I32, I32, P], True),
     "lps_boundary_hop": (C.c_int, [P, P, P, I64, P], True),
-    "lps_step_finish": (C.c_int, [P, P, P, P, I32, P, I32, P, P, I32, P, I32, P, P, P, SZ, P], True),
+    "lps_step_finish": (C.c_int, [P, P, P, P, I32, P, I32, P, P, I32, P, I32, P, P, P, P, SZ, P], True),
     "lps_prefill_scratch_bytes": (SZ, [P, I32], False),
     "lps_stage_prefill": (C.c_int, [P, PI32, I32, I32, P, I32, I32, P, SZ, P], True),
     "lps_embed_rows": (C.c_int, [P, I32, I32, I32, P, I32, P, P], True),
@@ -113,6 +117,7 @@ SIGS = {
     "lps_copy_f32": (C.c_int, [P, P, I64, P], True),
     "lps_hbm_stream_read": (C.c_int, [P, I64, P, P], True),
     "lps_logits_defer": (C.c_int, [P, P, I32, P, P, P, P, PP], True),
+    "lps_pending_mark": (C.c_int, [P, PP], True),
     "lps_pending_order": (C.c_int, [P, P], True),
     "lps_pending_wait": (C.c_int, [P], True),
     "lps_pending_drop": (C.c_int, [P], True),

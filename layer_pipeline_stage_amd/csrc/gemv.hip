@@ -430,6 +430,7 @@ __global__ __launch_bounds__(1024) void k_step_finish(const float* pval, const i
                                                       int vocab, int32_t* state, int pos_limit,
                                                       const int32_t* feed, int n_feed,
                                                       int32_t* tok_hist, int cap, int32_t* tok_cur,
+                                                      int32_t* ring_tok, int slots,
                                                       const void* table, int d, float* x_next) {
   const int s = state[1], pos = state[0];
   const bool use_feed = s + 1 >= 0 && s + 1 < n_feed;
@@ -438,6 +439,7 @@ __global__ __launch_bounds__(1024) void k_step_finish(const float* pval, const i
   __shared__ int nxt;
   if (threadIdx.x == 0) {
     if (tok_hist && s >= 0 && s < cap) tok_hist[s] = a;
+    if (ring_tok && s >= 0) ring_tok[s % slots] = a;
     const int t = use_feed ? fed : a;
     if (tok_cur) *tok_cur = t;
     nxt = t;
@@ -657,7 +659,8 @@ int launch_head(const lps_head_desc* h, const float* x, float* logits, int32_t* 
 int launch_step_finish(const lps_head_desc* h, const float* x, float* logits, int32_t* state,
                        int32_t pos_limit, const int32_t* feed, int32_t n_feed, int32_t* tok_hist,
                        float* logits_hist, int32_t hist_cap, const void* embed, int32_t embed_dtype,
-                       float* x_next, int32_t* tok_cur, void* scratch, hipStream_t st, Stamp sp) {
+                       float* x_next, int32_t* tok_cur, float* ring_logits, int32_t* ring_tok,
+                       int32_t ring_slots, void* scratch, hipStream_t st, Stamp sp) {
   GemvP p{};
   p.w = static_cast<const uint8_t*>(h->w_lm);
   p.N = h->vocab;
@@ -675,16 +678,17 @@ int launch_step_finish(const lps_head_desc* h, const float* x, float* logits, in
   int rc = launch_wt<EPI_LOGITS, true>(h->wdtype, p, st, Stamp{sp.start, nullptr}, &waves);
   if (rc) return rc;
   // the history copy reads the step before the finish launch advances it
-  rc = launch_step_advance_hist(state, logits, h->vocab, logits_hist, hist_cap, st);
+  rc = launch_step_advance_hist(state, logits, h->vocab, logits_hist, hist_cap, ring_logits,
+                                ring_slots, st);
   if (rc) return rc;
   if (embed_dtype == LPS_F32)
     LPS_LAUNCH(k_step_finish<LPS_F32>, dim3(1), dim3(1024), 0, st, nullptr, sp.stop, p.pval, p.pidx,
-               waves, h->vocab, state, pos_limit, feed, n_feed, tok_hist, hist_cap, tok_cur, embed,
-               h->d, x_next);
+               waves, h->vocab, state, pos_limit, feed, n_feed, tok_hist, hist_cap, tok_cur, ring_tok,
+               ring_slots, embed, h->d, x_next);
   else
     LPS_LAUNCH(k_step_finish<LPS_BF16>, dim3(1), dim3(1024), 0, st, nullptr, sp.stop, p.pval, p.pidx,
-               waves, h->vocab, state, pos_limit, feed, n_feed, tok_hist, hist_cap, tok_cur, embed,
-               h->d, x_next);
+               waves, h->vocab, state, pos_limit, feed, n_feed, tok_hist, hist_cap, tok_cur, ring_tok,
+               ring_slots, embed, h->d, x_next);
   LPS_HIP(hipGetLastError());
   return LPS_OK;
 }

@@ -268,6 +268,41 @@ static hipEvent_t pending_take(lps_pending* p) {
   g_pend_free.push_back(slot);
   return ev;
 }
+// The device address of pinned host memory (false for device memory, pageable
+// host memory or an address the runtime does not know).
+static bool pinned_host_on_device(void* p, void** dptr) {
+  hipPointerAttribute_t a{};
+  if (hipPointerGetAttributes(&a, p) != hipSuccess || a.type != hipMemoryTypeHost) {
+    (void)hipGetLastError();
+    return false;
+  }
+  if (hipHostGetDevicePointer(dptr, p, 0) != hipSuccess || *dptr == nullptr) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return true;
+}
+// Registers an event as a live pending and hands out its token; on failure the
+// event is destroyed.
+static int pending_issue(hipEvent_t ev, lps_pending** out, const char* who) {
+  std::lock_guard<std::mutex> lk(g_pend_mu);
+  uint32_t slot;
+  if (!g_pend_free.empty()) {
+    slot = g_pend_free.back();
+    g_pend_free.pop_back();
+  } else {
+    if (g_pend.size() >= 0xfffffffeu) {
+      (void)hipEventDestroy(ev);
+      return fail(LPS_ENOMEM, "%s: too many pending readbacks", who);
+    }
+    slot = uint32_t(g_pend.size());
+    g_pend.emplace_back();
+  }
+  g_pend[slot].drained = ev;
+  g_pend[slot].live = true;
+  *out = pending_token(slot, g_pend[slot].gen);
+  return LPS_OK;
+}
 }  // namespace lps
 
 using namespace lps;
@@ -873,8 +908,8 @@ int lps_head_forward(const lps_head_desc* h, const float* x, float* logits, int3
 int lps_step_finish(const lps_head_desc* h, const float* x, float* logits, int32_t* state,
                     int32_t pos_limit, const int32_t* feed, int32_t n_feed, int32_t* tok_hist,
                     float* logits_hist, int32_t hist_cap, const void* embed, int32_t embed_dtype,
-                    float* x_next, int32_t* tok_cur, void* scratch, size_t scratch_bytes,
-                    void* stream) {
+                    float* x_next, int32_t* tok_cur, const lps_host_ring* ring, void* scratch,
+                    size_t scratch_bytes, void* stream) {
   LPS_REQUIRE(h, LPS_EINVAL, "lps_step_finish: null head");
   LPS_REQUIRE(h->d > 0 && h->vocab > 0, LPS_EINVAL, "lps_step_finish: d %d / vocab %d", h->d, h->vocab);
   LPS_REQUIRE(h->wdtype == LPS_F32 || h->wdtype == LPS_BF16, LPS_EINVAL,
@@ -894,9 +929,23 @@ int lps_step_finish(const lps_head_desc* h, const float* x, float* logits, int32
               "lps_step_finish: a history of %d steps needs tok_hist", hist_cap);
   LPS_REQUIRE(scratch_bytes >= head_scratch(h), LPS_EINVAL, "lps_step_finish: scratch %zu < %zu",
               scratch_bytes, head_scratch(h));
+  float* ring_l = nullptr;
+  int32_t* ring_t = nullptr;
+  int32_t slots = 0;
+  if (ring) {
+    LPS_REQUIRE(ring->slots >= 1 && (ring->logits || ring->tok), LPS_EINVAL,
+                "lps_step_finish: a host ring needs slots >= 1 and logits or tok (slots %d)",
+                ring->slots);
+    // the kernels store through the device's mapping of the pinned rows
+    if (ring->logits && !pinned_host_on_device(ring->logits, reinterpret_cast<void**>(&ring_l)))
+      return fail(LPS_EINVAL, "lps_step_finish: ring logits are not pinned host memory");
+    if (ring->tok && !pinned_host_on_device(ring->tok, reinterpret_cast<void**>(&ring_t)))
+      return fail(LPS_EINVAL, "lps_step_finish: ring tok is not pinned host memory");
+    slots = ring->slots;
+  }
   return launch_step_finish(h, x, logits, state, pos_limit, feed, n_feed, tok_hist, logits_hist,
-                            hist_cap, embed, embed_dtype, x_next, tok_cur, scratch, as_stream(stream),
-                            timer_take(LPS_KIND_HEAD));
+                            hist_cap, embed, embed_dtype, x_next, tok_cur, ring_l, ring_t, slots,
+                            scratch, as_stream(stream), timer_take(LPS_KIND_HEAD));
 }
 
 // ---- benchmark timer ----------------------------------------------------------------------
@@ -1143,23 +1192,22 @@ int lps_logits_defer(const float* logits, const int32_t* tok, int32_t vocab, voi
     if (drained) (void)hipEventDestroy(drained);
     return fail(LPS_EHIP, "lps_logits_defer: %s", hipGetErrorString(e));
   }
-  std::lock_guard<std::mutex> lk(g_pend_mu);
-  uint32_t slot;
-  if (!g_pend_free.empty()) {
-    slot = g_pend_free.back();
-    g_pend_free.pop_back();
-  } else {
-    if (g_pend.size() >= 0xfffffffeu) {
-      (void)hipEventDestroy(drained);
-      return fail(LPS_ENOMEM, "lps_logits_defer: too many pending readbacks");
-    }
-    slot = uint32_t(g_pend.size());
-    g_pend.emplace_back();
+  return pending_issue(drained, out, "lps_logits_defer");
+}
+
+int lps_pending_mark(void* stream, lps_pending** out) {
+  LPS_REQUIRE(out, LPS_EINVAL, "lps_pending_mark: null out");
+  *out = nullptr;
+  // the system-scope fence of this event is what makes the device's stores to host
+  // memory visible to the host once it has fired
+  hipEvent_t ev = nullptr;
+  hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventRecord(ev, as_stream(stream));
+  if (e != hipSuccess) {
+    if (ev) (void)hipEventDestroy(ev);
+    return fail(LPS_EHIP, "lps_pending_mark: %s", hipGetErrorString(e));
   }
-  g_pend[slot].drained = drained;
-  g_pend[slot].live = true;
-  *out = pending_token(slot, g_pend[slot].gen);
-  return LPS_OK;
+  return pending_issue(ev, out, "lps_pending_mark");
 }
 
 int lps_pending_order(lps_pending* p, void* stream) {

@@ -100,11 +100,14 @@ int launch_copy2_f32(const float* src, float* dst0, float* dst1, int64_t n, hipS
 int launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t st);
 // decode step state (pos, step, flags): see lps_step_advance
 int launch_step_advance_hist(const int32_t* state, const float* logits, int32_t vocab,
-                             float* logits_hist, int32_t hist_cap, hipStream_t st);
+                             float* logits_hist, int32_t hist_cap, float* ring_logits,
+                             int32_t ring_slots, hipStream_t st);
+// ring_logits / ring_tok: device addresses of a host ring of ring_slots rows (or NULL)
 int launch_step_finish(const lps_head_desc* h, const float* x, float* logits, int32_t* state,
                        int32_t pos_limit, const int32_t* feed, int32_t n_feed, int32_t* tok_hist,
                        float* logits_hist, int32_t hist_cap, const void* embed, int32_t embed_dtype,
-                       float* x_next, int32_t* tok_cur, void* scratch, hipStream_t st, Stamp sp = {});
+                       float* x_next, int32_t* tok_cur, float* ring_logits, int32_t* ring_tok,
+                       int32_t ring_slots, void* scratch, hipStream_t st, Stamp sp = {});
 int launch_step_advance(int32_t* state, int32_t pos_limit, const int32_t* argmax, int32_t* tok_cur,
                         const int32_t* feed, int32_t n_feed, int32_t* tok_hist, int32_t hist_cap,
                         const float* logits, int32_t vocab, float* logits_hist, hipStream_t st);

@@ -165,13 +165,19 @@ __global__ __launch_bounds__(256) void k_stream_read(const u32x4* __restrict__ s
 // state[0] = position, state[1] = step, state[2] = flags (bit 0: the position
 // reached its limit and stayed).  Both kernels read the step from state[1], so
 // the copy runs before the advance in stream order.
+// ring (optional): host memory the device addresses directly (a pinned ring of
+// `slots` rows); row s % slots receives the logits too, stored from here so no
+// copy on another stream has to wait for the step
 __global__ void k_hist_logits(const int32_t* state, const float* logits, int vocab, float* hist,
-                              int cap) {
+                              int cap, float* ring, int slots) {
   const int s = state[1];
-  if (s < 0 || s >= cap) return;
-  float* dst = hist + (long long)s * vocab;
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < vocab; i += gridDim.x * blockDim.x)
-    dst[i] = logits[i];
+  float* dst = hist && s >= 0 && s < cap ? hist + (long long)s * vocab : nullptr;
+  float* rdst = ring && s >= 0 ? ring + (long long)(s % slots) * vocab : nullptr;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < vocab; i += gridDim.x * blockDim.x) {
+    const float v = logits[i];
+    if (dst) dst[i] = v;
+    if (rdst) rdst[i] = v;
+  }
 }
 
 __global__ void k_step_advance(int32_t* state, int pos_limit, const int32_t* argmax,
@@ -192,10 +198,12 @@ __global__ void k_step_advance(int32_t* state, int pos_limit, const int32_t* arg
 }
 
 int launch_step_advance_hist(const int32_t* state, const float* logits, int32_t vocab,
-                             float* logits_hist, int32_t hist_cap, hipStream_t st) {
-  if (logits_hist && hist_cap > 0) {
+                             float* logits_hist, int32_t hist_cap, float* ring_logits,
+                             int32_t ring_slots, hipStream_t st) {
+  if (!(logits_hist && hist_cap > 0)) logits_hist = nullptr;
+  if (logits_hist || ring_logits) {
     hipLaunchKernelGGL(k_hist_logits, grid_for(vocab / 4 + 1), dim3(256), 0, st, state, logits,
-                       vocab, logits_hist, hist_cap);
+                       vocab, logits_hist, hist_cap, ring_logits, ring_slots);
     LPS_HIP(hipGetLastError());
   }
   return LPS_OK;
@@ -204,7 +212,7 @@ int launch_step_advance_hist(const int32_t* state, const float* logits, int32_t 
 int launch_step_advance(int32_t* state, int32_t pos_limit, const int32_t* argmax, int32_t* tok_cur,
                         const int32_t* feed, int32_t n_feed, int32_t* tok_hist, int32_t hist_cap,
                         const float* logits, int32_t vocab, float* logits_hist, hipStream_t st) {
-  int rc = launch_step_advance_hist(state, logits, vocab, logits_hist, hist_cap, st);
+  int rc = launch_step_advance_hist(state, logits, vocab, logits_hist, hist_cap, nullptr, 0, st);
   if (rc) return rc;
   hipLaunchKernelGGL(k_step_advance, dim3(1), dim3(64), 0, st, state, pos_limit, argmax, tok_cur,
                      feed, n_feed, tok_hist, hist_cap);

@@ -398,12 +398,13 @@ class DeviceDecoder:
                                        ptr(self.scratch[s]), self.scratch_bytes, sp(st[s]))
         self.step_no += 1
 
-    def capture_step(self, feed_dev, n_feed, tok_hist, logits_hist, hist_cap):
+    def capture_step(self, feed_dev, n_feed, tok_hist, logits_hist, hist_cap, ring=None):
         """Capture one decode step (every stage and boundary, then the head and the
         token chain in lps_step_finish, which also writes the next step's input row
         into x[0]) into a graph on stage 0's stream; the other stage streams fork
         into it through the boundary events and are joined back at the end.  The
-        run seeds x[0] before the first replay.  Returns the graph handle
+        run seeds x[0] before the first replay.  ring: an optional lps.HostRing the
+        step's kernels write its logits and id into.  Returns the graph handle
         (lps_graph_destroy frees it)."""
         cfg = self.cfg
         st0, stl = self.streams[0], self.streams[-1]
@@ -415,8 +416,9 @@ class DeviceDecoder:
             lps.lps_step_finish(C.byref(self.head), ptr(self.x[-1]), ptr(self.g_logits),
                                 ptr(self.g_state), cfg.ctx_max, feed_dev, n_feed, tok_hist,
                                 logits_hist, hist_cap, ptr(self.embed), lps.DTYPES[cfg.wdtype],
-                                ptr(self.x[0]), ptr(self.g_tok), ptr(self.head_scratch),
-                                self.head_scratch.numel(), sp(stl))
+                                ptr(self.x[0]), ptr(self.g_tok),
+                                C.byref(ring) if ring is not None else None,
+                                ptr(self.head_scratch), self.head_scratch.numel(), sp(stl))
         finally:
             join = (C.c_void_p * len(self.streams))(*[sp(s) for s in self.streams])
             lps.lps_graph_end(sp(st0), join, len(self.streams), C.byref(g))
@@ -426,13 +428,14 @@ class DeviceDecoder:
                          timer=None) -> StepResult:
         """run_tokens with the whole step captured once and replayed: the
         position, the step and the next input id live on the device and are
-        advanced by the graph itself, so the host only launches replays.  Every
-        step's argmax (and, with logits=True, its logits) goes into a device
-        history slot of its own; after each replay that step's slot is handed to
-        the deferred readback (lps_logits_defer on the readback stream into a
-        pinned host ring of `ring` entries), and the host drains step t - ring
-        while later replays run.  timer: an optional callable run around the
-        replays and their readback (for the bench)."""
+        advanced by the graph itself, so the host only launches replays.  The
+        step's own kernels store its argmax (and, with logits=True, its logits)
+        into row t % ring of the pinned host ring; after each replay a pending
+        marks the step (lps_pending_mark), and the host drains step t - ring
+        while later replays run.  (A copy on the readback stream would make that
+        stream wait for every step, which costs the replays ~45 us per step.)
+        timer: an optional callable run around the replays and their readback
+        (for the bench)."""
         cfg = self.cfg
         assert self.head is not None, "model has no vocabulary"
         p = cfg.prefix if p0 is None else p0
@@ -443,13 +446,13 @@ class DeviceDecoder:
         dev = self.device
         feed_dev = torch.tensor(ids, dtype=torch.int32, device=dev)
         tok_hist = torch.zeros(total, dtype=torch.int32, device=dev)
-        lg_hist = (torch.zeros((total, cfg.vocab), dtype=torch.float32, device=dev)
-                   if logits else None)
+        R = self.ring
+        ring = lps.HostRing()
+        ring.logits = ptr(self.host_logits) if logits else None
+        ring.tok, ring.slots = ptr(self.host_tok), R
         self.g_state.copy_(torch.tensor([p, 0, 0, 0], dtype=torch.int32))
         self.g_tok.fill_(ids[0])
-        g = self.capture_step(ptr(feed_dev), P, ptr(tok_hist),
-                              ptr(lg_hist) if logits else None, total)
-        R = self.ring
+        g = self.capture_step(ptr(feed_dev), P, ptr(tok_hist), None, total, ring)
         pend = [None] * R
         toks, lg = [None] * total, [None] * total
 
@@ -473,10 +476,7 @@ class DeviceDecoder:
                     drain(i - R)             # frees host ring slot i % R
                 lps.lps_graph_launch(g, sp(st0))
                 h = C.c_void_p()
-                lps.lps_logits_defer(ptr(lg_hist) + 4 * cfg.vocab * i if logits else None,
-                                     ptr(tok_hist) + 4 * i, cfg.vocab, sp(st0), sp(self.readback),
-                                     ptr(self.host_logits[i % R]) if logits else None,
-                                     ptr(self.host_tok) + 4 * (i % R), C.byref(h))
+                lps.lps_pending_mark(sp(st0), C.byref(h))
                 pend[i % R] = h
             for i in range(max(0, total - R), total):
                 drain(i)

@@ -209,10 +209,15 @@ def test_graph_and_device_state_entry_points_refuse_bad_arguments(L):
             L.lps_step_advance(*a)
         assert e.value.code == L.LPS_EINVAL, a
     # lps_step_finish: (h, x, logits, state, pos_limit, feed, n_feed, tok_hist,
-    # logits_hist, hist_cap, embed, embed_dtype, x_next, tok_cur, scratch, bytes, stream)
+    # logits_hist, hist_cap, embed, embed_dtype, x_next, tok_cur, ring, scratch,
+    # bytes, stream)
     hd = L.HeadDesc()
     hd.d, hd.vocab, hd.wdtype, hd.eps, hd.g_out, hd.w_lm = 256, 100, L.LPS_F32, 1e-6, 16, 16
-    ok = [C.byref(hd), 16, 16, 16, 8, None, 0, None, None, 0, 16, L.LPS_F32, 16, None, 16, 1 << 20, None]
+    ok = [C.byref(hd), 16, 16, 16, 8, None, 0, None, None, 0, 16, L.LPS_F32, 16, None, None, 16,
+          1 << 20, None]
+    ring0, ring_empty = L.HostRing(), L.HostRing()
+    ring0.logits, ring0.tok, ring0.slots = 16, 16, 0
+    ring_empty.logits, ring_empty.tok, ring_empty.slots = None, None, 4
     bad_fin = [
         (0, None),              # null head
         (3, None),              # null state
@@ -222,7 +227,9 @@ def test_graph_and_device_state_entry_points_refuse_bad_arguments(L):
         (10, None),             # null embedding table
         (11, L.LPS_MXFP4),      # embedding dtype
         (12, None),             # null x_next
-        (15, 16),               # scratch below the head's
+        (14, C.byref(ring0)),   # a host ring of no slots
+        (14, C.byref(ring_empty)),  # a host ring with neither row
+        (16, 16),               # scratch below the head's
     ]
     for i, v in bad_fin:
         a = list(ok)

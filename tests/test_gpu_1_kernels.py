@@ -438,7 +438,7 @@ def test_step_finish_equals_head_advance_embed(L):
         if fused:
             L.lps_step_finish(C.byref(hd), ptr(xd), ptr(lg), ptr(st), pos_limit, ptr(feed), n_feed,
                               ptr(th), ptr(lh), cap, ptr(Ed), L.LPS_BF16, ptr(xn), ptr(tok),
-                              ptr(sc), sb, stream())
+                              None, ptr(sc), sb, stream())
         else:
             am = torch.zeros(1, dtype=torch.int32, device=DEV)
             L.lps_head_forward(C.byref(hd), ptr(xd), ptr(lg), ptr(am), ptr(sc), sb, stream())
@@ -460,6 +460,45 @@ def test_step_finish_equals_head_advance_embed(L):
         for u, v in zip(a, b):
             assert np.array_equal(u, v, equal_nan=True), (s0, nf)
     assert int(a[4][0]) == V and np.all(np.isnan(a[5]))
+
+    # the host ring: step s's logits and argmax land in pinned row s % slots, read
+    # after a pending marked behind the step; the other rows are left alone
+    R = 3
+    ring_l = torch.full((R, V), -7.0, dtype=torch.float32).pin_memory()
+    ring_t = torch.full((R,), -7, dtype=torch.int32).pin_memory()
+    ring = L.HostRing()
+    ring.logits, ring.tok, ring.slots = ptr(ring_l), ptr(ring_t), R
+    for xi, s0, lim, nf in cases + [(x, [60, 7, 0, 0], 100, 0)]:
+        ring_l.fill_(-7.0)
+        ring_t.fill_(-7)
+        sc = torch.zeros(sb, dtype=torch.uint8, device=DEV)
+        lg = torch.zeros(V, dtype=torch.float32, device=DEV)
+        st = dev(np.array(s0, np.int32))
+        tok = torch.full((1,), -7, dtype=torch.int32, device=DEV)
+        xn = torch.full((d,), -7.0, dtype=torch.float32, device=DEV)
+        L.lps_step_finish(C.byref(hd), ptr(dev(xi)), ptr(lg), ptr(st), lim, ptr(feed), nf, None,
+                          None, 0, ptr(Ed), L.LPS_BF16, ptr(xn), ptr(tok), C.byref(ring), ptr(sc),
+                          sb, stream())
+        h = C.c_void_p()
+        L.lps_pending_mark(stream(), C.byref(h))
+        L.lps_pending_wait(h)
+        ref = run(False, xi, s0, lim, nf)
+        k = s0[1] % R
+        assert np.array_equal(ring_l[k].numpy(), ref[0], equal_nan=True), s0
+        assert int(ring_t[k]) == int(ref[0].argmax()) if np.isfinite(ref[0]).all() else int(ring_t[k]) == V
+        for j in range(R):
+            if j != k:
+                assert np.all(ring_l[j].numpy() == -7.0) and int(ring_t[j]) == -7
+        with pytest.raises(L.LpsError) as e:
+            L.lps_pending_wait(h)                 # consumed
+        assert e.value.code == L.LPS_ESTATE
+    dbuf = torch.zeros(V, dtype=torch.float32, device=DEV)
+    ring.logits = ptr(dbuf)                       # device memory is not a host ring
+    with pytest.raises(L.LpsError) as e:
+        L.lps_step_finish(C.byref(hd), ptr(dev(x)), ptr(lg), ptr(st), 100, ptr(feed), 0, None, None,
+                          0, ptr(Ed), L.LPS_BF16, ptr(xn), ptr(tok), C.byref(ring), ptr(sc), sb,
+                          stream())
+    assert e.value.code == L.LPS_EINVAL
 
 
 @pytest.mark.parametrize("n16", [1, 4097, (1 << 22) + 333])
