@@ -410,6 +410,18 @@ int lps_boundary_recv(lps_boundary* b, float* x, int64_t step, void* consumer);
  * next receive), the same waits (for an earlier receive of that slot on another
  * stream) and counters (a send and a receive) as the two calls. */
 int lps_boundary_hop(lps_boundary* b, const float* x, float* x_out, int64_t step, void* stream);
+/* lps_stage_forward_dpos of `stage` followed by lps_boundary_hop(b, x, x_out, step,
+ * stream), with the hop's copy folded into the stage's last launch (the down
+ * projection's residual add, or the MoE combine): it stores every updated row of x
+ * also to slot[step & 1] and to x_out, so no copy launch follows.  The same
+ * checks as the two calls (the boundary's rows must be the stage's d values,
+ * LPS_EINVAL otherwise), the same order rules, waits and counters as the hop
+ * (ninfer pipeline stages, How it works: StageLink; memra pp docs, header: the
+ * boundary slots and their events). */
+int lps_stage_forward_dpos_hop(const lps_model* m, const int32_t* fence, int32_t n_stages,
+                               int32_t stage, float* x, const int32_t* pos_dev, void* scratch,
+                               size_t scratch_bytes, lps_boundary* b, float* x_out, int64_t step,
+                               void* stream);
 /* Synchronizes the boundary's events, then frees the handle. */
 int lps_boundary_destroy(lps_boundary* b);
 

@@ -92,6 +92,7 @@ SIGS = {
     "lps_stage_forward_static": (C.c_int, [P, PI32, I32, I32, P, I32, P], True),
     "lps_row_at_step": (C.c_int, [P, P, I64, P, I64, I32, I32, P], True),
     "lps_boundary_hop": (C.c_int, [P, P, P, I64, P], True),
+    "lps_stage_forward_dpos_hop": (C.c_int, [P, PI32, I32, I32, P, P, P, SZ, P, P, I64, P], True),
     "lps_step_finish": (C.c_int, [P, P, P, P, I32, P, I32, P, P, I32, P, I32, P, P, P, P, SZ, P], True),
     "lps_prefill_scratch_bytes": (SZ, [P, I32], False),
     "lps_stage_prefill": (C.c_int, [P, PI32, I32, I32, P, I32, I32, P, SZ, P], True),

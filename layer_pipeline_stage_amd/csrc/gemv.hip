@@ -45,6 +45,9 @@ struct GemvP {
   const float* g;
   float eps;
   float* y;
+  // residual add: when tee0 is set, every updated row also goes to tee0 and tee1
+  float* tee0;
+  float* tee1;
   // QKV epilogue
   int nq, nkv, hd, pos, ctx_max, kvdtype;
   void* kc;
@@ -120,8 +123,17 @@ __device__ __forceinline__ void epilogue(const GemvP& p, int u, int r0, int r1, 
     p.y[r0] = a0;
     if (r1 >= 0) p.y[r1] = a1;
   } else if constexpr (EPI == EPI_ADD) {   // y0, y1: the rows' residual values, loaded early
-    p.y[r0] = y0 + a0;
-    if (r1 >= 0) p.y[r1] = y1 + a1;
+    const float v0 = y0 + a0, v1 = y1 + a1;
+    p.y[r0] = v0;
+    if (r1 >= 0) p.y[r1] = v1;
+    if (p.tee0) {
+      p.tee0[r0] = v0;
+      p.tee1[r0] = v0;
+      if (r1 >= 0) {
+        p.tee0[r1] = v1;
+        p.tee1[r1] = v1;
+      }
+    }
   } else if constexpr (EPI == EPI_SWIGLU || EPI == EPI_MOEGU) {
     p.y[u] = silu(a0) * a1;
   } else if constexpr (EPI == EPI_MOEDN) {
@@ -520,7 +532,8 @@ static void set_rows(GemvP& p, int wdtype, int K) {
 }
 
 int launch_gemv(int wdtype, const void* w, const uint8_t* s, int N, int K, const float* x,
-                const float* g, float eps, float* y, int mode, hipStream_t st, Stamp sp) {
+                const float* g, float eps, float* y, int mode, hipStream_t st, Stamp sp,
+                float* tee0, float* tee1) {
   GemvP p{};
   p.w = static_cast<const uint8_t*>(w);
   p.s = s;
@@ -530,6 +543,10 @@ int launch_gemv(int wdtype, const void* w, const uint8_t* s, int N, int K, const
   p.g = g;
   p.eps = eps;
   p.y = y;
+  if (mode == EPI_ADD && tee0 && tee1) {
+    p.tee0 = tee0;
+    p.tee1 = tee1;
+  }
   set_rows(p, wdtype, K);
   const bool norm = g != nullptr;
   if (mode == EPI_SWIGLU) {

@@ -164,9 +164,11 @@ static LayerScratch layer_scratch(const lps_layer_desc* L) {
   return s;
 }
 
-// pos_dev set: the position is read on the device (pos unused)
+// pos_dev set: the position is read on the device (pos unused).  tee0 / tee1 set: the
+// layer's last launch also stores the updated residual row to both.
 static int layer_forward(const lps_layer_desc* L, float* x, int pos, void* scratch, hipStream_t st,
-                         const int32_t* pos_dev = nullptr) {
+                         const int32_t* pos_dev = nullptr, float* tee0 = nullptr,
+                         float* tee1 = nullptr) {
   const LayerScratch s = layer_scratch(L);
   char* sc = static_cast<char*>(scratch);
   float* m = reinterpret_cast<float*>(sc + s.m);
@@ -185,12 +187,12 @@ static int layer_forward(const lps_layer_desc* L, float* x, int pos, void* scrat
                      LPS_EPI_ADD, st, timer_take(LPS_KIND_OPROJ));
     if (rc) return rc;
   }
-  if (L->ffn_kind == LPS_FFN_MOE) return moe_decode(L->moe, x, m, st);
+  if (L->ffn_kind == LPS_FFN_MOE) return moe_decode(L->moe, x, m, st, tee0, tee1);
   rc = launch_gemv(L->wdtype, L->w_gu, L->s_gu, 2 * L->ff, L->d, x, L->g_ffn, L->eps, m,
                    LPS_EPI_SWIGLU, st, timer_take(LPS_KIND_GATEUP));
   if (rc) return rc;
   return launch_gemv(L->wdtype, L->w_d, L->s_d, L->d, L->ff, m, nullptr, 0.f, x, LPS_EPI_ADD, st,
-                     timer_take(LPS_KIND_DOWN));
+                     timer_take(LPS_KIND_DOWN), tee0, tee1);
 }
 
 static int check_fence(const int32_t* fence, int32_t n_stages, int32_t n_layers, const char* who) {
@@ -281,6 +283,43 @@ static bool pinned_host_on_device(void* p, void** dptr) {
     return false;
   }
   return true;
+}
+// The checks and the wait of a same-stream hop of `step` across b, before anything
+// writes the slot: the step is the next send and the next receive, and a slot whose
+// last receive ran on another stream of the same capture context is waited for.
+static int hop_begin(lps_boundary* b, int64_t step, hipStream_t st, unsigned long long* cid,
+                     const char* who) {
+  LPS_REQUIRE(step == b->next_send && step == b->next_recv, LPS_ESTATE,
+              "%s: step %lld out of order (next send %lld, next receive %lld)", who,
+              (long long)step, (long long)b->next_send, (long long)b->next_recv);
+  const int k = int(step & 1);
+  int rc = capture_of(st, cid);
+  if (rc) return rc;
+  if (b->rx_stream[k] && b->rx_stream[k] != st && b->rx_cap[k] == *cid) {
+    if (!b->rx_recorded[k]) {
+      unsigned long long rcid = 0;
+      rc = capture_of(b->rx_stream[k], &rcid);
+      if (rc) return rc;
+      LPS_REQUIRE(rcid == *cid, LPS_ESTATE,
+                  "%s: slot %d's last receive stream is in another capture context", who, k);
+      LPS_HIP(hipEventRecord(b->ev_rx[k], b->rx_stream[k]));
+      b->rx_recorded[k] = true;
+    }
+    LPS_HIP(hipStreamWaitEvent(st, b->ev_rx[k], 0));
+  }
+  return LPS_OK;
+}
+// The books of a same-stream hop whose row is in the slot: the slot was sent and
+// received on st, in capture context cid.
+static void hop_end(lps_boundary* b, int64_t step, hipStream_t st, unsigned long long cid) {
+  const int k = int(step & 1);
+  b->tx_recorded[k] = false;
+  b->tx_stream[k] = b->rx_stream[k] = st;
+  b->tx_cap[k] = b->rx_cap[k] = cid;
+  b->rx_recorded[k] = false;
+  b->next_send = b->next_recv = step + 1;
+  count_send();
+  count_recv();
 }
 // Registers an event as a live pending and hands out its token; on failure the
 // event is destroyed.
@@ -577,6 +616,28 @@ int lps_stage_forward(const lps_model* m, const int32_t* fence, int32_t n_stages
   return LPS_OK;
 }
 
+}  // extern "C"
+
+// The arguments of a device-position walk of one stage (the fence and stage checked).
+static int check_dpos_walk(const lps_model* m, const int32_t* fence, int32_t stage, const float* x,
+                           const int32_t* pos_dev, const void* scratch, size_t scratch_bytes,
+                           const char* who) {
+  LPS_REQUIRE(x && scratch && pos_dev, LPS_EINVAL, "%s: null x, scratch or pos", who);
+  LPS_REQUIRE(aligned16(x) && aligned16(scratch) && (reinterpret_cast<uintptr_t>(pos_dev) & 3) == 0,
+              LPS_EINVAL, "%s: x and scratch must be 16-byte aligned, pos 4", who);
+  LPS_REQUIRE(scratch_bytes >= m->scratch, LPS_EINVAL, "%s: scratch %zu < %zu needed", who,
+              scratch_bytes, m->scratch);
+  for (int l = fence[stage]; l < fence[stage + 1]; ++l) {
+    if (m->layers[l].nq == 0) continue;   // no attention: no position is read
+    const float* t = m->layers[l].rope_cs;
+    LPS_REQUIRE(t && (reinterpret_cast<uintptr_t>(t) & 7) == 0, LPS_EINVAL,
+                "%s: layer %d needs an 8-byte aligned rope_cs table", who, l);
+  }
+  return LPS_OK;
+}
+
+extern "C" {
+
 int lps_stage_forward_dpos(const lps_model* m, const int32_t* fence, int32_t n_stages,
                            int32_t stage, float* x, const int32_t* pos_dev, void* scratch,
                            size_t scratch_bytes, void* stream) {
@@ -585,17 +646,8 @@ int lps_stage_forward_dpos(const lps_model* m, const int32_t* fence, int32_t n_s
   if (rc) return rc;
   LPS_REQUIRE(stage >= 0 && stage < n_stages, LPS_ERANGE,
               "lps_stage_forward_dpos: stage %d outside [0, %d)", stage, n_stages);
-  LPS_REQUIRE(x && scratch && pos_dev, LPS_EINVAL, "lps_stage_forward_dpos: null x, scratch or pos");
-  LPS_REQUIRE(aligned16(x) && aligned16(scratch) && (reinterpret_cast<uintptr_t>(pos_dev) & 3) == 0,
-              LPS_EINVAL, "lps_stage_forward_dpos: x and scratch must be 16-byte aligned, pos 4");
-  LPS_REQUIRE(scratch_bytes >= m->scratch, LPS_EINVAL,
-              "lps_stage_forward_dpos: scratch %zu < %zu needed", scratch_bytes, m->scratch);
-  for (int l = fence[stage]; l < fence[stage + 1]; ++l) {
-    if (m->layers[l].nq == 0) continue;   // no attention: no position is read
-    const float* t = m->layers[l].rope_cs;
-    LPS_REQUIRE(t && (reinterpret_cast<uintptr_t>(t) & 7) == 0, LPS_EINVAL,
-                "lps_stage_forward_dpos: layer %d needs an 8-byte aligned rope_cs table", l);
-  }
+  rc = check_dpos_walk(m, fence, stage, x, pos_dev, scratch, scratch_bytes, "lps_stage_forward_dpos");
+  if (rc) return rc;
   hipStream_t st = as_stream(stream);
   for (int l = fence[stage]; l < fence[stage + 1]; ++l) {
     rc = layer_forward(&m->layers[l], x, 0, scratch, st, pos_dev);
@@ -1118,36 +1170,46 @@ int lps_boundary_hop(lps_boundary* b, const float* x, float* x_out, int64_t step
   LPS_REQUIRE(b && x && x_out, LPS_EINVAL, "lps_boundary_hop: null boundary, x or x_out");
   LPS_REQUIRE(aligned16(x) && aligned16(x_out), LPS_EINVAL,
               "lps_boundary_hop: x and x_out must be 16-byte aligned");
-  LPS_REQUIRE(step == b->next_send && step == b->next_recv, LPS_ESTATE,
-              "lps_boundary_hop: step %lld out of order (next send %lld, next receive %lld)",
-              (long long)step, (long long)b->next_send, (long long)b->next_recv);
-  const int k = int(step & 1);
   hipStream_t st = as_stream(stream);
   unsigned long long cid = 0;
-  int rc = capture_of(st, &cid);
+  int rc = hop_begin(b, step, st, &cid, "lps_boundary_hop");
   if (rc) return rc;
-  // the slot's last receive on another stream: this write waits for it (as a send)
-  if (b->rx_stream[k] && b->rx_stream[k] != st && b->rx_cap[k] == cid) {
-    if (!b->rx_recorded[k]) {
-      unsigned long long rcid = 0;
-      rc = capture_of(b->rx_stream[k], &rcid);
-      if (rc) return rc;
-      LPS_REQUIRE(rcid == cid, LPS_ESTATE,
-                  "lps_boundary_hop: slot %d's last receive stream is in another capture context", k);
-      LPS_HIP(hipEventRecord(b->ev_rx[k], b->rx_stream[k]));
-      b->rx_recorded[k] = true;
-    }
-    LPS_HIP(hipStreamWaitEvent(st, b->ev_rx[k], 0));
+  rc = launch_copy2_f32(x, b->slot[step & 1], x_out, b->n, st);
+  if (rc) return rc;
+  hop_end(b, step, st, cid);
+  return LPS_OK;
+}
+
+int lps_stage_forward_dpos_hop(const lps_model* m, const int32_t* fence, int32_t n_stages,
+                               int32_t stage, float* x, const int32_t* pos_dev, void* scratch,
+                               size_t scratch_bytes, lps_boundary* b, float* x_out, int64_t step,
+                               void* stream) {
+  LPS_REQUIRE(m, LPS_EINVAL, "lps_stage_forward_dpos_hop: null model");
+  int rc = check_fence(fence, n_stages, int32_t(m->layers.size()), "lps_stage_forward_dpos_hop");
+  if (rc) return rc;
+  LPS_REQUIRE(stage >= 0 && stage < n_stages, LPS_ERANGE,
+              "lps_stage_forward_dpos_hop: stage %d outside [0, %d)", stage, n_stages);
+  rc = check_dpos_walk(m, fence, stage, x, pos_dev, scratch, scratch_bytes,
+                       "lps_stage_forward_dpos_hop");
+  if (rc) return rc;
+  LPS_REQUIRE(b && x_out, LPS_EINVAL, "lps_stage_forward_dpos_hop: null boundary or x_out");
+  LPS_REQUIRE(aligned16(x_out), LPS_EINVAL, "lps_stage_forward_dpos_hop: x_out must be 16-byte aligned");
+  const lps_layer_desc& last = m->layers[fence[stage + 1] - 1];
+  LPS_REQUIRE(b->n == last.d, LPS_EINVAL,
+              "lps_stage_forward_dpos_hop: boundary rows of %d values, the stage's rows are %d",
+              b->n, last.d);
+  hipStream_t st = as_stream(stream);
+  unsigned long long cid = 0;
+  rc = hop_begin(b, step, st, &cid, "lps_stage_forward_dpos_hop");
+  if (rc) return rc;
+  for (int l = fence[stage]; l < fence[stage + 1]; ++l) {
+    const bool tail = l == fence[stage + 1] - 1;
+    rc = layer_forward(&m->layers[l], x, 0, scratch, st, pos_dev, tail ? b->slot[step & 1] : nullptr,
+                       tail ? x_out : nullptr);
+    if (rc) return rc;
   }
-  rc = launch_copy2_f32(x, b->slot[k], x_out, b->n, st);
-  if (rc) return rc;
-  b->tx_recorded[k] = false;
-  b->tx_stream[k] = b->rx_stream[k] = st;
-  b->tx_cap[k] = b->rx_cap[k] = cid;
-  b->rx_recorded[k] = false;
-  b->next_send = b->next_recv = step + 1;
-  count_send();
-  count_recv();
+  hop_end(b, step, st, cid);
+  count_stage_walk();
   return LPS_OK;
 }
 

@@ -71,8 +71,10 @@ struct QkvArgs {
   float* q;
   const int32_t* pos_dev = nullptr;   // if set: the position is read here (RoPE from L->rope_cs)
 };
+// mode EPI_ADD with tee0 and tee1: every updated row of y is also stored to both
 int launch_gemv(int wdtype, const void* w, const uint8_t* s, int N, int K, const float* x,
-                const float* g, float eps, float* y, int mode, hipStream_t st, Stamp sp = {});
+                const float* g, float eps, float* y, int mode, hipStream_t st, Stamp sp = {},
+                float* tee0 = nullptr, float* tee1 = nullptr);
 int launch_qkv(const QkvArgs& a, hipStream_t st, Stamp sp = {});
 // cs[0], cs[1] = f32 cos, sin of pos * base^(-2i / hd) (the QKV launch's own values)
 void rope_cos_sin(float base, int hd, int pos, int i, float* cs);
@@ -131,6 +133,8 @@ int check_layer(const lps_layer_desc* L, const char* who);
 // MoE FFN decode of one token (moe.hip): validation, scratch bytes, the launches
 int check_moe_decode(const lps_moe_desc* m, const char* who);
 size_t moe_decode_scratch(const lps_moe_desc* m);
-int moe_decode(const lps_moe_desc* m, float* x, void* scratch, hipStream_t st);
+// tee0 and tee1 (or NULL): the updated residual row is also stored to both
+int moe_decode(const lps_moe_desc* m, float* x, void* scratch, hipStream_t st,
+               float* tee0 = nullptr, float* tee1 = nullptr);
 
 }  // namespace lps

@@ -168,6 +168,8 @@ struct MoeCombP {
   const float* wts;      // [k]
   const float* z;        // [(k+1), d]
   float* x;              // [d] residual, updated
+  float* tee0;           // [d] or NULL: the updated row, also stored here and to tee1
+  float* tee1;
   int d, k, remote_from, E;
 };
 
@@ -199,7 +201,12 @@ __global__ __launch_bounds__(256) void k_moe_combine(MoeCombP p) {
   }
   const float r32 = static_cast<float>(static_cast<_Float16>(remote));
   const float y = (p.z[(long long)p.k * p.d + r] + local) + r32;
-  p.x[r] = p.x[r] + y;
+  const float v = p.x[r] + y;
+  p.x[r] = v;
+  if (p.tee0) {
+    p.tee0[r] = v;
+    p.tee1[r] = v;
+  }
 }
 
 struct MoeScratch {
@@ -273,7 +280,8 @@ size_t moe_decode_scratch(const lps_moe_desc* m) { return moe_scratch(m).total; 
 
 // One MoE FFN layer for one token (validated by the caller): route, the selected
 // and the shared expert's gate/up + SwiGLU and down GEMVs, the ordered combine.
-int moe_decode(const lps_moe_desc* m, float* x, void* scratch, hipStream_t st) {
+int moe_decode(const lps_moe_desc* m, float* x, void* scratch, hipStream_t st, float* tee0,
+               float* tee1) {
   const MoeScratch s = moe_scratch(m);
   char* sc = static_cast<char*>(scratch);
   int32_t* idx = reinterpret_cast<int32_t*>(sc + s.idx);
@@ -293,6 +301,10 @@ int moe_decode(const lps_moe_desc* m, float* x, void* scratch, hipStream_t st) {
   cp.wts = wts;
   cp.z = z;
   cp.x = x;
+  if (tee0 && tee1) {
+    cp.tee0 = tee0;
+    cp.tee1 = tee1;
+  }
   cp.d = m->d;
   cp.k = m->top_k;
   cp.remote_from = m->remote_from;

@@ -387,15 +387,22 @@ class DeviceDecoder:
 
     # ---- the whole pass as one graph --------------------------------------------
     def _walk_dpos(self):
-        """Enqueue all stages of one step, the position read from g_state[0]."""
+        """Enqueue all stages of one step, the position read from g_state[0].  On
+        one stream each boundary hop is folded into the producing stage's last
+        launch (lps_stage_forward_dpos_hop)."""
         n, st = self.n_stages, self.streams
         t = self.step_no
         pos_dev = ptr(self.g_state)
         for s in range(n):
-            if s > 0:
-                _hop(self.bounds[s - 1], ptr(self.x[s - 1]), ptr(self.x[s]), t, st[s - 1], st[s])
+            if s + 1 < n and st[s] is st[s + 1]:
+                lps.lps_stage_forward_dpos_hop(self.model, self._fence_c, n, s, ptr(self.x[s]),
+                                               pos_dev, ptr(self.scratch[s]), self.scratch_bytes,
+                                               self.bounds[s], ptr(self.x[s + 1]), t, sp(st[s]))
+                continue
             lps.lps_stage_forward_dpos(self.model, self._fence_c, n, s, ptr(self.x[s]), pos_dev,
                                        ptr(self.scratch[s]), self.scratch_bytes, sp(st[s]))
+            if s + 1 < n:
+                _hop(self.bounds[s], ptr(self.x[s]), ptr(self.x[s + 1]), t, st[s], st[s + 1])
         self.step_no += 1
 
     def capture_step(self, feed_dev, n_feed, tok_hist, logits_hist, hist_cap, ring=None):

@@ -251,6 +251,9 @@ def test_graph_and_device_state_entry_points_refuse_bad_arguments(L):
         L.lps_stage_forward_dpos(None, fence, 1, 0, 16, 16, 16, 1 << 20, None)
     assert e.value.code == L.LPS_EINVAL
     with pytest.raises(L.LpsError) as e:
+        L.lps_stage_forward_dpos_hop(None, fence, 1, 0, 16, 16, 16, 1 << 20, 16, 16, 0, None)
+    assert e.value.code == L.LPS_EINVAL
+    with pytest.raises(L.LpsError) as e:
         L.lps_stage_prefill(None, fence, 1, 0, 16, 4, 0, 16, 1 << 20, None)
     assert e.value.code == L.LPS_EINVAL
     assert L.lps_prefill_scratch_bytes(None, 4) == 0
@@ -282,6 +285,11 @@ def test_prefill_refuses_unsupported_layers_before_enqueue(L):
         with pytest.raises(L.LpsError) as e:        # rows past the cache
             L.lps_stage_prefill(h, fence, 1, 0, 256, 60, 8, 256, 1 << 30, None)
         assert e.value.code in (L.LPS_EUNSUP, L.LPS_ERANGE)
+        # the walk with a folded hop: no boundary, no receiver, a misaligned receiver
+        for b, xo in ((None, 256), (256, None), (256, 260)):
+            with pytest.raises(L.LpsError) as e:
+                L.lps_stage_forward_dpos_hop(h, fence, 1, 0, 256, 256, 256, 1 << 30, b, xo, 0, None)
+            assert e.value.code == L.LPS_EINVAL, (b, xo)
     finally:
         L.lps_model_destroy(h)
 

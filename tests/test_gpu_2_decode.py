@@ -316,3 +316,65 @@ def test_moe_stack_stages_equal_one_stage_decode_and_prefill(rt):
         got_pf = st.prefill(m["x_prefill"], n_pieces=8)
         assert np.array_equal(got_pf, ref_pf), fence
     st.close()
+
+
+@pytest.mark.parametrize("wdtype", ["f32", "bf16"])
+def test_stage_walk_with_folded_hop_equals_walk_then_hop(rt, wdtype):
+    """lps_stage_forward_dpos_hop (the hop's copy folded into the stage's last
+    launch) leaves the same bits as lps_stage_forward_dpos followed by
+    lps_boundary_hop: the stage's x, the slot of the step (the other slot left
+    alone) and the receiver's x, with one send and one receive counted; a step out
+    of order and a boundary of another width are refused before anything runs."""
+    import ctypes as C
+    from layer_pipeline_stage_amd import lps
+    from layer_pipeline_stage_amd.runtime import ptr
+    cfg = replace(synth.TINY, wdtype=wdtype, kvdtype=wdtype, prompt=2, steps=2)
+    m = synth.make_tiny(cfg)
+    dd = rt.DeviceDecoder(m, fence=[0, 2, 4], streams="single")
+    dd.g_state.copy_(torch.tensor([5, 0, 0, 0], dtype=torch.int32))
+    x0 = torch.from_numpy(np.random.default_rng(3).standard_normal(cfg.d).astype(np.float32))
+    st = torch.cuda.current_stream().cuda_stream
+    fence = lps.i32_array([0, 2, 4])
+
+    def boundary(n):
+        s0 = torch.full((n,), float("nan"), device="cuda")
+        s1 = torch.full((n,), float("nan"), device="cuda")
+        b = C.c_void_p()
+        lps.lps_boundary_create(n, ptr(s0), ptr(s1), C.byref(b))
+        return b, s0, s1
+
+    xa, xb = x0.cuda(), x0.cuda()
+    ya = torch.full((cfg.d,), float("nan"), device="cuda")
+    yb = ya.clone()
+    ba, sa0, sa1 = boundary(cfg.d)
+    bb, sb0, sb1 = boundary(cfg.d)
+    lps.lps_stage_forward_dpos(dd.model, fence, 2, 0, ptr(xa), ptr(dd.g_state), ptr(dd.scratch[0]),
+                               dd.scratch_bytes, st)
+    lps.lps_boundary_hop(ba, ptr(xa), ptr(ya), 0, st)
+    torch.cuda.synchronize()
+    c0 = lps.counters()
+    lps.lps_stage_forward_dpos_hop(dd.model, fence, 2, 0, ptr(xb), ptr(dd.g_state),
+                                   ptr(dd.scratch[0]), dd.scratch_bytes, bb, ptr(yb), 0, st)
+    torch.cuda.synchronize()
+    c1 = lps.counters()
+    assert torch.equal(xa, xb) and torch.equal(ya, yb) and torch.equal(sa0, sb0)
+    assert torch.equal(sb0, xb) and torch.equal(yb, xb) and not torch.equal(xb, x0.cuda())
+    assert torch.isnan(sb1).all()
+    assert c1["boundary_sends"] - c0["boundary_sends"] == 1
+    assert c1["boundary_recvs"] - c0["boundary_recvs"] == 1
+    assert c1["stage_walks"] - c0["stage_walks"] == 1
+    before = xb.clone()
+    with pytest.raises(lps.LpsError) as e:           # step 0 again
+        lps.lps_stage_forward_dpos_hop(dd.model, fence, 2, 0, ptr(xb), ptr(dd.g_state),
+                                       ptr(dd.scratch[0]), dd.scratch_bytes, bb, ptr(yb), 0, st)
+    assert e.value.code == lps.LPS_ESTATE
+    bw, _, _ = boundary(cfg.d + 8)
+    with pytest.raises(lps.LpsError) as e:           # rows of another width
+        lps.lps_stage_forward_dpos_hop(dd.model, fence, 2, 0, ptr(xb), ptr(dd.g_state),
+                                       ptr(dd.scratch[0]), dd.scratch_bytes, bw, ptr(yb), 0, st)
+    assert e.value.code == lps.LPS_EINVAL
+    torch.cuda.synchronize()
+    assert torch.equal(xb, before)
+    for b in (ba, bb, bw):
+        lps.lps_boundary_destroy(b)
+    dd.close()
