@@ -12,6 +12,7 @@
 #include "gemv_core.h"
 #include "internal.h"
 
+#include <algorithm>
 #include <cmath>
 
 namespace lps {
@@ -192,20 +193,139 @@ __global__ __launch_bounds__(256) void k_moe_combine(MoeCombP p) {
   __syncthreads();
   const int r = blockIdx.x * 256 + threadIdx.x;
   if (r >= p.d) return;
-  float local = 0.f, remote = 0.f;
-  for (int n = 0; n < p.k; ++n) {
-    const int j = order[n];
-    const float term = wts[j] * p.z[(long long)j * p.d + r];
-    if (ids[j] < p.remote_from) local += term;
-    else remote += term;
+  {
+    // every term is rounded before it is added: no product is fused into a sum
+#pragma clang fp contract(off)
+    float local = 0.f, remote = 0.f;
+    for (int n = 0; n < p.k; ++n) {
+      const int j = order[n];
+      const float term = wts[j] * p.z[(long long)j * p.d + r];
+      if (ids[j] < p.remote_from) local += term;
+      else remote += term;
+    }
+    const float r32 = static_cast<float>(static_cast<_Float16>(remote));
+    const float y = (p.z[(long long)p.k * p.d + r] + local) + r32;
+    const float v = p.x[r] + y;
+    p.x[r] = v;
+    if (p.tee0) {
+      p.tee0[r] = v;
+      p.tee1[r] = v;
+    }
   }
-  const float r32 = static_cast<float>(static_cast<_Float16>(remote));
-  const float y = (p.z[(long long)p.k * p.d + r] + local) + r32;
-  const float v = p.x[r] + y;
-  p.x[r] = v;
-  if (p.tee0) {
-    p.tee0[r] = v;
-    p.tee1[r] = v;
+}
+
+// The down projections and the combine in one launch (rows of up to 256 chunks,
+// ff <= 2048; longer rows take launch_moe_down and k_moe_combine).  A workgroup takes MOE_DC_R output rows for every slot: wave w walks the
+// slots j = w, w + nw, ... and for each the MOE_DC_R rows of slot j's down matrix,
+// each row's 16-byte chunks on the lanes as in the weight-streaming GEMV (lane l:
+// chunks l, l + 64, ...; chunks past the row load as zeros and meet zero
+// activations), so every z[j, r] is the GEMV's own value; the terms then meet in
+// LDS and the first MOE_DC_R threads add them as k_moe_combine does.
+#ifndef LPS_MOE_DC_R
+#define LPS_MOE_DC_R 4
+#endif
+constexpr int MOE_DC_R = LPS_MOE_DC_R;   // output rows per workgroup
+constexpr int MOE_DC_MAXW = 16;   // waves per workgroup at most
+struct MoeDownCombP {
+  const uint16_t* w_e;   // [E, d, ff] bf16
+  const uint16_t* w_s;   // [d, ff] bf16
+  const int32_t* idx;    // [k]
+  const float* wts;      // [k]
+  const float* m;        // [(k+1), ff] SwiGLU rows (slot k: the shared expert)
+  float* x;              // [d] residual, updated
+  float* tee0;           // [d] or NULL: the updated row, also stored here and to tee1
+  float* tee1;
+  int d, ff, k, remote_from, E;
+};
+
+template <int CPL>
+__global__ __launch_bounds__(MOE_DC_MAXW * WAVE) void k_moe_down_combine(MoeDownCombP p) {
+  __shared__ int ids[MOE_MAXK];
+  __shared__ float wts[MOE_MAXK];
+  __shared__ int order[MOE_MAXK];
+  __shared__ float zs[MOE_MAXK + 1][MOE_DC_R];
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
+  const int nw = blockDim.x / WAVE;
+  const int r0 = blockIdx.x * MOE_DC_R;
+  const int nck = p.ff / 8;
+  const int rowb = p.ff * 2;
+  if (threadIdx.x < p.k) {
+    ids[threadIdx.x] = min(max(p.idx[threadIdx.x], 0), p.E - 1);   // indices are device data
+    wts[threadIdx.x] = p.wts[threadIdx.x];
+  }
+  for (int j = wv; j <= p.k; j += nw) {
+    const int e = j < p.k ? min(max(p.idx[j], 0), p.E - 1) : 0;
+    const uint16_t* base = j < p.k ? p.w_e + (long long)e * p.d * p.ff : p.w_s;
+    u32x4 v[MOE_DC_R][CPL];
+#pragma unroll
+    for (int q = 0; q < MOE_DC_R; ++q) {
+      const int r = r0 + q;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(base + (long long)(r < p.d ? r : 0) * p.ff), (short)0,
+          r < p.d ? rowb : 0, 0x00020000);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c)
+        v[q][c] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (lane + WAVE * c) * 16, 0, 2));
+    }
+    f32x4 x0[CPL], x1[CPL];
+    const float* mj = p.m + (long long)j * p.ff;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int ch = lane + WAVE * c;
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+      x0[c] = ch < nck ? *reinterpret_cast<const f32x4*>(mj + ch * 8) : zero;
+      x1[c] = ch < nck ? *reinterpret_cast<const f32x4*>(mj + ch * 8 + 4) : zero;
+    }
+#pragma unroll
+    for (int q = 0; q < MOE_DC_R; ++q) {
+      // the products of acc_chunk<LPS_BF16>, in its order
+      float a = 0.f;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const u32x4 w = v[q][c];
+        a = fmaf(bf16_lo(w.x), x0[c].x, a);
+        a = fmaf(bf16_hi(w.x), x0[c].y, a);
+        a = fmaf(bf16_lo(w.y), x0[c].z, a);
+        a = fmaf(bf16_hi(w.y), x0[c].w, a);
+        a = fmaf(bf16_lo(w.z), x1[c].x, a);
+        a = fmaf(bf16_hi(w.z), x1[c].y, a);
+        a = fmaf(bf16_lo(w.w), x1[c].z, a);
+        a = fmaf(bf16_hi(w.w), x1[c].w, a);
+      }
+      a = wave_sum(a);
+      if (lane == 0) zs[j][q] = a;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < p.k) {
+    // rank of this slot by (expert id, slot): a permutation even if ids repeat
+    int rank = 0;
+    for (int j = 0; j < p.k; ++j)
+      rank += ids[j] < ids[threadIdx.x] || (ids[j] == ids[threadIdx.x] && j < int(threadIdx.x));
+    order[rank] = threadIdx.x;
+  }
+  __syncthreads();
+  if (threadIdx.x < MOE_DC_R && r0 + int(threadIdx.x) < p.d) {
+#pragma clang fp contract(off)
+    // as k_moe_combine: every term rounded before it is added
+    const int q = threadIdx.x, r = r0 + q;
+    float local = 0.f, remote = 0.f;
+    for (int n = 0; n < p.k; ++n) {
+      const int j = order[n];
+      const float term = wts[j] * zs[j][q];
+      if (ids[j] < p.remote_from) local += term;
+      else remote += term;
+    }
+    const float r32 = static_cast<float>(static_cast<_Float16>(remote));
+    const float y = (zs[p.k][q] + local) + r32;
+    const float v = p.x[r] + y;
+    p.x[r] = v;
+    if (p.tee0) {
+      p.tee0[r] = v;
+      p.tee1[r] = v;
+    }
   }
 }
 
@@ -292,6 +412,35 @@ int moe_decode(const lps_moe_desc* m, float* x, void* scratch, hipStream_t st, f
   rc = launch_moe_gu(m->w_gu_e, m->w_gu_s, idx, m->n_experts, m->top_k, m->ff, m->d, x, m->g_ffn,
                      m->eps, mbuf, st, timer_take(LPS_KIND_MOE_GU));
   if (rc) return rc;
+  const int cpl = (m->ff / 8 + WAVE - 1) / WAVE;
+  if (cpl <= 4) {   // rows of up to 256 chunks: down projections and combine in one launch
+    MoeDownCombP dp{};
+    dp.w_e = static_cast<const uint16_t*>(m->w_d_e);
+    dp.w_s = static_cast<const uint16_t*>(m->w_d_s);
+    dp.idx = idx;
+    dp.wts = wts;
+    dp.m = mbuf;
+    dp.x = x;
+    if (tee0 && tee1) {
+      dp.tee0 = tee0;
+      dp.tee1 = tee1;
+    }
+    dp.d = m->d;
+    dp.ff = m->ff;
+    dp.k = m->top_k;
+    dp.remote_from = m->remote_from;
+    dp.E = m->n_experts;
+    const dim3 grid((m->d + MOE_DC_R - 1) / MOE_DC_R);
+    const dim3 block(std::min(m->top_k + 1, MOE_DC_MAXW) * WAVE);
+    const Stamp sp = timer_take(LPS_KIND_MOE_DOWN);
+#define LPS_DC(C) LPS_LAUNCH(k_moe_down_combine<C>, grid, block, 0, st, sp.start, sp.stop, dp)
+    if (cpl <= 1) LPS_DC(1);
+    else if (cpl <= 2) LPS_DC(2);
+    else LPS_DC(4);
+#undef LPS_DC
+    LPS_HIP(hipGetLastError());
+    return LPS_OK;
+  }
   float* z = reinterpret_cast<float*>(sc + s.z);
   rc = launch_moe_down(m->w_d_e, m->w_d_s, idx, m->n_experts, m->top_k, m->d, m->ff, mbuf, z, st,
                        timer_take(LPS_KIND_MOE_DOWN));

@@ -730,3 +730,63 @@ def test_moe_route_parity(L, d, E):
     L.lps_moe_route(C.byref(desc2), ptr(Xd), 4, ptr(idx), ptr(w), ptr(sc), sb, stream())
     assert np.array_equal(idx.cpu().numpy()[:4], np.tile(np.arange(8, dtype=np.int32), (4, 1)))
     assert np.allclose(w.cpu().numpy()[:4], 1 / 8, rtol=0, atol=1e-7)
+
+
+@pytest.mark.parametrize("d,E,k,ff", [(2048, 64, 8, 1024), (512, 32, 4, 200), (512, 24, 15, 2048),
+                                      (256, 16, 4, 2304)])
+def test_moe_layer_down_and_combine_equal_slot_gemvs_and_ordered_sum(L, d, E, k, ff):
+    """The MoE decode layer's down projections and ordered combine (one launch for
+    rows of up to 256 chunks, two above): x' equals, bit for bit, lps_gemv on every
+    slot's down matrix with that slot's SwiGLU row (the layer's own selection,
+    weights and SwiGLU rows, read from its scratch) followed by the combine done
+    on the host in f32 in its order: terms w_j z_j in ascending expert id within
+    each half, y = (shared + local) + f32(f16(remote)), x + y.  Ragged rows (ff =
+    200: 25 chunks), 16 slots in one workgroup, and the two-launch form (ff = 2304)."""
+    cfg = synth.MoEConfig("dc", n_layers=1, d=d, n_experts=E, top_k=k, ff=ff, remote_from=E // 2,
+                          prefill_T=0, steps=1)
+    m = synth.make_moe(cfg)
+    Lw = m["layers"][0]
+    t = {n: dev(Lw[n]) for n in ("g_ffn", "w_r", "w_gu_e", "w_d_e", "w_gu_s", "w_d_s")}
+    desc = L.MoEDesc()
+    desc.d, desc.n_experts, desc.top_k, desc.ff, desc.remote_from, desc.eps = d, E, k, ff, E // 2, cfg.eps
+    for n in ("g_ffn", "w_r", "w_gu_e", "w_d_e", "w_gu_s", "w_d_s"):
+        setattr(desc, n, ptr(t[n]))
+    sb = L.lps_moe_layer_scratch_bytes(C.byref(desc))
+    sc = torch.zeros(sb, dtype=torch.uint8, device=DEV)
+    x0 = m["x_in"][0]
+    x = dev(x0)
+    L.lps_moe_layer_decode(C.byref(desc), ptr(x), ptr(sc), sb, stream())
+    torch.cuda.synchronize()
+    got = x.cpu().numpy()
+    # the layer's scratch: ids [16 int32], weights, logits [E], SwiGLU rows [(k+1), ff]
+    a256 = lambda n: (n + 255) // 256 * 256
+    o_w = a256(16 * 4)
+    o_m = o_w + a256(k * 4) + a256(E * 4)
+    ids = sc[:4 * k].view(torch.int32).cpu().numpy()
+    wts = sc[o_w:o_w + 4 * k].view(torch.float32).cpu().numpy()
+    mrows = sc[o_m:o_m + 4 * (k + 1) * ff].view(torch.float32).reshape(k + 1, ff)
+    assert len(set(ids.tolist())) == k and ids.min() >= 0 and ids.max() < E
+    z = []
+    for j in range(k + 1):
+        wj = t["w_d_e"][int(ids[j])] if j < k else t["w_d_s"]
+        zj = torch.zeros(d, dtype=torch.float32, device=DEV)
+        L.lps_gemv(L.LPS_BF16, ptr(wj), None, d, ff, ptr(mrows[j].contiguous()), None, 0.0, ptr(zj),
+                   L.LPS_EPI_STORE, stream())
+        z.append(zj)
+    torch.cuda.synchronize()
+    z = np.stack([zj.cpu().numpy() for zj in z])
+    order = sorted(range(k), key=lambda j: (int(ids[j]), j))
+    f32 = np.float32
+    want = np.empty(d, np.float32)
+    for r in range(d):
+        local, remote = f32(0), f32(0)
+        for j in order:
+            term = f32(wts[j]) * f32(z[j, r])
+            if ids[j] < E // 2:
+                local = f32(local + term)
+            else:
+                remote = f32(remote + term)
+        r32 = f32(np.float16(remote))
+        y = f32(f32(z[k, r] + local) + r32)
+        want[r] = f32(f32(x0[r]) + y)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))

@@ -378,3 +378,41 @@ def test_stage_walk_with_folded_hop_equals_walk_then_hop(rt, wdtype):
     for b in (ba, bb, bw):
         lps.lps_boundary_destroy(b)
     dd.close()
+
+
+def test_moe_stage_walk_with_folded_hop_equals_walk_then_hop(rt):
+    """The folded hop on an MoE stage (its last launch is the down projections and
+    the ordered combine): the same bits as lps_stage_forward + lps_boundary_hop in
+    x, the step's slot and the receiver's x."""
+    import ctypes as C
+    from layer_pipeline_stage_amd import lps
+    from layer_pipeline_stage_amd.runtime import ptr
+    cfg = synth.MoEConfig("moe-hop", n_layers=2, d=512, n_experts=16, top_k=4, ff=128, remote_from=8,
+                          prefill_T=0, steps=1)
+    m = synth.make_moe(cfg)
+    stk = rt.DeviceMoEStack(m, fence=[0, 1, 2], streams="single")
+    st = torch.cuda.current_stream().cuda_stream
+    fence = lps.i32_array([0, 1, 2])
+    pos = torch.zeros(4, dtype=torch.int32, device="cuda")
+    outs = []
+    for folded in (False, True):
+        s0 = torch.full((cfg.d,), float("nan"), device="cuda")
+        s1 = torch.full((cfg.d,), float("nan"), device="cuda")
+        b = C.c_void_p()
+        lps.lps_boundary_create(cfg.d, ptr(s0), ptr(s1), C.byref(b))
+        x = torch.from_numpy(m["x_in"][0].copy()).cuda()
+        y = torch.full((cfg.d,), float("nan"), device="cuda")
+        if folded:
+            lps.lps_stage_forward_dpos_hop(stk.model, fence, 2, 0, ptr(x), ptr(pos), ptr(stk.scratch[0]),
+                                           stk.scratch_bytes, b, ptr(y), 0, st)
+        else:
+            lps.lps_stage_forward(stk.model, fence, 2, 0, ptr(x), 0, ptr(stk.scratch[0]),
+                                  stk.scratch_bytes, st)
+            lps.lps_boundary_hop(b, ptr(x), ptr(y), 0, st)
+        torch.cuda.synchronize()
+        outs.append((x.cpu(), y.cpu(), s0.cpu(), s1.cpu()))
+        lps.lps_boundary_destroy(b)
+    (xa, ya, sa, _), (xb, yb, sb, sb1) = outs
+    assert torch.equal(xa, xb) and torch.equal(ya, yb) and torch.equal(sa, sb)
+    assert torch.equal(sb, xb) and torch.isnan(sb1).all()
+    stk.close()
