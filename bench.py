@@ -59,7 +59,7 @@ def algorithmic_bytes(cfg, n_rows: int) -> dict:
 # scaled by what the same counters read for the 256 MiB calibration copy
 # (`python bench.py --copy-calibration`: FETCH x 2.0, WRITE x 1.0).  Valid only for
 # the kernel sources it was taken on (hash below); otherwise reported as null.
-GATEUP_TRAFFIC = {"src_sha256_16": "02a09746001dbb4b", "fetch_kib": 114866.0, "write_kib": 112.0,
+GATEUP_TRAFFIC = {"src_sha256_16": "c4aa42dc9be3ee16", "fetch_kib": 114866.5, "write_kib": 112.0,
                   "fetch_scale": 2.0, "write_scale": 1.0}
 GEMV_SOURCES = ("layer_pipeline_stage_amd/csrc/gemv.hip", "layer_pipeline_stage_amd/csrc/gemv_core.h",
                 "layer_pipeline_stage_amd/csrc/dev.h")

@@ -51,6 +51,16 @@ constexpr int DPP_ROR8 = 0x128;        // lane i <- (i + 8) % 16, i.e. i ^ 8
 constexpr int DPP_BCAST15 = 0x142;     // rows 1, 3 <- lane 15 of rows 0, 2
 constexpr int DPP_BCAST31 = 0x143;     // rows 2, 3 <- lane 31
 
+// A workgroup barrier for LDS traffic only: this wave's LDS operations complete
+// (lgkmcnt 0), then s_barrier.  Unlike __syncthreads it does not wait for the
+// wave's outstanding global loads, so weight loads stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // vmcnt 63, expcnt 7, lgkmcnt 0
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 __device__ __forceinline__ float lane63(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }

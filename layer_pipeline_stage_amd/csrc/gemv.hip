@@ -330,21 +330,35 @@ __global__ __launch_bounds__(NT) void k_gemv_buf(GemvP p) {
   u32x4 va0[U], va1[U], vb0[U], vb1[U];
   uint32_t sa0[U], sa1[U], sb0[U], sb1[U];
   float ya0 = 0.f, ya1 = 0.f, yb0 = 0.f, yb1 = 0.f;   // residual rows (EPI_ADD)
-  BUF_LOAD(va0, va1, sa0, sa1, ya0, ya1, u, 0, u < p.units)
-  // a chunk past the row end (zero weights) reads the zero chunk after the staged vector
-  const int zoff = WT == LPS_MXFP4 ? nck * XS : p.K;
-  float xback = 1.f;   // MXFP4: the power of two the staged vector was scaled down by
+  // the vector's loads (and the norm gain's) go out before the first weight batch,
+  // so the staging waits one L2 round trip rather than that batch (loads complete
+  // in issue order)
+  constexpr int MXR = WT == LPS_MXFP4 ? mx16_maxr(U, NT) : 1;
+  Mx16Vec<NORM, MXR> xv;
+  f32x4 gpre[GPRE];
   if constexpr (WT == LPS_MXFP4) {
-    xback = stage_x_mx16<NORM, NT, mx16_maxr(U, NT)>(p.x, p.g, p.eps, p.K, xh);
+    stage_x_mx16_load<NORM, NT, MXR>(p.x, p.g, p.K, xv);
   } else {
-    if (threadIdx.x < CH) xs[zoff + threadIdx.x] = 0.f;   // zero chunk
     // MoE down: a workgroup's units all belong to one slot (the launch gives every
     // wave one unit and a slot's unit count is a multiple of the waves per group),
     // so it stages only that slot's activations
     const float* xsrc = p.x;
     if constexpr (EPI == EPI_MOEDN)
       xsrc += (long long)((blockIdx.x * NW) / (p.rps >> 1)) * p.K;
-    stage_x<NORM, NT>(xsrc, p.g, p.eps, p.K, xs);
+    stage_x_issue<NORM, NT>(xsrc, p.g, p.K, xs, gpre);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  BUF_LOAD(va0, va1, sa0, sa1, ya0, ya1, u, 0, u < p.units)
+  __builtin_amdgcn_sched_barrier(0);
+  // a chunk past the row end (zero weights) reads the zero chunk after the staged vector
+  const int zoff = WT == LPS_MXFP4 ? nck * XS : p.K;
+  float xback = 1.f;   // MXFP4: the power of two the staged vector was scaled down by
+  if constexpr (WT == LPS_MXFP4) {
+    xback = stage_x_mx16_store<NORM, NT, MXR>(xv, p.x, p.eps, p.K, xh);
+  } else {
+    if (threadIdx.x < CH) xs[zoff + threadIdx.x] = 0.f;   // zero chunk
+    // the weight batch above is 2 U loads (2 U + 2 with the residual rows) after the copy
+    stage_x_finish<NORM, NT, 2 * U>(p.g, p.eps, p.K, xs, gpre);
   }
   if (u < p.units) {
     // MXFP4: matrix-core accumulators (acc_chunk_mx16), one per row

@@ -60,19 +60,27 @@ __device__ __forceinline__ void scale4(float* px, float r, const f32x4 gg) {
   *reinterpret_cast<f32x4*>(px) = v;
 }
 
+// gfx9 s_waitcnt immediate that waits until at most vm vector-memory loads are
+// outstanding (lgkmcnt and expcnt left at their maxima)
+constexpr int vm_wait(int vm) { return (vm & 15) | (7 << 4) | (15 << 8) | ((vm >> 4) << 14); }
+
 // Stage the activation vector in LDS; with NORM, as RMSNorm(x) * g.  The copy
 // uses the LDS DMA path (global_load_lds_dwordx4: each lane's 16 bytes land at
 // the wave's LDS base + 16 * lane, no VGPRs): every wave issues all of its
 // 1 KiB pieces back to back, so staging costs one L2 round trip rather than one
 // per piece.  x must be 16-byte aligned and K a multiple of 4.
+// In two parts: stage_x_issue sends the gain's loads and the copy; stage_x_finish
+// waits until at most VM later loads are outstanding (loads complete in issue order,
+// so a caller that issues VM weight loads in between has them in flight while the
+// staging completes), then normalises.
 template <bool NORM, int NT = GEMV_THREADS>
-__device__ __forceinline__ void stage_x(const float* x, const float* g, float eps, int K, float* xs) {
+__device__ __forceinline__ void stage_x_issue(const float* x, const float* g, int K, float* xs,
+                                              f32x4 (&gpre)[GPRE]) {
   constexpr int NW = NT / WAVE;
   const int tid = threadIdx.x;
   const int lane = tid & (WAVE - 1);
   const int wv = tid / WAVE;
   // the norm gain goes out with the copy (same wait), for K <= NT * 4 * GPRE
-  f32x4 gpre[GPRE];
   if (NORM) {
 #pragma unroll
     for (int i = 0; i < GPRE; ++i) {
@@ -85,8 +93,20 @@ __device__ __forceinline__ void stage_x(const float* x, const float* g, float ep
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(x + b + 4 * lane),
                                        (__attribute__((address_space(3))) void*)(xs + b), 16, 0, 0);
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+}
+template <bool NORM, int NT, int VM>
+__device__ __forceinline__ void stage_x_finish(const float* g, float eps, int K, float* xs,
+                                               const f32x4 (&gpre)[GPRE]) {
+  constexpr int NW = NT / WAVE;
+  const int tid = threadIdx.x;
+  const int lane = tid & (WAVE - 1);
+  const int wv = tid / WAVE;
+  // the copy has landed (at most VM later loads outstanding) and this wave's LDS
+  // stores are done; the barrier leaves the later loads in flight
+  __builtin_amdgcn_s_waitcnt(vm_wait(VM) & ~(15 << 8));
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   if (NORM) {
     __shared__ float red[NW];
     float ss = 0.f;
@@ -96,7 +116,7 @@ __device__ __forceinline__ void stage_x(const float* x, const float* g, float ep
     }
     ss = wave_sum(ss);
     if (lane == 0) red[wv] = ss;
-    __syncthreads();
+    lds_barrier();
     float tot = 0.f;
 #pragma unroll
     for (int i = 0; i < NW; ++i) tot += red[i];
@@ -108,8 +128,14 @@ __device__ __forceinline__ void stage_x(const float* x, const float* g, float ep
     }
     for (int k = (tid + GPRE * NT) * 4; k < K; k += NT * 4)
       scale4(xs + k, r, *reinterpret_cast<const f32x4*>(g + k));
-    __syncthreads();
+    lds_barrier();
   }
+}
+template <bool NORM, int NT = GEMV_THREADS>
+__device__ __forceinline__ void stage_x(const float* x, const float* g, float eps, int K, float* xs) {
+  f32x4 gpre[GPRE];
+  stage_x_issue<NORM, NT>(x, g, K, xs, gpre);
+  stage_x_finish<NORM, NT, 0>(g, eps, K, xs, gpre);
 }
 
 // MXFP4 rows against f16 activations.  The activation vector is staged in LDS as
@@ -170,27 +196,43 @@ __device__ __forceinline__ float acc_value(f32x4m d) {
 // e the smallest power that brings it to at most 2^15, so none rounds to an f16
 // infinity; the return value 2^e scales the products back (exact powers of two,
 // and 1 for every vector below 2^15, where the staging is unchanged).
+// The staging in two parts, so that a caller can issue the vector's loads (and the
+// norm gain's) before its first weight loads: loads return in issue order, so a
+// staging whose loads follow the weight batch would wait for that whole batch.
+template <bool NORM, int MAXR>
+struct Mx16Vec {
+  f32x4 v[MAXR];
+  f32x4 g[NORM ? MAXR : 1];
+};
 template <bool NORM, int NT, int MAXR>
-__device__ __forceinline__ float stage_x_mx16(const float* x, const float* g, float eps, int K,
-                                              _Float16* xs) {
-  constexpr int NW = NT / WAVE;
+__device__ __forceinline__ void stage_x_mx16_load(const float* x, const float* g, int K,
+                                                  Mx16Vec<NORM, MAXR>& s) {
   const int tid = threadIdx.x;
   const int ng = K / 4;
-  f32x4 v[MAXR];
 #pragma unroll
   for (int i = 0; i < MAXR; ++i) {
     const int G = tid + i * NT;
-    v[i] = G < ng ? *reinterpret_cast<const f32x4*>(x + 4 * G) : f32x4{0.f, 0.f, 0.f, 0.f};
+    s.v[i] = G < ng ? *reinterpret_cast<const f32x4*>(x + 4 * G) : f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (NORM)
+      s.g[i] = G < ng ? *reinterpret_cast<const f32x4*>(g + 4 * G) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
+}
+template <bool NORM, int NT, int MAXR>
+__device__ __forceinline__ float stage_x_mx16_store(const Mx16Vec<NORM, MAXR>& s, const float* x,
+                                                   float eps, int K, _Float16* xs) {
+  constexpr int NW = NT / WAVE;
+  const int tid = threadIdx.x;
+  const int ng = K / 4;
   float r = 1.f;
   if (NORM) {
     __shared__ float red[NW];
     float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < MAXR; ++i) ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+    for (int i = 0; i < MAXR; ++i)
+      ss += s.v[i].x * s.v[i].x + s.v[i].y * s.v[i].y + s.v[i].z * s.v[i].z + s.v[i].w * s.v[i].w;
     ss = wave_sum(ss);
     if ((tid & (WAVE - 1)) == 0) red[tid / WAVE] = ss;
-    __syncthreads();
+    lds_barrier();
     float tot = 0.f;
 #pragma unroll
     for (int i = 0; i < NW; ++i) tot += red[i];
@@ -202,7 +244,7 @@ __device__ __forceinline__ float stage_x_mx16(const float* x, const float* g, fl
     float m = 0.f;
 #pragma unroll
     for (int i = 0; i < MAXR; ++i)
-      m = fmaxf(m, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(s.v[i].x), fabsf(s.v[i].y)), fmaxf(fabsf(s.v[i].z), fabsf(s.v[i].w))));
     m = wave_max(m);
     if ((tid & (WAVE - 1)) == 0) mx[tid / WAVE] = m;
   }
@@ -210,9 +252,9 @@ __device__ __forceinline__ float stage_x_mx16(const float* x, const float* g, fl
   for (int i = 0; i < MAXR; ++i) {
     const int G = tid + i * NT;
     if (G < ng) {
-      f32x4 y = v[i];
-      if (NORM) {
-        const f32x4 gg = *reinterpret_cast<const f32x4*>(g + 4 * G);
+      f32x4 y = s.v[i];
+      if constexpr (NORM) {
+        const f32x4 gg = s.g[i];
         y.x = y.x * r * gg.x;
         y.y = y.y * r * gg.y;
         y.z = y.z * r * gg.z;
@@ -225,7 +267,7 @@ __device__ __forceinline__ float stage_x_mx16(const float* x, const float* g, fl
     }
   }
   if (tid < 16) *reinterpret_cast<h2*>(xs + (K / 32) * MX16_XS + 2 * tid) = h2{0, 0};   // zero chunk
-  __syncthreads();
+  lds_barrier();
   float back = 1.f;
   if (!NORM) {
     float am = 0.f;
@@ -243,7 +285,7 @@ __device__ __forceinline__ float stage_x_mx16(const float* x, const float* g, fl
         *reinterpret_cast<h2*>(dst) = h2{(_Float16)(y.x * sc), (_Float16)(y.y * sc)};
         *reinterpret_cast<h2*>(dst + 2) = h2{(_Float16)(y.z * sc), (_Float16)(y.w * sc)};
       }
-      __syncthreads();
+      lds_barrier();
     }
   }
   return back;
