@@ -296,10 +296,12 @@ void k_attn_mfma(AttnP p) {
   for (int dt = 0; dt < DT; ++dt)
     vr[dt] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
                                            vrs, (vt + (16 * dt + col) * 16 + 4 * grp) * 2, 0, 2));
-  // every load is in flight before any arithmetic: one HBM round trip per wave
+  // every load is in flight before any arithmetic: one HBM round trip per wave.  The
+  // barrier waits for LDS traffic only, so the scores start once K has landed while
+  // V is still on its way.
   __builtin_amdgcn_sched_barrier(0);
   if (threadIdx.x < G * HD / 4) qs[threadIdx.x] = qv;
-  __syncthreads();
+  lds_barrier();
 
   // ---- scores ----
   // B operand: q of head col (zero for the padding columns), dims 32 kk + 8 grp .. + 7

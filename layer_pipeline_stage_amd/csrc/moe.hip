@@ -50,11 +50,17 @@ __global__ __launch_bounds__(ROUTE_EPB * WAVE) void k_route_logits(RouteP p) {
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(p.wr + (long long)(e < p.E ? e : 0) * p.d), (short)0,
       e < p.E ? p.d * 2 : 0, 0x00020000);
+  // the row's loads and the gain's go out first: loads complete in issue order, so
+  // the staging then waits one L2 round trip, not the expert rows
+  f32x4 gpre[GPRE];
+  stage_x_issue<true, ROUTE_EPB * WAVE>(p.x + (long long)t * p.d, p.g, p.d, xs, gpre);
+  __builtin_amdgcn_sched_barrier(0);
   u32x4 v[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c)
     v[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (lane + WAVE * c) * 16, 0, 0));
-  stage_x<true, ROUTE_EPB * WAVE>(p.x + (long long)t * p.d, p.g, p.eps, p.d, xs);
+  __builtin_amdgcn_sched_barrier(0);
+  stage_x_finish<true, ROUTE_EPB * WAVE, CPL>(p.g, p.eps, p.d, xs, gpre);
   float a = 0.f;
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
