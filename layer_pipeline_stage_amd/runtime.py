@@ -432,17 +432,18 @@ class DeviceDecoder:
         return g
 
     def run_tokens_graph(self, prompt, n_steps=0, feed=None, p0=None, logits=True,
-                         timer=None) -> StepResult:
+                         timer=None, mark_every=3) -> StepResult:
         """run_tokens with the whole step captured once and replayed: the
         position, the step and the next input id live on the device and are
         advanced by the graph itself, so the host only launches replays.  The
         step's own kernels store its argmax (and, with logits=True, its logits)
-        into row t % ring of the pinned host ring; after each replay a pending
-        marks the step (lps_pending_mark), and the host drains step t - ring
-        while later replays run.  (A copy on the readback stream would make that
-        stream wait for every step, which costs the replays ~45 us per step.)
-        timer: an optional callable run around the replays and their readback
-        (for the bench)."""
+        into row t % ring of the pinned host ring; a pending marks every
+        mark_every-th replay and the last (lps_pending_mark: each mark costs the
+        stream a system-scope fence), and the host drains step t - ring, waiting
+        for the first mark at or after it, while later replays run.  (A copy on
+        the readback stream would make that stream wait for every step, which
+        costs the replays ~45 us per step.)  timer: an optional callable run
+        around the replays and their readback (for the bench)."""
         cfg = self.cfg
         assert self.head is not None, "model has no vocabulary"
         p = cfg.prefix if p0 is None else p0
@@ -462,10 +463,16 @@ class DeviceDecoder:
         g = self.capture_step(ptr(feed_dev), P, ptr(tok_hist), None, total, ring)
         pend = [None] * R
         toks, lg = [None] * total, [None] * total
+        M = max(1, min(mark_every, R - 1))   # a mark is launched before its steps' rows are reused
+
+        def marked(i):
+            return i % M == M - 1 or i == total - 1
 
         def drain(i):
-            lps.lps_pending_wait(pend[i % R])
-            pend[i % R] = None
+            j = min(i + (M - 1 - i % M), total - 1)    # the first marked step at or after i
+            if pend[j % R] is not None:
+                lps.lps_pending_wait(pend[j % R])
+                pend[j % R] = None
             toks[i] = int(self.host_tok[i % R])
             if logits:
                 lg[i] = self.host_logits[i % R].numpy().copy()
@@ -482,9 +489,10 @@ class DeviceDecoder:
                 if i >= R:
                     drain(i - R)             # frees host ring slot i % R
                 lps.lps_graph_launch(g, sp(st0))
-                h = C.c_void_p()
-                lps.lps_pending_mark(sp(st0), C.byref(h))
-                pend[i % R] = h
+                if marked(i):
+                    h = C.c_void_p()
+                    lps.lps_pending_mark(sp(st0), C.byref(h))
+                    pend[i % R] = h
             for i in range(max(0, total - R), total):
                 drain(i)
             if timer is not None:

@@ -142,6 +142,20 @@ def test_graph_replay_equals_eager_tiny(rt):
         dd.close()
 
 
+def test_graph_replay_marks_every_few_steps(rt):
+    """The replay loop marks one replay in mark_every (and the last); every step's
+    row is still drained after a mark that covers it: the same ids and logits for
+    a mark every replay, every second, every third, and more than the ring holds."""
+    cfg = replace(synth.TINY, prompt=3, steps=13)
+    m = synth.make_tiny(cfg)
+    dd = rt.DeviceDecoder(m, fence=[0, 2, 4], streams="single")
+    ref = dd.run_tokens(m["prompt"], cfg.steps)
+    for me in (1, 2, 3, 9):
+        dd.reset()
+        _same(dd.run_tokens_graph(m["prompt"], cfg.steps, mark_every=me), ref)
+    dd.close()
+
+
 def test_graph_replay_per_stage_streams_and_eager_after(rt):
     """N = 4 on four streams: the capture forks the later stage streams in
     through the boundary events and joins them back; replays equal the eager
