@@ -81,6 +81,23 @@ def memory_balanced_fence(n_layers, d, nq, nkv, hd, ff, vocab, wdtype, kvdtype, 
                            n_stages, max_groups)
 
 
+def mark_schedule(total, ring, mark_every):
+    """The replay loop's marks: marked(i) says whether a pending follows replay i
+    (every mark_every-th and the last; mark_every is capped at ring - 1 so that
+    the mark covering step i is launched before step i + ring reuses its row), and
+    cover(i) is the first marked step at or after i, whose pending the drain of
+    step i waits for."""
+    m = max(1, min(mark_every, ring - 1))
+
+    def marked(i):
+        return i % m == m - 1 or i == total - 1
+
+    def cover(i):
+        return min(i + (m - 1 - i % m), total - 1)
+
+    return marked, cover
+
+
 def _hop(b, src, dst, step, producer, consumer):
     """One boundary crossing: the send and the receive, or on the same-stream seam
     the single-kernel hop."""
@@ -463,13 +480,10 @@ class DeviceDecoder:
         g = self.capture_step(ptr(feed_dev), P, ptr(tok_hist), None, total, ring)
         pend = [None] * R
         toks, lg = [None] * total, [None] * total
-        M = max(1, min(mark_every, R - 1))   # a mark is launched before its steps' rows are reused
-
-        def marked(i):
-            return i % M == M - 1 or i == total - 1
+        marked, cover = mark_schedule(total, R, mark_every)
 
         def drain(i):
-            j = min(i + (M - 1 - i % M), total - 1)    # the first marked step at or after i
+            j = cover(i)                    # the first marked step at or after i
             if pend[j % R] is not None:
                 lps.lps_pending_wait(pend[j % R])
                 pend[j % R] = None

@@ -365,3 +365,38 @@ def test_pending_tokens_refuse_a_second_use(L):
     with pytest.raises(L.LpsError) as e:
         L.lps_pending_order((1 << 32) | 1, None)
     assert e.value.code == L.LPS_ESTATE
+
+
+@pytest.mark.parametrize("ring", [1, 2, 3, 4, 8])
+def test_replay_mark_schedule_drains_every_step_after_its_mark(ring):
+    """The graph replay loop's marking (runtime.mark_schedule), run as the loop runs
+    it: every step is drained once, after a mark at or after it that was already
+    launched, before its host-ring row is reused; each mark is waited once and no
+    mark is stored over one that was never waited."""
+    from layer_pipeline_stage_amd.runtime import mark_schedule
+    for total in range(1, 30):
+        for every in (1, 2, 3, 5, 64):
+            marked, cover = mark_schedule(total, ring, every)
+            pend, waited, launched, drained = [None] * ring, set(), -1, []
+
+            def drain(i):
+                j = cover(i)
+                assert marked(j) and i <= j <= launched < i + ring, (total, every, i, j, launched)
+                if pend[j % ring] is not None:
+                    assert pend[j % ring] == j
+                    waited.add(j)
+                    pend[j % ring] = None
+                assert j in waited
+                drained.append(i)
+
+            for i in range(total):
+                if i >= ring:
+                    drain(i - ring)
+                launched = i
+                if marked(i):
+                    assert pend[i % ring] is None
+                    pend[i % ring] = i
+            for i in range(max(0, total - ring), total):
+                drain(i)
+            assert drained == list(range(total)) and all(p is None for p in pend)
+            assert waited == {i for i in range(total) if marked(i)}
