@@ -500,7 +500,9 @@ static int launch_t(const GemvP& p, hipStream_t st, Stamp sp, int* waves) {
     if (WT == LPS_MXFP4 && p.K / 4 > mx16_maxr(UU, NTV) * (NTV))                                \
       return fail(LPS_EUNSUP, "gemv: MXFP4 K %d above %d", p.K, 4 * mx16_maxr(UU, NTV) * (NTV)); \
     int grid = (p.units + NW_ - 1) / NW_;                                                        \
-    if (EPI != EPI_MOEDN && grid > (MAXBV)) grid = (MAXBV);  /* MoE down: one unit per wave */   \
+    /* MoE: one unit per wave (the expert gate/up's 9 x 1024 units would otherwise leave  \
+       one wave in eight with a second unit after the others are done) */                  \
+    if (EPI != EPI_MOEDN && EPI != EPI_MOEGU && grid > (MAXBV)) grid = (MAXBV);              \
     if (grid < 1) grid = 1;                                                                      \
     const bool db = p.units > grid * NW_ || per_lane > (UU);                                     \
     if (waves) *waves = grid * NW_;                                                              \
