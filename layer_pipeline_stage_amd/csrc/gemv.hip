@@ -500,9 +500,11 @@ static int launch_t(const GemvP& p, hipStream_t st, Stamp sp, int* waves) {
     if (WT == LPS_MXFP4 && p.K / 4 > mx16_maxr(UU, NTV) * (NTV))                                \
       return fail(LPS_EUNSUP, "gemv: MXFP4 K %d above %d", p.K, 4 * mx16_maxr(UU, NTV) * (NTV)); \
     int grid = (p.units + NW_ - 1) / NW_;                                                        \
-    /* MoE: one unit per wave (the expert gate/up's 9 x 1024 units would otherwise leave  \
-       one wave in eight with a second unit after the others are done) */                  \
-    if (EPI != EPI_MOEDN && EPI != EPI_MOEGU && grid > (MAXBV)) grid = (MAXBV);              \
+    /* one unit per wave for the MoE down, and for launches whose units are one batch     \
+       each and would come to fewer than two per wave under the cap (there the cap leaves \
+       some waves a second unit after the others are done); otherwise capped */           \
+    const bool each_ = EPI == EPI_MOEDN || (per_lane <= (UU) && p.units < 2 * (MAXBV) * NW_);  \
+    if (!each_ && grid > (MAXBV)) grid = (MAXBV);                                              \
     if (grid < 1) grid = 1;                                                                      \
     const bool db = p.units > grid * NW_ || per_lane > (UU);                                     \
     if (waves) *waves = grid * NW_;                                                              \
