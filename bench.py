@@ -54,27 +54,31 @@ def algorithmic_bytes(cfg, n_rows: int) -> dict:
     }
 
 
-# HBM traffic of the gate/up GEMV measured by rocprofv3 PMC counters (FETCH_SIZE,
-# WRITE_SIZE, KiB per dispatch) on `python bench.py --no-cpu --mode eager --steps 8 --warmup 2`,
-# scaled by what the same counters read for the 256 MiB calibration copy
-# (`python bench.py --copy-calibration`: FETCH x 2.0, WRITE x 1.0).  Valid only for
-# the kernel sources it was taken on (hash below); otherwise reported as null.
-GATEUP_TRAFFIC = {"src_sha256_16": "c4aa42dc9be3ee16", "fetch_kib": 114866.5, "write_kib": 112.0,
-                  "fetch_scale": 2.0, "write_scale": 1.0}
+# HBM traffic of the gate/up GEMVs measured by rocprofv3 PMC counters (FETCH_SIZE,
+# WRITE_SIZE, KiB per dispatch, median over the run's dispatches) on
+# `python bench.py --no-cpu --mode eager --steps 8 --warmup 2` (dense), `--config pad
+# --steps 8` and `--config moe --steps 8`, scaled by what the same counters read for the
+# 256 MiB calibration copy (`python bench.py --copy-calibration`: FETCH x 2.0, WRITE x 1.0).
+# Valid only for the kernel sources they were taken on (hash below); otherwise null.
+GEMV_TRAFFIC = {"src_sha256_16": "a1941fb4b9d0e5ec", "fetch_scale": 2.0, "write_scale": 1.0,
+                "dense": (114866.5, 112.0), "pad": (46630.5, 68.3), "moe": (36905.9, 72.0)}
 GEMV_SOURCES = ("layer_pipeline_stage_amd/csrc/gemv.hip", "layer_pipeline_stage_amd/csrc/gemv_core.h",
                 "layer_pipeline_stage_amd/csrc/dev.h")
 
 
-def gateup_traffic():
+def gateup_traffic(which="dense"):
+    """Counter-measured HBM bytes of one gate/up launch of the named workload, or None
+    when the GEMV sources have changed since the counters were taken."""
     import hashlib
     h = hashlib.sha256()
     for f in GEMV_SOURCES:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
-    t = GATEUP_TRAFFIC
+    t = GEMV_TRAFFIC
     if h.hexdigest()[:16] != t["src_sha256_16"]:
         return None
-    return int(1024 * (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]))
+    fetch, write = t[which]
+    return int(1024 * (fetch * t["fetch_scale"] + write * t["write_scale"]))
 
 
 def gateup_bytes(cfg) -> int:
@@ -255,7 +259,7 @@ def pad_bench(torch, synth, lps, runtime, steps, cpu=True):
     g = out["kernels"]["gateup"]
     out["roofline"] = _roofline("hbm", "rmsnorm + MXFP4 gate/up GEMV + SwiGLU ([34944, 5120], "
                                 "e2m1 + e8m0 per 32)", PAD_KERNEL_BYTES["gateup"](c, 0),
-                                g["avg_us"], HBM_PEAK_GBS, "GB/s",
+                                g["avg_us"], HBM_PEAK_GBS, "GB/s", traffic=gateup_traffic("pad"),
                                 bytes_per_launch=PAD_KERNEL_BYTES["gateup"](c, 0))
     out["config"] = {"workload": "padded-head MXFP4 decode: 4 layers, n_embd 5120, 36 q / 6 kv "
                                  "heads of 256 (12 q, 2 kv zero dummies), ff 17472, MXFP4 weights, "
@@ -343,7 +347,7 @@ def moe_bench(torch, synth, lps, runtime, steps, cpu=True):
            "roofline": _roofline("hbm", "rmsnorm + gate/up GEMV + SwiGLU of the 8 selected "
                                  "experts and the shared one (9 x [2048, 2048] bf16)", gu_bytes,
                                  kernels["moe_gateup"]["avg_us"], HBM_PEAK_GBS, "GB/s",
-                                 bytes_per_launch=gu_bytes),
+                                 traffic=gateup_traffic("moe"), bytes_per_launch=gu_bytes),
            "kernels": kernels,
            "prefill": {"tokens": T, "ms": round(1e3 * tp, 3), "tok_s": round(T / tp, 1),
                        "tflops": round(flop / tp / 1e12, 1),
