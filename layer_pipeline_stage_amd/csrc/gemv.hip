@@ -187,7 +187,8 @@ __device__ __forceinline__ void epilogue(const GemvP& p, int u, int r0, int r1, 
 // Launch shapes: threads per workgroup, workgroup cap and U (chunks per lane
 // and row in one batch).  Every workgroup stages the activation vector once, so
 // staging costs grid * 4K bytes of L2 reads next to the N * K weight bytes.
-//  - f32 / bf16 rows: 256 threads, up to 2048 groups, U = 4;
+//  - f32 / bf16 rows: 256 threads (512 for gate/up, O and down), up to 2048
+//    groups, U = 4;
 //  - MXFP4 rows (0.53 bytes per weight, so the f32 vector is large next to a
 //    row): U is the row's chunks per lane rounded up to 3, 5 or 9, so one batch
 //    holds a whole row; 512-thread groups for short rows (many units per wave,
@@ -525,8 +526,13 @@ static int launch_t(const GemvP& p, hipStream_t st, Stamp sp, int* waves) {
     else if (per_lane <= 9) LPS_GOB(9, LPS_MX_NTL, LPS_MX_MAXBL);
     else LPS_GOB(4, LPS_MX_NT, LPS_MX_MAXB);
   } else {
+    // gate/up and the residual-add projections (O, down) in 512-thread groups: half as
+    // many groups stage the vector, and at the 8B slice every wave then takes exactly
+    // one unit (gate/up 37.2 -> 36.8 us, down 21.0 -> 20.7 us); QKV and the head keep
+    // 256 threads (12.6 and 48.5 us at 512 against 11.5 and 47.4)
+    constexpr int NTB = (EPI == EPI_SWIGLU || EPI == EPI_ADD) ? 2 * LPS_BF_NT : LPS_BF_NT;
     if (per_lane <= 2) LPS_GOB(2, LPS_BF_NT, LPS_BF_MAXB);   // short rows: no empty chunk slots
-    else LPS_GOB(LPS_BF_U, LPS_BF_NT, LPS_BF_MAXB);
+    else LPS_GOB(LPS_BF_U, NTB, LPS_BF_MAXB);
   }
 #undef LPS_GOB
   LPS_HIP(hipGetLastError());
