@@ -199,24 +199,31 @@ __global__ __launch_bounds__(256) void k_pf_route(PfP p) {
 
 
 // The router on the matrix cores: 16 tokens per workgroup, their normed f32 rows
-// in LDS (row pitch d + 4 floats, so the 16 rows of an operand read fall on
-// distinct banks), logits[t, e] = sum_k h[t, k] Wr[e, k] on v_mfma_f32_16x16x4_f32
-// with f32 operands (the router reads the unrounded rows; bf16 weights widen
+// held in registers (each wave four rows) and staged in LDS one half of the columns
+// at a time (row pitch half + 4 floats, so the 16 rows of an operand read fall on
+// distinct banks; 66 KiB at d = 2048, so two workgroups share a CU),
+// logits[t, e] = sum_k h[t, k] Wr[e, k] on the matrix cores with the f32 rows split
+// exactly into bf16 parts (the router reads the unrounded rows; bf16 weights widen
 // exactly).  Wave wv takes experts 16 wv .. 16 wv + 15 (as 16 columns); lane
-// (n, g) supplies token n's and expert 16 wv + n's values at k = g d/4 + s for
-// step s, so each lane reads its k range contiguously (4 floats of h per LDS read,
-// 8 bf16 of Wr per global read).  The selection is the tile router's.  d % 32 == 0,
-// E <= 64, d <= 2300 (the 16 rows fit 144 KiB of LDS); wider rows take the tile router.
+// (n, g) supplies token n's and expert 16 wv + n's values at k = 32 s + 8 g .. + 7
+// for step s, the steps in ascending order across both halves.  The selection is
+// the tile router's.  d % 32 == 0, E <= 64, d <= 256 PF_MROW; wider rows take the
+// tile router.
 constexpr int PF_MTOK = 16;
 constexpr int PF_MUNR = 8;   // router k steps per lane and batch (two batches in flight)
 constexpr int PF_MROW = 9;   // float4s per lane of a normed row (d <= 2304)
 
+// floats of LDS the router stages per token row (the wider half plus the pad)
+inline int pf_mx_pitch(int d) { const int ns = d / 32; return 32 * (ns - ns / 2) + 4; }
+
 __global__ __launch_bounds__(256) void k_pf_route_mx(PfP p) {
-  extern __shared__ float hs[];            // [PF_MTOK][d + 4] normed rows (f32)
+  extern __shared__ float hs[];            // [PF_MTOK][pitch]: one half of the normed rows
   __shared__ float lg[PF_MTOK][PF_MAXE];
   const int t0 = blockIdx.x * PF_MTOK;
   const int lane = threadIdx.x & 63, wv = threadIdx.x / 64;
-  const int d = p.d, dp = d + 4;
+  const int d = p.d;
+  const int ns = d / 32, hb = ns / 2;      // k steps; the first half's
+  const int dp = 32 * (ns - hb) + 4;
   // each wave normalises four rows; the four rows' float4s all go out at once (rows
   // past T are zero)
   f32x4 vq[4][PF_MROW];
@@ -230,34 +237,17 @@ __global__ __launch_bounds__(256) void k_pf_route_mx(PfP p) {
                                     : f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
+  // the sum of squares visits the row in the order the tile router does
+  float rinv[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int r = wv * 4 + q, t = t0 + r;
-    float* h = hs + r * dp;
-    // the sum of squares and the scaling visit the row in the order the tile router does
-    f32x4* v = vq[q];
+    const f32x4* v = vq[q];
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < PF_MROW; ++i) ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
     ss = wave_sum(ss);
-    const float rinv = 1.0f / sqrtf(ss / float(d) + p.eps);
-#pragma unroll
-    for (int i = 0; i < PF_MROW; ++i) {
-      const int c = lane * 4 + 256 * i;
-      if (c < d) {
-        f32x4 y = v[i];
-        if (t < p.T) {
-          const f32x4 gg = *reinterpret_cast<const f32x4*>(p.g + c);
-          y.x = y.x * rinv * gg.x;
-          y.y = y.y * rinv * gg.y;
-          y.z = y.z * rinv * gg.z;
-          y.w = y.w * rinv * gg.w;
-        }
-        *reinterpret_cast<f32x4*>(h + c) = y;
-      }
-    }
+    rinv[q] = 1.0f / sqrtf(ss / float(d) + p.eps);
   }
-  __syncthreads();
   // logits[t, e] = sum_k h[t, k] Wr[e, k] on v_mfma_f32_16x16x32_bf16: wave wv takes
   // experts 16 wv .. 16 wv + 15 as columns, the 16 tokens as rows; lane (n, g) supplies
   // token n's and expert 16 wv + n's values at k = 32 s + 8 g .. + 7 for step s.  The
@@ -272,7 +262,6 @@ __global__ __launch_bounds__(256) void k_pf_route_mx(PfP p) {
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(p.wr), (short)0, p.E * d * 2, 0x00020000);
   const int boff = (e * d + 8 * g) * 2;     // this lane's row and k offset, in bytes
-  const int ns = d / 32;                    // k steps (d % 32 == 0)
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   u32x4 bq0[PF_MUNR], bq1[PF_MUNR];
 #define PF_RLOAD_B(BQ, S0)                                                                     \
@@ -282,9 +271,9 @@ __global__ __launch_bounds__(256) void k_pf_route_mx(PfP p) {
 #define PF_RMMA_B(BQ, S0)                                                                      \
   _Pragma("unroll") for (int u = 0; u < PF_MUNR; ++u) {                                        \
     const int st = (S0) + u;                                                                   \
-    if (st < ns) {                                                                             \
-      const f32x4 a0 = *reinterpret_cast<const f32x4*>(ha + 32 * st);                          \
-      const f32x4 a1 = *reinterpret_cast<const f32x4*>(ha + 32 * st + 4);                      \
+    if (st < se) {                                                                             \
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(ha + 32 * (st - sb));                   \
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(ha + 32 * (st - sb) + 4);               \
       const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};                    \
       bf16x8 hi, mid, lo;                                                                      \
       _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                          \
@@ -302,14 +291,63 @@ __global__ __launch_bounds__(256) void k_pf_route_mx(PfP p) {
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, b, acc, 0, 0, 0);                      \
     }                                                                                          \
   }
-  // the router rows stream from L2 in batches of PF_MUNR steps, double-buffered
-  PF_RLOAD_B(bq0, 0)
-  for (int s0 = 0; s0 < ns; s0 += 2 * PF_MUNR) {
-    PF_RLOAD_B(bq1, s0 + PF_MUNR)
-    PF_RMMA_B(bq0, s0)
-    PF_RLOAD_B(bq0, s0 + 2 * PF_MUNR)
-    PF_RMMA_B(bq1, s0 + PF_MUNR)
+  // the columns c_lo .. c_hi - 1 of the wave's four rows (v), scaled, into LDS
+  auto stage = [&](const f32x4 (&v)[4][PF_MROW], int c_lo, int c_hi) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = wv * 4 + q, t = t0 + r;
+      float* h = hs + r * dp - c_lo;
+#pragma unroll
+      for (int i = 0; i < PF_MROW; ++i) {
+        const int c = lane * 4 + 256 * i;
+        if (c >= c_lo && c < c_hi) {
+          f32x4 y = v[q][i];
+          if (t < p.T) {
+            const f32x4 gg = *reinterpret_cast<const f32x4*>(p.g + c);
+            y.x = y.x * rinv[q] * gg.x;
+            y.y = y.y * rinv[q] * gg.y;
+            y.z = y.z * rinv[q] * gg.z;
+            y.w = y.w * rinv[q] * gg.w;
+          }
+          *reinterpret_cast<f32x4*>(h + c) = y;
+        }
+      }
+    }
+  };
+  // the k steps sb .. se - 1 over the staged columns; the router rows stream from L2
+  // in batches of PF_MUNR steps, double-buffered
+  auto mma = [&](int sb, int se) {
+    PF_RLOAD_B(bq0, sb)
+    for (int s0 = sb; s0 < se; s0 += 2 * PF_MUNR) {
+      PF_RLOAD_B(bq1, s0 + PF_MUNR)
+      PF_RMMA_B(bq0, s0)
+      PF_RLOAD_B(bq0, s0 + 2 * PF_MUNR)
+      PF_RMMA_B(bq1, s0 + PF_MUNR)
+    }
+  };
+  stage(vq, 0, 32 * hb);
+  __syncthreads();
+  mma(0, hb);
+  __syncthreads();   // every wave is done with the first half's rows
+  {
+    // the second half's columns again (from L2), so the rows need not stay in
+    // registers through the first half's products
+    f32x4 v2[4][PF_MROW];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int t = t0 + wv * 4 + q;
+#pragma unroll
+      for (int i = 0; i < PF_MROW; ++i) {
+        const int c = lane * 4 + 256 * i;
+        v2[q][i] = (t < p.T && c >= 32 * hb && c < d)
+                       ? *reinterpret_cast<const f32x4*>(p.x + (long long)t * d + c)
+                       : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    stage(v2, 32 * hb, d);
   }
+  __syncthreads();
+  mma(hb, ns);
 #undef PF_RLOAD_B
 #undef PF_RMMA_B
   // acc[i] = logits[token 4 g + i][expert 16 wv + n]
@@ -747,9 +785,9 @@ extern "C" int lps_moe_prefill(const lps_moe_desc* m, float* x, int32_t T, int32
   hipStream_t st = as_stream(s_main), sr = as_stream(s_remote);
   uint16_t* xr = reinterpret_cast<uint16_t*>(sc + s.xr);
   const size_t rlds = size_t(PF_TOK) * m->d * 4;
-  // the matrix-core router where its LDS rows fit (d <= 2296), else the tile router
-  const size_t mlds = size_t(PF_MTOK) * (m->d + 4) * 4;
-  const bool route_mx = m->d % 32 == 0 && m->d <= 256 * PF_MROW && mlds <= 144 * 1024;
+  // the matrix-core router where its rows fit its registers (d <= 2304), else the tile router
+  const size_t mlds = size_t(PF_MTOK) * pf_mx_pitch(m->d) * 4;
+  const bool route_mx = m->d % 32 == 0 && m->d <= 256 * PF_MROW;
   int rc = ensure_lds((const void*)k_pf_route<false>, rlds);
   if (!rc) rc = route_mx ? ensure_lds((const void*)k_pf_route_mx, mlds)
                          : ensure_lds((const void*)k_pf_route<true>, rlds);
