@@ -416,10 +416,21 @@ __device__ __forceinline__ bool argmax_better(float v, int j, float b, int ix) {
 __device__ __forceinline__ int argmax_partials(const float* pval, const int* pidx, int n, int vocab) {
   float b = -INFINITY;
   int ix = 0x7fffffff;
-  for (int i = threadIdx.x; i < n; i += 1024) {
-    const float v = pval[i];
-    const int j = pidx[i];
-    if (argmax_better(v, j, b, ix)) { b = v; ix = j; }
+  // up to AB of a thread's partials loaded at once (one round trip, not one per
+  // partial); the selection is exact, so the order of the candidates does not matter
+  constexpr int AB = 8;
+  for (int i0 = threadIdx.x; i0 < n; i0 += 1024 * AB) {
+    float v[AB];
+    int j[AB];
+#pragma unroll
+    for (int u = 0; u < AB; ++u) {
+      const int i = i0 + 1024 * u;
+      v[u] = i < n ? pval[i] : -INFINITY;
+      j[u] = i < n ? pidx[i] : 0x7fffffff;
+    }
+#pragma unroll
+    for (int u = 0; u < AB; ++u)
+      if (i0 + 1024 * u < n && argmax_better(v[u], j[u], b, ix)) { b = v[u]; ix = j[u]; }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
