@@ -488,12 +488,20 @@ __global__ __launch_bounds__(1024) void k_step_finish(const float* pval, const i
   __syncthreads();
   const int t = nxt;
   const bool ok = t >= 0 && t < vocab;
-  for (int i = threadIdx.x; i < d; i += 1024) {
-    float v;
-    if (!ok) v = __uint_as_float(0x7FC00000u);
-    else if (WT == LPS_F32) v = static_cast<const float*>(table)[(long long)t * d + i];
-    else v = bf16_to_f32(static_cast<const uint16_t*>(table)[(long long)t * d + i]);
-    x_next[i] = v;
+  // the row's loads all go out before its stores (one round trip, not one per element)
+  constexpr int EB = 4;
+  for (int i0 = threadIdx.x; i0 < d; i0 += 1024 * EB) {
+    float v[EB];
+#pragma unroll
+    for (int u = 0; u < EB; ++u) {
+      const int i = i0 + 1024 * u;
+      if (i >= d || !ok) v[u] = __uint_as_float(0x7FC00000u);
+      else if (WT == LPS_F32) v[u] = static_cast<const float*>(table)[(long long)t * d + i];
+      else v[u] = bf16_to_f32(static_cast<const uint16_t*>(table)[(long long)t * d + i]);
+    }
+#pragma unroll
+    for (int u = 0; u < EB; ++u)
+      if (i0 + 1024 * u < d) x_next[i0 + 1024 * u] = v[u];
   }
 }
 

@@ -173,10 +173,22 @@ __global__ void k_hist_logits(const int32_t* state, const float* logits, int voc
   const int s = state[1];
   float* dst = hist && s >= 0 && s < cap ? hist + (long long)s * vocab : nullptr;
   float* rdst = ring && s >= 0 ? ring + (long long)(s % slots) * vocab : nullptr;
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < vocab; i += gridDim.x * blockDim.x) {
-    const float v = logits[i];
-    if (dst) dst[i] = v;
-    if (rdst) rdst[i] = v;
+  // a thread's HB values are loaded before any is stored (one round trip, not one per
+  // value: the stores could alias the loads, so they would otherwise wait in turn)
+  constexpr int HB = 4;
+  const int stride = gridDim.x * blockDim.x;
+  for (int i0 = blockIdx.x * blockDim.x + threadIdx.x; i0 < vocab; i0 += stride * HB) {
+    float v[HB];
+#pragma unroll
+    for (int u = 0; u < HB; ++u) v[u] = i0 + stride * u < vocab ? logits[i0 + stride * u] : 0.f;
+#pragma unroll
+    for (int u = 0; u < HB; ++u) {
+      const int i = i0 + stride * u;
+      if (i < vocab) {
+        if (dst) dst[i] = v[u];
+        if (rdst) rdst[i] = v[u];
+      }
+    }
   }
 }
 
