@@ -173,10 +173,20 @@ __global__ void k_hist_logits(const int32_t* state, const float* logits, int voc
   const int s = state[1];
   float* dst = hist && s >= 0 && s < cap ? hist + (long long)s * vocab : nullptr;
   float* rdst = ring && s >= 0 ? ring + (long long)(s % slots) * vocab : nullptr;
+  const int stride = gridDim.x * blockDim.x;
+  if ((vocab & 3) == 0 && ((reinterpret_cast<uintptr_t>(logits) | reinterpret_cast<uintptr_t>(dst) |
+                            reinterpret_cast<uintptr_t>(rdst)) & 15) == 0) {
+    // 16 bytes per lane: the ring row crosses to host memory in whole-line writes
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < vocab / 4; i += stride) {
+      const f32x4 v = reinterpret_cast<const f32x4*>(logits)[i];
+      if (dst) reinterpret_cast<f32x4*>(dst)[i] = v;
+      if (rdst) reinterpret_cast<f32x4*>(rdst)[i] = v;
+    }
+    return;
+  }
   // a thread's HB values are loaded before any is stored (one round trip, not one per
   // value: the stores could alias the loads, so they would otherwise wait in turn)
   constexpr int HB = 4;
-  const int stride = gridDim.x * blockDim.x;
   for (int i0 = blockIdx.x * blockDim.x + threadIdx.x; i0 < vocab; i0 += stride * HB) {
     float v[HB];
 #pragma unroll
