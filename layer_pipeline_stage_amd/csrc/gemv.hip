@@ -262,11 +262,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const uint8_t* base, 
     const uint8_t* ub_ = unit_base<EPI>(p, uu_);                                        \
     const auto w0_ = row_rsrc(ub_ + (long long)r0_ * p.wrow, wb_);                      \
     const auto w1_ = row_rsrc(ub_ + (long long)rr1_ * p.wrow, wb_);                     \
-    _Pragma("unroll") for (int i = 0; i < U; ++i) {                                     \
-      const int off = ((B0) + lane + WAVE * i) * 16;                                    \
-      V0[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w0_, off, 0, BUF_NT)); \
-      V1[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w1_, off, 0, BUF_NT)); \
-    }                                                                                   \
+    /* MXFP4: the batch's scale bytes go out before its codes: loads complete in issue \
+       order, and the products read every scale of the batch first, so scales issued  \
+       last would hold the first product until the whole batch had landed */           \
     if constexpr (WT == LPS_MXFP4) {                                                    \
       const int sb_ = (LIVE) ? (int)p.srow : 0;                                         \
       const auto s0_ = row_rsrc(p.s + (long long)r0_ * p.srow, sb_);                    \
@@ -278,6 +276,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const uint8_t* base, 
       }                                                                                 \
     } else {                                                                            \
       _Pragma("unroll") for (int i = 0; i < U; ++i) S0[i] = S1[i] = 0;                  \
+    }                                                                                   \
+    _Pragma("unroll") for (int i = 0; i < U; ++i) {                                     \
+      const int off = ((B0) + lane + WAVE * i) * 16;                                    \
+      V0[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w0_, off, 0, BUF_NT)); \
+      V1[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w1_, off, 0, BUF_NT)); \
+      /* MXFP4: the codes go out in the order the products read them (chunk i of   \
+         both rows, then chunk i + 1), so each product waits only for its own */    \
+      if constexpr (WT == LPS_MXFP4) __builtin_amdgcn_sched_barrier(0);                 \
     }                                                                                   \
   }
 #define BUF_FMA(V0, V1, S0, S1, B0, XO)                            \
