@@ -281,9 +281,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const uint8_t* base, 
       const int off = ((B0) + lane + WAVE * i) * 16;                                    \
       V0[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w0_, off, 0, BUF_NT)); \
       V1[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w1_, off, 0, BUF_NT)); \
-      /* MXFP4: the codes go out in the order the products read them (chunk i of   \
-         both rows, then chunk i + 1), so each product waits only for its own */    \
-      if constexpr (WT == LPS_MXFP4) __builtin_amdgcn_sched_barrier(0);                 \
+      /* the chunks go out in the order the products read them (chunk i of both    \
+         rows, then chunk i + 1), so each product waits only for its own */         \
+      __builtin_amdgcn_sched_barrier(0);                                                \
     }                                                                                   \
   }
 #define BUF_FMA(V0, V1, S0, S1, B0, XO)                            \
