@@ -164,7 +164,7 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attn(AttnP p) {
     float l = 0.f;
 #pragma unroll
     for (int r = 0; r < ATT_RPL; ++r) {
-      const float e = (v[r] == -INFINITY) ? 0.f : expf(v[r] - m);
+      const float e = (v[r] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(v[r] - m);
       sc[h][lane + WAVE * r] = e;
       l += e;
     }
@@ -340,7 +340,7 @@ void k_attn_mfma(AttnP p) {
   float pv[4], l = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    pv[i] = sv[i] == -INFINITY ? 0.f : expf(sv[i] - m);
+    pv[i] = sv[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[i] - m);
     l += pv[i];
   }
   l += __shfl_xor(l, 16, WAVE);
@@ -387,7 +387,7 @@ void k_attn_mfma(AttnP p) {
     f32x2 acc = {0.f, 0.f};
 #pragma unroll
     for (int v = 0; v < AM_WAVES; ++v) {
-      const float sc = mw[v][h] == -INFINITY ? 0.f : expf(mw[v][h] - M);
+      const float sc = mw[v][h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[v][h] - M);
       L = fmaf(sc, lw[v][h], L);
       const f32x2 x = *reinterpret_cast<const f32x2*>(red + (v * G + h) * HDP + 2 * e2);
       acc.x = fmaf(sc, x.x, acc.x);
@@ -402,7 +402,7 @@ void k_attn_mfma(AttnP p) {
 }
 
 // Merge of the chunk partials of one q head: M = max m_c, L = sum_c l_c
-// e^(m_c - M), o = sum_c o_c e^(m_c - M) / L.  A separate launch: the partials
+// 2^(m_c - M), o = sum_c o_c 2^(m_c - M) / L (the maxima in base-2 units).  A separate launch: the partials
 // of all tiles are complete when it starts (stream order), so no device-scope
 // fence or counter is needed.  One workgroup per q head; thread (part, e2) owns
 // output columns 2 e2, 2 e2 + 1 and the chunks c = part (mod P).  It loads the
@@ -449,13 +449,13 @@ __global__ __launch_bounds__(MERGE_THREADS) void k_attn_merge(AttnP p) {
 #pragma unroll
     for (int k = 0; k < MERGE_B; ++k) Mn = fmaxf(Mn, mv[k]);
     if (Mn != -INFINITY) {
-      const float r = M == -INFINITY ? 0.f : expf(M - Mn);
+      const float r = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
       L *= r;
       O.x *= r;
       O.y *= r;
 #pragma unroll
       for (int k = 0; k < MERGE_B; ++k) {
-        const float w = mv[k] == -INFINITY ? 0.f : expf(mv[k] - Mn);
+        const float w = mv[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv[k] - Mn);
         L = fmaf(w, lv[k], L);
         O.x = fmaf(w, ov[k].x, O.x);
         O.y = fmaf(w, ov[k].y, O.y);
@@ -477,7 +477,7 @@ __global__ __launch_bounds__(MERGE_THREADS) void k_attn_merge(AttnP p) {
     f32x2 o = {0.f, 0.f};
 #pragma unroll
     for (int q = 0; q < P; ++q) {
-      const float w = sM[q] == -INFINITY ? 0.f : expf(sM[q] - Mt);
+      const float w = sM[q] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sM[q] - Mt);
       Lt = fmaf(w, sL[q], Lt);
       o.x = fmaf(w, sO[q][t].x, o.x);
       o.y = fmaf(w, sO[q][t].y, o.y);
@@ -541,7 +541,9 @@ int launch_attention(int nq, int nkv, int hd, int kvdtype, const void* kc, const
   p.n = pos_dev ? ctx_max : n_rows;
   p.nch = nchunks(p.n);            // the grid; blocks past the device row count exit
   p.nstride = pos_dev ? nchunks(ctx_max) : p.nch;
-  p.scale = 1.0f / sqrtf(float(hd));
+  // scores in base 2: e^(q.k / sqrt(hd) - m) = 2^(q.k log2(e) / sqrt(hd) - m'), so every
+  // softmax and merge weight is one v_exp_f32 (the partials' maxima are in these units)
+  p.scale = float(1.4426950408889634 / std::sqrt(double(hd)));
   const size_t nch_max = nchunks(ctx_max);
   char* s = static_cast<char*>(scratch);
   p.pm = reinterpret_cast<float*>(s);
