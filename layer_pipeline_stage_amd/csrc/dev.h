@@ -104,6 +104,11 @@ __device__ __forceinline__ float strided_sum(float v) {
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+// e^x as one v_exp_f32 of x log2(e) (a few ulps from the correctly rounded expf, which
+// takes ~10 instructions): for softmax weights, whose selections never depend on it
+__device__ __forceinline__ float exp_native(float x) {
+  return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
 // silu from the native base-2 exponential and reciprocal (v_exp_f32, v_rcp_f32: about
 // one ulp each, a few ulp together): for epilogues that round the product to bf16
 // right after, where the correctly rounded expf and division cost ~20 VALU

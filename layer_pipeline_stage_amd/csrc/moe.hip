@@ -87,7 +87,7 @@ __global__ __launch_bounds__(WAVE) void k_route_topk(RouteP p) {
   m = wave_max(m);
   float z = 0.f;
 #pragma unroll
-  for (int q = 0; q < MOE_MAXE / 64; ++q) z += (lane + 64 * q < p.E) ? expf(r[q] - m) : 0.f;
+  for (int q = 0; q < MOE_MAXE / 64; ++q) z += (lane + 64 * q < p.E) ? exp_native(r[q] - m) : 0.f;
   z = wave_sum(z);
   // k rounds of argmax over the logits (ties -> lower id); softmax is monotone
   __shared__ float sel_pi[MOE_MAXK];
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(WAVE) void k_route_topk(RouteP p) {
 #pragma unroll
     for (int q = 0; q < MOE_MAXE / 64; ++q)
       if (lane + 64 * q == bi) r[q] = -INFINITY;
-    const float pi = none ? __uint_as_float(0x7FC00000u) : expf(bv - m) / z;
+    const float pi = none ? __uint_as_float(0x7FC00000u) : exp_native(bv - m) / z;
     if (lane == 0) {
       sel_pi[j] = pi;
       sel_id[j] = bi;

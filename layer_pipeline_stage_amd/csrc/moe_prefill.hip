@@ -86,7 +86,7 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) { return f32_to_bf16(f); }
 __device__ __forceinline__ void pf_select(const PfP& p, const float* lgr, int t, int lane) {
   float v = lane < p.E ? lgr[lane] : -INFINITY;
   const float m = wave_max(v);
-  const float z = wave_sum(lane < p.E ? expf(v - m) : 0.f);
+  const float z = wave_sum(lane < p.E ? exp_native(v - m) : 0.f);
   float ssum = 0.f;
   float pis = 0.f;   // this lane's selected pi, if selected
   int slot = -1;
@@ -94,7 +94,7 @@ __device__ __forceinline__ void pf_select(const PfP& p, const float* lgr, int t,
     const float mx = wave_max(v);
     const unsigned long long msk = __ballot(v == mx && lane < p.E);
     const int sel = msk ? __ffsll((long long)msk) - 1 : j;     // no finite logit: slot id
-    const float pi = msk ? expf(mx - m) / z : __uint_as_float(0x7FC00000u);
+    const float pi = msk ? exp_native(mx - m) / z : __uint_as_float(0x7FC00000u);
     if (lane == sel) {
       v = -INFINITY;
       pis = pi;
