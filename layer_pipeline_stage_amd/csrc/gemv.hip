@@ -27,6 +27,7 @@
 #include "gemv_core.h"
 #include "internal.h"
 
+#include <algorithm>
 #include <cmath>
 #include <type_traits>
 
@@ -188,7 +189,7 @@ __device__ __forceinline__ void epilogue(const GemvP& p, int u, int r0, int r1, 
 // and row in one batch).  Every workgroup stages the activation vector once, so
 // staging costs grid * 4K bytes of L2 reads next to the N * K weight bytes.
 //  - f32 / bf16 rows: 256 threads (512 for gate/up, O and down), up to 2048
-//    groups, U = 4;
+//    groups, U = 4; the LM head 512 threads, up to 1000 groups;
 //  - MXFP4 rows (0.53 bytes per weight, so the f32 vector is large next to a
 //    row): U is the row's chunks per lane rounded up to 3, 5 or 9, so one batch
 //    holds a whole row; 512-thread groups for short rows (many units per wave,
@@ -202,6 +203,15 @@ __device__ __forceinline__ void epilogue(const GemvP& p, int u, int r0, int r1, 
 #endif
 #ifndef LPS_BF_U
 #define LPS_BF_U 4
+#endif
+// the LM head: 512-thread groups, at most 1000 of them (at a 32000-row vocabulary
+// every wave walks two row pairs: 46.4 -> 45.1 us against 256-thread groups capped at
+// 2048, which leave some waves one pair and most two)
+#ifndef LPS_HEAD_NT
+#define LPS_HEAD_NT 512
+#endif
+#ifndef LPS_HEAD_MAXB
+#define LPS_HEAD_MAXB 1000
 #endif
 #ifndef LPS_MX_NT
 #define LPS_MX_NT 512
@@ -553,10 +563,11 @@ static int launch_t(const GemvP& p, hipStream_t st, Stamp sp, int* waves) {
   } else {
     // gate/up and the residual-add projections (O, down) in 512-thread groups: half as
     // many groups stage the vector, and at the 8B slice every wave then takes exactly
-    // one unit (gate/up 37.2 -> 36.8 us, down 21.0 -> 20.7 us); QKV and the head keep
-    // 256 threads (12.6 and 48.5 us at 512 against 11.5 and 47.4)
+    // one unit (gate/up 37.2 -> 36.8 us, down 21.0 -> 20.7 us); QKV keeps 256 threads
+    // (12.6 us at 512 against 11.5); the head has its own shape (above)
     constexpr int NTB = (EPI == EPI_SWIGLU || EPI == EPI_ADD) ? 2 * LPS_BF_NT : LPS_BF_NT;
     if (per_lane <= 2) LPS_GOB(2, LPS_BF_NT, LPS_BF_MAXB);   // short rows: no empty chunk slots
+    else if constexpr (EPI == EPI_LOGITS) LPS_GOB(LPS_BF_U, LPS_HEAD_NT, LPS_HEAD_MAXB);
     else LPS_GOB(LPS_BF_U, NTB, LPS_BF_MAXB);
   }
 #undef LPS_GOB
@@ -690,7 +701,10 @@ int launch_qkv(const QkvArgs& a, hipStream_t st, Stamp sp) {
 }
 
 // most per-wave (value, index) partials an LM-head launch can write
-static size_t head_waves_max() { return size_t(LPS_BF_MAXB) * (LPS_BF_NT / WAVE); }
+static size_t head_waves_max() {
+  return std::max(size_t(LPS_BF_MAXB) * (LPS_BF_NT / WAVE),
+                  size_t(LPS_HEAD_MAXB) * (LPS_HEAD_NT / WAVE));
+}
 
 size_t head_scratch(const lps_head_desc* h) {
   (void)h;
